@@ -1,0 +1,585 @@
+"""CPU oracle for one GPU's routed MoE expert layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain definition that the
+HIP kernels are checked against.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+never does.  It shares no code with the GPU library and does not import it.
+
+Everything is computed in float64 from the bf16 / fp32 values of the inputs.
+A rounding to bf16 or fp32 appears exactly where the layer stores a tensor in
+that format.  Passing ``exact=True`` removes every bf16 rounding, which turns
+the forward into a smooth function for finite-difference checks.
+
+Sources (the pages this follows):
+  [KOSMOS]  "KOSMOS: Self-scheduling Persistent Kernels for Communication-Compute
+            Overlap", section 3.3.1 (MoE forward: route, plan, dispatch with
+            GEMM1 and SwiGLU, GEMM2, fold), section 3.3.2 (backward), section
+            2.2 (MXFP8 training).
+  [OLMo-A]  "OLMo-core MoE, Appendix A: Kernel Interfaces and Profiling
+            Reference", A.1 (dispatch/combine and their adjoints, the fused
+            routed-expert node), A.2 (dst_rows route tensor, invalid routes),
+            A.3 (route id), A.4 (MXFP8 payload layout), A.5 (eq. 87).
+
+Readings where the pages are silent (each listed in the design notes):
+  score = softmax over all experts in fp32; top-K keyed on the fp32 logits,
+  ties to the lower expert index, slot 0 = best; renormalisation optional (off
+  by default); the per-expert bias is added to the logits before both; rows of
+  an expert segment are in ascending route id; SwiGLU = silu(gate) * up;
+  E8M0 exponent = floor(log2(amax)) - 8 (the OCP MX rule), E4M3 = OCP E4M3FN
+  with round-to-nearest-even and saturation at +-448.
+
+Parity pins: every function here is checked in tests/test_oracle_*.py against
+brute force, closed forms, library routines or invariants.  The exact fp32 bits
+of the softmax and of the fp32-rounded sums are not pinned beyond tolerance
+(parity unpinned at the last fp32 bit; the comparison is by tolerance).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+
+def bits_to_f64(u16) -> np.ndarray:
+    """bf16 bit patterns -> their exact values as float64."""
+    u = np.ascontiguousarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def values(a) -> np.ndarray:
+    """Accept bf16 bit patterns (uint16) or real values; return float64 values."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bits_to_f64(a)
+    return a.astype(np.float64, copy=False)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits; its smallest normal is 2^-126 and its
+    subnormal spacing is 2^-133.  Written with frexp so the rounding happens
+    once, straight from float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                 # x = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)            # below 2^-126 the spacing stays 2^-133
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+
+
+def round_f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits(v) -> np.ndarray:
+    """bf16-representable float64 values -> bit patterns (exact)."""
+    f = np.ascontiguousarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _identity(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _rounder(exact: bool):
+    return _identity if exact else round_bf16
+
+
+# --------------------------------------------------------------------------
+# route: logits, score, top-K      [KOSMOS 3.3.1 step 1 "Route"]
+# --------------------------------------------------------------------------
+
+
+def router_logits(x, w_r, bias=None) -> np.ndarray:
+    """L[t,e] = fp32(sum_d x[t,d] * W_r[e,d]) + b[e], bias added in fp32.
+
+    x: [N,D] bf16; w_r: [E,D] bf16 (stored expert-major); bias: [E] fp32 or None.
+    The dot products of bf16 values are summed in float64 and rounded once.
+    """
+    L = (values(x) @ values(w_r).T).astype(np.float32)
+    if bias is not None:
+        L = L + np.asarray(bias, dtype=np.float32)[None, :]
+    return L.astype(np.float32)
+
+
+def softmax(L) -> np.ndarray:
+    """Softmax over all experts of each token (float64)."""
+    L = np.asarray(L, dtype=np.float64)
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def topk_select(L, K: int) -> np.ndarray:
+    """The K largest logits of each token, best first; ties go to the lower index.
+
+    Done as K rounds of "take the maximum, then remove it"; argmax returns the
+    first (lowest-index) maximum, which is the tie rule.
+    """
+    work = np.array(L, dtype=np.float64, copy=True)
+    N, E = work.shape
+    if K > E:
+        raise ValueError("K > E")
+    out = np.empty((N, K), dtype=np.int32)
+    rows = np.arange(N)
+    for k in range(K):
+        j = np.argmax(work, axis=1)
+        out[:, k] = j
+        work[rows, j] = -np.inf
+    return out
+
+
+def route_probs(L, idx, renorm: int = 0) -> np.ndarray:
+    """Dispatch weight of each selected slot: the softmax probability of its
+    expert, optionally divided by the sum over the K selected slots; fp32."""
+    p = softmax(L)
+    sel = np.take_along_axis(p, np.asarray(idx, dtype=np.int64), axis=1)
+    if renorm:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# plan: the route map     [KOSMOS 3.3.1 step 2 "Plan"; OLMo-A A.2, A.3]
+# --------------------------------------------------------------------------
+
+
+def route_valid(idx, drop, E: int) -> np.ndarray:
+    """A route (t,k) is valid unless it is dropped or names no expert in [0,E)."""
+    idx = np.asarray(idx)
+    v = (idx >= 0) & (idx < E)
+    if drop is not None:
+        v &= np.asarray(drop) == 0
+    return v
+
+
+def route_map(idx, drop, E: int, align: int, rows_cap: int):
+    """Stable counting sort of the valid routes into expert-contiguous rows.
+
+    Route id r = t*K + k.  counts[e] = number of valid routes to e;
+    each expert's segment is counts[e] rounded up to a multiple of ``align``;
+    offsets is the exclusive scan of the segment sizes (E+1 entries).  Inside a
+    segment the routes sit in ascending route id.  dst_rows[t,k] is the row of
+    route (t,k) or -1 if invalid; row_route[i] is the route id held by row i, or
+    -1 for padding and unused rows.
+    Returns (counts int32 [E], offsets int32 [E+1], dst_rows int32 [N,K],
+    row_route int32 [rows_cap]).
+    """
+    idx = np.asarray(idx)
+    N, K = idx.shape
+    valid = route_valid(idx, drop, E)
+    e_of_r = np.where(valid, idx, E).reshape(-1).astype(np.int64)   # E = "no expert"
+    counts = np.bincount(e_of_r, minlength=E + 1)[:E]
+    seg = ((counts + align - 1) // align) * align
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(seg)
+    if offsets[E] > rows_cap:
+        raise ValueError("rows_cap too small")
+    order = np.argsort(e_of_r, kind="stable")      # grouped by expert, route id ascending
+    nvalid = int(counts.sum())
+    order = order[:nvalid]
+    first_in_order = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    e_sorted = e_of_r[order]
+    dst = offsets[e_sorted] + (np.arange(nvalid) - first_in_order[e_sorted])
+    dst_rows = np.full(N * K, -1, dtype=np.int64)
+    dst_rows[order] = dst
+    row_route = np.full(rows_cap, -1, dtype=np.int64)
+    row_route[dst] = order
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            dst_rows.reshape(N, K).astype(np.int32), row_route.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# dispatch / combine and their adjoints   [OLMo-A A.1-A.3; KOSMOS 3.3.1 steps 3, 5]
+# --------------------------------------------------------------------------
+
+
+def dispatch(x, row_route, K: int, weight=None, exact: bool = False) -> np.ndarray:
+    """X_d[i] = x[row_route[i] // K] for every row that holds a route; other
+    rows (padding, unused tail) are 0.
+
+    With ``weight`` ([N,K] fp32) each copy is scaled by its route's weight:
+    the product is formed in fp32 and stored as bf16 (the weighted PUT).
+    """
+    xv = values(x)
+    rr = np.asarray(row_route, dtype=np.int64)
+    out = np.zeros((rr.shape[0], xv.shape[1]), dtype=np.float64)
+    live = rr >= 0
+    tok = rr[live] // K
+    if weight is None:
+        out[live] = xv[tok]
+    else:
+        w = np.asarray(weight, dtype=np.float64).reshape(-1)[rr[live]]
+        prod = w[:, None] * xv[tok]                 # exact in float64 for fp32 weights
+        out[live] = prod if exact else round_bf16(round_f32(prod))
+    return out
+
+
+def combine(y, dst_rows, weight=None, exact: bool = False) -> np.ndarray:
+    """out[t] = sum over valid k of w[t,k] * Y[dst_rows[t,k]], stored once as bf16.
+
+    Invalid routes (dst_rows < 0) contribute nothing; ``weight`` None means 1.
+    The sum is exact (float64) and rounded once.
+    """
+    yv = values(y)
+    dst = np.asarray(dst_rows, dtype=np.int64)
+    N, K = dst.shape
+    acc = np.zeros((N, yv.shape[1]), dtype=np.float64)
+    for k in range(K):
+        ok = dst[:, k] >= 0
+        w = np.ones(N) if weight is None else np.asarray(weight, np.float64)[:, k]
+        acc[ok] += w[ok, None] * yv[dst[ok, k]]
+    return _rounder(exact)(acc)
+
+
+def combine_bwd(dout, dst_rows, weight, rows_cap: int, exact: bool = False) -> np.ndarray:
+    """Adjoint of the weighted combine: dY_d[dst_rows[t,k]] = w[t,k] * dOut[t]
+    (the router-weighted dY dispatch of the backward)."""
+    dst = np.asarray(dst_rows, dtype=np.int64)
+    N, K = dst.shape
+    rr = np.full(rows_cap, -1, dtype=np.int64)
+    ok = dst.reshape(-1) >= 0
+    rr[dst.reshape(-1)[ok]] = np.arange(N * K)[ok]
+    return dispatch(dout, rr, K, weight=weight, exact=exact)
+
+
+def dprob(dout, y, dst_rows) -> np.ndarray:
+    """Gradient w.r.t. each route's weight: <dOut[t], Y[dst_rows[t,k]]>, 0 if
+    invalid, fp32.  [KOSMOS 3.3.2: routing-weight gradients]"""
+    dv = values(dout)
+    yv = values(y)
+    dst = np.asarray(dst_rows, dtype=np.int64)
+    N, K = dst.shape
+    g = np.zeros((N, K), dtype=np.float64)
+    for k in range(K):
+        ok = dst[:, k] >= 0
+        g[ok, k] = np.einsum("nd,nd->n", dv[ok], yv[dst[ok, k]])
+    return g.astype(np.float32)
+
+
+def dispatch_bwd(dxd, dst_rows, exact: bool = False) -> np.ndarray:
+    """Adjoint of dispatch: dx[t] = sum over valid k of dX_d[dst_rows[t,k]]."""
+    return combine(dxd, dst_rows, None, exact=exact)
+
+
+# --------------------------------------------------------------------------
+# experts: GEMM1 + SwiGLU, GEMM2       [KOSMOS 3.3.1 steps 3-4; OLMo-A A.1]
+# --------------------------------------------------------------------------
+
+
+def silu(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-np.asarray(g, dtype=np.float64)))
+
+
+def swiglu(g, u, exact: bool = False):
+    """H = silu(gate) * up, from the stored (bf16) gate and up values."""
+    return _rounder(exact)(silu(g) * np.asarray(u, np.float64))
+
+
+def expert_mlp(xrows, wg, wu, wd, exact: bool = False):
+    """One expert on its rows.  wg, wu: [H,D]; wd: [D,H] (output-major storage).
+
+    G = X Wg^T, U = X Wu^T (each stored bf16), H = silu(G)*U (bf16),
+    Y = H Wd^T (bf16).  Returns (G, U, H, Y).
+    """
+    r = _rounder(exact)
+    X = values(xrows)
+    G = r(X @ values(wg).T)
+    U = r(X @ values(wu).T)
+    Hh = swiglu(G, U, exact)
+    Y = r(Hh @ values(wd).T)
+    return G, U, Hh, Y
+
+
+def experts_fwd(xd, offsets, w_gate, w_up, w_down, exact: bool = False):
+    """Apply expert e to rows offsets[e]..offsets[e+1] of X_d.  Rows outside
+    every segment stay 0.  Returns (G, U, H, Y) over all rows."""
+    xv = values(xd)
+    rows = xv.shape[0]
+    E = len(offsets) - 1
+    Hd = np.asarray(w_gate).shape[1]
+    D = xv.shape[1]
+    G = np.zeros((rows, Hd))
+    U = np.zeros((rows, Hd))
+    Hh = np.zeros((rows, Hd))
+    Y = np.zeros((rows, D))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue          # an expert with no rows is never read
+        G[a:b], U[a:b], Hh[a:b], Y[a:b] = expert_mlp(xv[a:b], w_gate[e], w_up[e], w_down[e], exact)
+    return G, U, Hh, Y
+
+
+# --------------------------------------------------------------------------
+# whole layer, forward       [KOSMOS 3.3.1; OLMo-A A.1 fused node, A.14 saved set]
+# --------------------------------------------------------------------------
+
+
+def layer_fwd(x, w_r, bias, w_gate, w_up, w_down, K: int, drop=None, renorm: int = 0,
+              align: int = 1, rows_cap: int = None, logits=None, exact: bool = False):
+    """Router -> top-K -> route map -> dispatch -> experts -> weighted combine.
+
+    ``logits`` may be given to skip the router product (route-map tests).
+    Returns a dict with every saved tensor and ``out``.
+    """
+    xv = values(x)
+    N = xv.shape[0]
+    E = np.asarray(w_r).shape[0]
+    if rows_cap is None:
+        rows_cap = N * K + E * (align - 1)
+    L = router_logits(x, w_r, bias) if logits is None else np.asarray(logits, np.float32)
+    idx = topk_select(L, K)
+    prob = route_probs(L, idx, renorm)
+    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap)
+    xd = dispatch(xv, row_route, K)
+    G, U, Hh, Y = experts_fwd(xd, offsets, w_gate, w_up, w_down, exact)
+    out = combine(Y, dst_rows, prob, exact)
+    return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
+                dst_rows=dst_rows, row_route=row_route, xd=xd, g=G, u=U, h=Hh, y=Y, out=out)
+
+
+def layer_fwd_tokens(fwd_route: dict, x, w_gate, w_up, w_down, tokens, K: int, exact=False):
+    """out[t] for a subset of tokens, given the route tensors of the whole batch.
+
+    Rows of a GEMM do not interact, so each sampled token's output needs only
+    its own K expert rows.  Returns (out [len(tokens), D], rows dict e -> Y rows).
+    """
+    xv = values(x)
+    idx = fwd_route["topk_idx"]
+    prob = fwd_route["topk_prob"]
+    dst = fwd_route["dst_rows"]
+    out = np.zeros((len(tokens), xv.shape[1]))
+    for j, t in enumerate(tokens):
+        acc = np.zeros(xv.shape[1])
+        for k in range(K):
+            if dst[t, k] < 0:
+                continue
+            e = int(idx[t, k])
+            _, _, _, y = expert_mlp(xv[t:t + 1], w_gate[e], w_up[e], w_down[e], exact)
+            acc += float(prob[t, k]) * y[0]
+        out[j] = acc
+    return _rounder(exact)(out)
+
+
+# --------------------------------------------------------------------------
+# whole layer, backward                   [KOSMOS 3.3.2; OLMo-A A.1 adjoint sequence]
+# --------------------------------------------------------------------------
+
+
+def experts_bwd(dyd, xd, g, u, h, offsets, w_gate, w_up, w_down, exact: bool = False):
+    """Down dgrad with the SwiGLU backward, down wgrad, gate/up dgrad and wgrad.
+
+    dH = dY W_down (kept at full precision; it only feeds the SwiGLU backward)
+    dG = dH * U * s * (1 + G (1 - s)), s = sigmoid(G);  dU = dH * silu(G)
+    dW_down[e] = dY_e^T H_e;  dX_d = dG W_gate + dU W_up (one sum);
+    dW_gate[e] = dG_e^T X_e;  dW_up[e] = dU_e^T X_e.   Every stored tensor is bf16.
+    """
+    r = _rounder(exact)
+    dy = values(dyd)
+    xv = values(xd)
+    rows, D = dy.shape
+    E = len(offsets) - 1
+    Hd = np.asarray(w_gate).shape[1]
+    dG = np.zeros((rows, Hd))
+    dU = np.zeros((rows, Hd))
+    dXd = np.zeros((rows, D))
+    dWg = np.zeros((E, Hd, D))
+    dWu = np.zeros((E, Hd, D))
+    dWd = np.zeros((E, D, Hd))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        Wg, Wu, Wd = values(w_gate[e]), values(w_up[e]), values(w_down[e])
+        G, U = np.asarray(g[a:b], np.float64), np.asarray(u[a:b], np.float64)
+        dH = dy[a:b] @ Wd
+        s = sigmoid(G)
+        dG[a:b] = r(dH * U * s * (1.0 + G * (1.0 - s)))
+        dU[a:b] = r(dH * G * s)
+        dWd[e] = r(dy[a:b].T @ np.asarray(h[a:b], np.float64))
+        dXd[a:b] = r(dG[a:b] @ Wg + dU[a:b] @ Wu)
+        dWg[e] = r(dG[a:b].T @ xv[a:b])
+        dWu[e] = r(dU[a:b].T @ xv[a:b])
+    return dict(dg=dG, du=dU, dxd=dXd, dw_gate=dWg, dw_up=dWu, dw_down=dWd)
+
+
+def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
+    """Adjoint sequence of the layer: combine-bwd (weighted dY dispatch) and the
+    route-weight gradient, expert backward, dispatch-bwd (sum of the K rows)."""
+    rows_cap = fwd["xd"].shape[0]
+    dyd = combine_bwd(dout, fwd["dst_rows"], fwd["topk_prob"], rows_cap, exact)
+    dp = dprob(dout, fwd["y"], fwd["dst_rows"])
+    eb = experts_bwd(dyd, fwd["xd"], fwd["g"], fwd["u"], fwd["h"], fwd["offsets"],
+                     w_gate, w_up, w_down, exact)
+    dx = dispatch_bwd(eb["dxd"], fwd["dst_rows"], exact)
+    eb.update(dyd=dyd, dprob=dp, dx=dx)
+    return eb
+
+
+# --------------------------------------------------------------------------
+# MXFP8: E4M3 elements with one E8M0 scale per 32    [KOSMOS 2.2; OLMo-A A.4, A.5]
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def floor_log2_f32(a) -> np.ndarray:
+    """floor(log2 a) for positive finite fp32 values, read from the bit fields."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = a.view(np.uint32)
+    ef = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+    man = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
+    E = ef - 127
+    sub = (ef == 0) & (man > 0)
+    if np.any(sub):
+        # subnormal: a = man * 2^-149; floor(log2 man) = bit length - 1
+        _, bl = np.frexp(man[sub].astype(np.float64))
+        E[sub] = -149 + (bl - 1)
+    return E
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """float64 -> OCP E4M3FN code: nearest-even on the 3-bit mantissa (subnormal
+    spacing 2^-9), magnitudes above 448 saturate to 448, sign kept (-0 -> 0x80)."""
+    y = np.asarray(y, dtype=np.float64)
+    neg = np.signbit(y)
+    a = np.abs(y)
+    _, ex = np.frexp(a)
+    E = np.maximum(ex - 1, -6)                  # binade; below 2^-6 spacing is 2^-9
+    q = np.ldexp(1.0, E - 3)
+    r = np.minimum(np.rint(a / q) * q, E4M3_MAX)
+    _, ex2 = np.frexp(r)
+    E2 = ex2 - 1
+    normal = r >= 2.0 ** -6
+    man_n = np.where(normal, r / np.ldexp(1.0, np.where(normal, E2, 0)) * 8 - 8, 0)
+    code_n = ((E2 + 7) << 3).astype(np.int64) + man_n.astype(np.int64)
+    code_s = np.rint(r / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    code = code | (neg.astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = c & 0x7
+    v = np.where(ef == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, ef - 7))
+    v = np.where((ef == 15) & (m == 7), np.nan, v)
+    return s * v
+
+
+def quantize_mxfp8(v, block: int = 32):
+    """Quantize along the last axis in blocks of 32 consecutive elements.
+
+    scale exponent e = clamp(floor(log2 amax) - 8, -127, 127), code e + 127
+    (amax = 0 gives code 0); q = E4M3(v * 2^-e).  Returns (q u8 [..., n],
+    scale u8 [..., n/32]).
+    """
+    v = values(v)
+    n = v.shape[-1]
+    if n % block:
+        raise ValueError("length not a multiple of the block")
+    blk = v.reshape(v.shape[:-1] + (n // block, block))
+    amax = np.abs(blk).max(axis=-1)
+    E = floor_log2_f32(np.where(amax > 0, amax, 1.0).astype(np.float32))
+    e = np.clip(E - 8, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    q = e4m3_encode(blk * np.ldexp(1.0, -e)[..., None])
+    return q.reshape(v.shape), (e + 127).astype(np.uint8)
+
+
+def dequantize_mxfp8(q, s, block: int = 32) -> np.ndarray:
+    q = np.asarray(q)
+    vals = e4m3_decode(q)
+    sc = np.ldexp(1.0, np.asarray(s, np.int64) - 127)
+    n = q.shape[-1]
+    return (vals.reshape(q.shape[:-1] + (n // block, block)) * sc[..., None]).reshape(q.shape)
+
+
+def mxfp8_gemm(aq, as_, bq, bs) -> np.ndarray:
+    """eq. 87 with C = 0: sum over k of (S_A a)(S_B b) in float64 -> bf16.
+    a: [M,K] row-quantized along K; b: [N,K] (output-major) quantized along K."""
+    return round_bf16(dequantize_mxfp8(aq, as_) @ dequantize_mxfp8(bq, bs).T)
+
+
+def dispatch_mxfp8(x, row_route, K: int):
+    """Quantize-on-dispatch: each token row quantized along D once, its bytes
+    and scales written to every row of its routes; other rows q = 0, s = 0."""
+    xq, xs = quantize_mxfp8(x)
+    rr = np.asarray(row_route, dtype=np.int64)
+    q = np.zeros((rr.shape[0], xq.shape[1]), np.uint8)
+    s = np.zeros((rr.shape[0], xs.shape[1]), np.uint8)
+    live = rr >= 0
+    q[live] = xq[rr[live] // K]
+    s[live] = xs[rr[live] // K]
+    return q, s
+
+
+def expert_mlp_mxfp8(xq, xs, wgq, wgs, wuq, wus, wdq, wds):
+    """GEMM1 on MXFP8 operands, bf16 G/U, H = bf16(silu(G)U) quantized along H,
+    GEMM2 on MXFP8 operands -> bf16 Y.  Returns (G, U, H, Hq, Hs, Y)."""
+    G = mxfp8_gemm(xq, xs, wgq, wgs)
+    U = mxfp8_gemm(xq, xs, wuq, wus)
+    Hh = swiglu(G, U)
+    hq, hs = quantize_mxfp8(Hh)
+    Y = mxfp8_gemm(hq, hs, wdq, wds)
+    return G, U, Hh, hq, hs, Y
+
+
+def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, rows_cap=None):
+    """MXFP8 forward: same route as bf16, groups padded to ``align`` rows,
+    quantize-on-dispatch, block-scaled expert GEMMs, bf16 weighted combine.
+
+    wq: dict with pre-quantized weights wg_q [E,H,D], wg_s [E,H,D/32], wu_q,
+    wu_s, wd_q [E,D,H], wd_s [E,D,H/32].
+    """
+    xv = values(x)
+    N, D = xv.shape
+    E = np.asarray(w_r).shape[0]
+    if rows_cap is None:
+        rows_cap = N * K + E * (align - 1)
+    L = router_logits(x, w_r, bias)
+    idx = topk_select(L, K)
+    prob = route_probs(L, idx, renorm)
+    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap)
+    xq, xs = dispatch_mxfp8(xv, row_route, K)
+    Hd = wq["wg_q"].shape[1]
+    G = np.zeros((rows_cap, Hd))
+    U = np.zeros((rows_cap, Hd))
+    Hh = np.zeros((rows_cap, Hd))
+    hq = np.zeros((rows_cap, Hd), np.uint8)
+    hs = np.zeros((rows_cap, Hd // 32), np.uint8)
+    Y = np.zeros((rows_cap, D))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        G[a:b], U[a:b], Hh[a:b], hq[a:b], hs[a:b], Y[a:b] = expert_mlp_mxfp8(
+            xq[a:b], xs[a:b], wq["wg_q"][e], wq["wg_s"][e], wq["wu_q"][e], wq["wu_s"][e],
+            wq["wd_q"][e], wq["wd_s"][e])
+    out = combine(Y, dst_rows, prob)
+    return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
+                dst_rows=dst_rows, row_route=row_route, xq=xq, xs=xs, g=G, u=U, h=Hh,
+                hq=hq, hs=hs, y=Y, out=out)
+
+
+def quantize_weights_mxfp8(w_gate, w_up, w_down):
+    """Pre-quantize the expert weights along their contraction dimension
+    (D for gate/up stored [E,H,D], H for down stored [E,D,H])."""
+    out = {}
+    for name, w in (("wg", w_gate), ("wu", w_up), ("wd", w_down)):
+        q = np.empty(np.asarray(w).shape, np.uint8)
+        s = np.empty(np.asarray(w).shape[:-1] + (np.asarray(w).shape[-1] // 32,), np.uint8)
+        for e in range(q.shape[0]):
+            q[e], s[e] = quantize_mxfp8(w[e])
+        out[name + "_q"], out[name + "_s"] = q, s
+    return out
