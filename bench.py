@@ -1,0 +1,362 @@
+"""Benchmark of one GPU's routed MoE expert layer on MI355X.
+
+One step = one forward pass of the whole layer over one batch of seeded
+synthetic input: router logits -> softmax/top-K/route map -> dispatch ->
+GEMM1 (gate/up, SwiGLU) -> GEMM2 (down) -> weighted combine.  The default
+workload is the DeepSeek-V3-shaped layer (N=4096 tokens, D=7168, E=256 experts,
+top-8, H=2048, Zipf(1.1) expert bias), bf16 with fp32 accumulation.  Inputs are
+resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0).  Usage:
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dsv3_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_synth as S  # noqa: E402
+
+METRIC = "MoE layer fwd tokens/s; grouped-GEMM TFLOP/s (% MFMA peak); dispatch GB/s"
+
+# MI355X published peaks (dense)
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_MXFP8_TFLOPS = 5000.0
+
+
+# ---------------------------------------------------------------------------
+# accounting (algorithmic work; OLMo-core Appendix A, A.8 eqs. 89-94 and
+# Table 43; routed FLOPs as in KOSMOS section 4.1.1)
+# ---------------------------------------------------------------------------
+
+def routed_flops(R, D, H, backward=False):
+    """Useful expert FLOPs: 6 R D H forward (eq. 92), 12 R D H backward."""
+    return (12 if backward else 6) * R * D * H
+
+
+def gemm1_work(R, D, H, E_act, b=2.0):
+    """GEMM1 with SwiGLU: F = 4RDH; bytes = X_d read + gate/up weights of the
+    active experts + G, U written (bf16) + H written (b bytes per element)."""
+    F = 4 * R * D * H
+    Q = b * R * D + b * 2 * E_act * D * H + 4 * R * H + b * R * H
+    return F, Q
+
+
+def gemm2_work(R, D, H, E_act, b=2.0):
+    F = 2 * R * D * H
+    Q = b * R * H + b * E_act * H * D + 2 * R * D
+    return F, Q
+
+
+def dispatch_bytes(N, D, K, R, b=2.0):
+    """Each token row read once and written to each of its valid routes."""
+    return 2 * N * D + b * R * D + 4 * N * K
+
+
+def combine_bytes(N, D, K, R):
+    return 2 * R * D + 8 * N * K + 2 * N * D
+
+
+def router_work(N, D, E):
+    return 2 * N * D * E, 2 * N * D + 2 * D * E + 4 * N * E
+
+
+def t_star(F, Q, peak_tflops, peak_gbs=PEAK_HBM_GBS):
+    """Roofline lower bound (eq. 89): max(F / C, Q / B) in seconds."""
+    return max(F / (peak_tflops * 1e12), Q / (peak_gbs * 1e9))
+
+
+def load_stats(counts, align=1):
+    """Expert-load statistics: I_max = the largest aligned expert load over the
+    mean rows per expert (OLMo-core Appendix A, A.9), active and empty
+    experts, the top-3 share of rows."""
+    c = np.asarray(counts, dtype=np.int64)
+    a = ((c + align - 1) // align) * align
+    tot = c.sum()
+    srt = np.sort(c)[::-1]
+    return dict(I_max=float(a.max() / (tot / len(c))) if tot else 0.0,
+                active=int((c > 0).sum()), empty=int((c == 0).sum()), max_rows=int(c.max()),
+                top3_share=float(srt[:3].sum() / max(1, c.sum())))
+
+
+# ---------------------------------------------------------------------------
+# the staged forward (same kernels as moe_layer_fwd, one C-ABI call per stage)
+# ---------------------------------------------------------------------------
+
+class StagedForward:
+    STAGES = ("router", "route", "dispatch", "gemm1", "gemm2", "combine")
+
+    def __init__(self, M, layer, x):
+        import torch
+        self.M, self.layer, self.x = M, layer, x
+        lib = M.load()
+        self.lib = lib
+        d = layer.d
+        sv = layer.saved
+        self.d = d
+        P = M._ptr
+        self.mx = layer.mxfp8
+        wts = layer.wts
+        rc = M.rows_cap(d)
+        self.ws_route = M.workspace(M.MOE_OP_ROUTE, d)
+        self.ws_gemm = M._gemm_ws(rc, d.E, x.device)
+        q = wts.wq or {}
+        dtype = M.MOE_MXFP8 if self.mx else M.MOE_BF16
+        if self.mx:
+            self.g1 = M.GemmFwdArgs(dtype, M.MOE_EPI_SWIGLU, d.E, rc, d.D, d.H, P(sv["offsets"]),
+                                    P(sv["xd_q"]), P(sv["xd_s"]), P(q["wg_q"]), P(q["wg_s"]),
+                                    P(q["wu_q"]), P(q["wu_s"]), P(sv["g"]), P(sv["u"]), P(sv["h"]),
+                                    P(sv["h_q"]), P(sv["h_s"]))
+            self.g2 = M.GemmFwdArgs(dtype, M.MOE_EPI_NONE, d.E, rc, d.H, d.D, P(sv["offsets"]),
+                                    P(sv["h_q"]), P(sv["h_s"]), P(q["wd_q"]), P(q["wd_s"]), None, None,
+                                    P(sv["y"]), None, None, None, None)
+        else:
+            self.g1 = M.GemmFwdArgs(dtype, M.MOE_EPI_SWIGLU, d.E, rc, d.D, d.H, P(sv["offsets"]),
+                                    P(sv["xd"]), None, P(wts.w_gate), None, P(wts.w_up), None,
+                                    P(sv["g"]), P(sv["u"]), P(sv["h"]), None, None)
+            self.g2 = M.GemmFwdArgs(dtype, M.MOE_EPI_NONE, d.E, rc, d.H, d.D, P(sv["offsets"]),
+                                    P(sv["h"]), None, P(wts.w_down), None, None, None, P(sv["y"]),
+                                    None, None, None, None)
+        self.ev = None
+
+    def run(self, events=None):
+        M, lib, d, sv, P = self.M, self.lib, self.d, self.layer.saved, self.M._ptr
+        s = M._stream()
+        chk = M._check
+        wts = self.layer.wts
+
+        def mark(i):
+            if events is not None:
+                events[i].record()
+
+        mark(0)
+        chk(lib.moe_router_logits(P(self.x), P(wts.w_r), P(wts.bias), C.byref(d), P(sv["logits"]), s),
+            "router")
+        mark(1)
+        chk(lib.moe_route(P(sv["logits"]), P(self.layer.drop), C.byref(d), P(sv["topk_idx"]),
+                          P(sv["topk_prob"]), P(sv["counts"]), P(sv["offsets"]), P(sv["dst_rows"]),
+                          P(sv["row_route"]), P(self.ws_route), self.ws_route.numel(), s), "route")
+        mark(2)
+        if self.mx:
+            chk(lib.moe_dispatch(P(self.x), P(sv["dst_rows"]), None, P(sv["counts"]), P(sv["offsets"]),
+                                 C.byref(d), M.MOE_MXFP8, P(sv["xd_q"]), P(sv["xd_s"]), s), "dispatch")
+        else:
+            chk(lib.moe_dispatch(P(self.x), P(sv["dst_rows"]), None, P(sv["counts"]), P(sv["offsets"]),
+                                 C.byref(d), M.MOE_BF16, P(sv["xd"]), None, s), "dispatch")
+        mark(3)
+        chk(lib.moe_grouped_gemm_fwd(C.byref(self.g1), P(self.ws_gemm), self.ws_gemm.numel(), s), "gemm1")
+        mark(4)
+        chk(lib.moe_grouped_gemm_fwd(C.byref(self.g2), P(self.ws_gemm), self.ws_gemm.numel(), s), "gemm2")
+        mark(5)
+        chk(lib.moe_combine(P(sv["y"]), P(sv["dst_rows"]), P(sv["topk_prob"]), C.byref(d),
+                            P(self.layer.out), s), "combine")
+        mark(6)
+
+
+def device_inputs(M, inp, mxfp8, torch):
+    def b(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).cuda()
+
+    w = M.LayerWeights(w_r=b(inp.w_r), bias=torch.from_numpy(inp.bias).cuda() if inp.bias is not None else None)
+    if mxfp8:
+        wg, wu, wd = b(inp.w_gate), b(inp.w_up), b(inp.w_down)
+        w.wq = M.quantize_weights_mxfp8(wg, wu, wd)
+        torch.cuda.synchronize()
+        del wg, wu, wd
+    else:
+        w.w_gate, w.w_up, w.w_down = b(inp.w_gate), b(inp.w_up), b(inp.w_down)
+    drop = torch.from_numpy(inp.drop).cuda() if inp.drop is not None else None
+    return b(inp.x), w, drop
+
+
+def cpu_baseline(inp, wl, budget_s=20.0):
+    """The oracle as it stands, on the first tokens of the same workload (a
+    bounded sample); returns tokens/s on the host cores."""
+    import oracle as O
+    n = 4
+    t_used = 0.0
+    res = None
+    while True:
+        t0 = time.perf_counter()
+        drop = inp.drop[:n] if inp.drop is not None else None
+        if wl.mxfp8:
+            wq = _sample_mxfp8_weights(O, inp, wl, n, drop)     # setup, not timed
+            t0 = time.perf_counter()
+            O.layer_fwd_mxfp8(inp.x[:n], inp.w_r, inp.bias, wq, wl.K, drop=drop)
+        else:
+            O.layer_fwd(inp.x[:n], inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K, drop=drop)
+        dt = time.perf_counter() - t0
+        res = (n, dt)
+        t_used += dt
+        if dt > budget_s / 4 or n >= wl.N or t_used > budget_s:
+            break
+        n = min(wl.N, n * 2)
+    n, dt = res
+    return dict(value=n / dt, unit="tokens/s", cores=_host_threads(), kind="oracle",
+                sample=f"first {n} of {wl.N} tokens of the same workload, full expert weights, "
+                       f"numpy float64 ({dt:.1f} s)")
+
+
+def _sample_mxfp8_weights(O, inp, wl, n, drop):
+    """Pre-quantized weights (the untimed setup step) for the experts the
+    sample routes to; the others stay zero and are never read."""
+    L = O.router_logits(inp.x[:n], inp.w_r, inp.bias)
+    idx = O.topk_select(L, wl.K)
+    used = np.unique(idx[O.route_valid(idx, drop, wl.E)])
+    E, H, D = wl.E, wl.H, wl.D
+    wq = dict(wg_q=np.zeros((E, H, D), np.uint8), wg_s=np.zeros((E, H, D // 32), np.uint8),
+              wu_q=np.zeros((E, H, D), np.uint8), wu_s=np.zeros((E, H, D // 32), np.uint8),
+              wd_q=np.zeros((E, D, H), np.uint8), wd_s=np.zeros((E, D, H // 32), np.uint8))
+    for e in used:
+        for name, w in (("wg", inp.w_gate), ("wu", inp.w_up), ("wd", inp.w_down)):
+            wq[name + "_q"][e], wq[name + "_s"][e] = O.quantize_mxfp8(w[e])
+    return wq
+
+
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        th = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if th:
+            return int(max(th))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_bf16", choices=sorted(S.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--layer-call", action="store_true", help="also time moe_layer_fwd as one call")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is a design note, not code); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_expert_router_amd as M
+
+    wl = S.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    inp = S.make_inputs(wl, args.seed)
+    x, w, drop = device_inputs(M, inp, wl.mxfp8, torch)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm)
+    st = StagedForward(M, layer, x)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"# setup {setup_s:.1f}s (inputs generated and resident)", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    nst = len(StagedForward.STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        st.run(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i, name in enumerate(StagedForward.STAGES)}
+    total_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(args.steps)]))
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][nst]) / args.steps
+
+    layer_ms = None
+    if args.layer_call:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            layer.forward(x)
+        e1.record()
+        torch.cuda.synchronize()
+        layer_ms = e0.elapsed_time(e1) / args.steps
+
+    counts = layer.saved["counts"].cpu().numpy()
+    stats = load_stats(counts, wl.align)
+    R = int(counts.sum())
+    E_act = stats["active"]
+    N, D, E, K, H = wl.N, wl.D, wl.E, wl.K, wl.H
+    b = (1 + 1 / 32) if wl.mxfp8 else 2.0
+    peak = PEAK_MXFP8_TFLOPS if wl.mxfp8 else PEAK_BF16_TFLOPS
+    F1, Q1 = gemm1_work(R, D, H, E_act, b)
+    F2, Q2 = gemm2_work(R, D, H, E_act, b)
+    t1 = stage_ms["gemm1"] / 1e3
+    t2 = stage_ms["gemm2"] / 1e3
+    bound1 = "hbm" if Q1 / (PEAK_HBM_GBS * 1e9) >= F1 / (peak * 1e12) else "mfma"
+    if bound1 == "hbm":
+        roof = dict(bound="hbm", achieved=Q1 / t1 / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=F1 / t1 / 1e12, peak=peak, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm1 (grouped gate/up GEMM with SwiGLU epilogue)"
+    roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
+
+    gemm_tflops = routed_flops(R, D, H) / (t1 + t2) / 1e12
+    qd = dispatch_bytes(N, D, K, R, b)
+    qc = combine_bytes(N, D, K, R)
+    tstar_layer = sum([t_star(*router_work(N, D, E), peak), qd / (PEAK_HBM_GBS * 1e9), t_star(F1, Q1, peak),
+                       t_star(F2, Q2, peak), qc / (PEAK_HBM_GBS * 1e9)])
+    out = {
+        "metric": METRIC,
+        "value": N / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3/bf16" if wl.mxfp8 else "bf16",
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {"workload": wl.name, "N": N, "D": D, "E": E, "K": K, "H": H, "zipf_s": wl.zipf_s,
+                   "p_drop": wl.p_drop, "align": wl.align, "seed": args.seed},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": gemm_tflops, "pct_mfma_peak": 100 * gemm_tflops / peak,
+                         "gemm1_ms": stage_ms["gemm1"], "gemm2_ms": stage_ms["gemm2"],
+                         "pct_of_roofline": 100 * (t_star(F1, Q1, peak) + t_star(F2, Q2, peak)) / (t1 + t2)},
+        "dispatch": {"gbs": qd / (stage_ms["dispatch"] / 1e3) / 1e9,
+                     "pct_hbm": 100 * qd / (stage_ms["dispatch"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "ms": stage_ms["dispatch"]},
+        "combine": {"gbs": qc / (stage_ms["combine"] / 1e3) / 1e9,
+                    "pct_hbm": 100 * qc / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                    "ms": stage_ms["combine"]},
+        "stage_ms": stage_ms,
+        "layer_pct_of_roofline": 100 * tstar_layer / (total_ms / 1e3),
+        "load": dict(stats, routes=R),
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+        "gpu_span_ms_per_step": gpu_ms,
+    }
+    if layer_ms is not None:
+        out["layer_call_ms"] = layer_ms
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

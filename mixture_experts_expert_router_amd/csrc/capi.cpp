@@ -1,0 +1,446 @@
+// C ABI of the MoE expert layer: argument checks, workspace carving and the
+// order of kernel launches.  Every call only enqueues work on the caller's
+// stream; nothing here synchronises or copies device data to the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "../../include/moe_rocm.h"
+#include "launch.h"
+
+namespace {
+
+std::atomic<int> g_last_hip_error{0};
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxK = 32;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error.store((int)e);
+  return MOE_ERR_HIP;
+}
+
+int64_t rows_cap_of(const moe_dims& d) { return d.N * d.K + d.E * (int64_t)(d.align - 1); }
+
+// shape rules shared by every entry point
+int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->N < 0 || d->E < 1 || d->E > kMaxE || d->K < 1 || d->K > d->E || d->K > kMaxK)
+    return MOE_ERR_SHAPE;
+  if (d->D <= 0 || d->D % 8) return MOE_ERR_SHAPE;
+  if (need_h && (d->H <= 0 || d->H % 8)) return MOE_ERR_SHAPE;
+  if (d->align != 1 && d->align != 32) return MOE_ERR_SHAPE;
+  if (mxfp8 && (d->D % 32 || (need_h && d->H % 32) || d->align != 32)) return MOE_ERR_SHAPE;
+  if (d->N * d->K >= (int64_t(1) << 31) || rows_cap_of(*d) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+#define REQUIRE(p)                          \
+  do {                                      \
+    if (!(p)) return MOE_ERR_NULL;          \
+    if (!aligned16(p)) return MOE_ERR_ALIGN; \
+  } while (0)
+#define OPTIONAL(p)                                \
+  do {                                             \
+    if ((p) && !aligned16(p)) return MOE_ERR_ALIGN; \
+  } while (0)
+// a buffer whose size is zero when `empty` holds may be NULL then
+#define REQUIRE_UNLESS(empty, p) \
+  do {                           \
+    if (empty) OPTIONAL(p);      \
+    else REQUIRE(p);             \
+  } while (0)
+
+size_t table_bytes(int64_t rows_cap, int64_t E) {
+  return round_up((size_t)moe::mtile_table_ints(rows_cap, E, 64) * 4, 256);
+}
+
+size_t route_bytes(const moe_dims& d) { return round_up(moe::route_workspace_bytes(d.N, d.E, d.K), 256); }
+
+size_t bwd_scratch_bytes(const moe_dims& d) {
+  const size_t rc = (size_t)rows_cap_of(d);
+  return 2 * round_up(rc * d.D * 2, 256) + 2 * round_up(rc * d.H * 2, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_rows_cap(const moe_dims* d) { return d ? rows_cap_of(*d) : -1; }
+
+size_t moe_workspace_size(int op, const moe_dims* d) {
+  if (!d) return 0;
+  const int64_t rc = rows_cap_of(*d);
+  switch (op) {
+    case MOE_OP_ROUTE: return route_bytes(*d);
+    case MOE_OP_GEMM: return table_bytes(rc, d->E);
+    case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, d->E);
+    case MOE_OP_LAYER_BWD: return table_bytes(rc, d->E) + bwd_scratch_bytes(*d);
+    default: return 0;
+  }
+}
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null argument";
+    case MOE_ERR_SHAPE: return "bad shape";
+    case MOE_ERR_DTYPE: return "bad dtype or epilogue";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error.load(); }
+
+int moe_router_logits(const void* x, const void* w_r, const float* bias, const moe_dims* d,
+                      float* logits, void* stream) {
+  int st = check_dims(d, false, false);
+  if (st) return st;
+  REQUIRE_UNLESS(d->N == 0, x);
+  REQUIRE(w_r);
+  REQUIRE_UNLESS(d->N == 0, logits);
+  OPTIONAL(bias);
+  return hip_status(moe::launch_router_logits(x, w_r, bias, d->N, d->D, d->E, logits, (hipStream_t)stream));
+}
+
+int moe_route(const float* logits, const uint8_t* drop, const moe_dims* d, int32_t* topk_idx,
+              float* topk_prob, int32_t* counts, int32_t* offsets, int32_t* dst_rows,
+              int32_t* row_route, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(d, false, false);
+  if (st) return st;
+  const bool no_tok = d->N == 0;
+  REQUIRE_UNLESS(no_tok, logits);
+  REQUIRE_UNLESS(no_tok, topk_idx);
+  REQUIRE_UNLESS(no_tok, topk_prob);
+  REQUIRE(counts);
+  REQUIRE(offsets);
+  REQUIRE_UNLESS(no_tok, dst_rows);
+  REQUIRE_UNLESS(rows_cap_of(*d) == 0, row_route);
+  REQUIRE(ws);
+  OPTIONAL(drop);
+  if (ws_bytes < route_bytes(*d)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(logits, drop, d->N, d->E, d->K, d->renorm, d->align,
+                                      rows_cap_of(*d), topk_idx, topk_prob, counts, offsets,
+                                      dst_rows, row_route, ws, (hipStream_t)stream));
+}
+
+int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, const int32_t* counts,
+                 const int32_t* offsets, const moe_dims* d, int out_dtype, void* xd,
+                 uint8_t* xd_scales, void* stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  const bool mx = out_dtype == MOE_MXFP8;
+  int st = check_dims(d, false, mx);
+  if (st) return st;
+  REQUIRE_UNLESS(d->N == 0, x);
+  REQUIRE_UNLESS(d->N == 0, dst_rows);
+  REQUIRE_UNLESS(rows_cap_of(*d) == 0, xd);
+  OPTIONAL(weight);
+  if (mx) {
+    REQUIRE_UNLESS(rows_cap_of(*d) == 0, xd_scales);
+    if (weight) return MOE_ERR_UNSUPPORTED;
+  }
+  if (d->align > 1) {
+    REQUIRE(counts);
+    REQUIRE(offsets);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (mx)
+    e = moe::launch_dispatch_mxfp8(x, dst_rows, d->N, d->D, d->K, (uint8_t*)xd, xd_scales, s);
+  else
+    e = moe::launch_dispatch_bf16(x, dst_rows, weight, d->N, d->D, d->K, xd, s);
+  if (e == hipSuccess && d->align > 1)
+    e = moe::launch_zero_padding(counts, offsets, d->E, mx ? d->D : d->D * 2, xd,
+                                 mx ? d->D / 32 : 0, mx ? xd_scales : nullptr, s);
+  return hip_status(e);
+}
+
+int moe_combine(const void* y, const int32_t* dst_rows, const float* weight, const moe_dims* d,
+                void* out, void* stream) {
+  int st = check_dims(d, false, false);
+  if (st) return st;
+  REQUIRE_UNLESS(d->N == 0, y);
+  REQUIRE_UNLESS(d->N == 0, dst_rows);
+  REQUIRE_UNLESS(d->N == 0, out);
+  OPTIONAL(weight);
+  return hip_status(moe::launch_combine(y, dst_rows, weight, d->N, d->D, d->K, out, (hipStream_t)stream));
+}
+
+int moe_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight, const void* y,
+                    const moe_dims* d, void* dyd, float* dprob, void* stream) {
+  int st = check_dims(d, false, false);
+  if (st) return st;
+  const bool no_tok = d->N == 0;
+  REQUIRE_UNLESS(no_tok, dout);
+  REQUIRE_UNLESS(no_tok, dst_rows);
+  REQUIRE_UNLESS(no_tok, weight);
+  REQUIRE_UNLESS(no_tok, dyd);
+  OPTIONAL(dprob);
+  if (dprob) REQUIRE_UNLESS(no_tok, y);
+  return hip_status(moe::launch_combine_bwd(dout, dst_rows, weight, y, d->N, d->D, d->K, dyd, dprob,
+                                            (hipStream_t)stream));
+}
+
+int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scales,
+                       void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || rows * cols >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  REQUIRE(src);
+  REQUIRE(q);
+  REQUIRE(scales);
+  return hip_status(moe::launch_quantize_rows(src, rows, cols, q, scales, (hipStream_t)stream));
+}
+
+int moe_swiglu(const void* g, const void* u, int64_t rows, int64_t n, int out_dtype, void* h,
+               uint8_t* h_q, uint8_t* h_scales, void* stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if (rows < 0 || n <= 0 || n % 8) return MOE_ERR_SHAPE;
+  REQUIRE(g);
+  REQUIRE(u);
+  if (out_dtype == MOE_MXFP8) {
+    if (n % 32) return MOE_ERR_SHAPE;
+    REQUIRE(h_q);
+    REQUIRE(h_scales);
+    OPTIONAL(h);
+  } else {
+    REQUIRE(h);
+    h_q = nullptr;
+    h_scales = nullptr;
+  }
+  return hip_status(moe::launch_swiglu(g, u, rows, n, h, h_q, h_scales, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_fwd(const moe_gemm_fwd_args* g, void* ws, size_t ws_bytes, void* stream) {
+  if (!g) return MOE_ERR_NULL;
+  if (g->dtype != MOE_BF16 && g->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if (g->epilogue != MOE_EPI_NONE && g->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_DTYPE;
+  const bool mx = g->dtype == MOE_MXFP8;
+  const bool sw = g->epilogue == MOE_EPI_SWIGLU;
+  const int64_t mult = mx ? 32 : 8;
+  if (g->E < 1 || g->E > kMaxE || g->rows_cap < 0 || g->rows_cap >= (int64_t(1) << 31) ||
+      g->k_dim <= 0 || g->n_dim <= 0 || g->k_dim % mult || g->n_dim % 8)
+    return MOE_ERR_SHAPE;
+  REQUIRE(g->offsets);
+  REQUIRE(g->a);
+  REQUIRE(g->b0);
+  REQUIRE(g->c0);
+  REQUIRE(ws);
+  if (mx) {
+    REQUIRE(g->a_scales);
+    REQUIRE(g->b0_scales);
+  }
+  if (sw) {
+    REQUIRE(g->b1);
+    REQUIRE(g->c1);
+    REQUIRE(g->act);
+    if (mx) REQUIRE(g->b1_scales);
+  }
+  OPTIONAL(g->act_q);
+  OPTIONAL(g->act_scales);
+  if ((g->act_q != nullptr) != (g->act_scales != nullptr)) return MOE_ERR_NULL;
+  if (g->act_q && (!sw || g->n_dim % 32)) return MOE_ERR_SHAPE;
+  if (ws_bytes < table_bytes(g->rows_cap, g->E)) return MOE_ERR_WORKSPACE;
+  moe::GemmFwd f{g->E, g->rows_cap, g->k_dim, g->n_dim, g->offsets, g->a, g->a_scales, g->b0,
+                 g->b0_scales, g->b1, g->b1_scales, g->c0, g->c1, g->act, g->act_q,
+                 g->act_scales, sw};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mx ? moe::launch_gemm_fwd_mxfp8(f, (int32_t*)ws, s)
+                    : moe::launch_gemm_fwd_bf16(f, (int32_t*)ws, s);
+  if (e == hipSuccess && !mx && g->act_q)
+    e = moe::launch_quantize_rows(g->act, g->rows_cap, g->n_dim, g->act_q, g->act_scales, s);
+  return hip_status(e);
+}
+
+int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, void* stream) {
+  if (!g) return MOE_ERR_NULL;
+  if (g->dtype != MOE_BF16) return g->dtype == MOE_MXFP8 ? MOE_ERR_UNSUPPORTED : MOE_ERR_DTYPE;
+  if (g->epilogue != MOE_EPI_NONE && g->epilogue != MOE_EPI_SWIGLU_BWD) return MOE_ERR_DTYPE;
+  const bool swb = g->epilogue == MOE_EPI_SWIGLU_BWD;
+  if (g->E < 1 || g->E > kMaxE || g->rows_cap < 0 || g->rows_cap >= (int64_t(1) << 31) ||
+      g->k_dim <= 0 || g->n_dim <= 0 || g->k_dim % 8 || g->n_dim % 8)
+    return MOE_ERR_SHAPE;
+  REQUIRE(g->offsets);
+  REQUIRE(g->dc0);
+  REQUIRE(ws);
+  OPTIONAL(g->dc1);
+  const bool want_dgrad = swb ? (g->dg != nullptr) : (g->da != nullptr);
+  const bool want_wgrad = g->db0 != nullptr || g->db1 != nullptr;
+  if (!want_dgrad && !want_wgrad) return MOE_ERR_NULL;
+  if (want_dgrad) {
+    REQUIRE(g->b0);
+    if (g->dc1) REQUIRE(g->b1);
+    if (swb) {
+      if (g->dc1) return MOE_ERR_UNSUPPORTED;
+      REQUIRE(g->g);
+      REQUIRE(g->u);
+      REQUIRE(g->dg);
+      REQUIRE(g->du);
+    } else {
+      REQUIRE(g->da);
+    }
+  }
+  if (want_wgrad) {
+    REQUIRE(g->a);
+    OPTIONAL(g->db0);
+    OPTIONAL(g->db1);
+    if (g->db1) REQUIRE(g->dc1);
+  }
+  if (ws_bytes < table_bytes(g->rows_cap, g->E)) return MOE_ERR_WORKSPACE;
+  moe::GemmBwd b{g->E, g->rows_cap, g->k_dim, g->n_dim, g->offsets, g->a, g->b0, g->b1,
+                 g->dc0, g->dc1, g->da, g->g, g->u, g->dg, g->du, swb};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (want_dgrad) e = moe::launch_gemm_dgrad_bf16(b, (int32_t*)ws, s);
+  if (e == hipSuccess && g->db0) e = moe::launch_gemm_wgrad_bf16(b, g->dc0, g->db0, s);
+  if (e == hipSuccess && g->db1) e = moe::launch_gemm_wgrad_bf16(b, g->dc1, g->db1, s);
+  return hip_status(e);
+}
+
+int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!a || !sv) return MOE_ERR_NULL;
+  if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  const bool mx = a->dtype == MOE_MXFP8;
+  const moe_dims& d = a->dims;
+  int st = check_dims(&d, true, mx);
+  if (st) return st;
+  REQUIRE(a->x);
+  REQUIRE(a->w_r);
+  OPTIONAL(a->bias);
+  OPTIONAL(a->drop);
+  REQUIRE(out);
+  REQUIRE(ws);
+  REQUIRE(sv->logits);
+  REQUIRE(sv->topk_idx);
+  REQUIRE(sv->topk_prob);
+  REQUIRE(sv->counts);
+  REQUIRE(sv->offsets);
+  REQUIRE(sv->dst_rows);
+  REQUIRE(sv->row_route);
+  REQUIRE(sv->g);
+  REQUIRE(sv->u);
+  REQUIRE(sv->h);
+  REQUIRE(sv->y);
+  if (mx) {
+    REQUIRE(a->wg_q);
+    REQUIRE(a->wg_s);
+    REQUIRE(a->wu_q);
+    REQUIRE(a->wu_s);
+    REQUIRE(a->wd_q);
+    REQUIRE(a->wd_s);
+    REQUIRE(sv->xd_q);
+    REQUIRE(sv->xd_s);
+    REQUIRE(sv->h_q);
+    REQUIRE(sv->h_s);
+  } else {
+    REQUIRE(a->w_gate);
+    REQUIRE(a->w_up);
+    REQUIRE(a->w_down);
+    REQUIRE(sv->xd);
+  }
+  const int64_t rc = rows_cap_of(d);
+  const size_t rb = route_bytes(d);
+  if (ws_bytes < rb + table_bytes(rc, d.E)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws_route = ws;
+  int32_t* table = (int32_t*)((char*)ws + rb);
+
+  hipError_t e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, s);
+  if (e == hipSuccess)
+    e = moe::launch_route(sv->logits, a->drop, d.N, d.E, d.K, d.renorm, d.align, rc, sv->topk_idx,
+                          sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,
+                          ws_route, s);
+  if (mx) {
+    if (e == hipSuccess) e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s);
+    if (e == hipSuccess)
+      e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D, sv->xd_q, d.D / 32, sv->xd_s, s);
+    moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
+                    a->wu_s, sv->g, sv->u, sv->h, sv->h_q, sv->h_s, true};
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_mxfp8(g1, table, s);
+    moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
+                    nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_mxfp8(g2, table, s);
+  } else {
+    if (e == hipSuccess) e = moe::launch_dispatch_bf16(a->x, sv->dst_rows, nullptr, d.N, d.D, d.K, sv->xd, s);
+    if (e == hipSuccess && d.align > 1)
+      e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, sv->xd, 0, nullptr, s);
+    moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd, nullptr, a->w_gate, nullptr, a->w_up,
+                    nullptr, sv->g, sv->u, sv->h, nullptr, nullptr, true};
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_bf16(g1, table, s);
+    moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h, nullptr, a->w_down, nullptr, nullptr,
+                    nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_bf16(g2, table, s);
+  }
+  if (e == hipSuccess) e = moe::launch_combine(sv->y, sv->dst_rows, sv->topk_prob, d.N, d.D, d.K, out, s);
+  return hip_status(e);
+}
+
+int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void* dout,
+                  moe_layer_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  if (!a || !sv || !gr) return MOE_ERR_NULL;
+  if (a->dtype != MOE_BF16) return a->dtype == MOE_MXFP8 ? MOE_ERR_UNSUPPORTED : MOE_ERR_DTYPE;
+  const moe_dims& d = a->dims;
+  int st = check_dims(&d, true, false);
+  if (st) return st;
+  REQUIRE(a->w_gate);
+  REQUIRE(a->w_up);
+  REQUIRE(a->w_down);
+  REQUIRE(dout);
+  REQUIRE(ws);
+  REQUIRE(sv->topk_prob);
+  REQUIRE(sv->counts);
+  REQUIRE(sv->offsets);
+  REQUIRE(sv->dst_rows);
+  REQUIRE(sv->xd);
+  REQUIRE(sv->g);
+  REQUIRE(sv->u);
+  REQUIRE(sv->h);
+  REQUIRE(sv->y);
+  REQUIRE(gr->dx);
+  REQUIRE(gr->dprob);
+  REQUIRE(gr->dw_gate);
+  REQUIRE(gr->dw_up);
+  REQUIRE(gr->dw_down);
+  const int64_t rc = rows_cap_of(d);
+  const size_t tb = table_bytes(rc, d.E);
+  if (ws_bytes < tb + bwd_scratch_bytes(d)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* p = (char*)ws;
+  int32_t* table = (int32_t*)p;
+  p += tb;
+  void* dyd = p;
+  p += round_up((size_t)rc * d.D * 2, 256);
+  void* dxd = p;
+  p += round_up((size_t)rc * d.D * 2, 256);
+  void* dg = p;
+  p += round_up((size_t)rc * d.H * 2, 256);
+  void* du = p;
+
+  hipError_t e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd,
+                                         gr->dprob, s);
+  if (e == hipSuccess && d.align > 1)
+    e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, dyd, 0, nullptr, s);
+  // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
+  moe::GemmBwd down{d.E, rc, d.H, d.D, sv->offsets, sv->h, a->w_down, nullptr, dyd, nullptr, nullptr,
+                    sv->g, sv->u, dg, du, true};
+  if (e == hipSuccess) e = moe::launch_gemm_dgrad_bf16(down, table, s);
+  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(down, dyd, gr->dw_down, s);
+  // gate/up: forward g = xd . w_gate^T, u = xd . w_up^T  (k_dim = D, n_dim = H)
+  moe::GemmBwd gu{d.E, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
+                  nullptr, nullptr, nullptr, nullptr, false};
+  if (e == hipSuccess) e = moe::launch_gemm_dgrad_bf16(gu, table, s);
+  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(gu, dg, gr->dw_gate, s);
+  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(gu, du, gr->dw_up, s);
+  if (e == hipSuccess) e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

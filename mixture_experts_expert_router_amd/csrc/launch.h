@@ -1,0 +1,84 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// forward grouped GEMM request (bf16 or MXFP8)
+struct GemmFwd {
+  int64_t E, rows_cap, k_dim, n_dim;
+  const int32_t* offsets;
+  const void* a;
+  const uint8_t* a_scales;
+  const void* b0;
+  const uint8_t* b0_scales;
+  const void* b1;
+  const uint8_t* b1_scales;
+  void* c0;
+  void* c1;
+  void* act;
+  uint8_t* act_q;
+  uint8_t* act_scales;
+  bool swiglu;
+};
+
+// backward grouped GEMM request (bf16)
+struct GemmBwd {
+  int64_t E, rows_cap, k_dim, n_dim;
+  const int32_t* offsets;
+  const void* a;
+  const void* b0;
+  const void* b1;
+  const void* dc0;
+  const void* dc1;
+  void* da;
+  const void* g;
+  const void* u;
+  void* dg;
+  void* du;
+  bool swiglu_bwd;
+};
+
+// router.hip
+hipError_t launch_router_logits(const void* x, const void* w_r, const float* bias, int64_t N,
+                                int64_t D, int64_t E, float* logits, hipStream_t s);
+
+// route.hip
+size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K);
+hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int64_t E, int64_t K,
+                        int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
+                        int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
+                        void* ws, hipStream_t s);
+
+// permute.hip
+hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,
+                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s);
+hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
+                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s);
+hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
+                               int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
+                               hipStream_t s);
+hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
+                          int64_t D, int64_t K, void* out, hipStream_t s);
+hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
+                              const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
+                              float* dprob, hipStream_t s);
+hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
+                                uint8_t* sc, hipStream_t s);
+hipError_t launch_swiglu(const void* g, const void* u, int64_t rows, int64_t n, void* h,
+                         uint8_t* hq, uint8_t* hs, hipStream_t s);
+
+// gemm_bf16.hip
+int64_t mtile_table_ints(int64_t rows_cap, int64_t E, int BM);
+hipError_t launch_build_mtiles(const int32_t* offsets, int64_t E, int BM, int32_t* table, hipStream_t s);
+hipError_t launch_gemm_fwd_bf16(const GemmFwd& f, int32_t* table, hipStream_t s);
+hipError_t launch_gemm_dgrad_bf16(const GemmBwd& b, int32_t* table, hipStream_t s);
+hipError_t launch_gemm_wgrad_bf16(const GemmBwd& b, const void* dc, void* db, hipStream_t s);
+
+// gemm_mxfp8.hip
+hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);
+
+}  // namespace moe

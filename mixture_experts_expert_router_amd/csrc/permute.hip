@@ -1,0 +1,385 @@
+// Row permutes of the MoE layer over local HBM: dispatch into expert-
+// contiguous rows, the weighted fold (combine), the combine backward with the
+// route-weight gradient, and the MXFP8 row quantizer (OLMo-core Appendix A,
+// A.1-A.4; KOSMOS section 3.3.1 steps 3 and 5, section 3.3.2 step 1).
+//
+// All of them move whole rows with 16-byte vectors, one wave per token row,
+// several vectors in flight per lane.  Dispatch reads each token row once and
+// writes it K times (scatter form), so x crosses HBM once.  Combine gathers the
+// K rows of a token and folds them in fp32 in ascending k with fmaf.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kVPL = 8;   // 16-byte vectors per lane per pass
+
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
+  uint4 o;
+  o.x = pack_bf16x2(w * bf16lo(v.x), w * bf16hi(v.x));
+  o.y = pack_bf16x2(w * bf16lo(v.y), w * bf16hi(v.y));
+  o.z = pack_bf16x2(w * bf16lo(v.z), w * bf16hi(v.z));
+  o.w = pack_bf16x2(w * bf16lo(v.w), w * bf16hi(v.w));
+  return o;
+}
+
+// dispatch (bf16): one wave per token; WEIGHTED multiplies by the route weight
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __restrict__ x,
+                                                            const int32_t* __restrict__ dst_rows,
+                                                            const float* __restrict__ weight,
+                                                            int N, int D, int K,
+                                                            uint16_t* __restrict__ xd) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  int dst[32];
+  float w[32];
+  for (int k = 0; k < K; ++k) {
+    dst[k] = dst_rows[(int64_t)t * K + k];
+    w[k] = WEIGHTED ? weight[(int64_t)t * K + k] : 1.0f;
+  }
+  const int nvec = D >> 3;
+  const uint16_t* src = x + (int64_t)t * D;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
+    uint4 r[kVPL];
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      if (v < nvec) r[j] = ldg16(src + v * 8);
+    }
+    for (int k = 0; k < K; ++k) {
+      if (dst[k] < 0) continue;
+      uint16_t* out = xd + (int64_t)dst[k] * D;
+#pragma unroll
+      for (int j = 0; j < kVPL; ++j) {
+        const int v = v0 + lane + j * kWave;
+        if (v < nvec) stg16(out + v * 8, WEIGHTED ? scale_bf16x8(r[j], w[k]) : r[j]);
+      }
+    }
+  }
+}
+
+// MXFP8 quantization of one 16-byte vector (8 bf16 values); lanes 4j..4j+3 of
+// a wave hold one 32-element block.  Returns the 8 E4M3 bytes and the scale.
+__device__ __forceinline__ uint2 quant_vec(uint4 v, int& code_out) {
+  float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int code = e8m0_code(amax);
+  const int e = code - 127;
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = e4m3_from_scaled(f[i], e);
+  code_out = code;
+  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+}
+
+// dispatch (MXFP8): quantize each token row once along D, write q and scales
+// to its K rows.  D is a multiple of 32, so 4 consecutive lanes own a block
+// and every wave-wide pass covers whole blocks.
+__global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __restrict__ x,
+                                                             const int32_t* __restrict__ dst_rows,
+                                                             int N, int D, int K,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  int dst[32];
+  for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
+  const int nvec = D >> 3;
+  const uint16_t* src = x + (int64_t)t * D;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
+    uint2 qv[kVPL];
+    int code[kVPL];
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (v < nvec) r = ldg16(src + v * 8);
+      qv[j] = quant_vec(r, code[j]);     // all lanes take part in the shuffles
+    }
+    for (int k = 0; k < K; ++k) {
+      if (dst[k] < 0) continue;
+#pragma unroll
+      for (int j = 0; j < kVPL; ++j) {
+        const int v = v0 + lane + j * kWave;
+        if (v < nvec) {
+          *reinterpret_cast<uint2*>(q + (int64_t)dst[k] * D + v * 8) = qv[j];
+          if ((v & 3) == 0) sc[(int64_t)dst[k] * (D >> 5) + (v >> 2)] = (uint8_t)code[j];
+        }
+      }
+    }
+  }
+}
+
+// zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert
+__global__ __launch_bounds__(256) void zero_padding_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int64_t row_bytes, uint8_t* __restrict__ a,
+                                                           int64_t row_bytes2,
+                                                           uint8_t* __restrict__ b) {
+  const int e = blockIdx.x;
+  const int64_t r0 = offsets[e] + counts[e];
+  const int64_t r1 = offsets[e + 1];
+  for (int64_t r = r0; r < r1; ++r) {
+    uint4* pa = reinterpret_cast<uint4*>(a + r * row_bytes);
+    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) pa[i] = make_uint4(0, 0, 0, 0);
+    if (b) {
+      uint8_t* pb = b + r * row_bytes2;
+      for (int64_t i = threadIdx.x; i < row_bytes2; i += blockDim.x) pb[i] = 0;
+    }
+  }
+}
+
+// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), fp32 fmaf in ascending k
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ dst_rows,
+                                                      const float* __restrict__ weight, int N,
+                                                      int D, int K, uint16_t* __restrict__ out) {
+  constexpr int VPL = 2;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  int dst[32];
+  float w[32];
+  for (int k = 0; k < K; ++k) {
+    dst[k] = dst_rows[(int64_t)t * K + k];
+    w[k] = WEIGHTED ? weight[(int64_t)t * K + k] : 1.0f;
+  }
+  const int nvec = D >> 3;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+    float acc[VPL][8];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      if (dst[k] < 0) continue;
+      const uint16_t* src = y + (int64_t)dst[k] * D;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + lane + j * kWave;
+        if (v < nvec) {
+          uint4 r = ldg16(src + v * 8);
+          const float wk = w[k];
+          acc[j][0] = fmaf(wk, bf16lo(r.x), acc[j][0]);
+          acc[j][1] = fmaf(wk, bf16hi(r.x), acc[j][1]);
+          acc[j][2] = fmaf(wk, bf16lo(r.y), acc[j][2]);
+          acc[j][3] = fmaf(wk, bf16hi(r.y), acc[j][3]);
+          acc[j][4] = fmaf(wk, bf16lo(r.z), acc[j][4]);
+          acc[j][5] = fmaf(wk, bf16hi(r.z), acc[j][5]);
+          acc[j][6] = fmaf(wk, bf16lo(r.w), acc[j][6]);
+          acc[j][7] = fmaf(wk, bf16hi(r.w), acc[j][7]);
+        }
+      }
+    }
+    uint16_t* o = out + (int64_t)t * D;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      if (v < nvec)
+        stg16(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
+                                    pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
+    }
+  }
+}
+
+// combine backward: dyd[dst] = bf16(w * dout[t]); dprob[t,k] = <dout[t], y[dst]>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dout,
+                                                          const int32_t* __restrict__ dst_rows,
+                                                          const float* __restrict__ weight,
+                                                          const uint16_t* __restrict__ y, int N,
+                                                          int D, int K, uint16_t* __restrict__ dyd,
+                                                          float* __restrict__ dprob) {
+  constexpr int VPL = 4;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  int dst[32];
+  float w[32], dot[32];
+  for (int k = 0; k < K; ++k) {
+    dst[k] = dst_rows[(int64_t)t * K + k];
+    w[k] = weight[(int64_t)t * K + k];
+    dot[k] = 0.0f;
+  }
+  const int nvec = D >> 3;
+  const uint16_t* src = dout + (int64_t)t * D;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+    uint4 r[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      if (v < nvec) r[j] = ldg16(src + v * 8);
+    }
+    for (int k = 0; k < K; ++k) {
+      if (dst[k] < 0) continue;
+      uint16_t* o = dyd + (int64_t)dst[k] * D;
+      const uint16_t* yr = y + (int64_t)dst[k] * D;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + lane + j * kWave;
+        if (v < nvec) {
+          stg16(o + v * 8, scale_bf16x8(r[j], w[k]));
+          if (dprob) {
+            uint4 yy = ldg16(yr + v * 8);
+            float s = dot[k];
+            s = fmaf(bf16lo(r[j].x), bf16lo(yy.x), s);
+            s = fmaf(bf16hi(r[j].x), bf16hi(yy.x), s);
+            s = fmaf(bf16lo(r[j].y), bf16lo(yy.y), s);
+            s = fmaf(bf16hi(r[j].y), bf16hi(yy.y), s);
+            s = fmaf(bf16lo(r[j].z), bf16lo(yy.z), s);
+            s = fmaf(bf16hi(r[j].z), bf16hi(yy.z), s);
+            s = fmaf(bf16lo(r[j].w), bf16lo(yy.w), s);
+            s = fmaf(bf16hi(r[j].w), bf16hi(yy.w), s);
+            dot[k] = s;
+          }
+        }
+      }
+    }
+  }
+  if (dprob) {
+    for (int k = 0; k < K; ++k) {
+      float s = wave_sum(dot[k]);
+      if (lane == 0) dprob[(int64_t)t * K + k] = dst[k] >= 0 ? s : 0.0f;
+    }
+  }
+}
+
+// row-wise MXFP8 quantization of bf16 [rows][cols]; one wave per row
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ src,
+                                                            int64_t rows, int cols,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nvec = cols >> 3;
+  const uint16_t* s = src + r * cols;
+  for (int v0 = 0; v0 < nvec; v0 += kWave) {
+    const int v = v0 + lane;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (v < nvec) x = ldg16(s + v * 8);
+    int code;
+    uint2 qq = quant_vec(x, code);
+    if (v < nvec) {
+      *reinterpret_cast<uint2*>(q + r * cols + v * 8) = qq;
+      if ((v & 3) == 0) sc[r * (cols >> 5) + (v >> 2)] = (uint8_t)code;
+    }
+  }
+}
+
+// h = bf16(silu(g) * u), optionally quantized row-wise; one wave per row
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ g,
+                                                     const uint16_t* __restrict__ u, int64_t rows,
+                                                     int n, uint16_t* __restrict__ h,
+                                                     uint8_t* __restrict__ hq,
+                                                     uint8_t* __restrict__ hs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nvec = n >> 3;
+  for (int v0 = 0; v0 < nvec; v0 += kWave) {
+    const int v = v0 + lane;
+    uint4 out = make_uint4(0, 0, 0, 0);
+    if (v < nvec) {
+      uint4 a = ldg16(g + r * n + v * 8), b = ldg16(u + r * n + v * 8);
+      uint32_t ga[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w}, o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float g0 = bf16lo(ga[i]), g1 = bf16hi(ga[i]);
+        float h0 = g0 * sigmoidf_(g0) * bf16lo(ub[i]);
+        float h1 = g1 * sigmoidf_(g1) * bf16hi(ub[i]);
+        o[i] = pack_bf16x2(h0, h1);
+      }
+      out = make_uint4(o[0], o[1], o[2], o[3]);
+      if (h) stg16(h + r * n + v * 8, out);
+    }
+    if (hq) {
+      int code;
+      uint2 qq = quant_vec(out, code);
+      if (v < nvec) {
+        *reinterpret_cast<uint2*>(hq + r * n + v * 8) = qq;
+        if ((v & 3) == 0) hs[r * (n >> 5) + (v >> 2)] = (uint8_t)code;
+      }
+    }
+  }
+}
+
+// ---- host launchers -----------------------------------------------------------
+static inline unsigned waves_grid(int64_t rows) { return (unsigned)((rows + 3) / 4); }
+
+hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,
+                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (weight)
+    dispatch_bf16_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, weight,
+                                                            (int)N, (int)D, (int)K, (uint16_t*)xd);
+  else
+    dispatch_bf16_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, nullptr,
+                                                             (int)N, (int)D, (int)K, (uint16_t*)xd);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
+                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  dispatch_mxfp8_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
+                                                      (int)K, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
+                               int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
+                               hipStream_t s) {
+  if (E == 0) return hipSuccess;
+  zero_padding_kernel<<<(unsigned)E, 256, 0, s>>>(counts, offsets, row_bytes, (uint8_t*)a,
+                                                   row_bytes2, (uint8_t*)b);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
+                          int64_t D, int64_t K, void* out, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (weight)
+    combine_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, weight, (int)N,
+                                                      (int)D, (int)K, (uint16_t*)out);
+  else
+    combine_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, nullptr,
+                                                       (int)N, (int)D, (int)K, (uint16_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
+                              const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
+                              float* dprob, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  combine_bwd_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)dout, dst_rows, weight,
+                                                   (const uint16_t*)y, (int)N, (int)D, (int)K,
+                                                   (uint16_t*)dyd, dprob);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
+                                uint8_t* sc, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  quantize_rows_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* g, const void* u, int64_t rows, int64_t n, void* h,
+                         uint8_t* hq, uint8_t* hs, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  swiglu_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)g, (const uint16_t*)u, rows, (int)n,
+                                                 (uint16_t*)h, hq, hs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -319,6 +319,56 @@ def experts_fwd(xd, offsets, w_gate, w_up, w_down, exact: bool = False):
 
 
 # --------------------------------------------------------------------------
+# grouped products on their own (the building blocks of the expert GEMMs)
+# --------------------------------------------------------------------------
+
+
+def grouped_gemm(a, w, offsets, exact: bool = False):
+    """c[i] = a[i] . w[e]^T for the rows i of expert e's segment; w: [E, n, k]
+    (output-major).  Rows outside every segment are 0."""
+    av = values(a)
+    E = len(offsets) - 1
+    n = np.asarray(w).shape[1]
+    c = np.zeros((av.shape[0], n))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            c[lo:hi] = av[lo:hi] @ values(w[e]).T
+    return _rounder(exact)(c)
+
+
+def grouped_dgrad(dc, w, offsets, dc1=None, w1=None, exact: bool = False):
+    """da[i] = dc[i] . w[e] (+ dc1[i] . w1[e], one sum): the gradient of
+    grouped_gemm with respect to a."""
+    dv = values(dc)
+    E = len(offsets) - 1
+    k = np.asarray(w).shape[2]
+    out = np.zeros((dv.shape[0], k))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            acc = dv[lo:hi] @ values(w[e])
+            if dc1 is not None:
+                acc = acc + values(dc1)[lo:hi] @ values(w1[e])
+            out[lo:hi] = acc
+    return _rounder(exact)(out)
+
+
+def grouped_wgrad(dc, a, offsets, exact: bool = False):
+    """dw[e] = sum over rows i of e of dc[i]^T a[i]: the gradient of grouped_gemm
+    with respect to w, shape [E, n, k]; experts without rows get 0."""
+    dv = values(dc)
+    av = values(a)
+    E = len(offsets) - 1
+    out = np.zeros((E, dv.shape[1], av.shape[1]))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[e] = dv[lo:hi].T @ av[lo:hi]
+    return _rounder(exact)(out)
+
+
+# --------------------------------------------------------------------------
 # whole layer, forward       [KOSMOS 3.3.1; OLMo-A A.1 fused node, A.14 saved set]
 # --------------------------------------------------------------------------
 

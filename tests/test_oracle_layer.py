@@ -196,3 +196,26 @@ def test_swiglu_backward_closed_form():
                         np.zeros((1, 8, 8)), np.zeros((1, 8, 8)), eye, exact=True)
     assert np.allclose(res["dg"].reshape(-1), g.grad.numpy(), rtol=1e-12, atol=1e-14)
     assert np.allclose(res["du"].reshape(-1), u.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_grouped_products_are_the_layer_parts():
+    """The stand-alone grouped products equal the corresponding pieces of the
+    expert forward and backward."""
+    wl = _small(N=24, D=32, E=4, K=2, H=48, bwd=True)
+    inp = S.make_inputs(wl, 9)
+    f = O.layer_fwd(inp.x, inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K)
+    o = f["offsets"]
+    assert np.array_equal(O.grouped_gemm(f["xd"], inp.w_gate, o), f["g"])
+    assert np.array_equal(O.grouped_gemm(f["h"], inp.w_down, o), f["y"])
+    b = O.layer_bwd(f, inp.dout, inp.w_gate, inp.w_up, inp.w_down)
+    assert np.array_equal(O.grouped_dgrad(b["dg"], inp.w_gate, o, b["du"], inp.w_up), b["dxd"])
+    assert np.array_equal(O.grouped_wgrad(b["dyd"], f["h"], o), b["dw_down"])
+    assert np.array_equal(O.grouped_wgrad(b["dg"], f["xd"], o), b["dw_gate"])
+    # dgrad/wgrad are the adjoints of the forward product (dot-product test)
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((f["xd"].shape[0], 32))
+    W = rng.standard_normal((4, 48, 32))
+    Z = rng.standard_normal((A.shape[0], 48))
+    lhs = np.sum(O.grouped_gemm(A, W, o, exact=True) * Z)
+    assert np.isclose(lhs, np.sum(A * O.grouped_dgrad(Z, W, o, exact=True)), rtol=1e-12)
+    assert np.isclose(lhs, np.sum(W * O.grouped_wgrad(Z, A, o, exact=True)), rtol=1e-12)
