@@ -245,6 +245,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--layer-call", action="store_true", help="also time moe_layer_fwd as one call")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
+                         "that calibrates the HBM byte counters of a profiler run")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -265,6 +268,16 @@ def main(argv=None):
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"# setup {setup_s:.1f}s (inputs generated and resident)", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         st.run()

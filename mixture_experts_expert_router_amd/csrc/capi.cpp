@@ -57,7 +57,15 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
   } while (0)
 
 size_t table_bytes(int64_t rows_cap, int64_t E) {
-  return round_up((size_t)moe::mtile_table_ints(rows_cap, E, 64) * 4, 256);
+  const size_t a = (size_t)moe::mtile_table_ints(rows_cap, E, 64) * 4;
+  const size_t b = (16 + moe::gemm_fwd_plan_ints(E)) * 4;
+  return round_up(a > b ? a : b, 256);
+}
+
+// bf16 forward GEMM: the persistent kernel where its shape rule holds
+hipError_t gemm_fwd_bf16(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
+  if (moe::gemm_fwd_fast_ok(f.k_dim, f.n_dim)) return moe::launch_gemm_fwd_fast(f, ws, s);
+  return moe::launch_gemm_fwd_bf16(f, ws, s);
 }
 
 size_t route_bytes(const moe_dims& d) { return round_up(moe::route_workspace_bytes(d.N, d.E, d.K), 256); }
@@ -253,7 +261,7 @@ int moe_grouped_gemm_fwd(const moe_gemm_fwd_args* g, void* ws, size_t ws_bytes, 
                  g->act_scales, sw};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mx ? moe::launch_gemm_fwd_mxfp8(f, (int32_t*)ws, s)
-                    : moe::launch_gemm_fwd_bf16(f, (int32_t*)ws, s);
+                    : gemm_fwd_bf16(f, (int32_t*)ws, s);
   if (e == hipSuccess && !mx && g->act_q)
     e = moe::launch_quantize_rows(g->act, g->rows_cap, g->n_dim, g->act_q, g->act_scales, s);
   return hip_status(e);
@@ -374,10 +382,10 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
       e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, sv->xd, 0, nullptr, s);
     moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd, nullptr, a->w_gate, nullptr, a->w_up,
                     nullptr, sv->g, sv->u, sv->h, nullptr, nullptr, true};
-    if (e == hipSuccess) e = moe::launch_gemm_fwd_bf16(g1, table, s);
+    if (e == hipSuccess) e = gemm_fwd_bf16(g1, table, s);
     moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h, nullptr, a->w_down, nullptr, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
-    if (e == hipSuccess) e = moe::launch_gemm_fwd_bf16(g2, table, s);
+    if (e == hipSuccess) e = gemm_fwd_bf16(g2, table, s);
   }
   if (e == hipSuccess) e = moe::launch_combine(sv->y, sv->dst_rows, sv->topk_prob, d.N, d.D, d.K, out, s);
   return hip_status(e);

@@ -78,6 +78,11 @@ hipError_t launch_gemm_fwd_bf16(const GemmFwd& f, int32_t* table, hipStream_t s)
 hipError_t launch_gemm_dgrad_bf16(const GemmBwd& b, int32_t* table, hipStream_t s);
 hipError_t launch_gemm_wgrad_bf16(const GemmBwd& b, const void* dc, void* db, hipStream_t s);
 
+// gemm_fwd.hip (persistent bf16 forward; k_dim % 64 == 0, n_dim % 16 == 0)
+size_t gemm_fwd_plan_ints(int64_t E);
+bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim);
+hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s);
+
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);
 

@@ -235,6 +235,13 @@ GEMM_CASES = [
     ((17,), 64, 8, 3),
     ((0, 0, 5), 8, 128, 0),
     ((129, 0, 64, 1, 255, 128), 384, 264, 40),
+    # shapes the persistent kernel takes (k % 64 == 0, n % 16 == 0), one per
+    # row-block rule (64 / 128 / 256 rows), partial n-tiles and empty experts
+    ((0, 1, 130, 64, 257), 192, 144, 8),
+    ((1000, 0, 777, 1), 128, 272, 0),
+    ((2000, 1700), 128, 160, 0),
+    ((5000,), 64, 512, 3),
+    ((3, 0, 0, 90, 0, 17, 0, 0, 200, 1, 0, 64, 0, 0, 0, 33), 320, 96, 0),
 ]
 
 
