@@ -110,6 +110,7 @@ class StagedForward:
         wts = layer.wts
         rc = M.rows_cap(d)
         self.ws_route = M.workspace(M.MOE_OP_ROUTE, d)
+        self.ws_router = M.workspace(M.MOE_OP_ROUTER, d)
         self.ws_gemm = M._gemm_ws(rc, d.E, x.device)
         q = wts.wq or {}
         dtype = M.MOE_MXFP8 if self.mx else M.MOE_BF16
@@ -141,8 +142,8 @@ class StagedForward:
                 events[i].record()
 
         mark(0)
-        chk(lib.moe_router_logits(P(self.x), P(wts.w_r), P(wts.bias), C.byref(d), P(sv["logits"]), s),
-            "router")
+        chk(lib.moe_router_logits(P(self.x), P(wts.w_r), P(wts.bias), C.byref(d), P(sv["logits"]),
+                                  P(self.ws_router), self.ws_router.numel(), s), "router")
         mark(1)
         chk(lib.moe_route(P(sv["logits"]), P(self.layer.drop), C.byref(d), P(sv["topk_idx"]),
                           P(sv["topk_prob"]), P(sv["counts"]), P(sv["offsets"]), P(sv["dst_rows"]),

@@ -66,6 +66,7 @@ extern "C" {
 #define MOE_OP_GEMM 2
 #define MOE_OP_LAYER_FWD 3
 #define MOE_OP_LAYER_BWD 4
+#define MOE_OP_ROUTER 5
 
 /* ---- shapes -------------------------------------------------------------
  * N tokens, D model width, E experts, K routes per token, H expert (SwiGLU)
@@ -93,9 +94,12 @@ int moe_last_hip_error(void);
 /* ---- router ------------------------------------------------------------
  * logits[t,e] = sum_d x[t,d] * w_r[e,d] (fp32 accumulate) + bias[e].
  * (KOSMOS section 3.3.1 step 1: router logits X W_r^T in FP32 tiles.)
- * x bf16 [N][D]; w_r bf16 [E][D]; bias fp32 [E] or NULL; logits fp32 [N][E]. */
+ * x bf16 [N][D]; w_r bf16 [E][D]; bias fp32 [E] or NULL; logits fp32 [N][E].
+ * ws: moe_workspace_size(MOE_OP_ROUTER) bytes (may be 0; ws may then be NULL):
+ * the contraction is split into fixed ranges whose fp32 partial products are
+ * added there in a fixed order. */
 int moe_router_logits(const void* x, const void* w_r, const float* bias, const moe_dims* d,
-                      float* logits, void* stream);
+                      float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- route -------------------------------------------------------------
  * Softmax and top-K of each token, then the route map (KOSMOS section 3.3.1

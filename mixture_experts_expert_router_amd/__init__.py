@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_rocm.so")
 MOE_OK = 0
 MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
-MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD = 1, 2, 3, 4
+MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD, MOE_OP_ROUTER = 1, 2, 3, 4, 5
 
 _vp = C.c_void_p
 _i64 = C.c_int64
@@ -70,7 +70,7 @@ EXPORTS = {
     "moe_workspace_size": (C.c_size_t, [C.c_int, C.POINTER(Dims)]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_last_hip_error": (C.c_int, []),
-    "moe_router_logits": (C.c_int, [_vp, _vp, _vp, C.POINTER(Dims), _vp, _vp]),
+    "moe_router_logits": (C.c_int, [_vp, _vp, _vp, C.POINTER(Dims), _vp, _vp, C.c_size_t, _vp]),
     "moe_route": (C.c_int, [_vp, _vp, C.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                             C.c_size_t, _vp]),
     "moe_dispatch": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.POINTER(Dims), C.c_int, _vp, _vp, _vp]),
@@ -146,14 +146,15 @@ def workspace(op: int, d: Dims, device=None):
 # ---- single steps --------------------------------------------------------------
 
 
-def router_logits(x, w_r, bias=None, out=None):
+def router_logits(x, w_r, bias=None, out=None, ws=None):
     torch = _torch()
     N, D = x.shape
     E = w_r.shape[0]
     d = dims(N, D, E, 1)
     out = out if out is not None else torch.empty((N, E), dtype=torch.float32, device=x.device)
-    _check(load().moe_router_logits(_ptr(x), _ptr(w_r), _ptr(bias), C.byref(d), _ptr(out), _stream()),
-           "moe_router_logits")
+    ws = ws if ws is not None else workspace(MOE_OP_ROUTER, d, x.device)
+    _check(load().moe_router_logits(_ptr(x), _ptr(w_r), _ptr(bias), C.byref(d), _ptr(out), _ptr(ws),
+                                    ws.numel(), _stream()), "moe_router_logits")
     return out
 
 

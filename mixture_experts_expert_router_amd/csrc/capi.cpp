@@ -70,6 +70,8 @@ hipError_t gemm_fwd_bf16(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
 
 size_t route_bytes(const moe_dims& d) { return round_up(moe::route_workspace_bytes(d.N, d.E, d.K), 256); }
 
+size_t router_bytes(const moe_dims& d) { return round_up(moe::router_workspace_bytes(d.N, d.D, d.E), 256); }
+
 size_t bwd_scratch_bytes(const moe_dims& d) {
   const size_t rc = (size_t)rows_cap_of(d);
   return 2 * round_up(rc * d.D * 2, 256) + 2 * round_up(rc * d.H * 2, 256);
@@ -87,7 +89,8 @@ size_t moe_workspace_size(int op, const moe_dims* d) {
   switch (op) {
     case MOE_OP_ROUTE: return route_bytes(*d);
     case MOE_OP_GEMM: return table_bytes(rc, d->E);
-    case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, d->E);
+    case MOE_OP_ROUTER: return router_bytes(*d);
+    case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, d->E) + router_bytes(*d);
     case MOE_OP_LAYER_BWD: return table_bytes(rc, d->E) + bwd_scratch_bytes(*d);
     default: return 0;
   }
@@ -110,14 +113,17 @@ const char* moe_status_string(int s) {
 int moe_last_hip_error(void) { return g_last_hip_error.load(); }
 
 int moe_router_logits(const void* x, const void* w_r, const float* bias, const moe_dims* d,
-                      float* logits, void* stream) {
+                      float* logits, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(d, false, false);
   if (st) return st;
   REQUIRE_UNLESS(d->N == 0, x);
   REQUIRE(w_r);
   REQUIRE_UNLESS(d->N == 0, logits);
   OPTIONAL(bias);
-  return hip_status(moe::launch_router_logits(x, w_r, bias, d->N, d->D, d->E, logits, (hipStream_t)stream));
+  const size_t need = router_bytes(*d);
+  REQUIRE_UNLESS(need == 0, ws);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_router_logits(x, w_r, bias, d->N, d->D, d->E, logits, ws, (hipStream_t)stream));
 }
 
 int moe_route(const float* logits, const uint8_t* drop, const moe_dims* d, int32_t* topk_idx,
@@ -355,13 +361,14 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     REQUIRE(sv->xd);
   }
   const int64_t rc = rows_cap_of(d);
-  const size_t rb = route_bytes(d);
-  if (ws_bytes < rb + table_bytes(rc, d.E)) return MOE_ERR_WORKSPACE;
+  const size_t rb = route_bytes(d), tb = table_bytes(rc, d.E);
+  if (ws_bytes < rb + tb + router_bytes(d)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   void* ws_route = ws;
   int32_t* table = (int32_t*)((char*)ws + rb);
+  void* ws_router = (char*)ws + rb + tb;
 
-  hipError_t e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, s);
+  hipError_t e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, ws_router, s);
   if (e == hipSuccess)
     e = moe::launch_route(sv->logits, a->drop, d.N, d.E, d.K, d.renorm, d.align, rc, sv->topk_idx,
                           sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,

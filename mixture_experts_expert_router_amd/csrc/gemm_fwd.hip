@@ -21,29 +21,16 @@
 // of small experts run beside the MFMA-bound tiles of large ones, and resets
 // the queue head.  Which workgroup computes an item never changes its result.
 //
-// Tile engine.  Operand tiles go from global memory straight into an NS-stage
-// LDS ring with global_load_lds_dwordx4 (each wave instruction writes 1 KB:
-// 64 lanes x 16 bytes at consecutive LDS addresses from M0), so no registers
-// stage the copies and NS-1 contraction steps are in flight while the MFMAs of
-// the current one run.  The loads are issued from inline assembly and their
-// completion is tracked here with explicit vmcnt waits: the vector-memory
-// loads of a wave complete in issue order, so "at most n outstanding" after
-// the loads of n later steps were issued means every older step has landed.
-// LDS rows hold 64 bf16 (128 bytes); chunk c of row r sits at slot c ^ (r & 7),
-// which, measured on gfx950, keeps the 16-row fragment reads (ds_read_b128)
-// free of bank conflicts; each lane fetches the global chunk that belongs at
-// its LDS slot.  Eight waves per workgroup (two per SIMD).  Operands are fed
-// swapped (weight tile as the MFMA's first operand) so each lane's four
-// accumulators are four consecutive output columns of one row.
+// The MFMA main loop (direct-to-LDS operand ring) is the shared tile engine;
+// eight waves per workgroup (two per SIMD).
 #include "common.h"
 #include "launch.h"
+#include "mfma_tile.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;          // contraction step (bf16 elements)
-constexpr int kRB = kBK * 2;     // bytes per LDS row
 constexpr int kBigRows = 256;    // experts with at least this many rows use 256-row tiles
 
 struct FwdParams {
@@ -64,100 +51,30 @@ struct FwdParams {
 // [2 .. 2+L) expert ids in processing order, [2+E .. 2+E+L] item prefix sums
 // (entry L = total).
 
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// wait until at most n_after steps' loads of this wave are outstanding
-template <int LPS, int KMAX>
-__device__ __forceinline__ void wait_steps(int n_after) {
-  if constexpr (KMAX > 0) {
-    if (n_after >= KMAX) { wait_vmcnt<KMAX * LPS>(); return; }
-    wait_steps<LPS, KMAX - 1>(n_after);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-__device__ __forceinline__ int slot_of(int r, int c) { return c ^ (r & 7); }
-
-template <int BM_, int BN_, int NS_, int WAVES_M, int WAVES_N, bool DUAL_>
-struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_;
-  static constexpr bool DUAL = DUAL_;
-  static constexpr int NW = WAVES_M * WAVES_N;
-  static constexpr int WAVES_N_ = WAVES_N;
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int TM = WM / 16, TN = WN / 16;
-  static constexpr int RPI = 1024 / kRB;                           // rows per DMA instruction
-  static constexpr int A_BYTES = BM * kRB, STAGE = (BM + BN) * kRB;
-  static constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;   // per wave per step
-  static constexpr int LPS = A_INS + B_INS;
-  static constexpr int NCOL = DUAL ? BN / 2 : BN;                  // output columns per tile
-  static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "even DMA split");
-  static_assert(WM % 16 == 0 && WN % 16 == 0 && (!DUAL || TN % 2 == 0), "wave tile");
-  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS ring");
-};
-
-// Row of the B tile that wave column wn, fragment j reads.  DUAL: gate rows
-// [0, BN/2), up rows [BN/2, BN); a wave holds TN/2 gate and TN/2 up fragments
-// of the same output columns.
-template <class C>
-__device__ __forceinline__ int b_row(int wn, int j) {
-  if (!C::DUAL) return wn * C::WN + j * 16;
-  constexpr int half = C::TN / 2;
-  const int jj = j < half ? j : j - half;
-  return (j < half ? 0 : C::BN / 2) + wn * (C::WN / 2) + jj * 16;
-}
-
 // One output tile: rows [m_start, min(m_start + BM, m1)) of expert e, columns
 // [n0, n0 + NCOL).  Rows past the expert's segment (or columns past N) load a
 // clamped valid row and are never stored.
 template <class C>
 __device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int e,
                                          int m_start, int m1, int n0) {
-  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, NS = C::NS;
+  using namespace tile;
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int nk = p.K / kBK;
   const int64_t K = p.K;
-
-  int a_off[TM][2], b_off[TN][2];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * WM + i * 16 + l16;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_off[i][ks] = r * kRB + (slot_of(r, ks * 4 + lg) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int r = b_row<C>(wn, j) + l16;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) b_off[j][ks] = C::A_BYTES + r * kRB + (slot_of(r, ks * 4 + lg) << 4);
-  }
-
-  // this lane's place in a DMA instruction: row within the 1 KB block and the
-  // global chunk that belongs at its slot (slot_of is an involution in c)
-  const int d_row = lane >> 3;
-  const int d_chunk = slot_of(d_row, lane & 7);
+  const int d_chunk = dma_chunk();
   const uint16_t* a_src[C::A_INS];
   const uint16_t* b_src[C::B_INS];
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
-    const int r = (wave * C::A_INS + q) * C::RPI + d_row;
-    const int row = min(m_start + r, m1 - 1);
+    const int row = min(m_start + dma_row(wave, C::A_INS, q), m1 - 1);
     a_src[q] = p.a + (int64_t)row * K + d_chunk * 8;
   }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
-    const int r = (wave * C::B_INS + q) * C::RPI + d_row;
+    const int r = dma_row(wave, C::B_INS, q);
     const uint16_t* base = p.b0;
     int col = n0 + r;
     if (C::DUAL && r >= C::BN / 2) {
@@ -167,48 +84,8 @@ __device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem
     col = min(col, p.N - 1);
     b_src[q] = base + ((int64_t)e * p.N + col) * K + d_chunk * 8;
   }
-  const uint32_t wave_a = (uint32_t)(wave * C::A_INS) * 1024u;
-  const uint32_t wave_b = (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((kt % NS) * C::STAGE);
-    const int64_t ko = (int64_t)kt * kBK;
-#pragma unroll
-    for (int q = 0; q < C::A_INS; ++q)
-      lds_dma16(a_src[q] + ko, __builtin_amdgcn_readfirstlane(st + wave_a + q * 1024u));
-#pragma unroll
-    for (int q = 0; q < C::B_INS; ++q)
-      lds_dma16(b_src[q] + ko, __builtin_amdgcn_readfirstlane(st + wave_b + q * 1024u));
-  };
-
   f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
-    __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
-    const uint8_t* st = smem + (kt % NS) * C::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][ks]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off[j][ks]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  }
-  __syncthreads();   // every wave is done reading the ring before it is refilled
+  mainloop<C>(smem, lds0, a_src, b_src, p.K / kBK, acc);
 
   // epilogue: lane holds row wm*WM + i*16 + l16, columns 4*lg .. 4*lg+3 of its
   // 16-column fragment
@@ -250,11 +127,11 @@ __device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem
 
 // The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
 template <bool DUAL>
-using BigTile = TileCfg<256, 256, 2, 4, 2, DUAL>;     // 2 x 64 KB ring
+using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL>;     // 2 x 64 KB ring
 template <bool DUAL>
-using SmallTile = TileCfg<128, 256, 3, 2, 4, DUAL>;   // 3 x 48 KB ring
-constexpr int kLdsBytes = 3 * (128 + 256) * kRB;     // the larger ring
-static_assert(kLdsBytes >= 2 * (256 + 256) * kRB, "ring size");
+using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL>;   // 3 x 48 KB ring
+constexpr int kLdsBytes = 3 * (128 + 256) * tile::kRB;     // the larger ring
+static_assert(kLdsBytes >= 2 * (256 + 256) * tile::kRB, "ring size");
 
 __device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
 
@@ -385,7 +262,7 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
 
 size_t gemm_fwd_plan_ints(int64_t E) { return (size_t)(4 + 2 * E + 64); }
 
-bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim) { return k_dim % kBK == 0 && n_dim % 16 == 0; }
+bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim) { return k_dim % tile::kBK == 0 && n_dim % 16 == 0; }
 
 hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s) {
   FwdParams p{};

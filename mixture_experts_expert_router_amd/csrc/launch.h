@@ -43,8 +43,9 @@ struct GemmBwd {
 };
 
 // router.hip
+size_t router_workspace_bytes(int64_t N, int64_t D, int64_t E);
 hipError_t launch_router_logits(const void* x, const void* w_r, const float* bias, int64_t N,
-                                int64_t D, int64_t E, float* logits, hipStream_t s);
+                                int64_t D, int64_t E, float* logits, void* ws, hipStream_t s);
 
 // route.hip
 size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K);

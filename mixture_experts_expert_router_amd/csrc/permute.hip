@@ -138,22 +138,18 @@ __global__ __launch_bounds__(256) void zero_padding_kernel(const int32_t* __rest
   }
 }
 
-// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), fp32 fmaf in ascending k
+// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), fp32 fmaf in ascending k.
+// The rows of up to 8 routes are loaded before any of them is added, so a
+// lane keeps 16 loads in flight instead of waiting on one route at a time.
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ dst_rows,
                                                       const float* __restrict__ weight, int N,
                                                       int D, int K, uint16_t* __restrict__ out) {
-  constexpr int VPL = 2;
+  constexpr int VPL = 2, KCH = 8;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[32];
-  float w[32];
-  for (int k = 0; k < K; ++k) {
-    dst[k] = dst_rows[(int64_t)t * K + k];
-    w[k] = WEIGHTED ? weight[(int64_t)t * K + k] : 1.0f;
-  }
   const int nvec = D >> 3;
   for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
     float acc[VPL][8];
@@ -161,23 +157,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int j = 0; j < VPL; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      if (dst[k] < 0) continue;
-      const uint16_t* src = y + (int64_t)dst[k] * D;
+    for (int kb = 0; kb < K; kb += KCH) {
+      uint4 r[KCH][VPL];
+      int dk[KCH];
+      float wk[KCH];
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const int v = v0 + lane + j * kWave;
-        if (v < nvec) {
-          uint4 r = ldg16(src + v * 8);
-          const float wk = w[k];
-          acc[j][0] = fmaf(wk, bf16lo(r.x), acc[j][0]);
-          acc[j][1] = fmaf(wk, bf16hi(r.x), acc[j][1]);
-          acc[j][2] = fmaf(wk, bf16lo(r.y), acc[j][2]);
-          acc[j][3] = fmaf(wk, bf16hi(r.y), acc[j][3]);
-          acc[j][4] = fmaf(wk, bf16lo(r.z), acc[j][4]);
-          acc[j][5] = fmaf(wk, bf16hi(r.z), acc[j][5]);
-          acc[j][6] = fmaf(wk, bf16lo(r.w), acc[j][6]);
-          acc[j][7] = fmaf(wk, bf16hi(r.w), acc[j][7]);
+      for (int kk = 0; kk < KCH; ++kk) {
+        const int k = kb + kk;
+        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : -1;
+        wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
+        const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + lane + j * kWave;
+          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16(src + v * 8) : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        if (dk[kk] < 0) continue;
+        const float w = wk[kk];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const uint4 q = r[kk][j];
+          acc[j][0] = fmaf(w, bf16lo(q.x), acc[j][0]);
+          acc[j][1] = fmaf(w, bf16hi(q.x), acc[j][1]);
+          acc[j][2] = fmaf(w, bf16lo(q.y), acc[j][2]);
+          acc[j][3] = fmaf(w, bf16hi(q.y), acc[j][3]);
+          acc[j][4] = fmaf(w, bf16lo(q.z), acc[j][4]);
+          acc[j][5] = fmaf(w, bf16hi(q.z), acc[j][5]);
+          acc[j][6] = fmaf(w, bf16lo(q.w), acc[j][6]);
+          acc[j][7] = fmaf(w, bf16hi(q.w), acc[j][7]);
         }
       }
     }

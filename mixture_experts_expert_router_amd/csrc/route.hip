@@ -15,7 +15,7 @@
 
 namespace moe {
 
-constexpr int kChunk = 64;         // tokens per workgroup in route_topk
+constexpr int kChunk = 16;         // tokens per workgroup in route_topk (4 per wave)
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;
 

@@ -1,21 +1,103 @@
 // Router logits L = X W_r^T + b on bf16 MFMA with fp32 accumulation (KOSMOS
-// section 3.3.1 step 1: router logits in FP32 tiles; its router tile is narrow
-// because the product has only as many columns as experts).
+// section 3.3.1 step 1: router logits in FP32 tiles; the router product has
+// only as many columns as experts, so its tile is narrow).
 //
-// One workgroup (4 waves) owns 16 token rows and all E columns.  The E/16
-// column tiles are split over the waves; when there are fewer than four
-// column tiles the waves split the contraction instead and their partial sums
-// are added in LDS in a fixed order.  Operands come straight from global
-// memory in 16-byte fragments: each token row is read from HBM once, W_r is
-// small and stays in L2.
+// The product is skinny (N tokens x D, times D x E with E <= 1024), so one
+// 64-row block per workgroup would leave most CUs idle.  The contraction is
+// split into S fixed ranges: item (row block, column tile, split) runs the
+// shared MFMA tile engine over its range and writes an fp32 partial tile;
+// a second kernel adds the S partials in ascending split order plus the bias.
+// The split is a function of the shape only, so the result is bitwise the
+// same run to run.  With S = 1 the tile kernel writes the logits directly.
+//
+// Shapes the engine does not take (D not a multiple of 64) use a direct
+// kernel: one workgroup per 16 rows, operands read straight from global
+// memory in 16-byte fragments, the contraction split over the waves when
+// there are few column tiles.
 #include "common.h"
 #include "launch.h"
+#include "mfma_tile.h"
 
 namespace moe {
 
+namespace {
+
+template <int BN>
+using RouterTile = tile::TileCfg<64, BN, 3, 1, 4, false>;
+
+struct RouterParams {
+  const uint16_t* x;    // [N][D]
+  const uint16_t* w;    // [E][D]
+  const float* bias;    // [E] or null (added only when S == 1)
+  float* out;           // S == 1: logits [N][E]; else partials [S][N][E]
+  int N, D, E, S, mblocks, ntiles;
+};
+
+template <int BN>
+__global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
+  using C = RouterTile<BN>;
+  using namespace tile;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  int item = blockIdx.x;
+  const int mb = item % p.mblocks;
+  item /= p.mblocks;
+  const int nt = item % p.ntiles;
+  const int split = item / p.ntiles;
+  const int nk = p.D / kBK;
+  const int k0 = (int)((int64_t)nk * split / p.S), k1 = (int)((int64_t)nk * (split + 1) / p.S);
+  const int m_start = mb * C::BM, n0 = nt * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d_chunk = dma_chunk();
+  const uint16_t* a_src[C::A_INS];
+  const uint16_t* b_src[C::B_INS];
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int row = min(m_start + dma_row(wave, C::A_INS, q), p.N - 1);
+    a_src[q] = p.x + (int64_t)row * p.D + (int64_t)k0 * kBK + d_chunk * 8;
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) {
+    const int col = min(n0 + dma_row(wave, C::B_INS, q), p.E - 1);
+    b_src[q] = p.w + (int64_t)col * p.D + (int64_t)k0 * kBK + d_chunk * 8;
+  }
+  f32x4_t acc[C::TM][C::TN];
+  mainloop<C>(smem, lds0, a_src, b_src, k1 - k0, acc);
+
+  // lane holds row i*16 + l16 (one wave row), columns wn*WN + j*16 + 4*lg + r
+  const int l16 = lane & 15, lg = lane >> 4, wn = wave;
+  float* out = p.out + (p.S > 1 ? (int64_t)split * p.N * p.E : 0);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = m_start + i * 16 + l16;
+    if (row >= p.N) continue;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int n = n0 + wn * C::WN + j * 16 + 4 * lg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (n + r < p.E) {
+          const float b = (p.S == 1 && p.bias) ? p.bias[n + r] : 0.0f;
+          out[(int64_t)row * p.E + n + r] = acc[i][j][r] + b;
+        }
+      }
+    }
+  }
+}
+
+// logits = sum over splits (ascending) of the partials, plus the bias
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, const float* __restrict__ bias,
+                                                            int64_t NE, int E, int S, float* __restrict__ logits) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < NE; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = part[i];
+    for (int k = 1; k < S; ++k) s += part[(int64_t)k * NE + i];
+    logits[i] = s + (bias ? bias[i % E] : 0.0f);
+  }
+}
+
 constexpr int kRouterMaxTiles = 16;   // column tiles per wave (E <= 1024)
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void router_direct_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int N,
                                                             int D, int E,
@@ -87,11 +169,56 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// tile width for E columns, and the number of contraction splits
+struct RouterPlan {
+  int bn, ntiles, mblocks, S;
+};
+
+RouterPlan router_plan(int64_t N, int64_t D, int64_t E) {
+  RouterPlan r{};
+  r.bn = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+  r.ntiles = (int)((E + r.bn - 1) / r.bn);
+  r.mblocks = (int)((N + 63) / 64);
+  const int nk = (int)(D / tile::kBK);
+  const int64_t base = (int64_t)r.mblocks * r.ntiles;
+  int S = (int)((512 + base - 1) / (base > 0 ? base : 1));   // about 512 items
+  S = S < 1 ? 1 : (S > nk ? nk : S);
+  S = S > 16 ? 16 : S;
+  r.S = S;
+  return r;
+}
+
+bool router_tiled(int64_t D, int64_t E) { return D % tile::kBK == 0 && E >= 16; }
+
+}  // namespace
+
+size_t router_workspace_bytes(int64_t N, int64_t D, int64_t E) {
+  if (N <= 0 || !router_tiled(D, E)) return 0;
+  const RouterPlan r = router_plan(N, D, E);
+  return r.S > 1 ? (size_t)r.S * N * E * 4 : 0;
+}
+
 hipError_t launch_router_logits(const void* x, const void* w_r, const float* bias, int64_t N,
-                                int64_t D, int64_t E, float* logits, hipStream_t s) {
+                                int64_t D, int64_t E, float* logits, void* ws, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  router_logits_kernel<<<(unsigned)((N + 15) / 16), 256, 0, s>>>(
-      (const uint16_t*)x, (const uint16_t*)w_r, bias, (int)N, (int)D, (int)E, logits);
+  if (!router_tiled(D, E)) {
+    router_direct_kernel<<<(unsigned)((N + 15) / 16), 256, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)w_r, bias, (int)N, (int)D, (int)E, logits);
+    return hipGetLastError();
+  }
+  const RouterPlan r = router_plan(N, D, E);
+  RouterParams p{(const uint16_t*)x, (const uint16_t*)w_r, bias, r.S > 1 ? (float*)ws : logits,
+                 (int)N, (int)D, (int)E, r.S, r.mblocks, r.ntiles};
+  const unsigned grid = (unsigned)((int64_t)r.mblocks * r.ntiles * r.S);
+  if (r.bn == 64) router_tile_kernel<64><<<grid, 256, 0, s>>>(p);
+  else if (r.bn == 128) router_tile_kernel<128><<<grid, 256, 0, s>>>(p);
+  else router_tile_kernel<256><<<grid, 256, 0, s>>>(p);
+  if (r.S > 1) {
+    const int64_t NE = N * E;
+    const int64_t nblk = (NE + 255) / 256;
+    const unsigned rg = (unsigned)(nblk < 4096 ? nblk : 4096);
+    router_reduce_kernel<<<rg, 256, 0, s>>>((const float*)ws, bias, NE, (int)E, r.S, logits);
+  }
   return hipGetLastError();
 }
 
