@@ -30,7 +30,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---- silu / sigmoid in fp32 ---------------------------------------------------
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// 1 / (1 + e^-g) with the hardware reciprocal (about 1 ulp) instead of an
+// IEEE division; the results are stored as bf16.
+__device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // ---- MXFP8 element and scale (OCP E4M3FN, E8M0) --------------------------------
 // floor(log2 a) of a positive finite fp32 value, read from its bit fields.

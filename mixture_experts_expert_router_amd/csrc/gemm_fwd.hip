@@ -51,53 +51,105 @@ struct FwdParams {
 // [2 .. 2+L) expert ids in processing order, [2+E .. 2+E+L] item prefix sums
 // (entry L = total).
 
-// One output tile: rows [m_start, min(m_start + BM, m1)) of expert e, columns
-// [n0, n0 + NCOL).  Rows past the expert's segment (or columns past N) load a
-// clamped valid row and are never stored.
+// A claimed queue item, decoded: rows [m_start, min(m_start + BM, m1)) of
+// expert e, output columns [n0, n0 + NCOL), tile class by the expert's rows.
+struct Item {
+  int e, m_start, m1, n0;
+  bool big, valid;
+};
+
+// The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
+template <bool DUAL>
+using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL>;     // 2 x 64 KB ring
+template <bool DUAL>
+using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL>;   // 3 x 48 KB ring
+constexpr int kLdsBytes = 3 * (128 + 256) * tile::kRB;     // the larger ring
+static_assert(kLdsBytes >= 2 * (256 + 256) * tile::kRB, "ring size");
+
+__device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
+
+// Claim the next item from the queue and decode it (every thread gets the
+// same result; li is the workgroup's position in the expert list, which only
+// moves forward because each workgroup's claims increase).
+template <bool DUAL>
+__device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) {
+  if (threadIdx.x == 0) *s_item = atomicAdd(p.head, 1);
+  __syncthreads();
+  const int item = *s_item;
+  Item it{};
+  const int total = p.plan[0];
+  if (item >= total) return it;
+  const int L = p.plan[1];
+  const int32_t* order = p.plan + 2;
+  const int32_t* pref = p.plan + 2 + p.E;
+  while (li + 1 < L && pref[li + 1] <= item) ++li;
+  it.e = order[li];
+  const int m0 = p.offsets[it.e];
+  it.m1 = p.offsets[it.e + 1];
+  it.big = is_big(it.m1 - m0);
+  const int bm = it.big ? BigTile<DUAL>::BM : SmallTile<DUAL>::BM;
+  const int nmb = (it.m1 - m0 + bm - 1) / bm;
+  const int w = item - pref[li];
+  const int n_t = w / nmb, mb = w - n_t * nmb;
+  it.m_start = m0 + mb * bm;
+  it.n0 = n_t * BigTile<DUAL>::NCOL;
+  it.valid = true;
+  return it;
+}
+
+// This lane's DMA source pointers for an item (rows past the expert's segment
+// or columns past N load a clamped valid row and are never stored).
 template <class C>
-__device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int e,
-                                         int m_start, int m1, int n0) {
+__device__ __forceinline__ void sources(const FwdParams& p, const Item& it, const uint16_t** a_src,
+                                        const uint16_t** b_src) {
   using namespace tile;
-  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int wave = threadIdx.x >> 6;
   const int64_t K = p.K;
   const int d_chunk = dma_chunk();
-  const uint16_t* a_src[C::A_INS];
-  const uint16_t* b_src[C::B_INS];
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
-    const int row = min(m_start + dma_row(wave, C::A_INS, q), m1 - 1);
+    const int row = min(it.m_start + dma_row(wave, C::A_INS, q), it.m1 - 1);
     a_src[q] = p.a + (int64_t)row * K + d_chunk * 8;
   }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
     const int r = dma_row(wave, C::B_INS, q);
     const uint16_t* base = p.b0;
-    int col = n0 + r;
+    int col = it.n0 + r;
     if (C::DUAL && r >= C::BN / 2) {
       base = p.b1;
-      col = n0 + r - C::BN / 2;
+      col = it.n0 + r - C::BN / 2;
     }
     col = min(col, p.N - 1);
-    b_src[q] = base + ((int64_t)e * p.N + col) * K + d_chunk * 8;
+    b_src[q] = base + ((int64_t)it.e * p.N + col) * K + d_chunk * 8;
   }
-  f32x4_t acc[TM][TN];
-  mainloop<C>(smem, lds0, a_src, b_src, p.K / kBK, acc);
+}
 
-  // epilogue: lane holds row wm*WM + i*16 + l16, columns 4*lg .. 4*lg+3 of its
+template <class C>
+__device__ __forceinline__ void start(const FwdParams& p, uint32_t lds0, const Item& it) {
+  const uint16_t* a_src[C::A_INS];
+  const uint16_t* b_src[C::B_INS];
+  sources<C>(p, it, a_src, b_src);
+  tile::prologue<C>(lds0, a_src, b_src, p.K / tile::kBK);
+}
+
+template <class C>
+__device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, const f32x4_t (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  const int l16 = lane & 15, lg = lane >> 4;
+  // lane holds row wm*WM + i*16 + l16, columns 4*lg .. 4*lg+3 of its
   // 16-column fragment
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = wm * WM + i * 16 + l16;
-    if (m_start + m >= m1) continue;
-    const int64_t row = m_start + m;
+    if (it.m_start + m >= it.m1) continue;
+    const int64_t row = it.m_start + m;
     if (!C::DUAL) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lg;
+        const int n = it.n0 + wn * WN + j * 16 + 4 * lg;
         if (n >= p.N) continue;
         const f32x4_t a = acc[i][j];
         *reinterpret_cast<uint2*>(p.c0 + row * p.N + n) =
@@ -106,7 +158,7 @@ __device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem
     } else {
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
-        const int n = n0 + wn * (WN / 2) + j * 16 + 4 * lg;
+        const int n = it.n0 + wn * (WN / 2) + j * 16 + 4 * lg;
         if (n >= p.N) continue;
         const f32x4_t a = acc[i][j], b = acc[i][j + TN / 2];
         const uint32_t gw0 = pack_bf16x2(a[0], a[1]), gw1 = pack_bf16x2(a[2], a[3]);
@@ -125,47 +177,39 @@ __device__ __forceinline__ void run_tile(const FwdParams& p, const uint8_t* smem
   }
 }
 
-// The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
-template <bool DUAL>
-using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL>;     // 2 x 64 KB ring
-template <bool DUAL>
-using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL>;   // 3 x 48 KB ring
-constexpr int kLdsBytes = 3 * (128 + 256) * tile::kRB;     // the larger ring
-static_assert(kLdsBytes >= 2 * (256 + 256) * tile::kRB, "ring size");
-
-__device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
+// Run the current item (its prologue already issued), then claim the next
+// one and issue its prologue before storing this item's outputs, so the
+// loads of the next tile overlap this epilogue.
+template <class C, bool DUAL>
+__device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int* s_item,
+                                         int& li, const Item& it) {
+  const uint16_t* a_src[C::A_INS];
+  const uint16_t* b_src[C::B_INS];
+  sources<C>(p, it, a_src, b_src);
+  f32x4_t acc[C::TM][C::TN];
+  tile::mainloop<C>(smem, lds0, a_src, b_src, p.K / tile::kBK, acc);
+  const Item next = claim<DUAL>(p, s_item, li);
+  if (next.valid) {
+    if (next.big) start<BigTile<DUAL>>(p, lds0, next);
+    else start<SmallTile<DUAL>>(p, lds0, next);
+  }
+  epilogue<C>(p, it, acc);
+  return next;
+}
 
 template <bool DUAL>
 __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   __shared__ int s_item;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const int total = p.plan[0];
-  const int L = p.plan[1];
-  const int32_t* order = p.plan + 2;
-  const int32_t* pref = p.plan + 2 + p.E;
-
-  int li = 0;   // position in the expert list; each workgroup's claims increase
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(p.head, 1);
-    __syncthreads();
-    const int item = s_item;
-    if (item >= total) break;
-    while (li + 1 < L && pref[li + 1] <= item) ++li;
-    const int e = order[li];
-    const int m0 = p.offsets[e], m1 = p.offsets[e + 1];
-    const int w = item - pref[li];
-    if (is_big(m1 - m0)) {
-      using C = BigTile<DUAL>;
-      const int nmb = (m1 - m0 + C::BM - 1) / C::BM;
-      const int n_t = w / nmb, mb = w - n_t * nmb;
-      run_tile<C>(p, smem, lds0, e, m0 + mb * C::BM, m1, n_t * C::NCOL);
-    } else {
-      using C = SmallTile<DUAL>;
-      const int nmb = (m1 - m0 + C::BM - 1) / C::BM;
-      const int n_t = w / nmb, mb = w - n_t * nmb;
-      run_tile<C>(p, smem, lds0, e, m0 + mb * C::BM, m1, n_t * C::NCOL);
-    }
+  int li = 0;
+  Item it = claim<DUAL>(p, &s_item, li);
+  if (!it.valid) return;
+  if (it.big) start<BigTile<DUAL>>(p, lds0, it);
+  else start<SmallTile<DUAL>>(p, lds0, it);
+  while (it.valid) {
+    if (it.big) it = run_item<BigTile<DUAL>, DUAL>(p, smem, lds0, &s_item, li, it);
+    else it = run_item<SmallTile<DUAL>, DUAL>(p, smem, lds0, &s_item, li, it);
   }
 }
 

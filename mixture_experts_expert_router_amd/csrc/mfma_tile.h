@@ -84,10 +84,35 @@ __device__ __forceinline__ int dma_chunk() {
   return slot_of(lane >> 3, lane & 7);
 }
 
-// Main loop: acc += A[rows, k] . B[cols, k]^T over nk contraction steps.
+// Issue the DMA loads of contraction step kt into its ring stage.
 // a_src[q] / b_src[q] point at this lane's chunk of its q-th DMA row at the
-// first step; step kt reads kt * kBK elements further.  The ring is free again
-// when this returns.
+// first step; step kt reads kt * kBK elements further.
+template <class C>
+__device__ __forceinline__ void issue_step(uint32_t lds0, const uint16_t* const* a_src, const uint16_t* const* b_src,
+                                           int kt) {
+  const int wave = threadIdx.x >> 6;
+  const uint32_t st = lds0 + (uint32_t)((kt % C::NS) * C::STAGE);
+  const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;
+  const uint32_t wave_b = st + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
+  const int64_t ko = (int64_t)kt * kBK;
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) lds_dma16(a_src[q] + ko, __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) lds_dma16(b_src[q] + ko, __builtin_amdgcn_readfirstlane(wave_b + q * 1024u));
+}
+
+// Issue the first NS-1 steps (the ring must be free).
+template <class C>
+__device__ __forceinline__ void prologue(uint32_t lds0, const uint16_t* const* a_src, const uint16_t* const* b_src,
+                                         int nk) {
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < nk) issue_step<C>(lds0, a_src, b_src, s);
+}
+
+// Main loop: acc = A[rows, k] . B[cols, k]^T over nk contraction steps, the
+// prologue already issued.  The ring is free again when this returns; vector
+// stores issued after the prologue only make the first waits stricter.
 template <class C>
 __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, const uint16_t* const* a_src,
                                          const uint16_t* const* b_src, int nk,
@@ -109,29 +134,14 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) b_off[j][ks] = C::A_BYTES + r * kRB + (slot_of(r, ks * 4 + lg) << 4);
   }
-  const uint32_t wave_a = (uint32_t)(wave * C::A_INS) * 1024u;
-  const uint32_t wave_b = (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((kt % NS) * C::STAGE);
-    const int64_t ko = (int64_t)kt * kBK;
-#pragma unroll
-    for (int q = 0; q < C::A_INS; ++q)
-      lds_dma16(a_src[q] + ko, __builtin_amdgcn_readfirstlane(st + wave_a + q * 1024u));
-#pragma unroll
-    for (int q = 0; q < C::B_INS; ++q)
-      lds_dma16(b_src[q] + ko, __builtin_amdgcn_readfirstlane(st + wave_b + q * 1024u));
-  };
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    if (kt + NS - 1 < nk) issue_step<C>(lds0, a_src, b_src, kt + NS - 1);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
     b_src[q] = p.w + (int64_t)col * p.D + (int64_t)k0 * kBK + d_chunk * 8;
   }
   f32x4_t acc[C::TM][C::TN];
+  prologue<C>(lds0, a_src, b_src, k1 - k0);
   mainloop<C>(smem, lds0, a_src, b_src, k1 - k0, acc);
 
   // lane holds row i*16 + l16 (one wave row), columns wn*WN + j*16 + 4*lg + r

@@ -1,0 +1,248 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (one C-ABI call per stage: router, route, dispatch, GEMM1,
+GEMM2, combine), plus the whole-layer backward of the Qwen3-235B-shaped
+workload.
+
+The oracle cannot run the whole layer at these sizes in seconds, so:
+  * the router logits are compared in full (tolerance), and the route map is
+    rebuilt by the oracle from the GPU's logits and compared bit for bit
+    (topk_idx, counts, offsets, dst_rows, row_route; probabilities to 1e-6);
+  * outputs are checked on sampled tokens, which the oracle computes one by
+    one: rows of a grouped GEMM do not interact, so a token's output needs
+    only its own K expert rows (G, U, H, Y rows and the combined output row;
+    for MXFP8 the quantized row and the oracle's own quantized weights);
+  * weight gradients are checked in full for the smallest experts, whose rows
+    the oracle recomputes entirely.
+Tolerances: bf16 max|diff| <= 1e-2*max|ref| + 1e-3 per tensor; MXFP8 relative
+Frobenius error <= 3e-2; byte results bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import mixture_experts_expert_router_amd as M
+import moe_synth as S
+import oracle as O
+from gpu_util import assert_bf16_close, bits, host, rel_frobenius, vals
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(wl, seed=0):
+    """Generate the workload, run the staged forward once, return host copies."""
+    inp = S.make_inputs(wl, seed)
+    print(f"  inputs generated ({wl.name})", flush=True)
+    x, w, drop = bench.device_inputs(M, inp, wl.mxfp8, torch)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=wl.bwd)
+    st = bench.StagedForward(M, layer, x)
+    st.run()
+    torch.cuda.synchronize()
+    return inp, x, w, layer
+
+
+def _check_route(wl, inp, sv):
+    """Logits within tolerance of the oracle's; route map bit-exact given the
+    GPU's logits.  Returns the oracle's route tensors."""
+    Lg = host(sv["logits"])
+    Lr = O.router_logits(inp.x, inp.w_r, inp.bias)
+    scale = float(np.max(np.abs(Lr)))
+    assert np.max(np.abs(Lg.astype(np.float64) - Lr)) <= 1e-4 * scale + 1e-6
+    idx = O.topk_select(Lg, wl.K)
+    prob = O.route_probs(Lg, idx, wl.renorm)
+    c, o, d, r = O.route_map(idx, inp.drop, wl.E, wl.align, wl.rows_cap)
+    assert np.array_equal(host(sv["topk_idx"]), idx)
+    assert np.max(np.abs(host(sv["topk_prob"]).astype(np.float64) - prob)) <= 1e-6
+    for name, ref in (("counts", c), ("offsets", o), ("dst_rows", d), ("row_route", r)):
+        assert np.array_equal(host(sv[name]), ref), name
+    return idx, prob, c, o, d, r
+
+
+def _sample_tokens(idx, dst, counts, n, max_experts):
+    """Tokens to check: one routed to the largest expert, one to the smallest
+    active expert, one with a dropped route if any, then tokens that add the
+    fewest new experts (the oracle's cost grows with distinct experts)."""
+    N, K = idx.shape
+    chosen, experts = [], set()
+
+    def add(t):
+        if t not in chosen:
+            chosen.append(int(t))
+            experts.update(int(e) for e, d in zip(idx[t], dst[t]) if d >= 0)
+
+    big = int(np.argmax(counts))
+    add(np.nonzero((idx == big).any(1))[0][0])
+    small = int(np.argmin(np.where(counts > 0, np.asarray(counts, np.int64), np.iinfo(np.int64).max)))
+    add(np.nonzero((idx == small).any(1))[0][-1])
+    dropped = np.nonzero((dst < 0).any(1))[0]
+    if len(dropped):
+        add(dropped[len(dropped) // 2])
+    cand = [int(t) for t in range(0, N, 7)]
+    for _ in range(n):
+        cand = [t for t in cand if t not in chosen]
+        if len(chosen) >= n or not cand:
+            break
+        cost = [len(set(int(e) for e, d in zip(idx[t], dst[t]) if d >= 0) - experts) for t in cand]
+        t = cand[int(np.argmin(cost))]
+        if len(experts | set(int(e) for e in idx[t])) > max_experts:
+            break
+        add(t)
+    print(f"  sampled tokens {chosen}, {len(experts)} experts", flush=True)
+    return chosen
+
+
+def _token_rows(wl, inp, tokens, idx, prob, dst, expert_fn):
+    """Oracle expert rows and combined outputs of the sampled tokens."""
+    rows, outs = {}, []
+    cache = {}
+    for t in tokens:
+        ys = np.zeros((wl.K, wl.D))
+        dl = np.full((1, wl.K), -1, np.int64)
+        for k in range(wl.K):
+            if dst[t, k] < 0:
+                continue
+            e = int(idx[t, k])
+            if e not in cache:
+                cache[e] = expert_fn(e)
+            r = cache[e](inp.x[t:t + 1])
+            rows[(t, k)] = r
+            ys[k] = r["y"][0]
+            dl[0, k] = k
+        outs.append(O.combine(ys, dl, prob[t:t + 1])[0])
+    return rows, np.array(outs)
+
+
+def _bf16_expert(inp):
+    def make(e):
+        wg, wu, wd = inp.w_gate[e], inp.w_up[e], inp.w_down[e]
+
+        def f(xrow):
+            g, u, h, y = O.expert_mlp(xrow, wg, wu, wd)
+            return dict(g=g, u=u, h=h, y=y)
+        return f
+    return make
+
+
+def _assert_rows(sv, rows, dst, names, close):
+    for name in names:
+        got = np.stack([vals(sv[name][int(dst[t, k])]) for (t, k) in rows])
+        ref = np.stack([rows[(t, k)][name][0] for (t, k) in rows])
+        close(got, ref, name)
+
+
+BF16_FWD = ["tiny_bf16", "mixtral_bf16", "dsv3_bf16", "qwen3_235b_bf16_fwdbwd"]
+
+
+@pytest.mark.parametrize("name", BF16_FWD)
+def test_full_size_forward_bf16(name):
+    wl = S.WORKLOADS[name]
+    print(f"full-size forward {name}", flush=True)
+    inp, x, w, layer = _run(wl)
+    sv = layer.saved
+    idx, prob, c, o, d, r = _check_route(wl, inp, sv)
+    tokens = _sample_tokens(idx, d, c, n=8, max_experts=24)
+    # dispatch: sampled rows are bit-exact copies of the token rows
+    for t in tokens:
+        for k in range(wl.K):
+            if d[t, k] >= 0:
+                assert np.array_equal(bits(sv["xd"][int(d[t, k])]), inp.x[t])
+    rows, outs = _token_rows(wl, inp, tokens, idx, prob, d, _bf16_expert(inp))
+    _assert_rows(sv, rows, d, ("g", "u", "h", "y"), assert_bf16_close)
+    assert_bf16_close(vals(layer.out)[tokens], outs, "out")
+
+
+def test_full_size_forward_mxfp8():
+    wl = S.WORKLOADS["dsv3_mxfp8"]
+    print("full-size forward dsv3_mxfp8", flush=True)
+    inp, x, w, layer = _run(wl)
+    sv = layer.saved
+    idx, prob, c, o, d, r = _check_route(wl, inp, sv)
+    tokens = _sample_tokens(idx, d, c, n=4, max_experts=20)
+    qcache = {}
+
+    def make(e):
+        # the oracle quantizes the expert's weights itself; they must also
+        # equal the GPU's pre-quantized bytes
+        q = O.quantize_weights_mxfp8(inp.w_gate[e:e + 1], inp.w_up[e:e + 1], inp.w_down[e:e + 1])
+        for k in q:
+            assert np.array_equal(host(w.wq[k][e]), q[k][0]), (e, k)
+        qcache[e] = q
+
+        def f(xrow):
+            xq, xs = O.quantize_mxfp8(xrow)
+            g, u, h, hq, hs, y = O.expert_mlp_mxfp8(xq, xs, q["wg_q"][0], q["wg_s"][0], q["wu_q"][0],
+                                                    q["wu_s"][0], q["wd_q"][0], q["wd_s"][0])
+            return dict(xq=xq, xs=xs, g=g, u=u, h=h, y=y)
+        return f
+
+    rows, outs = _token_rows(wl, inp, tokens, idx, prob, d, make)
+    for (t, k), rr in rows.items():
+        row = int(d[t, k])
+        assert np.array_equal(host(sv["xd_q"][row]), rr["xq"][0])
+        assert np.array_equal(host(sv["xd_s"][row]), rr["xs"][0])
+    keys = list(rows)
+    for name in ("g", "u", "h", "y"):
+        got = np.stack([vals(sv[name][int(d[t, k])]) for (t, k) in keys])
+        ref = np.stack([rows[key][name][0] for key in keys])
+        assert rel_frobenius(got, ref) <= 3e-2, name
+    assert rel_frobenius(vals(layer.out)[tokens], outs) <= 3e-2
+    # padding rows of every expert segment are zero bytes
+    cnt = host(sv["counts"])
+    off = host(sv["offsets"])
+    q = host(sv["xd_q"][: int(off[-1])])
+    for e in np.nonzero(off[1:] - off[:-1] > cnt)[0][:16]:
+        assert not q[off[e] + cnt[e]: off[e + 1]].any()
+
+
+def test_full_size_backward_qwen3():
+    wl = S.WORKLOADS["qwen3_235b_bf16_fwdbwd"]
+    print("full-size backward qwen3_235b_bf16_fwdbwd", flush=True)
+    inp, x, w, layer = _run(wl)
+    sv = layer.saved
+    idx, prob, c, o, d, r = _check_route(wl, inp, sv)
+    dout = inp.dout
+    g = layer.backward(x, torch.from_numpy(dout.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    tokens = _sample_tokens(idx, d, c, n=6, max_experts=20)
+    dx_ref, dprob_ref = [], []
+    for t in tokens:
+        acc = np.zeros((1, wl.D))
+        dp = np.zeros(wl.K)
+        for k in range(wl.K):
+            if d[t, k] < 0:
+                continue
+            e = int(idx[t, k])
+            xr = inp.x[t:t + 1]
+            G, U, Hh, Y = O.expert_mlp(xr, inp.w_gate[e], inp.w_up[e], inp.w_down[e])
+            dyd = O.combine_bwd(dout[t:t + 1], np.array([[0]]), prob[t:t + 1, k:k + 1], 1)
+            eb = O.experts_bwd(dyd, O.values(xr), G, U, Hh, np.array([0, 1]), inp.w_gate[e:e + 1],
+                               inp.w_up[e:e + 1], inp.w_down[e:e + 1])
+            acc += eb["dxd"]
+            dp[k] = np.sum(O.values(dout[t]) * Y[0])
+        dx_ref.append(O.round_bf16(acc[0]))
+        dprob_ref.append(dp.astype(np.float32))
+    assert_bf16_close(vals(g["dx"])[tokens], np.array(dx_ref), "dx")
+    assert_bf16_close(host(g["dprob"])[tokens], np.array(dprob_ref), "dprob")
+    assert np.all(host(g["dprob"])[d < 0] == 0)
+    # weight gradients of the two smallest experts, all their rows recomputed
+    order = np.argsort(np.where(c > 0, c, np.iinfo(np.int32).max))[:2]
+    for e in order:
+        seg = r[o[e]:o[e + 1]]
+        tok, kk = seg // wl.K, seg % wl.K
+        xr = inp.x[tok]
+        G, U, Hh, Y = O.expert_mlp(xr, inp.w_gate[e], inp.w_up[e], inp.w_down[e])
+        dyd = O.round_bf16(O.round_f32(prob[tok, kk].astype(np.float64)[:, None] * O.values(dout[tok])))
+        eb = O.experts_bwd(dyd, O.values(xr), G, U, Hh, np.array([0, len(seg)]), inp.w_gate[e:e + 1],
+                           inp.w_up[e:e + 1], inp.w_down[e:e + 1])
+        assert_bf16_close(vals(g["dw_down"][int(e)]), eb["dw_down"][0], f"dw_down[{e}]")
+        assert_bf16_close(vals(g["dw_gate"][int(e)]), eb["dw_gate"][0], f"dw_gate[{e}]")
+        assert_bf16_close(vals(g["dw_up"][int(e)]), eb["dw_up"][0], f"dw_up[{e}]")
