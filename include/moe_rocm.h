@@ -243,10 +243,15 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * backward -> down wgrad -> gate/up dgrad (one sum) -> gate/up wgrad ->
  * dispatch-bwd (KOSMOS section 3.3.2).  The intermediates dY_d, dG, dU, dX_d
  * live in the workspace. */
+#define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
+#define MOE_SCHED_READY 1   /* bf16: one persistent launch; GEMM1 tiles claimed in
+                               the order dispatch finishes experts, GEMM2 tiles
+                               gated on their GEMM1 row blocks                   */
+
 typedef struct moe_layer_args {
   moe_dims dims;
   int32_t dtype;
-  int32_t _pad;
+  int32_t sched;        /* MOE_SCHED_STAGED or MOE_SCHED_READY (forward only)  */
   const void* x;        /* bf16 [N][D] */
   const void* w_r;      /* bf16 [E][D] */
   const float* bias;    /* fp32 [E] or NULL */

@@ -23,6 +23,7 @@ MOE_OK = 0
 MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD, MOE_OP_ROUTER = 1, 2, 3, 4, 5
+MOE_SCHED_STAGED, MOE_SCHED_READY = 0, 1
 
 _vp = C.c_void_p
 _i64 = C.c_int64
@@ -49,7 +50,7 @@ class GemmBwdArgs(C.Structure):
 
 
 class LayerArgs(C.Structure):
-    _fields_ = [("dims", Dims), ("dtype", _i32), ("_pad", _i32), ("x", _vp), ("w_r", _vp),
+    _fields_ = [("dims", Dims), ("dtype", _i32), ("sched", _i32), ("x", _vp), ("w_r", _vp),
                 ("bias", _vp), ("drop", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("wg_q", _vp), ("wg_s", _vp), ("wu_q", _vp), ("wu_s", _vp), ("wd_q", _vp),
                 ("wd_s", _vp)]
@@ -340,7 +341,7 @@ def quantize_weights_mxfp8(w_gate, w_up, w_down) -> dict:
     return out
 
 
-def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8):
+def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_STAGED):
     N, D = x.shape
     E = wts.w_r.shape[0]
     if mxfp8:
@@ -349,7 +350,7 @@ def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8):
         H = wts.w_gate.shape[1]
     d = dims(N, D, E, K, H, align=32 if mxfp8 else 1, renorm=renorm)
     q = wts.wq or {}
-    a = LayerArgs(d, MOE_MXFP8 if mxfp8 else MOE_BF16, 0, _ptr(x), _ptr(wts.w_r), _ptr(wts.bias),
+    a = LayerArgs(d, MOE_MXFP8 if mxfp8 else MOE_BF16, sched, _ptr(x), _ptr(wts.w_r), _ptr(wts.bias),
                   _ptr(drop), _ptr(wts.w_gate), _ptr(wts.w_up), _ptr(wts.w_down),
                   _ptr(q.get("wg_q")), _ptr(q.get("wg_s")), _ptr(q.get("wu_q")), _ptr(q.get("wu_s")),
                   _ptr(q.get("wd_q")), _ptr(q.get("wd_s")))
@@ -383,12 +384,14 @@ def _saved_struct(sv: dict) -> LayerSaved:
 
 class MoeLayer:
     """Holds the weights, saved tensors and workspaces of one layer so that
-    repeated forward/backward calls allocate nothing."""
+    repeated forward/backward calls allocate nothing.  sched selects the
+    forward's launch scheme (MOE_SCHED_STAGED or MOE_SCHED_READY)."""
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
-                 device="cuda", with_bwd=False):
+                 device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED):
         torch = _torch()
         self.wts, self.K, self.mxfp8, self.renorm, self.drop = wts, K, mxfp8, renorm, drop
+        self.sched = sched
         D = wts.w_r.shape[1]
         self._x_proto = torch.empty((N, D), dtype=torch.bfloat16, device=device)
         _, self.d = _layer_args(self._x_proto, wts, K, drop, renorm, mxfp8)
@@ -408,7 +411,7 @@ class MoeLayer:
             self._gr = LayerGrads(*[_ptr(self.grads[n]) for n, _ in LayerGrads._fields_])
 
     def forward(self, x):
-        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8)
+        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched)
         _check(load().moe_layer_fwd(C.byref(a), C.byref(self._sv), _ptr(self.out), _ptr(self.ws_f),
                                     self.ws_f.numel(), _stream()), "moe_layer_fwd")
         return self.out

@@ -59,7 +59,10 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
 size_t table_bytes(int64_t rows_cap, int64_t E) {
   const size_t a = (size_t)moe::mtile_table_ints(rows_cap, E, 64) * 4;
   const size_t b = (16 + moe::gemm_fwd_plan_ints(E)) * 4;
-  return round_up(a > b ? a : b, 256);
+  const size_t c = moe::experts_fused_ws_ints(rows_cap, E) * 4;
+  size_t m = a > b ? a : b;
+  m = m > c ? m : c;
+  return round_up(m, 256);
 }
 
 // bf16 forward GEMM: the persistent kernel where its shape rule holds
@@ -322,6 +325,7 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                   size_t ws_bytes, void* stream) {
   if (!a || !sv) return MOE_ERR_NULL;
   if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY) return MOE_ERR_DTYPE;
   const bool mx = a->dtype == MOE_MXFP8;
   const moe_dims& d = a->dims;
   int st = check_dims(&d, true, mx);
@@ -383,6 +387,12 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
     if (e == hipSuccess) e = moe::launch_gemm_fwd_mxfp8(g2, table, s);
+  } else if (a->sched == MOE_SCHED_READY && d.align == 1 && moe::gemm_fwd_fast_ok(d.D, d.H) &&
+             moe::gemm_fwd_fast_ok(d.H, d.D)) {
+    // dispatch, GEMM1 and GEMM2 in one persistent launch scheduled by readiness
+    moe::ExpertsFwd xf{d.E, d.K, d.D, d.H, rc, sv->offsets, sv->row_route, a->x, a->w_gate, a->w_up,
+                       a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y};
+    if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
   } else {
     if (e == hipSuccess) e = moe::launch_dispatch_bf16(a->x, sv->dst_rows, nullptr, d.N, d.D, d.K, sv->xd, s);
     if (e == hipSuccess && d.align > 1)

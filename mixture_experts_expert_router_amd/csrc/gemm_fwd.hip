@@ -302,6 +302,262 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused expert forward: dispatch -> GEMM1 -> GEMM2 in one persistent launch,
+// scheduled by data readiness (KOSMOS section 3.1.1 and section 3.3.1 steps
+// 3-4, on one GPU).  One queue, claimed in order:
+//   1. dispatch items: (expert, chunk of kDispRows rows); each gathers its
+//      rows from the token rows (row_route) into X_d.  The workgroup that
+//      finishes an expert's last chunk appends the expert to the ready list
+//      with one 64-bit atomic that returns both its position and the number
+//      of row blocks of all experts appended before it;
+//   2. GEMM1 items, expert by expert in ready order (the order dispatch
+//      finished them): each waits until its position is published;
+//   3. GEMM2 items, same order; each waits until every GEMM1 n-tile of its
+//      (expert, row block) has stored H.
+// Every wait is on items claimed earlier by running workgroups, and those
+// never wait on later items, so the queue drains whatever the grid size.
+// Writers publish with an agent-scope release (fence, then atomic); readers
+// acquire before touching the data.  Waits are bounded: a wait that expires
+// sets the error word and the item proceeds, so no wave can hang.
+// ---------------------------------------------------------------------------
+
+constexpr int kDispRows = 64;
+constexpr int kSpinLimit = 1 << 22;
+
+struct FusedParams {
+  FwdParams g1, g2;             // g1: X_d -> G, U, H;  g2: H -> Y
+  const uint16_t* x;            // [N][D] token rows
+  const int32_t* row_route;     // [rows_cap]
+  int K;                        // routes per token
+  int32_t* st;                  // queue state (zeroed by the planner)
+  const int32_t* fplan;         // fused plan
+  int nt1, nt2;                 // n-tiles of GEMM1 / GEMM2
+};
+
+// queue state layout (int32 units)
+__device__ __host__ __forceinline__ int st_head() { return 0; }
+__device__ __host__ __forceinline__ int st_err() { return 1; }
+__device__ __host__ __forceinline__ int st_ticket() { return 2; }   // uint64 at ints 2..3
+__device__ __host__ __forceinline__ int st_ready_e(int E) { (void)E; return 4; }
+__device__ __host__ __forceinline__ int st_ready_cum(int E) { return 4 + E; }
+__device__ __host__ __forceinline__ int st_ready_ok(int E) { return 4 + 2 * E; }
+__device__ __host__ __forceinline__ int st_rows_done(int E) { return 4 + 3 * E; }
+__device__ __host__ __forceinline__ int st_g1_done(int E) { return 4 + 4 * E; }
+
+__device__ __forceinline__ int ld_acquire(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_relaxed(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// thread 0: wait until *p >= target (bounded); false if the bound expired
+__device__ __forceinline__ bool wait_ge(const int32_t* p, int target, int32_t* err) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (ld_acquire(p) >= target) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  atomicExch(err, 1);
+  return false;
+}
+
+__device__ __forceinline__ int rows_bm(int rows) { return is_big(rows) ? 256 : 128; }
+
+// thread 0: find the ready position holding GEMM item j (units of nt tiles per
+// row block), walking forward from *pos; returns the expert and its first
+// row-block number in ready order.
+__device__ __forceinline__ void locate(const FusedParams& f, int j, int nt, int* pos, int* e_out, int* cum_out) {
+  const int E = f.g1.E;
+  int32_t* st = f.st;
+  for (;;) {
+    const int ps = *pos;
+    if (ps >= E) {   // only after an expired wait: stay in bounds, results are flagged
+      atomicExch(st + st_err(), 1);
+      *e_out = 0;
+      *cum_out = 0;
+      return;
+    }
+    wait_ge(st + st_ready_ok(E) + ps, 1, st + st_err());
+    const int e = ld_relaxed(st + st_ready_e(E) + ps);
+    const int cum = ld_relaxed(st + st_ready_cum(E) + ps);
+    const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
+    const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
+    if (j < (cum + nmb) * nt) {
+      *e_out = e;
+      *cum_out = cum;
+      return;
+    }
+    *pos = ps + 1;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
+  const uint16_t* a_src[C::A_INS];
+  const uint16_t* b_src[C::B_INS];
+  sources<C>(p, it, a_src, b_src);
+  tile::prologue<C>(lds0, a_src, b_src, p.K / tile::kBK);
+  f32x4_t acc[C::TM][C::TN];
+  tile::mainloop<C>(smem, lds0, a_src, b_src, p.K / tile::kBK, acc);
+  epilogue<C>(p, it, acc);
+}
+
+__device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ int s_info[4];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int E = f.g1.E;
+  int32_t* st = f.st;
+  const int ND = f.fplan[0], NMB = f.fplan[1], L = f.fplan[2];
+  const int32_t* dorder = f.fplan + 3;
+  const int32_t* dpref = f.fplan + 3 + E;
+  const int N1 = NMB * f.nt1, N2 = NMB * f.nt2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ld = 0, p1 = 0, p2 = 0;   // walk positions (claims only increase)
+
+  for (;;) {
+    if (tid == 0) s_info[0] = atomicAdd(st + st_head(), 1);
+    __syncthreads();
+    const int item = s_info[0];
+    __syncthreads();
+    if (item >= ND + N1 + N2) break;
+
+    if (item < ND) {
+      // ---- dispatch chunk: gather token rows into X_d ------------------------
+      while (ld + 1 < L && dpref[ld + 1] <= item) ++ld;
+      const int e = dorder[ld];
+      const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
+      const int r0 = m0 + (item - dpref[ld]) * kDispRows, r1 = min(r0 + kDispRows, m1);
+      const int D = f.g1.K, nvec = D >> 3;
+      for (int i = r0 + wave; i < r1; i += 8) {
+        const int t = f.row_route[i] / f.K;
+        const uint16_t* src = f.x + (int64_t)t * D;
+        uint16_t* dst = const_cast<uint16_t*>(f.g1.a) + (int64_t)i * D;
+        for (int v0 = 0; v0 < nvec; v0 += 4 * 64) {
+          uint4 r[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int v = v0 + lane + j * 64;
+            if (v < nvec) r[j] = ldg16(src + v * 8);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int v = v0 + lane + j * 64;
+            if (v < nvec) stg16(dst + v * 8, r[j]);
+          }
+        }
+      }
+      release_fence();
+      __syncthreads();
+      if (tid == 0) {
+        const int m = m1 - m0;
+        const int done = atomicAdd(st + st_rows_done(E) + e, r1 - r0) + (r1 - r0);
+        if (done == m) {
+          const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
+          const unsigned long long t =
+              atomicAdd(reinterpret_cast<unsigned long long*>(st + st_ticket()), (1ull << 32) | (unsigned)nmb);
+          const int pos = (int)(t >> 32), cum = (int)(t & 0xffffffffu);
+          __hip_atomic_store(st + st_ready_e(E) + pos, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(st + st_ready_cum(E) + pos, cum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(st + st_ready_ok(E) + pos, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if (item < ND + N1) {
+      // ---- GEMM1 tile, experts in ready order ---------------------------------
+      const int j = item - ND;
+      if (tid == 0) {
+        int e, cum;
+        locate(f, j, f.nt1, &p1, &e, &cum);
+        s_info[1] = e;
+        s_info[2] = cum;
+      }
+      __syncthreads();
+      acquire_fence();
+      const int e = s_info[1], cum = s_info[2];
+      const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
+      const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
+      const int w = j - cum * f.nt1, n_t = w / nmb, mb = w - n_t * nmb;
+      Item it{e, m0 + mb * bm, m1, n_t * BigTile<true>::NCOL, is_big(m1 - m0), true};
+      if (it.big) run_plain<BigTile<true>>(f.g1, smem, lds0, it);
+      else run_plain<SmallTile<true>>(f.g1, smem, lds0, it);
+      release_fence();
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(st + st_g1_done(E) + cum + mb, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // ---- GEMM2 tile, gated on its GEMM1 row block ----------------------------
+      const int j = item - ND - N1;
+      if (tid == 0) {
+        int e, cum;
+        locate(f, j, f.nt2, &p2, &e, &cum);
+        const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
+        const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
+        const int mb = (j - cum * f.nt2) % nmb;
+        wait_ge(st + st_g1_done(E) + cum + mb, f.nt1, st + st_err());
+        s_info[1] = e;
+        s_info[2] = cum;
+      }
+      __syncthreads();
+      acquire_fence();
+      const int e = s_info[1], cum = s_info[2];
+      const int m0 = f.g2.offsets[e], m1 = f.g2.offsets[e + 1];
+      const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
+      const int w = j - cum * f.nt2, n_t = w / nmb, mb = w - n_t * nmb;
+      Item it{e, m0 + mb * bm, m1, n_t * BigTile<false>::NCOL, is_big(m1 - m0), true};
+      if (it.big) run_plain<BigTile<false>>(f.g2, smem, lds0, it);
+      else run_plain<SmallTile<false>>(f.g2, smem, lds0, it);
+    }
+  }
+}
+
+// Fused planner: one workgroup.  Dispatch order = the GEMM planner's expert
+// order; fplan = {ND, NMB, L, order[E], dispatch prefix[E+1]}.  Zeroes the
+// queue state for this launch.
+__global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restrict__ offsets, int E, int max_mb,
+                                                          const int32_t* __restrict__ gplan,
+                                                          int32_t* __restrict__ fplan, int32_t* __restrict__ st) {
+  __shared__ int s_w[16], s_m[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int L = gplan[1];
+  int chunks = 0, mbs = 0;
+  if (t < L) {
+    const int e = gplan[2 + t];
+    const int m = offsets[e + 1] - offsets[e];
+    chunks = (m + kDispRows - 1) / kDispRows;
+    mbs = (m + rows_bm(m) - 1) / rows_bm(m);
+  }
+  int inc = chunks, incm = mbs;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(inc, o, 64), b = __shfl_up(incm, o, 64);
+    if (lane >= o) { inc += a; incm += b; }
+  }
+  if (lane == 63) { s_w[wv] = inc; s_m[wv] = incm; }
+  __syncthreads();
+  if (t == 0) {
+    int r = 0, rm = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int a = s_w[w], b = s_m[w];
+      s_w[w] = r; s_m[w] = rm;
+      r += a; rm += b;
+    }
+    fplan[0] = r;
+    fplan[1] = rm;
+    fplan[2] = L;
+    fplan[3 + E + L] = r;
+  }
+  __syncthreads();
+  if (t < L) {
+    fplan[3 + t] = gplan[2 + t];
+    fplan[3 + E + t] = inc - chunks + s_w[wv];
+  }
+  for (int i = t; i < 4 + 4 * E + max_mb; i += blockDim.x) st[i] = 0;
+}
+
 }  // namespace
 
 size_t gemm_fwd_plan_ints(int64_t E) { return (size_t)(4 + 2 * E + 64); }
@@ -326,6 +582,57 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s) {
   const int ncol = f.swiglu ? BigTile<true>::NCOL : BigTile<false>::NCOL;
   p.n_tiles = (p.N + ncol - 1) / ncol;
   return f.swiglu ? run_fwd<true>(p, plan, s) : run_fwd<false>(p, plan, s);
+}
+
+// Workspace of the fused forward: GEMM plan, fused plan and queue state.
+size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E) {
+  const int64_t max_mb = rows_cap / 128 + E + 1;
+  return (size_t)(16 + gemm_fwd_plan_ints(E) + (3 + 2 * E + 8) + (4 + 4 * E + max_mb) + 64);
+}
+
+hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s) {
+  FusedParams f{};
+  FwdParams& g1 = f.g1;
+  g1.offsets = x.offsets;
+  g1.E = (int)x.E;
+  g1.N = (int)x.H;
+  g1.K = (int)x.D;
+  g1.a = (const uint16_t*)x.xd;
+  g1.b0 = (const uint16_t*)x.w_gate;
+  g1.b1 = (const uint16_t*)x.w_up;
+  g1.c0 = (uint16_t*)x.g;
+  g1.c1 = (uint16_t*)x.u;
+  g1.c2 = (uint16_t*)x.h;
+  FwdParams& g2 = f.g2;
+  g2.offsets = x.offsets;
+  g2.E = (int)x.E;
+  g2.N = (int)x.D;
+  g2.K = (int)x.H;
+  g2.a = (const uint16_t*)x.h;
+  g2.b0 = (const uint16_t*)x.w_down;
+  g2.c0 = (uint16_t*)x.y;
+  f.x = (const uint16_t*)x.x;
+  f.row_route = x.row_route;
+  f.K = (int)x.K;
+  f.nt1 = (int)((x.H + BigTile<true>::NCOL - 1) / BigTile<true>::NCOL);
+  f.nt2 = (int)((x.D + BigTile<false>::NCOL - 1) / BigTile<false>::NCOL);
+  int32_t* gplan = ws + 16;
+  int32_t* fplan = gplan + gemm_fwd_plan_ints(x.E);
+  int32_t* st = fplan + (3 + 2 * x.E + 8);
+  st = (int32_t*)(((uintptr_t)st + 7) & ~(uintptr_t)7);   // 8-byte aligned ticket
+  f.st = st;
+  f.fplan = fplan;
+  const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
+  plan_fwd_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
+  plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, fplan, st);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, experts_fwd_fused_kernel, 512, 0);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) per_cu = 1;
+  experts_fwd_fused_kernel<<<cus * per_cu, 512, 0, s>>>(f);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -79,7 +79,26 @@ hipError_t launch_gemm_fwd_bf16(const GemmFwd& f, int32_t* table, hipStream_t s)
 hipError_t launch_gemm_dgrad_bf16(const GemmBwd& b, int32_t* table, hipStream_t s);
 hipError_t launch_gemm_wgrad_bf16(const GemmBwd& b, const void* dc, void* db, hipStream_t s);
 
+// fused bf16 expert forward: dispatch -> GEMM1 (SwiGLU) -> GEMM2 in one
+// persistent launch (gemm_fwd.hip)
+struct ExpertsFwd {
+  int64_t E, K, D, H, rows_cap;
+  const int32_t* offsets;
+  const int32_t* row_route;
+  const void* x;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* xd;
+  void* g;
+  void* u;
+  void* h;
+  void* y;
+};
+
 // gemm_fwd.hip (persistent bf16 forward; k_dim % 64 == 0, n_dim % 16 == 0)
+size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E);
+hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s);
 size_t gemm_fwd_plan_ints(int64_t E);
 bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim);
 hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s);

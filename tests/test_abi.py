@@ -81,6 +81,8 @@ def test_null_align_workspace_errors():
     a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0)
     sv = M.LayerSaved()
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -1
+    a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0, 2)             # unknown schedule
+    assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -3
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -158,6 +158,18 @@ def test_full_size_forward_bf16(name):
     rows, outs = _token_rows(wl, inp, tokens, idx, prob, d, _bf16_expert(inp))
     _assert_rows(sv, rows, d, ("g", "u", "h", "y"), assert_bf16_close)
     assert_bf16_close(vals(layer.out)[tokens], outs, "out")
+    # the whole-layer call with dispatch and both GEMMs in one persistent
+    # launch scheduled by readiness reproduces the staged results bit for bit
+    staged = {k: bits(t) for k, t in (("out", layer.out), ("h", sv["h"]), ("y", sv["y"]))}
+    n = int(o[-1])
+    for t in (layer.out, sv["xd"], sv["g"], sv["u"], sv["h"], sv["y"]):
+        t.view(torch.int16).fill_(0x7FA0)
+    layer.sched = M.MOE_SCHED_READY
+    layer.forward(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(layer.out), staged["out"])
+    assert np.array_equal(bits(sv["h"])[:n], staged["h"][:n])
+    assert np.array_equal(bits(sv["y"])[:n], staged["y"][:n])
 
 
 def test_full_size_forward_mxfp8():

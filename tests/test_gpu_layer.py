@@ -65,14 +65,15 @@ LAYER_CASES = {
 }
 
 
+@pytest.mark.parametrize("sched", [M.MOE_SCHED_STAGED, M.MOE_SCHED_READY])
 @pytest.mark.parametrize("name", list(LAYER_CASES))
-def test_layer_fwd_bf16(name):
+def test_layer_fwd_bf16(name, sched):
     wl = LAYER_CASES[name]
-    print(f"layer fwd {name}", flush=True)
+    print(f"layer fwd {name} sched={sched}", flush=True)
     inp = S.make_inputs(wl, 1)
     w, _ = _weights(inp)
     drop = dev(inp.drop) if inp.drop is not None else None
-    layer = M.MoeLayer(w, wl.N, wl.K, drop=drop)
+    layer = M.MoeLayer(w, wl.N, wl.K, drop=drop, sched=sched)
     out = layer.forward(dev_bf16(inp.x))
     torch.cuda.synchronize()
     ref = O.layer_fwd(inp.x, inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K, drop=inp.drop)
@@ -150,13 +151,14 @@ def test_weight_prequantization_bit_exact():
         assert np.array_equal(host(q[k]), ref[k]), k
 
 
-def test_layer_deterministic_and_overwrites_outputs():
+@pytest.mark.parametrize("sched", [M.MOE_SCHED_STAGED, M.MOE_SCHED_READY])
+def test_layer_deterministic_and_overwrites_outputs(sched):
     """Bitwise identical results run to run, with every output poisoned in
     between (catches unwritten elements and races)."""
     wl = LAYER_CASES["qwen3_shape_small"]
     inp = S.make_inputs(wl, 5)
     w, _ = _weights(inp)
-    layer = M.MoeLayer(w, wl.N, wl.K, drop=dev(inp.drop), with_bwd=True)
+    layer = M.MoeLayer(w, wl.N, wl.K, drop=dev(inp.drop), with_bwd=True, sched=sched)
     x = dev_bf16(inp.x)
     dout = dev_bf16(inp.dout)
     runs = []
