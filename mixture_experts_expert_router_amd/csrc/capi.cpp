@@ -65,10 +65,16 @@ size_t table_bytes(int64_t rows_cap, int64_t E) {
   return round_up(m, 256);
 }
 
-// bf16 forward GEMM: the persistent kernel where its shape rule holds
+// forward GEMM: the persistent kernel where its shape and alignment rule
+// holds, else the m-tile kernels
 hipError_t gemm_fwd_bf16(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
-  if (moe::gemm_fwd_fast_ok(f.k_dim, f.n_dim)) return moe::launch_gemm_fwd_fast(f, ws, s);
+  if (moe::gemm_fwd_fast_ok(f, false)) return moe::launch_gemm_fwd_fast(f, false, ws, s);
   return moe::launch_gemm_fwd_bf16(f, ws, s);
+}
+
+hipError_t gemm_fwd_mxfp8(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
+  if (moe::gemm_fwd_fast_ok(f, true)) return moe::launch_gemm_fwd_fast(f, true, ws, s);
+  return moe::launch_gemm_fwd_mxfp8(f, ws, s);
 }
 
 size_t route_bytes(const moe_dims& d) { return round_up(moe::route_workspace_bytes(d.N, d.E, d.K), 256); }
@@ -269,7 +275,7 @@ int moe_grouped_gemm_fwd(const moe_gemm_fwd_args* g, void* ws, size_t ws_bytes, 
                  g->b0_scales, g->b1, g->b1_scales, g->c0, g->c1, g->act, g->act_q,
                  g->act_scales, sw};
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = mx ? moe::launch_gemm_fwd_mxfp8(f, (int32_t*)ws, s)
+  hipError_t e = mx ? gemm_fwd_mxfp8(f, (int32_t*)ws, s)
                     : gemm_fwd_bf16(f, (int32_t*)ws, s);
   if (e == hipSuccess && !mx && g->act_q)
     e = moe::launch_quantize_rows(g->act, g->rows_cap, g->n_dim, g->act_q, g->act_scales, s);
@@ -383,10 +389,10 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
       e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D, sv->xd_q, d.D / 32, sv->xd_s, s);
     moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
                     a->wu_s, sv->g, sv->u, sv->h, sv->h_q, sv->h_s, true};
-    if (e == hipSuccess) e = moe::launch_gemm_fwd_mxfp8(g1, table, s);
+    if (e == hipSuccess) e = gemm_fwd_mxfp8(g1, table, s);
     moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
-    if (e == hipSuccess) e = moe::launch_gemm_fwd_mxfp8(g2, table, s);
+    if (e == hipSuccess) e = gemm_fwd_mxfp8(g2, table, s);
   } else if (a->sched == MOE_SCHED_READY && d.align == 1 && moe::gemm_fwd_fast_ok(d.D, d.H) &&
              moe::gemm_fwd_fast_ok(d.H, d.D)) {
     // dispatch, GEMM1 and GEMM2 in one persistent launch scheduled by readiness

@@ -23,6 +23,13 @@
 //
 // The MFMA main loop (direct-to-LDS operand ring) is the shared tile engine;
 // eight waves per workgroup (two per SIMD).
+//
+// The same kernel runs the block-scaled MXFP8 variant (OLMo-core Appendix A,
+// A.5 eq. 87; KOSMOS section 2.2): E4M3 operands with one E8M0 scale per 32
+// contraction elements of each row, on the scaled 16x16x128 MFMA, fp32
+// accumulation and the same bf16 outputs; GEMM1's epilogue also stores H
+// quantized row-wise along its columns (blocks of 32, KOSMOS section 3.3.1
+// step 3), the A operand of the MXFP8 GEMM2.
 #include "common.h"
 #include "launch.h"
 #include "mfma_tile.h"
@@ -38,13 +45,19 @@ struct FwdParams {
   const int32_t* plan;      // planner output (layout below)
   int32_t* head;            // queue head counter
   int E, N, K;              // N output columns per weight, K contraction
+  int nk;                   // contraction steps (128 bytes of a row each)
   int n_tiles;              // ceil(N / NCOL)
-  const uint16_t* a;        // [rows][K]
-  const uint16_t* b0;       // [E][N][K]
-  const uint16_t* b1;       // DUAL: [E][N][K]
-  uint16_t* c0;             // [rows][N]  (G or Y)
+  const uint8_t* a;         // [rows][K]      bf16 or E4M3
+  const uint8_t* b0;        // [E][N][K]
+  const uint8_t* b1;        // DUAL: [E][N][K]
+  const uint8_t* as;        // MX: E8M0 [rows][K/32]
+  const uint8_t* bs0;       // MX: E8M0 [E][N][K/32]
+  const uint8_t* bs1;       // MX, DUAL
+  uint16_t* c0;             // [rows][N]  (G or Y), bf16
   uint16_t* c1;             // DUAL: U
   uint16_t* c2;             // DUAL: H
+  uint8_t* hq;              // DUAL, optional: H as E4M3 [rows][N]
+  uint8_t* hs;              //   and its E8M0 scales [rows][N/32]
 };
 
 // plan layout (int32): [0] total items, [1] number of listed experts L,
@@ -59,12 +72,17 @@ struct Item {
 };
 
 // The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
-template <bool DUAL>
-using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL>;     // 2 x 64 KB ring
-template <bool DUAL>
-using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL>;   // 3 x 48 KB ring
-constexpr int kLdsBytes = 3 * (128 + 256) * tile::kRB;     // the larger ring
-static_assert(kLdsBytes >= 2 * (256 + 256) * tile::kRB, "ring size");
+template <bool DUAL, bool MX = false>
+using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL, MX>;     // 2 x 64 KB ring (+2 x 2 KB scales)
+template <bool DUAL, bool MX = false>
+using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB ring (+3 x 2 KB scales)
+template <bool MX>
+constexpr int lds_bytes() {
+  constexpr int s = SmallTile<true, MX>::NS * SmallTile<true, MX>::STAGE;
+  constexpr int b = BigTile<true, MX>::NS * BigTile<true, MX>::STAGE;
+  return s > b ? s : b;
+}
+constexpr int kLdsBytes = lds_bytes<false>();
 
 __device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
 
@@ -98,39 +116,64 @@ __device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) 
 }
 
 // This lane's DMA source pointers for an item (rows past the expert's segment
-// or columns past N load a clamped valid row and are never stored).
+// or columns past N load a clamped valid row and are never stored).  MX: the
+// scale row of this thread (thread t loads stage scale row t: A rows, then B
+// rows, then padding that points at any valid row).
 template <class C>
-__device__ __forceinline__ void sources(const FwdParams& p, const Item& it, const uint16_t** a_src,
-                                        const uint16_t** b_src) {
+__device__ __forceinline__ void sources(const FwdParams& p, const Item& it, const uint8_t** a_src,
+                                        const uint8_t** b_src, const uint8_t** s_src) {
   using namespace tile;
   const int wave = threadIdx.x >> 6;
-  const int64_t K = p.K;
+  const int64_t RB = (int64_t)p.K * (C::MX ? 1 : 2);   // row bytes
   const int d_chunk = dma_chunk();
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const int row = min(it.m_start + dma_row(wave, C::A_INS, q), it.m1 - 1);
-    a_src[q] = p.a + (int64_t)row * K + d_chunk * 8;
+    a_src[q] = p.a + (int64_t)row * RB + d_chunk * 16;
   }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
     const int r = dma_row(wave, C::B_INS, q);
-    const uint16_t* base = p.b0;
+    const uint8_t* base = p.b0;
     int col = it.n0 + r;
     if (C::DUAL && r >= C::BN / 2) {
       base = p.b1;
       col = it.n0 + r - C::BN / 2;
     }
     col = min(col, p.N - 1);
-    b_src[q] = base + ((int64_t)it.e * p.N + col) * K + d_chunk * 8;
+    b_src[q] = base + ((int64_t)it.e * p.N + col) * RB + d_chunk * 16;
+  }
+  if constexpr (C::MX) {
+    const int64_t KS = p.K / 32;
+    const int c = threadIdx.x;
+    const bool in_a = c < C::BM, in_b = c >= C::BM && c < C::BM + C::BN;
+    const int r = c - C::BM;
+    const bool up = C::DUAL && in_b && r >= C::BN / 2;
+    const int col = min(it.n0 + (up ? r - C::BN / 2 : r), p.N - 1);
+    const int64_t a_off = (int64_t)min(it.m_start + (in_a ? c : 0), it.m1 - 1) * KS;
+    const int64_t b_off = ((int64_t)it.e * p.N + col) * KS;
+    const uint8_t* bsrc = (up ? p.bs1 : p.bs0) + b_off;
+    *s_src = in_b ? bsrc : p.as + a_off;
+  } else {
+    *s_src = nullptr;
   }
 }
 
 template <class C>
 __device__ __forceinline__ void start(const FwdParams& p, uint32_t lds0, const Item& it) {
-  const uint16_t* a_src[C::A_INS];
-  const uint16_t* b_src[C::B_INS];
-  sources<C>(p, it, a_src, b_src);
-  tile::prologue<C>(lds0, a_src, b_src, p.K / tile::kBK);
+  const uint8_t* a_src[C::A_INS];
+  const uint8_t* b_src[C::B_INS];
+  const uint8_t* s_src;
+  sources<C>(p, it, a_src, b_src, &s_src);
+  tile::prologue<C>(lds0, a_src, b_src, s_src, p.nk);
+}
+
+template <class C>
+__device__ __forceinline__ void mainloop_any(const uint8_t* smem, uint32_t lds0, const uint8_t* const* a_src,
+                                             const uint8_t* const* b_src, const uint8_t* s_src, int nk,
+                                             f32x4_t (&acc)[C::TM][C::TN]) {
+  if constexpr (C::MX) tile::mainloop_mx<C>(smem, lds0, a_src, b_src, s_src, nk, acc);
+  else tile::mainloop<C>(smem, lds0, a_src, b_src, nk, acc);
 }
 
 template <class C>
@@ -156,22 +199,52 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
             make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
       }
     } else {
+      uint32_t hw[TN / 2][2];
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
         const int n = it.n0 + wn * (WN / 2) + j * 16 + 4 * lg;
-        if (n >= p.N) continue;
         const f32x4_t a = acc[i][j], b = acc[i][j + TN / 2];
         const uint32_t gw0 = pack_bf16x2(a[0], a[1]), gw1 = pack_bf16x2(a[2], a[3]);
         const uint32_t uw0 = pack_bf16x2(b[0], b[1]), uw1 = pack_bf16x2(b[2], b[3]);
-        const int64_t off = row * p.N + n;
-        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(gw0, gw1);
-        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(uw0, uw1);
         const float g0 = bf16lo(gw0), g1 = bf16hi(gw0), g2 = bf16lo(gw1), g3 = bf16hi(gw1);
         const float h0 = g0 * sigmoidf_(g0) * bf16lo(uw0);
         const float h1 = g1 * sigmoidf_(g1) * bf16hi(uw0);
         const float h2 = g2 * sigmoidf_(g2) * bf16lo(uw1);
         const float h3 = g3 * sigmoidf_(g3) * bf16hi(uw1);
-        *reinterpret_cast<uint2*>(p.c2 + off) = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+        hw[j][0] = pack_bf16x2(h0, h1);
+        hw[j][1] = pack_bf16x2(h2, h3);
+        if (n >= p.N) continue;
+        const int64_t off = row * p.N + n;
+        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(gw0, gw1);
+        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(uw0, uw1);
+        *reinterpret_cast<uint2*>(p.c2 + off) = make_uint2(hw[j][0], hw[j][1]);
+      }
+      if (p.hq) {
+        // a 32-column block of H is fragments (j, j+1) over the four lane
+        // groups of one row (N % 32 == 0, so a block is all in or all out)
+#pragma unroll
+        for (int j = 0; j < TN / 2; j += 2) {
+          const float v[8] = {bf16lo(hw[j][0]),     bf16hi(hw[j][0]),     bf16lo(hw[j][1]),     bf16hi(hw[j][1]),
+                              bf16lo(hw[j + 1][0]), bf16hi(hw[j + 1][0]), bf16lo(hw[j + 1][1]), bf16hi(hw[j + 1][1])};
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          const int code = e8m0_code(amax);
+          uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            q0 |= e4m3_from_scaled(v[q], code - 127) << (8 * q);
+            q1 |= e4m3_from_scaled(v[4 + q], code - 127) << (8 * q);
+          }
+          const int nb = it.n0 + wn * (WN / 2) + j * 16;
+          if (nb >= p.N) continue;
+          uint8_t* qrow = p.hq + row * p.N + nb + 4 * lg;
+          *reinterpret_cast<uint32_t*>(qrow) = q0;
+          *reinterpret_cast<uint32_t*>(qrow + 16) = q1;
+          if (lg == 0) p.hs[row * (p.N / 32) + nb / 32] = (uint8_t)code;
+        }
       }
     }
   }
@@ -183,33 +256,36 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
 template <class C, bool DUAL>
 __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int* s_item,
                                          int& li, const Item& it) {
-  const uint16_t* a_src[C::A_INS];
-  const uint16_t* b_src[C::B_INS];
-  sources<C>(p, it, a_src, b_src);
+  const uint8_t* a_src[C::A_INS];
+  const uint8_t* b_src[C::B_INS];
+  const uint8_t* s_src;
+  sources<C>(p, it, a_src, b_src, &s_src);
   f32x4_t acc[C::TM][C::TN];
-  tile::mainloop<C>(smem, lds0, a_src, b_src, p.K / tile::kBK, acc);
+  mainloop_any<C>(smem, lds0, a_src, b_src, s_src, p.nk, acc);
   const Item next = claim<DUAL>(p, s_item, li);
   if (next.valid) {
-    if (next.big) start<BigTile<DUAL>>(p, lds0, next);
-    else start<SmallTile<DUAL>>(p, lds0, next);
+    if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
+    else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
   }
   epilogue<C>(p, it, acc);
   return next;
 }
 
-template <bool DUAL>
+template <bool DUAL, bool MX>
 __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<MX>()];
   __shared__ int s_item;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  using Big = BigTile<DUAL, MX>;
+  using Small = SmallTile<DUAL, MX>;
   int li = 0;
   Item it = claim<DUAL>(p, &s_item, li);
   if (!it.valid) return;
-  if (it.big) start<BigTile<DUAL>>(p, lds0, it);
-  else start<SmallTile<DUAL>>(p, lds0, it);
+  if (it.big) start<Big>(p, lds0, it);
+  else start<Small>(p, lds0, it);
   while (it.valid) {
-    if (it.big) it = run_item<BigTile<DUAL>, DUAL>(p, smem, lds0, &s_item, li, it);
-    else it = run_item<SmallTile<DUAL>, DUAL>(p, smem, lds0, &s_item, li, it);
+    if (it.big) it = run_item<Big, DUAL>(p, smem, lds0, &s_item, li, it);
+    else it = run_item<Small, DUAL>(p, smem, lds0, &s_item, li, it);
   }
 }
 
@@ -288,10 +364,10 @@ __global__ __launch_bounds__(1024) void plan_fwd_kernel(const int32_t* __restric
   }
 }
 
-template <bool DUAL>
+template <bool DUAL, bool MX>
 hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
   plan_fwd_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, p.n_tiles, plan, p.head);
-  auto kern = gemm_fwd_kernel<DUAL>;
+  auto kern = gemm_fwd_kernel<DUAL, MX>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -394,12 +470,13 @@ __device__ __forceinline__ void locate(const FusedParams& f, int j, int nt, int*
 
 template <class C>
 __device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
-  const uint16_t* a_src[C::A_INS];
-  const uint16_t* b_src[C::B_INS];
-  sources<C>(p, it, a_src, b_src);
-  tile::prologue<C>(lds0, a_src, b_src, p.K / tile::kBK);
+  const uint8_t* a_src[C::A_INS];
+  const uint8_t* b_src[C::B_INS];
+  const uint8_t* s_src;
+  sources<C>(p, it, a_src, b_src, &s_src);
+  tile::prologue<C>(lds0, a_src, b_src, s_src, p.nk);
   f32x4_t acc[C::TM][C::TN];
-  tile::mainloop<C>(smem, lds0, a_src, b_src, p.K / tile::kBK, acc);
+  mainloop_any<C>(smem, lds0, a_src, b_src, s_src, p.nk, acc);
   epilogue<C>(p, it, acc);
 }
 
@@ -436,7 +513,7 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
       for (int i = r0 + wave; i < r1; i += 8) {
         const int t = f.row_route[i] / f.K;
         const uint16_t* src = f.x + (int64_t)t * D;
-        uint16_t* dst = const_cast<uint16_t*>(f.g1.a) + (int64_t)i * D;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(f.g1.a)) + (int64_t)i * D;
         for (int v0 = 0; v0 < nvec; v0 += 4 * 64) {
           uint4 r[4];
 #pragma unroll
@@ -562,26 +639,47 @@ __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restr
 
 size_t gemm_fwd_plan_ints(int64_t E) { return (size_t)(4 + 2 * E + 64); }
 
+namespace {
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+}  // namespace
+
+// bf16: K % 64 == 0 (whole 128-byte steps), N % 16 == 0; MXFP8: K % 128 == 0,
+// N % 32 == 0.  Operands 16-byte aligned, scales 4-byte aligned.
+bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx) {
+  if (f.k_dim % (mx ? 128 : 64) || f.n_dim % (mx ? 32 : 16)) return false;
+  if (!aligned(f.a, 16) || !aligned(f.b0, 16) || (f.swiglu && !aligned(f.b1, 16))) return false;
+  if (mx && (!aligned(f.a_scales, 4) || !aligned(f.b0_scales, 4) || (f.swiglu && !aligned(f.b1_scales, 4))))
+    return false;
+  return true;
+}
+
 bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim) { return k_dim % tile::kBK == 0 && n_dim % 16 == 0; }
 
-hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s) {
+hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStream_t s) {
   FwdParams p{};
   p.offsets = f.offsets;
   p.E = (int)f.E;
   p.N = (int)f.n_dim;
   p.K = (int)f.k_dim;
-  p.a = (const uint16_t*)f.a;
-  p.b0 = (const uint16_t*)f.b0;
-  p.b1 = (const uint16_t*)f.b1;
+  p.nk = (int)(f.k_dim * (mx ? 1 : 2) / tile::kRB);
+  p.a = (const uint8_t*)f.a;
+  p.b0 = (const uint8_t*)f.b0;
+  p.b1 = (const uint8_t*)f.b1;
+  p.as = f.a_scales;
+  p.bs0 = f.b0_scales;
+  p.bs1 = f.b1_scales;
   p.c0 = (uint16_t*)f.c0;
   p.c1 = (uint16_t*)f.c1;
   p.c2 = (uint16_t*)f.act;
+  p.hq = (mx && f.swiglu) ? f.act_q : nullptr;   // bf16 callers quantize H separately
+  p.hs = (mx && f.swiglu) ? f.act_scales : nullptr;
   p.head = ws;
   int32_t* plan = ws + 16;
   p.plan = plan;
   const int ncol = f.swiglu ? BigTile<true>::NCOL : BigTile<false>::NCOL;
   p.n_tiles = (p.N + ncol - 1) / ncol;
-  return f.swiglu ? run_fwd<true>(p, plan, s) : run_fwd<false>(p, plan, s);
+  if (mx) return f.swiglu ? run_fwd<true, true>(p, plan, s) : run_fwd<false, true>(p, plan, s);
+  return f.swiglu ? run_fwd<true, false>(p, plan, s) : run_fwd<false, false>(p, plan, s);
 }
 
 // Workspace of the fused forward: GEMM plan, fused plan and queue state.
@@ -597,9 +695,10 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   g1.E = (int)x.E;
   g1.N = (int)x.H;
   g1.K = (int)x.D;
-  g1.a = (const uint16_t*)x.xd;
-  g1.b0 = (const uint16_t*)x.w_gate;
-  g1.b1 = (const uint16_t*)x.w_up;
+  g1.nk = (int)(x.D * 2 / tile::kRB);
+  g1.a = (const uint8_t*)x.xd;
+  g1.b0 = (const uint8_t*)x.w_gate;
+  g1.b1 = (const uint8_t*)x.w_up;
   g1.c0 = (uint16_t*)x.g;
   g1.c1 = (uint16_t*)x.u;
   g1.c2 = (uint16_t*)x.h;
@@ -608,8 +707,9 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   g2.E = (int)x.E;
   g2.N = (int)x.D;
   g2.K = (int)x.H;
-  g2.a = (const uint16_t*)x.h;
-  g2.b0 = (const uint16_t*)x.w_down;
+  g2.nk = (int)(x.H * 2 / tile::kRB);
+  g2.a = (const uint8_t*)x.h;
+  g2.b0 = (const uint8_t*)x.w_down;
   g2.c0 = (uint16_t*)x.y;
   f.x = (const uint16_t*)x.x;
   f.row_route = x.row_route;

@@ -96,12 +96,15 @@ struct ExpertsFwd {
   void* y;
 };
 
-// gemm_fwd.hip (persistent bf16 forward; k_dim % 64 == 0, n_dim % 16 == 0)
+// gemm_fwd.hip: persistent forward grouped GEMM, bf16 or MXFP8 (shape and
+// alignment rule in gemm_fwd_fast_ok), and the fused bf16 expert forward
+// (k_dim % 64 == 0, n_dim % 16 == 0 for both of its GEMMs)
 size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E);
 hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s);
 size_t gemm_fwd_plan_ints(int64_t E);
 bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim);
-hipError_t launch_gemm_fwd_fast(const GemmFwd& f, int32_t* ws, hipStream_t s);
+bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx);
+hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStream_t s);
 
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);

@@ -49,20 +49,20 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
   const int m_start = mb * C::BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d_chunk = dma_chunk();
-  const uint16_t* a_src[C::A_INS];
-  const uint16_t* b_src[C::B_INS];
+  const uint8_t* a_src[C::A_INS];
+  const uint8_t* b_src[C::B_INS];
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const int row = min(m_start + dma_row(wave, C::A_INS, q), p.N - 1);
-    a_src[q] = p.x + (int64_t)row * p.D + (int64_t)k0 * kBK + d_chunk * 8;
+    a_src[q] = reinterpret_cast<const uint8_t*>(p.x + (int64_t)row * p.D + (int64_t)k0 * kBK) + d_chunk * 16;
   }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
     const int col = min(n0 + dma_row(wave, C::B_INS, q), p.E - 1);
-    b_src[q] = p.w + (int64_t)col * p.D + (int64_t)k0 * kBK + d_chunk * 8;
+    b_src[q] = reinterpret_cast<const uint8_t*>(p.w + (int64_t)col * p.D + (int64_t)k0 * kBK) + d_chunk * 16;
   }
   f32x4_t acc[C::TM][C::TN];
-  prologue<C>(lds0, a_src, b_src, k1 - k0);
+  prologue<C>(lds0, a_src, b_src, nullptr, k1 - k0);
   mainloop<C>(smem, lds0, a_src, b_src, k1 - k0, acc);
 
   // lane holds row i*16 + l16 (one wave row), columns wn*WN + j*16 + 4*lg + r

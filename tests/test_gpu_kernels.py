@@ -312,8 +312,19 @@ def test_grouped_gemm_bwd_bf16(case):
             assert np.all(bits(r1["db0"])[e] == 0)
 
 
-@pytest.mark.parametrize("case", [((0, 32, 160, 64, 288), 256, 128), ((320, 96), 512, 256),
-                                  ((32,), 128, 64)], ids=lambda c: f"{len(c[0])}e-k{c[1]}-n{c[2]}")
+MX_GEMM_CASES = [
+    ((0, 32, 160, 64, 288), 256, 128),
+    ((320, 96), 512, 256),
+    ((32,), 128, 64),
+    # 256-row and 128-row tiles side by side, partial n-tiles, empty experts
+    ((256, 0, 64, 600, 1, 0, 33), 384, 160),
+    ((0, 0, 1000), 128, 96),
+    # k % 128 != 0: the m-tile kernel
+    ((96, 7), 160, 64),
+]
+
+
+@pytest.mark.parametrize("case", MX_GEMM_CASES, ids=lambda c: f"{len(c[0])}e-k{c[1]}-n{c[2]}")
 def test_grouped_gemm_fwd_mxfp8(case):
     """Block-scaled product of quantized operands (eq. 87) against the oracle's
     dequantized float64 product, both from the same synthetic bf16 sources."""
@@ -347,3 +358,6 @@ def test_grouped_gemm_fwd_mxfp8(case):
     assert_bf16_close(vals(H)[:n], refH[:n], "mx H")
     rq, rs = O.quantize_mxfp8(refH[:n])
     assert rel_frobenius(O.dequantize_mxfp8(host(hq)[:n], host(hs)[:n]), O.dequantize_mxfp8(rq, rs)) <= 3e-2
+    # the epilogue's quantization of the H it stored is the block rule exactly
+    oq, os_ = O.quantize_mxfp8(vals(H)[:n])
+    assert np.array_equal(host(hq)[:n], oq) and np.array_equal(host(hs)[:n], os_)
