@@ -115,65 +115,60 @@ __device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) 
   return it;
 }
 
-// This lane's DMA source pointers for an item (rows past the expert's segment
-// or columns past N load a clamped valid row and are never stored).  MX: the
-// scale row of this thread (thread t loads stage scale row t: A rows, then B
-// rows, then padding that points at any valid row).
+// DMA sources of an item (rows past the expert's segment or columns past N
+// load a clamped valid row and are never stored).  A rows are offsets from
+// the item's first row; a wave's B rows all belong to one weight (gate or
+// up), offsets from that expert's matrix.  MX: thread t loads stage scale row
+// t (A rows, then B rows, then padding that reloads the item's first A row);
+// each wave's 64 scale rows come from one operand.
 template <class C>
-__device__ __forceinline__ void sources(const FwdParams& p, const Item& it, const uint8_t** a_src,
-                                        const uint8_t** b_src, const uint8_t** s_src) {
+__device__ __forceinline__ void sources(const FwdParams& p, const Item& it, tile::Src<C>& src) {
   using namespace tile;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t RB = (int64_t)p.K * (C::MX ? 1 : 2);   // row bytes
   const int d_chunk = dma_chunk();
+  src.a = uniform_ptr(p.a + (int64_t)it.m_start * RB);
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const int row = min(it.m_start + dma_row(wave, C::A_INS, q), it.m1 - 1);
-    a_src[q] = p.a + (int64_t)row * RB + d_chunk * 16;
+    src.a_off[q] = (uint32_t)((row - it.m_start) * RB + d_chunk * 16);
   }
+  const bool up_w = C::DUAL && wave * C::B_INS * C::RPI >= C::BN / 2;
+  src.b = uniform_ptr((up_w ? p.b1 : p.b0) + (int64_t)it.e * p.N * RB);
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
-    const int r = dma_row(wave, C::B_INS, q);
-    const uint8_t* base = p.b0;
-    int col = it.n0 + r;
-    if (C::DUAL && r >= C::BN / 2) {
-      base = p.b1;
-      col = it.n0 + r - C::BN / 2;
-    }
-    col = min(col, p.N - 1);
-    b_src[q] = base + ((int64_t)it.e * p.N + col) * RB + d_chunk * 16;
+    const int col = min(it.n0 + dma_row(wave, C::B_INS, q) - (up_w ? C::BN / 2 : 0), p.N - 1);
+    src.b_off[q] = (uint32_t)(col * RB + d_chunk * 16);
   }
   if constexpr (C::MX) {
     const int64_t KS = p.K / 32;
-    const int c = threadIdx.x;
-    const bool in_a = c < C::BM, in_b = c >= C::BM && c < C::BM + C::BN;
-    const int r = c - C::BM;
-    const bool up = C::DUAL && in_b && r >= C::BN / 2;
-    const int col = min(it.n0 + (up ? r - C::BN / 2 : r), p.N - 1);
-    const int64_t a_off = (int64_t)min(it.m_start + (in_a ? c : 0), it.m1 - 1) * KS;
-    const int64_t b_off = ((int64_t)it.e * p.N + col) * KS;
-    const uint8_t* bsrc = (up ? p.bs1 : p.bs0) + b_off;
-    *s_src = in_b ? bsrc : p.as + a_off;
+    const int c = threadIdx.x, c0 = wave * 64;
+    const bool in_b = c0 >= C::BM && c0 < C::BM + C::BN;
+    const bool up_s = C::DUAL && c0 >= C::BM + C::BN / 2;
+    const uint8_t* bsb = (up_s ? p.bs1 : p.bs0) + (int64_t)it.e * p.N * KS;
+    const uint8_t* asb = p.as + (int64_t)it.m_start * KS;
+    src.s = uniform_ptr(in_b ? bsb : asb);
+    const int col = min(it.n0 + c - C::BM - (up_s ? C::BN / 2 : 0), p.N - 1);
+    const int row = c0 < C::BM ? min(it.m_start + c, it.m1 - 1) : it.m_start;
+    src.s_off = in_b ? (uint32_t)(col * KS) : (uint32_t)((row - it.m_start) * KS);
   } else {
-    *s_src = nullptr;
+    src.s = nullptr;
+    src.s_off = 0;
   }
 }
 
 template <class C>
 __device__ __forceinline__ void start(const FwdParams& p, uint32_t lds0, const Item& it) {
-  const uint8_t* a_src[C::A_INS];
-  const uint8_t* b_src[C::B_INS];
-  const uint8_t* s_src;
-  sources<C>(p, it, a_src, b_src, &s_src);
-  tile::prologue<C>(lds0, a_src, b_src, s_src, p.nk);
+  tile::Src<C> src;
+  sources<C>(p, it, src);
+  tile::prologue<C>(lds0, src, p.nk);
 }
 
 template <class C>
-__device__ __forceinline__ void mainloop_any(const uint8_t* smem, uint32_t lds0, const uint8_t* const* a_src,
-                                             const uint8_t* const* b_src, const uint8_t* s_src, int nk,
+__device__ __forceinline__ void mainloop_any(const uint8_t* smem, uint32_t lds0, const tile::Src<C>& src, int nk,
                                              f32x4_t (&acc)[C::TM][C::TN]) {
-  if constexpr (C::MX) tile::mainloop_mx<C>(smem, lds0, a_src, b_src, s_src, nk, acc);
-  else tile::mainloop<C>(smem, lds0, a_src, b_src, nk, acc);
+  if constexpr (C::MX) tile::mainloop_mx<C>(smem, lds0, src, nk, acc);
+  else tile::mainloop<C>(smem, lds0, src, nk, acc);
 }
 
 template <class C>
@@ -256,12 +251,10 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
 template <class C, bool DUAL>
 __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int* s_item,
                                          int& li, const Item& it) {
-  const uint8_t* a_src[C::A_INS];
-  const uint8_t* b_src[C::B_INS];
-  const uint8_t* s_src;
-  sources<C>(p, it, a_src, b_src, &s_src);
+  tile::Src<C> src;
+  sources<C>(p, it, src);
   f32x4_t acc[C::TM][C::TN];
-  mainloop_any<C>(smem, lds0, a_src, b_src, s_src, p.nk, acc);
+  mainloop_any<C>(smem, lds0, src, p.nk, acc);
   const Item next = claim<DUAL>(p, s_item, li);
   if (next.valid) {
     if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
@@ -470,13 +463,11 @@ __device__ __forceinline__ void locate(const FusedParams& f, int j, int nt, int*
 
 template <class C>
 __device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
-  const uint8_t* a_src[C::A_INS];
-  const uint8_t* b_src[C::B_INS];
-  const uint8_t* s_src;
-  sources<C>(p, it, a_src, b_src, &s_src);
-  tile::prologue<C>(lds0, a_src, b_src, s_src, p.nk);
+  tile::Src<C> src;
+  sources<C>(p, it, src);
+  tile::prologue<C>(lds0, src, p.nk);
   f32x4_t acc[C::TM][C::TN];
-  mainloop_any<C>(smem, lds0, a_src, b_src, s_src, p.nk, acc);
+  mainloop_any<C>(smem, lds0, src, p.nk, acc);
   epilogue<C>(p, it, acc);
 }
 
@@ -644,16 +635,20 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 }  // namespace
 
 // bf16: K % 64 == 0 (whole 128-byte steps), N % 16 == 0; MXFP8: K % 128 == 0,
-// N % 32 == 0.  Operands 16-byte aligned, scales 4-byte aligned.
+// N % 32 == 0.  One expert's weight matrix under 2 GiB (32-bit DMA offsets);
+// operands 16-byte aligned, scales 4-byte aligned.
 bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx) {
   if (f.k_dim % (mx ? 128 : 64) || f.n_dim % (mx ? 32 : 16)) return false;
+  if (f.n_dim * f.k_dim * (mx ? 1 : 2) >= (int64_t(1) << 31)) return false;   // 32-bit DMA offsets
   if (!aligned(f.a, 16) || !aligned(f.b0, 16) || (f.swiglu && !aligned(f.b1, 16))) return false;
   if (mx && (!aligned(f.a_scales, 4) || !aligned(f.b0_scales, 4) || (f.swiglu && !aligned(f.b1_scales, 4))))
     return false;
   return true;
 }
 
-bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim) { return k_dim % tile::kBK == 0 && n_dim % 16 == 0; }
+bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim) {
+  return k_dim % tile::kBK == 0 && n_dim % 16 == 0 && n_dim * k_dim * 2 < (int64_t(1) << 31);
+}
 
 hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStream_t s) {
   FwdParams p{};

@@ -7,13 +7,19 @@
 // current one run.  The loads are issued from inline assembly and their
 // completion is tracked with explicit vmcnt waits: the vector-memory loads of
 // a wave complete in issue order, so "at most n outstanding" after the loads
-// of n later steps were issued means every older step has landed.  LDS rows
-// hold 64 bf16 (128 bytes); chunk c of row r sits at slot c ^ (r & 7), which,
-// measured on gfx950, keeps the 16-row fragment reads (ds_read_b128) free of
-// bank conflicts; each lane fetches the global chunk that belongs at its LDS
-// slot.  MFMA operands are fed swapped (B tile as the instruction's first
-// operand), so each lane's four accumulators are four consecutive output
-// columns of one row.
+// of n later steps were issued means every older step has landed.  Each load
+// takes a wave-uniform 64-bit base in SGPRs (advanced by one step with a
+// scalar add) and a 32-bit per-lane byte offset, which keeps the address
+// registers of a tile to one VGPR per load.
+//
+// LDS rows hold 128 bytes (64 bf16); chunk c of row r sits at slot
+// c ^ (r & 7), which, measured on gfx950, keeps the 16-row fragment reads
+// (ds_read_b128) free of bank conflicts; each lane fetches the global chunk
+// that belongs at its LDS slot.  Fragment rows are 16-row aligned, so every
+// fragment address is one per-lane base plus a compile-time offset.  MFMA
+// operands are fed swapped (B tile as the instruction's first operand), so
+// each lane's four accumulators are four consecutive output columns of one
+// row.
 //
 // The same ring carries MXFP8 operands (TileCfg MX): an LDS row is then 128
 // E4M3 values, one step of the scaled 16x16x128 MFMA, and a lane's two
@@ -32,13 +38,16 @@ constexpr int kBK = 64;          // contraction step (bf16 elements)
 constexpr int kRB = kBK * 2;     // bytes per LDS row (also 128 E4M3 values)
 constexpr int kScRows = 512;     // rows of the per-stage scale area (MX)
 
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory");
+// 16 bytes per lane: LDS address M0 + 16 * lane
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(off), "s"(base)
+               : "memory");
 }
 
 // 4 bytes per lane: LDS address M0 + 4 * lane
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(g) : "memory");
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_addr), "v"(off), "s"(base)
+               : "memory");
 }
 
 template <int N>
@@ -57,6 +66,14 @@ __device__ __forceinline__ void wait_steps(int n_after) {
   }
 }
 
+// a pointer every lane holds the same value of, moved to SGPRs
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ (r & 7); }
 
 template <int BM_, int BN_, int NS_, int WAVES_M, int WAVES_N, bool DUAL_, bool MX_ = false>
@@ -67,6 +84,7 @@ struct TileCfg {
   static constexpr int WAVES_N_ = WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int WNB = DUAL ? WN / 2 : WN;                   // B rows per wave per half
   static constexpr int RPI = 1024 / kRB;                           // rows per DMA instruction
   static constexpr int A_BYTES = BM * kRB, SC_OFF = (BM + BN) * kRB;
   static constexpr int STAGE = SC_OFF + (MX ? kScRows * 4 : 0);
@@ -75,84 +93,96 @@ struct TileCfg {
   static constexpr int NCOL = DUAL ? BN / 2 : BN;                  // output columns per tile
   static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "even DMA split");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && (!DUAL || TN % 2 == 0), "wave tile");
+  static_assert(!DUAL || (BN / 2) % (B_INS * RPI) == 0, "a wave's B rows are all gate or all up");
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS ring");
-  static_assert(!MX || (NW * 64 == kScRows && BM + BN <= kScRows), "one scale load per wave");
+  static_assert(!MX || (NW * 64 == kScRows && BM + BN <= kScRows && BM % 64 == 0 && BN % 128 == 0),
+                "one scale load per wave, each wave's scale rows from one operand");
 };
 
-// Row of the B tile that wave column wn, fragment j reads.  DUAL: gate rows
-// [0, BN/2), up rows [BN/2, BN); a wave holds TN/2 gate and TN/2 up fragments
-// of the same output columns.
+// Row of the B tile that B fragment j of a wave reads, less the wave's own
+// offset wn * WNB.  DUAL: gate rows [0, BN/2), up rows [BN/2, BN); a wave
+// holds TN/2 gate and TN/2 up fragments of the same output columns.
 template <class C>
-__device__ __forceinline__ int b_row(int wn, int j) {
-  if (!C::DUAL) return wn * C::WN + j * 16;
-  constexpr int half = C::TN / 2;
-  const int jj = j < half ? j : j - half;
-  return (j < half ? 0 : C::BN / 2) + wn * (C::WN / 2) + jj * 16;
+constexpr int b_frag_row(int j) {
+  if (!C::DUAL) return j * 16;
+  return j < C::TN / 2 ? j * 16 : C::BN / 2 + (j - C::TN / 2) * 16;
 }
 
 // This lane's place in a DMA instruction: the tile row of the q-th load of
-// wave `wave` (ROWS_PER_WAVE = INS * RPI rows per wave) and the global chunk
-// that belongs at its slot (slot_of is an involution in c).
+// wave `wave` (ins loads per wave per operand) and the global chunk that
+// belongs at its slot (slot_of is an involution in c).
 __device__ __forceinline__ int dma_row(int wave, int ins, int q) { return (wave * ins + q) * (1024 / kRB) + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int dma_chunk() {
   const int lane = threadIdx.x & 63;
   return slot_of(lane >> 3, lane & 7);
 }
 
-// Issue the DMA loads of contraction step kt into its ring stage.
-// a_src[q] / b_src[q] point at this lane's 16-byte chunk of its q-th DMA row
-// at the first step; step kt reads kt * kRB bytes further.  MX: s_src points
-// at the 4 scale bytes of this lane's scale row at the first step.
+// DMA sources of one tile at its first contraction step: wave-uniform bases
+// and this lane's byte offsets from them (A rows, this wave's B rows, and
+// for MX this thread's scale row).
 template <class C>
-__device__ __forceinline__ void issue_step(uint32_t lds0, const uint8_t* const* a_src, const uint8_t* const* b_src,
-                                           const uint8_t* s_src, int kt) {
+struct Src {
+  const uint8_t* a;
+  const uint8_t* b;
+  const uint8_t* s;
+  uint32_t a_off[C::A_INS];
+  uint32_t b_off[C::B_INS];
+  uint32_t s_off;
+};
+
+// Issue the DMA loads of contraction step kt into its ring stage.
+template <class C>
+__device__ __forceinline__ void issue_step(uint32_t lds0, const Src<C>& src, int kt) {
   const int wave = threadIdx.x >> 6;
   const uint32_t st = lds0 + (uint32_t)((kt % C::NS) * C::STAGE);
   const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;
   const uint32_t wave_b = st + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
   const int64_t ko = (int64_t)kt * kRB;
+  const uint8_t* a = src.a + ko;
+  const uint8_t* b = src.b + ko;
 #pragma unroll
-  for (int q = 0; q < C::A_INS; ++q) lds_dma16(a_src[q] + ko, __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
+  for (int q = 0; q < C::A_INS; ++q) lds_dma16(a, src.a_off[q], __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
 #pragma unroll
-  for (int q = 0; q < C::B_INS; ++q) lds_dma16(b_src[q] + ko, __builtin_amdgcn_readfirstlane(wave_b + q * 1024u));
+  for (int q = 0; q < C::B_INS; ++q) lds_dma16(b, src.b_off[q], __builtin_amdgcn_readfirstlane(wave_b + q * 1024u));
   if constexpr (C::MX)
-    lds_dma4(s_src + (int64_t)kt * 4, __builtin_amdgcn_readfirstlane(st + (uint32_t)C::SC_OFF + wave * 256u));
+    lds_dma4(src.s + (int64_t)kt * 4, src.s_off,
+             __builtin_amdgcn_readfirstlane(st + (uint32_t)C::SC_OFF + wave * 256u));
 }
 
 // Issue the first NS-1 steps (the ring must be free).
 template <class C>
-__device__ __forceinline__ void prologue(uint32_t lds0, const uint8_t* const* a_src, const uint8_t* const* b_src,
-                                         const uint8_t* s_src, int nk) {
+__device__ __forceinline__ void prologue(uint32_t lds0, const Src<C>& src, int nk) {
 #pragma unroll
   for (int s = 0; s < C::NS - 1; ++s)
-    if (s < nk) issue_step<C>(lds0, a_src, b_src, s_src, s);
+    if (s < nk) issue_step<C>(lds0, src, s);
 }
+
+// Per-lane LDS fragment bases: chunk lg (lo) and chunk 4 + lg (hi) of the
+// lane's first A row and first B row; the two differ in bit 6 only.
+template <class C>
+struct FragBase {
+  uint32_t a_lo, a_hi, b_lo, b_hi;
+  __device__ __forceinline__ FragBase() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const uint32_t sw = (uint32_t)((lg ^ (l16 & 7)) << 4);
+    a_lo = (uint32_t)((wm * C::WM + l16) * kRB) + sw;
+    b_lo = (uint32_t)(C::A_BYTES + (wn * C::WNB + l16) * kRB) + sw;
+    a_hi = a_lo ^ 64u;
+    b_hi = b_lo ^ 64u;
+  }
+};
 
 // Main loop: acc = A[rows, k] . B[cols, k]^T over nk contraction steps, the
 // prologue already issued.  The ring is free again when this returns; vector
 // stores issued after the prologue only make the first waits stricter.
 template <class C>
-__device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, const uint8_t* const* a_src,
-                                         const uint8_t* const* b_src, int nk,
+__device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, const Src<C>& src, int nk,
                                          f32x4_t (&acc)[C::TM][C::TN]) {
   static_assert(!C::MX, "bf16 tiles");
-  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, NS = C::NS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
-  const int l16 = lane & 15, lg = lane >> 4;
-  int a_off[TM][2], b_off[TN][2];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * WM + i * 16 + l16;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_off[i][ks] = r * kRB + (slot_of(r, ks * 4 + lg) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int r = b_row<C>(wn, j) + l16;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) b_off[j][ks] = C::A_BYTES + r * kRB + (slot_of(r, ks * 4 + lg) << 4);
-  }
+  constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
+  const FragBase<C> fb;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -160,15 +190,17 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue_step<C>(lds0, a_src, b_src, nullptr, kt + NS - 1);
+    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const uint8_t* sa = st + (ks ? fb.a_hi : fb.a_lo);
+      const uint8_t* sb = st + (ks ? fb.b_hi : fb.b_lo);
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][ks]);
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(sa + i * 16 * kRB);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off[j][ks]);
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + b_frag_row<C>(j) * kRB);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -179,24 +211,27 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
   __syncthreads();   // every wave is done reading the ring before it is refilled
 }
 
-// MXFP8 main loop: one scaled MFMA per fragment pair per step.  Tile rows
-// that differ by a multiple of 8 share a swizzle, so every fragment offset is
-// a per-lane base plus a constant.  Lane group lg reads chunks lg and 4 + lg
-// of its row (slots s and s ^ 4) and the scale byte of block lg.
+__device__ __forceinline__ i32x8_t load_frag8(const uint8_t* lo, const uint8_t* hi) {
+  const uint4 l = *reinterpret_cast<const uint4*>(lo);
+  const uint4 h = *reinterpret_cast<const uint4*>(hi);
+  return i32x8_t{(int)l.x, (int)l.y, (int)l.z, (int)l.w, (int)h.x, (int)h.y, (int)h.z, (int)h.w};
+}
+
+// MXFP8 main loop: one scaled MFMA per fragment pair per step.  Lane group
+// lg reads chunks lg and 4 + lg of its row and the scale byte of block lg.
+// All A fragments of the step are read first; B fragments are read one
+// ahead of the MFMAs that use them.
 template <class C>
-__device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, const uint8_t* const* a_src,
-                                            const uint8_t* const* b_src, const uint8_t* s_src, int nk,
+__device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, const Src<C>& src, int nk,
                                             f32x4_t (&acc)[C::TM][C::TN]) {
   static_assert(C::MX, "MXFP8 tiles");
-  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, NS = C::NS;
+  constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
+  const FragBase<C> fb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int sw = (lg ^ (l16 & 7)) << 4;
-  const int a_base = (wm * WM + l16) * kRB + sw;
-  const int b_base = C::A_BYTES + l16 * kRB + sw;
-  const int as_base = C::SC_OFF + (wm * WM + l16) * 4 + lg;
-  const int bs_base = C::SC_OFF + (C::BM + l16) * 4 + lg;
+  const uint32_t as_b = (uint32_t)(C::SC_OFF + (wm * C::WM + l16) * 4 + lg);
+  const uint32_t bs_b = (uint32_t)(C::SC_OFF + (C::BM + wn * C::WNB + l16) * 4 + lg);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -204,29 +239,36 @@ __device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, 
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue_step<C>(lds0, a_src, b_src, s_src, kt + NS - 1);
+    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
+    const uint8_t* alo = st + fb.a_lo;
+    const uint8_t* ahi = st + fb.a_hi;
+    const uint8_t* blo = st + fb.b_lo;
+    const uint8_t* bhi = st + fb.b_hi;
+    const uint8_t* sa_p = st + as_b;
+    const uint8_t* sb_p = st + bs_b;
     i32x8_t af[TM];
     int sa[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int off = a_base + i * 16 * kRB;
-      const uint4 lo = *reinterpret_cast<const uint4*>(st + off);
-      const uint4 hi = *reinterpret_cast<const uint4*>(st + (off ^ 64));
-      af[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa[i] = st[as_base + i * 64];
+      af[i] = load_frag8(alo + i * 16 * kRB, ahi + i * 16 * kRB);
+      sa[i] = sa_p[i * 64];
     }
+    i32x8_t bcur = load_frag8(blo + b_frag_row<C>(0) * kRB, bhi + b_frag_row<C>(0) * kRB);
+    int scur = sb_p[b_frag_row<C>(0) * 4];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int br = b_row<C>(wn, j);
-      const int off = b_base + br * kRB;
-      const uint4 lo = *reinterpret_cast<const uint4*>(st + off);
-      const uint4 hi = *reinterpret_cast<const uint4*>(st + (off ^ 64));
-      const i32x8_t bf{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const int sb = st[bs_base + br * 4];
+      i32x8_t bnext = bcur;
+      int snext = scur;
+      if (j + 1 < TN) {
+        bnext = load_frag8(blo + b_frag_row<C>(j + 1) * kRB, bhi + b_frag_row<C>(j + 1) * kRB);
+        snext = sb_p[b_frag_row<C>(j + 1) * 4];
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], acc[i][j], 0, 0, 0, scur, 0, sa[i]);
+      bcur = bnext;
+      scur = snext;
     }
   }
   __syncthreads();   // every wave is done reading the ring before it is refilled

@@ -49,21 +49,25 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
   const int m_start = mb * C::BM, n0 = nt * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d_chunk = dma_chunk();
-  const uint8_t* a_src[C::A_INS];
-  const uint8_t* b_src[C::B_INS];
+  Src<C> src;
+  const int64_t rb = (int64_t)p.D * 2;   // row bytes
+  src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(p.x + (int64_t)m_start * p.D + (int64_t)k0 * kBK));
+  src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(p.w + (int64_t)k0 * kBK));
+  src.s = nullptr;
+  src.s_off = 0;
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const int row = min(m_start + dma_row(wave, C::A_INS, q), p.N - 1);
-    a_src[q] = reinterpret_cast<const uint8_t*>(p.x + (int64_t)row * p.D + (int64_t)k0 * kBK) + d_chunk * 16;
+    src.a_off[q] = (uint32_t)((row - m_start) * rb + d_chunk * 16);
   }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) {
     const int col = min(n0 + dma_row(wave, C::B_INS, q), p.E - 1);
-    b_src[q] = reinterpret_cast<const uint8_t*>(p.w + (int64_t)col * p.D + (int64_t)k0 * kBK) + d_chunk * 16;
+    src.b_off[q] = (uint32_t)(col * rb + d_chunk * 16);
   }
   f32x4_t acc[C::TM][C::TN];
-  prologue<C>(lds0, a_src, b_src, nullptr, k1 - k0);
-  mainloop<C>(smem, lds0, a_src, b_src, k1 - k0, acc);
+  prologue<C>(lds0, src, k1 - k0);
+  mainloop<C>(smem, lds0, src, k1 - k0, acc);
 
   // lane holds row i*16 + l16 (one wave row), columns wn*WN + j*16 + 4*lg + r
   const int l16 = lane & 15, lg = lane >> 4, wn = wave;
