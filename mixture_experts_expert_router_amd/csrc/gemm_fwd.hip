@@ -78,9 +78,10 @@ template <bool DUAL, bool MX = false>
 using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB ring (+3 x 2 KB scales)
 template <bool MX>
 constexpr int lds_bytes() {
-  constexpr int s = SmallTile<true, MX>::NS * SmallTile<true, MX>::STAGE;
-  constexpr int b = BigTile<true, MX>::NS * BigTile<true, MX>::STAGE;
-  return s > b ? s : b;
+  constexpr int s = SmallTile<true, MX>::LDS, s1 = SmallTile<false, MX>::LDS;
+  constexpr int b = BigTile<true, MX>::LDS, b1 = BigTile<false, MX>::LDS;
+  constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1;
+  return m0 > m1 ? m0 : m1;
 }
 constexpr int kLdsBytes = lds_bytes<false>();
 
@@ -93,7 +94,7 @@ template <bool DUAL>
 __device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) {
   if (threadIdx.x == 0) *s_item = atomicAdd(p.head, 1);
   __syncthreads();
-  const int item = *s_item;
+  const int item = __builtin_amdgcn_readfirstlane(*s_item);   // same for every lane
   Item it{};
   const int total = p.plan[0];
   if (item >= total) return it;
@@ -141,19 +142,24 @@ __device__ __forceinline__ void sources(const FwdParams& p, const Item& it, tile
     src.b_off[q] = (uint32_t)(col * RB + d_chunk * 16);
   }
   if constexpr (C::MX) {
-    const int64_t KS = p.K / 32;
-    const int c = threadIdx.x, c0 = wave * 64;
-    const bool in_b = c0 >= C::BM && c0 < C::BM + C::BN;
-    const bool up_s = C::DUAL && c0 >= C::BM + C::BN / 2;
-    const uint8_t* bsb = (up_s ? p.bs1 : p.bs0) + (int64_t)it.e * p.N * KS;
-    const uint8_t* asb = p.as + (int64_t)it.m_start * KS;
-    src.s = uniform_ptr(in_b ? bsb : asb);
-    const int col = min(it.n0 + c - C::BM - (up_s ? C::BN / 2 : 0), p.N - 1);
-    const int row = c0 < C::BM ? min(it.m_start + c, it.m1 - 1) : it.m_start;
-    src.s_off = in_b ? (uint32_t)(col * KS) : (uint32_t)((row - it.m_start) * KS);
-  } else {
-    src.s = nullptr;
-    src.s_off = 0;
+    // scale load q of this wave: tile rows [wave*SRW + 16q, +16), one operand
+    const int KS = p.K / 32;
+    src.s_ks = KS;
+    const uint8_t* a_sc = p.as + (int64_t)it.m_start * KS;
+#pragma unroll
+    for (int q = 0; q < C::SCI; ++q) {
+      const int r0 = wave * C::SRW + q * 16;
+      if (r0 < C::BM) {
+        src.s[q] = uniform_ptr(a_sc);
+        src.s_row0[q] = r0;
+        src.s_lim[q] = __builtin_amdgcn_readfirstlane(it.m1 - it.m_start - 1);
+      } else {
+        const bool up = C::DUAL && r0 >= C::BM + C::BN / 2;
+        src.s[q] = uniform_ptr((up ? p.bs1 : p.bs0) + (int64_t)it.e * p.N * KS);
+        src.s_row0[q] = __builtin_amdgcn_readfirstlane(it.n0 + r0 - C::BM - (up ? C::BN / 2 : 0));
+        src.s_lim[q] = p.N - 1;
+      }
+    }
   }
 }
 

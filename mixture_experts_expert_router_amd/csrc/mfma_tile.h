@@ -24,9 +24,12 @@
 // The same ring carries MXFP8 operands (TileCfg MX): an LDS row is then 128
 // E4M3 values, one step of the scaled 16x16x128 MFMA, and a lane's two
 // 16-byte chunks (lg and 4 + lg) are exactly that instruction's bytes 0..15
-// and 16..31.  Each stage also holds the E8M0 scales of the step: 4 bytes
-// (blocks of 32) per tile row, loaded with one global_load_lds_dword per wave
-// (64 rows each, A rows first, then B rows, then unused padding up to 512).
+// and 16..31.  The E8M0 scales (4 bytes, blocks of 32, per tile row and step)
+// travel in groups of 4 steps: 16 bytes per tile row, A rows then B rows,
+// loaded with global_load_lds_dword (4 lanes per row, 16 rows per wave
+// instruction, so an instruction touches 16 rows instead of 64) into two
+// alternating group buffers after the ring.  The group of steps 4g..4g+3 is
+// issued with step 4g's loads and lands with them.
 #pragma once
 
 #include "common.h"
@@ -36,7 +39,7 @@ namespace tile {
 
 constexpr int kBK = 64;          // contraction step (bf16 elements)
 constexpr int kRB = kBK * 2;     // bytes per LDS row (also 128 E4M3 values)
-constexpr int kScRows = 512;     // rows of the per-stage scale area (MX)
+constexpr int kScG = 4;          // steps per MXFP8 scale group
 
 // 16 bytes per lane: LDS address M0 + 16 * lane
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
@@ -86,17 +89,22 @@ struct TileCfg {
   static constexpr int TM = WM / 16, TN = WN / 16;
   static constexpr int WNB = DUAL ? WN / 2 : WN;                   // B rows per wave per half
   static constexpr int RPI = 1024 / kRB;                           // rows per DMA instruction
-  static constexpr int A_BYTES = BM * kRB, SC_OFF = (BM + BN) * kRB;
-  static constexpr int STAGE = SC_OFF + (MX ? kScRows * 4 : 0);
+  static constexpr int A_BYTES = BM * kRB, STAGE = (BM + BN) * kRB;
   static constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;   // per wave per step
-  static constexpr int LPS = A_INS + B_INS + (MX ? 1 : 0);
+  static constexpr int LPS = A_INS + B_INS;                        // loads per wave per step
+  // MX scale groups: 16 bytes per tile row, SCI loads of 16 rows per wave
+  static constexpr int SG_BYTES = (BM + BN) * 16;
+  static constexpr int SRW = (BM + BN) / NW;                       // scale rows per wave
+  static constexpr int SCI = MX ? SRW / 16 : 0;
+  static constexpr int SC_BASE = NS * STAGE;                        // group buffers after the ring
+  static constexpr int LDS = NS * STAGE + (MX ? 2 * SG_BYTES : 0);
   static constexpr int NCOL = DUAL ? BN / 2 : BN;                  // output columns per tile
   static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "even DMA split");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && (!DUAL || TN % 2 == 0), "wave tile");
   static_assert(!DUAL || (BN / 2) % (B_INS * RPI) == 0, "a wave's B rows are all gate or all up");
-  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS ring");
-  static_assert(!MX || (NW * 64 == kScRows && BM + BN <= kScRows && BM % 64 == 0 && BN % 128 == 0),
-                "one scale load per wave, each wave's scale rows from one operand");
+  static_assert(NS >= 2 && LDS <= 160 * 1024 - 64, "LDS ring");
+  static_assert(!MX || (SRW % 16 == 0 && BM % 16 == 0 && (BN / 2) % 16 == 0 && NS <= 3),
+                "whole 16-row scale loads, each from one operand; at most one step in flight past the current");
 };
 
 // Row of the B tile that B fragment j of a wave reads, less the wave's own
@@ -124,16 +132,35 @@ template <class C>
 struct Src {
   const uint8_t* a;
   const uint8_t* b;
-  const uint8_t* s;
   uint32_t a_off[C::A_INS];
   uint32_t b_off[C::B_INS];
-  uint32_t s_off;
+  // MX: per scale load q of this wave (uniform): base, the row of lane group
+  // 0 relative to it, the last valid row (later rows reload it), row bytes
+  const uint8_t* s[C::SCI > 0 ? C::SCI : 1];
+  int s_row0[C::SCI > 0 ? C::SCI : 1];
+  int s_lim[C::SCI > 0 ? C::SCI : 1];
+  int s_ks;
 };
 
-// Issue the DMA loads of contraction step kt into its ring stage.
+// Issue the DMA loads of contraction step kt into its ring stage (MX: with
+// the scale group of steps kt..kt+3 first when kt % 4 == 0; a lane's dword
+// past the last step reloads the last step's).
 template <class C>
-__device__ __forceinline__ void issue_step(uint32_t lds0, const Src<C>& src, int kt) {
+__device__ __forceinline__ void issue_step(uint32_t lds0, const Src<C>& src, int kt, int nk) {
   const int wave = threadIdx.x >> 6;
+  if constexpr (C::MX) {
+    if (kt % kScG == 0) {
+      const int lane = threadIdx.x & 63;
+      const int g = kt / kScG;
+      const uint32_t dst = lds0 + (uint32_t)(C::SC_BASE + (g & 1) * C::SG_BYTES + wave * C::SRW * 16);
+      const int d = min(g * kScG + (lane & 3), nk - 1);
+#pragma unroll
+      for (int q = 0; q < C::SCI; ++q) {
+        const int row = min(src.s_row0[q] + (lane >> 2), src.s_lim[q]);
+        lds_dma4(src.s[q], (uint32_t)(row * src.s_ks + d * 4), __builtin_amdgcn_readfirstlane(dst + q * 256u));
+      }
+    }
+  }
   const uint32_t st = lds0 + (uint32_t)((kt % C::NS) * C::STAGE);
   const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;
   const uint32_t wave_b = st + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
@@ -144,9 +171,6 @@ __device__ __forceinline__ void issue_step(uint32_t lds0, const Src<C>& src, int
   for (int q = 0; q < C::A_INS; ++q) lds_dma16(a, src.a_off[q], __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) lds_dma16(b, src.b_off[q], __builtin_amdgcn_readfirstlane(wave_b + q * 1024u));
-  if constexpr (C::MX)
-    lds_dma4(src.s + (int64_t)kt * 4, src.s_off,
-             __builtin_amdgcn_readfirstlane(st + (uint32_t)C::SC_OFF + wave * 256u));
 }
 
 // Issue the first NS-1 steps (the ring must be free).
@@ -154,7 +178,7 @@ template <class C>
 __device__ __forceinline__ void prologue(uint32_t lds0, const Src<C>& src, int nk) {
 #pragma unroll
   for (int s = 0; s < C::NS - 1; ++s)
-    if (s < nk) issue_step<C>(lds0, src, s);
+    if (s < nk) issue_step<C>(lds0, src, s, nk);
 }
 
 // Per-lane LDS fragment bases: chunk lg (lo) and chunk 4 + lg (hi) of the
@@ -190,7 +214,7 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1);
+    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1, nk);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -217,6 +241,15 @@ __device__ __forceinline__ i32x8_t load_frag8(const uint8_t* lo, const uint8_t* 
   return i32x8_t{(int)l.x, (int)l.y, (int)l.z, (int)l.w, (int)h.x, (int)h.y, (int)h.z, (int)h.w};
 }
 
+// Wait until step kt of an MXFP8 tile has landed (NS <= 3: at most step
+// kt+1 was issued after it, with its scale group when kt+1 starts one).
+template <class C>
+__device__ __forceinline__ void wait_step_mx(int kt, int nk) {
+  if (C::NS == 2 || kt + 1 >= nk) wait_vmcnt<0>();
+  else if ((kt + 1) % kScG == 0) wait_vmcnt<C::LPS + C::SCI>();
+  else wait_vmcnt<C::LPS>();
+}
+
 // MXFP8 main loop: one scaled MFMA per fragment pair per step.  Lane group
 // lg reads chunks lg and 4 + lg of its row and the scale byte of block lg.
 // All A fragments of the step are read first; B fragments are read one
@@ -230,39 +263,40 @@ __device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
-  const uint32_t as_b = (uint32_t)(C::SC_OFF + (wm * C::WM + l16) * 4 + lg);
-  const uint32_t bs_b = (uint32_t)(C::SC_OFF + (C::BM + wn * C::WNB + l16) * 4 + lg);
+  const uint32_t as_b = (uint32_t)(C::SC_BASE + (wm * C::WM + l16) * 16 + lg);
+  const uint32_t bs_b = (uint32_t)(C::SC_BASE + (C::BM + wn * C::WNB + l16) * 16 + lg);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int kt = 0; kt < nk; ++kt) {
-    wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+    wait_step_mx<C>(kt, nk);
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1);
+    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1, nk);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
     const uint8_t* alo = st + fb.a_lo;
     const uint8_t* ahi = st + fb.a_hi;
     const uint8_t* blo = st + fb.b_lo;
     const uint8_t* bhi = st + fb.b_hi;
-    const uint8_t* sa_p = st + as_b;
-    const uint8_t* sb_p = st + bs_b;
+    const int sgo = ((kt / kScG) & 1) * C::SG_BYTES + (kt % kScG) * 4;
+    const uint8_t* sa_p = smem + as_b + sgo;
+    const uint8_t* sb_p = smem + bs_b + sgo;
     i32x8_t af[TM];
     int sa[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       af[i] = load_frag8(alo + i * 16 * kRB, ahi + i * 16 * kRB);
-      sa[i] = sa_p[i * 64];
+      sa[i] = sa_p[i * 16 * 16];
     }
     i32x8_t bcur = load_frag8(blo + b_frag_row<C>(0) * kRB, bhi + b_frag_row<C>(0) * kRB);
-    int scur = sb_p[b_frag_row<C>(0) * 4];
+    int scur = sb_p[b_frag_row<C>(0) * 16];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       i32x8_t bnext = bcur;
       int snext = scur;
       if (j + 1 < TN) {
         bnext = load_frag8(blo + b_frag_row<C>(j + 1) * kRB, bhi + b_frag_row<C>(j + 1) * kRB);
-        snext = sb_p[b_frag_row<C>(j + 1) * 4];
+        snext = sb_p[b_frag_row<C>(j + 1) * 16];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)

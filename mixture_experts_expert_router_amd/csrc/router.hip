@@ -53,8 +53,6 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
   const int64_t rb = (int64_t)p.D * 2;   // row bytes
   src.a = uniform_ptr(reinterpret_cast<const uint8_t*>(p.x + (int64_t)m_start * p.D + (int64_t)k0 * kBK));
   src.b = uniform_ptr(reinterpret_cast<const uint8_t*>(p.w + (int64_t)k0 * kBK));
-  src.s = nullptr;
-  src.s_off = 0;
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const int row = min(m_start + dma_row(wave, C::A_INS, q), p.N - 1);
