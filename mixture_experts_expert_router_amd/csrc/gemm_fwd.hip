@@ -9,17 +9,24 @@
 //
 // Scheduling (KOSMOS section 3.1: persistent workgroups claiming tiles from a
 // device queue).  The grid is the number of workgroups that can be resident at
-// once; every workgroup claims items from one atomic head counter until the
-// queue is empty.  An item is (expert, n-tile, row block); inside an expert the
-// row blocks of one n-tile are consecutive, so the weight tile they share is
-// fetched once and served from cache to the others.  Experts with many rows
+// once; every workgroup claims items from atomic head counters until the work
+// is done.  An item is (expert, row block, n-tile).  Experts with many rows
 // use 256-row tiles, the others 128-row tiles (KOSMOS section 3.4 uses 256x256
 // tiles; small expert batches would waste most of such a tile).  A
 // one-workgroup planner builds the expert order and the item prefix sums on
 // the device from the expert offsets (no host round trip), interleaving the
 // two tile classes in proportion to their work so that weight-streaming tiles
 // of small experts run beside the MFMA-bound tiles of large ones, and resets
-// the queue head.  Which workgroup computes an item never changes its result.
+// the queue heads.  Which workgroup computes an item never changes its result.
+//
+// Cache locality across the chip's eight XCDs (each with its own L2): the item
+// sequence is cut into chunks of 32 consecutive items, and chunk c belongs to
+// the queue of XCD c % 8, so the 32 CUs of an XCD work on neighbouring items
+// at the same time and fetch their shared operand tiles once.  Inside an
+// expert the items run in super-blocks of 4 row blocks x 8 n-tiles (m
+// fastest), so a chunk of a large expert reads 4 A blocks and 8 weight tiles
+// instead of a whole operand.  A workgroup claims from its own XCD's queue and,
+// once that is empty, takes items from the other queues.
 //
 // The MFMA main loop (direct-to-LDS operand ring) is the shared tile engine;
 // eight waves per workgroup (two per SIMD).
@@ -39,11 +46,14 @@ namespace moe {
 namespace {
 
 constexpr int kBigRows = 256;    // experts with at least this many rows use 256-row tiles
+constexpr int kXcds = 8;         // XCDs of the chip; queue q holds chunks q, q + 8, ...
+constexpr int kChunk = 32;       // items per chunk (the CUs of one XCD)
+constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
 
 struct FwdParams {
   const int32_t* offsets;   // [E+1]
   const int32_t* plan;      // planner output (layout below)
-  int32_t* head;            // queue head counter
+  int32_t* head;            // queue head counters [kXcds]
   int E, N, K;              // N output columns per weight, K contraction
   int nk;                   // contraction steps (128 bytes of a row each)
   int n_tiles;              // ceil(N / NCOL)
@@ -87,20 +97,51 @@ constexpr int kLdsBytes = lds_bytes<false>();
 
 __device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
 
-// Claim the next item from the queue and decode it (every thread gets the
-// same result; li is the workgroup's position in the expert list, which only
-// moves forward because each workgroup's claims increase).
+// XCD this workgroup runs on (hardware register XCC_ID).  Only locality
+// depends on it: any value in range gives the same results.
+__device__ __forceinline__ int xcd_id() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1));
+}
+
+// global position of the k-th item of queue q
+__device__ __forceinline__ int queue_item(int q, int k) { return (kXcds * (k / kChunk) + q) * kChunk + k % kChunk; }
+
+// Claim the next item and decode it (every thread gets the same result).
+// Queue q's items have increasing positions and end at the first one past
+// the total, so a failed claim means the queue is exhausted.  li is the
+// workgroup's position in the expert list, walked forward for its own queue's
+// increasing items and searched for items taken from other queues.
 template <bool DUAL>
-__device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) {
-  if (threadIdx.x == 0) *s_item = atomicAdd(p.head, 1);
+__device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li, int xcd) {
+  const int total = p.plan[0];
+  if (threadIdx.x == 0) {
+    int g = -1;
+    for (int t = 0; t < kXcds; ++t) {
+      const int q = (xcd + t) & (kXcds - 1);
+      const int gi = queue_item(q, atomicAdd(p.head + q, 1));
+      if (gi < total) {
+        g = gi;
+        break;
+      }
+    }
+    *s_item = g;
+  }
   __syncthreads();
   const int item = __builtin_amdgcn_readfirstlane(*s_item);   // same for every lane
   Item it{};
-  const int total = p.plan[0];
-  if (item >= total) return it;
+  if (item < 0) return it;
   const int L = p.plan[1];
   const int32_t* order = p.plan + 2;
   const int32_t* pref = p.plan + 2 + p.E;
+  if (pref[li] > item) {   // an earlier item (taken from another queue): binary search
+    int lo = 0, hi = L - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    li = lo;
+  }
   while (li + 1 < L && pref[li + 1] <= item) ++li;
   it.e = order[li];
   const int m0 = p.offsets[it.e];
@@ -108,8 +149,17 @@ __device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li) 
   it.big = is_big(it.m1 - m0);
   const int bm = it.big ? BigTile<DUAL>::BM : SmallTile<DUAL>::BM;
   const int nmb = (it.m1 - m0 + bm - 1) / bm;
+  // item w of the expert: n-groups of kSbN tiles, in each m-groups of kSbM
+  // row blocks, row block fastest (the last group of each kind may be short)
   const int w = item - pref[li];
-  const int n_t = w / nmb, mb = w - n_t * nmb;
+  const int gn = w / (kSbN * nmb);
+  const int w1 = w - gn * kSbN * nmb;
+  const int nb = min(kSbN, p.n_tiles - gn * kSbN);
+  const int gm = w1 / (kSbM * nb);
+  const int w2 = w1 - gm * kSbM * nb;
+  const int mbk = min(kSbM, nmb - gm * kSbM);
+  const int mb = gm * kSbM + w2 % mbk;
+  const int n_t = gn * kSbN + w2 / mbk;
   it.m_start = m0 + mb * bm;
   it.n0 = n_t * BigTile<DUAL>::NCOL;
   it.valid = true;
@@ -256,12 +306,12 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
 // loads of the next tile overlap this epilogue.
 template <class C, bool DUAL>
 __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int* s_item,
-                                         int& li, const Item& it) {
+                                         int& li, int xcd, const Item& it) {
   tile::Src<C> src;
   sources<C>(p, it, src);
   f32x4_t acc[C::TM][C::TN];
   mainloop_any<C>(smem, lds0, src, p.nk, acc);
-  const Item next = claim<DUAL>(p, s_item, li);
+  const Item next = claim<DUAL>(p, s_item, li, xcd);
   if (next.valid) {
     if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
     else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
@@ -277,14 +327,15 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   using Big = BigTile<DUAL, MX>;
   using Small = SmallTile<DUAL, MX>;
+  const int xcd = xcd_id();
   int li = 0;
-  Item it = claim<DUAL>(p, &s_item, li);
+  Item it = claim<DUAL>(p, &s_item, li, xcd);
   if (!it.valid) return;
   if (it.big) start<Big>(p, lds0, it);
   else start<Small>(p, lds0, it);
   while (it.valid) {
-    if (it.big) it = run_item<Big, DUAL>(p, smem, lds0, &s_item, li, it);
-    else it = run_item<Small, DUAL>(p, smem, lds0, &s_item, li, it);
+    if (it.big) it = run_item<Big, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
+    else it = run_item<Small, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
   }
 }
 
@@ -354,8 +405,8 @@ __global__ __launch_bounds__(1024) void plan_fwd_kernel(const int32_t* __restric
     plan[0] = r;
     plan[1] = L;
     plan[2 + E + L] = r;
-    *head = 0;
   }
+  if (t < kXcds) head[t] = 0;
   __syncthreads();
   if (t < L) {
     plan[2 + t] = s_ids[t];
