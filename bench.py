@@ -13,9 +13,13 @@ Prints ONE JSON line (rank 0).  Usage:
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes as C
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +32,12 @@ if ROOT not in sys.path:
 import moe_synth as S  # noqa: E402
 
 METRIC = "MoE layer fwd tokens/s; grouped-GEMM TFLOP/s (% MFMA peak); dispatch GB/s"
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mixture_experts_expert_router_amd", "csrc")
+# sources of the persistent grouped GEMM: HBM counters taken on another
+# version of these no longer describe the kernel
+GEMM_SOURCES = ("gemm_fwd.hip", "mfma_tile.h", "common.h")
 
 # MI355X published peaks (dense)
 PEAK_HBM_GBS = 8000.0
@@ -75,6 +85,90 @@ def router_work(N, D, E):
 def t_star(F, Q, peak_tflops, peak_gbs=PEAK_HBM_GBS):
     """Roofline lower bound (eq. 89): max(F / C, Q / B) in seconds."""
     return max(F / (peak_tflops * 1e12), Q / (peak_gbs * 1e9))
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# ---------------------------------------------------------------------------
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_per_dispatch(run_dir, counter):
+    """{dispatch id: (kernel name, summed counter value in KiB)} from one
+    rocprofv3 --pmc CSV run (values are summed over the counter's instances)."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    out = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = (f, r["Dispatch_Id"])
+                name, v = out.get(k, (r["Kernel_Name"], 0.0))
+                out[k] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def pmc_report(fetch_dir, write_dir, copy_mib, workload):
+    """Traffic per kernel from a FETCH_SIZE run and a WRITE_SIZE run of
+    `bench.py --copy-probe copy_mib`: each counter is scaled by what it reads
+    for the plain device copy of copy_mib MiB in the same run."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 1024.0 * 1024.0
+
+    def copy_kib(d):
+        vals = [v for (n, v) in d.values() if "copyBuffer" in n]
+        if not vals:
+            raise RuntimeError("no device copy kernel in the counter run (use --copy-probe)")
+        return max(vals)
+
+    f_fetch = copy_bytes / (copy_kib(fetch) * 1024.0)
+    f_write = copy_bytes / (copy_kib(write) * 1024.0)
+
+    def per_kernel(d):
+        agg = {}
+        for n, v in d.values():
+            agg.setdefault(n, []).append(v)
+        return {n: float(np.mean(v)) for n, v in agg.items()}
+
+    fk, wk = per_kernel(fetch), per_kernel(write)
+    rows = []
+    for n in sorted(set(fk) | set(wk), key=lambda n: -(fk.get(n, 0) * f_fetch + wk.get(n, 0) * f_write)):
+        rb = fk.get(n, 0.0) * 1024 * f_fetch
+        wb = wk.get(n, 0.0) * 1024 * f_write
+        rows.append(dict(kernel=n, fetch_kib=fk.get(n), write_kib=wk.get(n), read_bytes=rb, write_bytes=wb,
+                         traffic_bytes=rb + wb))
+    gemm1 = [r for r in rows if re.search(r"gemm_fwd_kernel<true", r["kernel"])]
+    summary = dict(workload=workload, fetch_factor=f_fetch, write_factor=f_write,
+                   gemm_source_hash=gemm_source_hash(),
+                   gemm1_kernel=gemm1[0]["kernel"] if gemm1 else None,
+                   gemm1_traffic_bytes=gemm1[0]["traffic_bytes"] if gemm1 else None)
+    return summary, rows
+
+
+def recorded_traffic(workload):
+    """Bytes per launch of GEMM1 from the committed counter summary of this
+    workload, or None when there is none or the GEMM sources changed since."""
+    path = os.path.join(PROFILES, f"gemm1_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        m = re.search(r"```json\n(.*?)\n```", fh.read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("gemm_source_hash") != gemm_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("gemm1_traffic_bytes")
 
 
 def load_stats(counts, align=1):
@@ -200,7 +294,7 @@ def cpu_baseline(inp, wl, budget_s=20.0):
         dt = time.perf_counter() - t0
         res = (n, dt)
         t_used += dt
-        if dt > budget_s / 4 or n >= wl.N or t_used > budget_s:
+        if dt > budget_s / 2 or n >= wl.N or t_used > 2 * budget_s:
             break
         n = min(wl.N, n * 2)
     n, dt = res
@@ -249,7 +343,23 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
                          "that calibrates the HBM byte counters of a profiler run")
+    ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this script with --copy-probe, and exit")
     args = ap.parse_args(argv)
+
+    if args.pmc_report:
+        summary, rows = pmc_report(args.pmc_report[0], args.pmc_report[1], args.copy_probe or 1024, args.workload)
+        print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |")
+        print("|---|---|---|---|---|")
+        for r in rows[:16]:
+            print(f"| `{r['kernel'][:110]}` | {r['fetch_kib'] or 0:.0f} | {r['write_kib'] or 0:.0f} | "
+                  f"{r['read_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} |")
+        print()
+        print("```json")
+        print(json.dumps(summary, indent=1))
+        print("```")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -264,7 +374,9 @@ def main(argv=None):
     t0 = time.perf_counter()
     inp = S.make_inputs(wl, args.seed)
     x, w, drop = device_inputs(M, inp, wl.mxfp8, torch)
-    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=wl.bwd)
+    dout = (torch.from_numpy(np.ascontiguousarray(inp.dout).view(np.int16)).view(torch.bfloat16).cuda()
+            if wl.bwd else None)
     st = StagedForward(M, layer, x)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
@@ -280,22 +392,35 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    # one step: the staged forward, and for a forward+backward workload the
+    # layer backward (combine-bwd, down dgrad/wgrad with the SwiGLU backward,
+    # gate/up dgrad/wgrad, dispatch-bwd, router-prob grads) after it
+    def step(ev=None, ev_b=None):
+        st.run(ev)
+        if wl.bwd:
+            layer.backward(x, dout)
+            if ev_b is not None:
+                ev_b.record()
+
     for _ in range(args.warmup):
-        st.run()
+        step()
     torch.cuda.synchronize()
 
     nst = len(StagedForward.STAGES)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        st.run(evs[k])
+        step(evs[k], evb[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
                 for i, name in enumerate(StagedForward.STAGES)}
-    total_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(args.steps)]))
-    gpu_ms = evs[0][0].elapsed_time(evs[-1][nst]) / args.steps
+    fwd_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(args.steps)]))
+    bwd_ms = (float(np.mean([evs[k][nst].elapsed_time(evb[k]) for k in range(args.steps)])) if wl.bwd else 0.0)
+    total_ms = fwd_ms + bwd_ms
+    gpu_ms = evs[0][0].elapsed_time(evb[-1] if wl.bwd else evs[-1][nst]) / args.steps
 
     layer_ms = None
     if args.layer_call:
@@ -324,7 +449,7 @@ def main(argv=None):
     else:
         roof = dict(bound="mfma", achieved=F1 / t1 / 1e12, peak=peak, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(wl.name)
     roof["kernel"] = "gemm1 (grouped gate/up GEMM with SwiGLU epilogue)"
     roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
 
@@ -359,11 +484,16 @@ def main(argv=None):
                     "pct_hbm": 100 * qc / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS,
                     "ms": stage_ms["combine"]},
         "stage_ms": stage_ms,
-        "layer_pct_of_roofline": 100 * tstar_layer / (total_ms / 1e3),
+        "layer_fwd_pct_of_roofline": 100 * tstar_layer / (fwd_ms / 1e3),
         "load": dict(stats, routes=R),
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "gpu_span_ms_per_step": gpu_ms,
     }
+    out["fwd_ms"] = fwd_ms
+    if wl.bwd:
+        tf_b = routed_flops(R, D, H, backward=True) / (bwd_ms / 1e3) / 1e12
+        out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / peak,
+                           "note": "value and ms_per_step cover forward + backward"}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
     if not args.no_cpu_baseline:
