@@ -72,6 +72,17 @@ hipError_t gemm_fwd_bf16(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
   return moe::launch_gemm_fwd_bf16(f, ws, s);
 }
 
+// backward GEMMs: the persistent kernels where their rules hold
+hipError_t gemm_dgrad(const moe::GemmBwd& b, int32_t* ws, hipStream_t s) {
+  if (moe::gemm_dgrad_fast_ok(b)) return moe::launch_gemm_dgrad_fast(b, ws, s);
+  return moe::launch_gemm_dgrad_bf16(b, ws, s);
+}
+
+hipError_t gemm_wgrad(const moe::GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s) {
+  if (moe::gemm_wgrad_fast_ok(b, dc, db)) return moe::launch_gemm_wgrad_fast(b, dc, db, ws, s);
+  return moe::launch_gemm_wgrad_bf16(b, dc, db, s);
+}
+
 hipError_t gemm_fwd_mxfp8(const moe::GemmFwd& f, int32_t* ws, hipStream_t s) {
   if (moe::gemm_fwd_fast_ok(f, true)) return moe::launch_gemm_fwd_fast(f, true, ws, s);
   return moe::launch_gemm_fwd_mxfp8(f, ws, s);
@@ -321,9 +332,9 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
                  g->dc0, g->dc1, g->da, g->g, g->u, g->dg, g->du, swb};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (want_dgrad) e = moe::launch_gemm_dgrad_bf16(b, (int32_t*)ws, s);
-  if (e == hipSuccess && g->db0) e = moe::launch_gemm_wgrad_bf16(b, g->dc0, g->db0, s);
-  if (e == hipSuccess && g->db1) e = moe::launch_gemm_wgrad_bf16(b, g->dc1, g->db1, s);
+  if (want_dgrad) e = gemm_dgrad(b, (int32_t*)ws, s);
+  if (e == hipSuccess && g->db0) e = gemm_wgrad(b, g->dc0, g->db0, (int32_t*)ws, s);
+  if (e == hipSuccess && g->db1) e = gemm_wgrad(b, g->dc1, g->db1, (int32_t*)ws, s);
   return hip_status(e);
 }
 
@@ -462,14 +473,14 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
   moe::GemmBwd down{d.E, rc, d.H, d.D, sv->offsets, sv->h, a->w_down, nullptr, dyd, nullptr, nullptr,
                     sv->g, sv->u, dg, du, true};
-  if (e == hipSuccess) e = moe::launch_gemm_dgrad_bf16(down, table, s);
-  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(down, dyd, gr->dw_down, s);
+  if (e == hipSuccess) e = gemm_dgrad(down, table, s);
+  if (e == hipSuccess) e = gemm_wgrad(down, dyd, gr->dw_down, table, s);
   // gate/up: forward g = xd . w_gate^T, u = xd . w_up^T  (k_dim = D, n_dim = H)
   moe::GemmBwd gu{d.E, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
                   nullptr, nullptr, nullptr, nullptr, false};
-  if (e == hipSuccess) e = moe::launch_gemm_dgrad_bf16(gu, table, s);
-  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(gu, dg, gr->dw_gate, s);
-  if (e == hipSuccess) e = moe::launch_gemm_wgrad_bf16(gu, du, gr->dw_up, s);
+  if (e == hipSuccess) e = gemm_dgrad(gu, table, s);
+  if (e == hipSuccess) e = gemm_wgrad(gu, dg, gr->dw_gate, table, s);
+  if (e == hipSuccess) e = gemm_wgrad(gu, du, gr->dw_up, table, s);
   if (e == hipSuccess) e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s);
   return hip_status(e);
 }

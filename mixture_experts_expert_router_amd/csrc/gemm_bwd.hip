@@ -1,0 +1,383 @@
+// Persistent grouped GEMMs of the expert backward on bf16 MFMA (KOSMOS section
+// 3.3.2; OLMo-core Appendix A, A.1 and A.13: the adjoints of the grouped
+// forward products).  For a forward product c = a . b[e]^T per expert
+// (a [rows][k_dim], b [E][n_dim][k_dim], c [rows][n_dim]):
+//
+//   dgrad  da[r][k] = sum_n dc[r][n] b[e][n][k]  (+ dc1[r][n] b1[e][n][k])
+//          The weight is read k-major (its rows are the contraction), the
+//          upstream gradient row-major; the optional second product
+//          continues the same contraction (the gate/up dgrad sums
+//          dG W_gate + dU W_up in one accumulator).  The SwiGLU-backward
+//          epilogue turns dH into dG, dU with the saved G, U (down dgrad).
+//   wgrad  db[e][n][k] = sum_{r in e} dc[r][n] a[r][k]
+//          Both operands are contracted over the expert's rows, so both are
+//          read k-major; the contraction length is the expert's row count.
+//          The last step's rows past the segment reload its last row and the
+//          B tile's copies are zeroed in LDS, so they add nothing.
+//
+// Both run on the shared tile engine (direct-to-LDS ring, k-major fragments
+// through transposing LDS reads).  dgrad items are row blocks of expert
+// segments and use the row scheduler of the forward GEMMs; wgrad items are
+// (expert, output row tile, output column tile), experts with the most rows
+// first so the longest items do not trail, on the same per-XCD queues.
+#include "common.h"
+#include "launch.h"
+#include "mfma_tile.h"
+#include "sched.h"
+
+namespace moe {
+
+namespace {
+
+using namespace sched;
+using tile::kRB;
+
+// ---------------------------------------------------------------- dgrad ----
+
+struct DgradParams {
+  const int32_t* offsets;   // [E+1]
+  const int32_t* plan;      // row-scheduler plan
+  int32_t* head;            // queue heads [kXcds]
+  int E, N, K;              // N output columns (forward k_dim), K contraction (forward n_dim)
+  int nk, n_tiles;          // steps per product, ceil(N / 256)
+  bool kcat;                // second product present
+  const uint8_t* a0;        // dc0 [rows][K]
+  const uint8_t* a1;        // dc1 [rows][K] (kcat)
+  const uint8_t* b0;        // b0 [E][K][N]
+  const uint8_t* b1;        // b1 [E][K][N] (kcat)
+  uint16_t* c0;             // da, or dG [rows][N]
+  uint16_t* c1;             // dU (SwiGLU backward)
+  const uint16_t* g;        // saved G [rows][N] (SwiGLU backward)
+  const uint16_t* u;        // saved U
+};
+
+using DgBig = tile::TileCfg<256, 256, 2, 4, 2, false, false, false, true>;     // 2 x 64 KB
+using DgSmall = tile::TileCfg<128, 256, 3, 2, 4, false, false, false, true>;   // 3 x 48 KB
+constexpr int kDgLds = DgSmall::LDS > DgBig::LDS ? DgSmall::LDS : DgBig::LDS;
+
+template <class C>
+__device__ __forceinline__ void sources_dg(const DgradParams& p, const Item& it, tile::SrcB<C>& src) {
+  using namespace tile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t RB = (int64_t)p.K * 2;
+  const int d_chunk = dma_chunk();
+  src.a[0] = uniform_ptr(p.a0 + (int64_t)it.m_start * RB);
+  src.a[1] = uniform_ptr((p.kcat ? p.a1 : p.a0) + (int64_t)it.m_start * RB);
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int row = min(it.m_start + dma_row(wave, C::A_INS, q), it.m1 - 1);
+    src.a_off[q] = (uint32_t)((row - it.m_start) * RB + d_chunk * 16);
+  }
+  const int64_t ws = (int64_t)p.K * p.N * 2;   // bytes per expert's weight
+  src.b[0] = uniform_ptr(p.b0 + (int64_t)it.e * ws);
+  src.b[1] = uniform_ptr((p.kcat ? p.b1 : p.b0) + (int64_t)it.e * ws);
+  src.b_rs = p.N * 2;
+  src.b_lim = p.K - 1;
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) {
+    const int g = wave * C::B_INS + q;
+    const int x = min(it.n0 + (g >> 3) * 64 + tchunk_of(g) * 8, p.N - 8);
+    src.b_off[q] = (uint32_t)(x * 2);
+  }
+  src.a_rs = 0;
+  src.a_lim = 0;
+  src.nk1 = p.nk;
+}
+
+template <class C, bool SWB>
+__device__ __forceinline__ void epilogue_dg(const DgradParams& p, const Item& it, const f32x4_t (&acc)[C::TM][C::TN]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t row = it.m_start + wm * C::WM + i * 16 + l16;
+    if (row >= it.m1) continue;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+      if (n >= p.N) continue;
+      const f32x4_t a = acc[i][j];
+      const int64_t off = row * p.N + n;
+      if constexpr (!SWB) {
+        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+      } else {
+        // a = dH; dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G)
+        const uint2 gw = *reinterpret_cast<const uint2*>(p.g + off);
+        const uint2 uw = *reinterpret_cast<const uint2*>(p.u + off);
+        const float gg[4] = {bf16lo(gw.x), bf16hi(gw.x), bf16lo(gw.y), bf16hi(gw.y)};
+        const float uu[4] = {bf16lo(uw.x), bf16hi(uw.x), bf16lo(uw.y), bf16hi(uw.y)};
+        float dg[4], du[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float s = sigmoidf_(gg[q]);
+          dg[q] = a[q] * uu[q] * s * (1.0f + gg[q] * (1.0f - s));
+          du[q] = a[q] * gg[q] * s;
+        }
+        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ Item claim_dg(const DgradParams& p, int* s_item, int& li, int xcd) {
+  return claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, 256, s_item, li, xcd);
+}
+
+template <class C>
+__device__ __forceinline__ void start_dg(const DgradParams& p, uint32_t lds0, const Item& it) {
+  tile::SrcB<C> src;
+  sources_dg<C>(p, it, src);
+  tile::prologue_b<C>(lds0, src, p.kcat ? 2 * p.nk : p.nk);
+}
+
+template <class C, bool SWB>
+__device__ __forceinline__ Item run_dg(const DgradParams& p, const uint8_t* smem, uint32_t lds0, int* s_item, int& li,
+                                       int xcd, const Item& it) {
+  tile::SrcB<C> src;
+  sources_dg<C>(p, it, src);
+  f32x4_t acc[C::TM][C::TN];
+  tile::mainloop_b<C>(smem, lds0, src, p.kcat ? 2 * p.nk : p.nk, 64, acc);
+  const Item next = claim_dg(p, s_item, li, xcd);
+  if (next.valid) {
+    if (next.big) start_dg<DgBig>(p, lds0, next);
+    else start_dg<DgSmall>(p, lds0, next);
+  }
+  epilogue_dg<C, SWB>(p, it, acc);
+  return next;
+}
+
+template <bool SWB>
+__global__ __launch_bounds__(512) void gemm_dgrad_kernel(DgradParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDgLds];
+  __shared__ int s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int xcd = xcd_id();
+  int li = 0;
+  Item it = claim_dg(p, &s_item, li, xcd);
+  if (!it.valid) return;
+  if (it.big) start_dg<DgBig>(p, lds0, it);
+  else start_dg<DgSmall>(p, lds0, it);
+  while (it.valid) {
+    if (it.big) it = run_dg<DgBig, SWB>(p, smem, lds0, &s_item, li, xcd, it);
+    else it = run_dg<DgSmall, SWB>(p, smem, lds0, &s_item, li, xcd, it);
+  }
+}
+
+// ---------------------------------------------------------------- wgrad ----
+
+struct WgradParams {
+  const int32_t* offsets;   // [E+1]
+  const int32_t* plan;      // [0] total items, [1 ..] expert order (most rows first)
+  int32_t* head;            // queue heads [kXcds]
+  int E, M, N;              // per expert: output rows M (forward n_dim), columns N (forward k_dim)
+  int m_tiles, n_tiles;
+  const uint8_t* a;         // dc [rows][M]
+  const uint8_t* b;         // forward operand [rows][N]
+  uint16_t* c;              // db [E][M][N]
+};
+
+using WgTile = tile::TileCfg<256, 256, 2, 4, 2, false, false, true, true>;   // 2 x 64 KB
+
+struct WgItem {
+  int e, r0, rows, m0, n0;
+  bool valid;
+};
+
+__device__ __forceinline__ WgItem claim_wg(const WgradParams& p, int* s_item, int xcd) {
+  const int item = claim_global(p.head, p.plan[0], s_item, xcd);
+  WgItem it{};
+  if (item < 0) return it;
+  const int per_e = p.m_tiles * p.n_tiles;
+  const int ei = item / per_e;
+  it.e = p.plan[1 + ei];
+  it.r0 = p.offsets[it.e];
+  it.rows = p.offsets[it.e + 1] - it.r0;
+  int mt, nt;
+  superblock_decode(item - ei * per_e, p.m_tiles, p.n_tiles, mt, nt);
+  it.m0 = mt * WgTile::BM;
+  it.n0 = nt * WgTile::BN;
+  it.valid = true;
+  return it;
+}
+
+__device__ __forceinline__ void sources_wg(const WgradParams& p, const WgItem& it, tile::SrcB<WgTile>& src) {
+  using namespace tile;
+  using C = WgTile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  src.a[0] = src.a[1] = uniform_ptr(p.a + (int64_t)it.r0 * p.M * 2);
+  src.b[0] = src.b[1] = uniform_ptr(p.b + (int64_t)it.r0 * p.N * 2);
+  src.a_rs = p.M * 2;
+  src.b_rs = p.N * 2;
+  src.a_lim = src.b_lim = it.rows - 1;
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int g = wave * C::A_INS + q;
+    src.a_off[q] = (uint32_t)(min(it.m0 + (g >> 3) * 64 + tchunk_of(g) * 8, p.M - 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) {
+    const int g = wave * C::B_INS + q;
+    src.b_off[q] = (uint32_t)(min(it.n0 + (g >> 3) * 64 + tchunk_of(g) * 8, p.N - 8) * 2);
+  }
+  src.nk1 = 1 << 30;
+}
+
+__device__ __forceinline__ int wg_steps(const WgItem& it) { return (it.rows + 63) / 64; }
+
+__device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& it,
+                                            const f32x4_t (&acc)[WgTile::TM][WgTile::TN]) {
+  using C = WgTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  const int l16 = lane & 15, lg = lane >> 4;
+  uint16_t* c = p.c + (int64_t)it.e * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int m = it.m0 + wm * C::WM + i * 16 + l16;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+      if (n >= p.N) continue;
+      const f32x4_t a = acc[i][j];
+      *reinterpret_cast<uint2*>(c + (int64_t)m * p.N + n) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WgTile::LDS];
+  __shared__ int s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int xcd = xcd_id();
+  WgItem it = claim_wg(p, &s_item, xcd);
+  if (!it.valid) return;
+  {
+    tile::SrcB<WgTile> src;
+    sources_wg(p, it, src);
+    tile::prologue_b<WgTile>(lds0, src, wg_steps(it));
+  }
+  while (it.valid) {
+    tile::SrcB<WgTile> src;
+    sources_wg(p, it, src);
+    f32x4_t acc[WgTile::TM][WgTile::TN];
+    const int nk = wg_steps(it);
+    tile::mainloop_b<WgTile>(smem, lds0, src, nk, it.rows - 64 * (nk - 1), acc);
+    const WgItem next = claim_wg(p, &s_item, xcd);
+    if (next.valid) {
+      tile::SrcB<WgTile> ns;
+      sources_wg(p, next, ns);
+      tile::prologue_b<WgTile>(lds0, ns, wg_steps(next));
+    }
+    epilogue_wg(p, it, acc);
+    it = next;
+  }
+}
+
+// Expert order for wgrad: most rows first (ties: lower id), one workgroup.
+__global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restrict__ offsets, int E, int per_e,
+                                                          int32_t* __restrict__ plan, int32_t* __restrict__ head) {
+  __shared__ int s_rows[1024];
+  const int t = threadIdx.x;
+  const int rows = t < E ? offsets[t + 1] - offsets[t] : -1;
+  s_rows[t] = rows;
+  __syncthreads();
+  if (t < E) {
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const int rf = s_rows[f];
+      rank += (rf > rows) || (rf == rows && f < t);
+    }
+    plan[1 + rank] = t;
+  }
+  if (t == 0) plan[0] = E * per_e;
+  if (t < kXcds) head[t] = 0;
+}
+
+hipError_t grid_for(const void* kern, int* grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 512, 0);
+  if (per_cu < 1) per_cu = 1;
+  *grid = cus * per_cu;
+  return err;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+// dgrad: contraction (forward n_dim) in whole 64-row steps, output columns
+// (forward k_dim) a multiple of 16, 16-byte aligned operands, 32-bit offsets
+bool gemm_dgrad_fast_ok(const GemmBwd& b) {
+  if (b.n_dim % 64 || b.k_dim % 16 || b.k_dim < 16) return false;
+  if (b.n_dim * b.k_dim * 2 >= (int64_t(1) << 31) || 256 * b.n_dim * 2 >= (int64_t(1) << 31)) return false;
+  if (!aligned16(b.dc0) || !aligned16(b.b0) || (b.dc1 && (!aligned16(b.dc1) || !aligned16(b.b1)))) return false;
+  if (b.swiglu_bwd ? (!aligned16(b.dg) || !aligned16(b.du) || !aligned16(b.g) || !aligned16(b.u)) : !aligned16(b.da))
+    return false;
+  return true;
+}
+
+hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) {
+  DgradParams p{};
+  p.offsets = b.offsets;
+  p.E = (int)b.E;
+  p.N = (int)b.k_dim;
+  p.K = (int)b.n_dim;
+  p.nk = (int)(b.n_dim / 64);
+  p.n_tiles = (int)((b.k_dim + 255) / 256);
+  p.kcat = b.dc1 != nullptr;
+  p.a0 = (const uint8_t*)b.dc0;
+  p.a1 = (const uint8_t*)b.dc1;
+  p.b0 = (const uint8_t*)b.b0;
+  p.b1 = (const uint8_t*)b.b1;
+  p.c0 = (uint16_t*)(b.swiglu_bwd ? b.dg : b.da);
+  p.c1 = (uint16_t*)b.du;
+  p.g = (const uint16_t*)b.g;
+  p.u = (const uint16_t*)b.u;
+  p.head = ws;
+  p.plan = ws + 16;
+  plan_rows_kernel<<<1, 1024, 0, s>>>(b.offsets, (int)b.E, p.n_tiles, ws + 16, ws);
+  const void* kern = b.swiglu_bwd ? (const void*)gemm_dgrad_kernel<true> : (const void*)gemm_dgrad_kernel<false>;
+  int grid = 0;
+  hipError_t err = grid_for(kern, &grid);
+  if (err != hipSuccess) return err;
+  if (b.swiglu_bwd) gemm_dgrad_kernel<true><<<grid, 512, 0, s>>>(p);
+  else gemm_dgrad_kernel<false><<<grid, 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// wgrad: both output dims multiples of 16 (at least 16), 16-byte aligned
+// operands, every row offset inside an expert's segment within 32 bits
+bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db) {
+  if (b.n_dim % 16 || b.k_dim % 16 || b.n_dim < 16 || b.k_dim < 16) return false;
+  const int64_t w = b.n_dim > b.k_dim ? b.n_dim : b.k_dim;
+  if ((b.rows_cap + 64) * w * 2 >= (int64_t(1) << 31)) return false;
+  return aligned16(dc) && aligned16(b.a) && aligned16(db);
+}
+
+hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s) {
+  WgradParams p{};
+  p.offsets = b.offsets;
+  p.E = (int)b.E;
+  p.M = (int)b.n_dim;
+  p.N = (int)b.k_dim;
+  p.m_tiles = (p.M + WgTile::BM - 1) / WgTile::BM;
+  p.n_tiles = (p.N + WgTile::BN - 1) / WgTile::BN;
+  p.a = (const uint8_t*)dc;
+  p.b = (const uint8_t*)b.a;
+  p.c = (uint16_t*)db;
+  p.head = ws;
+  p.plan = ws + 16;
+  plan_wgrad_kernel<<<1, 1024, 0, s>>>(b.offsets, p.E, p.m_tiles * p.n_tiles, ws + 16, ws);
+  int grid = 0;
+  hipError_t err = grid_for((const void*)gemm_wgrad_kernel, &grid);
+  if (err != hipSuccess) return err;
+  gemm_wgrad_kernel<<<grid, 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

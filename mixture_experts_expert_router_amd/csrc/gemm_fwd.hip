@@ -40,15 +40,13 @@
 #include "common.h"
 #include "launch.h"
 #include "mfma_tile.h"
+#include "sched.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBigRows = 256;    // experts with at least this many rows use 256-row tiles
-constexpr int kXcds = 8;         // XCDs of the chip; queue q holds chunks q, q + 8, ...
-constexpr int kChunk = 32;       // items per chunk (the CUs of one XCD)
-constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
+using namespace sched;
 
 struct FwdParams {
   const int32_t* offsets;   // [E+1]
@@ -70,17 +68,6 @@ struct FwdParams {
   uint8_t* hs;              //   and its E8M0 scales [rows][N/32]
 };
 
-// plan layout (int32): [0] total items, [1] number of listed experts L,
-// [2 .. 2+L) expert ids in processing order, [2+E .. 2+E+L] item prefix sums
-// (entry L = total).
-
-// A claimed queue item, decoded: rows [m_start, min(m_start + BM, m1)) of
-// expert e, output columns [n0, n0 + NCOL), tile class by the expert's rows.
-struct Item {
-  int e, m_start, m1, n0;
-  bool big, valid;
-};
-
 // The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
 template <bool DUAL, bool MX = false>
 using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL, MX>;     // 2 x 64 KB ring (+2 x 2 KB scales)
@@ -95,75 +82,10 @@ constexpr int lds_bytes() {
 }
 constexpr int kLdsBytes = lds_bytes<false>();
 
-__device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
-
-// XCD this workgroup runs on (hardware register XCC_ID).  Only locality
-// depends on it: any value in range gives the same results.
-__device__ __forceinline__ int xcd_id() {
-  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1));
-}
-
-// global position of the k-th item of queue q
-__device__ __forceinline__ int queue_item(int q, int k) { return (kXcds * (k / kChunk) + q) * kChunk + k % kChunk; }
-
-// Claim the next item and decode it (every thread gets the same result).
-// Queue q's items have increasing positions and end at the first one past
-// the total, so a failed claim means the queue is exhausted.  li is the
-// workgroup's position in the expert list, walked forward for its own queue's
-// increasing items and searched for items taken from other queues.
+// Claim the next item of the row scheduler and decode it.
 template <bool DUAL>
 __device__ __forceinline__ Item claim(const FwdParams& p, int* s_item, int& li, int xcd) {
-  const int total = p.plan[0];
-  if (threadIdx.x == 0) {
-    int g = -1;
-    for (int t = 0; t < kXcds; ++t) {
-      const int q = (xcd + t) & (kXcds - 1);
-      const int gi = queue_item(q, atomicAdd(p.head + q, 1));
-      if (gi < total) {
-        g = gi;
-        break;
-      }
-    }
-    *s_item = g;
-  }
-  __syncthreads();
-  const int item = __builtin_amdgcn_readfirstlane(*s_item);   // same for every lane
-  Item it{};
-  if (item < 0) return it;
-  const int L = p.plan[1];
-  const int32_t* order = p.plan + 2;
-  const int32_t* pref = p.plan + 2 + p.E;
-  if (pref[li] > item) {   // an earlier item (taken from another queue): binary search
-    int lo = 0, hi = L - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pref[mid] <= item) lo = mid;
-      else hi = mid - 1;
-    }
-    li = lo;
-  }
-  while (li + 1 < L && pref[li + 1] <= item) ++li;
-  it.e = order[li];
-  const int m0 = p.offsets[it.e];
-  it.m1 = p.offsets[it.e + 1];
-  it.big = is_big(it.m1 - m0);
-  const int bm = it.big ? BigTile<DUAL>::BM : SmallTile<DUAL>::BM;
-  const int nmb = (it.m1 - m0 + bm - 1) / bm;
-  // item w of the expert: n-groups of kSbN tiles, in each m-groups of kSbM
-  // row blocks, row block fastest (the last group of each kind may be short)
-  const int w = item - pref[li];
-  const int gn = w / (kSbN * nmb);
-  const int w1 = w - gn * kSbN * nmb;
-  const int nb = min(kSbN, p.n_tiles - gn * kSbN);
-  const int gm = w1 / (kSbM * nb);
-  const int w2 = w1 - gm * kSbM * nb;
-  const int mbk = min(kSbM, nmb - gm * kSbM);
-  const int mb = gm * kSbM + w2 % mbk;
-  const int n_t = gn * kSbN + w2 / mbk;
-  it.m_start = m0 + mb * bm;
-  it.n0 = n_t * BigTile<DUAL>::NCOL;
-  it.valid = true;
-  return it;
+  return claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_item, li, xcd);
 }
 
 // DMA sources of an item (rows past the expert's segment or columns past N
@@ -339,84 +261,9 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   }
 }
 
-// Planner: one workgroup of 1024 threads (E <= 1024).  Each expert with rows
-// gets ceil(rows / BM) * n_tiles items, BM by its tile class.  The experts of
-// each class keep ascending id; the two classes are merged by the midpoint of
-// each expert's items within its class, so both progress at the same rate.
-__global__ __launch_bounds__(1024) void plan_fwd_kernel(const int32_t* __restrict__ offsets, int E, int n_tiles,
-                                                        int32_t* __restrict__ plan, int32_t* __restrict__ head) {
-  __shared__ int s_w0[16], s_w1[16], s_tot[2];
-  __shared__ float s_key[1024];
-  __shared__ int s_items[1024], s_ids[1024], s_pref[16];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  int items = 0, big = 0;
-  if (t < E) {
-    const int m = offsets[t + 1] - offsets[t];
-    big = is_big(m);
-    const int bm = big ? BigTile<true>::BM : SmallTile<true>::BM;
-    items = m > 0 ? ((m + bm - 1) / bm) * n_tiles : 0;
-  }
-  int i0 = big ? 0 : items, i1 = big ? items : 0;   // per-class inclusive scans
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(i0, o, 64), b = __shfl_up(i1, o, 64);
-    if (lane >= o) { i0 += a; i1 += b; }
-  }
-  if (lane == 63) { s_w0[wv] = i0; s_w1[wv] = i1; }
-  __syncthreads();
-  if (t == 0) {
-    int r0 = 0, r1 = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int a = s_w0[w], b = s_w1[w];
-      s_w0[w] = r0; s_w1[w] = r1;
-      r0 += a; r1 += b;
-    }
-    s_tot[0] = r0; s_tot[1] = r1;
-  }
-  __syncthreads();
-  const int pre = big ? (i1 - items + s_w1[wv]) : (i0 - items + s_w0[wv]);
-  const int tot = s_tot[big];
-  s_key[t] = (items > 0) ? ((float)pre + 0.5f * (float)items) / (float)tot : 2.0f;
-  __syncthreads();
-  if (items > 0) {
-    const float k = s_key[t];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const float kf = s_key[f];
-      rank += (kf < k) || (kf == k && f < t);
-    }
-    s_items[rank] = items;
-    s_ids[rank] = t;
-  }
-  const int L = __syncthreads_count(items > 0);
-  // exclusive scan of the items in rank order
-  const int v = t < L ? s_items[t] : 0;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += a;
-  }
-  if (lane == 63) s_pref[wv] = inc;
-  __syncthreads();
-  if (t == 0) {
-    int r = 0;
-    for (int w = 0; w < 16; ++w) { const int a = s_pref[w]; s_pref[w] = r; r += a; }
-    plan[0] = r;
-    plan[1] = L;
-    plan[2 + E + L] = r;
-  }
-  if (t < kXcds) head[t] = 0;
-  __syncthreads();
-  if (t < L) {
-    plan[2 + t] = s_ids[t];
-    plan[2 + E + t] = inc - v + s_pref[wv];
-  }
-}
-
 template <bool DUAL, bool MX>
 hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
-  plan_fwd_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, p.n_tiles, plan, p.head);
+  plan_rows_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, p.n_tiles, plan, p.head);
   auto kern = gemm_fwd_kernel<DUAL, MX>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -775,7 +622,7 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   f.st = st;
   f.fplan = fplan;
   const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
-  plan_fwd_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
+  plan_rows_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
   plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, fplan, st);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);

@@ -106,6 +106,13 @@ bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim);
 bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx);
 hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStream_t s);
 
+// gemm_bwd.hip: persistent backward GEMMs (shape and alignment rules in the
+// *_fast_ok predicates; ws is the GEMM table workspace)
+bool gemm_dgrad_fast_ok(const GemmBwd& b);
+hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s);
+bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db);
+hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s);
+
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);
 

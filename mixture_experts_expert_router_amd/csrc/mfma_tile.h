@@ -79,10 +79,12 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ (r & 7); }
 
-template <int BM_, int BN_, int NS_, int WAVES_M, int WAVES_N, bool DUAL_, bool MX_ = false>
+template <int BM_, int BN_, int NS_, int WAVES_M, int WAVES_N, bool DUAL_, bool MX_ = false, bool AT_ = false,
+          bool BT_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, NS = NS_;
   static constexpr bool DUAL = DUAL_, MX = MX_;
+  static constexpr bool AT = AT_, BT = BT_;   // operand stored k-major (transposed), see below
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int WAVES_N_ = WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -105,6 +107,8 @@ struct TileCfg {
   static_assert(NS >= 2 && LDS <= 160 * 1024 - 64, "LDS ring");
   static_assert(!MX || (SRW % 16 == 0 && BM % 16 == 0 && (BN / 2) % 16 == 0 && NS <= 3),
                 "whole 16-row scale loads, each from one operand; at most one step in flight past the current");
+  static_assert((!AT || BM % 64 == 0) && (!BT || BN % 64 == 0) && !((AT || BT) && (MX || DUAL)),
+                "k-major tiles: whole 64-column blocks, bf16, single B");
 };
 
 // Row of the B tile that B fragment j of a wave reads, less the wave's own
@@ -303,6 +307,168 @@ __device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, 
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], acc[i][j], 0, 0, 0, scur, 0, sa[i]);
       bcur = bnext;
       scur = snext;
+    }
+  }
+  __syncthreads();   // every wave is done reading the ring before it is refilled
+}
+
+// ---------------------------------------------------------------------------
+// k-major (transposed-storage) operands, for the backward GEMMs: the operand
+// is stored with its contraction index k as the row and the tile's own index
+// x contiguous (a weight read as W^T, or activations contracted over rows).
+// A k-major tile of X columns holds X/64 column blocks of 64 k-rows x 128
+// bytes; DMA instruction g (0 .. X/8-1) writes column block g/8, k-rows
+// (g%8)*8 .. +7 at LDS byte g*1024 (the same places as a row-major tile's
+// instructions), and chunk c of k-row r sits at slot c ^ tswz(r).  Fragments
+// are read with ds_read_b64_tr_b16, which, per 16-lane group, hands output
+// lane i the element i%4 of the 8 bytes addressed by source lane 4j + i/4 as
+// its j-th value (measured on gfx950).  Lane (l16 = s, lg) therefore points at
+// k-row 8 lg + s/4 (+4 for the second read) and columns x0 + 4 (s%4): both
+// reads give it row x0 + l16 of the fragment at k = 8 lg .. 8 lg + 7, the
+// MFMA operand layout.  With tswz the 8 k-rows one 32-lane pass reads fall on
+// 8 distinct bank ranges (checked by a bank model of every fragment).
+// ---------------------------------------------------------------------------
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+__device__ __host__ __forceinline__ int tswz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+
+// k-row within its 64-row step, and the 16-byte column chunk, that this lane
+// loads in DMA instruction g of a k-major tile
+__device__ __forceinline__ int trow_of(int g) { return ((g & 7) << 3) + ((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int tchunk_of(int g) {
+  const int lane = threadIdx.x & 63;
+  return (lane & 7) ^ tswz(((g & 7) << 3) + (lane >> 3));
+}
+
+// Per-lane parts of a k-major fragment address.
+struct TBase {
+  uint32_t tb, G;
+  __device__ __forceinline__ TBase() {
+    const int lane = threadIdx.x & 63;
+    const int s = lane & 15, lg = lane >> 4;
+    tb = (uint32_t)((8 * lg + (s >> 2)) * kRB + (s & 1) * 8);
+    G = (uint32_t)(((((s >> 3) & 1) << 1) | ((lg & 1) << 2) | ((s >> 1) & 1)) << 4);
+  }
+};
+
+// Fragment of a k-major tile at tile byte offset `tile`: rows x0 .. x0+15 (x0
+// a multiple of 16), contraction substep ks (32 k each).
+__device__ __forceinline__ bf16x8_t tfrag(const uint8_t* smem, uint32_t tile, const TBase& t, int x0, int ks) {
+  const uint32_t off = tile + (uint32_t)((x0 >> 6) * 8192 + ks * 4096) + t.tb + ((uint32_t)(((x0 & 63) >> 3) << 4) ^ t.G);
+  typedef __attribute__((address_space(3))) v4i16_t* lp;
+  const __attribute__((address_space(3))) uint8_t* l = (const __attribute__((address_space(3))) uint8_t*)smem;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(l + off));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(l + off + 512));
+  const v4i16_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+}
+
+// DMA sources of a backward tile.  K may be the concatenation of two
+// products (bases [0] for steps < nk1, [1] after; same offsets).  Row-major
+// operands: offsets at step 0, advanced kRB bytes a step through the base.
+// k-major operands: the column byte offset of the lane's chunk; its k-row
+// (step * 64 + trow) is clamped to `lim` (rows past it reload it) and scaled
+// by the row stride `rs` when issued.
+template <class C>
+struct SrcB {
+  const uint8_t* a[2];
+  const uint8_t* b[2];
+  int nk1;
+  uint32_t a_off[C::A_INS];
+  uint32_t b_off[C::B_INS];
+  int a_rs, b_rs, a_lim, b_lim;
+};
+
+template <class C>
+__device__ __forceinline__ void issue_step_b(uint32_t lds0, const SrcB<C>& src, int kt) {
+  const int wave = threadIdx.x >> 6;
+  const uint32_t st = lds0 + (uint32_t)((kt % C::NS) * C::STAGE);
+  const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;
+  const uint32_t wave_b = st + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
+  const bool second = kt >= src.nk1;
+  const int kk = second ? kt - src.nk1 : kt;
+  const uint8_t* a = second ? src.a[1] : src.a[0];
+  const uint8_t* b = second ? src.b[1] : src.b[0];
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(wave_a + q * 1024u);
+    if constexpr (C::AT) {
+      const int row = min(kk * 64 + trow_of(wave * C::A_INS + q), src.a_lim);
+      lds_dma16(a, (uint32_t)row * (uint32_t)src.a_rs + src.a_off[q], dst);
+    } else {
+      lds_dma16(a + (int64_t)kk * kRB, src.a_off[q], dst);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(wave_b + q * 1024u);
+    if constexpr (C::BT) {
+      const int row = min(kk * 64 + trow_of(wave * C::B_INS + q), src.b_lim);
+      lds_dma16(b, (uint32_t)row * (uint32_t)src.b_rs + src.b_off[q], dst);
+    } else {
+      lds_dma16(b + (int64_t)kk * kRB, src.b_off[q], dst);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void prologue_b(uint32_t lds0, const SrcB<C>& src, int nk) {
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < nk) issue_step_b<C>(lds0, src, s);
+}
+
+// Backward main loop over nk steps.  b_tail < 64: only the first b_tail
+// k-rows of the last step are valid, and the B tile's other k-rows are zeroed
+// after they land, so clamped reloads of the last valid row add nothing.
+template <class C>
+__device__ __forceinline__ void mainloop_b(const uint8_t* smem, uint32_t lds0, const SrcB<C>& src, int nk, int b_tail,
+                                           f32x4_t (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
+  const FragBase<C> fb;
+  const TBase tbase;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+    __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
+    if constexpr (C::BT) {
+      if (kt == nk - 1 && b_tail < 64) {
+        uint8_t* bt = const_cast<uint8_t*>(smem) + (kt % NS) * C::STAGE + C::A_BYTES;
+        const int n16 = (64 - b_tail) * 8;   // 16-byte pieces per column block
+        for (int idx = threadIdx.x; idx < n16 * (C::BN / 64); idx += C::NW * 64) {
+          const int cb = idx / n16, w = idx - cb * n16;
+          *reinterpret_cast<uint4*>(bt + cb * 8192 + (b_tail + (w >> 3)) * kRB + (w & 7) * 16) = make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+      }
+    }
+    if (kt + NS - 1 < nk) issue_step_b<C>(lds0, src, kt + NS - 1);
+    const uint32_t so = (uint32_t)((kt % NS) * C::STAGE);
+    const uint8_t* st = smem + so;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (C::AT) af[i] = tfrag(smem, so, tbase, wm * C::WM + i * 16, ks);
+        else af[i] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.a_hi : fb.a_lo) + i * 16 * kRB);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (C::BT) bfr[j] = tfrag(smem, so + C::A_BYTES, tbase, wn * C::WNB + b_frag_row<C>(j), ks);
+        else bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.b_hi : fb.b_lo) + b_frag_row<C>(j) * kRB);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
   __syncthreads();   // every wave is done reading the ring before it is refilled

@@ -243,6 +243,13 @@ GEMM_CASES = [
     ((2000, 1700), 128, 160, 0),
     ((5000,), 64, 512, 3),
     ((3, 0, 0, 90, 0, 17, 0, 0, 200, 1, 0, 64, 0, 0, 0, 33), 320, 96, 0),
+    # shapes the persistent backward kernels take (dgrad: n % 64 == 0 and
+    # k % 16 == 0; wgrad: n, k % 16 == 0): partial 256-column tiles, ragged
+    # and empty experts, experts above and below 256 rows
+    ((0, 1, 130, 64, 257), 176, 320, 8),
+    ((300, 0, 700, 17), 208, 192, 0),
+    ((3, 0, 0, 90, 0, 17, 0, 0, 200, 1, 0, 64, 0, 0, 0, 33), 144, 64, 0),
+    ((1100,), 48, 128, 5),
 ]
 
 
