@@ -72,13 +72,17 @@ struct FwdParams {
 template <bool DUAL, bool MX = false>
 using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL, MX>;     // 2 x 64 KB ring (+2 x 2 KB scales)
 template <bool DUAL, bool MX = false>
-using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB ring (+3 x 2 KB scales)
+using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB ring (+ scale groups)
+// bf16 experts with at most 64 rows: the same columns, half the A rows
+template <bool DUAL, bool MX = false>
+using TinyTile = tile::TileCfg<64, 256, 3, 2, 4, DUAL, MX>;     // 3 x 40 KB ring
 template <bool MX>
 constexpr int lds_bytes() {
   constexpr int s = SmallTile<true, MX>::LDS, s1 = SmallTile<false, MX>::LDS;
   constexpr int b = BigTile<true, MX>::LDS, b1 = BigTile<false, MX>::LDS;
-  constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1;
-  return m0 > m1 ? m0 : m1;
+  constexpr int t = TinyTile<true, false>::LDS, t1 = TinyTile<false, false>::LDS;
+  constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1, m2 = t > t1 ? t : t1;
+  return m0 > m1 ? (m0 > m2 ? m0 : m2) : (m1 > m2 ? m1 : m2);
 }
 constexpr int kLdsBytes = lds_bytes<false>();
 
@@ -121,9 +125,9 @@ __device__ __forceinline__ void sources(const FwdParams& p, const Item& it, tile
 #pragma unroll
     for (int q = 0; q < C::SCI; ++q) {
       const int r0 = wave * C::SRW + q * 16;
-      if (r0 < C::BM) {
+      if (r0 < C::BM || r0 >= C::BM + C::BN) {   // A rows, or padding (reloads the item's A rows)
         src.s[q] = uniform_ptr(a_sc);
-        src.s_row0[q] = r0;
+        src.s_row0[q] = r0 < C::BM ? r0 : 0;
         src.s_lim[q] = __builtin_amdgcn_readfirstlane(it.m1 - it.m_start - 1);
       } else {
         const bool up = C::DUAL && r0 >= C::BM + C::BN / 2;
@@ -236,6 +240,7 @@ __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem
   const Item next = claim<DUAL>(p, s_item, li, xcd);
   if (next.valid) {
     if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
+    else if (!C::MX && next.tiny) start<TinyTile<DUAL, false>>(p, lds0, next);
     else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
   }
   epilogue<C>(p, it, acc);
@@ -249,14 +254,17 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   using Big = BigTile<DUAL, MX>;
   using Small = SmallTile<DUAL, MX>;
+  using Tiny = TinyTile<DUAL, false>;   // bf16 only (no gain measured for MXFP8)
   const int xcd = xcd_id();
   int li = 0;
   Item it = claim<DUAL>(p, &s_item, li, xcd);
   if (!it.valid) return;
   if (it.big) start<Big>(p, lds0, it);
+  else if (!MX && it.tiny) start<Tiny>(p, lds0, it);
   else start<Small>(p, lds0, it);
   while (it.valid) {
     if (it.big) it = run_item<Big, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
+    else if (!MX && it.tiny) it = run_item<Tiny, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
     else it = run_item<Small, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
   }
 }

@@ -94,9 +94,11 @@ struct TileCfg {
   static constexpr int A_BYTES = BM * kRB, STAGE = (BM + BN) * kRB;
   static constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;   // per wave per step
   static constexpr int LPS = A_INS + B_INS;                        // loads per wave per step
-  // MX scale groups: 16 bytes per tile row, SCI loads of 16 rows per wave
-  static constexpr int SG_BYTES = (BM + BN) * 16;
-  static constexpr int SRW = (BM + BN) / NW;                       // scale rows per wave
+  // MX scale groups: 16 bytes per tile row (rows past BM + BN are padding
+  // that reloads an A row), SCI loads of 16 rows per wave
+  static constexpr int SC_ROWS = (BM + BN + NW * 16 - 1) / (NW * 16) * (NW * 16);
+  static constexpr int SG_BYTES = SC_ROWS * 16;
+  static constexpr int SRW = SC_ROWS / NW;                         // scale rows per wave
   static constexpr int SCI = MX ? SRW / 16 : 0;
   static constexpr int SC_BASE = NS * STAGE;                        // group buffers after the ring
   static constexpr int LDS = NS * STAGE + (MX ? 2 * SG_BYTES : 0);

@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kBigRows = 256;       // experts with at least this many rows use 256-row blocks
 constexpr int kBigBM = 256, kSmallBM = 128;
+constexpr int kTinyRows = 64;       // small experts this short may use 64-row tiles
 constexpr int kXcds = 8;            // XCDs of the chip; queue q holds chunks q, q + 8, ...
 constexpr int kChunk = 32;          // items per chunk (the CUs of one XCD)
 constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
@@ -35,6 +36,7 @@ constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
 struct Item {
   int e, m_start, m1, n0;
   bool big, valid;
+  bool tiny;   // the expert has at most kTinyRows rows (one row block either way)
 };
 
 __device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
@@ -108,6 +110,7 @@ __device__ __forceinline__ Item claim_rows(const int32_t* plan, const int32_t* o
   const int m0 = offsets[it.e];
   it.m1 = offsets[it.e + 1];
   it.big = is_big(it.m1 - m0);
+  it.tiny = it.m1 - m0 <= kTinyRows;
   const int bm = it.big ? kBigBM : kSmallBM;
   const int nmb = (it.m1 - m0 + bm - 1) / bm;
   int mb, n_t;
