@@ -222,6 +222,9 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
     if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1, nk);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
+    // dual-B tiles: MFMAs at raised wave priority, so the other wave of the
+    // SIMD issues its fragment reads while these run (measured +3% on the
+    // gate/up GEMM, -3% on single-B tiles)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint8_t* sa = st + (ks ? fb.a_hi : fb.a_lo);
@@ -231,11 +234,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
       for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(sa + i * 16 * kRB);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + b_frag_row<C>(j) * kRB);
+      if constexpr (C::DUAL) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      if constexpr (C::DUAL) __builtin_amdgcn_s_setprio(0);
     }
   }
   __syncthreads();   // every wave is done reading the ring before it is refilled
