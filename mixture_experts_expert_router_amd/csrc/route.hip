@@ -5,8 +5,9 @@
 // Three launches, none with a contended global atomic (the multi-XCD atomic
 // trap described in the Meta MI350X paper, section IV-B1):
 //   1. route_topk: one wave per token computes softmax and top-K; each
-//      workgroup owns a chunk of kChunk tokens and, in LDS, the stable rank of
-//      every route inside its chunk plus the chunk's per-expert histogram.
+//      workgroup (one wave per token of its chunk) owns a chunk of kChunk
+//      tokens and, in LDS, the stable rank of every route inside its chunk
+//      plus the chunk's per-expert histogram.
 //   2. route_scan: one workgroup turns the [chunks][E] histogram into counts,
 //      aligned offsets and the first row of every (chunk, expert) pair.
 //   3. route_scatter: every valid route's row = base(chunk, e) + rank.
@@ -15,7 +16,8 @@
 
 namespace moe {
 
-constexpr int kChunk = 16;         // tokens per workgroup in route_topk (4 per wave)
+constexpr int kChunk = 16;         // tokens per workgroup in route_topk (one per wave)
+constexpr int kTopkThreads = kChunk * 64;
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;
 
@@ -24,7 +26,7 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void route_topk_kernel(
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, const uint8_t* __restrict__ drop, int N, int E, int K,
     int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
     int32_t* __restrict__ row_route, int64_t rows_cap, int32_t* __restrict__ hist,
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     row_route[i] = -1;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
 
-  for (int tl = wave; tl < kChunk; tl += 4) {
+  for (int tl = wave; tl < kChunk; tl += kTopkThreads / 64) {
     const int t = t0 + tl;
     if (t >= N) {
       if (lane < K) s_sel[tl * K + lane] = -1;
@@ -134,7 +136,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   const int g = threadIdx.x / Ep;
   int sum = 0;
   if (e < E) {
-    for (int c = g * cpg; c < min(nchunks, (g + 1) * cpg); ++c) sum += hist[(int64_t)c * E + e];
+    // loads in batches of 16, so they are in flight together
+    const int c1 = min(nchunks, (g + 1) * cpg);
+    for (int c0 = g * cpg; c0 < c1; c0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = c0 + i < c1 ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += h[i];
+    }
   }
   s_part[threadIdx.x] = sum;
   __syncthreads();
@@ -177,10 +187,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   for (int ee = threadIdx.x; ee <= E; ee += blockDim.x) offsets[ee] = s_off[ee];
   if (e < E) {
     int run = s_off[e] + s_part[g * Ep + e];
-    for (int c = g * cpg; c < min(nchunks, (g + 1) * cpg); ++c) {
-      int h = hist[(int64_t)c * E + e];
-      hist[(int64_t)c * E + e] = run;            // first row of (chunk, e)
-      run += h;
+    const int c1 = min(nchunks, (g + 1) * cpg);
+    for (int c0 = g * cpg; c0 < c1; c0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = c0 + i < c1 ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < c1) hist[(int64_t)(c0 + i) * E + e] = run;   // first row of (chunk, e)
+        run += h[i];
+      }
     }
   }
 }
@@ -221,12 +237,12 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
   size_t hb = ((size_t)nalloc * E * 4 + 255) & ~(size_t)255;
   int32_t* rank = (int32_t*)((char*)ws + hb);
   if (nchunks > 0) {
-    route_topk_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
+    route_topk_kernel<<<dim3((unsigned)nchunks), dim3(kTopkThreads), 0, s>>>(
         logits, drop, (int)N, (int)E, (int)K, renorm, topk_idx, topk_prob, row_route, rows_cap,
         hist, rank);
   } else {
     // no tokens: still mark every row unused
-    route_topk_kernel<<<dim3(1), dim3(256), 0, s>>>(logits, drop, 0, (int)E, (int)K, renorm,
+    route_topk_kernel<<<dim3(1), dim3(kTopkThreads), 0, s>>>(logits, drop, 0, (int)E, (int)K, renorm,
                                                     topk_idx, topk_prob, row_route, rows_cap,
                                                     hist, rank);
   }
