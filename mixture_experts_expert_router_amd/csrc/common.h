@@ -59,59 +59,20 @@ __device__ __forceinline__ float exp2i(int k) {
   return __uint_as_float(1u << (k + 149));
 }
 
-// E4M3FN encode of y = v * 2^-e, with the scaling done exactly.  v is a bf16
-// value and e in [-127, 127], so v * 2^-e may leave the fp32 range only above
-// 2^128, which saturates anyway; below the E4M3 grid everything rounds in the
-// integer domain.  Round to nearest even, saturate to 448, keep the sign.
-__device__ __forceinline__ uint32_t e4m3_from_scaled(float v, int e) {
-  uint32_t bits = __float_as_uint(v);
-  uint32_t sign = (bits >> 24) & 0x80u;
-  uint32_t a = bits & 0x7FFFFFFFu;
-  if (a == 0) return sign;
-  // exponent of |v| and its 24-bit significand (bf16 inputs are normal or
-  // subnormal fp32; handle both)
-  int ev = (int)(a >> 23);
-  uint32_t sig;
-  int E;                       // |v| = sig * 2^(E - 23), sig in [2^23, 2^24)
-  if (ev != 0) {
-    sig = (a & 0x7FFFFFu) | 0x800000u;
-    E = ev - 127;
-  } else {
-    uint32_t m = a;
-    int lz = __clz((int)m) - 8;  // shift to put the top bit at bit 23
-    sig = m << lz;
-    E = -126 - lz;
-  }
-  int Ey = E - e;              // exponent of |y|
-  // quantum exponent: max(Ey, -6) - 3
-  int qe = (Ey > -6 ? Ey : -6) - 3;
-  // n = |y| / 2^qe = sig * 2^(Ey - 23 - qe); round to nearest even
-  int sh = 23 + qe - Ey;       // >= 20 (qe >= Ey - 3)
-  uint32_t n;
-  if (sh >= 32) {
-    n = 0;                     // sig < 2^24 < 2^(sh-1): below half a quantum
-  } else {
-    uint32_t q = sig >> sh;
-    uint32_t rem = sig & ((1u << sh) - 1u);
-    uint32_t half = 1u << (sh - 1);
-    n = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
-  }
-  // value = n * 2^qe; encode
-  uint32_t code;
-  if (qe == -9) {
-    // subnormal grid (or rounded up to the first normal 8 * 2^-9 = 2^-6)
-    code = n;                  // n in [0, 8]; n = 8 encodes 0x08 = 2^-6
-  } else {
-    // n in [8, 16]; n = 16 moves to the next binade
-    int Eo = qe + 3;
-    if (n == 16) { n = 8; Eo += 1; }
-    if (Eo > 8 || (Eo == 8 && n > 14)) {
-      code = 0x7Eu;            // saturate to 448
-    } else {
-      code = ((uint32_t)(Eo + 7) << 3) | (n - 8);
-    }
-  }
-  return sign | code;
+// E4M3FN codes of v0..v3 scaled by 2^-e, packed into one word (byte i from
+// vi).  The inputs are bf16 values of one block and e = e8m0_code(amax) - 127,
+// so |v * 2^-e| < 2^9 and the product is exact wherever it can round to a
+// nonzero code.  Clamping to +-448 first makes the conversion saturate; the
+// gfx950 conversion then rounds to nearest even and keeps the sign of zero,
+// which agrees with the OCP rule on every finite bf16 value and every scale
+// exponent a block can take (checked exhaustively).
+__device__ __forceinline__ float e4m3_prep(float v, float s) { return fminf(fmaxf(v * s, -448.0f), 448.0f); }
+
+__device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3, int e) {
+  const float s = exp2i(-e);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v0, s), e4m3_prep(v1, s), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v2, s), e4m3_prep(v3, s), w, true);
+  return (uint32_t)w;
 }
 
 // ---- small vector helpers ---------------------------------------------------

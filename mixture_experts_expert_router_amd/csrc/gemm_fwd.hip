@@ -209,12 +209,8 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
           amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
           amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
           const int code = e8m0_code(amax);
-          uint32_t q0 = 0, q1 = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            q0 |= e4m3_from_scaled(v[q], code - 127) << (8 * q);
-            q1 |= e4m3_from_scaled(v[4 + q], code - 127) << (8 * q);
-          }
+          const uint32_t q0 = e4m3x4(v[0], v[1], v[2], v[3], code - 127);
+          const uint32_t q1 = e4m3x4(v[4], v[5], v[6], v[7], code - 127);
           const int nb = it.n0 + wn * (WN / 2) + j * 16;
           if (nb >= p.N) continue;
           uint8_t* qrow = p.hq + row * p.N + nb + 4 * lg;

@@ -238,12 +238,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_mxfp8_kernel(MxPar
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const int code = e8m0_code(amax);
-        uint32_t q0 = 0, q1 = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          q0 |= e4m3_from_scaled(v[q], code - 127) << (8 * q);
-          q1 |= e4m3_from_scaled(v[4 + q], code - 127) << (8 * q);
-        }
+        const uint32_t q0 = e4m3x4(v[0], v[1], v[2], v[3], code - 127);
+        const uint32_t q1 = e4m3x4(v[4], v[5], v[6], v[7], code - 127);
         const int n = wn * WN + j * 16 + 4 * lg;
         if (mok && n < n_valid) {
           uint8_t* qrow = p.hq + row * p.N + n0;

@@ -72,12 +72,8 @@ __device__ __forceinline__ uint2 quant_vec(uint4 v, int& code_out) {
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int code = e8m0_code(amax);
   const int e = code - 127;
-  uint32_t b[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b[i] = e4m3_from_scaled(f[i], e);
   code_out = code;
-  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  return make_uint2(e4m3x4(f[0], f[1], f[2], f[3], e), e4m3x4(f[4], f[5], f[6], f[7], e));
 }
 
 // dispatch (MXFP8): quantize each token row once along D, write q and scales
@@ -113,6 +109,69 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
         if (v < nvec) {
           *reinterpret_cast<uint2*>(q + (int64_t)dst[k] * D + v * 8) = qv[j];
           if ((v & 3) == 0) sc[(int64_t)dst[k] * (D >> 5) + (v >> 2)] = (uint8_t)code[j];
+        }
+      }
+    }
+  }
+}
+
+// Same result for D % 128 == 0: each lane quantizes 16 adjacent elements (a
+// 32-block is a lane pair), so a route gets one 16-byte data store per lane
+// and lanes 8i pack the codes of four consecutive blocks into one 4-byte store.
+__device__ __forceinline__ uint32_t quant4(const float* f, int e) {
+  return e4m3x4(f[0], f[1], f[2], f[3], e);
+}
+
+__global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16_t* __restrict__ x,
+                                                                    const int32_t* __restrict__ dst_rows,
+                                                                    int N, int D, int K,
+                                                                    uint8_t* __restrict__ q,
+                                                                    uint8_t* __restrict__ sc) {
+  constexpr int PP = 2;   // lane pairs of vectors per pass
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= N) return;
+  int dst[32];
+  for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
+  const int npair = D >> 4;              // 16-element pieces per row
+  const int nblk = D >> 5;
+  const uint16_t* src = x + (int64_t)t * D;
+  for (int p0 = 0; p0 < npair; p0 += kWave * PP) {
+    uint4 qv[PP];
+    uint32_t packed[PP];
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      const int pc = p0 + lane + j * kWave;   // this lane's 16-element piece
+      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
+      if (pc < npair) {
+        r0 = ldg16(src + pc * 16);
+        r1 = ldg16(src + pc * 16 + 8);
+      }
+      float f[16] = {bf16lo(r0.x), bf16hi(r0.x), bf16lo(r0.y), bf16hi(r0.y), bf16lo(r0.z), bf16hi(r0.z),
+                     bf16lo(r0.w), bf16hi(r0.w), bf16lo(r1.x), bf16hi(r1.x), bf16lo(r1.y), bf16hi(r1.y),
+                     bf16lo(r1.z), bf16hi(r1.z), bf16lo(r1.w), bf16hi(r1.w)};
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const int code = e8m0_code(amax);
+      const int e = code - 127;
+      qv[j] = make_uint4(quant4(f, e), quant4(f + 4, e), quant4(f + 8, e), quant4(f + 12, e));
+      // block codes of lanes 8i, 8i+2, 8i+4, 8i+6 into lane 8i
+      const uint32_t c1 = (uint32_t)__shfl_down(code, 2, 64), c2 = (uint32_t)__shfl_down(code, 4, 64),
+                     c3 = (uint32_t)__shfl_down(code, 6, 64);
+      packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    for (int k = 0; k < K; ++k) {
+      if (dst[k] < 0) continue;
+      uint8_t* qrow = q + (int64_t)dst[k] * D;
+      uint8_t* srow = sc + (int64_t)dst[k] * nblk;
+#pragma unroll
+      for (int j = 0; j < PP; ++j) {
+        const int pc = p0 + lane + j * kWave;
+        if (pc < npair) {
+          *reinterpret_cast<uint4*>(qrow + pc * 16) = qv[j];
+          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(srow + (pc >> 1)) = packed[j];
         }
       }
     }
@@ -209,56 +268,72 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ y, int N,
                                                           int D, int K, uint16_t* __restrict__ dyd,
                                                           float* __restrict__ dprob) {
-  constexpr int VPL = 4;
+  // routes in chunks of KCH: every Y row of the chunk is loaded before any
+  // product uses it, so the gathers overlap instead of waiting one by one;
+  // each lane still sums its vectors in increasing order
+  constexpr int VPL = 2, KCH = 8;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[32];
-  float w[32], dot[32];
-  for (int k = 0; k < K; ++k) {
-    dst[k] = dst_rows[(int64_t)t * K + k];
-    w[k] = weight[(int64_t)t * K + k];
-    dot[k] = 0.0f;
-  }
   const int nvec = D >> 3;
   const uint16_t* src = dout + (int64_t)t * D;
-  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-    uint4 r[VPL];
+  for (int kb = 0; kb < K; kb += KCH) {
+    int dk[KCH];
+    float wk[KCH], dot[KCH];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + lane + j * kWave;
-      if (v < nvec) r[j] = ldg16(src + v * 8);
+    for (int kk = 0; kk < KCH; ++kk) {
+      const int k = kb + kk;
+      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : -1;
+      wk[kk] = k < K ? weight[(int64_t)t * K + k] : 0.0f;
+      dot[kk] = 0.0f;
     }
-    for (int k = 0; k < K; ++k) {
-      if (dst[k] < 0) continue;
-      uint16_t* o = dyd + (int64_t)dst[k] * D;
-      const uint16_t* yr = y + (int64_t)dst[k] * D;
+    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+      uint4 r[VPL];
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int v = v0 + lane + j * kWave;
-        if (v < nvec) {
-          stg16(o + v * 8, scale_bf16x8(r[j], w[k]));
+        r[j] = v < nvec ? ldg16(src + v * 8) : make_uint4(0, 0, 0, 0);
+      }
+      uint4 yy[KCH][VPL];
+      if (dprob) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk)
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + lane + j * kWave;
+            yy[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16(y + (int64_t)dk[kk] * D + v * 8) : make_uint4(0, 0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        if (dk[kk] < 0) continue;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + lane + j * kWave;
+          if (v >= nvec) continue;
+          stg16(dyd + (int64_t)dk[kk] * D + v * 8, scale_bf16x8(r[j], wk[kk]));
           if (dprob) {
-            uint4 yy = ldg16(yr + v * 8);
-            float s = dot[k];
-            s = fmaf(bf16lo(r[j].x), bf16lo(yy.x), s);
-            s = fmaf(bf16hi(r[j].x), bf16hi(yy.x), s);
-            s = fmaf(bf16lo(r[j].y), bf16lo(yy.y), s);
-            s = fmaf(bf16hi(r[j].y), bf16hi(yy.y), s);
-            s = fmaf(bf16lo(r[j].z), bf16lo(yy.z), s);
-            s = fmaf(bf16hi(r[j].z), bf16hi(yy.z), s);
-            s = fmaf(bf16lo(r[j].w), bf16lo(yy.w), s);
-            s = fmaf(bf16hi(r[j].w), bf16hi(yy.w), s);
-            dot[k] = s;
+            const uint4 q = yy[kk][j];
+            float s2 = dot[kk];
+            s2 = fmaf(bf16lo(r[j].x), bf16lo(q.x), s2);
+            s2 = fmaf(bf16hi(r[j].x), bf16hi(q.x), s2);
+            s2 = fmaf(bf16lo(r[j].y), bf16lo(q.y), s2);
+            s2 = fmaf(bf16hi(r[j].y), bf16hi(q.y), s2);
+            s2 = fmaf(bf16lo(r[j].z), bf16lo(q.z), s2);
+            s2 = fmaf(bf16hi(r[j].z), bf16hi(q.z), s2);
+            s2 = fmaf(bf16lo(r[j].w), bf16lo(q.w), s2);
+            s2 = fmaf(bf16hi(r[j].w), bf16hi(q.w), s2);
+            dot[kk] = s2;
           }
         }
       }
     }
-  }
-  if (dprob) {
-    for (int k = 0; k < K; ++k) {
-      float s = wave_sum(dot[k]);
-      if (lane == 0) dprob[(int64_t)t * K + k] = dst[k] >= 0 ? s : 0.0f;
+    if (dprob) {
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const float sum = wave_sum(dot[kk]);
+        if (lane == 0 && kb + kk < K) dprob[(int64_t)t * K + kb + kk] = dk[kk] >= 0 ? sum : 0.0f;
+      }
     }
   }
 }
@@ -341,8 +416,12 @@ hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const fl
 hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
                                  int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  dispatch_mxfp8_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
-                                                      (int)K, q, sc);
+  if (D % 128 == 0 && ((uintptr_t)sc & 3) == 0)
+    dispatch_mxfp8_packed_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
+                                                               (int)K, q, sc);
+  else
+    dispatch_mxfp8_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
+                                                        (int)K, q, sc);
   return hipGetLastError();
 }
 

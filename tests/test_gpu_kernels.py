@@ -130,7 +130,7 @@ def test_dispatch_bf16_and_weighted_bit_exact(N, D, E, K):
 
 
 @pytest.mark.parametrize("N,D,E,K", [(256, 128, 8, 2), (300, 7168, 64, 8), (45, 32, 4, 4),
-                                     (130, 4128, 16, 3)])
+                                     (130, 4128, 16, 3), (50, 384, 16, 10)])
 def test_dispatch_mxfp8_bit_exact(N, D, E, K):
     print(f"dispatch mxfp8 N={N} D={D} E={E} K={K}", flush=True)
     wl, inp, idx, prob, c, o, d, r = _routed(N, D, E, K, 32, 12)
@@ -162,7 +162,7 @@ def test_combine_and_unweighted(N, D, E, K, pdrop):
 
 
 @pytest.mark.parametrize("N,D,E,K,pdrop", [(256, 128, 8, 2, 0.0), (300, 4096, 64, 8, 0.05),
-                                           (61, 72, 4, 3, 0.3)])
+                                           (61, 72, 4, 3, 0.3), (120, 1040, 16, 10, 0.1)])
 def test_combine_bwd(N, D, E, K, pdrop):
     print(f"combine_bwd N={N} D={D} E={E} K={K}", flush=True)
     wl, inp, idx, prob, c, o, d, r = _routed(N, D, E, K, 1, 14, pdrop=pdrop)
@@ -212,6 +212,27 @@ def test_quantize_mxfp8_every_bf16_value():
     assert np.array_equal(host(s), rs)
     assert np.array_equal(host(q), rq)
 
+
+def test_quantize_mxfp8_every_value_at_every_scale():
+    """Each block's amax is the top of one bf16 binade (exponent field f = 1..254,
+    which spans every scale exponent a block can take); its other 31 slots run
+    over all values of binade f and below, both signs.  Every finite bf16 value
+    thus meets every scale that can apply to it."""
+    blocks = []
+    for f in range(1, 255):
+        mags = np.arange(0, (f + 1) << 7, dtype=np.uint32)
+        members = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        members = np.concatenate([members, np.zeros((-len(members)) % 31, np.uint16)]).reshape(-1, 31)
+        amax = np.full((members.shape[0], 1), (f << 7) | 0x7F, np.uint16)
+        blocks.append(np.concatenate([amax, members], axis=1))
+    u = np.concatenate(blocks)
+    u = np.concatenate([u, np.zeros(((-u.shape[0]) % 8, 32), np.uint16)]).reshape(-1, 256)
+    print(f"quantize rows={u.shape[0]} cols=256", flush=True)
+    q, s = M.quantize_mxfp8(dev_bf16(u))
+    _sync()
+    rq, rs = O.quantize_mxfp8(u)
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rq)
 
 def test_swiglu_standalone():
     rows, n = 333, 160
