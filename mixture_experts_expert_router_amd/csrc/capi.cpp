@@ -58,7 +58,7 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
 
 size_t table_bytes(int64_t rows_cap, int64_t E) {
   const size_t a = (size_t)moe::mtile_table_ints(rows_cap, E, 64) * 4;
-  const size_t b = (16 + moe::gemm_fwd_plan_ints(E)) * 4;
+  const size_t b = (moe::kGemmHeadInts + moe::gemm_fwd_plan_ints(E)) * 4;
   const size_t c = moe::experts_fused_ws_ints(rows_cap, E) * 4;
   size_t m = a > b ? a : b;
   m = m > c ? m : c;

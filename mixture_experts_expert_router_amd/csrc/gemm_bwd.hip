@@ -37,7 +37,7 @@ using tile::kRB;
 struct DgradParams {
   const int32_t* offsets;   // [E+1]
   const int32_t* plan;      // row-scheduler plan
-  int32_t* head;            // queue heads [kXcds]
+  int32_t* head;            // queue heads, kHeadStride apart
   int E, N, K;              // N output columns (forward k_dim), K contraction (forward n_dim)
   int nk, n_tiles;          // steps per product, ceil(N / 256)
   bool kcat;                // second product present
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(512) void gemm_dgrad_kernel(DgradParams p) {
 struct WgradParams {
   const int32_t* offsets;   // [E+1]
   const int32_t* plan;      // [0] total items, [1 ..] expert order (most rows first)
-  int32_t* head;            // queue heads [kXcds]
+  int32_t* head;            // queue heads, kHeadStride apart
   int E, M, N;              // per expert: output rows M (forward n_dim), columns N (forward k_dim)
   int m_tiles, n_tiles;
   const uint8_t* a;         // dc [rows][M]
@@ -247,6 +247,11 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
   }
 }
 
+// Items are claimed one ahead and their steps stream through the ring
+// without a drain between tiles: a tile with few rows (one or two steps)
+// would otherwise pay a claim, a full load latency and its stores in series.
+// Tiles of experts without rows have no steps: they issue no loads and store
+// zeros, and the tile after one issues its own first step.
 __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[WgTile::LDS];
   __shared__ int s_item;
@@ -254,25 +259,30 @@ __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
   const int xcd = xcd_id();
   WgItem it = claim_wg(p, &s_item, xcd);
   if (!it.valid) return;
-  {
-    tile::SrcB<WgTile> src;
-    sources_wg(p, it, src);
-    tile::prologue_b<WgTile>(lds0, src, wg_steps(it));
-  }
+  __syncthreads();   // every wave has read s_item before it is reused
+  WgItem next = claim_wg(p, &s_item, xcd);
+  tile::SrcB<WgTile> src;
+  sources_wg(p, it, src);
+  bool issued = false;   // step 0 of `it` is in the ring at position g0
+  int g0 = 0;
   while (it.valid) {
-    tile::SrcB<WgTile> src;
-    sources_wg(p, it, src);
-    f32x4_t acc[WgTile::TM][WgTile::TN];
     const int nk = wg_steps(it);
-    tile::mainloop_b<WgTile>(smem, lds0, src, nk, it.rows - 64 * (nk - 1), acc);
-    const WgItem next = claim_wg(p, &s_item, xcd);
-    if (next.valid) {
-      tile::SrcB<WgTile> ns;
-      sources_wg(p, next, ns);
-      tile::prologue_b<WgTile>(lds0, ns, wg_steps(next));
-    }
+    // the stage at g0 was last read two steps back, before the previous
+    // tile's last barrier, so it is free
+    if (nk > 0 && !issued) tile::issue_step_b_at<WgTile>(lds0, src, 0, g0 & 1);
+    const bool stream = nk > 0 && next.valid && wg_steps(next) > 0;
+    tile::SrcB<WgTile> ns;
+    if (next.valid) sources_wg(p, next, ns);
+    f32x4_t acc[WgTile::TM][WgTile::TN];
+    tile::mainloop_b_stream<WgTile>(smem, lds0, src, nk, it.rows - 64 * (nk - 1), ns, stream, g0, acc);
+    // claim the tile after next while next's first step is in flight
+    const WgItem after = next.valid ? claim_wg(p, &s_item, xcd) : WgItem{};
     epilogue_wg(p, it, acc);
+    g0 += nk;
+    issued = stream;
     it = next;
+    src = ns;
+    next = after;
   }
 }
 
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restr
     plan[1 + rank] = t;
   }
   if (t == 0) plan[0] = E * per_e;
-  if (t < kXcds) head[t] = 0;
+  if (t < kXcds) head[t * kHeadStride] = 0;
 }
 
 hipError_t grid_for(const void* kern, int* grid) {
@@ -339,8 +349,8 @@ hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) 
   p.g = (const uint16_t*)b.g;
   p.u = (const uint16_t*)b.u;
   p.head = ws;
-  p.plan = ws + 16;
-  plan_rows_kernel<<<1, 1024, 0, s>>>(b.offsets, (int)b.E, p.n_tiles, ws + 16, ws);
+  p.plan = ws + kGemmHeadInts;
+  plan_rows_kernel<<<1, 1024, 0, s>>>(b.offsets, (int)b.E, p.n_tiles, ws + kGemmHeadInts, ws);
   const void* kern = b.swiglu_bwd ? (const void*)gemm_dgrad_kernel<true> : (const void*)gemm_dgrad_kernel<false>;
   int grid = 0;
   hipError_t err = grid_for(kern, &grid);
@@ -371,8 +381,8 @@ hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, in
   p.b = (const uint8_t*)b.a;
   p.c = (uint16_t*)db;
   p.head = ws;
-  p.plan = ws + 16;
-  plan_wgrad_kernel<<<1, 1024, 0, s>>>(b.offsets, p.E, p.m_tiles * p.n_tiles, ws + 16, ws);
+  p.plan = ws + kGemmHeadInts;
+  plan_wgrad_kernel<<<1, 1024, 0, s>>>(b.offsets, p.E, p.m_tiles * p.n_tiles, ws + kGemmHeadInts, ws);
   int grid = 0;
   hipError_t err = grid_for((const void*)gemm_wgrad_kernel, &grid);
   if (err != hipSuccess) return err;

@@ -51,7 +51,7 @@ using namespace sched;
 struct FwdParams {
   const int32_t* offsets;   // [E+1]
   const int32_t* plan;      // planner output (layout below)
-  int32_t* head;            // queue head counters [kXcds]
+  int32_t* head;            // queue head counters, kHeadStride apart
   int E, N, K;              // N output columns per weight, K contraction
   int nk;                   // contraction steps (128 bytes of a row each)
   int n_tiles;              // ceil(N / NCOL)
@@ -577,7 +577,7 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStrea
   p.hq = (mx && f.swiglu) ? f.act_q : nullptr;   // bf16 callers quantize H separately
   p.hs = (mx && f.swiglu) ? f.act_scales : nullptr;
   p.head = ws;
-  int32_t* plan = ws + 16;
+  int32_t* plan = ws + kGemmHeadInts;
   p.plan = plan;
   const int ncol = f.swiglu ? BigTile<true>::NCOL : BigTile<false>::NCOL;
   p.n_tiles = (p.N + ncol - 1) / ncol;
@@ -588,7 +588,7 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStrea
 // Workspace of the fused forward: GEMM plan, fused plan and queue state.
 size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E) {
   const int64_t max_mb = rows_cap / 128 + E + 1;
-  return (size_t)(16 + gemm_fwd_plan_ints(E) + (3 + 2 * E + 8) + (4 + 4 * E + max_mb) + 64);
+  return (size_t)(kGemmHeadInts + gemm_fwd_plan_ints(E) + (3 + 2 * E + 8) + (4 + 4 * E + max_mb) + 64);
 }
 
 hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s) {
@@ -619,7 +619,7 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   f.K = (int)x.K;
   f.nt1 = (int)((x.H + BigTile<true>::NCOL - 1) / BigTile<true>::NCOL);
   f.nt2 = (int)((x.D + BigTile<false>::NCOL - 1) / BigTile<false>::NCOL);
-  int32_t* gplan = ws + 16;
+  int32_t* gplan = ws + kGemmHeadInts;
   int32_t* fplan = gplan + gemm_fwd_plan_ints(x.E);
   int32_t* st = fplan + (3 + 2 * x.E + 8);
   st = (int32_t*)(((uintptr_t)st + 7) & ~(uintptr_t)7);   // 8-byte aligned ticket

@@ -102,6 +102,10 @@ struct ExpertsFwd {
 size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E);
 hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s);
 size_t gemm_fwd_plan_ints(int64_t E);
+// The persistent GEMMs' workspace starts with the per-XCD queue heads, each
+// on its own 128-byte line (claims on one head serialize at the memory side;
+// heads that shared a line serialized every claim on the chip).
+constexpr int64_t kGemmHeadInts = 256;
 bool gemm_fwd_fast_ok(int64_t k_dim, int64_t n_dim);
 bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx);
 hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStream_t s);

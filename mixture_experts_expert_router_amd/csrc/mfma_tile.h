@@ -388,9 +388,9 @@ struct SrcB {
 };
 
 template <class C>
-__device__ __forceinline__ void issue_step_b(uint32_t lds0, const SrcB<C>& src, int kt) {
+__device__ __forceinline__ void issue_step_b_at(uint32_t lds0, const SrcB<C>& src, int kt, int stage) {
   const int wave = threadIdx.x >> 6;
-  const uint32_t st = lds0 + (uint32_t)((kt % C::NS) * C::STAGE);
+  const uint32_t st = lds0 + (uint32_t)(stage * C::STAGE);
   const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;
   const uint32_t wave_b = st + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_INS) * 1024u;
   const bool second = kt >= src.nk1;
@@ -420,10 +420,63 @@ __device__ __forceinline__ void issue_step_b(uint32_t lds0, const SrcB<C>& src, 
 }
 
 template <class C>
+__device__ __forceinline__ void issue_step_b(uint32_t lds0, const SrcB<C>& src, int kt) {
+  issue_step_b_at<C>(lds0, src, kt, kt % C::NS);
+}
+
+template <class C>
 __device__ __forceinline__ void prologue_b(uint32_t lds0, const SrcB<C>& src, int nk) {
 #pragma unroll
   for (int s = 0; s < C::NS - 1; ++s)
     if (s < nk) issue_step_b<C>(lds0, src, s);
+}
+
+// Zero the B tile's k-rows past b_tail (< 64) of the step in ring stage
+// `stage` after it landed, so clamped reloads of the last valid row add nothing.
+template <class C>
+__device__ __forceinline__ void zero_b_tail(const uint8_t* smem, int stage, int b_tail) {
+  uint8_t* bt = const_cast<uint8_t*>(smem) + stage * C::STAGE + C::A_BYTES;
+  const int n16 = (64 - b_tail) * 8;   // 16-byte pieces per column block
+  for (int idx = threadIdx.x; idx < n16 * (C::BN / 64); idx += C::NW * 64) {
+    const int cb = idx / n16, w = idx - cb * n16;
+    *reinterpret_cast<uint4*>(bt + cb * 8192 + (b_tail + (w >> 3)) * kRB + (w & 7) * 16) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// MFMAs of one landed step in ring stage `stage`.
+template <class C>
+__device__ __forceinline__ void compute_step_b(const uint8_t* smem, int stage, const FragBase<C>& fb, const TBase& tbase,
+                                               int wm, int wn, f32x4_t (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN;
+  const uint32_t so = (uint32_t)(stage * C::STAGE);
+  const uint8_t* st = smem + so;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (C::AT) af[i] = tfrag(smem, so, tbase, wm * C::WM + i * 16, ks);
+      else af[i] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.a_hi : fb.a_lo) + i * 16 * kRB);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (C::BT) bfr[j] = tfrag(smem, so + C::A_BYTES, tbase, wn * C::WNB + b_frag_row<C>(j), ks);
+      else bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.b_hi : fb.b_lo) + b_frag_row<C>(j) * kRB);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x4_t (&acc)[C::TM][C::TN]) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
 // Backward main loop over nk steps.  b_tail < 64: only the first b_tail
@@ -432,53 +485,56 @@ __device__ __forceinline__ void prologue_b(uint32_t lds0, const SrcB<C>& src, in
 template <class C>
 __device__ __forceinline__ void mainloop_b(const uint8_t* smem, uint32_t lds0, const SrcB<C>& src, int nk, int b_tail,
                                            f32x4_t (&acc)[C::TM][C::TN]) {
-  constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
+  constexpr int NS = C::NS;
   const FragBase<C> fb;
   const TBase tbase;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  zero_acc<C>(acc);
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
     if constexpr (C::BT) {
       if (kt == nk - 1 && b_tail < 64) {
-        uint8_t* bt = const_cast<uint8_t*>(smem) + (kt % NS) * C::STAGE + C::A_BYTES;
-        const int n16 = (64 - b_tail) * 8;   // 16-byte pieces per column block
-        for (int idx = threadIdx.x; idx < n16 * (C::BN / 64); idx += C::NW * 64) {
-          const int cb = idx / n16, w = idx - cb * n16;
-          *reinterpret_cast<uint4*>(bt + cb * 8192 + (b_tail + (w >> 3)) * kRB + (w & 7) * 16) = make_uint4(0, 0, 0, 0);
-        }
+        zero_b_tail<C>(smem, kt % NS, b_tail);
         __syncthreads();
       }
     }
     if (kt + NS - 1 < nk) issue_step_b<C>(lds0, src, kt + NS - 1);
-    const uint32_t so = (uint32_t)((kt % NS) * C::STAGE);
-    const uint8_t* st = smem + so;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if constexpr (C::AT) af[i] = tfrag(smem, so, tbase, wm * C::WM + i * 16, ks);
-        else af[i] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.a_hi : fb.a_lo) + i * 16 * kRB);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (C::BT) bfr[j] = tfrag(smem, so + C::A_BYTES, tbase, wn * C::WNB + b_frag_row<C>(j), ks);
-        else bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + (ks ? fb.b_hi : fb.b_lo) + b_frag_row<C>(j) * kRB);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+    compute_step_b<C>(smem, kt % NS, fb, tbase, wm, wn, acc);
   }
   __syncthreads();   // every wave is done reading the ring before it is refilled
+}
+
+// The same loop for a sequence of tiles fed through the two-stage ring as one
+// stream of steps: step 0 of this tile sits at ring position g0, and during
+// this tile's last step the first step of the next tile (nsrc, when has_next)
+// is issued, so its loads overlap this tile's last MFMAs and its epilogue
+// instead of following them.  The caller issues the first tile's step 0.
+template <class C>
+__device__ __forceinline__ void mainloop_b_stream(const uint8_t* smem, uint32_t lds0, const SrcB<C>& src, int nk,
+                                                  int b_tail, const SrcB<C>& nsrc, bool has_next, int g0,
+                                                  f32x4_t (&acc)[C::TM][C::TN]) {
+  static_assert(C::NS == 2, "one step in flight past the current one");
+  const FragBase<C> fb;
+  const TBase tbase;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  zero_acc<C>(acc);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stage = (g0 + kt) & 1;
+    wait_vmcnt<0>();
+    __syncthreads();   // step kt landed for every wave; every wave is done with the step before it
+    if constexpr (C::BT) {
+      if (kt == nk - 1 && b_tail < 64) {
+        zero_b_tail<C>(smem, stage, b_tail);
+        __syncthreads();
+      }
+    }
+    if (kt + 1 < nk) issue_step_b_at<C>(lds0, src, kt + 1, stage ^ 1);
+    else if (has_next) issue_step_b_at<C>(lds0, nsrc, 0, stage ^ 1);
+    compute_step_b<C>(smem, stage, fb, tbase, wm, wn, acc);
+  }
 }
 
 }  // namespace tile

@@ -15,6 +15,7 @@
 #pragma once
 
 #include "common.h"
+#include "launch.h"
 
 namespace moe {
 namespace sched {
@@ -27,9 +28,12 @@ constexpr int kXcds = 8;            // XCDs of the chip; queue q holds chunks q,
 constexpr int kChunk = 32;          // items per chunk (the CUs of one XCD)
 constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
 
+constexpr int kHeadStride = 32;     // ints between queue heads: one 128-byte line each
+static_assert(kXcds * kHeadStride == kGemmHeadInts, "head block of the workspace");
+
 // plan layout (int32): [0] total items, [1] number of listed experts L,
 // [2 .. 2+L) expert ids in processing order, [2+E .. 2+E+L] item prefix sums
-// (entry L = total).  The queue heads are kXcds separate counters.
+// (entry L = total).  The queue heads are kXcds counters kHeadStride apart.
 
 // A claimed queue item, decoded: rows [m_start, min(m_start + BM, m1)) of
 // expert e, output columns [n0, n0 + NCOL), tile class by the expert's rows.
@@ -76,7 +80,7 @@ __device__ __forceinline__ int claim_global(int32_t* head, int total, int* s_ite
     int g = -1;
     for (int t = 0; t < kXcds; ++t) {
       const int q = (xcd + t) & (kXcds - 1);
-      const int gi = queue_item(q, atomicAdd(head + q, 1));
+      const int gi = queue_item(q, atomicAdd(head + q * kHeadStride, 1));
       if (gi < total) {
         g = gi;
         break;
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restri
     plan[1] = L;
     plan[2 + E + L] = r;
   }
-  if (t < kXcds) head[t] = 0;
+  if (t < kXcds) head[t * kHeadStride] = 0;
   __syncthreads();
   if (t < L) {
     plan[2 + t] = s_ids[t];
