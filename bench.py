@@ -37,7 +37,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_expert_router_amd", "csrc")
 # sources of the persistent grouped GEMM: HBM counters taken on another
 # version of these no longer describe the kernel
-GEMM_SOURCES = ("gemm_fwd.hip", "mfma_tile.h", "common.h")
+GEMM_SOURCES = ("gemm_fwd.hip", "mfma_tile.h", "common.h", "sched.h")
 
 # MI355X published peaks (dense)
 PEAK_HBM_GBS = 8000.0

@@ -3,12 +3,16 @@
 // only as many columns as experts, so its tile is narrow).
 //
 // The product is skinny (N tokens x D, times D x E with E <= 1024), so one
-// 64-row block per workgroup would leave most CUs idle.  The contraction is
+// row block per workgroup would leave most CUs idle.  The contraction is
 // split into S fixed ranges: item (row block, column tile, split) runs the
 // shared MFMA tile engine over its range and writes an fp32 partial tile;
 // a second kernel adds the S partials in ascending split order plus the bias.
 // The split is a function of the shape only, so the result is bitwise the
 // same run to run.  With S = 1 the tile kernel writes the logits directly.
+// Every row block re-reads its column tile of W_r, so large N takes 128-row
+// blocks (half the re-reads of 64-row ones).  The split is the fastest part
+// of the item index: with 8 splits, workgroup b (on XCD b % 8) always reads
+// the same slice of W_r, which stays in that XCD's L2.
 //
 // Shapes the engine does not take (D not a multiple of 64) use a direct
 // kernel: one workgroup per 16 rows, operands read straight from global
@@ -22,8 +26,8 @@ namespace moe {
 
 namespace {
 
-template <int BN>
-using RouterTile = tile::TileCfg<64, BN, 3, 1, 4, false>;
+template <int BM, int BN>
+using RouterTile = tile::TileCfg<BM, BN, 3, BM / 64, 4, false>;   // 4 or 8 waves
 
 struct RouterParams {
   const uint16_t* x;    // [N][D]
@@ -33,17 +37,18 @@ struct RouterParams {
   int N, D, E, S, mblocks, ntiles;
 };
 
-template <int BN>
-__global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
-  using C = RouterTile<BN>;
+template <int BM, int BN>
+__global__ __launch_bounds__(BM * 4) void router_tile_kernel(RouterParams p) {
+  using C = RouterTile<BM, BN>;
   using namespace tile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+  static_assert(C::NW * 64 == BM * 4, "block size");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   int item = blockIdx.x;
+  const int split = item % p.S;
+  item /= p.S;
   const int mb = item % p.mblocks;
-  item /= p.mblocks;
-  const int nt = item % p.ntiles;
-  const int split = item / p.ntiles;
+  const int nt = item / p.mblocks;
   const int nk = p.D / kBK;
   const int k0 = (int)((int64_t)nk * split / p.S), k1 = (int)((int64_t)nk * (split + 1) / p.S);
   const int m_start = mb * C::BM, n0 = nt * BN;
@@ -67,12 +72,13 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterParams p) {
   prologue<C>(lds0, src, k1 - k0);
   mainloop<C>(smem, lds0, src, k1 - k0, acc);
 
-  // lane holds row i*16 + l16 (one wave row), columns wn*WN + j*16 + 4*lg + r
-  const int l16 = lane & 15, lg = lane >> 4, wn = wave;
+  // lane holds row wm*WM + i*16 + l16, columns wn*WN + j*16 + 4*lg + r
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   float* out = p.out + (p.S > 1 ? (int64_t)split * p.N * p.E : 0);
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
-    const int row = m_start + i * 16 + l16;
+    const int row = m_start + wm * C::WM + i * 16 + l16;
     if (row >= p.N) continue;
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
@@ -172,19 +178,21 @@ __global__ __launch_bounds__(256) void router_direct_kernel(const uint16_t* __re
   }
 }
 
-// tile width for E columns, and the number of contraction splits
+// tile height and width for the shape, and the number of contraction splits
 struct RouterPlan {
-  int bn, ntiles, mblocks, S;
+  int bm, bn, ntiles, mblocks, S;
 };
 
 RouterPlan router_plan(int64_t N, int64_t D, int64_t E) {
   RouterPlan r{};
+  r.bm = N >= 2048 ? 128 : 64;
   r.bn = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
   r.ntiles = (int)((E + r.bn - 1) / r.bn);
-  r.mblocks = (int)((N + 63) / 64);
+  r.mblocks = (int)((N + r.bm - 1) / r.bm);
   const int nk = (int)(D / tile::kBK);
   const int64_t base = (int64_t)r.mblocks * r.ntiles;
-  int S = (int)((512 + base - 1) / (base > 0 ? base : 1));   // about 512 items
+  const int64_t target = r.bm == 128 ? 256 : 512;   // about one (8-wave) or two (4-wave) items per CU
+  int S = (int)((target + base - 1) / (base > 0 ? base : 1));
   S = S < 1 ? 1 : (S > nk ? nk : S);
   S = S > 16 ? 16 : S;
   r.S = S;
@@ -213,9 +221,15 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
   RouterParams p{(const uint16_t*)x, (const uint16_t*)w_r, bias, r.S > 1 ? (float*)ws : logits,
                  (int)N, (int)D, (int)E, r.S, r.mblocks, r.ntiles};
   const unsigned grid = (unsigned)((int64_t)r.mblocks * r.ntiles * r.S);
-  if (r.bn == 64) router_tile_kernel<64><<<grid, 256, 0, s>>>(p);
-  else if (r.bn == 128) router_tile_kernel<128><<<grid, 256, 0, s>>>(p);
-  else router_tile_kernel<256><<<grid, 256, 0, s>>>(p);
+  if (r.bm == 128) {
+    if (r.bn == 64) router_tile_kernel<128, 64><<<grid, 512, 0, s>>>(p);
+    else if (r.bn == 128) router_tile_kernel<128, 128><<<grid, 512, 0, s>>>(p);
+    else router_tile_kernel<128, 256><<<grid, 512, 0, s>>>(p);
+  } else {
+    if (r.bn == 64) router_tile_kernel<64, 64><<<grid, 256, 0, s>>>(p);
+    else if (r.bn == 128) router_tile_kernel<64, 128><<<grid, 256, 0, s>>>(p);
+    else router_tile_kernel<64, 256><<<grid, 256, 0, s>>>(p);
+  }
   if (r.S > 1) {
     const int64_t NE = N * E;
     const int64_t nblk = (NE + 255) / 256;
