@@ -131,14 +131,20 @@ def topk_select(L, K: int) -> np.ndarray:
     return out
 
 
-def route_probs(L, idx, renorm: int = 0) -> np.ndarray:
-    """Dispatch weight of each selected slot: the softmax probability of its
-    expert, optionally divided by the sum over the K selected slots; fp32."""
+def route_weights(L, idx, renorm: int = 0) -> np.ndarray:
+    """Dispatch weight of each selected slot in float64: the softmax
+    probability of its expert, optionally divided by the sum over the K
+    selected slots (dropped slots included: a drop happens after routing)."""
     p = softmax(L)
     sel = np.take_along_axis(p, np.asarray(idx, dtype=np.int64), axis=1)
     if renorm:
         sel = sel / sel.sum(axis=1, keepdims=True)
-    return sel.astype(np.float32)
+    return sel
+
+
+def route_probs(L, idx, renorm: int = 0) -> np.ndarray:
+    """The dispatch weights as the layer stores them: fp32."""
+    return route_weights(L, idx, renorm).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -472,6 +478,38 @@ def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
     dx = dispatch_bwd(eb["dxd"], fwd["dst_rows"], exact)
     eb.update(dyd=dyd, dprob=dp, dx=dx)
     return eb
+
+
+def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0) -> dict:
+    """Gradients of the router from the route-weight gradient dprob [N,K]
+    (0 for invalid routes), in float64.  [KOSMOS 3.3.2 step 2: the router's
+    dX_r and dW_r; the adjoint of router_logits and route_weights]
+
+    The chain, token by token, with p = softmax(L) and s_k = p[idx_k]:
+      renorm: w_k = s_k / S, S = sum_j s_j, so ds_k = (dprob_k - sum_j w_j dprob_j) / S;
+      else ds_k = dprob_k;
+      g_e = ds_k where e = idx_k (the K experts are distinct), else 0;
+      dL_e = p_e (g_e - sum_j p_j g_j)          (softmax backward);
+    then dX_r = dL W_r, dW_r = dL^T x, db_r = sum over tokens of dL.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    N, E = L.shape
+    ix = np.asarray(idx, dtype=np.int64)
+    gw = np.asarray(dprob, dtype=np.float64)
+    p = softmax(L)
+    s = np.take_along_axis(p, ix, axis=1)
+    if renorm:
+        tot = s.sum(axis=1, keepdims=True)
+        w = s / tot
+        ds = (gw - np.sum(w * gw, axis=1, keepdims=True)) / tot
+    else:
+        ds = gw
+    g = np.zeros((N, E))
+    np.put_along_axis(g, ix, ds, axis=1)
+    dL = p * (g - np.sum(p * g, axis=1, keepdims=True))
+    xv = values(x)
+    wv = values(w_r)
+    return dict(dlogits=dL, dx_r=dL @ wv, dw_r=dL.T @ xv, db_r=dL.sum(axis=0))
 
 
 # --------------------------------------------------------------------------

@@ -131,3 +131,75 @@ def test_route_map_invariants(name, seed):
         assert np.all(seg >= 0) and np.all(np.diff(seg) > 0)        # ascending route id
         assert np.all(idx.reshape(-1)[seg] == e)
         assert np.all(r[o[e] + c[e]:o[e + 1]] == -1)                # padding
+
+
+# ------------------------------------------------------ router backward ----
+def _router_case(N, D, E, K, seed, pdrop=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, D))
+    w = rng.standard_normal((E, D)) * 0.3
+    b = rng.standard_normal(E) * 0.1
+    L = x @ w.T + b
+    idx = O.topk_select(L, K)
+    dprob = rng.standard_normal((N, K))
+    dprob[rng.random((N, K)) < pdrop] = 0.0      # dropped routes carry no gradient
+    return x, w, b, L, idx, dprob
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("pdrop", [0.0, 0.3])
+def test_router_bwd_matches_finite_differences(renorm, pdrop):
+    """fp64 central differences of sum(dprob * route_weights(x W^T + b)), with
+    the selection fixed (it is piecewise constant in the logits)."""
+    N, D, E, K = 12, 16, 8, 3
+    x, w, b, L, idx, dprob = _router_case(N, D, E, K, 5 + renorm, pdrop)
+
+    def loss_L(Lm):
+        return float(np.sum(dprob * O.route_weights(Lm, idx, renorm)))
+
+    def loss(xm, wm, bm):
+        return loss_L(xm @ wm.T + bm)
+
+    g = O.router_bwd(L, idx, dprob, x, w, renorm)
+    rng = np.random.default_rng(2)
+    eps = 1e-6
+    base = (x, w, b)
+    for i, gr in enumerate((g["dx_r"], g["dw_r"], g["db_r"])):
+        v = rng.standard_normal(base[i].shape)
+        plus, minus = list(base), list(base)
+        plus[i] = base[i] + eps * v
+        minus[i] = base[i] - eps * v
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = float(np.sum(gr * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (i, fd, an)
+    v = rng.standard_normal(L.shape)
+    fd = (loss_L(L + eps * v) - loss_L(L - eps * v)) / (2 * eps)
+    assert abs(fd - float(np.sum(g["dlogits"] * v))) <= 1e-7 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_router_bwd_dlogits_vs_torch_autograd(renorm):
+    N, E, K = 20, 32, 6
+    x, w, b, L, idx, dprob = _router_case(N, 8, E, K, 11)
+    Lt = torch.tensor(L, dtype=torch.float64, requires_grad=True)
+    p = torch.softmax(Lt, dim=1)
+    sel = torch.gather(p, 1, torch.tensor(idx, dtype=torch.int64))
+    if renorm:
+        sel = sel / sel.sum(dim=1, keepdim=True)
+    (sel * torch.tensor(dprob)).sum().backward()
+    got = O.router_bwd(L, idx, dprob, x, w, renorm)["dlogits"]
+    assert np.allclose(got, Lt.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_router_bwd_closed_forms():
+    # one expert per token, renormalised: the weight is 1 whatever the logits
+    x, w, b, L, idx, dprob = _router_case(10, 8, 6, 1, 3)
+    g = O.router_bwd(L, idx, dprob, x, w, renorm=1)
+    assert np.all(g["dlogits"] == 0.0)
+    # every expert selected with the same upstream gradient: the weights sum to 1
+    x, w, b, L, idx, _ = _router_case(10, 8, 6, 6, 4)
+    g = O.router_bwd(L, idx, np.full((10, 6), 0.7), x, w, renorm=0)
+    assert np.max(np.abs(g["dlogits"])) <= 1e-15
+    # no upstream gradient, no router gradient
+    g = O.router_bwd(L, idx, np.zeros((10, 6)), x, w, renorm=1)
+    assert not np.any(g["dlogits"]) and not np.any(g["dw_r"]) and not np.any(g["db_r"])
