@@ -374,7 +374,8 @@ def main(argv=None):
     t0 = time.perf_counter()
     inp = S.make_inputs(wl, args.seed)
     x, w, drop = device_inputs(M, inp, wl.mxfp8, torch)
-    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=wl.bwd)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=wl.bwd,
+                       router_bwd=wl.bwd)
     dout = (torch.from_numpy(np.ascontiguousarray(inp.dout).view(np.int16)).view(torch.bfloat16).cuda()
             if wl.bwd else None)
     st = StagedForward(M, layer, x)
@@ -394,7 +395,8 @@ def main(argv=None):
 
     # one step: the staged forward, and for a forward+backward workload the
     # layer backward (combine-bwd, down dgrad/wgrad with the SwiGLU backward,
-    # gate/up dgrad/wgrad, dispatch-bwd, router-prob grads) after it
+    # gate/up dgrad/wgrad, router-prob grads, the router backward: dlogits,
+    # dX_r, dW_r, db_r; dispatch-bwd folding in dX_r) after it
     def step(ev=None, ev_b=None):
         st.run(ev)
         if wl.bwd:
@@ -493,7 +495,8 @@ def main(argv=None):
     if wl.bwd:
         tf_b = routed_flops(R, D, H, backward=True) / (bwd_ms / 1e3) / 1e12
         out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / peak,
-                           "note": "value and ms_per_step cover forward + backward"}
+                           "note": "value and ms_per_step cover forward + backward, router backward included; "
+                                   "routed_tflops counts the expert GEMMs only"}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
     if not args.no_cpu_baseline:

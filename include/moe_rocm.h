@@ -295,6 +295,15 @@ typedef struct moe_layer_grads {
   void* dw_gate;   /* bf16 [E][H][D] */
   void* dw_up;     /* bf16 [E][H][D] */
   void* dw_down;   /* bf16 [E][D][H] */
+  /* Router backward (KOSMOS section 3.3.2 step 2: the router's dX_r and dW_r),
+   * run when dw_r is not NULL: dlogits through the (optionally renormalised)
+   * softmax weights, dw_r = dlogits^T x, db_r = column sums of dlogits, and
+   * dx then also holds dlogits W_r.  Needs saved logits and topk_idx, a->x and
+   * a->w_r, and E a multiple of 8 (else MOE_ERR_SHAPE).  db_r and dlogits
+   * may be NULL. */
+  void* dw_r;      /* bf16 [E][D] */
+  float* db_r;     /* fp32 [E] */
+  float* dlogits;  /* fp32 [N][E] */
 } moe_layer_grads;
 
 int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* saved, const void* dout,

@@ -63,7 +63,7 @@ class LayerSaved(C.Structure):
 
 
 class LayerGrads(C.Structure):
-    _fields_ = [(n, _vp) for n in ("dx", "dprob", "dw_gate", "dw_up", "dw_down")]
+    _fields_ = [(n, _vp) for n in ("dx", "dprob", "dw_gate", "dw_up", "dw_down", "dw_r", "db_r", "dlogits")]
 
 
 EXPORTS = {
@@ -388,7 +388,7 @@ class MoeLayer:
     forward's launch scheme (MOE_SCHED_STAGED or MOE_SCHED_READY)."""
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
-                 device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED):
+                 device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False):
         torch = _torch()
         self.wts, self.K, self.mxfp8, self.renorm, self.drop = wts, K, mxfp8, renorm, drop
         self.sched = sched
@@ -408,7 +408,12 @@ class MoeLayer:
                               dw_gate=torch.empty((E, H, D), dtype=torch.bfloat16, device=device),
                               dw_up=torch.empty((E, H, D), dtype=torch.bfloat16, device=device),
                               dw_down=torch.empty((E, D, H), dtype=torch.bfloat16, device=device))
-            self._gr = LayerGrads(*[_ptr(self.grads[n]) for n, _ in LayerGrads._fields_])
+            if router_bwd:
+                # router gradients too; dx then includes dlogits . W_r
+                self.grads.update(dw_r=torch.empty((E, D), dtype=torch.bfloat16, device=device),
+                                  db_r=torch.empty((E,), dtype=torch.float32, device=device),
+                                  dlogits=torch.empty((N, E), dtype=torch.float32, device=device))
+            self._gr = LayerGrads(*[_ptr(self.grads.get(n)) for n, _ in LayerGrads._fields_])
 
     def forward(self, x):
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched)

@@ -92,9 +92,37 @@ size_t route_bytes(const moe_dims& d) { return round_up(moe::route_workspace_byt
 
 size_t router_bytes(const moe_dims& d) { return round_up(moe::router_workspace_bytes(d.N, d.D, d.E), 256); }
 
+// router backward scratch: dlogits fp32 and bf16, dX_r, split offsets, wgrad
+// partials and column partials
+struct RouterBwdLayout {
+  size_t dl, dlb, dxr, offs, part, colpart, total;
+  int S;
+};
+
+RouterBwdLayout router_bwd_layout(const moe_dims& d) {
+  RouterBwdLayout l{};
+  const size_t N = (size_t)d.N, E = (size_t)d.E, D = (size_t)d.D;
+  l.S = moe::router_wgrad_splits(d.N, d.D, d.E);
+  size_t o = 0;
+  l.dl = o;
+  o += round_up(N * E * 4, 256);
+  l.dlb = o;
+  o += round_up(N * E * 2, 256);
+  l.dxr = o;
+  o += round_up(N * D * 2, 256);
+  l.offs = o;
+  o += 256;
+  l.part = o;
+  o += round_up((size_t)l.S * E * D * 4, 256);
+  l.colpart = o;
+  o += round_up(((N + 63) / 64) * E * 4, 256);
+  l.total = o;
+  return l;
+}
+
 size_t bwd_scratch_bytes(const moe_dims& d) {
   const size_t rc = (size_t)rows_cap_of(d);
-  return 2 * round_up(rc * d.D * 2, 256) + 2 * round_up(rc * d.H * 2, 256);
+  return 2 * round_up(rc * d.D * 2, 256) + 2 * round_up(rc * d.H * 2, 256) + router_bwd_layout(d).total;
 }
 
 }  // namespace
@@ -451,6 +479,16 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   REQUIRE(gr->dw_gate);
   REQUIRE(gr->dw_up);
   REQUIRE(gr->dw_down);
+  if (gr->dw_r) {
+    REQUIRE(gr->dw_r);
+    REQUIRE(sv->logits);
+    REQUIRE(sv->topk_idx);
+    REQUIRE(a->x);
+    REQUIRE(a->w_r);
+    OPTIONAL(gr->db_r);
+    OPTIONAL(gr->dlogits);
+    if (d.E % 8) return MOE_ERR_SHAPE;   // the router's GEMMs read dlogits rows in 16-byte chunks
+  }
   const int64_t rc = rows_cap_of(d);
   const size_t tb = table_bytes(rc, d.E);
   if (ws_bytes < tb + bwd_scratch_bytes(d)) return MOE_ERR_WORKSPACE;
@@ -481,7 +519,37 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   if (e == hipSuccess) e = gemm_dgrad(gu, table, s);
   if (e == hipSuccess) e = gemm_wgrad(gu, dg, gr->dw_gate, table, s);
   if (e == hipSuccess) e = gemm_wgrad(gu, du, gr->dw_up, table, s);
-  if (e == hipSuccess) e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s);
+  const void* dxr = nullptr;
+  if (e == hipSuccess && gr->dw_r) {
+    // router backward, after the expert backward so the fold below adds dX_r
+    p += round_up((size_t)rc * d.H * 2, 256);
+    const RouterBwdLayout l = router_bwd_layout(d);
+    float* dl = gr->dlogits ? gr->dlogits : (float*)(p + l.dl);
+    uint16_t* dlb = (uint16_t*)(p + l.dlb);
+    int32_t* offs = (int32_t*)(p + l.offs);
+    int32_t* offs1 = offs + 48;   // the block is 64 ints; the S + 1 <= 33 split offsets come first
+    float* part = (float*)(p + l.part);
+    float* colpart = (float*)(p + l.colpart);
+    dxr = p + l.dxr;
+    e = moe::launch_router_bwd(sv->logits, sv->topk_idx, gr->dprob, d.N, d.E, d.K, d.renorm, dl, dlb, colpart,
+                               offs, l.S, offs1, s);
+    // forward L = x . w_r^T: k_dim = D, n_dim = E, one expert over all N rows
+    moe::GemmBwd rt{1, d.N, d.D, d.E, offs1, a->x, a->w_r, nullptr, dlb, nullptr, (void*)dxr,
+                    nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = gemm_dgrad(rt, table, s);
+    // dW_r: the token range cut into S pseudo-experts, fp32 partials summed in order
+    moe::GemmBwd rs{l.S, d.N, d.D, d.E, offs, a->x, a->w_r, nullptr, dlb, nullptr, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, false};
+    const bool split = moe::gemm_wgrad_fast_ok(rs, dlb, part);
+    if (e == hipSuccess) {
+      if (split) e = moe::launch_gemm_wgrad_fast(rs, dlb, part, table, s, true);
+      else e = gemm_wgrad(rt, dlb, gr->dw_r, table, s);
+    }
+    if (e == hipSuccess)
+      e = moe::launch_router_bwd_reduce(split ? part : nullptr, l.S, d.E * d.D, (uint16_t*)gr->dw_r, colpart,
+                                        (d.N + 63) / 64, d.E, gr->db_r, s);
+  }
+  if (e == hipSuccess) e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s, dxr);
   return hip_status(e);
 }
 

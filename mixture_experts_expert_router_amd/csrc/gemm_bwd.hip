@@ -175,7 +175,8 @@ struct WgradParams {
   int m_tiles, n_tiles;
   const uint8_t* a;         // dc [rows][M]
   const uint8_t* b;         // forward operand [rows][N]
-  uint16_t* c;              // db [E][M][N]
+  void* c;                  // db [E][M][N], bf16 (or fp32 when f32)
+  bool f32;
 };
 
 using WgTile = tile::TileCfg<256, 256, 2, 4, 2, false, false, true, true>;   // 2 x 64 KB
@@ -232,7 +233,7 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
-  uint16_t* c = p.c + (int64_t)it.e * p.M * p.N;
+  const int64_t cbase = (int64_t)it.e * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int m = it.m0 + wm * C::WM + i * 16 + l16;
@@ -242,7 +243,9 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
       const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
       if (n >= p.N) continue;
       const f32x4_t a = acc[i][j];
-      *reinterpret_cast<uint2*>(c + (int64_t)m * p.N + n) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+      const int64_t off = cbase + (int64_t)m * p.N + n;
+      if (p.f32) *reinterpret_cast<float4*>(static_cast<float*>(p.c) + off) = make_float4(a[0], a[1], a[2], a[3]);
+      else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + off) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
     }
   }
 }
@@ -369,7 +372,8 @@ bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db) {
   return aligned16(dc) && aligned16(b.a) && aligned16(db);
 }
 
-hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s) {
+hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s,
+                                  bool f32) {
   WgradParams p{};
   p.offsets = b.offsets;
   p.E = (int)b.E;
@@ -379,7 +383,8 @@ hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, in
   p.n_tiles = (p.N + WgTile::BN - 1) / WgTile::BN;
   p.a = (const uint8_t*)dc;
   p.b = (const uint8_t*)b.a;
-  p.c = (uint16_t*)db;
+  p.c = db;
+  p.f32 = f32;
   p.head = ws;
   p.plan = ws + kGemmHeadInts;
   plan_wgrad_kernel<<<1, 1024, 0, s>>>(b.offsets, p.E, p.m_tiles * p.n_tiles, ws + kGemmHeadInts, ws);

@@ -46,6 +46,17 @@ struct GemmBwd {
 size_t router_workspace_bytes(int64_t N, int64_t D, int64_t E);
 hipError_t launch_router_logits(const void* x, const void* w_r, const float* bias, int64_t N,
                                 int64_t D, int64_t E, float* logits, void* ws, hipStream_t s);
+// router backward: dlogits (fp32 and bf16) from the route-weight gradient,
+// per-64-token column partials of dlogits, and the token-split offsets
+// (S + 1 entries) plus the whole-range offsets {0, N} for the router's GEMMs
+int router_wgrad_splits(int64_t N, int64_t D, int64_t E);
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* dprob, int64_t N,
+                             int64_t E, int64_t K, int renorm, float* dl, uint16_t* dlb, float* colpart,
+                             int32_t* offs, int S, int32_t* offs1, hipStream_t s);
+// dw_r = bf16(sum over S fp32 partials [S][E*D], in order) when part != NULL;
+// db_r = sum over the ceil(N/64) column partials, in order, when db_r != NULL
+hipError_t launch_router_bwd_reduce(const float* part, int S, int64_t ED, uint16_t* dw_r, const float* colpart,
+                                    int64_t P, int64_t E, float* db_r, hipStream_t s);
 
 // route.hip
 size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K);
@@ -62,8 +73,9 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
                                hipStream_t s);
+// addend (bf16 [N][D], optional) is added to each token's fp32 sum before rounding
 hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
-                          int64_t D, int64_t K, void* out, hipStream_t s);
+                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend = nullptr);
 hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
                               const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
                               float* dprob, hipStream_t s);
@@ -115,7 +127,8 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStrea
 bool gemm_dgrad_fast_ok(const GemmBwd& b);
 hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s);
 bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db);
-hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s);
+hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s,
+                                  bool f32 = false);
 
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);

@@ -204,7 +204,8 @@ template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ dst_rows,
                                                       const float* __restrict__ weight, int N,
-                                                      int D, int K, uint16_t* __restrict__ out) {
+                                                      int D, int K, uint16_t* __restrict__ out,
+                                                      const uint16_t* __restrict__ addend) {
   constexpr int VPL = 2, KCH = 8;
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -213,9 +214,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
     float acc[VPL][8];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      const uint4 q = (addend && v < nvec) ? ldg16(addend + (int64_t)t * D + v * 8) : make_uint4(0, 0, 0, 0);
+      acc[j][0] = bf16lo(q.x);
+      acc[j][1] = bf16hi(q.x);
+      acc[j][2] = bf16lo(q.y);
+      acc[j][3] = bf16hi(q.y);
+      acc[j][4] = bf16lo(q.z);
+      acc[j][5] = bf16hi(q.z);
+      acc[j][6] = bf16lo(q.w);
+      acc[j][7] = bf16hi(q.w);
+    }
     for (int kb = 0; kb < K; kb += KCH) {
       uint4 r[KCH][VPL];
       int dk[KCH];
@@ -435,14 +445,15 @@ hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, in
 }
 
 hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
-                          int64_t D, int64_t K, void* out, hipStream_t s) {
+                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend) {
   if (N == 0) return hipSuccess;
   if (weight)
     combine_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, weight, (int)N,
-                                                      (int)D, (int)K, (uint16_t*)out);
+                                                      (int)D, (int)K, (uint16_t*)out, (const uint16_t*)addend);
   else
     combine_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, nullptr,
-                                                       (int)N, (int)D, (int)K, (uint16_t*)out);
+                                                       (int)N, (int)D, (int)K, (uint16_t*)out,
+                                                       (const uint16_t*)addend);
   return hipGetLastError();
 }
 

@@ -239,4 +239,168 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Router backward (KOSMOS section 3.3.2 step 2: the router's dX_r and dW_r).
+// From the route-weight gradient dprob [N][K], token by token, with p the
+// softmax of the saved logits and s_k = p[idx_k]:
+//   ds_k = dprob_k, or (dprob_k - sum_j w_j dprob_j) / S with renormalised
+//   weights w_k = s_k / S, S = sum_j s_j;
+//   dL_e = p_e (g_e - sum_k s_k ds_k), g_e = ds_k at e = idx_k, else 0.
+// One wave per token (kRbTok tokens per wave, 4 waves per workgroup); g goes
+// through a per-wave LDS row.  Each workgroup also writes the column sums of
+// its 64 tokens' dL, added in wave order, for the bias gradient.  The GEMMs
+// dX_r = dL W_r and dW_r = dL^T x run on the grouped-GEMM kernels.
+// ---------------------------------------------------------------------------
+
+constexpr int kRbTok = 16;
+constexpr int kRbMaxE = 1024;
+constexpr int kRbCols = kRbMaxE / 64;   // logits per lane
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits,
+                                                         const int32_t* __restrict__ topk_idx,
+                                                         const float* __restrict__ dprob, int N, int E, int K,
+                                                         int renorm, float* __restrict__ dl,
+                                                         uint16_t* __restrict__ dlb, float* __restrict__ colpart,
+                                                         int32_t* __restrict__ offs, int S,
+                                                         int32_t* __restrict__ offs1) {
+  __shared__ float s_g[4][kRbMaxE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (blockIdx.x == 0) {
+    if ((int)threadIdx.x <= S) offs[threadIdx.x] = (int)((int64_t)N * threadIdx.x / S);
+    if (threadIdx.x < 2) offs1[threadIdx.x] = threadIdx.x ? N : 0;
+  }
+  const int nI = (E + 63) >> 6;
+  float* g = s_g[w];
+  float col[kRbCols];
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i) {
+    col[i] = 0.0f;
+    if (i < nI && lane + 64 * i < E) g[lane + 64 * i] = 0.0f;
+  }
+  wave_lds_fence();
+  const int t0 = blockIdx.x * 64 + w * kRbTok;
+  for (int j = 0; j < kRbTok; ++j) {
+    const int t = t0 + j;
+    if (t >= N) break;
+    const float* Lr = logits + (int64_t)t * E;
+    float l[kRbCols];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = (i < nI && e < E) ? Lr[e] : -INFINITY;
+      m = fmaxf(m, l[i]);
+    }
+    m = wave_max(m);
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i)
+      if (i < nI && lane + 64 * i < E) z += expf(l[i] - m);
+    z = wave_sum(z);
+    const float rz = 1.0f / z;
+    // the selected slots: lane k < K
+    int ek = -1;
+    float sk = 0.0f, dk = 0.0f;
+    if (lane < K) {
+      ek = topk_idx[(int64_t)t * K + lane];
+      dk = dprob[(int64_t)t * K + lane];
+      if (ek >= 0 && ek < E) sk = expf(Lr[ek] - m) * rz;
+      else ek = -1;
+    }
+    float ds = dk;
+    if (renorm) {
+      const float tot = wave_sum(sk);
+      const float c = wave_sum(sk * dk) / tot;   // sum_j w_j dprob_j
+      ds = (dk - c) / tot;
+    }
+    const float dot = wave_sum(sk * ds);
+    if (ek >= 0) g[ek] = ds;
+    wave_lds_fence();
+    float* dlr = dl + (int64_t)t * E;
+    uint16_t* dlbr = dlb + (int64_t)t * E;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nI && e < E) {
+        const float d = expf(l[i] - m) * rz * (g[e] - dot);
+        dlr[e] = d;
+        dlbr[e] = (uint16_t)(pack_bf16x2(d, 0.0f) & 0xFFFFu);
+        col[i] += d;
+      }
+    }
+    wave_lds_fence();
+    if (ek >= 0) g[ek] = 0.0f;
+    wave_lds_fence();
+  }
+  // column partials of this workgroup's tokens, added in wave order
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i)
+    if (i < nI && lane + 64 * i < E) s_g[w][lane + 64 * i] = col[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    colpart[(int64_t)blockIdx.x * E + e] = ((s_g[0][e] + s_g[1][e]) + s_g[2][e]) + s_g[3][e];
+}
+
+__global__ __launch_bounds__(256) void router_bwd_reduce_kernel(const float* __restrict__ part, int S, int64_t ED,
+                                                                uint16_t* __restrict__ dw_r,
+                                                                const float* __restrict__ colpart, int64_t P,
+                                                                int64_t E, float* __restrict__ db_r) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (part) {
+    for (int64_t i = tid; i < ED / 4; i += stride) {
+      float4 a = reinterpret_cast<const float4*>(part)[i];
+      for (int sp = 1; sp < S; ++sp) {
+        const float4 b = reinterpret_cast<const float4*>(part + (int64_t)sp * ED)[i];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+      }
+      reinterpret_cast<uint2*>(dw_r)[i] = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+    }
+  }
+  if (db_r) {
+    for (int64_t e = tid; e < E; e += stride) {
+      float a = 0.0f;
+      for (int64_t b = 0; b < P; ++b) a += colpart[b * E + e];
+      db_r[e] = a;
+    }
+  }
+}
+
+// token splits of the router's wgrad: about 256 tiles, at least 64 rows each
+int router_wgrad_splits(int64_t N, int64_t D, int64_t E) {
+  const int64_t tiles = ((E + 255) / 256) * ((D + 255) / 256);
+  int64_t S = (256 + tiles - 1) / tiles;
+  S = S > 32 ? 32 : S;
+  const int64_t cap = N / 64;
+  S = S > cap ? cap : S;
+  return (int)(S < 1 ? 1 : S);
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* dprob, int64_t N,
+                             int64_t E, int64_t K, int renorm, float* dl, uint16_t* dlb, float* colpart,
+                             int32_t* offs, int S, int32_t* offs1, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  router_bwd_kernel<<<(unsigned)((N + 63) / 64), 256, 0, s>>>(logits, topk_idx, dprob, (int)N, (int)E, (int)K,
+                                                               renorm, dl, dlb, colpart, offs, S, offs1);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd_reduce(const float* part, int S, int64_t ED, uint16_t* dw_r, const float* colpart,
+                                    int64_t P, int64_t E, float* db_r, hipStream_t s) {
+  router_bwd_reduce_kernel<<<1024, 256, 0, s>>>(part, S, ED, dw_r, colpart, P, E, db_r);
+  return hipGetLastError();
+}
+
 }  // namespace moe
