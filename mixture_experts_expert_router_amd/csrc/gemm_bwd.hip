@@ -93,20 +93,36 @@ __device__ __forceinline__ void epilogue_dg(const DgradParams& p, const Item& it
   for (int i = 0; i < C::TM; ++i) {
     const int64_t row = it.m_start + wm * C::WM + i * 16 + l16;
     if (row >= it.m1) continue;
+    if constexpr (!SWB) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
-      if (n >= p.N) continue;
-      const f32x4_t a = acc[i][j];
-      const int64_t off = row * p.N + n;
-      if constexpr (!SWB) {
-        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-      } else {
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+        if (n >= p.N) continue;
+        const f32x4_t a = acc[i][j];
+        *reinterpret_cast<uint2*>(p.c0 + row * p.N + n) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+      }
+    } else {
+      // the saved G and U of the whole fragment row first, so their loads
+      // overlap instead of waiting one fragment at a time
+      uint2 gw[C::TN], uw[C::TN];
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+        gw[j] = uw[j] = make_uint2(0, 0);
+        if (n < p.N) {
+          gw[j] = *reinterpret_cast<const uint2*>(p.g + row * p.N + n);
+          uw[j] = *reinterpret_cast<const uint2*>(p.u + row * p.N + n);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+        if (n >= p.N) continue;
+        const f32x4_t a = acc[i][j];
+        const int64_t off = row * p.N + n;
         // a = dH; dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G)
-        const uint2 gw = *reinterpret_cast<const uint2*>(p.g + off);
-        const uint2 uw = *reinterpret_cast<const uint2*>(p.u + off);
-        const float gg[4] = {bf16lo(gw.x), bf16hi(gw.x), bf16lo(gw.y), bf16hi(gw.y)};
-        const float uu[4] = {bf16lo(uw.x), bf16hi(uw.x), bf16lo(uw.y), bf16hi(uw.y)};
+        const float gg[4] = {bf16lo(gw[j].x), bf16hi(gw[j].x), bf16lo(gw[j].y), bf16hi(gw[j].y)};
+        const float uu[4] = {bf16lo(uw[j].x), bf16hi(uw[j].x), bf16lo(uw[j].y), bf16hi(uw[j].y)};
         float dg[4], du[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

@@ -54,7 +54,7 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
                              int64_t E, int64_t K, int renorm, float* dl, uint16_t* dlb, float* colpart,
                              int32_t* offs, int S, int32_t* offs1, hipStream_t s);
 // dw_r = bf16(sum over S fp32 partials [S][E*D], in order) when part != NULL;
-// db_r = sum over the ceil(N/64) column partials, in order, when db_r != NULL
+// db_r = sum over the ceil(N/64) column partials, in a fixed order, when db_r != NULL
 hipError_t launch_router_bwd_reduce(const float* part, int S, int64_t ED, uint16_t* dw_r, const float* colpart,
                                     int64_t P, int64_t E, float* db_r, hipStream_t s);
 

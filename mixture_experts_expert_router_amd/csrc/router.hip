@@ -369,12 +369,14 @@ __global__ __launch_bounds__(256) void router_bwd_reduce_kernel(const float* __r
       reinterpret_cast<uint2*>(dw_r)[i] = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
     }
   }
-  if (db_r) {
-    for (int64_t e = tid; e < E; e += stride) {
-      float a = 0.0f;
-      for (int64_t b = 0; b < P; ++b) a += colpart[b * E + e];
-      db_r[e] = a;
-    }
+  if (db_r && blockIdx.x < E && threadIdx.x < 64) {
+    // one wave per expert: lane l adds partials l, l + 64, ... in order, then
+    // the lanes' sums are added by a fixed shuffle tree
+    const int64_t e = blockIdx.x;
+    float a = 0.0f;
+    for (int64_t b = threadIdx.x; b < P; b += 64) a += colpart[b * E + e];
+    a = wave_sum(a);
+    if (threadIdx.x == 0) db_r[e] = a;
   }
 }
 
@@ -399,7 +401,7 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
 
 hipError_t launch_router_bwd_reduce(const float* part, int S, int64_t ED, uint16_t* dw_r, const float* colpart,
                                     int64_t P, int64_t E, float* db_r, hipStream_t s) {
-  router_bwd_reduce_kernel<<<1024, 256, 0, s>>>(part, S, ED, dw_r, colpart, P, E, db_r);
+  router_bwd_reduce_kernel<<<1024, 256, 0, s>>>(part, S, ED, dw_r, colpart, P, E, db_r);   // E <= 1024 blocks
   return hipGetLastError();
 }
 
