@@ -280,7 +280,9 @@ typedef struct moe_layer_saved {
   uint8_t* xd_s;        /* MXFP8 [rows_cap][D/32] */
   void* g;              /* bf16 [rows_cap][H] */
   void* u;              /* bf16 [rows_cap][H] */
-  void* h;              /* bf16 [rows_cap][H] */
+  void* h;              /* bf16 [rows_cap][H]; may be NULL for moe_layer_bwd, which then
+                           recomputes H = silu(G) U from g and u (KOSMOS's SwiGLU-recompute
+                           mode), bitwise equal to the forward's H */
   uint8_t* h_q;         /* MXFP8 [rows_cap][H] */
   uint8_t* h_s;         /* MXFP8 [rows_cap][H/32] */
   void* y;              /* bf16 [rows_cap][D] */

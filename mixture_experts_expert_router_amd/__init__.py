@@ -421,9 +421,14 @@ class MoeLayer:
                                     self.ws_f.numel(), _stream()), "moe_layer_fwd")
         return self.out
 
-    def backward(self, x, dout):
+    def backward(self, x, dout, recompute_h=False):
+        """recompute_h: do not read the saved H; the library recomputes it from G and U."""
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8)
-        _check(load().moe_layer_bwd(C.byref(a), C.byref(self._sv), _ptr(dout), C.byref(self._gr),
+        sv = self._sv
+        if recompute_h:
+            sv = LayerSaved(*[getattr(self._sv, n) for n, _ in LayerSaved._fields_])
+            sv.h = None
+        _check(load().moe_layer_bwd(C.byref(a), C.byref(sv), _ptr(dout), C.byref(self._gr),
                                     _ptr(self.ws_b), self.ws_b.numel(), _stream()), "moe_layer_bwd")
         return self.grads
 

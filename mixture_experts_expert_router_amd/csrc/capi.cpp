@@ -122,7 +122,8 @@ RouterBwdLayout router_bwd_layout(const moe_dims& d) {
 
 size_t bwd_scratch_bytes(const moe_dims& d) {
   const size_t rc = (size_t)rows_cap_of(d);
-  return 2 * round_up(rc * d.D * 2, 256) + 2 * round_up(rc * d.H * 2, 256) + router_bwd_layout(d).total;
+  // dY_d, dX_d, dG, dU, H when recomputed, the router backward's scratch
+  return 2 * round_up(rc * d.D * 2, 256) + 3 * round_up(rc * d.H * 2, 256) + router_bwd_layout(d).total;
 }
 
 }  // namespace
@@ -472,7 +473,7 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   REQUIRE(sv->xd);
   REQUIRE(sv->g);
   REQUIRE(sv->u);
-  REQUIRE(sv->h);
+  OPTIONAL(sv->h);   // NULL: recomputed from G and U
   REQUIRE(sv->y);
   REQUIRE(gr->dx);
   REQUIRE(gr->dprob);
@@ -503,13 +504,18 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   void* dg = p;
   p += round_up((size_t)rc * d.H * 2, 256);
   void* du = p;
+  p += round_up((size_t)rc * d.H * 2, 256);
+  // SwiGLU-recompute mode: H = silu(G) U from the saved bf16 G and U, the
+  // same arithmetic as GEMM1's epilogue, so it equals the forward's H bit for bit
+  const void* h = sv->h ? sv->h : (const void*)p;
 
   hipError_t e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd,
                                          gr->dprob, s);
+  if (e == hipSuccess && !sv->h) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, (void*)h, nullptr, nullptr, s);
   if (e == hipSuccess && d.align > 1)
     e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, dyd, 0, nullptr, s);
   // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
-  moe::GemmBwd down{d.E, rc, d.H, d.D, sv->offsets, sv->h, a->w_down, nullptr, dyd, nullptr, nullptr,
+  moe::GemmBwd down{d.E, rc, d.H, d.D, sv->offsets, h, a->w_down, nullptr, dyd, nullptr, nullptr,
                     sv->g, sv->u, dg, du, true};
   if (e == hipSuccess) e = gemm_dgrad(down, table, s);
   if (e == hipSuccess) e = gemm_wgrad(down, dyd, gr->dw_down, table, s);
@@ -522,7 +528,7 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   const void* dxr = nullptr;
   if (e == hipSuccess && gr->dw_r) {
     // router backward, after the expert backward so the fold below adds dX_r
-    p += round_up((size_t)rc * d.H * 2, 256);
+    p += round_up((size_t)rc * d.H * 2, 256);   // past H
     const RouterBwdLayout l = router_bwd_layout(d);
     float* dl = gr->dlogits ? gr->dlogits : (float*)(p + l.dl);
     uint16_t* dlb = (uint16_t*)(p + l.dlb);

@@ -164,6 +164,27 @@ def test_layer_bwd_router(name, renorm):
     assert_bf16_close(vals(g["dw_down"]), rb["dw_down"], "dw_down")
 
 
+@pytest.mark.parametrize("name", ["qwen3_shape_small", "mixtral_shape_small"])
+def test_layer_bwd_recompute_h_is_bitwise_equal(name):
+    """SwiGLU-recompute mode: the backward without the saved H (recomputed from
+    G and U) gives every gradient bit for bit as with it."""
+    wl = LAYER_CASES[name]
+    print(f"layer bwd recompute H {name}", flush=True)
+    inp = S.make_inputs(wl, 4)
+    dout = dev_bf16(inp.dout if inp.dout is not None else S.random_bf16((wl.N, wl.D), 4, 9))
+    w, _ = _weights(inp)
+    drop = dev(inp.drop) if inp.drop is not None else None
+    layer = M.MoeLayer(w, wl.N, wl.K, drop=drop, with_bwd=True, router_bwd=True)
+    x = dev_bf16(inp.x)
+    layer.forward(x)
+    g1 = {k: v.clone() for k, v in layer.backward(x, dout).items()}
+    layer.saved["h"].fill_(float("nan"))        # the saved H must not be read
+    g2 = layer.backward(x, dout, recompute_h=True)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k].view(torch.uint8), g2[k].view(torch.uint8)), k
+
+
 @pytest.mark.parametrize("N,D,E,K,H", [(256, 256, 16, 4, 128), (300, 512, 32, 8, 256)])
 def test_layer_fwd_mxfp8(N, D, E, K, H):
     wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_small", N=N, D=D, E=E, K=K, H=H)
