@@ -155,6 +155,52 @@ def pmc_report(fetch_dir, write_dir, copy_mib, workload):
     return summary, rows
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+
+
+def mfma_report(run_dir, cus=256, xcds=8):
+    """MFMA utilisation per GEMM kernel from one rocprofv3 --pmc run with
+    MFMA_COUNTERS.  rocprofv3 reports each counter summed over its instances:
+    GRBM_GUI_ACTIVE over the xcds XCDs, the SQ counters over every SIMD.  So
+    busy share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * cus * 4
+    SIMDs), and the clock the kernel ran at = GRBM_GUI_ACTIVE / xcds / duration.
+    Achieved FLOP/s = 512 FLOP per MFMA MOP over the dispatch's duration.
+    Averaged over each kernel's dispatches; durations are the counted runs' own."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    disp = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault((f, r["Dispatch_Id"]), {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) -
+                                                              int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = {}
+    for d in disp.values():
+        if "gemm" not in d["name"] or not d.get("GRBM_GUI_ACTIVE"):
+            continue
+        gui = d["GRBM_GUI_ACTIVE"] / xcds
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * cus * 4)
+        ghz = gui / d["ns"]
+        mops_bf = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        mops_f8 = d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0)
+        s_ = d["ns"] * 1e-9
+        per.setdefault(d["name"], []).append((busy, 512 * mops_bf / s_ / 1e12, 512 * mops_f8 / s_ / 1e12, d["ns"], ghz))
+    rows = []
+    for name, v in per.items():
+        n = len(v)
+        busy, tf_bf, tf_f8, ns, ghz = (sum(x[i] for x in v) / n for i in range(5))
+        mx = tf_f8 > tf_bf
+        peak = PEAK_MXFP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+        rows.append(dict(kernel=name, dispatches=n, busy_pct=100 * busy, tflops=tf_f8 if mx else tf_bf,
+                         pct_peak=100 * (tf_f8 if mx else tf_bf) / peak, dtype="mxfp8" if mx else "bf16",
+                         us=ns / 1e3, ghz=ghz))
+    rows.sort(key=lambda r: -r["us"] * r["dispatches"])
+    return rows
+
+
 def recorded_traffic(workload):
     """Bytes per launch of GEMM1 from the committed counter summary of this
     workload, or None when there is none or the GEMM sources changed since."""
@@ -343,10 +389,22 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
                          "that calibrates the HBM byte counters of a profiler run")
+    ap.add_argument("--pmc-mfma-report", metavar="DIR",
+                    help="print MFMA utilisation per GEMM kernel from one rocprofv3 --pmc run with the counters "
+                         + " ".join(MFMA_COUNTERS) + ", and exit")
     ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script with --copy-probe, and exit")
     args = ap.parse_args(argv)
+
+    if args.pmc_mfma_report:
+        print("| kernel | dispatches | avg us (counted run) | clock GHz | MFMA busy % | TFLOP/s (MOPS x 512) "
+              "| % of dense peak at 2.4 GHz |")
+        print("|---|---|---|---|---|---|---|")
+        for r in mfma_report(args.pmc_mfma_report):
+            print(f"| `{r['kernel'][:100]}` | {r['dispatches']} | {r['us']:.1f} | {r['ghz']:.2f} | {r['busy_pct']:.1f} | "
+                  f"{r['tflops']:.0f} ({r['dtype']}) | {r['pct_peak']:.1f} |")
+        return 0
 
     if args.pmc_report:
         summary, rows = pmc_report(args.pmc_report[0], args.pmc_report[1], args.copy_probe or 1024, args.workload)
