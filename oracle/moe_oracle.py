@@ -131,6 +131,55 @@ def topk_select(L, K: int) -> np.ndarray:
     return out
 
 
+def group_scores(L, n_group: int) -> np.ndarray:
+    """[N, n_group] score of each expert group: the sum of the two largest
+    routing probabilities in the group (the one probability of a one-expert
+    group).  Groups are n_group contiguous ranges of E / n_group experts."""
+    p = softmax(L)
+    N, E = p.shape
+    gs = E // n_group
+    top = -np.sort(-p.reshape(N, n_group, gs), axis=2)
+    return top[:, :, :2].sum(axis=2)
+
+
+def topk_select_grouped(L, K: int, n_group: int, topk_group: int) -> np.ndarray:
+    """Group-limited top-K [KOSMOS 3.3.1 step 1, "(group-limited) top-k";
+    the pages give no rule, see group_scores]: keep the topk_group groups with
+    the largest scores (ties to the lower group), then take the K largest logits
+    among the kept groups' experts (ties to the lower expert, best first)."""
+    L = np.asarray(L, dtype=np.float64)
+    N, E = L.shape
+    if E % n_group or topk_group > n_group or topk_group * (E // n_group) < K:
+        raise ValueError("bad grouping")
+    gkeep = topk_select(group_scores(L, n_group), topk_group)     # same ranking rule on the groups
+    gs = E // n_group
+    keep = np.zeros((N, n_group), dtype=bool)
+    np.put_along_axis(keep, gkeep.astype(np.int64), True, axis=1)
+    masked = np.where(np.repeat(keep, gs, axis=1), L, -np.inf)
+    return topk_select(masked, K)
+
+
+def aux_loss(L, counts, K: int, alpha: float):
+    """Load-balance loss from the route step's aux-loss inputs [KOSMOS 3.3.1
+    step 1; the pages give no formula, so the Switch-style reading]:
+    f_e = valid routes to e / (N K), P_e = mean over tokens of the routing
+    probability of e, aux = alpha * E * sum_e f_e P_e.  Returns (aux, P)."""
+    p = softmax(L)
+    N, E = p.shape
+    f = np.asarray(counts, dtype=np.float64) / (N * K)
+    P = p.mean(axis=0)
+    return float(alpha * E * np.sum(f * P)), P
+
+
+def aux_dlogits(L, counts, K: int, alpha: float, d_aux: float = 1.0) -> np.ndarray:
+    """Gradient of d_aux * aux_loss with respect to the logits, the counts
+    (a selection) held fixed: alpha E / N * p_te (f_e - sum_j p_tj f_j)."""
+    p = softmax(L)
+    N, E = p.shape
+    f = np.asarray(counts, dtype=np.float64) / (N * K)
+    return d_aux * alpha * E / N * p * (f[None, :] - (p @ f)[:, None])
+
+
 def route_weights(L, idx, renorm: int = 0) -> np.ndarray:
     """Dispatch weight of each selected slot in float64: the softmax
     probability of its expert, optionally divided by the sum over the K
@@ -480,7 +529,7 @@ def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
     return eb
 
 
-def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0) -> dict:
+def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0, aux_dl=None) -> dict:
     """Gradients of the router from the route-weight gradient dprob [N,K]
     (0 for invalid routes), in float64.  [KOSMOS 3.3.2 step 2: the router's
     dX_r and dW_r; the adjoint of router_logits and route_weights]
@@ -491,6 +540,7 @@ def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0) -> dict:
       g_e = ds_k where e = idx_k (the K experts are distinct), else 0;
       dL_e = p_e (g_e - sum_j p_j g_j)          (softmax backward);
     then dX_r = dL W_r, dW_r = dL^T x, db_r = sum over tokens of dL.
+    aux_dl, when given, is added to dL first (the aux loss's gradient).
     """
     L = np.asarray(logits, dtype=np.float64)
     N, E = L.shape
@@ -507,6 +557,8 @@ def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0) -> dict:
     g = np.zeros((N, E))
     np.put_along_axis(g, ix, ds, axis=1)
     dL = p * (g - np.sum(p * g, axis=1, keepdims=True))
+    if aux_dl is not None:          # the aux loss's own gradient (aux_dlogits)
+        dL = dL + aux_dl
     xv = values(x)
     wv = values(w_r)
     return dict(dlogits=dL, dx_r=dL @ wv, dw_r=dL.T @ xv, db_r=dL.sum(axis=0))

@@ -203,3 +203,61 @@ def test_router_bwd_closed_forms():
     # no upstream gradient, no router gradient
     g = O.router_bwd(L, idx, np.zeros((10, 6)), x, w, renorm=1)
     assert not np.any(g["dlogits"]) and not np.any(g["dw_r"]) and not np.any(g["db_r"])
+
+
+# -------------------------------------------- group-limited top-K, aux loss ----
+def test_grouped_topk_worked_example():
+    """Eight experts in four pairs, keep two groups, top-2.  Probabilities are
+    proportional to exp(logit): group sums e^5 = 148.4 (pair 0), e^4.9 + e^4.8 =
+    255.8 (pair 1), e^4.95 = 141.2 (pair 2), ~0 (pair 3).  Pairs 1 and 0 are
+    kept, so expert 4 (logit 4.95, second best overall) is excluded and the
+    selection is experts 0 and 2 instead of the plain 0 and 4."""
+    L = np.array([[5.0, -9.0, 4.9, 4.8, 4.95, -9.0, -9.0, -9.0]])
+    assert O.topk_select(L, 2).tolist() == [[0, 4]]
+    assert O.topk_select_grouped(L, 2, n_group=4, topk_group=2).tolist() == [[0, 2]]
+    g = O.group_scores(L, 4)
+    assert np.argsort(-g[0]).tolist()[:2] == [1, 0]
+
+
+def test_grouped_topk_reduces_to_plain():
+    rng = np.random.default_rng(7)
+    L = rng.standard_normal((50, 32))
+    assert np.array_equal(O.topk_select_grouped(L, 4, 1, 1), O.topk_select(L, 4))
+    assert np.array_equal(O.topk_select_grouped(L, 4, 8, 8), O.topk_select(L, 4))
+
+
+def test_grouped_topk_keeps_whole_groups_and_ties():
+    rng = np.random.default_rng(8)
+    L = rng.standard_normal((40, 24))
+    # K = topk_group * group size: exactly the kept groups' experts, best first
+    sel = O.topk_select_grouped(L, 12, n_group=6, topk_group=3)
+    gsc = O.group_scores(L, 6)
+    for t in range(40):
+        groups = set((sel[t] // 4).tolist())
+        assert len(groups) == 3 and all(len([e for e in sel[t] if e // 4 == g]) == 4 for g in groups)
+        assert min(gsc[t, list(groups)]) >= max(np.delete(gsc[t], list(groups)))
+        assert np.all(np.diff(L[t, sel[t]]) <= 0)
+    # two groups with equal scores: the lower group is kept
+    L = np.zeros((1, 8))
+    L[0, [2, 3, 6, 7]] = 1.0
+    assert O.topk_select_grouped(L, 2, n_group=4, topk_group=1).tolist() == [[2, 3]]
+
+
+def test_aux_loss_closed_form_and_gradient():
+    # uniform probabilities and loads: f = P = 1/E, so aux = alpha exactly
+    N, E, K = 64, 16, 4
+    aux, P = O.aux_loss(np.zeros((N, E)), np.full(E, N * K // E), K, 0.01)
+    assert abs(aux - 0.01) <= 1e-15 and np.allclose(P, 1 / E)
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((N, E))
+    counts = rng.integers(0, 3 * N * K // E, E)
+    alpha, d_aux = 0.003, 1.7
+    g = O.aux_dlogits(L, counts, K, alpha, d_aux)
+    v = rng.standard_normal(L.shape)
+    eps = 1e-6
+    fd = d_aux * (O.aux_loss(L + eps * v, counts, K, alpha)[0] - O.aux_loss(L - eps * v, counts, K, alpha)[0]) / (2 * eps)
+    assert abs(fd - float(np.sum(g * v))) <= 1e-8 * max(1.0, abs(fd))
+    Lt = torch.tensor(L, requires_grad=True)
+    f = torch.tensor(counts, dtype=torch.float64) / (N * K)
+    (d_aux * alpha * E * (f * torch.softmax(Lt, dim=1).mean(dim=0)).sum()).backward()
+    assert np.allclose(g, Lt.grad.numpy(), rtol=1e-12, atol=1e-16)
