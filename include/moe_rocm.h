@@ -77,6 +77,14 @@ typedef struct moe_dims {
   int64_t N, D, E, K, H;
   int32_t align;
   int32_t renorm;
+  /* Group-limited top-K (KOSMOS section 3.3.1 step 1), on when n_group > 1:
+   * the E experts form n_group contiguous groups (E % n_group == 0,
+   * n_group <= 64); a group scores the sum of its two largest routing
+   * probabilities; the topk_group best groups (ties to the lower group) are
+   * kept and top-K runs over their experts (1 <= topk_group <= n_group,
+   * topk_group * E / n_group >= K).  0 or 1: plain top-K. */
+  int32_t n_group;
+  int32_t topk_group;
 } moe_dims;
 
 /* Rows of every expert-contiguous buffer: N*K + E*(align-1).  No routing can
@@ -265,6 +273,11 @@ typedef struct moe_layer_args {
   const uint8_t* wu_s;
   const uint8_t* wd_q;
   const uint8_t* wd_s;
+  /* Aux loss (KOSMOS section 3.3.1 step 1: the routing step's aux-loss
+   * inputs, reduced once): aux = aux_alpha * E * sum_e f_e P_e with f_e the
+   * share of valid routes to e and P_e the mean routing probability of e.
+   * Computed into saved->aux when aux_alpha != 0 and saved->aux != NULL. */
+  float aux_alpha;
 } moe_layer_args;
 
 typedef struct moe_layer_saved {
@@ -286,6 +299,7 @@ typedef struct moe_layer_saved {
   uint8_t* h_q;         /* MXFP8 [rows_cap][H] */
   uint8_t* h_s;         /* MXFP8 [rows_cap][H/32] */
   void* y;              /* bf16 [rows_cap][D] */
+  float* aux;           /* fp32 [1], optional: the aux loss */
 } moe_layer_saved;
 
 int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* saved, void* out, void* ws,
@@ -306,6 +320,10 @@ typedef struct moe_layer_grads {
   void* dw_r;      /* bf16 [E][D] */
   float* db_r;     /* fp32 [E] */
   float* dlogits;  /* fp32 [N][E] */
+  /* Upstream gradient of the aux loss (a host value; 0 = none).  With
+   * a->aux_alpha != 0 the router backward adds d_aux times the aux loss's
+   * logit gradient, the counts held fixed. */
+  float d_aux;
 } moe_layer_grads;
 
 int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* saved, const void* dout,

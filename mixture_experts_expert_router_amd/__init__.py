@@ -32,7 +32,7 @@ _i32 = C.c_int32
 
 class Dims(C.Structure):
     _fields_ = [("N", _i64), ("D", _i64), ("E", _i64), ("K", _i64), ("H", _i64),
-                ("align", _i32), ("renorm", _i32)]
+                ("align", _i32), ("renorm", _i32), ("n_group", _i32), ("topk_group", _i32)]
 
 
 class GemmFwdArgs(C.Structure):
@@ -53,17 +53,18 @@ class LayerArgs(C.Structure):
     _fields_ = [("dims", Dims), ("dtype", _i32), ("sched", _i32), ("x", _vp), ("w_r", _vp),
                 ("bias", _vp), ("drop", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("wg_q", _vp), ("wg_s", _vp), ("wu_q", _vp), ("wu_s", _vp), ("wd_q", _vp),
-                ("wd_s", _vp)]
+                ("wd_s", _vp), ("aux_alpha", C.c_float)]
 
 
 class LayerSaved(C.Structure):
     _fields_ = [(n, _vp) for n in ("logits", "topk_idx", "topk_prob", "counts", "offsets",
                                    "dst_rows", "row_route", "xd", "xd_q", "xd_s", "g", "u", "h",
-                                   "h_q", "h_s", "y")]
+                                   "h_q", "h_s", "y", "aux")]
 
 
 class LayerGrads(C.Structure):
-    _fields_ = [(n, _vp) for n in ("dx", "dprob", "dw_gate", "dw_up", "dw_down", "dw_r", "db_r", "dlogits")]
+    _fields_ = [(n, _vp) for n in ("dx", "dprob", "dw_gate", "dw_up", "dw_down", "dw_r", "db_r", "dlogits")] + \
+               [("d_aux", C.c_float)]
 
 
 EXPORTS = {
@@ -130,8 +131,8 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
-def dims(N, D, E, K, H=0, align=1, renorm=0) -> Dims:
-    return Dims(int(N), int(D), int(E), int(K), int(H), int(align), int(renorm))
+def dims(N, D, E, K, H=0, align=1, renorm=0, n_group=0, topk_group=0) -> Dims:
+    return Dims(int(N), int(D), int(E), int(K), int(H), int(align), int(renorm), int(n_group), int(topk_group))
 
 
 def rows_cap(d: Dims) -> int:
@@ -159,11 +160,12 @@ def router_logits(x, w_r, bias=None, out=None, ws=None):
     return out
 
 
-def route(logits, K, drop=None, renorm=0, align=1, ws=None):
-    """Returns dict(topk_idx, topk_prob, counts, offsets, dst_rows, row_route)."""
+def route(logits, K, drop=None, renorm=0, align=1, ws=None, n_group=0, topk_group=0):
+    """Returns dict(topk_idx, topk_prob, counts, offsets, dst_rows, row_route).
+    n_group > 1: group-limited top-K keeping topk_group groups."""
     torch = _torch()
     N, E = logits.shape
-    d = dims(N, 8, E, K, align=align, renorm=renorm)
+    d = dims(N, 8, E, K, align=align, renorm=renorm, n_group=n_group, topk_group=topk_group)
     dev = logits.device
     rc = rows_cap(d)
     o = dict(topk_idx=torch.empty((N, K), dtype=torch.int32, device=dev),
@@ -341,19 +343,20 @@ def quantize_weights_mxfp8(w_gate, w_up, w_down) -> dict:
     return out
 
 
-def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_STAGED):
+def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_STAGED, n_group=0, topk_group=0,
+                aux_alpha=0.0):
     N, D = x.shape
     E = wts.w_r.shape[0]
     if mxfp8:
         H = wts.wq["wg_q"].shape[1]
     else:
         H = wts.w_gate.shape[1]
-    d = dims(N, D, E, K, H, align=32 if mxfp8 else 1, renorm=renorm)
+    d = dims(N, D, E, K, H, align=32 if mxfp8 else 1, renorm=renorm, n_group=n_group, topk_group=topk_group)
     q = wts.wq or {}
     a = LayerArgs(d, MOE_MXFP8 if mxfp8 else MOE_BF16, sched, _ptr(x), _ptr(wts.w_r), _ptr(wts.bias),
                   _ptr(drop), _ptr(wts.w_gate), _ptr(wts.w_up), _ptr(wts.w_down),
                   _ptr(q.get("wg_q")), _ptr(q.get("wg_s")), _ptr(q.get("wu_q")), _ptr(q.get("wu_s")),
-                  _ptr(q.get("wd_q")), _ptr(q.get("wd_s")))
+                  _ptr(q.get("wd_q")), _ptr(q.get("wd_s")), float(aux_alpha))
     return a, d
 
 
@@ -388,14 +391,20 @@ class MoeLayer:
     forward's launch scheme (MOE_SCHED_STAGED or MOE_SCHED_READY)."""
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
-                 device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False):
+                 device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False, n_group=0,
+                 topk_group=0, aux_alpha=0.0):
+        """n_group/topk_group: group-limited top-K; aux_alpha != 0: the aux loss
+        goes to saved["aux"] and its gradient into the router backward."""
         torch = _torch()
         self.wts, self.K, self.mxfp8, self.renorm, self.drop = wts, K, mxfp8, renorm, drop
         self.sched = sched
+        self._opts = dict(n_group=n_group, topk_group=topk_group, aux_alpha=aux_alpha)
         D = wts.w_r.shape[1]
         self._x_proto = torch.empty((N, D), dtype=torch.bfloat16, device=device)
-        _, self.d = _layer_args(self._x_proto, wts, K, drop, renorm, mxfp8)
+        _, self.d = _layer_args(self._x_proto, wts, K, drop, renorm, mxfp8, **self._opts)
         self.saved = alloc_saved(self.d, mxfp8, device)
+        if aux_alpha:
+            self.saved["aux"] = torch.zeros(1, dtype=torch.float32, device=device)
         self._sv = _saved_struct(self.saved)
         self.out = torch.empty((N, D), dtype=torch.bfloat16, device=device)
         self.ws_f = workspace(MOE_OP_LAYER_FWD, self.d, device)
@@ -413,17 +422,19 @@ class MoeLayer:
                 self.grads.update(dw_r=torch.empty((E, D), dtype=torch.bfloat16, device=device),
                                   db_r=torch.empty((E,), dtype=torch.float32, device=device),
                                   dlogits=torch.empty((N, E), dtype=torch.float32, device=device))
-            self._gr = LayerGrads(*[_ptr(self.grads.get(n)) for n, _ in LayerGrads._fields_])
+            self._gr = LayerGrads(**{n: _ptr(self.grads.get(n)) for n, t in LayerGrads._fields_ if t is _vp})
 
     def forward(self, x):
-        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched)
+        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched, **self._opts)
         _check(load().moe_layer_fwd(C.byref(a), C.byref(self._sv), _ptr(self.out), _ptr(self.ws_f),
                                     self.ws_f.numel(), _stream()), "moe_layer_fwd")
         return self.out
 
-    def backward(self, x, dout, recompute_h=False):
-        """recompute_h: do not read the saved H; the library recomputes it from G and U."""
-        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8)
+    def backward(self, x, dout, recompute_h=False, d_aux=0.0):
+        """recompute_h: do not read the saved H; the library recomputes it from G and U.
+        d_aux: upstream gradient of the aux loss (used when aux_alpha != 0)."""
+        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, **self._opts)
+        self._gr.d_aux = float(d_aux)
         sv = self._sv
         if recompute_h:
             sv = LayerSaved(*[getattr(self._sv, n) for n, _ in LayerSaved._fields_])

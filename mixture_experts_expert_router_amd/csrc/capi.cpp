@@ -37,6 +37,10 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
   if (d->align != 1 && d->align != 32) return MOE_ERR_SHAPE;
   if (mxfp8 && (d->D % 32 || (need_h && d->H % 32) || d->align != 32)) return MOE_ERR_SHAPE;
   if (d->N * d->K >= (int64_t(1) << 31) || rows_cap_of(*d) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (d->n_group < 0) return MOE_ERR_SHAPE;
+  if (d->n_group > 1 && (d->n_group > 64 || d->E % d->n_group || d->topk_group < 1 ||
+                         d->topk_group > d->n_group || d->topk_group * (d->E / d->n_group) < d->K))
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -193,7 +197,8 @@ int moe_route(const float* logits, const uint8_t* drop, const moe_dims* d, int32
   if (ws_bytes < route_bytes(*d)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_route(logits, drop, d->N, d->E, d->K, d->renorm, d->align,
                                       rows_cap_of(*d), topk_idx, topk_prob, counts, offsets,
-                                      dst_rows, row_route, ws, (hipStream_t)stream));
+                                      dst_rows, row_route, ws, (hipStream_t)stream, d->n_group,
+                                      d->topk_group));
 }
 
 int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, const int32_t* counts,
@@ -410,6 +415,8 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     REQUIRE(a->w_down);
     REQUIRE(sv->xd);
   }
+  OPTIONAL(sv->aux);
+  const bool aux = sv->aux != nullptr && a->aux_alpha != 0.0f;
   const int64_t rc = rows_cap_of(d);
   const size_t rb = route_bytes(d), tb = table_bytes(rc, d.E);
   if (ws_bytes < rb + tb + router_bytes(d)) return MOE_ERR_WORKSPACE;
@@ -422,7 +429,8 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (e == hipSuccess)
     e = moe::launch_route(sv->logits, a->drop, d.N, d.E, d.K, d.renorm, d.align, rc, sv->topk_idx,
                           sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,
-                          ws_route, s);
+                          ws_route, s, d.n_group, d.topk_group, aux);
+  if (e == hipSuccess && aux) e = moe::launch_aux_loss(ws_route, d.N, d.E, d.K, sv->counts, a->aux_alpha, sv->aux, s);
   if (mx) {
     if (e == hipSuccess) e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s);
     if (e == hipSuccess)
@@ -537,8 +545,11 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     float* part = (float*)(p + l.part);
     float* colpart = (float*)(p + l.colpart);
     dxr = p + l.dxr;
+    // the aux loss's gradient: d_aux alpha E / N * p (f - sum_j p_j f_j), f = counts / (N K)
+    const bool aux = a->aux_alpha != 0.0f && gr->d_aux != 0.0f;
+    const float aux_c = aux ? gr->d_aux * a->aux_alpha * (float)d.E / ((float)d.N * (float)d.N * (float)d.K) : 0.0f;
     e = moe::launch_router_bwd(sv->logits, sv->topk_idx, gr->dprob, d.N, d.E, d.K, d.renorm, dl, dlb, colpart,
-                               offs, l.S, offs1, s);
+                               offs, l.S, offs1, s, aux ? sv->counts : nullptr, aux_c);
     // forward L = x . w_r^T: k_dim = D, n_dim = E, one expert over all N rows
     moe::GemmBwd rt{1, d.N, d.D, d.E, offs1, a->x, a->w_r, nullptr, dlb, nullptr, (void*)dxr,
                     nullptr, nullptr, nullptr, nullptr, false};

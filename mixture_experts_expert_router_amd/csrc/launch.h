@@ -52,7 +52,8 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
 int router_wgrad_splits(int64_t N, int64_t D, int64_t E);
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* dprob, int64_t N,
                              int64_t E, int64_t K, int renorm, float* dl, uint16_t* dlb, float* colpart,
-                             int32_t* offs, int S, int32_t* offs1, hipStream_t s);
+                             int32_t* offs, int S, int32_t* offs1, hipStream_t s,
+                             const int32_t* aux_counts = nullptr, float aux_c = 0.0f);
 // dw_r = bf16(sum over S fp32 partials [S][E*D], in order) when part != NULL;
 // db_r = sum over the ceil(N/64) column partials, in a fixed order, when db_r != NULL
 hipError_t launch_router_bwd_reduce(const float* part, int S, int64_t ED, uint16_t* dw_r, const float* colpart,
@@ -63,7 +64,12 @@ size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K);
 hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int64_t E, int64_t K,
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
-                        void* ws, hipStream_t s);
+                        void* ws, hipStream_t s,
+                        int n_group = 0, int topk_group = 0, bool aux_inputs = false);
+// aux loss of the routed layer from the route step's probability sums (left
+// in the route workspace by launch_route with aux_inputs) and the counts
+hipError_t launch_aux_loss(void* route_ws, int64_t N, int64_t E, int64_t K, const int32_t* counts, float alpha,
+                           float* aux, hipStream_t s);
 
 // permute.hip
 hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,

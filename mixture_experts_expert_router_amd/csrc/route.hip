@@ -26,16 +26,27 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Group-limited selection (n_group > 1): the experts form n_group contiguous
+// groups; a group scores the sum of its two largest routing probabilities,
+// the topk_group best groups (ties to the lower group) are kept, and top-K
+// runs over their experts.  psum (optional): this chunk's per-expert sums of
+// the routing probabilities, the aux-loss input.  Both use a dynamic LDS row
+// of E floats per wave.
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, const uint8_t* __restrict__ drop, int N, int E, int K,
     int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
     int32_t* __restrict__ row_route, int64_t rows_cap, int32_t* __restrict__ hist,
-    int32_t* __restrict__ rank) {
+    int32_t* __restrict__ rank, int n_group, int topk_group, float* __restrict__ psum) {
   __shared__ int s_sel[kChunk * 32];      // K <= 32 checked on the host
   __shared__ int s_hist[kMaxE];
+  extern __shared__ float s_row[];        // [kChunk][E] when grouped or psum
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kChunk;
+  const bool grouped = n_group > 1;
+  float pacc[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) pacc[j] = 0.0f;
 
   // row_route = -1 everywhere first (the scatter overwrites the used rows)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows_cap;
@@ -67,8 +78,52 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       if (e < E) se += expf(v[j] - mx);
     }
     se = wave_sum(se);
-    // top-K: K rounds of a wave arg-max (value desc, index asc)
     uint32_t taken = 0;
+    if (grouped || psum) {
+      float* prow = s_row + wave * E;
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) {
+        const int e = lane + j * kWave;
+        if (e < E) {
+          const float pj = expf(v[j] - mx) / se;
+          pacc[j] += pj;
+          prow[e] = pj;
+        }
+      }
+      if (grouped) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const int gs = E / n_group;
+        float sc = -INFINITY;                  // lane g < n_group: group g's score
+        if (lane < n_group) {
+          float b1 = -INFINITY, b2 = -INFINITY;
+          for (int i = 0; i < gs; ++i) {
+            const float q = prow[lane * gs + i];
+            if (q > b1) { b2 = b1; b1 = q; }
+            else if (q > b2) b2 = q;
+          }
+          sc = gs > 1 ? b1 + b2 : b1;
+        }
+        uint64_t keep = 0;
+        for (int r = 0; r < topk_group; ++r) {
+          float bv = (lane < n_group && !((keep >> lane) & 1ull)) ? sc : -INFINITY;
+          int bi = lane < n_group && !((keep >> lane) & 1ull) ? lane : 0x7FFFFFFF;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+          }
+          keep |= 1ull << bi;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+          const int e = lane + j * kWave;
+          if (e < E && !((keep >> (e / gs)) & 1ull)) taken |= 1u << j;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    }
+    // top-K: K rounds of a wave arg-max (value desc, index asc)
     float psel = 0.0f;       // this lane's slot-k probability, lane k holds slot k
     int isel = 0;
     for (int k = 0; k < K; ++k) {
@@ -117,6 +172,42 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = s_hist[e];
+  if (psum) {
+    // the chunk's probability sums, added over its waves in order
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = lane + j * kWave;
+      if (e < E) s_row[wave * E + e] = pacc[j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float a = 0.0f;
+      for (int w = 0; w < kChunk; ++w) a += s_row[w * E + e];
+      psum[(int64_t)blockIdx.x * E + e] = a;
+    }
+  }
+}
+
+// Aux loss (KOSMOS section 3.3.1 step 1: the routing step's aux-loss inputs,
+// reduced once per layer): P_e = the routing probabilities of expert e summed
+// over tokens (one wave per expert, chunks strided over lanes, fixed order),
+// then aux = alpha E sum_e (counts_e / (N K)) (P_e / N) in one wave.
+__global__ __launch_bounds__(64) void aux_psum_kernel(const float* __restrict__ psum, int64_t nchunks, int E,
+                                                      float* __restrict__ prob_sum) {
+  const int e = blockIdx.x;
+  float a = 0.0f;
+  for (int64_t c = threadIdx.x; c < nchunks; c += 64) a += psum[c * E + e];
+  a = wave_sum(a);
+  if (threadIdx.x == 0) prob_sum[e] = a;
+}
+
+__global__ __launch_bounds__(64) void aux_loss_kernel(const float* __restrict__ prob_sum,
+                                                      const int32_t* __restrict__ counts, int64_t N, int E,
+                                                      int K, float alpha, float* __restrict__ aux) {
+  float a = 0.0f;
+  for (int e = threadIdx.x; e < E; e += 64) a += (float)counts[e] * prob_sum[e];
+  a = wave_sum(a);
+  if (threadIdx.x == 0) aux[0] = alpha * (float)E * a / ((float)N * (float)K * (float)N);
 }
 
 // One workgroup of 1024 threads.  Thread (e, g) owns expert e and the chunk
@@ -219,32 +310,55 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
   row_route[dst] = (int32_t)r;
 }
 
-size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K) {
+namespace {
+size_t route_psum_offset(int64_t N, int64_t E, int64_t K) {
   const int64_t nchunks = N > 0 ? (N + kChunk - 1) / kChunk : 1;
   size_t b = (size_t)nchunks * E * 4;   // hist / bases
   b = (b + 255) & ~(size_t)255;
   b += (size_t)N * K * 4;               // in-chunk ranks
   return (b + 255) & ~(size_t)255;
 }
+}  // namespace
+
+size_t route_workspace_bytes(int64_t N, int64_t E, int64_t K) {
+  const int64_t nchunks = N > 0 ? (N + kChunk - 1) / kChunk : 1;
+  // then per-chunk probability sums [chunks][E] and P [E] for the aux loss
+  return route_psum_offset(N, E, K) + (((size_t)nchunks * E * 4 + 255) & ~(size_t)255) +
+         (((size_t)E * 4 + 255) & ~(size_t)255);
+}
+
+hipError_t launch_aux_loss(void* ws, int64_t N, int64_t E, int64_t K, const int32_t* counts, float alpha,
+                           float* aux, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int64_t nchunks = (N + kChunk - 1) / kChunk;
+  float* psum = (float*)((char*)ws + route_psum_offset(N, E, K));
+  float* prob_sum = psum + (((size_t)nchunks * E * 4 + 255) & ~(size_t)255) / 4;
+  aux_psum_kernel<<<(unsigned)E, 64, 0, s>>>(psum, nchunks, (int)E, prob_sum);
+  aux_loss_kernel<<<1, 64, 0, s>>>(prob_sum, counts, N, (int)E, (int)K, alpha, aux);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int64_t E, int64_t K,
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, int n_group, int topk_group, bool aux_inputs) {
   const int64_t nchunks = (N + kChunk - 1) / kChunk;
   const int64_t nalloc = nchunks > 0 ? nchunks : 1;
   int32_t* hist = (int32_t*)ws;
   size_t hb = ((size_t)nalloc * E * 4 + 255) & ~(size_t)255;
   int32_t* rank = (int32_t*)((char*)ws + hb);
+  float* psum = aux_inputs ? (float*)((char*)ws + route_psum_offset(N, E, K)) : nullptr;
+  const int ng = n_group > 1 ? n_group : 0;
+  const size_t lds = (ng || psum) ? (size_t)kChunk * E * 4 : 0;
   if (nchunks > 0) {
-    route_topk_kernel<<<dim3((unsigned)nchunks), dim3(kTopkThreads), 0, s>>>(
+    route_topk_kernel<<<dim3((unsigned)nchunks), dim3(kTopkThreads), lds, s>>>(
         logits, drop, (int)N, (int)E, (int)K, renorm, topk_idx, topk_prob, row_route, rows_cap,
-        hist, rank);
+        hist, rank, ng, topk_group, psum);
   } else {
     // no tokens: still mark every row unused
     route_topk_kernel<<<dim3(1), dim3(kTopkThreads), 0, s>>>(logits, drop, 0, (int)E, (int)K, renorm,
                                                     topk_idx, topk_prob, row_route, rows_cap,
-                                                    hist, rank);
+                                                    hist, rank, 0, 0, nullptr);
   }
   route_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(hist, (int)nchunks, (int)E, align, counts,
                                                    offsets);

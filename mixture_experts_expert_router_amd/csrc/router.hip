@@ -245,7 +245,9 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
 // softmax of the saved logits and s_k = p[idx_k]:
 //   ds_k = dprob_k, or (dprob_k - sum_j w_j dprob_j) / S with renormalised
 //   weights w_k = s_k / S, S = sum_j s_j;
-//   dL_e = p_e (g_e - sum_k s_k ds_k), g_e = ds_k at e = idx_k, else 0.
+//   dL_e = p_e (g_e - sum_j p_j g_j), g_e = ds_k at e = idx_k, else 0, plus
+//   aux_c counts_e for every e when the aux loss is on (its gradient with
+//   the counts fixed).
 // One wave per token (kRbTok tokens per wave, 4 waves per workgroup); g goes
 // through a per-wave LDS row.  Each workgroup also writes the column sums of
 // its 64 tokens' dL, added in wave order, for the bias gradient.  The GEMMs
@@ -270,7 +272,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
                                                          int renorm, float* __restrict__ dl,
                                                          uint16_t* __restrict__ dlb, float* __restrict__ colpart,
                                                          int32_t* __restrict__ offs, int S,
-                                                         int32_t* __restrict__ offs1) {
+                                                         int32_t* __restrict__ offs1,
+                                                         const int32_t* __restrict__ aux_counts, float aux_c) {
   __shared__ float s_g[4][kRbMaxE];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (blockIdx.x == 0) {
@@ -285,6 +288,11 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     col[i] = 0.0f;
     if (i < nI && lane + 64 * i < E) g[lane + 64 * i] = 0.0f;
   }
+  // aux loss (optional): a_e = aux_c counts_e joins g for every expert
+  float aj[kRbCols];
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i)
+    aj[i] = (aux_counts && i < nI && lane + 64 * i < E) ? aux_c * (float)aux_counts[lane + 64 * i] : 0.0f;
   wave_lds_fence();
   const int t0 = blockIdx.x * 64 + w * kRbTok;
   for (int j = 0; j < kRbTok; ++j) {
@@ -321,7 +329,13 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
       const float c = wave_sum(sk * dk) / tot;   // sum_j w_j dprob_j
       ds = (dk - c) / tot;
     }
-    const float dot = wave_sum(sk * ds);
+    float pa = 0.0f;
+    if (aux_counts) {
+#pragma unroll
+      for (int i = 0; i < kRbCols; ++i)
+        if (i < nI && lane + 64 * i < E) pa += expf(l[i] - m) * rz * aj[i];
+    }
+    const float dot = wave_sum(sk * ds + pa);
     if (ek >= 0) g[ek] = ds;
     wave_lds_fence();
     float* dlr = dl + (int64_t)t * E;
@@ -330,7 +344,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     for (int i = 0; i < kRbCols; ++i) {
       const int e = lane + 64 * i;
       if (i < nI && e < E) {
-        const float d = expf(l[i] - m) * rz * (g[e] - dot);
+        const float d = expf(l[i] - m) * rz * (g[e] + aj[i] - dot);
         dlr[e] = d;
         dlbr[e] = (uint16_t)(pack_bf16x2(d, 0.0f) & 0xFFFFu);
         col[i] += d;
@@ -392,10 +406,12 @@ int router_wgrad_splits(int64_t N, int64_t D, int64_t E) {
 
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* dprob, int64_t N,
                              int64_t E, int64_t K, int renorm, float* dl, uint16_t* dlb, float* colpart,
-                             int32_t* offs, int S, int32_t* offs1, hipStream_t s) {
+                             int32_t* offs, int S, int32_t* offs1, hipStream_t s, const int32_t* aux_counts,
+                             float aux_c) {
   if (N == 0) return hipSuccess;
   router_bwd_kernel<<<(unsigned)((N + 63) / 64), 256, 0, s>>>(logits, topk_idx, dprob, (int)N, (int)E, (int)K,
-                                                               renorm, dl, dlb, colpart, offs, S, offs1);
+                                                               renorm, dl, dlb, colpart, offs, S, offs1,
+                                                               aux_counts, aux_c);
   return hipGetLastError();
 }
 

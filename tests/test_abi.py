@@ -94,3 +94,34 @@ def test_binding_fails_loudly_without_library(tmp_path):
             M.load(str(tmp_path / "missing.so"))
         finally:
             M._lib = saved
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structs have the header's sizes and field offsets."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    hdr = os.path.join(os.path.dirname(__file__), "..", "include", "moe_rocm.h")
+    checks = {"moe_dims": (M.Dims, ["N", "renorm", "n_group", "topk_group"]),
+              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha"]),
+              "moe_layer_saved": (M.LayerSaved, ["logits", "y", "aux"]),
+              "moe_layer_grads": (M.LayerGrads, ["dx", "dlogits", "d_aux"]),
+              "moe_gemm_fwd_args": (M.GemmFwdArgs, ["dtype", "act_scales"]),
+              "moe_gemm_bwd_args": (M.GemmBwdArgs, ["dtype", "db1"])}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include <stdint.h>', f'#include "{os.path.abspath(hdr)}"',
+             "int main(void) {"]
+    for st, (_, fields) in checks.items():
+        lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
+        for f in fields:
+            lines.append(f'  printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", str(src), "-o", str(exe)], check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                   check=True).stdout.splitlines())
+    for st, (cls, fields) in checks.items():
+        assert int(out[st]) == C.sizeof(cls), st
+        for f in fields:
+            assert int(out[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)

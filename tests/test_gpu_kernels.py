@@ -101,6 +101,36 @@ def test_route_bit_exact(case):
     assert np.array_equal(host(g["row_route"]), r)
 
 
+@pytest.mark.parametrize("N,E,K,G,M_,renorm", [(2000, 256, 8, 8, 4, 0), (700, 64, 6, 16, 3, 1),
+                                               (333, 32, 8, 4, 2, 0), (129, 128, 4, 64, 8, 0),
+                                               (50, 16, 4, 2, 1, 1)])
+def test_route_grouped_bit_exact(N, E, K, G, M_, renorm):
+    """Group-limited top-K through moe_route against the oracle.  Group scores
+    are sums of fp32 probabilities on the GPU and fp64 ones in the oracle, so a
+    token may differ only where the oracle's kept/dropped group boundary is a
+    near-tie; every other token, and the whole route map of identical
+    selections, is compared bit for bit."""
+    print(f"route grouped N={N} E={E} K={K} G={G} M={M_}", flush=True)
+    L = _logits(N, E, "zipf", N + E + G)
+    g = M.route(dev(L), K, renorm=renorm, n_group=G, topk_group=M_)
+    _sync()
+    idx = O.topk_select_grouped(L, K, G, M_)
+    got = host(g["topk_idx"])
+    diff = np.any(got != idx, axis=1)
+    if np.any(diff):
+        sc = -np.sort(-O.group_scores(L[diff], G), axis=1)
+        gap = sc[:, M_ - 1] - sc[:, M_]
+        assert np.all(gap <= 1e-5 * sc[:, 0]), "selection differs away from a group-score tie"
+    assert diff.mean() < 0.01
+    keep = ~diff
+    prob = O.route_probs(L, idx, renorm)
+    assert np.max(np.abs(host(g["topk_prob"])[keep].astype(np.float64) - prob[keep]), initial=0.0) <= 1e-6
+    if not np.any(diff):
+        c, o, d, r = O.route_map(idx, None, E, 1, N * K)
+        for k, ref in (("counts", c), ("offsets", o), ("dst_rows", d), ("row_route", r)):
+            assert np.array_equal(host(g[k]), ref), k
+
+
 # -------------------------------------------------------------- dispatch ----
 def _routed(N, D, E, K, align, seed, pdrop=0.0):
     wl = S.scaled(S.WORKLOADS["dsv3_bf16"], N=N, D=D, E=E, K=K, H=32, p_drop=pdrop,
