@@ -210,7 +210,7 @@ def route_valid(idx, drop, E: int) -> np.ndarray:
     return v
 
 
-def route_map(idx, drop, E: int, align: int, rows_cap: int):
+def route_map(idx, drop, E: int, align: int, rows_cap: int, n_shared: int = 0):
     """Stable counting sort of the valid routes into expert-contiguous rows.
 
     Route id r = t*K + k.  counts[e] = number of valid routes to e;
@@ -221,6 +221,9 @@ def route_map(idx, drop, E: int, align: int, rows_cap: int):
     -1 for padding and unused rows.
     Returns (counts int32 [E], offsets int32 [E+1], dst_rows int32 [N,K],
     row_route int32 [rows_cap]).
+    n_shared = 1 appends the shared expert's segment: all N tokens, in token
+    order, at offsets[E] (counts gets N, offsets a last entry; its rows hold
+    no route, row_route -1).
     """
     idx = np.asarray(idx)
     N, K = idx.shape
@@ -242,6 +245,11 @@ def route_map(idx, drop, E: int, align: int, rows_cap: int):
     dst_rows[order] = dst
     row_route = np.full(rows_cap, -1, dtype=np.int64)
     row_route[dst] = order
+    if n_shared:
+        counts = np.append(counts, N)
+        offsets = np.append(offsets, offsets[E] + N)
+        if offsets[-1] > rows_cap:
+            raise ValueError("rows_cap too small")
     return (counts.astype(np.int32), offsets.astype(np.int32),
             dst_rows.reshape(N, K).astype(np.int32), row_route.astype(np.int32))
 
@@ -272,16 +280,17 @@ def dispatch(x, row_route, K: int, weight=None, exact: bool = False) -> np.ndarr
     return out
 
 
-def combine(y, dst_rows, weight=None, exact: bool = False) -> np.ndarray:
+def combine(y, dst_rows, weight=None, exact: bool = False, addend=None) -> np.ndarray:
     """out[t] = sum over valid k of w[t,k] * Y[dst_rows[t,k]], stored once as bf16.
 
     Invalid routes (dst_rows < 0) contribute nothing; ``weight`` None means 1.
-    The sum is exact (float64) and rounded once.
+    ``addend`` [N, D] (a shared expert's rows, say) joins the sum.  The sum is
+    exact (float64) and rounded once.
     """
     yv = values(y)
     dst = np.asarray(dst_rows, dtype=np.int64)
     N, K = dst.shape
-    acc = np.zeros((N, yv.shape[1]), dtype=np.float64)
+    acc = np.zeros((N, yv.shape[1]), dtype=np.float64) if addend is None else np.array(values(addend), np.float64)
     for k in range(K):
         ok = dst[:, k] >= 0
         w = np.ones(N) if weight is None else np.asarray(weight, np.float64)[:, k]
@@ -314,9 +323,10 @@ def dprob(dout, y, dst_rows) -> np.ndarray:
     return g.astype(np.float32)
 
 
-def dispatch_bwd(dxd, dst_rows, exact: bool = False) -> np.ndarray:
-    """Adjoint of dispatch: dx[t] = sum over valid k of dX_d[dst_rows[t,k]]."""
-    return combine(dxd, dst_rows, None, exact=exact)
+def dispatch_bwd(dxd, dst_rows, exact: bool = False, addend=None) -> np.ndarray:
+    """Adjoint of dispatch: dx[t] = sum over valid k of dX_d[dst_rows[t,k]]
+    (plus ``addend``, e.g. the shared expert's dX_d rows, in the same sum)."""
+    return combine(dxd, dst_rows, None, exact=exact, addend=addend)
 
 
 # --------------------------------------------------------------------------
@@ -429,26 +439,33 @@ def grouped_wgrad(dc, a, offsets, exact: bool = False):
 
 
 def layer_fwd(x, w_r, bias, w_gate, w_up, w_down, K: int, drop=None, renorm: int = 0,
-              align: int = 1, rows_cap: int = None, logits=None, exact: bool = False):
+              align: int = 1, rows_cap: int = None, logits=None, exact: bool = False, n_shared: int = 0):
     """Router -> top-K -> route map -> dispatch -> experts -> weighted combine.
 
     ``logits`` may be given to skip the router product (route-map tests).
+    n_shared = 1: a shared expert (the last of the expert weights, after the E
+    routed ones) sees every token and adds its output with weight 1 [KOSMOS
+    Appendix A, Table A.1: the shared expert in the MoE launch]; it is expert
+    E over a segment that holds x itself.
     Returns a dict with every saved tensor and ``out``.
     """
     xv = values(x)
     N = xv.shape[0]
     E = np.asarray(w_r).shape[0]
     if rows_cap is None:
-        rows_cap = N * K + E * (align - 1)
+        rows_cap = N * K + E * (align - 1) + n_shared * N
     L = router_logits(x, w_r, bias) if logits is None else np.asarray(logits, np.float32)
     idx = topk_select(L, K)
     prob = route_probs(L, idx, renorm)
-    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap)
+    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap, n_shared)
     xd = dispatch(xv, row_route, K)
+    if n_shared:
+        xd[offsets[E]:offsets[E] + N] = xv
     G, U, Hh, Y = experts_fwd(xd, offsets, w_gate, w_up, w_down, exact)
-    out = combine(Y, dst_rows, prob, exact)
+    out = combine(Y, dst_rows, prob, exact, addend=Y[offsets[E]:offsets[E] + N] if n_shared else None)
     return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
-                dst_rows=dst_rows, row_route=row_route, xd=xd, g=G, u=U, h=Hh, y=Y, out=out)
+                dst_rows=dst_rows, row_route=row_route, xd=xd, g=G, u=U, h=Hh, y=Y, out=out,
+                n_shared=n_shared)
 
 
 def layer_fwd_tokens(fwd_route: dict, x, w_gate, w_up, w_down, tokens, K: int, exact=False):
@@ -521,10 +538,15 @@ def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
     route-weight gradient, expert backward, dispatch-bwd (sum of the K rows)."""
     rows_cap = fwd["xd"].shape[0]
     dyd = combine_bwd(dout, fwd["dst_rows"], fwd["topk_prob"], rows_cap, exact)
+    shared = None
+    if fwd.get("n_shared"):
+        o = fwd["offsets"]
+        shared = slice(int(o[-2]), int(o[-1]))
+        dyd[shared] = values(dout)           # the shared expert's weight is 1
     dp = dprob(dout, fwd["y"], fwd["dst_rows"])
     eb = experts_bwd(dyd, fwd["xd"], fwd["g"], fwd["u"], fwd["h"], fwd["offsets"],
                      w_gate, w_up, w_down, exact)
-    dx = dispatch_bwd(eb["dxd"], fwd["dst_rows"], exact)
+    dx = dispatch_bwd(eb["dxd"], fwd["dst_rows"], exact, addend=eb["dxd"][shared] if shared else None)
     eb.update(dyd=dyd, dprob=dp, dx=dx)
     return eb
 

@@ -219,3 +219,58 @@ def test_grouped_products_are_the_layer_parts():
     lhs = np.sum(O.grouped_gemm(A, W, o, exact=True) * Z)
     assert np.isclose(lhs, np.sum(A * O.grouped_dgrad(Z, W, o, exact=True)), rtol=1e-12)
     assert np.isclose(lhs, np.sum(W * O.grouped_wgrad(Z, A, o, exact=True)), rtol=1e-12)
+
+
+# ------------------------------------------------------------ shared expert ----
+def _shared_case(seed=12):
+    wl = _small(N=24, D=32, E=4, K=2, H=32, bwd=True)
+    inp = S.make_inputs(wl, seed)
+    rng = np.random.default_rng(seed)
+    extra = lambda a: np.concatenate([O.bits_to_f64(a), rng.standard_normal((1,) + a.shape[1:]) * 0.1])
+    return wl, inp, extra(inp.w_gate), extra(inp.w_up), extra(inp.w_down)
+
+
+def test_shared_expert_with_zero_down_weights_changes_nothing():
+    wl, inp, wg, wu, wd = _shared_case()
+    wd[-1] = 0.0
+    a = O.layer_fwd(inp.x, inp.w_r, inp.bias, wg[:-1], wu[:-1], wd[:-1], wl.K)
+    b = O.layer_fwd(inp.x, inp.w_r, inp.bias, wg, wu, wd, wl.K, n_shared=1)
+    assert np.array_equal(a["out"], b["out"])
+    assert int(b["counts"][-1]) == wl.N and int(b["offsets"][-1] - b["offsets"][-2]) == wl.N
+
+
+def test_shared_expert_adds_a_dense_swiglu_mlp():
+    """Exact mode: the layer with a shared expert minus the layer without it is
+    the dense SwiGLU MLP of the shared weights on every token (torch)."""
+    wl, inp, wg, wu, wd = _shared_case(13)
+    a = O.layer_fwd(inp.x, inp.w_r, inp.bias, wg[:-1], wu[:-1], wd[:-1], wl.K, exact=True)
+    b = O.layer_fwd(inp.x, inp.w_r, inp.bias, wg, wu, wd, wl.K, exact=True, n_shared=1)
+    x = torch.tensor(O.bits_to_f64(inp.x))
+    mlp = (F.silu(x @ torch.tensor(wg[-1]).T) * (x @ torch.tensor(wu[-1]).T)) @ torch.tensor(wd[-1]).T
+    assert np.allclose(b["out"] - a["out"], mlp.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_with_shared_expert_matches_finite_differences():
+    wl, inp, wg, wu, wd = _shared_case(14)
+    x = O.bits_to_f64(inp.x)
+    L = O.router_logits(inp.x, inp.w_r, inp.bias)     # routing fixed
+    dout = O.bits_to_f64(inp.dout)
+
+    def fwd(x, wg, wu, wd):
+        return O.layer_fwd(x, inp.w_r, None, wg, wu, wd, wl.K, logits=L, exact=True, n_shared=1)
+
+    def loss(*a):
+        return float(np.sum(fwd(*a)["out"] * dout))
+
+    base = (x, wg, wu, wd)
+    g = O.layer_bwd(fwd(*base), dout, wg, wu, wd, exact=True)
+    rng = np.random.default_rng(3)
+    eps = 1e-6
+    for i, gr in enumerate((g["dx"], g["dw_gate"], g["dw_up"], g["dw_down"])):
+        v = rng.standard_normal(base[i].shape)
+        plus, minus = list(base), list(base)
+        plus[i] = base[i] + eps * v
+        minus[i] = base[i] - eps * v
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = float(np.sum(gr * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (i, fd, an)
