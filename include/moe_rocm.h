@@ -85,10 +85,21 @@ typedef struct moe_dims {
    * topk_group * E / n_group >= K).  0 or 1: plain top-K. */
   int32_t n_group;
   int32_t topk_group;
+  /* Shared expert (KOSMOS Appendix A, Table A.1: in the same launch as the
+   * routed experts), 0 or 1.  In the layer calls the expert weights then hold
+   * E + 1 experts, the shared one last; it sees every token with weight 1.
+   * moe_route appends counts[E] = N and offsets[E+1] (its segment, N rows
+   * rounded up to align, after the routed ones; so counts/offsets hold E + 1 /
+   * E + 2 entries), and rows_cap grows by N + align - 1.  moe_dispatch,
+   * moe_combine and moe_combine_bwd reject it (MOE_ERR_UNSUPPORTED), as does
+   * the MOE_SCHED_READY forward. */
+  int32_t n_shared;
+  int32_t reserved;     /* 0 */
 } moe_dims;
 
-/* Rows of every expert-contiguous buffer: N*K + E*(align-1).  No routing can
- * need more, so these buffers never overflow. */
+/* Rows of every expert-contiguous buffer: N*K + E*(align-1), plus
+ * N + align - 1 with a shared expert.  No routing can need more, so these
+ * buffers never overflow. */
 int64_t moe_rows_cap(const moe_dims* d);
 
 /* Bytes of workspace an operation needs (0 if none).  For MOE_OP_GEMM only

@@ -32,7 +32,8 @@ _i32 = C.c_int32
 
 class Dims(C.Structure):
     _fields_ = [("N", _i64), ("D", _i64), ("E", _i64), ("K", _i64), ("H", _i64),
-                ("align", _i32), ("renorm", _i32), ("n_group", _i32), ("topk_group", _i32)]
+                ("align", _i32), ("renorm", _i32), ("n_group", _i32), ("topk_group", _i32),
+                ("n_shared", _i32), ("reserved", _i32)]
 
 
 class GemmFwdArgs(C.Structure):
@@ -131,8 +132,9 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
-def dims(N, D, E, K, H=0, align=1, renorm=0, n_group=0, topk_group=0) -> Dims:
-    return Dims(int(N), int(D), int(E), int(K), int(H), int(align), int(renorm), int(n_group), int(topk_group))
+def dims(N, D, E, K, H=0, align=1, renorm=0, n_group=0, topk_group=0, n_shared=0) -> Dims:
+    return Dims(int(N), int(D), int(E), int(K), int(H), int(align), int(renorm), int(n_group), int(topk_group),
+                int(n_shared), 0)
 
 
 def rows_cap(d: Dims) -> int:
@@ -347,11 +349,13 @@ def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_ST
                 aux_alpha=0.0):
     N, D = x.shape
     E = wts.w_r.shape[0]
-    if mxfp8:
-        H = wts.wq["wg_q"].shape[1]
-    else:
-        H = wts.w_gate.shape[1]
-    d = dims(N, D, E, K, H, align=32 if mxfp8 else 1, renorm=renorm, n_group=n_group, topk_group=topk_group)
+    wg = wts.wq["wg_q"] if mxfp8 else wts.w_gate
+    H = wg.shape[1]
+    n_shared = wg.shape[0] - E          # expert weights beyond the routed ones: the shared expert
+    if n_shared not in (0, 1):
+        raise ValueError("expert weights must hold E or E + 1 experts")
+    d = dims(N, D, E, K, H, align=32 if mxfp8 else 1, renorm=renorm, n_group=n_group, topk_group=topk_group,
+             n_shared=n_shared)
     q = wts.wq or {}
     a = LayerArgs(d, MOE_MXFP8 if mxfp8 else MOE_BF16, sched, _ptr(x), _ptr(wts.w_r), _ptr(wts.bias),
                   _ptr(drop), _ptr(wts.w_gate), _ptr(wts.w_up), _ptr(wts.w_down),
@@ -369,8 +373,8 @@ def alloc_saved(d: Dims, mxfp8: bool, device):
     sv = dict(logits=torch.empty((N, E), dtype=torch.float32, device=device),
               topk_idx=torch.empty((N, K), dtype=torch.int32, device=device),
               topk_prob=torch.empty((N, K), dtype=torch.float32, device=device),
-              counts=torch.empty(E, dtype=torch.int32, device=device),
-              offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+              counts=torch.empty(E + d.n_shared, dtype=torch.int32, device=device),
+              offsets=torch.empty(E + d.n_shared + 1, dtype=torch.int32, device=device),
               dst_rows=torch.empty((N, K), dtype=torch.int32, device=device),
               row_route=torch.empty(rc, dtype=torch.int32, device=device),
               g=bf(rc, H), u=bf(rc, H), h=bf(rc, H), y=bf(rc, D))
@@ -410,7 +414,7 @@ class MoeLayer:
         self.ws_f = workspace(MOE_OP_LAYER_FWD, self.d, device)
         self.grads = None
         if with_bwd:
-            E, H = self.d.E, self.d.H
+            E, H = self.d.E + self.d.n_shared, self.d.H
             self.ws_b = workspace(MOE_OP_LAYER_BWD, self.d, device)
             self.grads = dict(dx=torch.empty((N, D), dtype=torch.bfloat16, device=device),
                               dprob=torch.empty((N, K), dtype=torch.float32, device=device),
@@ -419,9 +423,10 @@ class MoeLayer:
                               dw_down=torch.empty((E, D, H), dtype=torch.bfloat16, device=device))
             if router_bwd:
                 # router gradients too; dx then includes dlogits . W_r
-                self.grads.update(dw_r=torch.empty((E, D), dtype=torch.bfloat16, device=device),
-                                  db_r=torch.empty((E,), dtype=torch.float32, device=device),
-                                  dlogits=torch.empty((N, E), dtype=torch.float32, device=device))
+                Er = self.d.E
+                self.grads.update(dw_r=torch.empty((Er, D), dtype=torch.bfloat16, device=device),
+                                  db_r=torch.empty((Er,), dtype=torch.float32, device=device),
+                                  dlogits=torch.empty((N, Er), dtype=torch.float32, device=device))
             self._gr = LayerGrads(**{n: _ptr(self.grads.get(n)) for n, t in LayerGrads._fields_ if t is _vp})
 
     def forward(self, x):

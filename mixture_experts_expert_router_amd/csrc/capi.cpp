@@ -25,7 +25,12 @@ int hip_status(hipError_t e) {
   return MOE_ERR_HIP;
 }
 
-int64_t rows_cap_of(const moe_dims& d) { return d.N * d.K + d.E * (int64_t)(d.align - 1); }
+// routed rows, each expert's alignment padding, and the shared expert's segment
+int64_t rows_cap_of(const moe_dims& d) {
+  return d.N * d.K + d.E * (int64_t)(d.align - 1) + (int64_t)d.n_shared * (d.N + d.align - 1);
+}
+// experts of the grouped GEMMs: the routed ones and the shared one
+int64_t experts_of(const moe_dims& d) { return d.E + d.n_shared; }
 
 // shape rules shared by every entry point
 int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
@@ -37,7 +42,7 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
   if (d->align != 1 && d->align != 32) return MOE_ERR_SHAPE;
   if (mxfp8 && (d->D % 32 || (need_h && d->H % 32) || d->align != 32)) return MOE_ERR_SHAPE;
   if (d->N * d->K >= (int64_t(1) << 31) || rows_cap_of(*d) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
-  if (d->n_group < 0) return MOE_ERR_SHAPE;
+  if (d->n_group < 0 || d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_SHAPE;
   if (d->n_group > 1 && (d->n_group > 64 || d->E % d->n_group || d->topk_group < 1 ||
                          d->topk_group > d->n_group || d->topk_group * (d->E / d->n_group) < d->K))
     return MOE_ERR_SHAPE;
@@ -141,10 +146,10 @@ size_t moe_workspace_size(int op, const moe_dims* d) {
   const int64_t rc = rows_cap_of(*d);
   switch (op) {
     case MOE_OP_ROUTE: return route_bytes(*d);
-    case MOE_OP_GEMM: return table_bytes(rc, d->E);
+    case MOE_OP_GEMM: return table_bytes(rc, experts_of(*d));
     case MOE_OP_ROUTER: return router_bytes(*d);
-    case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, d->E) + router_bytes(*d);
-    case MOE_OP_LAYER_BWD: return table_bytes(rc, d->E) + bwd_scratch_bytes(*d);
+    case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, experts_of(*d)) + router_bytes(*d);
+    case MOE_OP_LAYER_BWD: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d);
     default: return 0;
   }
 }
@@ -198,7 +203,7 @@ int moe_route(const float* logits, const uint8_t* drop, const moe_dims* d, int32
   return hip_status(moe::launch_route(logits, drop, d->N, d->E, d->K, d->renorm, d->align,
                                       rows_cap_of(*d), topk_idx, topk_prob, counts, offsets,
                                       dst_rows, row_route, ws, (hipStream_t)stream, d->n_group,
-                                      d->topk_group));
+                                      d->topk_group, false, d->n_shared));
 }
 
 int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, const int32_t* counts,
@@ -207,6 +212,7 @@ int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, co
   if (out_dtype != MOE_BF16 && out_dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   const bool mx = out_dtype == MOE_MXFP8;
   int st = check_dims(d, false, mx);
+  if (!st && d->n_shared) return MOE_ERR_UNSUPPORTED;   // the shared expert is a layer-level option
   if (st) return st;
   REQUIRE_UNLESS(d->N == 0, x);
   REQUIRE_UNLESS(d->N == 0, dst_rows);
@@ -235,6 +241,7 @@ int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, co
 int moe_combine(const void* y, const int32_t* dst_rows, const float* weight, const moe_dims* d,
                 void* out, void* stream) {
   int st = check_dims(d, false, false);
+  if (!st && d->n_shared) return MOE_ERR_UNSUPPORTED;   // the shared expert is a layer-level option
   if (st) return st;
   REQUIRE_UNLESS(d->N == 0, y);
   REQUIRE_UNLESS(d->N == 0, dst_rows);
@@ -246,6 +253,7 @@ int moe_combine(const void* y, const int32_t* dst_rows, const float* weight, con
 int moe_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight, const void* y,
                     const moe_dims* d, void* dyd, float* dprob, void* stream) {
   int st = check_dims(d, false, false);
+  if (!st && d->n_shared) return MOE_ERR_UNSUPPORTED;   // the shared expert is a layer-level option
   if (st) return st;
   const bool no_tok = d->N == 0;
   REQUIRE_UNLESS(no_tok, dout);
@@ -377,6 +385,7 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (!a || !sv) return MOE_ERR_NULL;
   if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY) return MOE_ERR_DTYPE;
+  if (a->sched == MOE_SCHED_READY && a->dims.n_shared) return MOE_ERR_UNSUPPORTED;
   const bool mx = a->dtype == MOE_MXFP8;
   const moe_dims& d = a->dims;
   int st = check_dims(&d, true, mx);
@@ -418,7 +427,9 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   OPTIONAL(sv->aux);
   const bool aux = sv->aux != nullptr && a->aux_alpha != 0.0f;
   const int64_t rc = rows_cap_of(d);
-  const size_t rb = route_bytes(d), tb = table_bytes(rc, d.E);
+  const int64_t Ex = experts_of(d);
+  const int32_t* shared_row0 = d.n_shared ? sv->offsets + d.E : nullptr;   // the shared expert's segment
+  const size_t rb = route_bytes(d), tb = table_bytes(rc, Ex);
   if (ws_bytes < rb + tb + router_bytes(d)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   void* ws_route = ws;
@@ -429,16 +440,16 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (e == hipSuccess)
     e = moe::launch_route(sv->logits, a->drop, d.N, d.E, d.K, d.renorm, d.align, rc, sv->topk_idx,
                           sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,
-                          ws_route, s, d.n_group, d.topk_group, aux);
+                          ws_route, s, d.n_group, d.topk_group, aux, d.n_shared);
   if (e == hipSuccess && aux) e = moe::launch_aux_loss(ws_route, d.N, d.E, d.K, sv->counts, a->aux_alpha, sv->aux, s);
   if (mx) {
-    if (e == hipSuccess) e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s);
+    if (e == hipSuccess) e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s, shared_row0);
     if (e == hipSuccess)
-      e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D, sv->xd_q, d.D / 32, sv->xd_s, s);
-    moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
+      e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D, sv->xd_q, d.D / 32, sv->xd_s, s);
+    moe::GemmFwd g1{Ex, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
                     a->wu_s, sv->g, sv->u, sv->h, sv->h_q, sv->h_s, true};
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g1, table, s);
-    moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
+    moe::GemmFwd g2{Ex, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g2, table, s);
   } else if (a->sched == MOE_SCHED_READY && d.align == 1 && moe::gemm_fwd_fast_ok(d.D, d.H) &&
@@ -448,17 +459,19 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                        a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y};
     if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
   } else {
-    if (e == hipSuccess) e = moe::launch_dispatch_bf16(a->x, sv->dst_rows, nullptr, d.N, d.D, d.K, sv->xd, s);
+    if (e == hipSuccess)
+      e = moe::launch_dispatch_bf16(a->x, sv->dst_rows, nullptr, d.N, d.D, d.K, sv->xd, s, shared_row0);
     if (e == hipSuccess && d.align > 1)
-      e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, sv->xd, 0, nullptr, s);
-    moe::GemmFwd g1{d.E, rc, d.D, d.H, sv->offsets, sv->xd, nullptr, a->w_gate, nullptr, a->w_up,
+      e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, sv->xd, 0, nullptr, s);
+    moe::GemmFwd g1{Ex, rc, d.D, d.H, sv->offsets, sv->xd, nullptr, a->w_gate, nullptr, a->w_up,
                     nullptr, sv->g, sv->u, sv->h, nullptr, nullptr, true};
     if (e == hipSuccess) e = gemm_fwd_bf16(g1, table, s);
-    moe::GemmFwd g2{d.E, rc, d.H, d.D, sv->offsets, sv->h, nullptr, a->w_down, nullptr, nullptr,
+    moe::GemmFwd g2{Ex, rc, d.H, d.D, sv->offsets, sv->h, nullptr, a->w_down, nullptr, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
     if (e == hipSuccess) e = gemm_fwd_bf16(g2, table, s);
   }
-  if (e == hipSuccess) e = moe::launch_combine(sv->y, sv->dst_rows, sv->topk_prob, d.N, d.D, d.K, out, s);
+  if (e == hipSuccess)
+    e = moe::launch_combine(sv->y, sv->dst_rows, sv->topk_prob, d.N, d.D, d.K, out, s, nullptr, shared_row0);
   return hip_status(e);
 }
 
@@ -499,7 +512,9 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     if (d.E % 8) return MOE_ERR_SHAPE;   // the router's GEMMs read dlogits rows in 16-byte chunks
   }
   const int64_t rc = rows_cap_of(d);
-  const size_t tb = table_bytes(rc, d.E);
+  const int64_t Ex = experts_of(d);
+  const int32_t* shared_row0 = d.n_shared ? sv->offsets + d.E : nullptr;   // the shared expert's segment
+  const size_t tb = table_bytes(rc, Ex);
   if (ws_bytes < tb + bwd_scratch_bytes(d)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* p = (char*)ws;
@@ -518,17 +533,17 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   const void* h = sv->h ? sv->h : (const void*)p;
 
   hipError_t e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd,
-                                         gr->dprob, s);
+                                         gr->dprob, s, shared_row0);
   if (e == hipSuccess && !sv->h) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, (void*)h, nullptr, nullptr, s);
   if (e == hipSuccess && d.align > 1)
-    e = moe::launch_zero_padding(sv->counts, sv->offsets, d.E, d.D * 2, dyd, 0, nullptr, s);
+    e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
   // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
-  moe::GemmBwd down{d.E, rc, d.H, d.D, sv->offsets, h, a->w_down, nullptr, dyd, nullptr, nullptr,
+  moe::GemmBwd down{Ex, rc, d.H, d.D, sv->offsets, h, a->w_down, nullptr, dyd, nullptr, nullptr,
                     sv->g, sv->u, dg, du, true};
   if (e == hipSuccess) e = gemm_dgrad(down, table, s);
   if (e == hipSuccess) e = gemm_wgrad(down, dyd, gr->dw_down, table, s);
   // gate/up: forward g = xd . w_gate^T, u = xd . w_up^T  (k_dim = D, n_dim = H)
-  moe::GemmBwd gu{d.E, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
+  moe::GemmBwd gu{Ex, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
                   nullptr, nullptr, nullptr, nullptr, false};
   if (e == hipSuccess) e = gemm_dgrad(gu, table, s);
   if (e == hipSuccess) e = gemm_wgrad(gu, dg, gr->dw_gate, table, s);
@@ -566,7 +581,8 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
       e = moe::launch_router_bwd_reduce(split ? part : nullptr, l.S, d.E * d.D, (uint16_t*)gr->dw_r, colpart,
                                         (d.N + 63) / 64, d.E, gr->db_r, s);
   }
-  if (e == hipSuccess) e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s, dxr);
+  if (e == hipSuccess)
+    e = moe::launch_combine(dxd, sv->dst_rows, nullptr, d.N, d.D, d.K, gr->dx, s, dxr, shared_row0);
   return hip_status(e);
 }
 

@@ -65,7 +65,7 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
                         void* ws, hipStream_t s,
-                        int n_group = 0, int topk_group = 0, bool aux_inputs = false);
+                        int n_group = 0, int topk_group = 0, bool aux_inputs = false, int n_shared = 0);
 // aux loss of the routed layer from the route step's probability sums (left
 // in the route workspace by launch_route with aux_inputs) and the counts
 hipError_t launch_aux_loss(void* route_ws, int64_t N, int64_t E, int64_t K, const int32_t* counts, float alpha,
@@ -73,18 +73,22 @@ hipError_t launch_aux_loss(void* route_ws, int64_t N, int64_t E, int64_t K, cons
 
 // permute.hip
 hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,
-                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s);
+                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s,
+                         const int32_t* shared_row0 = nullptr);
 hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
-                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s);
+                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s,
+                         const int32_t* shared_row0 = nullptr);
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
                                hipStream_t s);
 // addend (bf16 [N][D], optional) is added to each token's fp32 sum before rounding
 hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
-                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend = nullptr);
+                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend = nullptr,
+                          const int32_t* shared_row0 = nullptr);
 hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
                               const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
-                              float* dprob, hipStream_t s);
+                              float* dprob, hipStream_t s,
+                         const int32_t* shared_row0 = nullptr);
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
                                 uint8_t* sc, hipStream_t s);
 hipError_t launch_swiglu(const void* g, const void* u, int64_t rows, int64_t n, void* h,

@@ -29,16 +29,22 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ dst_rows,
                                                             const float* __restrict__ weight,
                                                             int N, int D, int K,
-                                                            uint16_t* __restrict__ xd) {
+                                                            uint16_t* __restrict__ xd,
+                                                            const int32_t* __restrict__ shared_row0) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;
-  int dst[32];
-  float w[32];
+  int dst[33];
+  float w[33];
   for (int k = 0; k < K; ++k) {
     dst[k] = dst_rows[(int64_t)t * K + k];
     w[k] = WEIGHTED ? weight[(int64_t)t * K + k] : 1.0f;
   }
+  if (shared_row0) {              // the shared expert's row of this token, weight 1
+    dst[K] = *shared_row0 + t;
+    w[K] = 1.0f;
+  }
+  const int KK = K + (shared_row0 ? 1 : 0);
   const int nvec = D >> 3;
   const uint16_t* src = x + (int64_t)t * D;
   for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
@@ -48,13 +54,13 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
       const int v = v0 + lane + j * kWave;
       if (v < nvec) r[j] = ldg16(src + v * 8);
     }
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KK; ++k) {
       if (dst[k] < 0) continue;
       uint16_t* out = xd + (int64_t)dst[k] * D;
 #pragma unroll
       for (int j = 0; j < kVPL; ++j) {
         const int v = v0 + lane + j * kWave;
-        if (v < nvec) stg16(out + v * 8, WEIGHTED ? scale_bf16x8(r[j], w[k]) : r[j]);
+        if (v < nvec) stg16(out + v * 8, (WEIGHTED && k < K) ? scale_bf16x8(r[j], w[k]) : r[j]);
       }
     }
   }
@@ -83,12 +89,15 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ dst_rows,
                                                              int N, int D, int K,
                                                              uint8_t* __restrict__ q,
-                                                             uint8_t* __restrict__ sc) {
+                                                             uint8_t* __restrict__ sc,
+                                                             const int32_t* __restrict__ shared_row0) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;
-  int dst[32];
+  int dst[33];
   for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
+  if (shared_row0) dst[K] = *shared_row0 + t;   // the shared expert's row of this token
+  const int KK = K + (shared_row0 ? 1 : 0);
   const int nvec = D >> 3;
   const uint16_t* src = x + (int64_t)t * D;
   for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
       if (v < nvec) r = ldg16(src + v * 8);
       qv[j] = quant_vec(r, code[j]);     // all lanes take part in the shuffles
     }
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KK; ++k) {
       if (dst[k] < 0) continue;
 #pragma unroll
       for (int j = 0; j < kVPL; ++j) {
@@ -126,13 +135,16 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
                                                                     const int32_t* __restrict__ dst_rows,
                                                                     int N, int D, int K,
                                                                     uint8_t* __restrict__ q,
-                                                                    uint8_t* __restrict__ sc) {
+                                                                    uint8_t* __restrict__ sc,
+                                                             const int32_t* __restrict__ shared_row0) {
   constexpr int PP = 2;   // lane pairs of vectors per pass
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[32];
+  int dst[33];
   for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
+  if (shared_row0) dst[K] = *shared_row0 + t;   // the shared expert's row of this token
+  const int KK = K + (shared_row0 ? 1 : 0);
   const int npair = D >> 4;              // 16-element pieces per row
   const int nblk = D >> 5;
   const uint16_t* src = x + (int64_t)t * D;
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
                      c3 = (uint32_t)__shfl_down(code, 6, 64);
       packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KK; ++k) {
       if (dst[k] < 0) continue;
       uint8_t* qrow = q + (int64_t)dst[k] * D;
       uint8_t* srow = sc + (int64_t)dst[k] * nblk;
@@ -205,12 +217,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ dst_rows,
                                                       const float* __restrict__ weight, int N,
                                                       int D, int K, uint16_t* __restrict__ out,
-                                                      const uint16_t* __restrict__ addend) {
+                                                      const uint16_t* __restrict__ addend,
+                                                      const int32_t* __restrict__ shared_row0) {
   constexpr int VPL = 2, KCH = 8;
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
   const int nvec = D >> 3;
+  // route K (when there is a shared expert): its row of this token, weight 1
+  const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
   for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
     float acc[VPL][8];
 #pragma unroll
@@ -226,14 +242,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       acc[j][6] = bf16lo(q.w);
       acc[j][7] = bf16hi(q.w);
     }
-    for (int kb = 0; kb < K; kb += KCH) {
+    for (int kb = 0; kb < KK; kb += KCH) {
       uint4 r[KCH][VPL];
       int dk[KCH];
       float wk[KCH];
 #pragma unroll
       for (int kk = 0; kk < KCH; ++kk) {
         const int k = kb + kk;
-        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : -1;
+        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
         wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
         const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
 #pragma unroll
@@ -277,7 +293,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
                                                           const float* __restrict__ weight,
                                                           const uint16_t* __restrict__ y, int N,
                                                           int D, int K, uint16_t* __restrict__ dyd,
-                                                          float* __restrict__ dprob) {
+                                                          float* __restrict__ dprob,
+                                                          const int32_t* __restrict__ shared_row0) {
   // routes in chunks of KCH: every Y row of the chunk is loaded before any
   // product uses it, so the gathers overlap instead of waiting one by one;
   // each lane still sums its vectors in increasing order
@@ -287,14 +304,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   if (t >= N) return;
   const int nvec = D >> 3;
   const uint16_t* src = dout + (int64_t)t * D;
-  for (int kb = 0; kb < K; kb += KCH) {
+  // route K (when there is a shared expert): dY of its row is dOut, weight 1,
+  // and it has no route weight to differentiate
+  const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
+  for (int kb = 0; kb < KK; kb += KCH) {
     int dk[KCH];
     float wk[KCH], dot[KCH];
 #pragma unroll
     for (int kk = 0; kk < KCH; ++kk) {
       const int k = kb + kk;
-      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : -1;
-      wk[kk] = k < K ? weight[(int64_t)t * K + k] : 0.0f;
+      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
+      wk[kk] = k < K ? weight[(int64_t)t * K + k] : 1.0f;
       dot[kk] = 0.0f;
     }
     for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
@@ -311,7 +332,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
             const int v = v0 + lane + j * kWave;
-            yy[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16(y + (int64_t)dk[kk] * D + v * 8) : make_uint4(0, 0, 0, 0);
+            yy[kk][j] = (dk[kk] >= 0 && kb + kk < K && v < nvec) ? ldg16(y + (int64_t)dk[kk] * D + v * 8)
+                                                                  : make_uint4(0, 0, 0, 0);
           }
       }
 #pragma unroll
@@ -412,26 +434,27 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
 static inline unsigned waves_grid(int64_t rows) { return (unsigned)((rows + 3) / 4); }
 
 hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,
-                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s) {
+                                int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s,
+                                const int32_t* shared_row0) {
   if (N == 0) return hipSuccess;
   if (weight)
     dispatch_bf16_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, weight,
-                                                            (int)N, (int)D, (int)K, (uint16_t*)xd);
+                                                            (int)N, (int)D, (int)K, (uint16_t*)xd, shared_row0);
   else
     dispatch_bf16_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, nullptr,
-                                                             (int)N, (int)D, (int)K, (uint16_t*)xd);
+                                                             (int)N, (int)D, (int)K, (uint16_t*)xd, shared_row0);
   return hipGetLastError();
 }
 
 hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
-                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s) {
+                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s, const int32_t* shared_row0) {
   if (N == 0) return hipSuccess;
   if (D % 128 == 0 && ((uintptr_t)sc & 3) == 0)
     dispatch_mxfp8_packed_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
-                                                               (int)K, q, sc);
+                                                               (int)K, q, sc, shared_row0);
   else
     dispatch_mxfp8_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
-                                                        (int)K, q, sc);
+                                                        (int)K, q, sc, shared_row0);
   return hipGetLastError();
 }
 
@@ -445,25 +468,27 @@ hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, in
 }
 
 hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
-                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend) {
+                          int64_t D, int64_t K, void* out, hipStream_t s, const void* addend,
+                          const int32_t* shared_row0) {
   if (N == 0) return hipSuccess;
   if (weight)
     combine_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, weight, (int)N,
-                                                      (int)D, (int)K, (uint16_t*)out, (const uint16_t*)addend);
+                                                      (int)D, (int)K, (uint16_t*)out, (const uint16_t*)addend,
+                                                      shared_row0);
   else
     combine_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, nullptr,
                                                        (int)N, (int)D, (int)K, (uint16_t*)out,
-                                                       (const uint16_t*)addend);
+                                                       (const uint16_t*)addend, shared_row0);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
                               const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
-                              float* dprob, hipStream_t s) {
+                              float* dprob, hipStream_t s, const int32_t* shared_row0) {
   if (N == 0) return hipSuccess;
   combine_bwd_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)dout, dst_rows, weight,
                                                    (const uint16_t*)y, (int)N, (int)D, (int)K,
-                                                   (uint16_t*)dyd, dprob);
+                                                   (uint16_t*)dyd, dprob, shared_row0);
   return hipGetLastError();
 }
 

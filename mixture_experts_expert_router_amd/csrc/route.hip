@@ -212,10 +212,12 @@ __global__ __launch_bounds__(64) void aux_loss_kernel(const float* __restrict__ 
 
 // One workgroup of 1024 threads.  Thread (e, g) owns expert e and the chunk
 // range of group g; partial sums are scanned over groups, then over experts.
+// n_shared = 1: counts[E] = N and offsets[E+1] = offsets[E] + N rounded up to
+// align, the shared expert's segment of every token.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nchunks,
                                                           int E, int align,
                                                           int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets) {
+                                                          int32_t* __restrict__ offsets, int N, int n_shared) {
   __shared__ int s_part[1024];
   __shared__ int s_tot[kMaxE];
   __shared__ int s_off[kMaxE + 1];
@@ -276,6 +278,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
   __syncthreads();
   for (int ee = threadIdx.x; ee <= E; ee += blockDim.x) offsets[ee] = s_off[ee];
+  if (n_shared && threadIdx.x == 0) {
+    counts[E] = N;
+    offsets[E + 1] = s_off[E] + ((N + align - 1) / align) * align;
+  }
   if (e < E) {
     int run = s_off[e] + s_part[g * Ep + e];
     const int c1 = min(nchunks, (g + 1) * cpg);
@@ -341,7 +347,7 @@ hipError_t launch_aux_loss(void* ws, int64_t N, int64_t E, int64_t K, const int3
 hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int64_t E, int64_t K,
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
-                        void* ws, hipStream_t s, int n_group, int topk_group, bool aux_inputs) {
+                        void* ws, hipStream_t s, int n_group, int topk_group, bool aux_inputs, int n_shared) {
   const int64_t nchunks = (N + kChunk - 1) / kChunk;
   const int64_t nalloc = nchunks > 0 ? nchunks : 1;
   int32_t* hist = (int32_t*)ws;
@@ -361,7 +367,7 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
                                                     hist, rank, 0, 0, nullptr);
   }
   route_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(hist, (int)nchunks, (int)E, align, counts,
-                                                   offsets);
+                                                   offsets, (int)N, n_shared);
   const int64_t NK = N * K;
   if (NK > 0) {
     route_scatter_kernel<<<dim3((unsigned)((NK + 255) / 256)), dim3(256), 0, s>>>(

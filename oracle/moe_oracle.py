@@ -222,8 +222,8 @@ def route_map(idx, drop, E: int, align: int, rows_cap: int, n_shared: int = 0):
     Returns (counts int32 [E], offsets int32 [E+1], dst_rows int32 [N,K],
     row_route int32 [rows_cap]).
     n_shared = 1 appends the shared expert's segment: all N tokens, in token
-    order, at offsets[E] (counts gets N, offsets a last entry; its rows hold
-    no route, row_route -1).
+    order, at offsets[E], padded to ``align`` like every group (counts gets N,
+    offsets a last entry; its rows hold no route, row_route -1).
     """
     idx = np.asarray(idx)
     N, K = idx.shape
@@ -247,7 +247,7 @@ def route_map(idx, drop, E: int, align: int, rows_cap: int, n_shared: int = 0):
     row_route[dst] = order
     if n_shared:
         counts = np.append(counts, N)
-        offsets = np.append(offsets, offsets[E] + N)
+        offsets = np.append(offsets, offsets[E] + ((N + align - 1) // align) * align)
         if offsets[-1] > rows_cap:
             raise ValueError("rows_cap too small")
     return (counts.astype(np.int32), offsets.astype(np.int32),
@@ -453,7 +453,7 @@ def layer_fwd(x, w_r, bias, w_gate, w_up, w_down, K: int, drop=None, renorm: int
     N = xv.shape[0]
     E = np.asarray(w_r).shape[0]
     if rows_cap is None:
-        rows_cap = N * K + E * (align - 1) + n_shared * N
+        rows_cap = N * K + E * (align - 1) + n_shared * (N + align - 1)
     L = router_logits(x, w_r, bias) if logits is None else np.asarray(logits, np.float32)
     idx = topk_select(L, K)
     prob = route_probs(L, idx, renorm)
@@ -697,23 +697,26 @@ def expert_mlp_mxfp8(xq, xs, wgq, wgs, wuq, wus, wdq, wds):
     return G, U, Hh, hq, hs, Y
 
 
-def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, rows_cap=None):
+def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, rows_cap=None, n_shared: int = 0):
     """MXFP8 forward: same route as bf16, groups padded to ``align`` rows,
     quantize-on-dispatch, block-scaled expert GEMMs, bf16 weighted combine.
 
     wq: dict with pre-quantized weights wg_q [E,H,D], wg_s [E,H,D/32], wu_q,
-    wu_s, wd_q [E,D,H], wd_s [E,D,H/32].
+    wu_s, wd_q [E,D,H], wd_s [E,D,H/32] (one more expert, the shared one, with
+    n_shared = 1, whose segment holds every token's quantized row).
     """
     xv = values(x)
     N, D = xv.shape
     E = np.asarray(w_r).shape[0]
     if rows_cap is None:
-        rows_cap = N * K + E * (align - 1)
+        rows_cap = N * K + E * (align - 1) + n_shared * (N + align - 1)
     L = router_logits(x, w_r, bias)
     idx = topk_select(L, K)
     prob = route_probs(L, idx, renorm)
-    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap)
+    counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap, n_shared)
     xq, xs = dispatch_mxfp8(xv, row_route, K)
+    if n_shared:
+        xq[offsets[E]:offsets[E] + N], xs[offsets[E]:offsets[E] + N] = quantize_mxfp8(xv)
     Hd = wq["wg_q"].shape[1]
     G = np.zeros((rows_cap, Hd))
     U = np.zeros((rows_cap, Hd))
@@ -721,14 +724,14 @@ def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, row
     hq = np.zeros((rows_cap, Hd), np.uint8)
     hs = np.zeros((rows_cap, Hd // 32), np.uint8)
     Y = np.zeros((rows_cap, D))
-    for e in range(E):
+    for e in range(E + n_shared):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b == a:
             continue
         G[a:b], U[a:b], Hh[a:b], hq[a:b], hs[a:b], Y[a:b] = expert_mlp_mxfp8(
             xq[a:b], xs[a:b], wq["wg_q"][e], wq["wg_s"][e], wq["wu_q"][e], wq["wu_s"][e],
             wq["wd_q"][e], wq["wd_s"][e])
-    out = combine(Y, dst_rows, prob)
+    out = combine(Y, dst_rows, prob, addend=Y[offsets[E]:offsets[E] + N] if n_shared else None)
     return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
                 dst_rows=dst_rows, row_route=row_route, xq=xq, xs=xs, g=G, u=U, h=Hh,
                 hq=hq, hs=hs, y=Y, out=out)
