@@ -321,6 +321,23 @@ def device_inputs(M, inp, mxfp8, torch):
     return b(inp.x), w, drop
 
 
+def shared_expert_weights(M, w, wl, seed, torch):
+    """The workload's expert weights plus one shared expert, the last, drawn like
+    the others (N(0, 1/D) for gate/up, N(0, 1/H) for down)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7919)
+    D, H = wl.D, wl.H
+    ws = M.LayerWeights(w_r=w.w_r, bias=w.bias)
+    mk = lambda *shape, std: (torch.randn(shape, device="cuda", generator=g) * std).bfloat16()
+    sg, su, sd = mk(1, H, D, std=D ** -0.5), mk(1, H, D, std=D ** -0.5), mk(1, D, H, std=H ** -0.5)
+    if w.wq:
+        q = M.quantize_weights_mxfp8(sg, su, sd)
+        ws.wq = {k: torch.cat([w.wq[k], q[k]]) for k in w.wq}
+    else:
+        ws.w_gate, ws.w_up, ws.w_down = (torch.cat([a, b]) for a, b in ((w.w_gate, sg), (w.w_up, su), (w.w_down, sd)))
+    return ws
+
+
 def cpu_baseline(inp, wl, budget_s=20.0):
     """The oracle as it stands, on the first tokens of the same workload (a
     bounded sample); returns tokens/s on the host cores."""
@@ -386,6 +403,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--layer-call", action="store_true", help="also time moe_layer_fwd as one call")
+    ap.add_argument("--shared-expert", action="store_true",
+                    help="also time moe_layer_fwd with one shared expert (N(0,1/D), N(0,1/H) weights) in the same "
+                         "grouped-GEMM launches, beside the routed-only layer call")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
                          "that calibrates the HBM byte counters of a profiler run")
@@ -482,15 +502,26 @@ def main(argv=None):
     total_ms = fwd_ms + bwd_ms
     gpu_ms = evs[0][0].elapsed_time(evb[-1] if wl.bwd else evs[-1][nst]) / args.steps
 
-    layer_ms = None
-    if args.layer_call:
+    def time_layer(lay):
+        for _ in range(2):
+            lay.forward(x)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            layer.forward(x)
+            lay.forward(x)
         e1.record()
         torch.cuda.synchronize()
-        layer_ms = e0.elapsed_time(e1) / args.steps
+        return e0.elapsed_time(e1) / args.steps
+
+    layer_ms = time_layer(layer) if (args.layer_call or args.shared_expert) else None
+    shared = None
+    if args.shared_expert:
+        ws = shared_expert_weights(M, w, wl, args.seed, torch)
+        lay_s = M.MoeLayer(ws, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm)
+        shared = {"layer_fwd_ms": time_layer(lay_s), "routed_only_layer_fwd_ms": layer_ms,
+                  "note": "moe_layer_fwd with one shared expert (expert E over every token) in the same "
+                          "grouped-GEMM launches"}
+        del lay_s, ws
 
     counts = layer.saved["counts"].cpu().numpy()
     stats = load_stats(counts, wl.align)
@@ -557,6 +588,8 @@ def main(argv=None):
                                    "routed_tflops counts the expert GEMMs only"}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
+    if shared is not None:
+        out["shared_expert"] = shared
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
     print(json.dumps(out), flush=True)
