@@ -496,6 +496,13 @@ def layer_fwd_tokens(fwd_route: dict, x, w_gate, w_up, w_down, tokens, K: int, e
 # --------------------------------------------------------------------------
 
 
+def swiglu_bwd(dH, G, U):
+    """Adjoint of H = silu(G) U at the stored G, U, in float64:
+    dG = dH U s (1 + G (1 - s)), dU = dH G s, with s = sigmoid(G)."""
+    s = sigmoid(G)
+    return dH * U * s * (1.0 + G * (1.0 - s)), dH * G * s
+
+
 def experts_bwd(dyd, xd, g, u, h, offsets, w_gate, w_up, w_down, exact: bool = False):
     """Down dgrad with the SwiGLU backward, down wgrad, gate/up dgrad and wgrad.
 
@@ -522,10 +529,9 @@ def experts_bwd(dyd, xd, g, u, h, offsets, w_gate, w_up, w_down, exact: bool = F
             continue
         Wg, Wu, Wd = values(w_gate[e]), values(w_up[e]), values(w_down[e])
         G, U = np.asarray(g[a:b], np.float64), np.asarray(u[a:b], np.float64)
-        dH = dy[a:b] @ Wd
-        s = sigmoid(G)
-        dG[a:b] = r(dH * U * s * (1.0 + G * (1.0 - s)))
-        dU[a:b] = r(dH * G * s)
+        dg_e, du_e = swiglu_bwd(dy[a:b] @ Wd, G, U)
+        dG[a:b] = r(dg_e)
+        dU[a:b] = r(du_e)
         dWd[e] = r(dy[a:b].T @ np.asarray(h[a:b], np.float64))
         dXd[a:b] = r(dG[a:b] @ Wg + dU[a:b] @ Wu)
         dWg[e] = r(dG[a:b].T @ xv[a:b])
@@ -533,22 +539,31 @@ def experts_bwd(dyd, xd, g, u, h, offsets, w_gate, w_up, w_down, exact: bool = F
     return dict(dg=dG, du=dU, dxd=dXd, dw_gate=dWg, dw_up=dWu, dw_down=dWd)
 
 
-def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
-    """Adjoint sequence of the layer: combine-bwd (weighted dY dispatch) and the
-    route-weight gradient, expert backward, dispatch-bwd (sum of the K rows)."""
-    rows_cap = fwd["xd"].shape[0]
+def _layer_bwd_around(fwd: dict, dout, experts, exact: bool = False):
+    """The layer's adjoint sequence around an expert backward ``experts(dyd)``:
+    combine-bwd (weighted dY dispatch) and the route-weight gradient before it,
+    dispatch-bwd (sum of each token's K rows) after it."""
+    rows_cap = fwd["y"].shape[0]
     dyd = combine_bwd(dout, fwd["dst_rows"], fwd["topk_prob"], rows_cap, exact)
     shared = None
     if fwd.get("n_shared"):
         o = fwd["offsets"]
-        shared = slice(int(o[-2]), int(o[-1]))
+        n = values(dout).shape[0]
+        shared = slice(int(o[-2]), int(o[-2]) + n)   # its first N rows; the rest pads to the alignment
         dyd[shared] = values(dout)           # the shared expert's weight is 1
     dp = dprob(dout, fwd["y"], fwd["dst_rows"])
-    eb = experts_bwd(dyd, fwd["xd"], fwd["g"], fwd["u"], fwd["h"], fwd["offsets"],
-                     w_gate, w_up, w_down, exact)
+    eb = experts(dyd)
     dx = dispatch_bwd(eb["dxd"], fwd["dst_rows"], exact, addend=eb["dxd"][shared] if shared else None)
     eb.update(dyd=dyd, dprob=dp, dx=dx)
     return eb
+
+
+def layer_bwd(fwd: dict, dout, w_gate, w_up, w_down, exact: bool = False):
+    """Adjoint sequence of the layer: combine-bwd (weighted dY dispatch) and the
+    route-weight gradient, expert backward, dispatch-bwd (sum of the K rows)."""
+    return _layer_bwd_around(
+        fwd, dout, lambda dyd: experts_bwd(dyd, fwd["xd"], fwd["g"], fwd["u"], fwd["h"], fwd["offsets"],
+                                           w_gate, w_up, w_down, exact), exact)
 
 
 def router_bwd(logits, idx, dprob, x, w_r, renorm: int = 0, aux_dl=None) -> dict:
@@ -734,7 +749,7 @@ def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, row
     out = combine(Y, dst_rows, prob, addend=Y[offsets[E]:offsets[E] + N] if n_shared else None)
     return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
                 dst_rows=dst_rows, row_route=row_route, xq=xq, xs=xs, g=G, u=U, h=Hh,
-                hq=hq, hs=hs, y=Y, out=out)
+                hq=hq, hs=hs, y=Y, out=out, n_shared=n_shared)
 
 
 def quantize_weights_mxfp8(w_gate, w_up, w_down):
@@ -748,3 +763,95 @@ def quantize_weights_mxfp8(w_gate, w_up, w_down):
             q[e], s[e] = quantize_mxfp8(w[e])
         out[name + "_q"], out[name + "_s"] = q, s
     return out
+
+
+# --------------------------------------------------------------------------
+# MXFP8 backward            [KOSMOS 2.2 and 3.3.2; OLMo-A A.13 wgrad policy]
+# --------------------------------------------------------------------------
+
+
+def quantize_weights_mxfp8_dgrad(w_gate, w_up, w_down):
+    """The expert weights quantized for the data-gradient GEMMs, whose
+    contraction runs over the other dimension of each matrix: each copy is
+    quantized from the bf16 weights, never from the forward's copy [KOSMOS 2.2:
+    a matrix and its transpose are both quantized from the high-precision
+    source; OLMo-A A.13: the right-hand operand prequantized for dgrad].
+
+    wdt_q [E,H,D], wdt_s [E,H,D/32]: W_down[e]^T quantized along D;
+    wgut_q [E,D,2H], wgut_s [E,D,2H/32]: [W_gate[e]^T | W_up[e]^T] quantized
+    along H (H % 32 == 0, so no block straddles the two halves).
+    """
+    wg, wu, wd = values(w_gate), values(w_up), values(w_down)
+    out = {"wdt_q": [], "wdt_s": [], "wgut_q": [], "wgut_s": []}
+    for e in range(wg.shape[0]):
+        q, s = quantize_mxfp8(wd[e].T)
+        out["wdt_q"].append(q)
+        out["wdt_s"].append(s)
+        q, s = quantize_mxfp8(np.concatenate([wg[e].T, wu[e].T], axis=1))
+        out["wgut_q"].append(q)
+        out["wgut_s"].append(s)
+    return {k: np.stack(v) for k, v in out.items()}
+
+
+def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
+    """Expert backward with block-scaled data gradients and bf16 weight
+    gradients on dequantized activations.
+
+    dY_d is quantized row-wise along D from its bf16 values [KOSMOS 3.3.2
+    step 1: dY arrives in bf16 and is quantized where it lands];
+    dH = deq(dY_q) deq(W_down^T q)^T in float64 (it only feeds the SwiGLU
+    backward); dG, dU from the SwiGLU backward, stored bf16;
+    [dG | dU] quantized row-wise along 2H from those bf16 values;
+    dX_d = bf16(deq([dG|dU]_q) deq([W_gate^T|W_up^T]_q)^T), one sum over 2H
+    [KOSMOS 3.3.2 steps 2-3; OLMo-A A.13: forward and dgrad on the scaled
+    grouped GEMM];
+    dW_down = bf16(dY_d^T deq(H_q)), dW_gate = bf16(dG^T deq(X_q)),
+    dW_up = bf16(dU^T deq(X_q)) [OLMo-A A.13: wgrad dequantizes its operands
+    and runs a bf16 grouped GEMM].
+    """
+    dy = values(dyd)
+    rows, D = dy.shape
+    E = len(offsets) - 1
+    Hd = np.asarray(g).shape[1]
+    dyq, dys = quantize_mxfp8(dy)
+    dy_deq = dequantize_mxfp8(dyq, dys)
+    x_deq = dequantize_mxfp8(xq, xs)
+    h_deq = dequantize_mxfp8(hq, hs)
+    dG = np.zeros((rows, Hd))
+    dU = np.zeros((rows, Hd))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        wdt = dequantize_mxfp8(wqt["wdt_q"][e], wqt["wdt_s"][e])          # [H, D]
+        dg_e, du_e = swiglu_bwd(dy_deq[a:b] @ wdt.T, np.asarray(g[a:b], np.float64),
+                                np.asarray(u[a:b], np.float64))
+        dG[a:b] = round_bf16(dg_e)
+        dU[a:b] = round_bf16(du_e)
+    guq, gus = quantize_mxfp8(np.concatenate([dG, dU], axis=1))
+    gu_deq = dequantize_mxfp8(guq, gus)
+    dXd = np.zeros((rows, D))
+    dWg = np.zeros((E, Hd, D))
+    dWu = np.zeros((E, Hd, D))
+    dWd = np.zeros((E, D, Hd))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        wgut = dequantize_mxfp8(wqt["wgut_q"][e], wqt["wgut_s"][e])        # [D, 2H]
+        dXd[a:b] = round_bf16(gu_deq[a:b] @ wgut.T)
+        dWd[e] = round_bf16(dy[a:b].T @ h_deq[a:b])
+        dWg[e] = round_bf16(dG[a:b].T @ x_deq[a:b])
+        dWu[e] = round_bf16(dU[a:b].T @ x_deq[a:b])
+    return dict(dg=dG, du=dU, dxd=dXd, dw_gate=dWg, dw_up=dWu, dw_down=dWd,
+                dyq=dyq, dys=dys, guq=guq, gus=gus)
+
+
+def layer_bwd_mxfp8(fwd: dict, dout, wqt):
+    """MXFP8 layer backward: the bf16 adjoint sequence around the experts
+    (weighted dY dispatch, route-weight gradient, fold of the K rows) with
+    experts_bwd_mxfp8 in the middle.  fwd is layer_fwd_mxfp8's result; wqt
+    comes from quantize_weights_mxfp8_dgrad."""
+    return _layer_bwd_around(
+        fwd, dout, lambda dyd: experts_bwd_mxfp8(dyd, fwd["xq"], fwd["xs"], fwd["g"], fwd["u"], fwd["hq"],
+                                                 fwd["hs"], fwd["offsets"], wqt))
