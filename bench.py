@@ -305,7 +305,7 @@ class StagedForward:
         mark(6)
 
 
-def device_inputs(M, inp, mxfp8, torch):
+def device_inputs(M, inp, mxfp8, torch, backward=False):
     def b(u):
         return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -313,6 +313,9 @@ def device_inputs(M, inp, mxfp8, torch):
     if mxfp8:
         wg, wu, wd = b(inp.w_gate), b(inp.w_up), b(inp.w_down)
         w.wq = M.quantize_weights_mxfp8(wg, wu, wd)
+        if backward:
+            # the data gradients' weight copies, quantized along the other dimension
+            w.wq.update(M.quantize_weights_mxfp8_dgrad(wg, wu, wd))
         torch.cuda.synchronize()
         del wg, wu, wd
     else:
@@ -332,6 +335,8 @@ def shared_expert_weights(M, w, wl, seed, torch):
     sg, su, sd = mk(1, H, D, std=D ** -0.5), mk(1, H, D, std=D ** -0.5), mk(1, D, H, std=H ** -0.5)
     if w.wq:
         q = M.quantize_weights_mxfp8(sg, su, sd)
+        if "wdt_q" in w.wq:
+            q.update(M.quantize_weights_mxfp8_dgrad(sg, su, sd))
         ws.wq = {k: torch.cat([w.wq[k], q[k]]) for k in w.wq}
     else:
         ws.w_gate, ws.w_up, ws.w_down = (torch.cat([a, b]) for a, b in ((w.w_gate, sg), (w.w_up, su), (w.w_down, sd)))
@@ -403,6 +408,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--layer-call", action="store_true", help="also time moe_layer_fwd as one call")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (moe_layer_bwd with the router backward) on a forward "
+                         "workload; dOut is N(0, 1) bf16 from the seed")
     ap.add_argument("--shared-expert", action="store_true",
                     help="also time moe_layer_fwd with one shared expert (N(0,1/D), N(0,1/H) weights) in the same "
                          "grouped-GEMM launches, beside the routed-only layer call")
@@ -448,14 +456,16 @@ def main(argv=None):
     import mixture_experts_expert_router_amd as M
 
     wl = S.WORKLOADS[args.workload]
+    bwd = wl.bwd or args.backward
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     inp = S.make_inputs(wl, args.seed)
-    x, w, drop = device_inputs(M, inp, wl.mxfp8, torch)
-    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=wl.bwd,
-                       router_bwd=wl.bwd)
-    dout = (torch.from_numpy(np.ascontiguousarray(inp.dout).view(np.int16)).view(torch.bfloat16).cuda()
-            if wl.bwd else None)
+    x, w, drop = device_inputs(M, inp, wl.mxfp8, torch, backward=bwd)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=bwd,
+                       router_bwd=bwd)
+    dout_bits = inp.dout if inp.dout is not None else (S.random_bf16((wl.N, wl.D), args.seed, 9) if bwd else None)
+    dout = (torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
+            if bwd else None)
     st = StagedForward(M, layer, x)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
@@ -477,7 +487,7 @@ def main(argv=None):
     # dX_r, dW_r, db_r; dispatch-bwd folding in dX_r) after it
     def step(ev=None, ev_b=None):
         st.run(ev)
-        if wl.bwd:
+        if bwd:
             layer.backward(x, dout)
             if ev_b is not None:
                 ev_b.record()
@@ -498,9 +508,9 @@ def main(argv=None):
     stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
                 for i, name in enumerate(StagedForward.STAGES)}
     fwd_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(args.steps)]))
-    bwd_ms = (float(np.mean([evs[k][nst].elapsed_time(evb[k]) for k in range(args.steps)])) if wl.bwd else 0.0)
+    bwd_ms = (float(np.mean([evs[k][nst].elapsed_time(evb[k]) for k in range(args.steps)])) if bwd else 0.0)
     total_ms = fwd_ms + bwd_ms
-    gpu_ms = evs[0][0].elapsed_time(evb[-1] if wl.bwd else evs[-1][nst]) / args.steps
+    gpu_ms = evs[0][0].elapsed_time(evb[-1] if bwd else evs[-1][nst]) / args.steps
 
     def time_layer(lay):
         for _ in range(2):
@@ -563,7 +573,8 @@ def main(argv=None):
         "dtype": "mxfp8-e4m3/bf16" if wl.mxfp8 else "bf16",
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {"workload": wl.name, "N": N, "D": D, "E": E, "K": K, "H": H, "zipf_s": wl.zipf_s,
-                   "p_drop": wl.p_drop, "align": wl.align, "seed": args.seed},
+                   "p_drop": wl.p_drop, "align": wl.align, "seed": args.seed,
+                   "pass": "fwd+bwd" if bwd else "fwd"},
         "roofline": roof,
         "grouped_gemm": {"tflops": gemm_tflops, "pct_mfma_peak": 100 * gemm_tflops / peak,
                          "gemm1_ms": stage_ms["gemm1"], "gemm2_ms": stage_ms["gemm2"],
@@ -581,11 +592,12 @@ def main(argv=None):
         "gpu_span_ms_per_step": gpu_ms,
     }
     out["fwd_ms"] = fwd_ms
-    if wl.bwd:
+    if bwd:
         tf_b = routed_flops(R, D, H, backward=True) / (bwd_ms / 1e3) / 1e12
-        out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / peak,
+        out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / PEAK_BF16_TFLOPS,
                            "note": "value and ms_per_step cover forward + backward, router backward included; "
-                                   "routed_tflops counts the expert GEMMs only"}
+                                   "routed_tflops counts the expert GEMMs only; pct_mfma_peak against the bf16 "
+                                   "peak" + (" (MXFP8: block-scaled dgrads, bf16 wgrads)" if wl.mxfp8 else "")}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
     if shared is not None:

@@ -67,6 +67,7 @@ extern "C" {
 #define MOE_OP_LAYER_FWD 3
 #define MOE_OP_LAYER_BWD 4
 #define MOE_OP_ROUTER 5
+#define MOE_OP_LAYER_BWD_MXFP8 6
 
 /* ---- shapes -------------------------------------------------------------
  * N tokens, D model width, E experts, K routes per token, H expert (SwiGLU)
@@ -180,6 +181,21 @@ int moe_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weig
 int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scales,
                        void* stream);
 
+/* Column-wise blocks with transpose, the same element and scale rules: the
+ * copy of a matrix for the product that contracts over its other dimension,
+ * quantized from the bf16 source (KOSMOS section 2.2: both orientations come
+ * from the high-precision tensor; OLMo-core Appendix A, A.13: the right-hand
+ * operand prequantized for dgrad).
+ *   src bf16 [batch][rows][cols]  ->  q[b][c][col0 + r]  (row stride ld),
+ *   each block = 32 consecutive r of one column c;
+ *   scales[b][c][(col0 + r) / 32]  (row stride ld / 32).
+ * Only columns col0 .. col0 + rows - 1 of each q row are written, so two calls
+ * with col0 = 0 and col0 = rows fill [A^T | B^T].  rows % 32, cols % 8,
+ * ld % 32 and col0 % 32 must be 0 and col0 + rows <= ld (else MOE_ERR_SHAPE);
+ * src and q 16-byte aligned (else MOE_ERR_ALIGN). */
+int moe_quantize_mxfp8_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                            int64_t col0, uint8_t* q, uint8_t* scales, void* stream);
+
 /* ---- SwiGLU ------------------------------------------------------------
  * h = bf16(silu(g) * u) from bf16 g, u [rows][n] (KOSMOS section 3.3.1 step 3
  * epilogue).  out_dtype MOE_MXFP8 also quantizes h row-wise into h_q/h_scales
@@ -258,10 +274,19 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * saved tensors; KOSMOS section 3.3.1 steps 1-5).  For MXFP8 the dispatch
  * quantizes (xd_q/xd_s), GEMM1 is block-scaled, H is quantized (h_q/h_s), and
  * GEMM2 is block-scaled; the combine is bf16.
- * Backward (bf16 only): combine-bwd and dprob -> down dgrad with the SwiGLU
+ * Backward: combine-bwd and dprob -> down dgrad with the SwiGLU
  * backward -> down wgrad -> gate/up dgrad (one sum) -> gate/up wgrad ->
  * dispatch-bwd (KOSMOS section 3.3.2).  The intermediates dY_d, dG, dU, dX_d
- * live in the workspace. */
+ * live in the workspace (moe_workspace_size(MOE_OP_LAYER_BWD)).
+ * MXFP8 backward (workspace MOE_OP_LAYER_BWD_MXFP8): dY_d is quantized
+ * row-wise along D from its bf16 values; the down dgrad is block-scaled with
+ * wdt_q, its epilogue stores dG, dU (bf16) and [dG | dU] quantized along 2H;
+ * the gate/up dgrad is one block-scaled product with wgut_q over 2H; the
+ * weight gradients are bf16 products of the bf16 dY_d, dG, dU with the
+ * saved activations dequantized from xd_q and h_q (OLMo-core Appendix A,
+ * A.13: dgrad on the scaled grouped GEMM, wgrad in bf16 on dequantized
+ * operands).  It reads the saved xd_q/xd_s, g, u, h_q/h_s, y and no bf16
+ * expert weights; it needs D % 128 == 0 and H % 64 == 0 (else MOE_ERR_SHAPE). */
 #define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
 #define MOE_SCHED_READY 1   /* bf16: one persistent launch; GEMM1 tiles claimed in
                                the order dispatch finishes experts, GEMM2 tiles
@@ -289,6 +314,14 @@ typedef struct moe_layer_args {
    * share of valid routes to e and P_e the mean routing probability of e.
    * Computed into saved->aux when aux_alpha != 0 and saved->aux != NULL. */
   float aux_alpha;
+  /* MXFP8 backward: the weight copies of the data gradients, quantized from
+   * the bf16 weights along their other dimension (moe_quantize_mxfp8_cols):
+   * wdt_q [E][H][D] = W_down^T along D, scales [E][H][D/32];
+   * wgut_q [E][D][2H] = [W_gate^T | W_up^T] along H, scales [E][D][2H/32]. */
+  const uint8_t* wdt_q;
+  const uint8_t* wdt_s;
+  const uint8_t* wgut_q;
+  const uint8_t* wgut_s;
 } moe_layer_args;
 
 typedef struct moe_layer_saved {

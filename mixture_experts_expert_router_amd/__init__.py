@@ -23,6 +23,7 @@ MOE_OK = 0
 MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD, MOE_OP_ROUTER = 1, 2, 3, 4, 5
+MOE_OP_LAYER_BWD_MXFP8 = 6
 MOE_SCHED_STAGED, MOE_SCHED_READY = 0, 1
 
 _vp = C.c_void_p
@@ -54,7 +55,8 @@ class LayerArgs(C.Structure):
     _fields_ = [("dims", Dims), ("dtype", _i32), ("sched", _i32), ("x", _vp), ("w_r", _vp),
                 ("bias", _vp), ("drop", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("wg_q", _vp), ("wg_s", _vp), ("wu_q", _vp), ("wu_s", _vp), ("wd_q", _vp),
-                ("wd_s", _vp), ("aux_alpha", C.c_float)]
+                ("wd_s", _vp), ("aux_alpha", C.c_float), ("wdt_q", _vp), ("wdt_s", _vp), ("wgut_q", _vp),
+                ("wgut_s", _vp)]
 
 
 class LayerSaved(C.Structure):
@@ -80,6 +82,7 @@ EXPORTS = {
     "moe_combine": (C.c_int, [_vp, _vp, _vp, C.POINTER(Dims), _vp, _vp]),
     "moe_combine_bwd": (C.c_int, [_vp, _vp, _vp, _vp, C.POINTER(Dims), _vp, _vp, _vp]),
     "moe_quantize_mxfp8": (C.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "moe_quantize_mxfp8_cols": (C.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
     "moe_swiglu": (C.c_int, [_vp, _vp, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_fwd": (C.c_int, [C.POINTER(GemmFwdArgs), _vp, C.c_size_t, _vp]),
     "moe_grouped_gemm_bwd": (C.c_int, [C.POINTER(GemmBwdArgs), _vp, C.c_size_t, _vp]),
@@ -331,7 +334,8 @@ class LayerWeights:
     w_up: Optional[object] = None
     w_down: Optional[object] = None
     bias: Optional[object] = None
-    wq: Optional[dict] = None        # MXFP8: wg_q, wg_s, wu_q, wu_s, wd_q, wd_s
+    wq: Optional[dict] = None        # MXFP8: wg_q, wg_s, wu_q, wu_s, wd_q, wd_s; for the backward
+                                     # also wdt_q, wdt_s, wgut_q, wgut_s (quantize_weights_mxfp8_dgrad)
 
 
 def quantize_weights_mxfp8(w_gate, w_up, w_down) -> dict:
@@ -342,6 +346,30 @@ def quantize_weights_mxfp8(w_gate, w_up, w_down) -> dict:
         q, s = quantize_mxfp8(w.reshape(E * n, k))
         out[name + "_q"] = q.reshape(E, n, k)
         out[name + "_s"] = s.reshape(E, n, k // 32)
+    return out
+
+
+def quantize_mxfp8_cols(src, q, scales, col0=0):
+    """Column-wise MXFP8 copy of bf16 src [B, R, C] into q [B, C, ld] (columns
+    col0 .. col0 + R - 1) and scales [B, C, ld // 32], blocks along R."""
+    B, R, Cn = src.shape
+    ld = q.shape[2]
+    _check(load().moe_quantize_mxfp8_cols(_ptr(src), B, R, Cn, ld, col0, _ptr(q), _ptr(scales), _stream()),
+           "moe_quantize_mxfp8_cols")
+
+
+def quantize_weights_mxfp8_dgrad(w_gate, w_up, w_down) -> dict:
+    """The weight copies of the MXFP8 data gradients, each quantized from the
+    bf16 weights along its other dimension: wdt_q [E, H, D] (W_down^T along D)
+    and wgut_q [E, D, 2H] ([W_gate^T | W_up^T] along H), with their scales."""
+    torch = _torch()
+    E, H, D = w_gate.shape
+    dev = w_gate.device
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    out = dict(wdt_q=u8(E, H, D), wdt_s=u8(E, H, D // 32), wgut_q=u8(E, D, 2 * H), wgut_s=u8(E, D, 2 * H // 32))
+    quantize_mxfp8_cols(w_down, out["wdt_q"], out["wdt_s"])
+    quantize_mxfp8_cols(w_gate, out["wgut_q"], out["wgut_s"], 0)
+    quantize_mxfp8_cols(w_up, out["wgut_q"], out["wgut_s"], H)
     return out
 
 
@@ -360,7 +388,8 @@ def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_ST
     a = LayerArgs(d, MOE_MXFP8 if mxfp8 else MOE_BF16, sched, _ptr(x), _ptr(wts.w_r), _ptr(wts.bias),
                   _ptr(drop), _ptr(wts.w_gate), _ptr(wts.w_up), _ptr(wts.w_down),
                   _ptr(q.get("wg_q")), _ptr(q.get("wg_s")), _ptr(q.get("wu_q")), _ptr(q.get("wu_s")),
-                  _ptr(q.get("wd_q")), _ptr(q.get("wd_s")), float(aux_alpha))
+                  _ptr(q.get("wd_q")), _ptr(q.get("wd_s")), float(aux_alpha), _ptr(q.get("wdt_q")),
+                  _ptr(q.get("wdt_s")), _ptr(q.get("wgut_q")), _ptr(q.get("wgut_s")))
     return a, d
 
 
@@ -415,7 +444,7 @@ class MoeLayer:
         self.grads = None
         if with_bwd:
             E, H = self.d.E + self.d.n_shared, self.d.H
-            self.ws_b = workspace(MOE_OP_LAYER_BWD, self.d, device)
+            self.ws_b = workspace(MOE_OP_LAYER_BWD_MXFP8 if mxfp8 else MOE_OP_LAYER_BWD, self.d, device)
             self.grads = dict(dx=torch.empty((N, D), dtype=torch.bfloat16, device=device),
                               dprob=torch.empty((N, K), dtype=torch.float32, device=device),
                               dw_gate=torch.empty((E, H, D), dtype=torch.bfloat16, device=device),
@@ -436,7 +465,8 @@ class MoeLayer:
         return self.out
 
     def backward(self, x, dout, recompute_h=False, d_aux=0.0):
-        """recompute_h: do not read the saved H; the library recomputes it from G and U.
+        """recompute_h: do not read the saved H; the library recomputes it from G and U
+        (bf16; the MXFP8 backward reads the saved h_q instead).
         d_aux: upstream gradient of the aux loss (used when aux_alpha != 0)."""
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, **self._opts)
         self._gr.d_aux = float(d_aux)

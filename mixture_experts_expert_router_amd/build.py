@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_rocm.so")
 
-SOURCES = ["capi.cpp", "router.hip", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_mxfp8.hip"]
+SOURCES = ["capi.cpp", "router.hip", "route.hip", "permute.hip", "quant.hip", "gemm_bf16.hip", "gemm_fwd.hip", "gemm_bwd.hip", "gemm_mxfp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -129,11 +129,39 @@ RouterBwdLayout router_bwd_layout(const moe_dims& d) {
   return l;
 }
 
-size_t bwd_scratch_bytes(const moe_dims& d) {
-  const size_t rc = (size_t)rows_cap_of(d);
-  // dY_d, dX_d, dG, dU, H when recomputed, the router backward's scratch
-  return 2 * round_up(rc * d.D * 2, 256) + 3 * round_up(rc * d.H * 2, 256) + router_bwd_layout(d).total;
+// layer backward scratch (after the GEMM table): dY_d, dX_d, dG, dU and H
+// (recomputed, or dequantized from h_q), then for MXFP8 dY_d quantized,
+// [dG | dU] quantized and X_d dequantized, then the router backward's scratch
+struct BwdLayout {
+  size_t dyd, dxd, dg, du, h, dyq, dys, guq, gus, xdeq, router, total;
+};
+
+BwdLayout bwd_layout(const moe_dims& d, bool mx) {
+  BwdLayout l{};
+  const size_t rc = (size_t)rows_cap_of(d), D = (size_t)d.D, H = (size_t)d.H;
+  size_t o = 0;
+  auto take = [&o](size_t& at, size_t bytes) {
+    at = o;
+    o += round_up(bytes, 256);
+  };
+  take(l.dyd, rc * D * 2);
+  take(l.dxd, rc * D * 2);
+  take(l.dg, rc * H * 2);
+  take(l.du, rc * H * 2);
+  take(l.h, rc * H * 2);
+  if (mx) {
+    take(l.dyq, rc * D);
+    take(l.dys, rc * D / 32);
+    take(l.guq, rc * 2 * H);
+    take(l.gus, rc * 2 * H / 32);
+    take(l.xdeq, rc * D * 2);
+  }
+  take(l.router, router_bwd_layout(d).total);
+  l.total = o;
+  return l;
 }
+
+size_t bwd_scratch_bytes(const moe_dims& d, bool mx) { return bwd_layout(d, mx).total; }
 
 }  // namespace
 
@@ -149,7 +177,8 @@ size_t moe_workspace_size(int op, const moe_dims* d) {
     case MOE_OP_GEMM: return table_bytes(rc, experts_of(*d));
     case MOE_OP_ROUTER: return router_bytes(*d);
     case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, experts_of(*d)) + router_bytes(*d);
-    case MOE_OP_LAYER_BWD: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d);
+    case MOE_OP_LAYER_BWD: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, false);
+    case MOE_OP_LAYER_BWD_MXFP8: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, true);
     default: return 0;
   }
 }
@@ -273,6 +302,18 @@ int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t cols, uint8_t* q, 
   REQUIRE(q);
   REQUIRE(scales);
   return hip_status(moe::launch_quantize_rows(src, rows, cols, q, scales, (hipStream_t)stream));
+}
+
+int moe_quantize_mxfp8_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                            int64_t col0, uint8_t* q, uint8_t* scales, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || rows % 32 || cols % 8 || ld <= 0 || ld % 32 || col0 < 0 ||
+      col0 % 32 || col0 + rows > ld || batch > 65535 || (rows + 127) / 128 > 65535 ||
+      batch * cols * ld >= (int64_t(1) << 40))
+    return MOE_ERR_SHAPE;
+  REQUIRE(src);
+  REQUIRE(q);
+  REQUIRE(scales);
+  return hip_status(moe::launch_quantize_cols(src, batch, rows, cols, ld, col0, q, scales, (hipStream_t)stream));
 }
 
 int moe_swiglu(const void* g, const void* u, int64_t rows, int64_t n, int out_dtype, void* h,
@@ -478,23 +519,38 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
 int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void* dout,
                   moe_layer_grads* gr, void* ws, size_t ws_bytes, void* stream) {
   if (!a || !sv || !gr) return MOE_ERR_NULL;
-  if (a->dtype != MOE_BF16) return a->dtype == MOE_MXFP8 ? MOE_ERR_UNSUPPORTED : MOE_ERR_DTYPE;
+  if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  const bool mx = a->dtype == MOE_MXFP8;
   const moe_dims& d = a->dims;
-  int st = check_dims(&d, true, false);
+  int st = check_dims(&d, true, mx);
   if (st) return st;
-  REQUIRE(a->w_gate);
-  REQUIRE(a->w_up);
-  REQUIRE(a->w_down);
+  if (mx) {
+    // the block-scaled dgrads run on the persistent engine: whole 128-element
+    // contraction steps over D and over 2H
+    if (d.D % 128 || d.H % 64) return MOE_ERR_SHAPE;
+    REQUIRE(a->wdt_q);
+    REQUIRE(a->wdt_s);
+    REQUIRE(a->wgut_q);
+    REQUIRE(a->wgut_s);
+    REQUIRE(sv->xd_q);
+    REQUIRE(sv->xd_s);
+    REQUIRE(sv->h_q);
+    REQUIRE(sv->h_s);
+  } else {
+    REQUIRE(a->w_gate);
+    REQUIRE(a->w_up);
+    REQUIRE(a->w_down);
+    REQUIRE(sv->xd);
+    OPTIONAL(sv->h);   // NULL: recomputed from G and U
+  }
   REQUIRE(dout);
   REQUIRE(ws);
   REQUIRE(sv->topk_prob);
   REQUIRE(sv->counts);
   REQUIRE(sv->offsets);
   REQUIRE(sv->dst_rows);
-  REQUIRE(sv->xd);
   REQUIRE(sv->g);
   REQUIRE(sv->u);
-  OPTIONAL(sv->h);   // NULL: recomputed from G and U
   REQUIRE(sv->y);
   REQUIRE(gr->dx);
   REQUIRE(gr->dprob);
@@ -515,43 +571,78 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   const int64_t Ex = experts_of(d);
   const int32_t* shared_row0 = d.n_shared ? sv->offsets + d.E : nullptr;   // the shared expert's segment
   const size_t tb = table_bytes(rc, Ex);
-  if (ws_bytes < tb + bwd_scratch_bytes(d)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < tb + bwd_scratch_bytes(d, mx)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  char* p = (char*)ws;
-  int32_t* table = (int32_t*)p;
-  p += tb;
-  void* dyd = p;
-  p += round_up((size_t)rc * d.D * 2, 256);
-  void* dxd = p;
-  p += round_up((size_t)rc * d.D * 2, 256);
-  void* dg = p;
-  p += round_up((size_t)rc * d.H * 2, 256);
-  void* du = p;
-  p += round_up((size_t)rc * d.H * 2, 256);
-  // SwiGLU-recompute mode: H = silu(G) U from the saved bf16 G and U, the
-  // same arithmetic as GEMM1's epilogue, so it equals the forward's H bit for bit
-  const void* h = sv->h ? sv->h : (const void*)p;
+  int32_t* table = (int32_t*)ws;
+  char* p0 = (char*)ws + tb;
+  const BwdLayout bl = bwd_layout(d, mx);
+  void* dyd = p0 + bl.dyd;
+  void* dxd = p0 + bl.dxd;
+  void* dg = p0 + bl.dg;
+  void* du = p0 + bl.du;
+  const int32_t* rows_end = sv->offsets + Ex;   // rows past the last segment are never read
 
-  hipError_t e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd,
-                                         gr->dprob, s, shared_row0);
-  if (e == hipSuccess && !sv->h) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, (void*)h, nullptr, nullptr, s);
-  if (e == hipSuccess && d.align > 1)
-    e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
-  // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
-  moe::GemmBwd down{Ex, rc, d.H, d.D, sv->offsets, h, a->w_down, nullptr, dyd, nullptr, nullptr,
-                    sv->g, sv->u, dg, du, true};
-  if (e == hipSuccess) e = gemm_dgrad(down, table, s);
-  if (e == hipSuccess) e = gemm_wgrad(down, dyd, gr->dw_down, table, s);
-  // gate/up: forward g = xd . w_gate^T, u = xd . w_up^T  (k_dim = D, n_dim = H)
-  moe::GemmBwd gu{Ex, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
-                  nullptr, nullptr, nullptr, nullptr, false};
-  if (e == hipSuccess) e = gemm_dgrad(gu, table, s);
-  if (e == hipSuccess) e = gemm_wgrad(gu, dg, gr->dw_gate, table, s);
-  if (e == hipSuccess) e = gemm_wgrad(gu, du, gr->dw_up, table, s);
+  hipError_t e = hipSuccess;
+  if (mx) {
+    uint8_t* dyq = (uint8_t*)(p0 + bl.dyq);
+    uint8_t* dys = (uint8_t*)(p0 + bl.dys);
+    uint8_t* guq = (uint8_t*)(p0 + bl.guq);
+    uint8_t* gus = (uint8_t*)(p0 + bl.gus);
+    void* hdq = p0 + bl.h;
+    void* xdq = p0 + bl.xdeq;
+    // down dgrad, block-scaled: dH = dY_d . (W_down^T)^T over D, the SwiGLU
+    // backward and the quantization of [dG | dU] in its epilogue
+    moe::GemmFwd dn{Ex, rc, d.D, d.H, sv->offsets, dyq, dys, a->wdt_q, a->wdt_s, nullptr,
+                    nullptr, dg, du, nullptr, guq, gus, false};
+    dn.dswiglu = true;
+    dn.g = sv->g;
+    dn.u = sv->u;
+    // gate/up dgrad, block-scaled: dX_d = [dG | dU] . [W_gate^T | W_up^T]^T over 2H
+    moe::GemmFwd gu{Ex, rc, 2 * d.H, d.D, sv->offsets, guq, gus, a->wgut_q, a->wgut_s, nullptr,
+                    nullptr, dxd, nullptr, nullptr, nullptr, nullptr, false};
+    if (!moe::gemm_fwd_fast_ok(dn, true) || !moe::gemm_fwd_fast_ok(gu, true)) return MOE_ERR_SHAPE;
+    e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd, gr->dprob, s,
+                                shared_row0);
+    if (e == hipSuccess) e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
+    // dY arrives in bf16 and is quantized where it lands (KOSMOS section 3.3.2 step 1)
+    if (e == hipSuccess) e = moe::launch_quantize_rows(dyd, rc, d.D, dyq, dys, s, rows_end);
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(dn, true, table, s);
+    if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(gu, true, table, s);
+    // weight gradients: bf16 products on the dequantized activations
+    if (e == hipSuccess) e = moe::launch_dequant_rows(sv->h_q, sv->h_s, rc, d.H, rows_end, hdq, s);
+    if (e == hipSuccess) e = moe::launch_dequant_rows(sv->xd_q, sv->xd_s, rc, d.D, rows_end, xdq, s);
+    moe::GemmBwd wd{Ex, rc, d.H, d.D, sv->offsets, hdq, nullptr, nullptr, dyd, nullptr, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = gemm_wgrad(wd, dyd, gr->dw_down, table, s);
+    moe::GemmBwd wgu{Ex, rc, d.D, d.H, sv->offsets, xdq, nullptr, nullptr, dg, du, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = gemm_wgrad(wgu, dg, gr->dw_gate, table, s);
+    if (e == hipSuccess) e = gemm_wgrad(wgu, du, gr->dw_up, table, s);
+  } else {
+    // SwiGLU-recompute mode: H = silu(G) U from the saved bf16 G and U, the
+    // same arithmetic as GEMM1's epilogue, so it equals the forward's H bit for bit
+    const void* h = sv->h ? sv->h : (const void*)(p0 + bl.h);
+    e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd, gr->dprob, s,
+                                shared_row0);
+    if (e == hipSuccess && !sv->h) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, (void*)h, nullptr, nullptr, s);
+    if (e == hipSuccess && d.align > 1)
+      e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
+    // down: forward y = h . w_down^T  (k_dim = H, n_dim = D)
+    moe::GemmBwd down{Ex, rc, d.H, d.D, sv->offsets, h, a->w_down, nullptr, dyd, nullptr, nullptr,
+                      sv->g, sv->u, dg, du, true};
+    if (e == hipSuccess) e = gemm_dgrad(down, table, s);
+    if (e == hipSuccess) e = gemm_wgrad(down, dyd, gr->dw_down, table, s);
+    // gate/up: forward g = xd . w_gate^T, u = xd . w_up^T  (k_dim = D, n_dim = H)
+    moe::GemmBwd gu{Ex, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
+                    nullptr, nullptr, nullptr, nullptr, false};
+    if (e == hipSuccess) e = gemm_dgrad(gu, table, s);
+    if (e == hipSuccess) e = gemm_wgrad(gu, dg, gr->dw_gate, table, s);
+    if (e == hipSuccess) e = gemm_wgrad(gu, du, gr->dw_up, table, s);
+  }
   const void* dxr = nullptr;
   if (e == hipSuccess && gr->dw_r) {
     // router backward, after the expert backward so the fold below adds dX_r
-    p += round_up((size_t)rc * d.H * 2, 256);   // past H
+    char* p = p0 + bl.router;
     const RouterBwdLayout l = router_bwd_layout(d);
     float* dl = gr->dlogits ? gr->dlogits : (float*)(p + l.dl);
     uint16_t* dlb = (uint16_t*)(p + l.dlb);

@@ -37,6 +37,15 @@
 // accumulation and the same bf16 outputs; GEMM1's epilogue also stores H
 // quantized row-wise along its columns (blocks of 32, KOSMOS section 3.3.1
 // step 3), the A operand of the MXFP8 GEMM2.
+//
+// The MXFP8 data gradient of the down projection runs here too (KOSMOS
+// section 3.3.2 step 2; OLMo-core Appendix A, A.13: dgrad on the scaled
+// grouped GEMM with a right-hand operand prequantized for it): A = dY_d
+// quantized along D, B = W_down^T quantized along D, so the accumulator is
+// dH.  Its epilogue applies the SwiGLU backward with the saved G and U,
+// stores dG and dU in bf16 and quantizes [dG | dU] row-wise in blocks of 32,
+// the A operand of the gate/up data gradient (a plain single-B MXFP8 GEMM over
+// 2H contraction elements).
 #include "common.h"
 #include "launch.h"
 #include "mfma_tile.h"
@@ -64,8 +73,10 @@ struct FwdParams {
   uint16_t* c0;             // [rows][N]  (G or Y), bf16
   uint16_t* c1;             // DUAL: U
   uint16_t* c2;             // DUAL: H
-  uint8_t* hq;              // DUAL, optional: H as E4M3 [rows][N]
-  uint8_t* hs;              //   and its E8M0 scales [rows][N/32]
+  uint8_t* hq;              // DUAL, optional: H as E4M3 [rows][N]; DSW: [dG | dU] [rows][2N]
+  uint8_t* hs;              //   and its E8M0 scales [rows][N/32]; DSW: [rows][2N/32]
+  const uint16_t* g;        // DSW: saved G and U [rows][N], bf16
+  const uint16_t* u;
 };
 
 // The two tile classes; both have BN = 256 (DUAL: 128 gate + 128 up columns).
@@ -223,10 +234,101 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
   }
 }
 
+// MX data gradient of the down projection: acc = dH [rows][N] (N = H).
+// dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G) from the saved
+// bf16 G and U, stored bf16 in c0 / c1; the bf16 values are then quantized
+// row-wise, dG into columns [0, N) and dU into [N, 2N) of hq / hs.  A 32-column
+// block is fragments (j, j+1) over the four lane groups of one row, as in the
+// H quantization above (N % 32 == 0: a block is all in or all out).
+template <class C>
+__device__ __forceinline__ void epilogue_dsw(const FwdParams& p, const Item& it,
+                                             const f32x4_t (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
+  constexpr int kDswFrags = 4;
+  static_assert(!C::DUAL && TN % kDswFrags == 0, "single-B tile, whole 32-column blocks per wave");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t N2 = 2 * (int64_t)p.N;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = wm * WM + i * 16 + l16;
+    if (it.m_start + m >= it.m1) continue;
+    const int64_t row = it.m_start + m;
+    // four fragments (two 32-column blocks) at a time: their G and U loads are
+    // issued together, and fewer values stay live beside the accumulators
+#pragma unroll
+    for (int j0 = 0; j0 < TN; j0 += kDswFrags) {
+      uint2 gw[kDswFrags], uw[kDswFrags];
+#pragma unroll
+      for (int jj = 0; jj < kDswFrags; ++jj) {
+        const int n = it.n0 + wn * WN + (j0 + jj) * 16 + 4 * lg;
+        gw[jj] = uw[jj] = make_uint2(0, 0);
+        if (n < p.N) {
+          gw[jj] = *reinterpret_cast<const uint2*>(p.g + row * p.N + n);
+          uw[jj] = *reinterpret_cast<const uint2*>(p.u + row * p.N + n);
+        }
+      }
+      uint32_t dgw[kDswFrags][2], duw[kDswFrags][2];
+#pragma unroll
+      for (int jj = 0; jj < kDswFrags; ++jj) {
+        const f32x4_t a = acc[i][j0 + jj];
+        const float gg[4] = {bf16lo(gw[jj].x), bf16hi(gw[jj].x), bf16lo(gw[jj].y), bf16hi(gw[jj].y)};
+        const float uu[4] = {bf16lo(uw[jj].x), bf16hi(uw[jj].x), bf16lo(uw[jj].y), bf16hi(uw[jj].y)};
+        float dg[4], du[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sg = sigmoidf_(gg[q]);
+          dg[q] = a[q] * uu[q] * sg * (1.0f + gg[q] * (1.0f - sg));
+          du[q] = a[q] * gg[q] * sg;
+        }
+        dgw[jj][0] = pack_bf16x2(dg[0], dg[1]);
+        dgw[jj][1] = pack_bf16x2(dg[2], dg[3]);
+        duw[jj][0] = pack_bf16x2(du[0], du[1]);
+        duw[jj][1] = pack_bf16x2(du[2], du[3]);
+        const int n = it.n0 + wn * WN + (j0 + jj) * 16 + 4 * lg;
+        if (n >= p.N) continue;
+        const int64_t off = row * p.N + n;
+        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(dgw[jj][0], dgw[jj][1]);
+        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(duw[jj][0], duw[jj][1]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kDswFrags; jj += 2) {
+        uint32_t qw[2][2];
+        int code[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t(&w)[kDswFrags][2] = h ? duw : dgw;
+          const float v[8] = {bf16lo(w[jj][0]),     bf16hi(w[jj][0]),     bf16lo(w[jj][1]),
+                              bf16hi(w[jj][1]),     bf16lo(w[jj + 1][0]), bf16hi(w[jj + 1][0]),
+                              bf16lo(w[jj + 1][1]), bf16hi(w[jj + 1][1])};
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          code[h] = e8m0_code(amax);
+          qw[h][0] = e4m3x4(v[0], v[1], v[2], v[3], code[h] - 127);
+          qw[h][1] = e4m3x4(v[4], v[5], v[6], v[7], code[h] - 127);
+        }
+        const int nb = it.n0 + wn * WN + (j0 + jj) * 16;
+        if (nb >= p.N) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint8_t* qrow = p.hq + row * N2 + h * p.N + nb + 4 * lg;
+          *reinterpret_cast<uint32_t*>(qrow) = qw[h][0];
+          *reinterpret_cast<uint32_t*>(qrow + 16) = qw[h][1];
+          if (lg == 0) p.hs[row * (N2 / 32) + (h * p.N + nb) / 32] = (uint8_t)code[h];
+        }
+      }
+    }
+  }
+}
+
 // Run the current item (its prologue already issued), then claim the next
 // one and issue its prologue before storing this item's outputs, so the
 // loads of the next tile overlap this epilogue.
-template <class C, bool DUAL>
+template <class C, bool DUAL, bool DSW = false>
 __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem, uint32_t lds0, int* s_item,
                                          int& li, int xcd, const Item& it) {
   tile::Src<C> src;
@@ -239,11 +341,12 @@ __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem
     else if (!C::MX && next.tiny) start<TinyTile<DUAL, false>>(p, lds0, next);
     else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
   }
-  epilogue<C>(p, it, acc);
+  if constexpr (DSW) epilogue_dsw<C>(p, it, acc);
+  else epilogue<C>(p, it, acc);
   return next;
 }
 
-template <bool DUAL, bool MX>
+template <bool DUAL, bool MX, bool DSW = false>
 __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<MX>()];
   __shared__ int s_item;
@@ -259,16 +362,16 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   else if (!MX && it.tiny) start<Tiny>(p, lds0, it);
   else start<Small>(p, lds0, it);
   while (it.valid) {
-    if (it.big) it = run_item<Big, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
-    else if (!MX && it.tiny) it = run_item<Tiny, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
-    else it = run_item<Small, DUAL>(p, smem, lds0, &s_item, li, xcd, it);
+    if (it.big) it = run_item<Big, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
+    else if (!MX && it.tiny) it = run_item<Tiny, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
+    else it = run_item<Small, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
   }
 }
 
-template <bool DUAL, bool MX>
+template <bool DUAL, bool MX, bool DSW = false>
 hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
   plan_rows_kernel<<<1, 1024, 0, s>>>(p.offsets, p.E, p.n_tiles, plan, p.head);
-  auto kern = gemm_fwd_kernel<DUAL, MX>;
+  auto kern = gemm_fwd_kernel<DUAL, MX, DSW>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -547,6 +650,9 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // operands 16-byte aligned, scales 4-byte aligned.
 bool gemm_fwd_fast_ok(const GemmFwd& f, bool mx) {
   if (f.k_dim % (mx ? 128 : 64) || f.n_dim % (mx ? 32 : 16)) return false;
+  if (f.dswiglu && (!mx || f.swiglu || !aligned(f.g, 8) || !aligned(f.u, 8) || !aligned(f.c0, 8) ||
+                    !aligned(f.c1, 8) || !aligned(f.act_q, 4)))
+    return false;
   if (f.n_dim * f.k_dim * (mx ? 1 : 2) >= (int64_t(1) << 31)) return false;   // 32-bit DMA offsets
   if (!aligned(f.a, 16) || !aligned(f.b0, 16) || (f.swiglu && !aligned(f.b1, 16))) return false;
   if (mx && (!aligned(f.a_scales, 4) || !aligned(f.b0_scales, 4) || (f.swiglu && !aligned(f.b1_scales, 4))))
@@ -574,13 +680,16 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStrea
   p.c0 = (uint16_t*)f.c0;
   p.c1 = (uint16_t*)f.c1;
   p.c2 = (uint16_t*)f.act;
-  p.hq = (mx && f.swiglu) ? f.act_q : nullptr;   // bf16 callers quantize H separately
-  p.hs = (mx && f.swiglu) ? f.act_scales : nullptr;
+  p.hq = (mx && (f.swiglu || f.dswiglu)) ? f.act_q : nullptr;   // bf16 callers quantize H separately
+  p.hs = (mx && (f.swiglu || f.dswiglu)) ? f.act_scales : nullptr;
+  p.g = (const uint16_t*)f.g;
+  p.u = (const uint16_t*)f.u;
   p.head = ws;
   int32_t* plan = ws + kGemmHeadInts;
   p.plan = plan;
   const int ncol = f.swiglu ? BigTile<true>::NCOL : BigTile<false>::NCOL;
   p.n_tiles = (p.N + ncol - 1) / ncol;
+  if (mx && f.dswiglu) return run_fwd<false, true, true>(p, plan, s);
   if (mx) return f.swiglu ? run_fwd<true, true>(p, plan, s) : run_fwd<false, true>(p, plan, s);
   return f.swiglu ? run_fwd<true, false>(p, plan, s) : run_fwd<false, false>(p, plan, s);
 }

@@ -23,6 +23,13 @@ struct GemmFwd {
   uint8_t* act_q;
   uint8_t* act_scales;
   bool swiglu;
+  // MXFP8 data gradient of the down projection (single B): the epilogue takes
+  // acc = dH, applies the SwiGLU backward with the saved g/u [rows][n_dim],
+  // stores dG in c0 and dU in c1 (bf16) and [dG | dU] quantized row-wise in
+  // act_q [rows][2 n_dim] / act_scales [rows][2 n_dim / 32]
+  bool dswiglu = false;
+  const void* g = nullptr;
+  const void* u = nullptr;
 };
 
 // backward grouped GEMM request (bf16)
@@ -90,7 +97,14 @@ hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const f
                               float* dprob, hipStream_t s,
                          const int32_t* shared_row0 = nullptr);
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
-                                uint8_t* sc, hipStream_t s);
+                                uint8_t* sc, hipStream_t s, const int32_t* rows_end = nullptr);
+// src bf16 [batch][rows][cols] -> q[b][c][col0 + r] (row stride ld), quantized
+// along r; scales [b][c][(col0 + r) / 32] (row stride ld / 32)
+hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                                int64_t col0, uint8_t* q, uint8_t* sc, hipStream_t s);
+// bf16 [rows][cols] from E4M3 + E8M0 row-wise blocks; rows >= *rows_end skipped
+hipError_t launch_dequant_rows(const uint8_t* q, const uint8_t* sc, int64_t rows, int64_t cols,
+                               const int32_t* rows_end, void* out, hipStream_t s);
 hipError_t launch_swiglu(const void* g, const void* u, int64_t rows, int64_t n, void* h,
                          uint8_t* hq, uint8_t* hs, hipStream_t s);
 

@@ -370,14 +370,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
   }
 }
 
-// row-wise MXFP8 quantization of bf16 [rows][cols]; one wave per row
+// row-wise MXFP8 quantization of bf16 [rows][cols]; one wave per row.  Rows
+// at or past *rows_end (when given) are skipped.
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ src,
                                                             int64_t rows, int cols,
                                                             uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ sc) {
+                                                            uint8_t* __restrict__ sc,
+                                                            const int32_t* __restrict__ rows_end) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  if (r >= rows || (rows_end && r >= *rows_end)) return;
   const int nvec = cols >> 3;
   const uint16_t* s = src + r * cols;
   for (int v0 = 0; v0 < nvec; v0 += kWave) {
@@ -493,9 +495,9 @@ hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const f
 }
 
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
-                                uint8_t* sc, hipStream_t s) {
+                                uint8_t* sc, hipStream_t s, const int32_t* rows_end) {
   if (rows == 0) return hipSuccess;
-  quantize_rows_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc);
+  quantize_rows_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc, rows_end);
   return hipGetLastError();
 }
 

@@ -1,0 +1,121 @@
+// MXFP8 conversions of the backward pass (gfx950).
+//
+// A matrix used in both orientations is quantized twice, each copy along its
+// own contraction dimension and each from the bf16 source, never one copy
+// from the other (KOSMOS section 2.2).  The forward's weights are quantized
+// row-wise (along D for gate/up, along H for down); the data gradients need
+// the transposed copies quantized along the other dimension (OLMo-core
+// Appendix A, A.13: the right-hand operand prequantized for dgrad), which
+// quantize_cols_kernel produces.  The weight gradients take bf16 operands:
+// the saved MXFP8 activations are dequantized (A.13's wgrad policy), which
+// dequant_rows_kernel does exactly (an E4M3 value times a power of two has at
+// most four significant bits, so it is a bf16 value).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+// Column-wise quantization with transpose:
+//   src bf16 [B][R][C]  ->  q[b][c][col0 + r] (row stride ld bytes),
+//   blocks of 32 consecutive r of one column c, scale [b][c][(col0 + r) / 32]
+//   (row stride ld / 32).
+// A 256-thread block moves a 128 (r) x 64 (c) tile through LDS: the loads are
+// 16-byte row pieces of src; thread (blk, c) then quantizes column c's 32
+// elements r0 + 32 blk .. + 31 and stores 32 code bytes and one scale.
+constexpr int kQR = 128, kQC = 64, kQPad = 8;
+
+__global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ src, int64_t R,
+                                                            int64_t C, int64_t ld, int64_t col0,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kQR][kQC + kQPad];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kQR, c0 = (int64_t)blockIdx.x * kQC;
+  const uint16_t* s = src + b * R * C;
+  const int t = threadIdx.x;
+  // load: thread t takes piece t % 8 (8 columns) of rows t / 8 + 32 i
+#pragma unroll
+  for (int i = 0; i < kQR / 32; ++i) {
+    const int rr = t / 8 + 32 * i, cc = (t % 8) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + rr < R && c0 + cc < C) v = ldg16(s + (r0 + rr) * C + c0 + cc);
+    *reinterpret_cast<uint4*>(&tile[rr][cc]) = v;
+  }
+  __syncthreads();
+  const int c = t % kQC, blk = t / kQC;
+  const int64_t r = r0 + 32 * blk;
+  if (c0 + c >= C || r >= R) return;
+  float f[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    f[i] = bf16_to_f32(tile[32 * blk + i][c]);
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+  const int code = e8m0_code(amax);
+  const int e = code - 127;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], e);
+  const int64_t qrow = (b * C + c0 + c) * ld;
+  uint8_t* dst = q + qrow + col0 + r;
+  stg16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+  stg16(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  sc[(b * C + c0 + c) * (ld / 32) + (col0 + r) / 32] = (uint8_t)code;
+}
+
+// E4M3FN code -> its value as fp32 (exact; codes 0x7F / 0xFF, NaN in E4M3FN,
+// are never produced by the quantizer).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t ef = (c >> 3) & 0xFu, m = c & 7u;
+  const float v = ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+}
+
+// bf16 [rows][cols] = E4M3 [rows][cols] x 2^(scale - 127); each lane converts
+// 16 codes (half a block) per pass, one wave per row.  Rows at or past
+// *rows_end (when given) are skipped.
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ sc, int64_t rows,
+                                                           int cols, const int32_t* __restrict__ rows_end,
+                                                           uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows || (rows_end && r >= *rows_end)) return;
+  const int nvec = cols >> 4;
+  for (int v = lane; v < nvec; v += kWave) {
+    const uint4 c = ldg16(q + r * cols + v * 16);
+    const float s = exp2i((int)sc[r * (cols >> 5) + (v >> 1)] - 127);
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = pack_bf16x2(e4m3_value(cw[i] & 0xFF) * s, e4m3_value((cw[i] >> 8) & 0xFF) * s);
+      o[2 * i + 1] = pack_bf16x2(e4m3_value((cw[i] >> 16) & 0xFF) * s, e4m3_value(cw[i] >> 24) * s);
+    }
+    uint16_t* dst = out + r * cols + v * 16;
+    stg16(dst, make_uint4(o[0], o[1], o[2], o[3]));
+    stg16(dst + 8, make_uint4(o[4], o[5], o[6], o[7]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                                int64_t col0, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + kQC - 1) / kQC), (unsigned)((rows + kQR - 1) / kQR), (unsigned)batch);
+  quantize_cols_kernel<<<grid, 256, 0, s>>>((const uint16_t*)src, rows, cols, ld, col0, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const uint8_t* q, const uint8_t* sc, int64_t rows, int64_t cols,
+                               const int32_t* rows_end, void* out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  dequant_rows_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(q, sc, rows, (int)cols, rows_end,
+                                                                  (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

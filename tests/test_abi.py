@@ -45,6 +45,12 @@ def test_status_strings_and_rows_cap():
     assert lib.moe_rows_cap(C.byref(d)) == 131072
     assert lib.moe_workspace_size(M.MOE_OP_ROUTE, C.byref(d)) > 0
     assert lib.moe_workspace_size(M.MOE_OP_LAYER_BWD, C.byref(d)) > 2 * 131072 * 4096 * 2
+    # the MXFP8 backward also holds dY_d and [dG | dU] quantized and X_d dequantized
+    dm = M.dims(4096, 7168, 256, 8, 2048, align=32)
+    rc = 4096 * 8 + 256 * 31
+    extra = lib.moe_workspace_size(M.MOE_OP_LAYER_BWD_MXFP8, C.byref(dm)) - \
+        lib.moe_workspace_size(M.MOE_OP_LAYER_BWD, C.byref(dm))
+    assert extra >= rc * 7168 * (1 + 1 / 32 + 2) + rc * 2 * 2048 * (1 + 1 / 32)
 
 
 def _route(lib, d, logits=16, ws=16, wsb=1 << 20, p=16):
@@ -83,6 +89,17 @@ def test_null_align_workspace_errors():
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -1
     a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0, 2)             # unknown schedule
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -3
+    # column-wise quantization: rows % 32, cols % 8, ld % 32, col0 % 32, col0 + rows <= ld
+    qc = lib.moe_quantize_mxfp8_cols
+    for bad in ((1, 40, 48, 64, 0), (1, 64, 44, 64, 0), (1, 64, 48, 80, 0), (1, 64, 48, 128, 16),
+                (1, 64, 48, 96, 64), (-1, 64, 48, 64, 0)):
+        assert qc(16, *bad, 16, 16, None) == -2, bad
+    assert qc(24, 1, 64, 48, 64, 0, 16, 16, None) == -5
+    # MXFP8 layer backward: D % 128 and H % 64 (the block-scaled dgrads' steps)
+    gr = M.LayerGrads()
+    for D, H in ((96, 64), (128, 96)):
+        a = M.LayerArgs(M.dims(16, D, 8, 2, H, align=32), M.MOE_MXFP8)
+        assert lib.moe_layer_bwd(C.byref(a), C.byref(sv), 16, C.byref(gr), 16, 1 << 20, None) == -2, (D, H)
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -103,7 +120,7 @@ def test_struct_layouts_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     hdr = os.path.join(os.path.dirname(__file__), "..", "include", "moe_rocm.h")
     checks = {"moe_dims": (M.Dims, ["N", "renorm", "n_group", "topk_group"]),
-              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha"]),
+              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha", "wdt_q", "wgut_s"]),
               "moe_layer_saved": (M.LayerSaved, ["logits", "y", "aux"]),
               "moe_layer_grads": (M.LayerGrads, ["dx", "dlogits", "d_aux"]),
               "moe_gemm_fwd_args": (M.GemmFwdArgs, ["dtype", "act_scales"]),

@@ -265,6 +265,62 @@ def test_quantize_mxfp8_every_value_at_every_scale():
     assert np.array_equal(host(s), rs)
     assert np.array_equal(host(q), rq)
 
+def test_quantize_mxfp8_cols_every_value_at_every_scale():
+    """The column-wise quantizer on the same exhaustive blocks, each block laid
+    along a column (32 rows of src): bytes and scales equal the oracle's."""
+    blocks = []
+    for f in range(1, 255):
+        mags = np.arange(0, (f + 1) << 7, dtype=np.uint32)
+        members = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        members = np.concatenate([members, np.zeros((-len(members)) % 31, np.uint16)]).reshape(-1, 31)
+        amax = np.full((members.shape[0], 1), (f << 7) | 0x7F, np.uint16)
+        blocks.append(np.concatenate([amax, members], axis=1))
+    u = np.concatenate(blocks)                              # [blocks, 32]
+    u = np.concatenate([u, np.zeros(((-u.shape[0]) % 8, 32), np.uint16)])   # columns: a multiple of 8
+    src = np.ascontiguousarray(u.T)[None]                   # [1, 32, blocks]: a block per column
+    nb = u.shape[0]
+    print(f"quantize cols blocks={nb}", flush=True)
+    q = torch.empty((1, nb, 32), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((1, nb, 1), dtype=torch.uint8, device="cuda")
+    M.quantize_mxfp8_cols(dev_bf16(src), q, sc)
+    _sync()
+    rq, rs = O.quantize_mxfp8(u)
+    assert np.array_equal(host(sc)[0, :, 0], rs[:, 0])
+    assert np.array_equal(host(q)[0], rq)
+
+
+@pytest.mark.parametrize("B,R,C,ld,col0", [(3, 96, 200, 192, 96), (2, 160, 64, 160, 0), (1, 288, 328, 320, 32)])
+def test_quantize_mxfp8_cols_ragged_and_offset(B, R, C, ld, col0):
+    """Tails in both tile dimensions, a column offset inside a wider row:
+    exactly columns col0 .. col0 + R - 1 of each q row are written."""
+    print(f"quantize cols B={B} R={R} C={C} ld={ld} col0={col0}", flush=True)
+    src = S.random_bf16((B, R, C), 41, 1, std=2.0)
+    src[:, :32, :5] = 0                                     # all-zero blocks take scale code 0
+    q = torch.full((B, C, ld), 0xAB, dtype=torch.uint8, device="cuda")
+    sc = torch.full((B, C, ld // 32), 0xCD, dtype=torch.uint8, device="cuda")
+    M.quantize_mxfp8_cols(dev_bf16(src), q, sc, col0)
+    _sync()
+    qh, sh = host(q), host(sc)
+    for b in range(B):
+        rq, rs = O.quantize_mxfp8(np.ascontiguousarray(src[b].T))
+        assert np.array_equal(qh[b][:, col0:col0 + R], rq), b
+        assert np.array_equal(sh[b][:, col0 // 32:(col0 + R) // 32], rs), b
+    assert np.all(np.delete(qh, np.s_[col0:col0 + R], axis=2) == 0xAB)
+    assert np.all(np.delete(sh, np.s_[col0 // 32:(col0 + R) // 32], axis=2) == 0xCD)
+
+
+def test_weight_copies_for_dgrad_bit_exact():
+    """W_down^T along D and [W_gate^T | W_up^T] along H, from the bf16 weights."""
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_wt", N=8, D=384, E=5, K=2, H=160)
+    inp = S.make_inputs(wl, 42)
+    print("weight copies for dgrad", flush=True)
+    q = M.quantize_weights_mxfp8_dgrad(dev_bf16(inp.w_gate), dev_bf16(inp.w_up), dev_bf16(inp.w_down))
+    _sync()
+    ref = O.quantize_weights_mxfp8_dgrad(inp.w_gate, inp.w_up, inp.w_down)
+    for k in ref:
+        assert np.array_equal(host(q[k]), ref[k]), k
+
+
 def test_swiglu_standalone():
     rows, n = 333, 160
     g = S.random_bf16((rows, n), 23, 1, std=3.0)

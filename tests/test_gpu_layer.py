@@ -299,6 +299,92 @@ def test_layer_shared_expert_mxfp8():
     assert rel_frobenius(vals(out), ref["out"]) <= 3e-2
 
 
+MX_BWD_CASES = {
+    "mx_16e": dict(N=256, D=256, E=16, K=4, H=128),
+    "mx_32e": dict(N=300, D=512, E=32, K=8, H=256),
+    "mx_8e_ragged": dict(N=333, D=384, E=8, K=2, H=192),
+}
+
+
+@pytest.mark.parametrize("shared,router", [(False, False), (True, False), (False, True)])
+@pytest.mark.parametrize("name", list(MX_BWD_CASES))
+def test_layer_bwd_mxfp8(name, shared, router):
+    """MXFP8 backward through moe_layer_bwd against the oracle's: block-scaled
+    dgrads, bf16 wgrads on dequantized activations.
+
+    Tolerances (relative Frobenius): the quantized operands of the down dgrad
+    (dY_d from the same bf16 values, the weight copies) are identical on both
+    sides, so dG and dU differ only by fp32-vs-float64 accumulation and their
+    bf16 rounding (2^-9 relative), and with them the gate/up weight gradients:
+    5e-3.  dX_d re-quantizes [dG | dU] and dW_down reads the forward's
+    quantized H: where the two sides' bf16 inputs differ in the last bit, an
+    E4M3 code can move by one step (2^-4 of that element) on a small fraction
+    of elements, so dx, dw_down and dprob (from the forward's Y) get 1e-2;
+    the router's gradients follow dprob."""
+    cfg = MX_BWD_CASES[name]
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], name, bwd=True, **cfg)
+    print(f"layer bwd mxfp8 {name} shared={shared} router={router}", flush=True)
+    inp = S.make_inputs(wl, 31)
+    wg, wu, wd = _with_shared(inp, 31) if shared else (inp.w_gate, inp.w_up, inp.w_down)
+    q = O.quantize_weights_mxfp8(wg, wu, wd)
+    qt = O.quantize_weights_mxfp8_dgrad(wg, wu, wd)
+    w = M.LayerWeights(w_r=dev_bf16(inp.w_r), bias=dev(inp.bias) if inp.bias is not None else None)
+    w.wq = {k: dev(v) for k, v in q.items()}
+    w.wq.update(M.quantize_weights_mxfp8_dgrad(dev_bf16(wg), dev_bf16(wu), dev_bf16(wd)))
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, with_bwd=True, router_bwd=router)
+    x = dev_bf16(inp.x)
+    layer.forward(x)
+    g = layer.backward(x, dev_bf16(inp.dout))
+    torch.cuda.synchronize()
+    for k in qt:
+        assert np.array_equal(host(w.wq[k]), qt[k]), k
+    ref = O.layer_fwd_mxfp8(inp.x, inp.w_r, inp.bias, q, wl.K, n_shared=1 if shared else 0)
+    same = check_routing(layer.saved, ref, wl.K)
+    if not np.all(same):
+        pytest.skip("near-tie routing flip for this seed; forward parity covers it")
+    rb = O.layer_bwd_mxfp8(ref, inp.dout, qt)
+    for k, tol in (("dw_gate", 5e-3), ("dw_up", 5e-3), ("dw_down", 1e-2), ("dprob", 1e-2)):
+        got = vals(g[k]) if k != "dprob" else host(g[k])
+        assert np.all(np.isfinite(got)), k
+        err = rel_frobenius(got, rb[k])
+        print(f"  {k} rel {err:.2e}", flush=True)
+        assert err <= tol, (k, err)
+    for e in np.nonzero(ref["counts"] == 0)[0]:
+        assert np.all(bits(g["dw_gate"])[e] == 0)
+    dx_ref = rb["dx"]
+    if router:
+        rr = O.router_bwd(ref["logits"], ref["topk_idx"], rb["dprob"], inp.x, inp.w_r, 0)
+        dx_ref = O.values(rb["dx"]) + rr["dx_r"]
+        err = rel_frobenius(host(g["dlogits"]), rr["dlogits"])
+        err_w = rel_frobenius(vals(g["dw_r"]), rr["dw_r"])
+        print(f"  dlogits rel {err:.2e}  dw_r rel {err_w:.2e}", flush=True)
+        assert err <= 1e-2, ("dlogits", err)
+        assert err_w <= 1e-2, ("dw_r", err_w)
+    err = rel_frobenius(vals(g["dx"]), dx_ref)
+    print(f"  dx rel {err:.2e}", flush=True)
+    assert err <= 1e-2, ("dx", err)
+
+
+def test_layer_bwd_mxfp8_deterministic():
+    """Two MXFP8 backward calls give the same bits (the persistent GEMMs'
+    results do not depend on which workgroup claims a tile)."""
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_det", N=400, D=256, E=16, K=4, H=128, bwd=True)
+    print("layer bwd mxfp8 determinism", flush=True)
+    inp = S.make_inputs(wl, 32)
+    w = M.LayerWeights(w_r=dev_bf16(inp.w_r), bias=dev(inp.bias) if inp.bias is not None else None)
+    wg, wu, wd = dev_bf16(inp.w_gate), dev_bf16(inp.w_up), dev_bf16(inp.w_down)
+    w.wq = M.quantize_weights_mxfp8(wg, wu, wd)
+    w.wq.update(M.quantize_weights_mxfp8_dgrad(wg, wu, wd))
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, with_bwd=True)
+    x, dout = dev_bf16(inp.x), dev_bf16(inp.dout)
+    layer.forward(x)
+    g1 = {k: v.clone() for k, v in layer.backward(x, dout).items()}
+    g2 = layer.backward(x, dout)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k].view(torch.uint8), g2[k].view(torch.uint8)), k
+
+
 @pytest.mark.parametrize("N,D,E,K,H", [(256, 256, 16, 4, 128), (300, 512, 32, 8, 256)])
 def test_layer_fwd_mxfp8(N, D, E, K, H):
     wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_small", N=N, D=D, E=E, K=K, H=H)
