@@ -198,7 +198,7 @@ struct WgradParams {
 using WgTile = tile::TileCfg<256, 256, 2, 4, 2, false, false, true, true>;   // 2 x 64 KB
 
 struct WgItem {
-  int e, r0, rows, m0, n0;
+  int e, r0, rows, m0, n0, idx;   // idx: the item's index within its expert
   bool valid;
 };
 
@@ -212,7 +212,8 @@ __device__ __forceinline__ WgItem claim_wg(const WgradParams& p, int* s_item, in
   it.r0 = p.offsets[it.e];
   it.rows = p.offsets[it.e + 1] - it.r0;
   int mt, nt;
-  superblock_decode(item - ei * per_e, p.m_tiles, p.n_tiles, mt, nt);
+  it.idx = item - ei * per_e;
+  superblock_decode(it.idx, p.m_tiles, p.n_tiles, mt, nt);
   it.m0 = mt * WgTile::BM;
   it.n0 = nt * WgTile::BN;
   it.valid = true;
@@ -250,27 +251,67 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
   const int64_t cbase = (int64_t)it.e * p.M * p.N;
+  if (p.f32) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const int m = it.m0 + wm * C::WM + i * 16 + l16;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+        if (n >= p.N) continue;
+        const f32x4_t a = acc[i][j];
+        *reinterpret_cast<float4*>(static_cast<float*>(p.c) + cbase + (int64_t)m * p.N + n) =
+            make_float4(a[0], a[1], a[2], a[3]);
+      }
+    }
+    return;
+  }
+  // bf16: lane groups 2q and 2q+1 trade half of fragments j and j+1, so each
+  // lane stores 8 adjacent columns (16 bytes): group 2q columns 8q .. 8q+7 of
+  // fragment j, group 2q+1 the same columns of fragment j+1.  N % 16 == 0, so
+  // a fragment is all in or all out.
+  const bool odd = lg & 1;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int m = it.m0 + wm * C::WM + i * 16 + l16;
-    if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
-      if (n >= p.N) continue;
-      const f32x4_t a = acc[i][j];
-      const int64_t off = cbase + (int64_t)m * p.N + n;
-      if (p.f32) *reinterpret_cast<float4*>(static_cast<float*>(p.c) + off) = make_float4(a[0], a[1], a[2], a[3]);
-      else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + off) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    for (int j = 0; j < C::TN; j += 2) {
+      const f32x4_t a = acc[i][j], b = acc[i][j + 1];
+      const uint32_t a0 = pack_bf16x2(a[0], a[1]), a1 = pack_bf16x2(a[2], a[3]);
+      const uint32_t b0 = pack_bf16x2(b[0], b[1]), b1 = pack_bf16x2(b[2], b[3]);
+      // even groups send their fragment j+1 values, odd groups their fragment j values
+      const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
+      const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
+      const uint4 v = odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+      const int n = it.n0 + wn * C::WN + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
+      if (m >= p.M || n >= p.N) continue;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.c) + cbase + (int64_t)m * p.N + n) = v;
     }
   }
+}
+
+// An expert without rows has a zero gradient.  Its items do not store tiles:
+// item idx clears bytes [idx, idx + 1) x (one tile's bytes) of the expert's
+// dW as a flat range, 16 bytes per lane, so every wave writes whole
+// contiguous kilobytes (the expert's items cover at least its M x N values).
+__device__ __forceinline__ void zero_wg(const WgradParams& p, const WgItem& it) {
+  const int64_t esz = p.f32 ? 4 : 2;
+  const int64_t total = (int64_t)p.M * p.N * esz;   // a multiple of 32 bytes (N % 16 == 0)
+  const int64_t chunk = (int64_t)WgTile::BM * WgTile::BN * esz;
+  const int64_t c0 = (int64_t)it.idx * chunk;
+  const int64_t c1 = min(c0 + chunk, total);
+  uint8_t* base = static_cast<uint8_t*>(p.c) + (int64_t)it.e * total;
+  for (int64_t off = c0 + (int64_t)threadIdx.x * 16; off < c1; off += (int64_t)blockDim.x * 16)
+    *reinterpret_cast<uint4*>(base + off) = make_uint4(0, 0, 0, 0);
 }
 
 // Items are claimed one ahead and their steps stream through the ring
 // without a drain between tiles: a tile with few rows (one or two steps)
 // would otherwise pay a claim, a full load latency and its stores in series.
-// Tiles of experts without rows have no steps: they issue no loads and store
-// zeros, and the tile after one issues its own first step.
+// Tiles of experts without rows have no steps: they issue no loads and clear
+// a flat range of the expert's gradient, and the tile after one issues its
+// own first step.
 __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[WgTile::LDS];
   __shared__ int s_item;
@@ -296,7 +337,8 @@ __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
     tile::mainloop_b_stream<WgTile>(smem, lds0, src, nk, it.rows - 64 * (nk - 1), ns, stream, g0, acc);
     // claim the tile after next while next's first step is in flight
     const WgItem after = next.valid ? claim_wg(p, &s_item, xcd) : WgItem{};
-    epilogue_wg(p, it, acc);
+    if (nk > 0) epilogue_wg(p, it, acc);
+    else zero_wg(p, it);
     g0 += nk;
     issued = stream;
     it = next;

@@ -258,3 +258,93 @@ def test_full_size_backward_qwen3():
         assert_bf16_close(vals(g["dw_down"][int(e)]), eb["dw_down"][0], f"dw_down[{e}]")
         assert_bf16_close(vals(g["dw_gate"][int(e)]), eb["dw_gate"][0], f"dw_gate[{e}]")
         assert_bf16_close(vals(g["dw_up"][int(e)]), eb["dw_up"][0], f"dw_up[{e}]")
+
+
+def test_full_size_backward_mxfp8():
+    """MXFP8 backward at the DeepSeek-V3-shaped size in the launch configuration
+    of bench.py --backward (staged forward, then moe_layer_bwd with the router
+    backward; dOut N(0, 1) bf16 from the seed).  dx (with the router's dX_r)
+    and dprob on sampled tokens, weight gradients of the two smallest experts
+    in full, the data gradients' weight copies of every expert involved
+    bit-exact.  Relative Frobenius bounds as in the small-size MXFP8 backward
+    tests: 5e-3 for the gate/up weight gradients, 1e-2 for the rest."""
+    wl = S.WORKLOADS["dsv3_mxfp8"]
+    print("full-size backward dsv3_mxfp8", flush=True)
+    inp = S.make_inputs(wl, 0)
+    x, w, drop = bench.device_inputs(M, inp, True, torch, backward=True)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, drop=drop, renorm=wl.renorm, with_bwd=True, router_bwd=True)
+    bench.StagedForward(M, layer, x).run()
+    dout = S.random_bf16((wl.N, wl.D), 0, 9)
+    g = layer.backward(x, torch.from_numpy(dout.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    sv = layer.saved
+    idx, prob, c, o, d, r = _check_route(wl, inp, sv)
+    Lg = host(sv["logits"])
+    qcache = {}
+
+    def expert_q(e):
+        if e not in qcache:
+            sl = slice(e, e + 1)
+            q = O.quantize_weights_mxfp8(inp.w_gate[sl], inp.w_up[sl], inp.w_down[sl])
+            q.update(O.quantize_weights_mxfp8_dgrad(inp.w_gate[sl], inp.w_up[sl], inp.w_down[sl]))
+            for k in q:
+                assert np.array_equal(host(w.wq[k][e]), q[k][0]), (e, k)
+            qcache[e] = q
+        return qcache[e]
+
+    def expert_bwd(e, xr, dyd):
+        """The oracle's MXFP8 forward and backward of expert e on the given rows."""
+        q = expert_q(e)
+        xq, xs = O.quantize_mxfp8(xr)
+        G, U, Hh, hq, hs, Y = O.expert_mlp_mxfp8(xq, xs, q["wg_q"][0], q["wg_s"][0], q["wu_q"][0],
+                                                 q["wu_s"][0], q["wd_q"][0], q["wd_s"][0])
+        eb = O.experts_bwd_mxfp8(dyd, xq, xs, G, U, hq, hs, np.array([0, len(xr)]),
+                                 {k: q[k] for k in ("wdt_q", "wdt_s", "wgut_q", "wgut_s")})
+        return Y, eb
+
+    # the oracle's cost is per expert (its weights), so the sampled routes of
+    # one expert go through it together (rows of the GEMMs do not interact)
+    tokens = _sample_tokens(idx, d, c, n=2, max_experts=6)
+    routes = {}
+    for t in tokens:
+        for k in range(wl.K):
+            if d[t, k] >= 0:
+                routes.setdefault(int(idx[t, k]), []).append((t, k))
+    dxd, yrow = {}, {}
+    for e, tk in routes.items():
+        rows_t = np.array([t for t, _ in tk])
+        wk = np.array([prob[t, k] for t, k in tk], np.float32)
+        dyd = O.round_bf16(O.round_f32(wk.astype(np.float64)[:, None] * O.values(dout[rows_t])))
+        Y, eb = expert_bwd(e, O.values(inp.x[rows_t]), dyd)
+        for j, key in enumerate(tk):
+            dxd[key], yrow[key] = eb["dxd"][j], Y[j]
+    dx_ref, dprob_ref = [], []
+    for t in tokens:
+        acc = np.zeros(wl.D)
+        dp = np.zeros(wl.K)
+        for k in range(wl.K):
+            if d[t, k] >= 0:
+                acc += dxd[(t, k)]
+                dp[k] = np.sum(O.values(dout[t]) * yrow[(t, k)])
+        rr = O.router_bwd(Lg[t:t + 1], idx[t:t + 1], dp[None].astype(np.float32), inp.x[t:t + 1], inp.w_r,
+                          wl.renorm)
+        dx_ref.append(acc + rr["dx_r"][0])
+        dprob_ref.append(dp)
+    for name, got, ref in (("dx", vals(g["dx"])[tokens], np.array(dx_ref)),
+                           ("dprob", host(g["dprob"])[tokens], np.array(dprob_ref))):
+        err = rel_frobenius(got, ref)
+        print(f"  {name} rel {err:.2e}", flush=True)
+        assert err <= 1e-2, (name, err)
+    # weight gradients of the two smallest experts, all their rows recomputed
+    order = np.argsort(np.where(c > 0, c, np.iinfo(np.int32).max))[:2]
+    for e in order:
+        seg = r[o[e]:o[e] + c[e]]
+        tok, kk = seg // wl.K, seg % wl.K
+        dyd = O.round_bf16(O.round_f32(prob[tok, kk].astype(np.float64)[:, None] * O.values(dout[tok])))
+        _, eb = expert_bwd(int(e), O.values(inp.x[tok]), dyd)
+        for name, tol in (("dw_gate", 5e-3), ("dw_up", 5e-3), ("dw_down", 1e-2)):
+            err = rel_frobenius(vals(g[name][int(e)]), eb[name][0])
+            print(f"  {name}[{e}] rel {err:.2e}", flush=True)
+            assert err <= tol, (name, int(e), err)
+    for e in np.nonzero(c == 0)[0][:8]:
+        assert not bits(g["dw_down"][int(e)]).any()
