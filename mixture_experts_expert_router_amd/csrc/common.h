@@ -79,6 +79,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// MFMA output fragments hold, per lane, 4 adjacent columns of one row (lane
+// group lg = lane / 16 has columns 4 lg .. 4 lg + 3 of a 16-column fragment).
+// For two adjacent fragments j, j+1 (packed bf16 words a0 a1 and b0 b1), lane
+// groups 2q and 2q+1 trade halves so that each lane holds 8 adjacent columns:
+// group 2q columns 8q .. 8q+7 of fragment j, group 2q+1 the same of fragment
+// j+1.  One 16-byte store per lane then covers the pair.  Every lane of the
+// wave must take part (the partner is lane ^ 16, same row).
+__device__ __forceinline__ uint4 frag_pair_16b(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, bool odd) {
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
+  const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
+  return odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -94,12 +94,17 @@ __device__ __forceinline__ void epilogue_dg(const DgradParams& p, const Item& it
     const int64_t row = it.m_start + wm * C::WM + i * 16 + l16;
     if (row >= it.m1) continue;
     if constexpr (!SWB) {
+      // 16-byte stores of fragment pairs (frag_pair_16b); N % 16 == 0
+      static_assert(C::TN % 2 == 0, "fragment pairs");
+      const bool odd = lg & 1;
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
+      for (int j = 0; j < C::TN; j += 2) {
+        const f32x4_t a = acc[i][j], b = acc[i][j + 1];
+        const uint4 v = frag_pair_16b(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                      pack_bf16x2(b[2], b[3]), odd);
+        const int n = it.n0 + wn * C::WN + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
         if (n >= p.N) continue;
-        const f32x4_t a = acc[i][j];
-        *reinterpret_cast<uint2*>(p.c0 + row * p.N + n) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+        *reinterpret_cast<uint4*>(p.c0 + row * p.N + n) = v;
       }
     } else {
       // the saved G and U of the whole fragment row first, so their loads
@@ -267,10 +272,8 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
     }
     return;
   }
-  // bf16: lane groups 2q and 2q+1 trade half of fragments j and j+1, so each
-  // lane stores 8 adjacent columns (16 bytes): group 2q columns 8q .. 8q+7 of
-  // fragment j, group 2q+1 the same columns of fragment j+1.  N % 16 == 0, so
-  // a fragment is all in or all out.
+  // bf16: 16-byte stores of fragment pairs (frag_pair_16b); N % 16 == 0, so
+  // a fragment is all in or all out
   const bool odd = lg & 1;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
@@ -278,12 +281,8 @@ __device__ __forceinline__ void epilogue_wg(const WgradParams& p, const WgItem& 
 #pragma unroll
     for (int j = 0; j < C::TN; j += 2) {
       const f32x4_t a = acc[i][j], b = acc[i][j + 1];
-      const uint32_t a0 = pack_bf16x2(a[0], a[1]), a1 = pack_bf16x2(a[2], a[3]);
-      const uint32_t b0 = pack_bf16x2(b[0], b[1]), b1 = pack_bf16x2(b[2], b[3]);
-      // even groups send their fragment j+1 values, odd groups their fragment j values
-      const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
-      const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
-      const uint4 v = odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+      const uint4 v = frag_pair_16b(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                    pack_bf16x2(b[2], b[3]), odd);
       const int n = it.n0 + wn * C::WN + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
       if (m >= p.M || n >= p.N) continue;
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.c) + cbase + (int64_t)m * p.N + n) = v;

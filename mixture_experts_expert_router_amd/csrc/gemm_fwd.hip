@@ -170,6 +170,7 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
+  static_assert(TN % 2 == 0 && (!C::DUAL || (TN / 2) % 2 == 0), "fragment pairs");
   // lane holds row wm*WM + i*16 + l16, columns 4*lg .. 4*lg+3 of its
   // 16-column fragment
 #pragma unroll
@@ -177,35 +178,47 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
     const int m = wm * WM + i * 16 + l16;
     if (it.m_start + m >= it.m1) continue;
     const int64_t row = it.m_start + m;
+    const bool odd = lg & 1;
     if (!C::DUAL) {
+      // 16-byte stores of fragment pairs (frag_pair_16b); N % 16 == 0
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = it.n0 + wn * WN + j * 16 + 4 * lg;
+      for (int j = 0; j < TN; j += 2) {
+        const f32x4_t a = acc[i][j], b = acc[i][j + 1];
+        const uint4 v = frag_pair_16b(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                      pack_bf16x2(b[2], b[3]), odd);
+        const int n = it.n0 + wn * WN + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
         if (n >= p.N) continue;
-        const f32x4_t a = acc[i][j];
-        *reinterpret_cast<uint2*>(p.c0 + row * p.N + n) =
-            make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+        *reinterpret_cast<uint4*>(p.c0 + row * p.N + n) = v;
       }
     } else {
-      uint32_t hw[TN / 2][2];
+      uint32_t gw[TN / 2][2], uw[TN / 2][2], hw[TN / 2][2];
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
-        const int n = it.n0 + wn * (WN / 2) + j * 16 + 4 * lg;
         const f32x4_t a = acc[i][j], b = acc[i][j + TN / 2];
-        const uint32_t gw0 = pack_bf16x2(a[0], a[1]), gw1 = pack_bf16x2(a[2], a[3]);
-        const uint32_t uw0 = pack_bf16x2(b[0], b[1]), uw1 = pack_bf16x2(b[2], b[3]);
-        const float g0 = bf16lo(gw0), g1 = bf16hi(gw0), g2 = bf16lo(gw1), g3 = bf16hi(gw1);
-        const float h0 = g0 * sigmoidf_(g0) * bf16lo(uw0);
-        const float h1 = g1 * sigmoidf_(g1) * bf16hi(uw0);
-        const float h2 = g2 * sigmoidf_(g2) * bf16lo(uw1);
-        const float h3 = g3 * sigmoidf_(g3) * bf16hi(uw1);
+        gw[j][0] = pack_bf16x2(a[0], a[1]);
+        gw[j][1] = pack_bf16x2(a[2], a[3]);
+        uw[j][0] = pack_bf16x2(b[0], b[1]);
+        uw[j][1] = pack_bf16x2(b[2], b[3]);
+        const float g0 = bf16lo(gw[j][0]), g1 = bf16hi(gw[j][0]), g2 = bf16lo(gw[j][1]), g3 = bf16hi(gw[j][1]);
+        const float h0 = g0 * sigmoidf_(g0) * bf16lo(uw[j][0]);
+        const float h1 = g1 * sigmoidf_(g1) * bf16hi(uw[j][0]);
+        const float h2 = g2 * sigmoidf_(g2) * bf16lo(uw[j][1]);
+        const float h3 = g3 * sigmoidf_(g3) * bf16hi(uw[j][1]);
         hw[j][0] = pack_bf16x2(h0, h1);
         hw[j][1] = pack_bf16x2(h2, h3);
+      }
+      // G, U and H as 16-byte stores of fragment pairs (frag_pair_16b)
+#pragma unroll
+      for (int j = 0; j < TN / 2; j += 2) {
+        const uint4 gv = frag_pair_16b(gw[j][0], gw[j][1], gw[j + 1][0], gw[j + 1][1], odd);
+        const uint4 uv = frag_pair_16b(uw[j][0], uw[j][1], uw[j + 1][0], uw[j + 1][1], odd);
+        const uint4 hv = frag_pair_16b(hw[j][0], hw[j][1], hw[j + 1][0], hw[j + 1][1], odd);
+        const int n = it.n0 + wn * (WN / 2) + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
         if (n >= p.N) continue;
         const int64_t off = row * p.N + n;
-        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(gw0, gw1);
-        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(uw0, uw1);
-        *reinterpret_cast<uint2*>(p.c2 + off) = make_uint2(hw[j][0], hw[j][1]);
+        *reinterpret_cast<uint4*>(p.c0 + off) = gv;
+        *reinterpret_cast<uint4*>(p.c1 + off) = uv;
+        *reinterpret_cast<uint4*>(p.c2 + off) = hv;
       }
       if (p.hq) {
         // a 32-column block of H is fragments (j, j+1) over the four lane
