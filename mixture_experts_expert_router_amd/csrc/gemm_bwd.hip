@@ -107,36 +107,49 @@ __device__ __forceinline__ void epilogue_dg(const DgradParams& p, const Item& it
         *reinterpret_cast<uint4*>(p.c0 + row * p.N + n) = v;
       }
     } else {
-      // the saved G and U of the whole fragment row first, so their loads
-      // overlap instead of waiting one fragment at a time
-      uint2 gw[C::TN], uw[C::TN];
+      // fragment pairs in the 16-byte layout of frag_pair_16b: the lane's 8
+      // columns of dH come from its own 4 and its partner's 4 (lane ^ 16),
+      // and G, U, dG, dU move as 16 bytes per lane.  The saved G and U of the
+      // whole fragment row are loaded first, so their loads overlap.
+      static_assert(C::TN % 2 == 0, "fragment pairs");
+      const bool odd = lg & 1;
+      uint4 gv[C::TN / 2], uv[C::TN / 2];
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
-        gw[j] = uw[j] = make_uint2(0, 0);
+      for (int jp = 0; jp < C::TN / 2; ++jp) {
+        const int n = it.n0 + wn * C::WN + (2 * jp + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
+        gv[jp] = uv[jp] = make_uint4(0, 0, 0, 0);
         if (n < p.N) {
-          gw[j] = *reinterpret_cast<const uint2*>(p.g + row * p.N + n);
-          uw[j] = *reinterpret_cast<const uint2*>(p.u + row * p.N + n);
+          gv[jp] = ldg16(p.g + row * p.N + n);
+          uv[jp] = ldg16(p.u + row * p.N + n);
         }
       }
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int n = it.n0 + wn * C::WN + j * 16 + 4 * lg;
-        if (n >= p.N) continue;
-        const f32x4_t a = acc[i][j];
-        const int64_t off = row * p.N + n;
-        // a = dH; dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G)
-        const float gg[4] = {bf16lo(gw[j].x), bf16hi(gw[j].x), bf16lo(gw[j].y), bf16hi(gw[j].y)};
-        const float uu[4] = {bf16lo(uw[j].x), bf16hi(uw[j].x), bf16lo(uw[j].y), bf16hi(uw[j].y)};
-        float dg[4], du[4];
+      for (int jp = 0; jp < C::TN / 2; ++jp) {
+        const f32x4_t a = acc[i][2 * jp], b = acc[i][2 * jp + 1];
+        float dh[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float s = sigmoidf_(gg[q]);
-          dg[q] = a[q] * uu[q] * s * (1.0f + gg[q] * (1.0f - s));
-          du[q] = a[q] * gg[q] * s;
+          const float r = __shfl_xor(odd ? a[q] : b[q], 16, 64);
+          dh[q] = odd ? r : a[q];
+          dh[4 + q] = odd ? b[q] : r;
         }
-        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        const int n = it.n0 + wn * C::WN + (2 * jp + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
+        if (n >= p.N) continue;
+        const uint32_t gw[4] = {gv[jp].x, gv[jp].y, gv[jp].z, gv[jp].w};
+        const uint32_t uw[4] = {uv[jp].x, uv[jp].y, uv[jp].z, uv[jp].w};
+        uint32_t dgw[4], duw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dH; dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G)
+          const float g0 = bf16lo(gw[w]), g1 = bf16hi(gw[w]), u0 = bf16lo(uw[w]), u1 = bf16hi(uw[w]);
+          const float s0 = sigmoidf_(g0), s1 = sigmoidf_(g1);
+          dgw[w] = pack_bf16x2(dh[2 * w] * u0 * s0 * (1.0f + g0 * (1.0f - s0)),
+                               dh[2 * w + 1] * u1 * s1 * (1.0f + g1 * (1.0f - s1)));
+          duw[w] = pack_bf16x2(dh[2 * w] * g0 * s0, dh[2 * w + 1] * g1 * s1);
+        }
+        const int64_t off = row * p.N + n;
+        stg16(p.c0 + off, make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]));
+        stg16(p.c1 + off, make_uint4(duw[0], duw[1], duw[2], duw[3]));
       }
     }
   }

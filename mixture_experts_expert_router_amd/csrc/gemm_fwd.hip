@@ -250,87 +250,91 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
 // MX data gradient of the down projection: acc = dH [rows][N] (N = H).
 // dG = dH U s (1 + G (1 - s)), dU = dH G s with s = sigmoid(G) from the saved
 // bf16 G and U, stored bf16 in c0 / c1; the bf16 values are then quantized
-// row-wise, dG into columns [0, N) and dU into [N, 2N) of hq / hs.  A 32-column
-// block is fragments (j, j+1) over the four lane groups of one row, as in the
-// H quantization above (N % 32 == 0: a block is all in or all out).
+// row-wise, dG into columns [0, N) and dU into [N, 2N) of hq / hs.  Fragment
+// pairs are handled in the 16-byte layout of frag_pair_16b (each lane owns 8
+// adjacent columns; its dH values come from its own fragment and its
+// partner's, lane ^ 16).  A 32-column block is one pair over the four lane
+// groups of a row, so a block's amax is two shuffles away (N % 32 == 0: a
+// block is all in or all out).
 template <class C>
 __device__ __forceinline__ void epilogue_dsw(const FwdParams& p, const Item& it,
                                              const f32x4_t (&acc)[C::TM][C::TN]) {
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
-  constexpr int kDswFrags = 4;
-  static_assert(!C::DUAL && TN % kDswFrags == 0, "single-B tile, whole 32-column blocks per wave");
+  static_assert(!C::DUAL && TN % 2 == 0, "single-B tile, fragment pairs");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   const int l16 = lane & 15, lg = lane >> 4;
+  const bool odd = lg & 1;
   const int64_t N2 = 2 * (int64_t)p.N;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = wm * WM + i * 16 + l16;
     if (it.m_start + m >= it.m1) continue;
     const int64_t row = it.m_start + m;
-    // four fragments (two 32-column blocks) at a time: their G and U loads are
-    // issued together, and fewer values stay live beside the accumulators
+    // two pairs (64 columns) at a time: their G and U loads are issued
+    // together, and fewer values stay live beside the accumulators
 #pragma unroll
-    for (int j0 = 0; j0 < TN; j0 += kDswFrags) {
-      uint2 gw[kDswFrags], uw[kDswFrags];
+    for (int j0 = 0; j0 < TN / 2; j0 += 2) {
+      constexpr int kPairs = 2;
+      static_assert((TN / 2) % kPairs == 0, "whole pair groups");
+      uint4 gv[kPairs], uv[kPairs];
 #pragma unroll
-      for (int jj = 0; jj < kDswFrags; ++jj) {
-        const int n = it.n0 + wn * WN + (j0 + jj) * 16 + 4 * lg;
-        gw[jj] = uw[jj] = make_uint2(0, 0);
+      for (int jj = 0; jj < kPairs; ++jj) {
+        const int n = it.n0 + wn * WN + (2 * (j0 + jj) + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
+        gv[jj] = uv[jj] = make_uint4(0, 0, 0, 0);
         if (n < p.N) {
-          gw[jj] = *reinterpret_cast<const uint2*>(p.g + row * p.N + n);
-          uw[jj] = *reinterpret_cast<const uint2*>(p.u + row * p.N + n);
+          gv[jj] = ldg16(p.g + row * p.N + n);
+          uv[jj] = ldg16(p.u + row * p.N + n);
         }
       }
-      uint32_t dgw[kDswFrags][2], duw[kDswFrags][2];
 #pragma unroll
-      for (int jj = 0; jj < kDswFrags; ++jj) {
-        const f32x4_t a = acc[i][j0 + jj];
-        const float gg[4] = {bf16lo(gw[jj].x), bf16hi(gw[jj].x), bf16lo(gw[jj].y), bf16hi(gw[jj].y)};
-        const float uu[4] = {bf16lo(uw[jj].x), bf16hi(uw[jj].x), bf16lo(uw[jj].y), bf16hi(uw[jj].y)};
-        float dg[4], du[4];
+      for (int jj = 0; jj < kPairs; ++jj) {
+        const int jp = j0 + jj;
+        const f32x4_t a = acc[i][2 * jp], b = acc[i][2 * jp + 1];
+        float dh[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float sg = sigmoidf_(gg[q]);
-          dg[q] = a[q] * uu[q] * sg * (1.0f + gg[q] * (1.0f - sg));
-          du[q] = a[q] * gg[q] * sg;
+          const float r = __shfl_xor(odd ? a[q] : b[q], 16, 64);
+          dh[q] = odd ? r : a[q];
+          dh[4 + q] = odd ? b[q] : r;
         }
-        dgw[jj][0] = pack_bf16x2(dg[0], dg[1]);
-        dgw[jj][1] = pack_bf16x2(dg[2], dg[3]);
-        duw[jj][0] = pack_bf16x2(du[0], du[1]);
-        duw[jj][1] = pack_bf16x2(du[2], du[3]);
-        const int n = it.n0 + wn * WN + (j0 + jj) * 16 + 4 * lg;
-        if (n >= p.N) continue;
-        const int64_t off = row * p.N + n;
-        *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(dgw[jj][0], dgw[jj][1]);
-        *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(duw[jj][0], duw[jj][1]);
-      }
+        const uint32_t gw[4] = {gv[jj].x, gv[jj].y, gv[jj].z, gv[jj].w};
+        const uint32_t uw[4] = {uv[jj].x, uv[jj].y, uv[jj].z, uv[jj].w};
+        uint32_t dgw[4], duw[4];
 #pragma unroll
-      for (int jj = 0; jj < kDswFrags; jj += 2) {
-        uint32_t qw[2][2];
+        for (int w = 0; w < 4; ++w) {
+          const float g0 = bf16lo(gw[w]), g1 = bf16hi(gw[w]), u0 = bf16lo(uw[w]), u1 = bf16hi(uw[w]);
+          const float s0 = sigmoidf_(g0), s1 = sigmoidf_(g1);
+          dgw[w] = pack_bf16x2(dh[2 * w] * u0 * s0 * (1.0f + g0 * (1.0f - s0)),
+                               dh[2 * w + 1] * u1 * s1 * (1.0f + g1 * (1.0f - s1)));
+          duw[w] = pack_bf16x2(dh[2 * w] * g0 * s0, dh[2 * w + 1] * g1 * s1);
+        }
+        // quantize the bf16 values: a 32-column block spans the row's four lane groups
+        uint2 qv[2];
         int code[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t(&w)[kDswFrags][2] = h ? duw : dgw;
-          const float v[8] = {bf16lo(w[jj][0]),     bf16hi(w[jj][0]),     bf16lo(w[jj][1]),
-                              bf16hi(w[jj][1]),     bf16lo(w[jj + 1][0]), bf16hi(w[jj + 1][0]),
-                              bf16lo(w[jj + 1][1]), bf16hi(w[jj + 1][1])};
+          const uint32_t* w = h ? duw : dgw;
+          const float v[8] = {bf16lo(w[0]), bf16hi(w[0]), bf16lo(w[1]), bf16hi(w[1]),
+                              bf16lo(w[2]), bf16hi(w[2]), bf16lo(w[3]), bf16hi(w[3])};
           float amax = 0.0f;
 #pragma unroll
           for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
           amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
           amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
           code[h] = e8m0_code(amax);
-          qw[h][0] = e4m3x4(v[0], v[1], v[2], v[3], code[h] - 127);
-          qw[h][1] = e4m3x4(v[4], v[5], v[6], v[7], code[h] - 127);
+          qv[h] = make_uint2(e4m3x4(v[0], v[1], v[2], v[3], code[h] - 127),
+                             e4m3x4(v[4], v[5], v[6], v[7], code[h] - 127));
         }
-        const int nb = it.n0 + wn * WN + (j0 + jj) * 16;
+        const int nb = it.n0 + wn * WN + 2 * jp * 16;   // the block's first column
         if (nb >= p.N) continue;
+        const int n = nb + (odd ? 16 : 0) + 8 * (lg >> 1);
+        const int64_t off = row * p.N + n;
+        stg16(p.c0 + off, make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]));
+        stg16(p.c1 + off, make_uint4(duw[0], duw[1], duw[2], duw[3]));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          uint8_t* qrow = p.hq + row * N2 + h * p.N + nb + 4 * lg;
-          *reinterpret_cast<uint32_t*>(qrow) = qw[h][0];
-          *reinterpret_cast<uint32_t*>(qrow + 16) = qw[h][1];
+          *reinterpret_cast<uint2*>(p.hq + row * N2 + h * p.N + n) = qv[h];
           if (lg == 0) p.hs[row * (N2 / 32) + (h * p.N + nb) / 32] = (uint8_t)code[h];
         }
       }
