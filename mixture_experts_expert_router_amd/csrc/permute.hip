@@ -23,6 +23,15 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
   return o;
 }
 
+// Destination row of route k of token t (wave-uniform t and k, so a scalar
+// load): routes 0..K-1 from dst_rows, route K the shared expert's row srow.
+// Read where it is used rather than kept in a per-lane array, which the
+// compiler would place in scratch memory.
+__device__ __forceinline__ int route_row(const int32_t* __restrict__ dst_rows, int t, int K, int k,
+                                         int srow) {
+  return k < K ? dst_rows[(int64_t)t * K + k] : srow;
+}
+
 // dispatch (bf16): one wave per token; WEIGHTED multiplies by the route weight
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __restrict__ x,
@@ -32,19 +41,11 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ xd,
                                                             const int32_t* __restrict__ shared_row0) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[33];
-  float w[33];
-  for (int k = 0; k < K; ++k) {
-    dst[k] = dst_rows[(int64_t)t * K + k];
-    w[k] = WEIGHTED ? weight[(int64_t)t * K + k] : 1.0f;
-  }
-  if (shared_row0) {              // the shared expert's row of this token, weight 1
-    dst[K] = *shared_row0 + t;
-    w[K] = 1.0f;
-  }
+  // route K (when there is a shared expert): its row of this token, weight 1
   const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
   const int nvec = D >> 3;
   const uint16_t* src = x + (int64_t)t * D;
   for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
@@ -55,12 +56,14 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
       if (v < nvec) r[j] = ldg16(src + v * 8);
     }
     for (int k = 0; k < KK; ++k) {
-      if (dst[k] < 0) continue;
-      uint16_t* out = xd + (int64_t)dst[k] * D;
+      const int dk = route_row(dst_rows, t, K, k, srow);
+      if (dk < 0) continue;
+      const float wk = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
+      uint16_t* out = xd + (int64_t)dk * D;
 #pragma unroll
       for (int j = 0; j < kVPL; ++j) {
         const int v = v0 + lane + j * kWave;
-        if (v < nvec) stg16(out + v * 8, (WEIGHTED && k < K) ? scale_bf16x8(r[j], w[k]) : r[j]);
+        if (v < nvec) stg16(out + v * 8, (WEIGHTED && k < K) ? scale_bf16x8(r[j], wk) : r[j]);
       }
     }
   }
@@ -92,12 +95,10 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ sc,
                                                              const int32_t* __restrict__ shared_row0) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[33];
-  for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
-  if (shared_row0) dst[K] = *shared_row0 + t;   // the shared expert's row of this token
   const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;   // the shared expert's row of this token
   const int nvec = D >> 3;
   const uint16_t* src = x + (int64_t)t * D;
   for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
@@ -111,13 +112,14 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
       qv[j] = quant_vec(r, code[j]);     // all lanes take part in the shuffles
     }
     for (int k = 0; k < KK; ++k) {
-      if (dst[k] < 0) continue;
+      const int dk = route_row(dst_rows, t, K, k, srow);
+      if (dk < 0) continue;
 #pragma unroll
       for (int j = 0; j < kVPL; ++j) {
         const int v = v0 + lane + j * kWave;
         if (v < nvec) {
-          *reinterpret_cast<uint2*>(q + (int64_t)dst[k] * D + v * 8) = qv[j];
-          if ((v & 3) == 0) sc[(int64_t)dst[k] * (D >> 5) + (v >> 2)] = (uint8_t)code[j];
+          *reinterpret_cast<uint2*>(q + (int64_t)dk * D + v * 8) = qv[j];
+          if ((v & 3) == 0) sc[(int64_t)dk * (D >> 5) + (v >> 2)] = (uint8_t)code[j];
         }
       }
     }
@@ -141,10 +143,8 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  int dst[33];
-  for (int k = 0; k < K; ++k) dst[k] = dst_rows[(int64_t)t * K + k];
-  if (shared_row0) dst[K] = *shared_row0 + t;   // the shared expert's row of this token
   const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;   // the shared expert's row of this token
   const int npair = D >> 4;              // 16-element pieces per row
   const int nblk = D >> 5;
   const uint16_t* src = x + (int64_t)t * D;
@@ -175,15 +175,16 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
       packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
     for (int k = 0; k < KK; ++k) {
-      if (dst[k] < 0) continue;
-      uint8_t* qrow = q + (int64_t)dst[k] * D;
-      uint8_t* srow = sc + (int64_t)dst[k] * nblk;
+      const int dk = route_row(dst_rows, t, K, k, srow);
+      if (dk < 0) continue;
+      uint8_t* qrow = q + (int64_t)dk * D;
+      uint8_t* crow = sc + (int64_t)dk * nblk;
 #pragma unroll
       for (int j = 0; j < PP; ++j) {
         const int pc = p0 + lane + j * kWave;
         if (pc < npair) {
           *reinterpret_cast<uint4*>(qrow + pc * 16) = qv[j];
-          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(srow + (pc >> 1)) = packed[j];
+          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(crow + (pc >> 1)) = packed[j];
         }
       }
     }
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(256) void zero_padding_kernel(const int32_t* __rest
 // combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), fp32 fmaf in ascending k.
 // The rows of up to 8 routes are loaded before any of them is added, so a
 // lane keeps 16 loads in flight instead of waiting on one route at a time.
+// The gathered rows and the output are touched once: non-temporal accesses.
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ dst_rows,
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
           const int v = v0 + lane + j * kWave;
-          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16(src + v * 8) : make_uint4(0, 0, 0, 0);
+          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16_nt(src + v * 8) : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
@@ -281,8 +283,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + lane + j * kWave;
       if (v < nvec)
-        stg16(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
-                                    pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
+        stg16_nt(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
+                                       pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
     }
   }
 }
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
             const int v = v0 + lane + j * kWave;
-            yy[kk][j] = (dk[kk] >= 0 && kb + kk < K && v < nvec) ? ldg16(y + (int64_t)dk[kk] * D + v * 8)
+            yy[kk][j] = (dk[kk] >= 0 && kb + kk < K && v < nvec) ? ldg16_nt(y + (int64_t)dk[kk] * D + v * 8)
                                                                   : make_uint4(0, 0, 0, 0);
           }
       }
