@@ -191,21 +191,26 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
   }
 }
 
-// zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert
-__global__ __launch_bounds__(256) void zero_padding_kernel(const int32_t* __restrict__ counts,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int64_t row_bytes, uint8_t* __restrict__ a,
-                                                           int64_t row_bytes2,
-                                                           uint8_t* __restrict__ b) {
+// zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert:
+// one workgroup of 16 waves per expert, padding row i on wave i % 16, 16-byte
+// stores for the data rows (row_bytes is a multiple of 16) and bytes for the
+// scale rows
+constexpr int kPadThreads = 1024;
+__global__ __launch_bounds__(kPadThreads) void zero_padding_kernel(const int32_t* __restrict__ counts,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   int64_t row_bytes, uint8_t* __restrict__ a,
+                                                                   int64_t row_bytes2,
+                                                                   uint8_t* __restrict__ b) {
   const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r0 = offsets[e] + counts[e];
   const int64_t r1 = offsets[e + 1];
-  for (int64_t r = r0; r < r1; ++r) {
+  for (int64_t r = r0 + wave; r < r1; r += kPadThreads / 64) {
     uint4* pa = reinterpret_cast<uint4*>(a + r * row_bytes);
-    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) pa[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t i = lane; i < row_bytes / 16; i += 64) pa[i] = make_uint4(0, 0, 0, 0);
     if (b) {
       uint8_t* pb = b + r * row_bytes2;
-      for (int64_t i = threadIdx.x; i < row_bytes2; i += blockDim.x) pb[i] = 0;
+      for (int64_t i = lane; i < row_bytes2; i += 64) pb[i] = 0;
     }
   }
 }
@@ -466,7 +471,7 @@ hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, in
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
                                hipStream_t s) {
   if (E == 0) return hipSuccess;
-  zero_padding_kernel<<<(unsigned)E, 256, 0, s>>>(counts, offsets, row_bytes, (uint8_t*)a,
+  zero_padding_kernel<<<(unsigned)E, kPadThreads, 0, s>>>(counts, offsets, row_bytes, (uint8_t*)a,
                                                    row_bytes2, (uint8_t*)b);
   return hipGetLastError();
 }

@@ -227,17 +227,23 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   const int cpg = (nchunks + G - 1) / G;         // chunks per group
   const int e = threadIdx.x % Ep;
   const int g = threadIdx.x / Ep;
+  // The first kScanRegs counts of a thread's chunk range are loaded at once
+  // and kept in registers for the second pass; the rest (large N only) are
+  // read in batches of 16 in both passes.
+  constexpr int kScanRegs = 64;
+  const int cb = g * cpg, c1 = e < E ? min(nchunks, cb + cpg) : cb;
+  int hr[kScanRegs];
   int sum = 0;
-  if (e < E) {
-    // loads in batches of 16, so they are in flight together
-    const int c1 = min(nchunks, (g + 1) * cpg);
-    for (int c0 = g * cpg; c0 < c1; c0 += 16) {
-      int h[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) h[i] = c0 + i < c1 ? hist[(int64_t)(c0 + i) * E + e] : 0;
+  for (int i = 0; i < kScanRegs; ++i) hr[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum += h[i];
-    }
+  for (int i = 0; i < kScanRegs; ++i) sum += hr[i];
+  for (int c0 = cb + kScanRegs; c0 < c1; c0 += 16) {
+    int h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) h[i] = c0 + i < c1 ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += h[i];
   }
   s_part[threadIdx.x] = sum;
   __syncthreads();
@@ -284,14 +290,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
   if (e < E) {
     int run = s_off[e] + s_part[g * Ep + e];
-    const int c1 = min(nchunks, (g + 1) * cpg);
-    for (int c0 = g * cpg; c0 < c1; c0 += 16) {
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) {
+      if (cb + i < c1) hist[(int64_t)(cb + i) * E + e] = run;   // first row of (chunk, e)
+      run += hr[i];
+    }
+    for (int c0 = cb + kScanRegs; c0 < c1; c0 += 16) {
       int h[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) h[i] = c0 + i < c1 ? hist[(int64_t)(c0 + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (c0 + i < c1) hist[(int64_t)(c0 + i) * E + e] = run;   // first row of (chunk, e)
+        if (c0 + i < c1) hist[(int64_t)(c0 + i) * E + e] = run;
         run += h[i];
       }
     }
