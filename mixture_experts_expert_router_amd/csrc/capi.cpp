@@ -257,13 +257,13 @@ int moe_dispatch(const void* x, const int32_t* dst_rows, const float* weight, co
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (mx)
-    e = moe::launch_dispatch_mxfp8(x, dst_rows, d->N, d->D, d->K, (uint8_t*)xd, xd_scales, s);
+  if (mx)   // the padding rows are zeroed in the same launch
+    e = moe::launch_dispatch_mxfp8(x, dst_rows, d->N, d->D, d->K, (uint8_t*)xd, xd_scales, s, nullptr,
+                                   d->align > 1 ? counts : nullptr, offsets, d->E);
   else
     e = moe::launch_dispatch_bf16(x, dst_rows, weight, d->N, d->D, d->K, xd, s);
-  if (e == hipSuccess && d->align > 1)
-    e = moe::launch_zero_padding(counts, offsets, d->E, mx ? d->D : d->D * 2, xd,
-                                 mx ? d->D / 32 : 0, mx ? xd_scales : nullptr, s);
+  if (e == hipSuccess && d->align > 1 && !mx)
+    e = moe::launch_zero_padding(counts, offsets, d->E, d->D * 2, xd, 0, nullptr, s);
   return hip_status(e);
 }
 
@@ -484,9 +484,10 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                           ws_route, s, d.n_group, d.topk_group, aux, d.n_shared);
   if (e == hipSuccess && aux) e = moe::launch_aux_loss(ws_route, d.N, d.E, d.K, sv->counts, a->aux_alpha, sv->aux, s);
   if (mx) {
-    if (e == hipSuccess) e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s, shared_row0);
+    // quantize-on-dispatch; the same launch zeroes the padding rows
     if (e == hipSuccess)
-      e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D, sv->xd_q, d.D / 32, sv->xd_s, s);
+      e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s, shared_row0,
+                                     sv->counts, sv->offsets, Ex);
     moe::GemmFwd g1{Ex, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
                     a->wu_s, sv->g, sv->u, sv->h, sv->h_q, sv->h_s, true};
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g1, table, s);

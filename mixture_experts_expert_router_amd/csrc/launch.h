@@ -82,9 +82,12 @@ hipError_t launch_aux_loss(void* route_ws, int64_t N, int64_t E, int64_t K, cons
 hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const float* weight,
                                 int64_t N, int64_t D, int64_t K, void* xd, hipStream_t s,
                          const int32_t* shared_row0 = nullptr);
+// pad_counts/pad_offsets (optional): also zero the padding rows of pad_E
+// experts, in trailing workgroups of the same launch
 hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
                                  int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s,
-                         const int32_t* shared_row0 = nullptr);
+                                 const int32_t* shared_row0 = nullptr, const int32_t* pad_counts = nullptr,
+                                 const int32_t* pad_offsets = nullptr, int64_t pad_E = 0);
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
                                hipStream_t s);

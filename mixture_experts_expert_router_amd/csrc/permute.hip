@@ -85,6 +85,24 @@ __device__ __forceinline__ uint2 quant_vec(uint4 v, int& code_out) {
   return make_uint2(e4m3x4(f[0], f[1], f[2], f[3], e), e4m3x4(f[4], f[5], f[6], f[7], e));
 }
 
+// Zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of expert e in
+// the MXFP8 dispatch output: codes (D bytes a row, 16-byte stores) and scales
+// (D/32 bytes a row).  Run by the dispatch launch's trailing workgroups, one
+// per expert, its four waves taking the rows in turn.
+__device__ __forceinline__ void zero_pad_rows_mx(int e, const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ offsets, int D,
+                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
+  const int nb = D >> 5;
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    uint4* pq = reinterpret_cast<uint4*>(q + r * D);
+    for (int i = lane; i < (D >> 4); i += 64) pq[i] = make_uint4(0, 0, 0, 0);
+    uint8_t* ps = sc + r * nb;
+    for (int i = lane; i < nb; i += 64) ps[i] = 0;
+  }
+}
+
 // dispatch (MXFP8): quantize each token row once along D, write q and scales
 // to its K rows.  D is a multiple of 32, so 4 consecutive lanes own a block
 // and every wave-wide pass covers whole blocks.
@@ -93,7 +111,14 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
                                                              int N, int D, int K,
                                                              uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ sc,
-                                                             const int32_t* __restrict__ shared_row0) {
+                                                             const int32_t* __restrict__ shared_row0,
+    const int32_t* __restrict__ pad_counts, const int32_t* __restrict__ pad_offsets) {
+  // trailing workgroups: one per expert, zeroing its padding rows
+  const int tok_blocks = (N + 3) / 4;
+  if (pad_counts && (int)blockIdx.x >= tok_blocks) {
+    zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
@@ -138,8 +163,15 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
                                                                     int N, int D, int K,
                                                                     uint8_t* __restrict__ q,
                                                                     uint8_t* __restrict__ sc,
-                                                             const int32_t* __restrict__ shared_row0) {
-  constexpr int PP = 2;   // lane pairs of vectors per pass
+                                                             const int32_t* __restrict__ shared_row0,
+    const int32_t* __restrict__ pad_counts, const int32_t* __restrict__ pad_offsets) {
+  // trailing workgroups: one per expert, zeroing its padding rows
+  const int tok_blocks = (N + 3) / 4;
+  if (pad_counts && (int)blockIdx.x >= tok_blocks) {
+    zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc);
+    return;
+  }
+  constexpr int PP = 4;   // lane pairs of vectors per pass
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
@@ -456,14 +488,16 @@ hipError_t launch_dispatch_bf16(const void* x, const int32_t* dst_rows, const fl
 }
 
 hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t N, int64_t D,
-                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s, const int32_t* shared_row0) {
+                                 int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s, const int32_t* shared_row0,
+                                 const int32_t* pad_counts, const int32_t* pad_offsets, int64_t pad_E) {
   if (N == 0) return hipSuccess;
+  const unsigned grid = waves_grid(N) + (pad_counts ? (unsigned)pad_E : 0u);
   if (D % 128 == 0 && ((uintptr_t)sc & 3) == 0)
-    dispatch_mxfp8_packed_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
-                                                               (int)K, q, sc, shared_row0);
+    dispatch_mxfp8_packed_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D, (int)K, q,
+                                                      sc, shared_row0, pad_counts, pad_offsets);
   else
-    dispatch_mxfp8_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D,
-                                                        (int)K, q, sc, shared_row0);
+    dispatch_mxfp8_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D, (int)K, q, sc,
+                                               shared_row0, pad_counts, pad_offsets);
   return hipGetLastError();
 }
 
