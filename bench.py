@@ -201,9 +201,12 @@ def mfma_report(run_dir, cus=256, xcds=8):
     return rows
 
 
-def recorded_traffic(workload):
+def recorded_traffic(workload, seed=0):
     """Bytes per launch of GEMM1 from the committed counter summary of this
-    workload, or None when there is none or the GEMM sources changed since."""
+    workload, or None when there is none, the GEMM sources changed since, or
+    the inputs differ (the counters were taken at seed 0)."""
+    if seed != 0:
+        return None
     path = os.path.join(PROFILES, f"gemm1_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -550,7 +553,7 @@ def main(argv=None):
     else:
         roof = dict(bound="mfma", achieved=F1 / t1 / 1e12, peak=peak, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(wl.name)
+    roof["traffic"] = recorded_traffic(wl.name, args.seed)
     roof["kernel"] = "gemm1 (grouped gate/up GEMM with SwiGLU epilogue)"
     roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
 
