@@ -76,6 +76,8 @@ __global__ __launch_bounds__(BM * 4) void router_tile_kernel(RouterParams p) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
   float* out = p.out + (p.S > 1 ? (int64_t)split * p.N * p.E : 0);
+  // rows of E floats start 16-byte aligned when E % 4 == 0 (outputs are 16-byte aligned)
+  const bool vec4 = (p.E & 3) == 0;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int row = m_start + wm * C::WM + i * 16 + l16;
@@ -83,12 +85,15 @@ __global__ __launch_bounds__(BM * 4) void router_tile_kernel(RouterParams p) {
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       const int n = n0 + wn * C::WN + j * 16 + 4 * lg;
+      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (n + r < p.E) {
-          const float b = (p.S == 1 && p.bias) ? p.bias[n + r] : 0.0f;
-          out[(int64_t)row * p.E + n + r] = acc[i][j][r] + b;
-        }
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] + ((p.S == 1 && p.bias && n + r < p.E) ? p.bias[n + r] : 0.0f);
+      if (vec4 && n < p.E) {   // the lane's 4 adjacent columns (n % 4 == 0) in one 16-byte store
+        *reinterpret_cast<f32x4_t*>(out + (int64_t)row * p.E + n) = f32x4_t{v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < p.E) out[(int64_t)row * p.E + n + r] = v[r];
       }
     }
   }
