@@ -19,7 +19,6 @@ namespace moe {
 constexpr int kChunk = 16;         // tokens per workgroup in route_topk (one per wave)
 constexpr int kTopkThreads = kChunk * 64;
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / kWave;
 
 // (value desc, index asc): true if (va, ia) ranks before (vb, ib)
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
@@ -32,6 +31,9 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 // runs over their experts.  psum (optional): this chunk's per-expert sums of
 // the routing probabilities, the aux-loss input.  Both use a dynamic LDS row
 // of E floats per wave.
+// NPL: logits per lane (E <= 64 NPL), so loads, exps and the arg-max rounds
+// touch only the experts that exist
+template <int NPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, const uint8_t* __restrict__ drop, int N, int E, int K,
     int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
@@ -44,9 +46,9 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kChunk;
   const bool grouped = n_group > 1;
-  float pacc[kMaxPerLane];
+  float pacc[NPL];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) pacc[j] = 0.0f;
+  for (int j = 0; j < NPL; ++j) pacc[j] = 0.0f;
 
   // row_route = -1 everywhere first (the scatter overwrites the used rows)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows_cap;
@@ -60,11 +62,11 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       if (lane < K) s_sel[tl * K + lane] = -1;
       continue;
     }
-    float v[kMaxPerLane];
+    float v[NPL];
     const float* row = logits + (int64_t)t * E;
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NPL; ++j) {
       int e = lane + j * kWave;
       v[j] = (e < E) ? row[e] : -INFINITY;
       mx = fmaxf(mx, v[j]);
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     float se = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NPL; ++j) {
       int e = lane + j * kWave;
       if (e < E) se += expf(v[j] - mx);
     }
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     if (grouped || psum) {
       float* prow = s_row + wave * E;
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
+      for (int j = 0; j < NPL; ++j) {
         const int e = lane + j * kWave;
         if (e < E) {
           const float pj = expf(v[j] - mx) / se;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
           keep |= 1ull << bi;
         }
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
+        for (int j = 0; j < NPL; ++j) {
           const int e = lane + j * kWave;
           if (e < E && !((keep >> (e / gs)) & 1ull)) taken |= 1u << j;
         }
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
+      for (int j = 0; j < NPL; ++j) {
         int e = lane + j * kWave;
         if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
       }
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   if (psum) {
     // the chunk's probability sums, added over its waves in order
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NPL; ++j) {
       const int e = lane + j * kWave;
       if (e < E) s_row[wave * E + e] = pacc[j];
     }
@@ -366,15 +368,24 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
   float* psum = aux_inputs ? (float*)((char*)ws + route_psum_offset(N, E, K)) : nullptr;
   const int ng = n_group > 1 ? n_group : 0;
   const size_t lds = (ng || psum) ? (size_t)kChunk * E * 4 : 0;
-  if (nchunks > 0) {
-    route_topk_kernel<<<dim3((unsigned)nchunks), dim3(kTopkThreads), lds, s>>>(
-        logits, drop, (int)N, (int)E, (int)K, renorm, topk_idx, topk_prob, row_route, rows_cap,
-        hist, rank, ng, topk_group, psum);
-  } else {
-    // no tokens: still mark every row unused
-    route_topk_kernel<<<dim3(1), dim3(kTopkThreads), 0, s>>>(logits, drop, 0, (int)E, (int)K, renorm,
-                                                    topk_idx, topk_prob, row_route, rows_cap,
-                                                    hist, rank, 0, 0, nullptr);
+  int npl = 1;
+  while (npl * kWave < E) npl <<= 1;   // E <= kMaxE is checked by the caller
+  // no tokens: one workgroup still marks every row unused
+  const unsigned grid = nchunks > 0 ? (unsigned)nchunks : 1u;
+  const int Nk = nchunks > 0 ? (int)N : 0;
+  const size_t lds_k = nchunks > 0 ? lds : 0;
+  auto go = [&](auto kern) {
+    kern<<<dim3(grid), dim3(kTopkThreads), lds_k, s>>>(logits, drop, Nk, (int)E, (int)K, renorm, topk_idx,
+                                                       topk_prob, row_route, rows_cap, hist, rank,
+                                                       nchunks > 0 ? ng : 0, nchunks > 0 ? topk_group : 0,
+                                                       nchunks > 0 ? psum : nullptr);
+  };
+  switch (npl) {
+    case 1: go(route_topk_kernel<1>); break;
+    case 2: go(route_topk_kernel<2>); break;
+    case 4: go(route_topk_kernel<4>); break;
+    case 8: go(route_topk_kernel<8>); break;
+    default: go(route_topk_kernel<16>); break;
   }
   route_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(hist, (int)nchunks, (int)E, align, counts,
                                                    offsets, (int)N, n_shared);

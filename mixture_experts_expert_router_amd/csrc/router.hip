@@ -99,13 +99,29 @@ __global__ __launch_bounds__(BM * 4) void router_tile_kernel(RouterParams p) {
   }
 }
 
-// logits = sum over splits (ascending) of the partials, plus the bias
+// logits = sum over splits (ascending) of the partials, plus the bias; VEC:
+// four adjacent logits per thread (E % 4 == 0), the same sums element by element
+template <bool VEC>
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, const float* __restrict__ bias,
                                                             int64_t NE, int E, int S, float* __restrict__ logits) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < NE; i += (int64_t)gridDim.x * blockDim.x) {
-    float s = part[i];
-    for (int k = 1; k < S; ++k) s += part[(int64_t)k * NE + i];
-    logits[i] = s + (bias ? bias[i % E] : 0.0f);
+  if constexpr (VEC) {
+    const int64_t NE4 = NE >> 2;
+    const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(part);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < NE4; i += (int64_t)gridDim.x * blockDim.x) {
+      f32x4_t s = p4[i];
+      for (int k = 1; k < S; ++k) s += p4[(int64_t)k * NE4 + i];
+      if (bias) {
+        const int e = (int)((i << 2) % E);
+        s += f32x4_t{bias[e], bias[e + 1], bias[e + 2], bias[e + 3]};
+      }
+      reinterpret_cast<f32x4_t*>(logits)[i] = s;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < NE; i += (int64_t)gridDim.x * blockDim.x) {
+      float s = part[i];
+      for (int k = 1; k < S; ++k) s += part[(int64_t)k * NE + i];
+      logits[i] = s + (bias ? bias[i % E] : 0.0f);
+    }
   }
 }
 
@@ -237,9 +253,11 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
   }
   if (r.S > 1) {
     const int64_t NE = N * E;
-    const int64_t nblk = (NE + 255) / 256;
+    const bool vec = (E & 3) == 0;
+    const int64_t nblk = ((vec ? NE / 4 : NE) + 255) / 256;
     const unsigned rg = (unsigned)(nblk < 4096 ? nblk : 4096);
-    router_reduce_kernel<<<rg, 256, 0, s>>>((const float*)ws, bias, NE, (int)E, r.S, logits);
+    if (vec) router_reduce_kernel<true><<<rg, 256, 0, s>>>((const float*)ws, bias, NE, (int)E, r.S, logits);
+    else router_reduce_kernel<false><<<rg, 256, 0, s>>>((const float*)ws, bias, NE, (int)E, r.S, logits);
   }
   return hipGetLastError();
 }
