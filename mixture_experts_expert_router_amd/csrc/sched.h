@@ -38,7 +38,7 @@ static_assert(kXcds * kHeadStride == kGemmHeadInts, "head block of the workspace
 // A claimed queue item, decoded: rows [m_start, min(m_start + BM, m1)) of
 // expert e, output columns [n0, n0 + NCOL), tile class by the expert's rows
 // (a large expert's last row block takes the 128-row class when it holds at
-// most 128 rows).
+// most 128 rows, the 64-row one at most 64).
 struct Item {
   int e, m_start, m1, n0;
   bool big, valid;
@@ -125,9 +125,13 @@ __device__ __forceinline__ Item claim_rows(const int32_t* plan, const int32_t* o
   it.n0 = n_t * ncol;
   it.valid = true;
   // the last row block of a large expert, when at most kSmallBM rows are
-  // left, runs as a 128-row tile (every tile class accumulates the same
+  // left, runs as a 128-row tile, or a 64-row one where that class exists
+  // and kTinyRows rows are left (every tile class accumulates the same
   // contraction steps in the same order, so the result is the same)
-  if (it.big && it.m1 - it.m_start <= kSmallBM) it.big = false;
+  if (it.big && it.m1 - it.m_start <= kSmallBM) {
+    it.big = false;
+    it.tiny = it.m1 - it.m_start <= kTinyRows;
+  }
   return it;
 }
 
