@@ -64,6 +64,12 @@ ROUTE_CASES = [
     (100, 1024, 32, 1, 0.0, 0, "normal"),
     (65, 7, 2, 1, 0.0, 0, "normal"),
     (0, 8, 2, 1, 0.0, 0, "normal"),
+    # expert counts just past each logits-per-lane size of the top-K kernel
+    # (64, 128, 256 per wave) and inside the 8-per-lane one
+    (200, 65, 4, 1, 0.1, 0, "normal"),
+    (300, 129, 6, 1, 0.0, 1, "zipf"),
+    (400, 384, 8, 32, 0.0, 0, "zipf"),
+    (150, 512, 16, 1, 0.0, 0, "ties"),
 ]
 
 
@@ -103,7 +109,7 @@ def test_route_bit_exact(case):
 
 @pytest.mark.parametrize("N,E,K,G,M_,renorm", [(2000, 256, 8, 8, 4, 0), (700, 64, 6, 16, 3, 1),
                                                (333, 32, 8, 4, 2, 0), (129, 128, 4, 64, 8, 0),
-                                               (50, 16, 4, 2, 1, 1)])
+                                               (50, 16, 4, 2, 1, 1), (300, 512, 8, 8, 4, 0)])
 def test_route_grouped_bit_exact(N, E, K, G, M_, renorm):
     """Group-limited top-K through moe_route against the oracle.  Group scores
     are sums of fp32 probabilities on the GPU and fp64 ones in the oracle, so a
