@@ -434,6 +434,60 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
   }
 }
 
+// Same result for cols % 128 == 0 (and 4-byte aligned scale rows): each lane
+// quantizes 16 adjacent elements, so a 32-block is a lane pair, with four
+// such pieces per lane in flight; 16-byte code stores, and lanes 8i store the
+// codes of four consecutive blocks as one 4-byte word.
+__global__ __launch_bounds__(256) void quantize_rows_packed_kernel(const uint16_t* __restrict__ src,
+                                                                   int64_t rows, int cols,
+                                                                   uint8_t* __restrict__ q,
+                                                                   uint8_t* __restrict__ sc,
+                                                                   const int32_t* __restrict__ rows_end) {
+  constexpr int PP = 4;   // 16-element pieces per lane per pass
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows || (rows_end && r >= *rows_end)) return;
+  const int npair = cols >> 4, nblk = cols >> 5;
+  const uint16_t* s = src + r * cols;
+  uint8_t* qrow = q + r * cols;
+  uint8_t* crow = sc + r * nblk;
+  for (int p0 = 0; p0 < npair; p0 += kWave * PP) {
+    uint4 x0[PP], x1[PP];
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      const int pc = p0 + lane + j * kWave;
+      x0[j] = make_uint4(0, 0, 0, 0);
+      x1[j] = make_uint4(0, 0, 0, 0);
+      if (pc < npair) {
+        x0[j] = ldg16(s + pc * 16);
+        x1[j] = ldg16(s + pc * 16 + 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      const int pc = p0 + lane + j * kWave;
+      const uint4 r0 = x0[j], r1 = x1[j];
+      float f[16] = {bf16lo(r0.x), bf16hi(r0.x), bf16lo(r0.y), bf16hi(r0.y), bf16lo(r0.z), bf16hi(r0.z),
+                     bf16lo(r0.w), bf16hi(r0.w), bf16lo(r1.x), bf16hi(r1.x), bf16lo(r1.y), bf16hi(r1.y),
+                     bf16lo(r1.z), bf16hi(r1.z), bf16lo(r1.w), bf16hi(r1.w)};
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));   // every lane takes part
+      const int code = e8m0_code(amax);
+      const int e = code - 127;
+      const uint4 qv = make_uint4(quant4(f, e), quant4(f + 4, e), quant4(f + 8, e), quant4(f + 12, e));
+      const uint32_t c1 = (uint32_t)__shfl_down(code, 2, 64), c2 = (uint32_t)__shfl_down(code, 4, 64),
+                     c3 = (uint32_t)__shfl_down(code, 6, 64);
+      if (pc < npair) {
+        *reinterpret_cast<uint4*>(qrow + pc * 16) = qv;
+        if ((lane & 7) == 0)
+          *reinterpret_cast<uint32_t*>(crow + (pc >> 1)) = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      }
+    }
+  }
+}
+
 // h = bf16(silu(g) * u), optionally quantized row-wise; one wave per row
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ g,
                                                      const uint16_t* __restrict__ u, int64_t rows,
@@ -538,7 +592,11 @@ hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const f
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
                                 uint8_t* sc, hipStream_t s, const int32_t* rows_end) {
   if (rows == 0) return hipSuccess;
-  quantize_rows_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc, rows_end);
+  if (cols % 128 == 0 && ((uintptr_t)q & 15) == 0 && ((uintptr_t)sc & 3) == 0)
+    quantize_rows_packed_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc,
+                                                                 rows_end);
+  else
+    quantize_rows_kernel<<<waves_grid(rows), 256, 0, s>>>((const uint16_t*)src, rows, (int)cols, q, sc, rows_end);
   return hipGetLastError();
 }
 

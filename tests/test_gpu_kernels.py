@@ -232,6 +232,23 @@ def test_quantize_mxfp8_bit_exact():
     assert np.array_equal(host(q), rq)
 
 
+@pytest.mark.parametrize("rows,cols", [(37, 32), (50, 160), (64, 384), (21, 7168)])
+def test_quantize_mxfp8_widths(rows, cols):
+    """Row quantization at widths that take the one-block-per-four-lanes path
+    (cols % 128 != 0) and the 16-elements-per-lane path (cols % 128 == 0, one
+    partial pass at 7168 columns), against the oracle."""
+    print(f"quantize rows={rows} cols={cols}", flush=True)
+    rng = np.random.default_rng(rows + cols)
+    v = rng.standard_normal((rows, cols)) * np.ldexp(1.0, rng.integers(-20, 20, (rows, 1)))
+    v[0, : cols // 2] = 0.0                                        # all-zero blocks
+    u = S.f32_to_bf16_bits(v.astype(np.float32))
+    q, s = M.quantize_mxfp8(dev_bf16(u))
+    _sync()
+    rq, rs = O.quantize_mxfp8(u)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s), rs)
+
+
 def test_quantize_mxfp8_every_bf16_value():
     """All finite bf16 patterns, each in a block with an amax that fixes a range
     of scales: the element encoder sees every input value."""
