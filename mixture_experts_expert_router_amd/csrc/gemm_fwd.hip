@@ -87,13 +87,19 @@ using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB rin
 // bf16 experts with at most 64 rows: the same columns, half the A rows
 template <bool DUAL, bool MX = false>
 using TinyTile = tile::TileCfg<64, 256, 3, 2, 4, DUAL, MX>;     // 3 x 40 KB ring
+// bf16 experts with at most 32 rows: waves 0-3 load the A rows, and the
+// smaller stage leaves room for a fourth, so three steps are in flight
+template <bool DUAL, bool MX = false>
+using Tiny32Tile = tile::TileCfg<32, 256, 4, 2, 4, DUAL, MX>;   // 4 x 36 KB ring
 template <bool MX>
 constexpr int lds_bytes() {
   constexpr int s = SmallTile<true, MX>::LDS, s1 = SmallTile<false, MX>::LDS;
   constexpr int b = BigTile<true, MX>::LDS, b1 = BigTile<false, MX>::LDS;
   constexpr int t = TinyTile<true, false>::LDS, t1 = TinyTile<false, false>::LDS;
-  constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1, m2 = t > t1 ? t : t1;
-  return m0 > m1 ? (m0 > m2 ? m0 : m2) : (m1 > m2 ? m1 : m2);
+  constexpr int u = Tiny32Tile<true, false>::LDS, u1 = Tiny32Tile<false, false>::LDS;
+  constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1, m2 = t > t1 ? t : t1, m3 = u > u1 ? u : u1;
+  constexpr int m01 = m0 > m1 ? m0 : m1, m23 = m2 > m3 ? m2 : m3;
+  return m01 > m23 ? m01 : m23;
 }
 constexpr int kLdsBytes = lds_bytes<false>();
 
@@ -355,6 +361,7 @@ __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem
   const Item next = claim<DUAL>(p, s_item, li, xcd);
   if (next.valid) {
     if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
+    else if (!C::MX && next.tiny32) start<Tiny32Tile<DUAL, false>>(p, lds0, next);
     else if (!C::MX && next.tiny) start<TinyTile<DUAL, false>>(p, lds0, next);
     else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
   }
@@ -371,15 +378,18 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   using Big = BigTile<DUAL, MX>;
   using Small = SmallTile<DUAL, MX>;
   using Tiny = TinyTile<DUAL, false>;   // bf16 only (no gain measured for MXFP8)
+  using Tiny32 = Tiny32Tile<DUAL, false>;
   const int xcd = xcd_id();
   int li = 0;
   Item it = claim<DUAL>(p, &s_item, li, xcd);
   if (!it.valid) return;
   if (it.big) start<Big>(p, lds0, it);
+  else if (!MX && it.tiny32) start<Tiny32>(p, lds0, it);
   else if (!MX && it.tiny) start<Tiny>(p, lds0, it);
   else start<Small>(p, lds0, it);
   while (it.valid) {
     if (it.big) it = run_item<Big, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
+    else if (!MX && it.tiny32) it = run_item<Tiny32, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
     else if (!MX && it.tiny) it = run_item<Tiny, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
     else it = run_item<Small, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
   }

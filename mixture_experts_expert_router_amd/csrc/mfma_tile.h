@@ -92,8 +92,13 @@ struct TileCfg {
   static constexpr int WNB = DUAL ? WN / 2 : WN;                   // B rows per wave per half
   static constexpr int RPI = 1024 / kRB;                           // rows per DMA instruction
   static constexpr int A_BYTES = BM * kRB, STAGE = (BM + BN) * kRB;
-  static constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;   // per wave per step
-  static constexpr int LPS = A_INS + B_INS;                        // loads per wave per step
+  // A rows are loaded by A_WAVES waves: all of them, unless the tile has fewer
+  // A rows than one DMA instruction per wave covers (a 32-row tile: waves
+  // 0-3 load A, waves 4-7 only B)
+  static constexpr int A_WAVES = (BM / RPI) < NW ? BM / RPI : NW;
+  static constexpr int A_INS = BM / RPI / A_WAVES, B_INS = BN / RPI / NW;   // per loading wave per step
+  static constexpr int LPS = A_INS + B_INS;                        // loads per step of a wave that loads A
+  static constexpr int LPS_NOA = B_INS;                            // of a wave that does not
   // MX scale groups: 16 bytes per tile row (rows past BM + BN are padding
   // that reloads an A row), SCI loads of 16 rows per wave
   static constexpr int SC_ROWS = (BM + BN + NW * 16 - 1) / (NW * 16) * (NW * 16);
@@ -103,7 +108,7 @@ struct TileCfg {
   static constexpr int SC_BASE = NS * STAGE;                        // group buffers after the ring
   static constexpr int LDS = NS * STAGE + (MX ? 2 * SG_BYTES : 0);
   static constexpr int NCOL = DUAL ? BN / 2 : BN;                  // output columns per tile
-  static_assert(A_INS * RPI * NW == BM && B_INS * RPI * NW == BN, "even DMA split");
+  static_assert(A_WAVES >= 1 && A_INS * RPI * A_WAVES == BM && B_INS * RPI * NW == BN, "even DMA split");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && (!DUAL || TN % 2 == 0), "wave tile");
   static_assert(!DUAL || (BN / 2) % (B_INS * RPI) == 0, "a wave's B rows are all gate or all up");
   static_assert(NS >= 2 && LDS <= 160 * 1024 - 64, "LDS ring");
@@ -173,8 +178,12 @@ __device__ __forceinline__ void issue_step(uint32_t lds0, const Src<C>& src, int
   const int64_t ko = (int64_t)kt * kRB;
   const uint8_t* a = src.a + ko;
   const uint8_t* b = src.b + ko;
+  // a wave-uniform (scalar) test, so a wave that loads no A rows issues no
+  // A instruction at all and its vmcnt counts only its B loads
+  if (C::A_WAVES == C::NW || __builtin_amdgcn_readfirstlane(wave) < C::A_WAVES) {
 #pragma unroll
-  for (int q = 0; q < C::A_INS; ++q) lds_dma16(a, src.a_off[q], __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
+    for (int q = 0; q < C::A_INS; ++q) lds_dma16(a, src.a_off[q], __builtin_amdgcn_readfirstlane(wave_a + q * 1024u));
+  }
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q) lds_dma16(b, src.b_off[q], __builtin_amdgcn_readfirstlane(wave_b + q * 1024u));
 }
@@ -217,8 +226,10 @@ __device__ __forceinline__ void mainloop(const uint8_t* smem, uint32_t lds0, con
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool loads_a = C::A_WAVES == C::NW || __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < C::A_WAVES;
   for (int kt = 0; kt < nk; ++kt) {
-    wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+    if (loads_a) wait_steps<C::LPS, NS - 2>(min(NS - 2, nk - 1 - kt));
+    else wait_steps<C::LPS_NOA, NS - 2>(min(NS - 2, nk - 1 - kt));
     __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
     if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1, nk);
     const uint8_t* st = smem + (kt % NS) * C::STAGE;
@@ -269,6 +280,7 @@ template <class C>
 __device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, const Src<C>& src, int nk,
                                             f32x4_t (&acc)[C::TM][C::TN]) {
   static_assert(C::MX, "MXFP8 tiles");
+  static_assert(C::A_WAVES == C::NW, "every wave loads A rows");
   constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
   const FragBase<C> fb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -389,6 +401,7 @@ struct SrcB {
 
 template <class C>
 __device__ __forceinline__ void issue_step_b_at(uint32_t lds0, const SrcB<C>& src, int kt, int stage) {
+  static_assert(C::A_WAVES == C::NW, "every wave loads A rows");
   const int wave = threadIdx.x >> 6;
   const uint32_t st = lds0 + (uint32_t)(stage * C::STAGE);
   const uint32_t wave_a = st + (uint32_t)(wave * C::A_INS) * 1024u;

@@ -24,6 +24,7 @@ namespace {
 constexpr int kBigRows = 256;       // experts with at least this many rows use 256-row blocks
 constexpr int kBigBM = 256, kSmallBM = 128;
 constexpr int kTinyRows = 64;       // small experts this short may use 64-row tiles
+constexpr int kTiny32Rows = 32;     // and this short 32-row tiles
 constexpr int kXcds = 8;            // XCDs of the chip; queue q holds chunks q, q + 8, ...
 constexpr int kChunk = 32;          // items per chunk (the CUs of one XCD)
 constexpr int kSbM = 4, kSbN = 8;   // super-block: row blocks x n-tiles
@@ -38,11 +39,12 @@ static_assert(kXcds * kHeadStride == kGemmHeadInts, "head block of the workspace
 // A claimed queue item, decoded: rows [m_start, min(m_start + BM, m1)) of
 // expert e, output columns [n0, n0 + NCOL), tile class by the expert's rows
 // (a large expert's last row block takes the 128-row class when it holds at
-// most 128 rows, the 64-row one at most 64).
+// most 128 rows, the 64-row one at most 64, the 32-row one at most 32).
 struct Item {
   int e, m_start, m1, n0;
   bool big, valid;
   bool tiny;   // the expert has at most kTinyRows rows (one row block either way)
+  bool tiny32; // at most kTiny32Rows rows
 };
 
 __device__ __host__ __forceinline__ bool is_big(int rows) { return rows >= kBigRows; }
@@ -117,6 +119,7 @@ __device__ __forceinline__ Item claim_rows(const int32_t* plan, const int32_t* o
   it.m1 = offsets[it.e + 1];
   it.big = is_big(it.m1 - m0);
   it.tiny = it.m1 - m0 <= kTinyRows;
+  it.tiny32 = it.m1 - m0 <= kTiny32Rows;
   const int bm = it.big ? kBigBM : kSmallBM;
   const int nmb = (it.m1 - m0 + bm - 1) / bm;
   int mb, n_t;
@@ -125,12 +128,13 @@ __device__ __forceinline__ Item claim_rows(const int32_t* plan, const int32_t* o
   it.n0 = n_t * ncol;
   it.valid = true;
   // the last row block of a large expert, when at most kSmallBM rows are
-  // left, runs as a 128-row tile, or a 64-row one where that class exists
-  // and kTinyRows rows are left (every tile class accumulates the same
+  // left, runs as a 128-row tile, or a 64- or 32-row one where those classes
+  // exist and that few rows are left (every tile class accumulates the same
   // contraction steps in the same order, so the result is the same)
   if (it.big && it.m1 - it.m_start <= kSmallBM) {
     it.big = false;
     it.tiny = it.m1 - it.m_start <= kTinyRows;
+    it.tiny32 = it.m1 - it.m_start <= kTiny32Rows;
   }
   return it;
 }

@@ -374,6 +374,9 @@ GEMM_CASES = [
     ((2000, 1700), 128, 160, 0),
     ((5000,), 64, 512, 3),
     ((3, 0, 0, 90, 0, 17, 0, 0, 200, 1, 0, 64, 0, 0, 0, 33), 320, 96, 0),
+    # 32- and 64-row tile boundaries: whole experts of 32 and 33 rows, and
+    # large experts whose last row block holds exactly 32 or 64 rows
+    ((288, 32, 33, 320, 2), 256, 192, 0),
     # shapes the persistent backward kernels take (dgrad: n % 64 == 0 and
     # k % 16 == 0; wgrad: n, k % 16 == 0): partial 256-column tiles, ragged
     # and empty experts, experts above and below 256 rows
