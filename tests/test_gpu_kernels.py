@@ -36,7 +36,9 @@ def _sync():
 @pytest.mark.parametrize("N,D,E", [(256, 128, 8), (100, 136, 24), (33, 7168, 256), (70, 4096, 128),
                                    (5, 64, 1), (130, 256, 1024), (17, 512, 40), (4096, 7168, 256),
                                    (2000, 4096, 128), (8192, 4096, 8), (300, 192, 16),
-                                   (2100, 1024, 200), (3000, 640, 1000), (16384, 4096, 128), (2048, 64, 64)])
+                                   (2100, 1024, 200), (3000, 640, 1000), (16384, 4096, 128), (2048, 64, 64),
+                                   # E % 4 != 0 on the tiled path: scalar tile stores and split reduce
+                                   (500, 256, 18), (3000, 1024, 250)])
 def test_router_logits(N, D, E):
     print(f"router N={N} D={D} E={E}", flush=True)
     wl = S.scaled(S.WORKLOADS["dsv3_bf16"], N=N, D=D, E=E, K=1, H=32)
