@@ -84,7 +84,7 @@ template <bool DUAL, bool MX = false>
 using BigTile = tile::TileCfg<256, 256, 2, 4, 2, DUAL, MX>;     // 2 x 64 KB ring (+2 x 2 KB scales)
 template <bool DUAL, bool MX = false>
 using SmallTile = tile::TileCfg<128, 256, 3, 2, 4, DUAL, MX>;   // 3 x 48 KB ring (+ scale groups)
-// bf16 experts with at most 64 rows: the same columns, half the A rows
+// experts with at most 64 rows: the same columns, half the A rows
 template <bool DUAL, bool MX = false>
 using TinyTile = tile::TileCfg<64, 256, 3, 2, 4, DUAL, MX>;     // 3 x 40 KB ring
 // bf16 experts with at most 32 rows: waves 0-3 load the A rows, and the
@@ -95,7 +95,7 @@ template <bool MX>
 constexpr int lds_bytes() {
   constexpr int s = SmallTile<true, MX>::LDS, s1 = SmallTile<false, MX>::LDS;
   constexpr int b = BigTile<true, MX>::LDS, b1 = BigTile<false, MX>::LDS;
-  constexpr int t = TinyTile<true, false>::LDS, t1 = TinyTile<false, false>::LDS;
+  constexpr int t = TinyTile<true, MX>::LDS, t1 = TinyTile<false, MX>::LDS;
   constexpr int u = Tiny32Tile<true, false>::LDS, u1 = Tiny32Tile<false, false>::LDS;
   constexpr int m0 = s > b ? s : b, m1 = s1 > b1 ? s1 : b1, m2 = t > t1 ? t : t1, m3 = u > u1 ? u : u1;
   constexpr int m01 = m0 > m1 ? m0 : m1, m23 = m2 > m3 ? m2 : m3;
@@ -362,7 +362,7 @@ __device__ __forceinline__ Item run_item(const FwdParams& p, const uint8_t* smem
   if (next.valid) {
     if (next.big) start<BigTile<DUAL, C::MX>>(p, lds0, next);
     else if (!C::MX && next.tiny32) start<Tiny32Tile<DUAL, false>>(p, lds0, next);
-    else if (!C::MX && next.tiny) start<TinyTile<DUAL, false>>(p, lds0, next);
+    else if (next.tiny) start<TinyTile<DUAL, C::MX>>(p, lds0, next);
     else start<SmallTile<DUAL, C::MX>>(p, lds0, next);
   }
   if constexpr (DSW) epilogue_dsw<C>(p, it, acc);
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   using Big = BigTile<DUAL, MX>;
   using Small = SmallTile<DUAL, MX>;
-  using Tiny = TinyTile<DUAL, false>;   // bf16 only (no gain measured for MXFP8)
+  using Tiny = TinyTile<DUAL, MX>;
   using Tiny32 = Tiny32Tile<DUAL, false>;
   const int xcd = xcd_id();
   int li = 0;
@@ -385,12 +385,12 @@ __global__ __launch_bounds__(512) void gemm_fwd_kernel(FwdParams p) {
   if (!it.valid) return;
   if (it.big) start<Big>(p, lds0, it);
   else if (!MX && it.tiny32) start<Tiny32>(p, lds0, it);
-  else if (!MX && it.tiny) start<Tiny>(p, lds0, it);
+  else if (it.tiny) start<Tiny>(p, lds0, it);
   else start<Small>(p, lds0, it);
   while (it.valid) {
     if (it.big) it = run_item<Big, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
     else if (!MX && it.tiny32) it = run_item<Tiny32, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
-    else if (!MX && it.tiny) it = run_item<Tiny, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
+    else if (it.tiny) it = run_item<Tiny, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
     else it = run_item<Small, DUAL, DSW>(p, smem, lds0, &s_item, li, xcd, it);
   }
 }
