@@ -468,29 +468,6 @@ def layer_fwd(x, w_r, bias, w_gate, w_up, w_down, K: int, drop=None, renorm: int
                 n_shared=n_shared)
 
 
-def layer_fwd_tokens(fwd_route: dict, x, w_gate, w_up, w_down, tokens, K: int, exact=False):
-    """out[t] for a subset of tokens, given the route tensors of the whole batch.
-
-    Rows of a GEMM do not interact, so each sampled token's output needs only
-    its own K expert rows.  Returns (out [len(tokens), D], rows dict e -> Y rows).
-    """
-    xv = values(x)
-    idx = fwd_route["topk_idx"]
-    prob = fwd_route["topk_prob"]
-    dst = fwd_route["dst_rows"]
-    out = np.zeros((len(tokens), xv.shape[1]))
-    for j, t in enumerate(tokens):
-        acc = np.zeros(xv.shape[1])
-        for k in range(K):
-            if dst[t, k] < 0:
-                continue
-            e = int(idx[t, k])
-            _, _, _, y = expert_mlp(xv[t:t + 1], w_gate[e], w_up[e], w_down[e], exact)
-            acc += float(prob[t, k]) * y[0]
-        out[j] = acc
-    return _rounder(exact)(out)
-
-
 # --------------------------------------------------------------------------
 # whole layer, backward                   [KOSMOS 3.3.2; OLMo-A A.1 adjoint sequence]
 # --------------------------------------------------------------------------
