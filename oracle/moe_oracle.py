@@ -785,6 +785,9 @@ def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
     dW_down = bf16(dY_d^T deq(H_q)), dW_gate = bf16(dG^T deq(X_q)),
     dW_up = bf16(dU^T deq(X_q)) [OLMo-A A.13: wgrad dequantizes its operands
     and runs a bf16 grouped GEMM].
+    hq = None is the SwiGLU-recompute mode [OLMo-A A.14: H rebuilt in the
+    backward instead of saved]: dW_down takes H = bf16(silu(G) U) from the
+    saved bf16 G and U in place of deq(H_q).
     """
     dy = values(dyd)
     rows, D = dy.shape
@@ -793,7 +796,7 @@ def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
     dyq, dys = quantize_mxfp8(dy)
     dy_deq = dequantize_mxfp8(dyq, dys)
     x_deq = dequantize_mxfp8(xq, xs)
-    h_deq = dequantize_mxfp8(hq, hs)
+    h_deq = swiglu(g, u) if hq is None else dequantize_mxfp8(hq, hs)
     dG = np.zeros((rows, Hd))
     dU = np.zeros((rows, Hd))
     for e in range(E):
@@ -824,11 +827,13 @@ def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
                 dyq=dyq, dys=dys, guq=guq, gus=gus)
 
 
-def layer_bwd_mxfp8(fwd: dict, dout, wqt):
+def layer_bwd_mxfp8(fwd: dict, dout, wqt, recompute: bool = False):
     """MXFP8 layer backward: the bf16 adjoint sequence around the experts
     (weighted dY dispatch, route-weight gradient, fold of the K rows) with
     experts_bwd_mxfp8 in the middle.  fwd is layer_fwd_mxfp8's result; wqt
-    comes from quantize_weights_mxfp8_dgrad."""
+    comes from quantize_weights_mxfp8_dgrad.  recompute: the saved H codes are
+    not read (SwiGLU-recompute mode)."""
+    hq = None if recompute else fwd["hq"]
     return _layer_bwd_around(
-        fwd, dout, lambda dyd: experts_bwd_mxfp8(dyd, fwd["xq"], fwd["xs"], fwd["g"], fwd["u"], fwd["hq"],
+        fwd, dout, lambda dyd: experts_bwd_mxfp8(dyd, fwd["xq"], fwd["xs"], fwd["g"], fwd["u"], hq,
                                                  fwd["hs"], fwd["offsets"], wqt))

@@ -112,3 +112,36 @@ def test_random_inputs_stay_within_mxfp8_error_of_the_bf16_backward():
     for k in ("dx", "dw_gate", "dw_up", "dw_down", "dprob"):
         err = np.linalg.norm(mx[k] - ref[k]) / np.linalg.norm(ref[k])
         assert err <= 0.15, (k, err)
+
+
+def test_recompute_mode_takes_h_from_the_saved_g_and_u():
+    """SwiGLU-recompute (OLMo-core Appendix A, A.14): the down weight gradient
+    uses H = bf16(silu(G) U) rebuilt from the saved bf16 G and U (a torch silu
+    here) instead of the dequantized H codes; every other gradient is the
+    same as with the saved codes.  On the lossless case both modes agree."""
+    import torch
+    import torch.nn.functional as F
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_bwd_rc", N=64, D=128, E=8, K=3, H=64, bwd=True)
+    inp = S.make_inputs(wl, 23)
+    q = O.quantize_weights_mxfp8(inp.w_gate, inp.w_up, inp.w_down)
+    wqt = O.quantize_weights_mxfp8_dgrad(inp.w_gate, inp.w_up, inp.w_down)
+    f = O.layer_fwd_mxfp8(inp.x, inp.w_r, inp.bias, q, wl.K)
+    saved = O.layer_bwd_mxfp8(f, inp.dout, wqt)
+    rc = O.layer_bwd_mxfp8(f, inp.dout, wqt, recompute=True)
+    for k in ("dyd", "dg", "du", "dxd", "dw_gate", "dw_up", "dx", "dprob"):
+        assert np.array_equal(rc[k], saved[k]), k
+    o = f["offsets"]
+    h = O.round_bf16((F.silu(torch.from_numpy(f["g"])) * torch.from_numpy(f["u"])).numpy())
+    for e in range(wl.E):
+        a, b = int(o[e]), int(o[e + 1])
+        want = O.round_bf16(rc["dyd"][a:b].T @ h[a:b]) if b > a else np.zeros((wl.D, wl.H))
+        assert np.array_equal(rc["dw_down"][e], want), e
+    assert not np.array_equal(rc["dw_down"], saved["dw_down"])   # H codes are lossy here
+    fwd, dout, wg, wu, wd = _lossless_case(9)
+    wqt = O.quantize_weights_mxfp8_dgrad(wg, wu, wd)
+    fwd["g"] = np.where(fwd["g"] > 0, 64.0, 0.0)
+    fwd["h"] = O.swiglu(fwd["g"], fwd["u"])
+    fwd["hq"], fwd["hs"] = O.quantize_mxfp8(fwd["h"])
+    a = O.layer_bwd_mxfp8(fwd, dout, wqt)
+    b = O.layer_bwd_mxfp8(fwd, dout, wqt, recompute=True)
+    assert np.array_equal(a["dw_down"], b["dw_down"])
