@@ -260,7 +260,7 @@ class StagedForward:
         if self.mx:
             self.g1 = M.GemmFwdArgs(dtype, M.MOE_EPI_SWIGLU, d.E, rc, d.D, d.H, P(sv["offsets"]),
                                     P(sv["xd_q"]), P(sv["xd_s"]), P(q["wg_q"]), P(q["wg_s"]),
-                                    P(q["wu_q"]), P(q["wu_s"]), P(sv["g"]), P(sv["u"]), P(sv["h"]),
+                                    P(q["wu_q"]), P(q["wu_s"]), P(sv["g"]), P(sv["u"]), P(sv.get("h")),
                                     P(sv["h_q"]), P(sv["h_s"]))
             self.g2 = M.GemmFwdArgs(dtype, M.MOE_EPI_NONE, d.E, rc, d.H, d.D, P(sv["offsets"]),
                                     P(sv["h_q"]), P(sv["h_s"]), P(q["wd_q"]), P(q["wd_s"]), None, None,
@@ -371,7 +371,9 @@ def cpu_baseline(inp, wl, budget_s=20.0):
     n, dt = res
     return dict(value=n / dt, unit="tokens/s", cores=_host_threads(), kind="oracle",
                 sample=f"first {n} of {wl.N} tokens of the same workload, full expert weights, "
-                       f"numpy float64 ({dt:.1f} s)")
+                       f"numpy float64 ({dt:.1f} s)",
+                host_cpus=os.cpu_count(), cpu_model=_cpu_model(),
+                note="cores = the BLAS threads the oracle ran on; host_cpus = os.cpu_count()")
 
 
 def _sample_mxfp8_weights(O, inp, wl, n, drop):
@@ -390,6 +392,17 @@ def _sample_mxfp8_weights(O, inp, wl, n, drop):
     return wq
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _host_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -401,6 +414,158 @@ def _host_threads():
     return os.cpu_count() or 1
 
 
+# the workloads measured after the headline in the same run (their step
+# times, GEMM rates and permute bandwidths; the tiny case is a parity case)
+EXTRA_WORKLOADS = ("mixtral_bf16", "qwen3_235b_bf16_fwdbwd", "dsv3_mxfp8")
+
+
+def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False):
+    """Time `steps` steps of one workload (after `warmup`), inputs resident in
+    HBM; returns the result dict of the JSON line (without cpu_baseline)."""
+    bwd = wl.bwd or backward
+    t0 = time.perf_counter()
+    x, w, drop = device_inputs(M, inp, wl.mxfp8, torch, backward=bwd)
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=bwd,
+                       router_bwd=bwd)
+    dout_bits = inp.dout if inp.dout is not None else (S.random_bf16((wl.N, wl.D), seed, 9) if bwd else None)
+    dout = (torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
+            if bwd else None)
+    st = StagedForward(M, layer, x)
+    torch.cuda.synchronize()
+    print(f"# {wl.name}: resident on the GPU in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # one step: the staged forward, and for a forward+backward workload the
+    # layer backward (combine-bwd, down dgrad/wgrad with the SwiGLU backward,
+    # gate/up dgrad/wgrad, router-prob grads, the router backward: dlogits,
+    # dX_r, dW_r, db_r; dispatch-bwd folding in dX_r) after it
+    def step(ev=None, ev_b=None):
+        st.run(ev)
+        if bwd:
+            layer.backward(x, dout)
+            if ev_b is not None:
+                ev_b.record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nst = len(StagedForward.STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        step(evs[k], evb[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+                for i, name in enumerate(StagedForward.STAGES)}
+    fwd_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(steps)]))
+    bwd_ms = (float(np.mean([evs[k][nst].elapsed_time(evb[k]) for k in range(steps)])) if bwd else 0.0)
+    total_ms = fwd_ms + bwd_ms
+    gpu_ms = evs[0][0].elapsed_time(evb[-1] if bwd else evs[-1][nst]) / steps
+
+    def time_layer(lay):
+        for _ in range(2):
+            lay.forward(x)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            lay.forward(x)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    layer_ms = time_layer(layer) if (layer_call or shared_expert) else None
+    shared = None
+    if shared_expert:
+        ws = shared_expert_weights(M, w, wl, seed, torch)
+        lay_s = M.MoeLayer(ws, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm)
+        shared = {"layer_fwd_ms": time_layer(lay_s), "routed_only_layer_fwd_ms": layer_ms,
+                  "note": "moe_layer_fwd with one shared expert (expert E over every token) in the same "
+                          "grouped-GEMM launches"}
+        del lay_s, ws
+
+    counts = layer.saved["counts"].cpu().numpy()
+    stats = load_stats(counts, wl.align)
+    R = int(counts.sum())
+    E_act = stats["active"]
+    N, D, E, K, H = wl.N, wl.D, wl.E, wl.K, wl.H
+    b = (1 + 1 / 32) if wl.mxfp8 else 2.0
+    peak = PEAK_MXFP8_TFLOPS if wl.mxfp8 else PEAK_BF16_TFLOPS
+    F1, Q1 = gemm1_work(R, D, H, E_act, b)
+    F2, Q2 = gemm2_work(R, D, H, E_act, b)
+    t1 = stage_ms["gemm1"] / 1e3
+    t2 = stage_ms["gemm2"] / 1e3
+    bound1 = "hbm" if Q1 / (PEAK_HBM_GBS * 1e9) >= F1 / (peak * 1e12) else "mfma"
+    if bound1 == "hbm":
+        roof = dict(bound="hbm", achieved=Q1 / t1 / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=F1 / t1 / 1e12, peak=peak, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(wl.name, seed)
+    roof["kernel"] = "gemm1 (grouped gate/up GEMM with SwiGLU epilogue)"
+    roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
+
+    gemm_tflops = routed_flops(R, D, H) / (t1 + t2) / 1e12
+    qd = dispatch_bytes(N, D, K, R, b)
+    qc = combine_bytes(N, D, K, R)
+    tstar_layer = sum([t_star(*router_work(N, D, E), peak), qd / (PEAK_HBM_GBS * 1e9), t_star(F1, Q1, peak),
+                       t_star(F2, Q2, peak), qc / (PEAK_HBM_GBS * 1e9)])
+    out = {
+        "metric": METRIC,
+        "value": N / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": total_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3/bf16" if wl.mxfp8 else "bf16",
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {"workload": wl.name, "N": N, "D": D, "E": E, "K": K, "H": H, "zipf_s": wl.zipf_s,
+                   "p_drop": wl.p_drop, "align": wl.align, "seed": seed,
+                   "pass": "fwd+bwd" if bwd else "fwd"},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": gemm_tflops, "pct_mfma_peak": 100 * gemm_tflops / peak,
+                         "gemm1_ms": stage_ms["gemm1"], "gemm2_ms": stage_ms["gemm2"],
+                         "pct_of_roofline": 100 * (t_star(F1, Q1, peak) + t_star(F2, Q2, peak)) / (t1 + t2)},
+        "dispatch": {"gbs": qd / (stage_ms["dispatch"] / 1e3) / 1e9,
+                     "pct_hbm": 100 * qd / (stage_ms["dispatch"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "ms": stage_ms["dispatch"]},
+        "combine": {"gbs": qc / (stage_ms["combine"] / 1e3) / 1e9,
+                    "pct_hbm": 100 * qc / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                    "ms": stage_ms["combine"]},
+        "stage_ms": stage_ms,
+        "layer_fwd_pct_of_roofline": 100 * tstar_layer / (fwd_ms / 1e3),
+        "load": dict(stats, routes=R),
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "gpu_span_ms_per_step": gpu_ms,
+    }
+    out["fwd_ms"] = fwd_ms
+    if bwd:
+        tf_b = routed_flops(R, D, H, backward=True) / (bwd_ms / 1e3) / 1e12
+        out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / PEAK_BF16_TFLOPS,
+                           "note": "value and ms_per_step cover forward + backward, router backward included; "
+                                   "routed_tflops counts the expert GEMMs only; pct_mfma_peak against the bf16 "
+                                   "peak" + (" (MXFP8: block-scaled dgrads, bf16 wgrads)" if wl.mxfp8 else "")}
+    if layer_ms is not None:
+        out["layer_call_ms"] = layer_ms
+    if shared is not None:
+        out["shared_expert"] = shared
+    del layer, st, x, w, drop, dout
+    return out
+
+
+def summary_of(r):
+    """The keys of a non-headline workload's result kept in the JSON line."""
+    keep = ("value", "unit", "ms_per_step", "fwd_ms", "dtype", "config", "roofline", "grouped_gemm", "dispatch",
+            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward")
+    return {k: r[k] for k in keep if k in r}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +574,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="dsv3_bf16", choices=sorted(S.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only --workload (by default the Mixtral-shaped forward, the Qwen3-shaped "
+                         "forward + backward and the MXFP8 forward follow, as extra keys)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--layer-call", action="store_true", help="also time moe_layer_fwd as one call")
     ap.add_argument("--backward", action="store_true",
@@ -459,20 +627,10 @@ def main(argv=None):
     import mixture_experts_expert_router_amd as M
 
     wl = S.WORKLOADS[args.workload]
-    bwd = wl.bwd or args.backward
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     inp = S.make_inputs(wl, args.seed)
-    x, w, drop = device_inputs(M, inp, wl.mxfp8, torch, backward=bwd)
-    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=bwd,
-                       router_bwd=bwd)
-    dout_bits = inp.dout if inp.dout is not None else (S.random_bf16((wl.N, wl.D), args.seed, 9) if bwd else None)
-    dout = (torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
-            if bwd else None)
-    st = StagedForward(M, layer, x)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t0
-    print(f"# setup {setup_s:.1f}s (inputs generated and resident)", file=sys.stderr, flush=True)
+    print(f"# inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
     if args.copy_probe:
         n = args.copy_probe << 20
@@ -484,127 +642,28 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    # one step: the staged forward, and for a forward+backward workload the
-    # layer backward (combine-bwd, down dgrad/wgrad with the SwiGLU backward,
-    # gate/up dgrad/wgrad, router-prob grads, the router backward: dlogits,
-    # dX_r, dW_r, db_r; dispatch-bwd folding in dX_r) after it
-    def step(ev=None, ev_b=None):
-        st.run(ev)
-        if bwd:
-            layer.backward(x, dout)
-            if ev_b is not None:
-                ev_b.record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    nst = len(StagedForward.STAGES)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
-    evb = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k], evb[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-                for i, name in enumerate(StagedForward.STAGES)}
-    fwd_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][nst]) for k in range(args.steps)]))
-    bwd_ms = (float(np.mean([evs[k][nst].elapsed_time(evb[k]) for k in range(args.steps)])) if bwd else 0.0)
-    total_ms = fwd_ms + bwd_ms
-    gpu_ms = evs[0][0].elapsed_time(evb[-1] if bwd else evs[-1][nst]) / args.steps
-
-    def time_layer(lay):
-        for _ in range(2):
-            lay.forward(x)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            lay.forward(x)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    layer_ms = time_layer(layer) if (args.layer_call or args.shared_expert) else None
-    shared = None
-    if args.shared_expert:
-        ws = shared_expert_weights(M, w, wl, args.seed, torch)
-        lay_s = M.MoeLayer(ws, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm)
-        shared = {"layer_fwd_ms": time_layer(lay_s), "routed_only_layer_fwd_ms": layer_ms,
-                  "note": "moe_layer_fwd with one shared expert (expert E over every token) in the same "
-                          "grouped-GEMM launches"}
-        del lay_s, ws
-
-    counts = layer.saved["counts"].cpu().numpy()
-    stats = load_stats(counts, wl.align)
-    R = int(counts.sum())
-    E_act = stats["active"]
-    N, D, E, K, H = wl.N, wl.D, wl.E, wl.K, wl.H
-    b = (1 + 1 / 32) if wl.mxfp8 else 2.0
-    peak = PEAK_MXFP8_TFLOPS if wl.mxfp8 else PEAK_BF16_TFLOPS
-    F1, Q1 = gemm1_work(R, D, H, E_act, b)
-    F2, Q2 = gemm2_work(R, D, H, E_act, b)
-    t1 = stage_ms["gemm1"] / 1e3
-    t2 = stage_ms["gemm2"] / 1e3
-    bound1 = "hbm" if Q1 / (PEAK_HBM_GBS * 1e9) >= F1 / (peak * 1e12) else "mfma"
-    if bound1 == "hbm":
-        roof = dict(bound="hbm", achieved=Q1 / t1 / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
-    else:
-        roof = dict(bound="mfma", achieved=F1 / t1 / 1e12, peak=peak, unit="TFLOP/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(wl.name, args.seed)
-    roof["kernel"] = "gemm1 (grouped gate/up GEMM with SwiGLU epilogue)"
-    roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
-
-    gemm_tflops = routed_flops(R, D, H) / (t1 + t2) / 1e12
-    qd = dispatch_bytes(N, D, K, R, b)
-    qc = combine_bytes(N, D, K, R)
-    tstar_layer = sum([t_star(*router_work(N, D, E), peak), qd / (PEAK_HBM_GBS * 1e9), t_star(F1, Q1, peak),
-                       t_star(F2, Q2, peak), qc / (PEAK_HBM_GBS * 1e9)])
-    out = {
-        "metric": METRIC,
-        "value": N / (total_ms / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": total_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "mxfp8-e4m3/bf16" if wl.mxfp8 else "bf16",
-        "data": "synthetic (seeded; random-init weights of the stated shape)",
-        "config": {"workload": wl.name, "N": N, "D": D, "E": E, "K": K, "H": H, "zipf_s": wl.zipf_s,
-                   "p_drop": wl.p_drop, "align": wl.align, "seed": args.seed,
-                   "pass": "fwd+bwd" if bwd else "fwd"},
-        "roofline": roof,
-        "grouped_gemm": {"tflops": gemm_tflops, "pct_mfma_peak": 100 * gemm_tflops / peak,
-                         "gemm1_ms": stage_ms["gemm1"], "gemm2_ms": stage_ms["gemm2"],
-                         "pct_of_roofline": 100 * (t_star(F1, Q1, peak) + t_star(F2, Q2, peak)) / (t1 + t2)},
-        "dispatch": {"gbs": qd / (stage_ms["dispatch"] / 1e3) / 1e9,
-                     "pct_hbm": 100 * qd / (stage_ms["dispatch"] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                     "ms": stage_ms["dispatch"]},
-        "combine": {"gbs": qc / (stage_ms["combine"] / 1e3) / 1e9,
-                    "pct_hbm": 100 * qc / (stage_ms["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                    "ms": stage_ms["combine"]},
-        "stage_ms": stage_ms,
-        "layer_fwd_pct_of_roofline": 100 * tstar_layer / (fwd_ms / 1e3),
-        "load": dict(stats, routes=R),
-        "wall_ms_per_step": 1e3 * wall / args.steps,
-        "gpu_span_ms_per_step": gpu_ms,
-    }
-    out["fwd_ms"] = fwd_ms
-    if bwd:
-        tf_b = routed_flops(R, D, H, backward=True) / (bwd_ms / 1e3) / 1e12
-        out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / PEAK_BF16_TFLOPS,
-                           "note": "value and ms_per_step cover forward + backward, router backward included; "
-                                   "routed_tflops counts the expert GEMMs only; pct_mfma_peak against the bf16 "
-                                   "peak" + (" (MXFP8: block-scaled dgrads, bf16 wgrads)" if wl.mxfp8 else "")}
-    if layer_ms is not None:
-        out["layer_call_ms"] = layer_ms
-    if shared is not None:
-        out["shared_expert"] = shared
+    out = measure(M, torch, wl, inp, args.steps, args.warmup, args.seed, backward=args.backward,
+                  layer_call=args.layer_call, shared_expert=args.shared_expert)
+    if not args.headline_only:
+        # the other workloads of the same run, each its own step (parity cases
+        # aside from the headline): keys only, the headline value is above
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            if name == wl.name:
+                continue
+            wx = S.WORKLOADS[name]
+            t0 = time.perf_counter()
+            same_inputs = (wx.N, wx.D, wx.E, wx.K, wx.H, wx.zipf_s, wx.p_drop) == \
+                (wl.N, wl.D, wl.E, wl.K, wl.H, wl.zipf_s, wl.p_drop)
+            ix = inp if same_inputs else S.make_inputs(wx, args.seed)
+            print(f"# {name}: inputs in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+            r = measure(M, torch, wx, ix, args.steps, args.warmup, args.seed)
+            extra[name] = summary_of(r)
+            print(f"# {name}: {extra[name]['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+            del ix
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

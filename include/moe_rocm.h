@@ -45,13 +45,25 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define MOE_OK 0
 #define MOE_ERR_NULL (-1)        /* a required pointer is NULL                    */
-#define MOE_ERR_SHAPE (-2)       /* N<0, K<1, K>E, E>1024, D or H not a multiple of
-                                    8 (32 for MXFP8), align not 1/32, N*K >= 2^31  */
+#define MOE_ERR_SHAPE (-2)       /* N<0, K<1, K>E, E + n_shared > 1024, D or H not a
+                                    multiple of 8 (32 for MXFP8), align not 1/32,
+                                    N*K >= 2^31                                     */
 #define MOE_ERR_DTYPE (-3)       /* unknown dtype or epilogue                      */
 #define MOE_ERR_WORKSPACE (-4)   /* workspace smaller than moe_workspace_size      */
 #define MOE_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned               */
 #define MOE_ERR_UNSUPPORTED (-6) /* valid request this build does not implement    */
 #define MOE_ERR_HIP (-7)         /* a kernel launch failed                         */
+
+/* ---- device status word ---------------------------------------------------
+ * moe_layer_fwd writes these bits into the optional device int32
+ * moe_layer_saved.status (0 = nothing to report).  They describe device-side
+ * events that no host check can see; the call itself has returned MOE_OK. */
+#define MOE_STATUS_WAIT_EXPIRED 1   /* MOE_SCHED_READY: a bounded readiness wait gave
+                                       up; the items that waited were skipped, so
+                                       G, U, H, Y and the output are incomplete      */
+#define MOE_STATUS_NO_FINITE_LOGIT 2 /* a token had fewer than K non-NaN logits; each
+                                       slot left without one has topk_idx = -1,
+                                       probability 0 and no row (an invalid route)   */
 
 /* ---- enums ------------------------------------------------------------- */
 #define MOE_BF16 0
@@ -134,7 +146,9 @@ int moe_router_logits(const void* x, const void* w_r, const float* bias, const m
  *   dst_rows  int32 [N][K]  row of each route, -1 if invalid
  *   row_route int32 [rows_cap] route id held by each row, -1 for padding/unused
  * drop: u8 [N][K] or NULL; a non-zero entry marks that route invalid (it keeps
- * its topk_idx/topk_prob but gets no row).  ws: moe_workspace_size(MOE_OP_ROUTE). */
+ * its topk_idx/topk_prob but gets no row).  ws: moe_workspace_size(MOE_OP_ROUTE).
+ * NaN logits never win a slot; a slot left with no candidate (fewer than K
+ * non-NaN logits) gets topk_idx -1, probability 0 and no row. */
 int moe_route(const float* logits, const uint8_t* drop, const moe_dims* d, int32_t* topk_idx,
               float* topk_prob, int32_t* counts, int32_t* offsets, int32_t* dst_rows,
               int32_t* row_route, void* ws, size_t ws_bytes, void* stream);
@@ -227,7 +241,8 @@ typedef struct moe_gemm_fwd_args {
   const uint8_t* b1_scales;
   void* c0;                 /* bf16 [rows_cap][n_dim] */
   void* c1;                 /* SWIGLU: bf16 [rows_cap][n_dim] */
-  void* act;                /* SWIGLU: bf16 [rows_cap][n_dim] */
+  void* act;                /* SWIGLU: bf16 [rows_cap][n_dim]; may be NULL for MXFP8
+                               when act_q is given (H then only stored quantized) */
   uint8_t* act_q;           /* optional: u8 [rows_cap][n_dim] */
   uint8_t* act_scales;      /* optional: u8 [rows_cap][n_dim/32] */
 } moe_gemm_fwd_args;
@@ -273,7 +288,8 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * into `saved` (OLMo-core Appendix A, A.1 fused routed-expert node and A.14
  * saved tensors; KOSMOS section 3.3.1 steps 1-5).  For MXFP8 the dispatch
  * quantizes (xd_q/xd_s), GEMM1 is block-scaled, H is quantized (h_q/h_s), and
- * GEMM2 is block-scaled; the combine is bf16.
+ * GEMM2 is block-scaled; the combine is bf16.  The MXFP8 forward stores H
+ * only quantized: saved->h is ignored there and may be NULL.
  * Backward: combine-bwd and dprob -> down dgrad with the SwiGLU
  * backward -> down wgrad -> gate/up dgrad (one sum) -> gate/up wgrad ->
  * dispatch-bwd (KOSMOS section 3.3.2).  The intermediates dY_d, dG, dU, dX_d
@@ -286,11 +302,17 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * saved activations dequantized from xd_q and h_q (OLMo-core Appendix A,
  * A.13: dgrad on the scaled grouped GEMM, wgrad in bf16 on dequantized
  * operands).  It reads the saved xd_q/xd_s, g, u, h_q/h_s, y and no bf16
- * expert weights; it needs D % 128 == 0 and H % 64 == 0 (else MOE_ERR_SHAPE). */
+ * expert weights; it needs D % 128 == 0 and H % 64 == 0 (else MOE_ERR_SHAPE).
+ * With saved->h_q NULL (SwiGLU-recompute mode, OLMo-core Appendix A, A.14:
+ * H is rebuilt in the backward instead of being saved) the down weight
+ * gradient takes H = bf16(silu(G) U) recomputed from the saved bf16 G and U
+ * instead of the dequantized h_q; h_s is then ignored. */
 #define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
 #define MOE_SCHED_READY 1   /* bf16: one persistent launch; GEMM1 tiles claimed in
                                the order dispatch finishes experts, GEMM2 tiles
-                               gated on their GEMM1 row blocks                   */
+                               gated on their GEMM1 row blocks.  MOE_ERR_UNSUPPORTED
+                               for MXFP8, a shared expert, or D, H off the rule
+                               D % 64 == 0 and H % 64 == 0                       */
 
 typedef struct moe_layer_args {
   moe_dims dims;
@@ -322,6 +344,13 @@ typedef struct moe_layer_args {
   const uint8_t* wdt_s;
   const uint8_t* wgut_q;
   const uint8_t* wgut_s;
+  /* Testing the status word only; 0 in normal use.  A positive value makes a
+   * MOE_SCHED_READY forward withhold its readiness flags and give up every
+   * bounded wait after this many polls, so that each wait expires, the
+   * waiting items are skipped, every kernel exits normally and
+   * MOE_STATUS_WAIT_EXPIRED is reported.  Ignored by the staged schedule. */
+  int32_t ready_test_polls;
+  int32_t reserved;     /* 0 */
 } moe_layer_args;
 
 typedef struct moe_layer_saved {
@@ -340,11 +369,25 @@ typedef struct moe_layer_saved {
   void* h;              /* bf16 [rows_cap][H]; may be NULL for moe_layer_bwd, which then
                            recomputes H = silu(G) U from g and u (KOSMOS's SwiGLU-recompute
                            mode), bitwise equal to the forward's H */
-  uint8_t* h_q;         /* MXFP8 [rows_cap][H] */
+  uint8_t* h_q;         /* MXFP8 [rows_cap][H]; may be NULL for moe_layer_bwd (recompute) */
   uint8_t* h_s;         /* MXFP8 [rows_cap][H/32] */
   void* y;              /* bf16 [rows_cap][D] */
   float* aux;           /* fp32 [1], optional: the aux loss */
+  int32_t* status;      /* int32 [1], optional: the device status word (MOE_STATUS_*
+                           bits), written by every moe_layer_fwd that gets it */
 } moe_layer_saved;
+
+/* Bytes of one buffer that holds every tensor moe_layer_fwd saves for this
+ * shape and dtype (OLMo-core Appendix A, A.14: the saved set of the routed
+ * expert node), each at a 256-byte offset: logits, topk_idx, topk_prob,
+ * counts, offsets, dst_rows, row_route, then xd (bf16) or xd_q, xd_s (MXFP8),
+ * g, u, h (bf16) or h_q, h_s (MXFP8; no bf16 H), y, aux and status.
+ * 0 if the dims are invalid. */
+size_t moe_saved_size(const moe_dims* d, int dtype);
+/* Points every field of *out into base (moe_saved_size bytes, 256-byte
+ * aligned, caller-owned) in the order above; fields the dtype does not use
+ * are set to NULL.  Returns a status code. */
+int moe_saved_carve(const moe_dims* d, int dtype, void* base, size_t bytes, moe_layer_saved* out);
 
 int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* saved, void* out, void* ws,
                   size_t ws_bytes, void* stream);

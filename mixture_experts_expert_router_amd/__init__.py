@@ -13,6 +13,8 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+
+import numpy as np
 from dataclasses import dataclass
 from typing import Optional
 
@@ -56,13 +58,19 @@ class LayerArgs(C.Structure):
                 ("bias", _vp), ("drop", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("wg_q", _vp), ("wg_s", _vp), ("wu_q", _vp), ("wu_s", _vp), ("wd_q", _vp),
                 ("wd_s", _vp), ("aux_alpha", C.c_float), ("wdt_q", _vp), ("wdt_s", _vp), ("wgut_q", _vp),
-                ("wgut_s", _vp)]
+                ("wgut_s", _vp), ("ready_test_polls", _i32), ("reserved", _i32)]
 
 
 class LayerSaved(C.Structure):
     _fields_ = [(n, _vp) for n in ("logits", "topk_idx", "topk_prob", "counts", "offsets",
                                    "dst_rows", "row_route", "xd", "xd_q", "xd_s", "g", "u", "h",
-                                   "h_q", "h_s", "y", "aux")]
+                                   "h_q", "h_s", "y", "aux", "status")]
+
+# moe_layer_saved fields in order, with their element type and shape
+# (rows_cap rc, Ex = E + n_shared experts) as moe_saved_carve lays them out
+_SAVED_FIELDS = ("logits", "topk_idx", "topk_prob", "counts", "offsets", "dst_rows", "row_route", "xd",
+                 "xd_q", "xd_s", "g", "u", "h", "h_q", "h_s", "y", "aux", "status")
+MOE_STATUS_WAIT_EXPIRED, MOE_STATUS_NO_FINITE_LOGIT = 1, 2
 
 
 class LayerGrads(C.Structure):
@@ -86,6 +94,8 @@ EXPORTS = {
     "moe_swiglu": (C.c_int, [_vp, _vp, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_fwd": (C.c_int, [C.POINTER(GemmFwdArgs), _vp, C.c_size_t, _vp]),
     "moe_grouped_gemm_bwd": (C.c_int, [C.POINTER(GemmBwdArgs), _vp, C.c_size_t, _vp]),
+    "moe_saved_size": (C.c_size_t, [C.POINTER(Dims), C.c_int]),
+    "moe_saved_carve": (C.c_int, [C.POINTER(Dims), C.c_int, _vp, C.c_size_t, C.POINTER(LayerSaved)]),
     "moe_layer_fwd": (C.c_int, [C.POINTER(LayerArgs), C.POINTER(LayerSaved), _vp, _vp, C.c_size_t, _vp]),
     "moe_layer_bwd": (C.c_int, [C.POINTER(LayerArgs), C.POINTER(LayerSaved), _vp,
                                 C.POINTER(LayerGrads), _vp, C.c_size_t, _vp]),
@@ -394,28 +404,44 @@ def _layer_args(x, wts: LayerWeights, K, drop, renorm, mxfp8, sched=MOE_SCHED_ST
 
 
 def alloc_saved(d: Dims, mxfp8: bool, device):
+    """One buffer of moe_saved_size bytes, carved by moe_saved_carve; returns
+    the dict of torch views of every field the dtype uses (plus "_buf")."""
     torch = _torch()
+    lib = load()
+    dt = MOE_MXFP8 if mxfp8 else MOE_BF16
+    n = lib.moe_saved_size(C.byref(d), dt)
+    if n == 0:
+        raise MoeError("moe_saved_size: invalid dims")
+    buf = torch.empty(int(n) + 256, dtype=torch.uint8, device=device)
+    base = (buf.data_ptr() + 255) // 256 * 256
+    sv_c = LayerSaved()
+    _check(lib.moe_saved_carve(C.byref(d), dt, base, int(n), C.byref(sv_c)), "moe_saved_carve")
     N, D, E, K, H = d.N, d.D, d.E, d.K, d.H
-    rc = rows_cap(d)
-    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=device)
-    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=device)
-    sv = dict(logits=torch.empty((N, E), dtype=torch.float32, device=device),
-              topk_idx=torch.empty((N, K), dtype=torch.int32, device=device),
-              topk_prob=torch.empty((N, K), dtype=torch.float32, device=device),
-              counts=torch.empty(E + d.n_shared, dtype=torch.int32, device=device),
-              offsets=torch.empty(E + d.n_shared + 1, dtype=torch.int32, device=device),
-              dst_rows=torch.empty((N, K), dtype=torch.int32, device=device),
-              row_route=torch.empty(rc, dtype=torch.int32, device=device),
-              g=bf(rc, H), u=bf(rc, H), h=bf(rc, H), y=bf(rc, D))
-    if mxfp8:
-        sv.update(xd_q=u8(rc, D), xd_s=u8(rc, D // 32), h_q=u8(rc, H), h_s=u8(rc, H // 32))
-    else:
-        sv.update(xd=bf(rc, D))
+    rc, Ex = rows_cap(d), d.E + d.n_shared
+    f32, i32, bf, u8 = torch.float32, torch.int32, torch.bfloat16, torch.uint8
+    spec = dict(logits=(f32, (N, E)), topk_idx=(i32, (N, K)), topk_prob=(f32, (N, K)), counts=(i32, (Ex,)),
+                offsets=(i32, (Ex + 1,)), dst_rows=(i32, (N, K)), row_route=(i32, (rc,)), xd=(bf, (rc, D)),
+                xd_q=(u8, (rc, D)), xd_s=(u8, (rc, D // 32)), g=(bf, (rc, H)), u=(bf, (rc, H)), h=(bf, (rc, H)),
+                h_q=(u8, (rc, H)), h_s=(u8, (rc, H // 32)), y=(bf, (rc, D)), aux=(f32, (1,)), status=(i32, (1,)))
+    sv = {"_buf": buf}
+    for name in _SAVED_FIELDS:
+        p = getattr(sv_c, name)
+        if p is None:
+            continue
+        dtype, shape = spec[name]
+        off = p - buf.data_ptr()
+        nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        sv[name] = buf[off:off + nbytes].view(dtype).view(shape)
     return sv
 
 
 def _saved_struct(sv: dict) -> LayerSaved:
     return LayerSaved(*[_ptr(sv.get(n)) for n, _ in LayerSaved._fields_])
+
+
+def saved_tensors(sv: dict) -> dict:
+    """The saved tensors without the backing buffer."""
+    return {k: v for k, v in sv.items() if not k.startswith("_")}
 
 
 class MoeLayer:
@@ -436,9 +462,8 @@ class MoeLayer:
         self._x_proto = torch.empty((N, D), dtype=torch.bfloat16, device=device)
         _, self.d = _layer_args(self._x_proto, wts, K, drop, renorm, mxfp8, **self._opts)
         self.saved = alloc_saved(self.d, mxfp8, device)
-        if aux_alpha:
-            self.saved["aux"] = torch.zeros(1, dtype=torch.float32, device=device)
         self._sv = _saved_struct(self.saved)
+        self.ready_test_polls = 0      # testing the status word of the READY schedule only
         self.out = torch.empty((N, D), dtype=torch.bfloat16, device=device)
         self.ws_f = workspace(MOE_OP_LAYER_FWD, self.d, device)
         self.grads = None
@@ -460,13 +485,14 @@ class MoeLayer:
 
     def forward(self, x):
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched, **self._opts)
+        a.ready_test_polls = int(self.ready_test_polls)
         _check(load().moe_layer_fwd(C.byref(a), C.byref(self._sv), _ptr(self.out), _ptr(self.ws_f),
                                     self.ws_f.numel(), _stream()), "moe_layer_fwd")
         return self.out
 
     def backward(self, x, dout, recompute_h=False, d_aux=0.0):
-        """recompute_h: do not read the saved H; the library recomputes it from G and U
-        (bf16; the MXFP8 backward reads the saved h_q instead).
+        """recompute_h: do not read the saved H (bf16) or H codes (MXFP8); the
+        library recomputes H from the saved G and U (SwiGLU-recompute mode).
         d_aux: upstream gradient of the aux loss (used when aux_alpha != 0)."""
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, **self._opts)
         self._gr.d_aux = float(d_aux)
@@ -474,6 +500,8 @@ class MoeLayer:
         if recompute_h:
             sv = LayerSaved(*[getattr(self._sv, n) for n, _ in LayerSaved._fields_])
             sv.h = None
+            sv.h_q = None
+            sv.h_s = None
         _check(load().moe_layer_bwd(C.byref(a), C.byref(sv), _ptr(dout), C.byref(self._gr),
                                     _ptr(self.ws_b), self.ws_b.numel(), _stream()), "moe_layer_bwd")
         return self.grads

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 
 #include "../../include/moe_rocm.h"
 #include "launch.h"
@@ -43,6 +44,7 @@ int check_dims(const moe_dims* d, bool need_h, bool mxfp8) {
   if (mxfp8 && (d->D % 32 || (need_h && d->H % 32) || d->align != 32)) return MOE_ERR_SHAPE;
   if (d->N * d->K >= (int64_t(1) << 31) || rows_cap_of(*d) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (d->n_group < 0 || d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_SHAPE;
+  if (experts_of(*d) > kMaxE) return MOE_ERR_SHAPE;   // the planners give one thread per expert
   if (d->n_group > 1 && (d->n_group > 64 || d->E % d->n_group || d->topk_group < 1 ||
                          d->topk_group > d->n_group || d->topk_group * (d->E / d->n_group) < d->K))
     return MOE_ERR_SHAPE;
@@ -163,6 +165,37 @@ BwdLayout bwd_layout(const moe_dims& d, bool mx) {
 
 size_t bwd_scratch_bytes(const moe_dims& d, bool mx) { return bwd_layout(d, mx).total; }
 
+// The saved set carved from one buffer, every tensor at a 256-byte offset;
+// at[i] = SIZE_MAX marks a field the dtype does not use.
+struct SavedLayout {
+  size_t at[18];
+  size_t total;
+};
+
+SavedLayout saved_layout(const moe_dims& d, bool mx) {
+  SavedLayout l{};
+  const size_t N = (size_t)d.N, D = (size_t)d.D, E = (size_t)d.E, K = (size_t)d.K, H = (size_t)d.H;
+  const size_t Ex = (size_t)experts_of(d), rc = (size_t)rows_cap_of(d);
+  const size_t none = SIZE_MAX;
+  // logits, topk_idx, topk_prob, counts, offsets, dst_rows, row_route, xd, xd_q,
+  // xd_s, g, u, h, h_q, h_s, y, aux, status (the field order of moe_layer_saved)
+  const size_t bytes[18] = {N * E * 4, N * K * 4, N * K * 4, Ex * 4, (Ex + 1) * 4, N * K * 4, rc * 4,
+                            mx ? none : rc * D * 2, mx ? rc * D : none, mx ? rc * D / 32 : none,
+                            rc * H * 2, rc * H * 2, mx ? none : rc * H * 2, mx ? rc * H : none,
+                            mx ? rc * H / 32 : none, rc * D * 2, 4, 4};
+  size_t o = 0;
+  for (int i = 0; i < 18; ++i) {
+    if (bytes[i] == none) {
+      l.at[i] = none;
+      continue;
+    }
+    l.at[i] = o;
+    o += round_up(bytes[i] > 0 ? bytes[i] : 1, 256);
+  }
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +214,45 @@ size_t moe_workspace_size(int op, const moe_dims* d) {
     case MOE_OP_LAYER_BWD_MXFP8: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, true);
     default: return 0;
   }
+}
+
+size_t moe_saved_size(const moe_dims* d, int dtype) {
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return 0;
+  if (check_dims(d, true, dtype == MOE_MXFP8)) return 0;
+  return saved_layout(*d, dtype == MOE_MXFP8).total;
+}
+
+int moe_saved_carve(const moe_dims* d, int dtype, void* base, size_t bytes, moe_layer_saved* out) {
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  const bool mx = dtype == MOE_MXFP8;
+  int st = check_dims(d, true, mx);
+  if (st) return st;
+  if (!out) return MOE_ERR_NULL;
+  REQUIRE(base);
+  if ((uintptr_t)base & 255u) return MOE_ERR_ALIGN;
+  const SavedLayout l = saved_layout(*d, mx);
+  if (bytes < l.total) return MOE_ERR_WORKSPACE;
+  void* p[18];
+  for (int i = 0; i < 18; ++i) p[i] = l.at[i] == SIZE_MAX ? nullptr : (char*)base + l.at[i];
+  out->logits = (float*)p[0];
+  out->topk_idx = (int32_t*)p[1];
+  out->topk_prob = (float*)p[2];
+  out->counts = (int32_t*)p[3];
+  out->offsets = (int32_t*)p[4];
+  out->dst_rows = (int32_t*)p[5];
+  out->row_route = (int32_t*)p[6];
+  out->xd = p[7];
+  out->xd_q = (uint8_t*)p[8];
+  out->xd_s = (uint8_t*)p[9];
+  out->g = p[10];
+  out->u = p[11];
+  out->h = p[12];
+  out->h_q = (uint8_t*)p[13];
+  out->h_s = (uint8_t*)p[14];
+  out->y = p[15];
+  out->aux = (float*)p[16];
+  out->status = (int32_t*)p[17];
+  return MOE_OK;
 }
 
 const char* moe_status_string(int s) {
@@ -357,7 +429,8 @@ int moe_grouped_gemm_fwd(const moe_gemm_fwd_args* g, void* ws, size_t ws_bytes, 
   if (sw) {
     REQUIRE(g->b1);
     REQUIRE(g->c1);
-    REQUIRE(g->act);
+    if (mx && g->act_q) OPTIONAL(g->act);   // H may be kept quantized only
+    else REQUIRE(g->act);
     if (mx) REQUIRE(g->b1_scales);
   }
   OPTIONAL(g->act_q);
@@ -426,11 +499,16 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (!a || !sv) return MOE_ERR_NULL;
   if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY) return MOE_ERR_DTYPE;
-  if (a->sched == MOE_SCHED_READY && a->dims.n_shared) return MOE_ERR_UNSUPPORTED;
   const bool mx = a->dtype == MOE_MXFP8;
   const moe_dims& d = a->dims;
   int st = check_dims(&d, true, mx);
   if (st) return st;
+  const bool ready = a->sched == MOE_SCHED_READY;
+  // the readiness-ordered launch is the bf16 persistent engine, routed experts only
+  if (ready && (mx || d.n_shared || d.align != 1 || !moe::gemm_fwd_fast_ok(d.D, d.H) ||
+                !moe::gemm_fwd_fast_ok(d.H, d.D)))
+    return MOE_ERR_UNSUPPORTED;
+  if (a->ready_test_polls < 0) return MOE_ERR_SHAPE;
   REQUIRE(a->x);
   REQUIRE(a->w_r);
   OPTIONAL(a->bias);
@@ -446,9 +524,10 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   REQUIRE(sv->row_route);
   REQUIRE(sv->g);
   REQUIRE(sv->u);
-  REQUIRE(sv->h);
   REQUIRE(sv->y);
+  OPTIONAL(sv->status);
   if (mx) {
+    OPTIONAL(sv->h);   // not written: the MXFP8 path keeps H quantized only
     REQUIRE(a->wg_q);
     REQUIRE(a->wg_s);
     REQUIRE(a->wu_q);
@@ -464,6 +543,7 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     REQUIRE(a->w_up);
     REQUIRE(a->w_down);
     REQUIRE(sv->xd);
+    REQUIRE(sv->h);
   }
   OPTIONAL(sv->aux);
   const bool aux = sv->aux != nullptr && a->aux_alpha != 0.0f;
@@ -477,11 +557,13 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   int32_t* table = (int32_t*)((char*)ws + rb);
   void* ws_router = (char*)ws + rb + tb;
 
-  hipError_t e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, ws_router, s);
+  hipError_t e = sv->status ? moe::launch_status_clear(sv->status, s) : hipSuccess;
+  if (e == hipSuccess)
+    e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, ws_router, s);
   if (e == hipSuccess)
     e = moe::launch_route(sv->logits, a->drop, d.N, d.E, d.K, d.renorm, d.align, rc, sv->topk_idx,
                           sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,
-                          ws_route, s, d.n_group, d.topk_group, aux, d.n_shared);
+                          ws_route, s, d.n_group, d.topk_group, aux, d.n_shared, sv->status);
   if (e == hipSuccess && aux) e = moe::launch_aux_loss(ws_route, d.N, d.E, d.K, sv->counts, a->aux_alpha, sv->aux, s);
   if (mx) {
     // quantize-on-dispatch; the same launch zeroes the padding rows
@@ -489,16 +571,15 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
       e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s, shared_row0,
                                      sv->counts, sv->offsets, Ex);
     moe::GemmFwd g1{Ex, rc, d.D, d.H, sv->offsets, sv->xd_q, sv->xd_s, a->wg_q, a->wg_s, a->wu_q,
-                    a->wu_s, sv->g, sv->u, sv->h, sv->h_q, sv->h_s, true};
+                    a->wu_s, sv->g, sv->u, nullptr, sv->h_q, sv->h_s, true};
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g1, table, s);
     moe::GemmFwd g2{Ex, rc, d.H, d.D, sv->offsets, sv->h_q, sv->h_s, a->wd_q, a->wd_s, nullptr,
                     nullptr, sv->y, nullptr, nullptr, nullptr, nullptr, false};
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g2, table, s);
-  } else if (a->sched == MOE_SCHED_READY && d.align == 1 && moe::gemm_fwd_fast_ok(d.D, d.H) &&
-             moe::gemm_fwd_fast_ok(d.H, d.D)) {
+  } else if (ready) {
     // dispatch, GEMM1 and GEMM2 in one persistent launch scheduled by readiness
     moe::ExpertsFwd xf{d.E, d.K, d.D, d.H, rc, sv->offsets, sv->row_route, a->x, a->w_gate, a->w_up,
-                       a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y};
+                       a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y, sv->status, a->ready_test_polls};
     if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
   } else {
     if (e == hipSuccess)
@@ -535,8 +616,8 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     REQUIRE(a->wgut_s);
     REQUIRE(sv->xd_q);
     REQUIRE(sv->xd_s);
-    REQUIRE(sv->h_q);
-    REQUIRE(sv->h_s);
+    OPTIONAL(sv->h_q);   // NULL: H recomputed from G and U for the down weight gradient
+    if (sv->h_q) REQUIRE(sv->h_s);
   } else {
     REQUIRE(a->w_gate);
     REQUIRE(a->w_up);
@@ -609,8 +690,12 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     if (e == hipSuccess) e = moe::launch_quantize_rows(dyd, rc, d.D, dyq, dys, s, rows_end);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(dn, true, table, s);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(gu, true, table, s);
-    // weight gradients: bf16 products on the dequantized activations
-    if (e == hipSuccess) e = moe::launch_dequant_rows(sv->h_q, sv->h_s, rc, d.H, rows_end, hdq, s);
+    // weight gradients: bf16 products on the dequantized activations; in the
+    // SwiGLU-recompute mode (no saved h_q) on H = silu(G) U rebuilt in bf16
+    if (e == hipSuccess) {
+      if (sv->h_q) e = moe::launch_dequant_rows(sv->h_q, sv->h_s, rc, d.H, rows_end, hdq, s);
+      else e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, hdq, nullptr, nullptr, s);
+    }
     if (e == hipSuccess) e = moe::launch_dequant_rows(sv->xd_q, sv->xd_s, rc, d.D, rows_end, xdq, s);
     moe::GemmBwd wd{Ex, rc, d.H, d.D, sv->offsets, hdq, nullptr, nullptr, dyd, nullptr, nullptr,
                     nullptr, nullptr, nullptr, nullptr, false};

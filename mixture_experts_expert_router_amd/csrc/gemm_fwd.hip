@@ -224,7 +224,7 @@ __device__ __forceinline__ void epilogue(const FwdParams& p, const Item& it, con
         const int64_t off = row * p.N + n;
         *reinterpret_cast<uint4*>(p.c0 + off) = gv;
         *reinterpret_cast<uint4*>(p.c1 + off) = uv;
-        *reinterpret_cast<uint4*>(p.c2 + off) = hv;
+        if (p.c2) *reinterpret_cast<uint4*>(p.c2 + off) = hv;   // MXFP8 may keep H quantized only
       }
       if (p.hq) {
         // a 32-column block of H is fragments (j, j+1) over the four lane
@@ -426,7 +426,9 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
 // never wait on later items, so the queue drains whatever the grid size.
 // Writers publish with an agent-scope release (fence, then atomic); readers
 // acquire before touching the data.  Waits are bounded: a wait that expires
-// sets the error word and the item proceeds, so no wave can hang.
+// or-s MOE_STATUS_WAIT_EXPIRED into the caller's status word and the item that
+// waited is skipped (no load, no store), so no wave can hang and nothing is
+// computed from unpublished data.
 // ---------------------------------------------------------------------------
 
 constexpr int kDispRows = 64;
@@ -440,6 +442,9 @@ struct FusedParams {
   int32_t* st;                  // queue state (zeroed by the planner)
   const int32_t* fplan;         // fused plan
   int nt1, nt2;                 // n-tiles of GEMM1 / GEMM2
+  int32_t* status;              // optional caller status word
+  int polls;                    // bound of every wait
+  int publish;                  // 0: readiness withheld (testing the bound)
 };
 
 // queue state layout (int32 units)
@@ -459,33 +464,35 @@ __device__ __forceinline__ int ld_relaxed(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// thread 0: wait until *p >= target (bounded); false if the bound expired
-__device__ __forceinline__ bool wait_ge(const int32_t* p, int target, int32_t* err) {
-  for (int it = 0; it < kSpinLimit; ++it) {
+// thread 0: wait until *p >= target (bounded); false if the bound expired,
+// which is recorded in the queue state and the caller's status word
+__device__ __forceinline__ bool wait_ge(const FusedParams& f, const int32_t* p, int target) {
+  for (int it = 0; it < f.polls; ++it) {
     if (ld_acquire(p) >= target) return true;
     __builtin_amdgcn_s_sleep(2);
   }
-  atomicExch(err, 1);
+  atomicOr(f.st + st_err(), 1);
+  if (f.status) atomicOr(f.status, 1);
   return false;
 }
 
 __device__ __forceinline__ int rows_bm(int rows) { return is_big(rows) ? 256 : 128; }
 
 // thread 0: find the ready position holding GEMM item j (units of nt tiles per
-// row block), walking forward from *pos; returns the expert and its first
-// row-block number in ready order.
-__device__ __forceinline__ void locate(const FusedParams& f, int j, int nt, int* pos, int* e_out, int* cum_out) {
+// row block), walking forward from *pos; gives the expert and its first
+// row-block number in ready order.  false if a wait expired: the item is then
+// skipped.
+__device__ __forceinline__ bool locate(const FusedParams& f, int j, int nt, int* pos, int* e_out, int* cum_out) {
   const int E = f.g1.E;
   int32_t* st = f.st;
   for (;;) {
     const int ps = *pos;
-    if (ps >= E) {   // only after an expired wait: stay in bounds, results are flagged
-      atomicExch(st + st_err(), 1);
-      *e_out = 0;
-      *cum_out = 0;
-      return;
+    if (ps >= E) {   // reached only after an expired wait left an expert unpublished
+      atomicOr(st + st_err(), 1);
+      if (f.status) atomicOr(f.status, 1);
+      return false;
     }
-    wait_ge(st + st_ready_ok(E) + ps, 1, st + st_err());
+    if (!wait_ge(f, st + st_ready_ok(E) + ps, 1)) return false;
     const int e = ld_relaxed(st + st_ready_e(E) + ps);
     const int cum = ld_relaxed(st + st_ready_cum(E) + ps);
     const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
@@ -493,7 +500,7 @@ __device__ __forceinline__ void locate(const FusedParams& f, int j, int nt, int*
     if (j < (cum + nmb) * nt) {
       *e_out = e;
       *cum_out = cum;
-      return;
+      return true;
     }
     *pos = ps + 1;
   }
@@ -561,8 +568,11 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
       __syncthreads();
       if (tid == 0) {
         const int m = m1 - m0;
-        const int done = atomicAdd(st + st_rows_done(E) + e, r1 - r0) + (r1 - r0);
-        if (done == m) {
+        // acquire-release: the workgroup that completes the expert acquires
+        // every other chunk's release, so its release below carries them all
+        const int done = __hip_atomic_fetch_add(st + st_rows_done(E) + e, r1 - r0, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT) + (r1 - r0);
+        if (done == m && f.publish) {
           const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
           const unsigned long long t =
               atomicAdd(reinterpret_cast<unsigned long long*>(st + st_ticket()), (1ull << 32) | (unsigned)nmb);
@@ -576,12 +586,13 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
       // ---- GEMM1 tile, experts in ready order ---------------------------------
       const int j = item - ND;
       if (tid == 0) {
-        int e, cum;
-        locate(f, j, f.nt1, &p1, &e, &cum);
+        int e = 0, cum = 0;
+        s_info[3] = locate(f, j, f.nt1, &p1, &e, &cum);
         s_info[1] = e;
         s_info[2] = cum;
       }
       __syncthreads();
+      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
       acquire_fence();
       const int e = s_info[1], cum = s_info[2];
       const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
@@ -598,16 +609,20 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
       // ---- GEMM2 tile, gated on its GEMM1 row block ----------------------------
       const int j = item - ND - N1;
       if (tid == 0) {
-        int e, cum;
-        locate(f, j, f.nt2, &p2, &e, &cum);
-        const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
-        const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
-        const int mb = (j - cum * f.nt2) % nmb;
-        wait_ge(st + st_g1_done(E) + cum + mb, f.nt1, st + st_err());
+        int e = 0, cum = 0;
+        bool ok = locate(f, j, f.nt2, &p2, &e, &cum);
+        if (ok) {
+          const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
+          const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
+          const int mb = (j - cum * f.nt2) % nmb;
+          ok = wait_ge(f, st + st_g1_done(E) + cum + mb, f.nt1);
+        }
+        s_info[3] = ok;
         s_info[1] = e;
         s_info[2] = cum;
       }
       __syncthreads();
+      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
       acquire_fence();
       const int e = s_info[1], cum = s_info[2];
       const int m0 = f.g2.offsets[e], m1 = f.g2.offsets[e + 1];
@@ -761,6 +776,9 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   st = (int32_t*)(((uintptr_t)st + 7) & ~(uintptr_t)7);   // 8-byte aligned ticket
   f.st = st;
   f.fplan = fplan;
+  f.status = x.status;
+  f.polls = x.test_polls > 0 ? x.test_polls : kSpinLimit;
+  f.publish = x.test_polls > 0 ? 0 : 1;
   const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
   plan_rows_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
   plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, fplan, st);

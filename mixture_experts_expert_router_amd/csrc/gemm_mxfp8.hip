@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_mxfp8_kernel(MxPar
         if (ok) {
           *reinterpret_cast<uint2*>(p.c0 + off) = make_uint2(gw0, gw1);
           *reinterpret_cast<uint2*>(p.c1 + off) = make_uint2(uw0, uw1);
-          *reinterpret_cast<uint2*>(p.c2 + off) = make_uint2(hw[j][0], hw[j][1]);
+          if (p.c2) *reinterpret_cast<uint2*>(p.c2 + off) = make_uint2(hw[j][0], hw[j][1]);
         }
       }
     }

@@ -72,7 +72,10 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
                         void* ws, hipStream_t s,
-                        int n_group = 0, int topk_group = 0, bool aux_inputs = false, int n_shared = 0);
+                        int n_group = 0, int topk_group = 0, bool aux_inputs = false, int n_shared = 0,
+                        int32_t* status = nullptr);
+// the device status word (moe_layer_saved.status) set to 0 on the stream
+hipError_t launch_status_clear(int32_t* status, hipStream_t s);
 // aux loss of the routed layer from the route step's probability sums (left
 // in the route workspace by launch_route with aux_inputs) and the counts
 hipError_t launch_aux_loss(void* route_ws, int64_t N, int64_t E, int64_t K, const int32_t* counts, float alpha,
@@ -133,6 +136,8 @@ struct ExpertsFwd {
   void* u;
   void* h;
   void* y;
+  int32_t* status;   // optional device status word: MOE_STATUS_WAIT_EXPIRED is or-ed in
+  int test_polls;    // > 0: withhold readiness, bound every wait to this many polls
 };
 
 // gemm_fwd.hip: persistent forward grouped GEMM, bf16 or MXFP8 (shape and

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, const uint8_t* __restrict__ drop, int N, int E, int K,
     int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
     int32_t* __restrict__ row_route, int64_t rows_cap, int32_t* __restrict__ hist,
-    int32_t* __restrict__ rank, int n_group, int topk_group, float* __restrict__ psum) {
+    int32_t* __restrict__ rank, int n_group, int topk_group, float* __restrict__ psum,
+    int32_t* __restrict__ status) {
   __shared__ int s_sel[kChunk * 32];      // K <= 32 checked on the host
   __shared__ int s_hist[kMaxE];
   extern __shared__ float s_row[];        // [kChunk][E] when grouped or psum
@@ -142,8 +143,15 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         int oi = __shfl_xor(bi, o, 64);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == k) { isel = bi; psel = expf(bv - mx) / se; }
+      // no candidate left only when the remaining logits are NaN: the slot
+      // becomes an invalid route (expert -1, probability 0, no row)
+      const bool found = bi != 0x7FFFFFFF;
+      if (found && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == k) {
+        isel = found ? bi : -1;
+        psel = found ? expf(bv - mx) / se : 0.0f;
+        if (!found && status) atomicOr(status, 2);
+      }
     }
     if (renorm) {
       float s = (lane < K) ? psel : 0.0f;
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       const int64_t r = (int64_t)t * K + lane;
       topk_idx[r] = isel;
       topk_prob[r] = psel;
-      const bool valid = drop == nullptr || drop[r] == 0;
+      const bool valid = (drop == nullptr || drop[r] == 0) && isel >= 0;
       s_sel[tl * K + lane] = valid ? isel : -1;
     }
   }
@@ -359,7 +367,8 @@ hipError_t launch_aux_loss(void* ws, int64_t N, int64_t E, int64_t K, const int3
 hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int64_t E, int64_t K,
                         int renorm, int align, int64_t rows_cap, int32_t* topk_idx, float* topk_prob,
                         int32_t* counts, int32_t* offsets, int32_t* dst_rows, int32_t* row_route,
-                        void* ws, hipStream_t s, int n_group, int topk_group, bool aux_inputs, int n_shared) {
+                        void* ws, hipStream_t s, int n_group, int topk_group, bool aux_inputs, int n_shared,
+                        int32_t* status) {
   const int64_t nchunks = (N + kChunk - 1) / kChunk;
   const int64_t nalloc = nchunks > 0 ? nchunks : 1;
   int32_t* hist = (int32_t*)ws;
@@ -378,7 +387,7 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
     kern<<<dim3(grid), dim3(kTopkThreads), lds_k, s>>>(logits, drop, Nk, (int)E, (int)K, renorm, topk_idx,
                                                        topk_prob, row_route, rows_cap, hist, rank,
                                                        nchunks > 0 ? ng : 0, nchunks > 0 ? topk_group : 0,
-                                                       nchunks > 0 ? psum : nullptr);
+                                                       nchunks > 0 ? psum : nullptr, status);
   };
   switch (npl) {
     case 1: go(route_topk_kernel<1>); break;
@@ -394,6 +403,13 @@ hipError_t launch_route(const float* logits, const uint8_t* drop, int64_t N, int
     route_scatter_kernel<<<dim3((unsigned)((NK + 255) / 256)), dim3(256), 0, s>>>(
         topk_idx, drop, hist, rank, NK, (int)K, (int)E, dst_rows, row_route);
   }
+  return hipGetLastError();
+}
+
+__global__ void status_clear_kernel(int32_t* status) { *status = 0; }
+
+hipError_t launch_status_clear(int32_t* status, hipStream_t s) {
+  status_clear_kernel<<<1, 1, 0, s>>>(status);
   return hipGetLastError();
 }
 

@@ -689,20 +689,22 @@ def expert_mlp_mxfp8(xq, xs, wgq, wgs, wuq, wus, wdq, wds):
     return G, U, Hh, hq, hs, Y
 
 
-def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, rows_cap=None, n_shared: int = 0):
+def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, rows_cap=None, n_shared: int = 0,
+                    logits=None):
     """MXFP8 forward: same route as bf16, groups padded to ``align`` rows,
     quantize-on-dispatch, block-scaled expert GEMMs, bf16 weighted combine.
 
     wq: dict with pre-quantized weights wg_q [E,H,D], wg_s [E,H,D/32], wu_q,
     wu_s, wd_q [E,D,H], wd_s [E,D,H/32] (one more expert, the shared one, with
     n_shared = 1, whose segment holds every token's quantized row).
+    ``logits`` may be given to skip the router product, as in layer_fwd.
     """
     xv = values(x)
     N, D = xv.shape
     E = np.asarray(w_r).shape[0]
     if rows_cap is None:
         rows_cap = N * K + E * (align - 1) + n_shared * (N + align - 1)
-    L = router_logits(x, w_r, bias)
+    L = router_logits(x, w_r, bias) if logits is None else np.asarray(logits, np.float32)
     idx = topk_select(L, K)
     prob = route_probs(L, idx, renorm)
     counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap, n_shared)

@@ -120,8 +120,8 @@ def test_struct_layouts_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     hdr = os.path.join(os.path.dirname(__file__), "..", "include", "moe_rocm.h")
     checks = {"moe_dims": (M.Dims, ["N", "renorm", "n_group", "topk_group"]),
-              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha", "wdt_q", "wgut_s"]),
-              "moe_layer_saved": (M.LayerSaved, ["logits", "y", "aux"]),
+              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha", "wdt_q", "wgut_s", "ready_test_polls"]),
+              "moe_layer_saved": (M.LayerSaved, ["logits", "y", "aux", "status"]),
               "moe_layer_grads": (M.LayerGrads, ["dx", "dlogits", "d_aux"]),
               "moe_gemm_fwd_args": (M.GemmFwdArgs, ["dtype", "act_scales"]),
               "moe_gemm_bwd_args": (M.GemmBwdArgs, ["dtype", "db1"])}
@@ -142,3 +142,82 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(out[st]) == C.sizeof(cls), st
         for f in fields:
             assert int(out[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
+def test_expert_count_limit_includes_the_shared_expert():
+    """E + n_shared experts go through one-thread-per-expert planners, so the
+    sum is limited to 1024 (E = 1024 with a shared expert is rejected)."""
+    lib = M.load()
+    assert lib.moe_saved_size(C.byref(M.dims(16, 64, 1024, 2, 64)), M.MOE_BF16) > 0   # E = 1024 alone is valid
+    for kw in (dict(E=1024, n_shared=1), dict(E=1025)):
+        d = M.dims(**dict(dict(N=16, D=64, K=2, H=64), **kw))
+        assert _route(lib, d) == -2, kw
+        assert lib.moe_saved_size(C.byref(d), M.MOE_BF16) == 0
+        a = M.LayerArgs(d, M.MOE_BF16)
+        sv = M.LayerSaved()
+        assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -2, kw
+
+
+def _full_saved(lib, d, dt, base=1 << 20):
+    sv = M.LayerSaved()
+    assert lib.moe_saved_carve(C.byref(d), dt, base, lib.moe_saved_size(C.byref(d), dt), C.byref(sv)) == 0
+    return sv
+
+
+def test_ready_schedule_is_refused_where_it_does_not_run():
+    """MOE_SCHED_READY exists for bf16 routed experts with D, H multiples of
+    64; MXFP8, a shared expert, and other widths get MOE_ERR_UNSUPPORTED
+    instead of silently running staged.  (Every pointer is a fake aligned
+    address: the call returns before any launch.)"""
+    lib = M.load()
+    cases = [(M.dims(64, 256, 8, 2, 128, align=32), M.MOE_MXFP8),
+             (M.dims(64, 256, 8, 2, 128, n_shared=1), M.MOE_BF16),
+             (M.dims(64, 264, 8, 2, 128), M.MOE_BF16),
+             (M.dims(64, 256, 8, 2, 136), M.MOE_BF16)]
+    for d, dt in cases:
+        a = M.LayerArgs(d, dt, M.MOE_SCHED_READY, *([1 << 20] * 15))
+        sv = _full_saved(lib, d, dt)
+        assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 1 << 20, 1 << 20, 1 << 40, None) == -6, (d.D, d.H, dt)
+    d = M.dims(64, 256, 8, 2, 128)
+    a = M.LayerArgs(d, M.MOE_BF16, M.MOE_SCHED_READY, *([1 << 20] * 15))
+    a.ready_test_polls = -1
+    sv = _full_saved(lib, d, M.MOE_BF16)
+    assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 1 << 20, 1 << 20, 1 << 40, None) == -2
+
+
+def test_saved_size_and_carve():
+    """moe_saved_size covers every saved tensor at 256-byte offsets in the
+    struct's field order; moe_saved_carve fills exactly the fields the dtype
+    uses (bf16: xd and h; MXFP8: xd_q, xd_s, h_q, h_s and no bf16 H)."""
+    lib = M.load()
+    r = lambda n: (n + 255) // 256 * 256
+    for dt, d in ((M.MOE_BF16, M.dims(100, 64, 8, 2, 96)), (M.MOE_MXFP8, M.dims(100, 64, 8, 2, 96, align=32)),
+                  (M.MOE_BF16, M.dims(100, 64, 8, 2, 96, n_shared=1))):
+        N, D, E, K, H = 100, 64, 8, 2, 96
+        Ex = E + d.n_shared
+        rc = lib.moe_rows_cap(C.byref(d))
+        mx = dt == M.MOE_MXFP8
+        sizes = dict(logits=N * E * 4, topk_idx=N * K * 4, topk_prob=N * K * 4, counts=Ex * 4,
+                     offsets=(Ex + 1) * 4, dst_rows=N * K * 4, row_route=rc * 4)
+        sizes.update(dict(xd_q=rc * D, xd_s=rc * D // 32) if mx else dict(xd=rc * D * 2))
+        sizes.update(g=rc * H * 2, u=rc * H * 2)
+        sizes.update(dict(h_q=rc * H, h_s=rc * H // 32) if mx else dict(h=rc * H * 2))
+        sizes.update(y=rc * D * 2, aux=4, status=4)
+        total = lib.moe_saved_size(C.byref(d), dt)
+        assert total == sum(r(v) for v in sizes.values())
+        base = 1 << 30
+        sv = M.LayerSaved()
+        assert lib.moe_saved_carve(C.byref(d), dt, base, total - 1, C.byref(sv)) == -4
+        assert lib.moe_saved_carve(C.byref(d), dt, base + 16, total, C.byref(sv)) == -5
+        assert lib.moe_saved_carve(C.byref(d), dt, None, total, C.byref(sv)) == -1
+        assert lib.moe_saved_carve(C.byref(d), 5, base, total, C.byref(sv)) == -3
+        assert lib.moe_saved_carve(C.byref(d), dt, base, total, C.byref(sv)) == 0
+        o = base
+        for name in M._SAVED_FIELDS:
+            p = getattr(sv, name)
+            if name in sizes:
+                assert p == o, name
+                o += r(sizes[name])
+            else:
+                assert p is None, name
+        assert o == base + total
