@@ -392,6 +392,21 @@ int moe_saved_carve(const moe_dims* d, int dtype, void* base, size_t bytes, moe_
 int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* saved, void* out, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_layer_fwd with its workspace in the library's own static
+ * device scratch of MOE_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU,
+ * held until the process ends.  The caller still passes every
+ * input, output and saved tensor.  No call allocates: not this function, not
+ * the kernels, not a library routine.  A shape whose
+ * moe_workspace_size(MOE_OP_LAYER_FWD) exceeds the scratch returns
+ * MOE_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's contents (each call rebuilds
+ * what it reads); calls that overlap on one GPU, on different streams or from
+ * different threads, race and must be serialized by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_fwd_noalloc(const moe_layer_args* a, moe_layer_saved* saved, void* out, void* stream);
+
 typedef struct moe_layer_grads {
   void* dx;        /* bf16 [N][D] */
   float* dprob;    /* fp32 [N][K] */

@@ -71,6 +71,7 @@ class LayerSaved(C.Structure):
 _SAVED_FIELDS = ("logits", "topk_idx", "topk_prob", "counts", "offsets", "dst_rows", "row_route", "xd",
                  "xd_q", "xd_s", "g", "u", "h", "h_q", "h_s", "y", "aux", "status")
 MOE_STATUS_WAIT_EXPIRED, MOE_STATUS_NO_FINITE_LOGIT = 1, 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LayerGrads(C.Structure):
@@ -97,6 +98,7 @@ EXPORTS = {
     "moe_saved_size": (C.c_size_t, [C.POINTER(Dims), C.c_int]),
     "moe_saved_carve": (C.c_int, [C.POINTER(Dims), C.c_int, _vp, C.c_size_t, C.POINTER(LayerSaved)]),
     "moe_layer_fwd": (C.c_int, [C.POINTER(LayerArgs), C.POINTER(LayerSaved), _vp, _vp, C.c_size_t, _vp]),
+    "moe_layer_fwd_noalloc": (C.c_int, [C.POINTER(LayerArgs), C.POINTER(LayerSaved), _vp, _vp]),
     "moe_layer_bwd": (C.c_int, [C.POINTER(LayerArgs), C.POINTER(LayerSaved), _vp,
                                 C.POINTER(LayerGrads), _vp, C.c_size_t, _vp]),
 }
@@ -488,6 +490,14 @@ class MoeLayer:
         a.ready_test_polls = int(self.ready_test_polls)
         _check(load().moe_layer_fwd(C.byref(a), C.byref(self._sv), _ptr(self.out), _ptr(self.ws_f),
                                     self.ws_f.numel(), _stream()), "moe_layer_fwd")
+        return self.out
+
+    def forward_noalloc(self, x):
+        """The forward through moe_layer_fwd_noalloc: the library's static
+        scratch instead of this layer's workspace."""
+        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched, **self._opts)
+        _check(load().moe_layer_fwd_noalloc(C.byref(a), C.byref(self._sv), _ptr(self.out), _stream()),
+               "moe_layer_fwd_noalloc")
         return self.out
 
     def backward(self, x, dout, recompute_h=False, d_aux=0.0):

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe_rocm.h"
 #include "launch.h"
@@ -194,6 +195,36 @@ SavedLayout saved_layout(const moe_dims& d, bool mx) {
   }
   l.total = o;
   return l;
+}
+
+// Scratch of the allocation-free forward: a file-scope device array, one copy
+// per GPU, alive until the process ends.  Host code never uses its name as an
+// address (that is a host-side stand-in): each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address, or NULL with *err set
+void* scratch_ptr(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -596,6 +627,24 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (e == hipSuccess)
     e = moe::launch_combine(sv->y, sv->dst_rows, sv->topk_prob, d.N, d.D, d.K, out, s, nullptr, shared_row0);
   return hip_status(e);
+}
+
+int moe_layer_fwd_noalloc(const moe_layer_args* a, moe_layer_saved* sv, void* out, void* stream) {
+  if (!a || !sv) return MOE_ERR_NULL;
+  const bool mx = a->dtype == MOE_MXFP8;
+  int st = check_dims(&a->dims, true, mx);
+  if (st) return st;
+  // the workspace moe_layer_fwd would take must fit the static scratch
+  const moe_dims& d = a->dims;
+  if (route_bytes(d) + table_bytes(rows_cap_of(d), experts_of(d)) + router_bytes(d) > kScratchBytes)
+    return MOE_ERR_WORKSPACE;
+  hipError_t err = hipSuccess;
+  void* ws = scratch_ptr(&err);
+  if (!ws) return hip_status(err);
+  // every part of the workspace is written by the kernels that read it (plans,
+  // queue heads and route histograms are built in the same call), so stale
+  // contents from an earlier call do not matter
+  return moe_layer_fwd(a, sv, out, ws, kScratchBytes, stream);
 }
 
 int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void* dout,

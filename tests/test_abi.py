@@ -221,3 +221,25 @@ def test_saved_size_and_carve():
             else:
                 assert p is None, name
         assert o == base + total
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch():
+    """moe_layer_fwd_noalloc runs moe_layer_fwd on the library's static
+    scratch: a shape whose forward workspace exceeds it is refused with
+    MOE_ERR_WORKSPACE before anything is enqueued (fake aligned pointers: the
+    call returns before any HIP call)."""
+    lib = M.load()
+    big = M.dims(262144, 1024, 1024, 8, 256)         # the route histograms alone exceed 64 MiB
+    assert lib.moe_workspace_size(M.MOE_OP_LAYER_FWD, C.byref(big)) > M.MOE_NOALLOC_SCRATCH_BYTES
+    a = M.LayerArgs(big, M.MOE_BF16, M.MOE_SCHED_STAGED, *([1 << 20] * 15))
+    sv = _full_saved(lib, big, M.MOE_BF16)
+    assert lib.moe_layer_fwd_noalloc(C.byref(a), C.byref(sv), 1 << 20, None) == -4
+    assert lib.moe_layer_fwd_noalloc(None, C.byref(sv), 1 << 20, None) == -1
+    bad = M.LayerArgs(M.dims(16, 64, 8, 9, 64), M.MOE_BF16)
+    assert lib.moe_layer_fwd_noalloc(C.byref(bad), C.byref(sv), 1 << 20, None) == -2
+    # the headline shapes fit
+    for wl in ("dsv3_bf16", "qwen3_235b_bf16_fwdbwd", "dsv3_mxfp8", "mixtral_bf16"):
+        import moe_synth as S
+        w = S.WORKLOADS[wl]
+        d = M.dims(w.N, w.D, w.E, w.K, w.H, align=w.align)
+        assert lib.moe_workspace_size(M.MOE_OP_LAYER_FWD, C.byref(d)) <= M.MOE_NOALLOC_SCRATCH_BYTES, wl
