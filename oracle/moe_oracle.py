@@ -709,8 +709,10 @@ def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, row
     prob = route_probs(L, idx, renorm)
     counts, offsets, dst_rows, row_route = route_map(idx, drop, E, align, rows_cap, n_shared)
     xq, xs = dispatch_mxfp8(xv, row_route, K)
+    xd = dispatch(xv, row_route, K)            # the bf16 rows the codes were made from
     if n_shared:
         xq[offsets[E]:offsets[E] + N], xs[offsets[E]:offsets[E] + N] = quantize_mxfp8(xv)
+        xd[offsets[E]:offsets[E] + N] = xv
     Hd = wq["wg_q"].shape[1]
     G = np.zeros((rows_cap, Hd))
     U = np.zeros((rows_cap, Hd))
@@ -727,7 +729,7 @@ def layer_fwd_mxfp8(x, w_r, bias, wq, K: int, drop=None, renorm=0, align=32, row
             wq["wd_q"][e], wq["wd_s"][e])
     out = combine(Y, dst_rows, prob, addend=Y[offsets[E]:offsets[E] + N] if n_shared else None)
     return dict(logits=L, topk_idx=idx, topk_prob=prob, counts=counts, offsets=offsets,
-                dst_rows=dst_rows, row_route=row_route, xq=xq, xs=xs, g=G, u=U, h=Hh,
+                dst_rows=dst_rows, row_route=row_route, xq=xq, xs=xs, xd=xd, g=G, u=U, h=Hh,
                 hq=hq, hs=hs, y=Y, out=out, n_shared=n_shared)
 
 
@@ -772,7 +774,40 @@ def quantize_weights_mxfp8_dgrad(w_gate, w_up, w_down):
     return {k: np.stack(v) for k, v in out.items()}
 
 
-def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
+def quantize_mxfp8_cols(v, offsets):
+    """Column-wise MXFP8 copy of a row-segmented matrix v [rows, W]: for each
+    expert segment [offsets[e], offsets[e+1]) (lengths multiples of 32), the
+    transposed block v[seg].T [W, len] quantized along its rows, i.e. blocks
+    of 32 consecutive rows of one column [KOSMOS 2.2: the copy for the product
+    that contracts over rows is quantized along rows, from the bf16 source;
+    OLMo-A A.15: native MXFP8 grouped wgrad].  Returns {e: (q [W, len],
+    s [W, len/32])} for the experts with rows."""
+    vv = values(v)
+    out = {}
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            if (b - a) % 32:
+                raise ValueError("segments must be multiples of 32 rows")
+            out[e] = quantize_mxfp8(vv[a:b].T)
+    return out
+
+
+def mx_wgrad(dc, a, offsets):
+    """Native MXFP8 weight gradient: dw[e] = bf16(deq(colq(dc_e)) .
+    deq(colq(a_e))^T), eq. 87 over the expert's rows with both operands
+    quantized column-wise (quantize_mxfp8_cols) from their bf16 values;
+    experts without rows get 0.  dc [rows, n], a [rows, k] -> dw [E, n, k]."""
+    E = len(offsets) - 1
+    qc = quantize_mxfp8_cols(dc, offsets)
+    qa = quantize_mxfp8_cols(a, offsets)
+    out = np.zeros((E, values(dc).shape[1], values(a).shape[1]))
+    for e, (q, s) in qc.items():
+        out[e] = round_bf16(dequantize_mxfp8(q, s) @ dequantize_mxfp8(*qa[e]).T)
+    return out
+
+
+def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt, wgrad: str = "bf16", xd=None):
     """Expert backward with block-scaled data gradients and bf16 weight
     gradients on dequantized activations.
 
@@ -790,6 +825,11 @@ def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
     hq = None is the SwiGLU-recompute mode [OLMo-A A.14: H rebuilt in the
     backward instead of saved]: dW_down takes H = bf16(silu(G) U) from the
     saved bf16 G and U in place of deq(H_q).
+    wgrad = "mx": the native MXFP8 weight gradients instead [OLMo-A A.15;
+    KOSMOS 3.3.1 step 3 and 3.3.2 step 1: column-wise copies quantized from
+    the bf16 sources]: dW_down = mx_wgrad(dY_d, H), dW_gate = mx_wgrad(dG,
+    X_d), dW_up = mx_wgrad(dU, X_d), with H = bf16(silu(G) U) and X_d the
+    bf16 dispatched rows (``xd``), not the dequantized codes.
     """
     dy = values(dyd)
     rows, D = dy.shape
@@ -822,20 +862,30 @@ def experts_bwd_mxfp8(dyd, xq, xs, g, u, hq, hs, offsets, wqt):
             continue
         wgut = dequantize_mxfp8(wqt["wgut_q"][e], wqt["wgut_s"][e])        # [D, 2H]
         dXd[a:b] = round_bf16(gu_deq[a:b] @ wgut.T)
-        dWd[e] = round_bf16(dy[a:b].T @ h_deq[a:b])
-        dWg[e] = round_bf16(dG[a:b].T @ x_deq[a:b])
-        dWu[e] = round_bf16(dU[a:b].T @ x_deq[a:b])
+        if wgrad == "bf16":
+            dWd[e] = round_bf16(dy[a:b].T @ h_deq[a:b])
+            dWg[e] = round_bf16(dG[a:b].T @ x_deq[a:b])
+            dWu[e] = round_bf16(dU[a:b].T @ x_deq[a:b])
+    if wgrad == "mx":
+        if xd is None:
+            raise ValueError("the native MXFP8 wgrad takes the bf16 dispatched rows")
+        dWd = mx_wgrad(dy, swiglu(g, u), offsets)
+        dWg = mx_wgrad(dG, xd, offsets)
+        dWu = mx_wgrad(dU, xd, offsets)
+    elif wgrad != "bf16":
+        raise ValueError("wgrad is 'bf16' or 'mx'")
     return dict(dg=dG, du=dU, dxd=dXd, dw_gate=dWg, dw_up=dWu, dw_down=dWd,
                 dyq=dyq, dys=dys, guq=guq, gus=gus)
 
 
-def layer_bwd_mxfp8(fwd: dict, dout, wqt, recompute: bool = False):
+def layer_bwd_mxfp8(fwd: dict, dout, wqt, recompute: bool = False, wgrad: str = "bf16"):
     """MXFP8 layer backward: the bf16 adjoint sequence around the experts
     (weighted dY dispatch, route-weight gradient, fold of the K rows) with
     experts_bwd_mxfp8 in the middle.  fwd is layer_fwd_mxfp8's result; wqt
     comes from quantize_weights_mxfp8_dgrad.  recompute: the saved H codes are
-    not read (SwiGLU-recompute mode)."""
+    not read (SwiGLU-recompute mode).  wgrad = "mx": native MXFP8 weight
+    gradients (experts_bwd_mxfp8)."""
     hq = None if recompute else fwd["hq"]
     return _layer_bwd_around(
         fwd, dout, lambda dyd: experts_bwd_mxfp8(dyd, fwd["xq"], fwd["xs"], fwd["g"], fwd["u"], hq,
-                                                 fwd["hs"], fwd["offsets"], wqt))
+                                                 fwd["hs"], fwd["offsets"], wqt, wgrad, fwd.get("xd")))

@@ -145,3 +145,73 @@ def test_recompute_mode_takes_h_from_the_saved_g_and_u():
     a = O.layer_bwd_mxfp8(fwd, dout, wqt)
     b = O.layer_bwd_mxfp8(fwd, dout, wqt, recompute=True)
     assert np.array_equal(a["dw_down"], b["dw_down"])
+
+
+def test_native_mx_wgrad_lossless_case_equals_the_bf16_backward():
+    """Native MXFP8 weight gradients (OLMo-core Appendix A, A.15; column-wise
+    copies of dY, X and H quantized from their bf16 values, KOSMOS 3.3.2 step
+    1): with every column-wise copy exact they equal the bf16 backward's bit
+    for bit, with the shared expert too."""
+    for n_shared in (0, 1):
+        fwd, dout, wg, wu, wd = _lossless_case(13 + n_shared, n_shared=n_shared)
+        fwd["h"] = O.swiglu(fwd["g"], fwd["u"])          # the bf16 H the native path takes
+        fwd["hq"], fwd["hs"] = O.quantize_mxfp8(fwd["h"])
+        wqt = O.quantize_weights_mxfp8_dgrad(wg, wu, wd)
+        mx = O.layer_bwd_mxfp8(fwd, dout, wqt, wgrad="mx")
+        ref = O.layer_bwd(fwd, dout, wg, wu, wd)
+        for k in ("dw_gate", "dw_up", "dw_down", "dx", "dprob"):
+            assert np.array_equal(mx[k], ref[k]), (n_shared, k)
+            assert np.count_nonzero(ref[k]) > ref[k].size // 20, (n_shared, k)
+        # the native path takes H and X from their bf16 values, never from the
+        # saved row-wise codes: erasing the codes changes no weight gradient
+        fwd["hq"] = np.zeros_like(fwd["hq"])
+        fwd["xq"] = np.zeros_like(fwd["xq"])
+        mx2 = O.layer_bwd_mxfp8(fwd, dout, wqt, wgrad="mx")
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            assert np.array_equal(mx2[k], mx[k]), (n_shared, k)
+
+
+def test_native_mx_wgrad_quantizes_along_rows():
+    """The column-wise copy quantizes blocks of 32 rows of one column: with a
+    gradient whose columns have very different magnitudes (2^-20 against
+    2^0) but uniform magnitude down each column, every column block is exact,
+    so the native wgrad equals the exact product, while row-wise blocks
+    (which mix the magnitudes) would flush the small columns to zero."""
+    rng = np.random.default_rng(3)
+    rows, n, k = 64, 64, 32
+    offsets = np.array([0, 32, 64])
+    col_exp = np.where(np.arange(n) % 2 == 0, -20.0, 0.0)
+    dc = rng.choice([-1.0, 1.0], size=(rows, n)) * np.ldexp(1.0, col_exp.astype(int))[None, :]
+    a = rng.choice([-1.0, 0.0, 1.0], size=(rows, k))
+    got = O.mx_wgrad(dc, a, offsets)
+    for e in range(2):
+        sl = slice(offsets[e], offsets[e + 1])
+        assert np.array_equal(got[e], O.round_bf16(dc[sl].T @ a[sl]))
+        assert np.count_nonzero(got[e][0::2]) > 0             # the 2^-20 columns survive
+    # the row-wise reading of the same operand loses them
+    rq, rs = O.quantize_mxfp8(dc)
+    assert not np.any(O.dequantize_mxfp8(rq, rs)[:, 0::2])
+    # shapes of the copies: [W, segment rows] codes, [W, rows/32] scales
+    cq = O.quantize_mxfp8_cols(dc, offsets)
+    assert cq[0][0].shape == (n, 32) and cq[0][1].shape == (n, 1)
+
+
+def test_native_mx_wgrad_random_inputs_within_mxfp8_error():
+    """Workload-shaped random inputs: the native MXFP8 weight gradients stay
+    within a few E4M3 spacings of the bf16 backward's; the other gradients do
+    not depend on the wgrad mode."""
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_wg", N=96, D=128, E=8, K=4, H=64, bwd=True)
+    inp = S.make_inputs(wl, 25)
+    q = O.quantize_weights_mxfp8(inp.w_gate, inp.w_up, inp.w_down)
+    wqt = O.quantize_weights_mxfp8_dgrad(inp.w_gate, inp.w_up, inp.w_down)
+    f = O.layer_fwd_mxfp8(inp.x, inp.w_r, inp.bias, q, wl.K)
+    assert np.array_equal(f["xd"], O.dispatch(inp.x, f["row_route"], wl.K))
+    mx = O.layer_bwd_mxfp8(f, inp.dout, wqt, wgrad="mx")
+    base = O.layer_bwd_mxfp8(f, inp.dout, wqt)
+    for k in ("dx", "dprob", "dg", "du"):
+        assert np.array_equal(mx[k], base[k]), k
+    fb = O.layer_fwd(inp.x, inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K, align=32)
+    ref = O.layer_bwd(fb, inp.dout, inp.w_gate, inp.w_up, inp.w_down)
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        err = np.linalg.norm(mx[k] - ref[k]) / np.linalg.norm(ref[k])
+        assert err <= 0.15, (k, err)
