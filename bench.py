@@ -419,14 +419,15 @@ def _host_threads():
 EXTRA_WORKLOADS = ("mixtral_bf16", "qwen3_235b_bf16_fwdbwd", "dsv3_mxfp8")
 
 
-def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False):
+def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False,
+            mx_wgrad=False):
     """Time `steps` steps of one workload (after `warmup`), inputs resident in
     HBM; returns the result dict of the JSON line (without cpu_baseline)."""
     bwd = wl.bwd or backward
     t0 = time.perf_counter()
     x, w, drop = device_inputs(M, inp, wl.mxfp8, torch, backward=bwd)
     layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, with_bwd=bwd,
-                       router_bwd=bwd)
+                       router_bwd=bwd, mx_wgrad=mx_wgrad)
     dout_bits = inp.dout if inp.dout is not None else (S.random_bf16((wl.N, wl.D), seed, 9) if bwd else None)
     dout = (torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
             if bwd else None)
@@ -550,7 +551,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         out["backward"] = {"ms": bwd_ms, "routed_tflops": tf_b, "pct_mfma_peak": 100 * tf_b / PEAK_BF16_TFLOPS,
                            "note": "value and ms_per_step cover forward + backward, router backward included; "
                                    "routed_tflops counts the expert GEMMs only; pct_mfma_peak against the bf16 "
-                                   "peak" + (" (MXFP8: block-scaled dgrads, bf16 wgrads)" if wl.mxfp8 else "")}
+                                   "peak" + ((" (MXFP8: block-scaled dgrads and wgrads)" if mx_wgrad else
+                                              " (MXFP8: block-scaled dgrads, bf16 wgrads)") if wl.mxfp8 else "")}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
     if shared is not None:
@@ -582,6 +584,8 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (moe_layer_bwd with the router backward) on a forward "
                          "workload; dOut is N(0, 1) bf16 from the seed")
+    ap.add_argument("--mx-wgrad", action="store_true",
+                    help="MXFP8 backward: native block-scaled weight gradients on column-wise copies")
     ap.add_argument("--shared-expert", action="store_true",
                     help="also time moe_layer_fwd with one shared expert (N(0,1/D), N(0,1/H) weights) in the same "
                          "grouped-GEMM launches, beside the routed-only layer call")
@@ -643,7 +647,7 @@ def main(argv=None):
         del src, dst
 
     out = measure(M, torch, wl, inp, args.steps, args.warmup, args.seed, backward=args.backward,
-                  layer_call=args.layer_call, shared_expert=args.shared_expert)
+                  layer_call=args.layer_call, shared_expert=args.shared_expert, mx_wgrad=args.mx_wgrad)
     if not args.headline_only:
         # the other workloads of the same run, each its own step (parity cases
         # aside from the headline): keys only, the headline value is above

@@ -80,6 +80,7 @@ extern "C" {
 #define MOE_OP_LAYER_BWD 4
 #define MOE_OP_ROUTER 5
 #define MOE_OP_LAYER_BWD_MXFP8 6
+#define MOE_OP_LAYER_BWD_MXFP8_NATIVE 7   /* MXFP8 backward with mx_wgrad = 1 */
 
 /* ---- shapes -------------------------------------------------------------
  * N tokens, D model width, E experts, K routes per token, H expert (SwiGLU)
@@ -350,7 +351,14 @@ typedef struct moe_layer_args {
    * waiting items are skipped, every kernel exits normally and
    * MOE_STATUS_WAIT_EXPIRED is reported.  Ignored by the staged schedule. */
   int32_t ready_test_polls;
-  int32_t reserved;     /* 0 */
+  /* MXFP8 backward only: 0 = weight gradients as bf16 products on the
+   * dequantized activations (OLMo-core Appendix A, A.13); 1 = native
+   * block-scaled weight gradients (A.15) on column-wise MXFP8 copies of dY_d,
+   * H, dG, dU and X_d, each quantized from its bf16 values (KOSMOS section
+   * 3.3.1 step 3, section 3.3.2 step 1): dY_d as it lands, H recomputed from
+   * the saved G and U, X_d gathered from the token rows x through row_route.
+   * Workspace MOE_OP_LAYER_BWD_MXFP8_NATIVE; needs saved->row_route. */
+  int32_t mx_wgrad;
 } moe_layer_args;
 
 typedef struct moe_layer_saved {

@@ -26,6 +26,7 @@ MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD, MOE_OP_ROUTER = 1, 2, 3, 4, 5
 MOE_OP_LAYER_BWD_MXFP8 = 6
+MOE_OP_LAYER_BWD_MXFP8_NATIVE = 7
 MOE_SCHED_STAGED, MOE_SCHED_READY = 0, 1
 
 _vp = C.c_void_p
@@ -58,7 +59,7 @@ class LayerArgs(C.Structure):
                 ("bias", _vp), ("drop", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("wg_q", _vp), ("wg_s", _vp), ("wu_q", _vp), ("wu_s", _vp), ("wd_q", _vp),
                 ("wd_s", _vp), ("aux_alpha", C.c_float), ("wdt_q", _vp), ("wdt_s", _vp), ("wgut_q", _vp),
-                ("wgut_s", _vp), ("ready_test_polls", _i32), ("reserved", _i32)]
+                ("wgut_s", _vp), ("ready_test_polls", _i32), ("mx_wgrad", _i32)]
 
 
 class LayerSaved(C.Structure):
@@ -453,12 +454,15 @@ class MoeLayer:
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
                  device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False, n_group=0,
-                 topk_group=0, aux_alpha=0.0):
+                 topk_group=0, aux_alpha=0.0, mx_wgrad=False):
         """n_group/topk_group: group-limited top-K; aux_alpha != 0: the aux loss
-        goes to saved["aux"] and its gradient into the router backward."""
+        goes to saved["aux"] and its gradient into the router backward;
+        mx_wgrad: the MXFP8 backward's weight gradients on block-scaled MFMA
+        (column-wise copies) instead of bf16 products."""
         torch = _torch()
         self.wts, self.K, self.mxfp8, self.renorm, self.drop = wts, K, mxfp8, renorm, drop
         self.sched = sched
+        self.mx_wgrad = bool(mx_wgrad and mxfp8)
         self._opts = dict(n_group=n_group, topk_group=topk_group, aux_alpha=aux_alpha)
         D = wts.w_r.shape[1]
         self._x_proto = torch.empty((N, D), dtype=torch.bfloat16, device=device)
@@ -471,7 +475,9 @@ class MoeLayer:
         self.grads = None
         if with_bwd:
             E, H = self.d.E + self.d.n_shared, self.d.H
-            self.ws_b = workspace(MOE_OP_LAYER_BWD_MXFP8 if mxfp8 else MOE_OP_LAYER_BWD, self.d, device)
+            op = (MOE_OP_LAYER_BWD_MXFP8_NATIVE if self.mx_wgrad else MOE_OP_LAYER_BWD_MXFP8) if mxfp8 \
+                else MOE_OP_LAYER_BWD
+            self.ws_b = workspace(op, self.d, device)
             self.grads = dict(dx=torch.empty((N, D), dtype=torch.bfloat16, device=device),
                               dprob=torch.empty((N, K), dtype=torch.float32, device=device),
                               dw_gate=torch.empty((E, H, D), dtype=torch.bfloat16, device=device),
@@ -505,6 +511,7 @@ class MoeLayer:
         library recomputes H from the saved G and U (SwiGLU-recompute mode).
         d_aux: upstream gradient of the aux loss (used when aux_alpha != 0)."""
         a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, **self._opts)
+        a.mx_wgrad = int(self.mx_wgrad)
         self._gr.d_aux = float(d_aux)
         sv = self._sv
         if recompute_h:

@@ -137,9 +137,16 @@ RouterBwdLayout router_bwd_layout(const moe_dims& d) {
 // [dG | dU] quantized and X_d dequantized, then the router backward's scratch
 struct BwdLayout {
   size_t dyd, dxd, dg, du, h, dyq, dys, guq, gus, xdeq, router, total;
+  // native MXFP8 wgrad: column-wise copies [width][ldt] and scales [width][ldt/32]
+  size_t dyt_q, dyt_s, xt_q, xt_s, ht_q, ht_s, dgt_q, dgt_s, dut_q, dut_s;
+  int64_t ldt;
 };
 
-BwdLayout bwd_layout(const moe_dims& d, bool mx) {
+// columns of the column-wise copies: every row of the expert-contiguous
+// buffers, rounded up to whole 128-column contraction steps
+int64_t cols_ld(const moe_dims& d) { return (rows_cap_of(d) + 127) / 128 * 128; }
+
+BwdLayout bwd_layout(const moe_dims& d, bool mx, bool mxw = false) {
   BwdLayout l{};
   const size_t rc = (size_t)rows_cap_of(d), D = (size_t)d.D, H = (size_t)d.H;
   size_t o = 0;
@@ -159,12 +166,26 @@ BwdLayout bwd_layout(const moe_dims& d, bool mx) {
     take(l.gus, rc * 2 * H / 32);
     take(l.xdeq, rc * D * 2);
   }
+  if (mx && mxw) {
+    const size_t ldt = (size_t)cols_ld(d);
+    l.ldt = (int64_t)ldt;
+    take(l.dyt_q, D * ldt);
+    take(l.dyt_s, D * ldt / 32);
+    take(l.xt_q, D * ldt);
+    take(l.xt_s, D * ldt / 32);
+    take(l.ht_q, H * ldt);
+    take(l.ht_s, H * ldt / 32);
+    take(l.dgt_q, H * ldt);
+    take(l.dgt_s, H * ldt / 32);
+    take(l.dut_q, H * ldt);
+    take(l.dut_s, H * ldt / 32);
+  }
   take(l.router, router_bwd_layout(d).total);
   l.total = o;
   return l;
 }
 
-size_t bwd_scratch_bytes(const moe_dims& d, bool mx) { return bwd_layout(d, mx).total; }
+size_t bwd_scratch_bytes(const moe_dims& d, bool mx, bool mxw = false) { return bwd_layout(d, mx, mxw).total; }
 
 // The saved set carved from one buffer, every tensor at a 256-byte offset;
 // at[i] = SIZE_MAX marks a field the dtype does not use.
@@ -243,6 +264,7 @@ size_t moe_workspace_size(int op, const moe_dims* d) {
     case MOE_OP_LAYER_FWD: return route_bytes(*d) + table_bytes(rc, experts_of(*d)) + router_bytes(*d);
     case MOE_OP_LAYER_BWD: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, false);
     case MOE_OP_LAYER_BWD_MXFP8: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, true);
+    case MOE_OP_LAYER_BWD_MXFP8_NATIVE: return table_bytes(rc, experts_of(*d)) + bwd_scratch_bytes(*d, true, true);
     default: return 0;
   }
 }
@@ -655,10 +677,18 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   const moe_dims& d = a->dims;
   int st = check_dims(&d, true, mx);
   if (st) return st;
+  if (a->mx_wgrad != 0 && (a->mx_wgrad != 1 || !mx)) return MOE_ERR_DTYPE;
+  const bool mxw = mx && a->mx_wgrad == 1;
   if (mx) {
     // the block-scaled dgrads run on the persistent engine: whole 128-element
     // contraction steps over D and over 2H
     if (d.D % 128 || d.H % 64) return MOE_ERR_SHAPE;
+    if (mxw) {
+      REQUIRE(sv->row_route);
+      REQUIRE(a->x);
+      if (!moe::gemm_wgrad_mx_ok(d.D, d.H, cols_ld(d)) || !moe::gemm_wgrad_mx_ok(d.H, d.D, cols_ld(d)))
+        return MOE_ERR_SHAPE;
+    }
     REQUIRE(a->wdt_q);
     REQUIRE(a->wdt_s);
     REQUIRE(a->wgut_q);
@@ -702,11 +732,11 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   const int64_t Ex = experts_of(d);
   const int32_t* shared_row0 = d.n_shared ? sv->offsets + d.E : nullptr;   // the shared expert's segment
   const size_t tb = table_bytes(rc, Ex);
-  if (ws_bytes < tb + bwd_scratch_bytes(d, mx)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < tb + bwd_scratch_bytes(d, mx, mxw)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   int32_t* table = (int32_t*)ws;
   char* p0 = (char*)ws + tb;
-  const BwdLayout bl = bwd_layout(d, mx);
+  const BwdLayout bl = bwd_layout(d, mx, mxw);
   void* dyd = p0 + bl.dyd;
   void* dxd = p0 + bl.dxd;
   void* dg = p0 + bl.dg;
@@ -739,20 +769,54 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     if (e == hipSuccess) e = moe::launch_quantize_rows(dyd, rc, d.D, dyq, dys, s, rows_end);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(dn, true, table, s);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(gu, true, table, s);
-    // weight gradients: bf16 products on the dequantized activations; in the
-    // SwiGLU-recompute mode (no saved h_q) on H = silu(G) U rebuilt in bf16
-    if (e == hipSuccess) {
-      if (sv->h_q) e = moe::launch_dequant_rows(sv->h_q, sv->h_s, rc, d.H, rows_end, hdq, s);
-      else e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, hdq, nullptr, nullptr, s);
+    if (mxw) {
+      // native block-scaled weight gradients on column-wise copies, each
+      // quantized from its bf16 values: dY_d as it landed, H rebuilt from the
+      // saved G and U, dG and dU from the down dgrad, X_d gathered from x
+      const int64_t ld = bl.ldt;
+      auto cp = [&](size_t o) { return (uint8_t*)(p0 + o); };
+      if (e == hipSuccess) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, hdq, nullptr, nullptr, s);
+      if (e == hipSuccess)
+        e = moe::launch_quantize_cols_seg(dyd, rc, d.D, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dyt_q),
+                                          cp(bl.dyt_s), s);
+      if (e == hipSuccess)
+        e = moe::launch_quantize_cols_seg(hdq, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.ht_q),
+                                          cp(bl.ht_s), s);
+      if (e == hipSuccess)
+        e = moe::launch_quantize_cols_seg(dg, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dgt_q),
+                                          cp(bl.dgt_s), s);
+      if (e == hipSuccess)
+        e = moe::launch_quantize_cols_seg(du, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dut_q),
+                                          cp(bl.dut_s), s);
+      if (e == hipSuccess)
+        e = moe::launch_quantize_cols_seg(a->x, rc, d.D, ld, rows_end, sv->row_route, d.K, shared_row0, d.N,
+                                          cp(bl.xt_q), cp(bl.xt_s), s);
+      // dW_down[e] [D][H] = dY_e^T H_e; dW_gate / dW_up [H][D] = dG_e^T X_e, dU_e^T X_e
+      if (e == hipSuccess)
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.D, d.H, ld, cp(bl.dyt_q), cp(bl.dyt_s), cp(bl.ht_q),
+                                      cp(bl.ht_s), gr->dw_down, table, s);
+      if (e == hipSuccess)
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.H, d.D, ld, cp(bl.dgt_q), cp(bl.dgt_s), cp(bl.xt_q),
+                                      cp(bl.xt_s), gr->dw_gate, table, s);
+      if (e == hipSuccess)
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.H, d.D, ld, cp(bl.dut_q), cp(bl.dut_s), cp(bl.xt_q),
+                                      cp(bl.xt_s), gr->dw_up, table, s);
+    } else {
+      // weight gradients: bf16 products on the dequantized activations; in the
+      // SwiGLU-recompute mode (no saved h_q) on H = silu(G) U rebuilt in bf16
+      if (e == hipSuccess) {
+        if (sv->h_q) e = moe::launch_dequant_rows(sv->h_q, sv->h_s, rc, d.H, rows_end, hdq, s);
+        else e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, hdq, nullptr, nullptr, s);
+      }
+      if (e == hipSuccess) e = moe::launch_dequant_rows(sv->xd_q, sv->xd_s, rc, d.D, rows_end, xdq, s);
+      moe::GemmBwd wd{Ex, rc, d.H, d.D, sv->offsets, hdq, nullptr, nullptr, dyd, nullptr, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, false};
+      if (e == hipSuccess) e = gemm_wgrad(wd, dyd, gr->dw_down, table, s);
+      moe::GemmBwd wgu{Ex, rc, d.D, d.H, sv->offsets, xdq, nullptr, nullptr, dg, du, nullptr,
+                       nullptr, nullptr, nullptr, nullptr, false};
+      if (e == hipSuccess) e = gemm_wgrad(wgu, dg, gr->dw_gate, table, s);
+      if (e == hipSuccess) e = gemm_wgrad(wgu, du, gr->dw_up, table, s);
     }
-    if (e == hipSuccess) e = moe::launch_dequant_rows(sv->xd_q, sv->xd_s, rc, d.D, rows_end, xdq, s);
-    moe::GemmBwd wd{Ex, rc, d.H, d.D, sv->offsets, hdq, nullptr, nullptr, dyd, nullptr, nullptr,
-                    nullptr, nullptr, nullptr, nullptr, false};
-    if (e == hipSuccess) e = gemm_wgrad(wd, dyd, gr->dw_down, table, s);
-    moe::GemmBwd wgu{Ex, rc, d.D, d.H, sv->offsets, xdq, nullptr, nullptr, dg, du, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, false};
-    if (e == hipSuccess) e = gemm_wgrad(wgu, dg, gr->dw_gate, table, s);
-    if (e == hipSuccess) e = gemm_wgrad(wgu, du, gr->dw_up, table, s);
   } else {
     // SwiGLU-recompute mode: H = silu(G) U from the saved bf16 G and U, the
     // same arithmetic as GEMM1's epilogue, so it equals the forward's H bit for bit

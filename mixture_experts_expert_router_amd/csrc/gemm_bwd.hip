@@ -379,6 +379,163 @@ __global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restr
   if (t < kXcds) head[t * kHeadStride] = 0;
 }
 
+// ---------------------------------------------------------- MXFP8 wgrad ----
+// Native block-scaled weight gradient (OLMo-core Appendix A, A.15; KOSMOS
+// section 3.3.2 step 1: the operands' column-wise copies quantized from their
+// bf16 values):  db[e][m][n] = sum over the rows r of expert e of
+// aT[m][r] bT[n][r] (eq. 87), with aT [M][ld] and bT [N][ld] E4M3 copies
+// quantized along r in blocks of 32 and their E8M0 scales [M][ld/32],
+// [N][ld/32].  Items are (expert, 256-row tile of db, 256-column tile) on the
+// wgrad planner's order and queues.  An expert's rows start on a multiple of
+// 32, so its contraction window starts inside a 128-column step: the steps
+// are taken 128-aligned in the copies (whole chunks and 4-byte scale
+// groups) and the B tile's columns outside the window are zeroed in LDS.
+
+struct WgradMxParams {
+  const int32_t* offsets;   // [E+1], row segments (multiples of 32)
+  const int32_t* plan;      // wgrad planner output
+  int32_t* head;            // queue heads
+  int E, M, N, m_tiles, n_tiles;
+  int64_t ld;               // columns of the copies (bytes per code row), % 128 == 0
+  const uint8_t* aq;        // [M][ld]
+  const uint8_t* as;        // [M][ld/32]
+  const uint8_t* bq;        // [N][ld]
+  const uint8_t* bs;        // [N][ld/32]
+  uint16_t* c;              // [E][M][N] bf16
+};
+
+using WmxTile = tile::TileCfg<256, 256, 2, 4, 2, false, true>;   // 2 x 64 KB ring + scale groups
+
+struct WmxItem {
+  int e, c0, c1, m0, n0, idx;   // contraction window [c0, c1) of the copies' columns
+  bool valid;
+};
+
+__device__ __forceinline__ WmxItem claim_wmx(const WgradMxParams& p, int* s_item, int xcd) {
+  const int item = claim_global(p.head, p.plan[0], s_item, xcd);
+  WmxItem it{};
+  if (item < 0) return it;
+  const int per_e = p.m_tiles * p.n_tiles;
+  const int ei = item / per_e;
+  it.e = p.plan[1 + ei];
+  it.c0 = p.offsets[it.e];
+  it.c1 = p.offsets[it.e + 1];
+  int mt, nt;
+  it.idx = item - ei * per_e;
+  superblock_decode(it.idx, p.m_tiles, p.n_tiles, mt, nt);
+  it.m0 = mt * WmxTile::BM;
+  it.n0 = nt * WmxTile::BN;
+  it.valid = true;
+  return it;
+}
+
+__device__ __forceinline__ int wmx_steps(const WmxItem& it) {
+  return it.c1 > it.c0 ? (it.c1 + tile::kRB - 1) / tile::kRB - it.c0 / tile::kRB : 0;
+}
+
+// DMA sources (rows past M or N reload the last row and are never stored);
+// scale load q of a wave: A rows, then B rows, then padding rows that reload
+// the tile's first A rows.
+__device__ __forceinline__ void sources_wmx(const WgradMxParams& p, const WmxItem& it, tile::Src<WmxTile>& src) {
+  using namespace tile;
+  using C = WmxTile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s0 = it.c0 / kRB;
+  const int d_chunk = dma_chunk();
+  src.a = uniform_ptr(p.aq + (int64_t)s0 * kRB);
+  src.b = uniform_ptr(p.bq + (int64_t)s0 * kRB);
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q)
+    src.a_off[q] = (uint32_t)(min(it.m0 + dma_row(wave, C::A_INS, q), p.M - 1) * p.ld + d_chunk * 16);
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q)
+    src.b_off[q] = (uint32_t)(min(it.n0 + dma_row(wave, C::B_INS, q), p.N - 1) * p.ld + d_chunk * 16);
+  src.s_ks = (int)(p.ld / 32);
+#pragma unroll
+  for (int q = 0; q < C::SCI; ++q) {
+    const int r0 = wave * C::SRW + q * 16;
+    if (r0 < C::BM || r0 >= C::BM + C::BN) {
+      src.s[q] = uniform_ptr(p.as + (int64_t)s0 * 4);
+      src.s_row0[q] = it.m0 + (r0 < C::BM ? r0 : 0);
+      src.s_lim[q] = p.M - 1;
+    } else {
+      src.s[q] = uniform_ptr(p.bs + (int64_t)s0 * 4);
+      src.s_row0[q] = __builtin_amdgcn_readfirstlane(it.n0 + r0 - C::BM);
+      src.s_lim[q] = p.N - 1;
+    }
+  }
+}
+
+__device__ __forceinline__ void epilogue_wmx(const WgradMxParams& p, const WmxItem& it,
+                                             const f32x4_t (&acc)[WmxTile::TM][WmxTile::TN]) {
+  using C = WmxTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const bool odd = lg & 1;
+  uint16_t* cb = p.c + (int64_t)it.e * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int m = it.m0 + wm * C::WM + i * 16 + l16;
+#pragma unroll
+    for (int j = 0; j < C::TN; j += 2) {
+      const f32x4_t a = acc[i][j], b = acc[i][j + 1];
+      const uint4 v = frag_pair_16b(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                    pack_bf16x2(b[2], b[3]), odd);
+      const int n = it.n0 + wn * C::WN + (j + (odd ? 1 : 0)) * 16 + 8 * (lg >> 1);
+      if (m >= p.M || n >= p.N) continue;
+      *reinterpret_cast<uint4*>(cb + (int64_t)m * p.N + n) = v;
+    }
+  }
+}
+
+// an expert without rows: item idx clears its share of the expert's db as a
+// flat range (the expert's items cover at least its M x N values)
+__device__ __forceinline__ void zero_wmx(const WgradMxParams& p, const WmxItem& it) {
+  const int64_t total = (int64_t)p.M * p.N * 2;
+  const int64_t chunk = (int64_t)WmxTile::BM * WmxTile::BN * 2;
+  const int64_t c0 = (int64_t)it.idx * chunk;
+  const int64_t c1 = min(c0 + chunk, total);
+  uint8_t* base = reinterpret_cast<uint8_t*>(p.c) + (int64_t)it.e * total;
+  for (int64_t off = c0 + (int64_t)threadIdx.x * 16; off < c1; off += (int64_t)blockDim.x * 16)
+    *reinterpret_cast<uint4*>(base + off) = make_uint4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512) void gemm_wgrad_mx_kernel(WgradMxParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WmxTile::LDS];
+  __shared__ int s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int xcd = xcd_id();
+  WmxItem it = claim_wmx(p, &s_item, xcd);
+  if (!it.valid) return;
+  if (wmx_steps(it) > 0) {
+    tile::Src<WmxTile> src;
+    sources_wmx(p, it, src);
+    tile::prologue<WmxTile>(lds0, src, wmx_steps(it));
+  }
+  while (it.valid) {
+    const int nk = wmx_steps(it);
+    f32x4_t acc[WmxTile::TM][WmxTile::TN];
+    if (nk > 0) {
+      tile::Src<WmxTile> src;
+      sources_wmx(p, it, src);
+      const int s0 = it.c0 / tile::kRB;
+      tile::mainloop_mx_window<WmxTile>(smem, lds0, src, nk, it.c0 - s0 * tile::kRB,
+                                        it.c1 - (s0 + nk - 1) * tile::kRB, acc);
+    }
+    __syncthreads();   // every wave has read s_item before the next claim rewrites it
+    const WmxItem next = claim_wmx(p, &s_item, xcd);
+    if (next.valid && wmx_steps(next) > 0) {
+      tile::Src<WmxTile> ns;
+      sources_wmx(p, next, ns);
+      tile::prologue<WmxTile>(lds0, ns, wmx_steps(next));
+    }
+    if (nk > 0) epilogue_wmx(p, it, acc);
+    else zero_wmx(p, it);
+    it = next;
+  }
+}
+
 hipError_t grid_for(const void* kern, int* grid) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -462,6 +619,39 @@ hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, in
   hipError_t err = grid_for((const void*)gemm_wgrad_kernel, &grid);
   if (err != hipSuccess) return err;
   gemm_wgrad_kernel<<<grid, 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// MXFP8 wgrad: copies of ld columns (% 128), output dims % 32, 32-bit
+// offsets into the copies
+bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t ld) {
+  return M % 32 == 0 && N % 32 == 0 && M >= 32 && N >= 32 && ld % 128 == 0 && M * ld < (int64_t(1) << 31) &&
+         N * ld < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, int64_t E, int64_t M, int64_t N, int64_t ld,
+                                const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, void* db,
+                                int32_t* ws, hipStream_t s) {
+  WgradMxParams p{};
+  p.offsets = offsets;
+  p.E = (int)E;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.m_tiles = (p.M + WmxTile::BM - 1) / WmxTile::BM;
+  p.n_tiles = (p.N + WmxTile::BN - 1) / WmxTile::BN;
+  p.ld = ld;
+  p.aq = aq;
+  p.as = as;
+  p.bq = bq;
+  p.bs = bs;
+  p.c = (uint16_t*)db;
+  p.head = ws;
+  p.plan = ws + kGemmHeadInts;
+  plan_wgrad_kernel<<<1, 1024, 0, s>>>(offsets, p.E, p.m_tiles * p.n_tiles, ws + kGemmHeadInts, ws);
+  int grid = 0;
+  hipError_t err = grid_for((const void*)gemm_wgrad_mx_kernel, &grid);
+  if (err != hipSuccess) return err;
+  gemm_wgrad_mx_kernel<<<grid, 512, 0, s>>>(p);
   return hipGetLastError();
 }
 

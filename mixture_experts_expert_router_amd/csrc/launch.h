@@ -108,6 +108,14 @@ hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uin
 // along r; scales [b][c][(col0 + r) / 32] (row stride ld / 32)
 hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                                 int64_t col0, uint8_t* q, uint8_t* sc, hipStream_t s);
+// column-wise copy for the native MXFP8 wgrad: src bf16 [rows][cols] (or the
+// token rows x [N][cols] gathered through row_route / K and the shared
+// segment at *shared0 when row_route is given) -> q [cols][ld] and scales
+// [cols][ld/32], blocks of 32 rows of one column; rows >= *rows_end and
+// columns past rows are zero (ld % 128 == 0)
+hipError_t launch_quantize_cols_seg(const void* src, int64_t rows, int64_t cols, int64_t ld, const int32_t* rows_end,
+                                    const int32_t* row_route, int64_t K, const int32_t* shared0, int64_t N,
+                                    uint8_t* q, uint8_t* sc, hipStream_t s);
 // bf16 [rows][cols] from E4M3 + E8M0 row-wise blocks; rows >= *rows_end skipped
 hipError_t launch_dequant_rows(const uint8_t* q, const uint8_t* sc, int64_t rows, int64_t cols,
                                const int32_t* rows_end, void* out, hipStream_t s);
@@ -161,6 +169,13 @@ hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s);
 bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db);
 hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s,
                                   bool f32 = false);
+// native MXFP8 wgrad: db[e][m][n] = sum over expert e's rows r of aT[m][r] bT[n][r]
+// with column-wise copies aT [M][ld], bT [N][ld] (E4M3) and scales [.][ld/32];
+// row segments from offsets (multiples of 32); bf16 db [E][M][N]
+bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t ld);
+hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, int64_t E, int64_t M, int64_t N, int64_t ld,
+                                const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, void* db,
+                                int32_t* ws, hipStream_t s);
 
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);

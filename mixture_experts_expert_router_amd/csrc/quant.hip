@@ -65,6 +65,63 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
   sc[(b * C + c0 + c) * (ld / 32) + (col0 + r) / 32] = (uint8_t)code;
 }
 
+// Column-wise copy of a row-segmented matrix for the native MXFP8 weight
+// gradient: src bf16 [R][C] (expert segments along the rows, multiples of 32
+// rows) -> q[c][r] (row stride ld, ld % 128 == 0), blocks of 32 rows of one
+// column, scales [c][r / 32] (row stride ld / 32).  Rows at or past
+// *rows_end, and the columns r in [R, ld), are written as zero codes and
+// scales.  gather: row r of src is instead token row_route[r] / K of x (rows
+// without a route are zero), and the shared expert's segment (shared0 ..
+// shared0 + N, when given) holds x itself; this reads the bf16 token rows a
+// dispatched matrix was made from.
+__global__ __launch_bounds__(256) void quantize_cols_seg_kernel(const uint16_t* __restrict__ src, int64_t R,
+                                                                int64_t C, int64_t ld,
+                                                                const int32_t* __restrict__ rows_end,
+                                                                const int32_t* __restrict__ row_route, int K,
+                                                                const int32_t* __restrict__ shared0, int64_t N,
+                                                                uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kQR][kQC + kQPad];
+  const int64_t r0 = (int64_t)blockIdx.y * kQR, c0 = (int64_t)blockIdx.x * kQC;
+  const int64_t rend = min(R, (int64_t)*rows_end);
+  const int64_t s0 = shared0 ? (int64_t)*shared0 : -1;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kQR / 32; ++i) {
+    const int rr = t / 8 + 32 * i, cc = (t % 8) * 8;
+    const int64_t r = r0 + rr;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rend && c0 + cc < C) {
+      int64_t srow = r;
+      if (row_route) {
+        const int rt = row_route[r];
+        srow = rt >= 0 ? rt / K : ((s0 >= 0 && r >= s0 && r < s0 + N) ? r - s0 : -1);
+      }
+      if (srow >= 0) v = ldg16(src + srow * C + c0 + cc);
+    }
+    *reinterpret_cast<uint4*>(&tile[rr][cc]) = v;
+  }
+  __syncthreads();
+  const int c = t % kQC, blk = t / kQC;
+  const int64_t r = r0 + 32 * blk;
+  if (c0 + c >= C || r >= ld) return;
+  float f[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    f[i] = bf16_to_f32(tile[32 * blk + i][c]);
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+  const int code = e8m0_code(amax);
+  const int e = code - 127;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], e);
+  uint8_t* dst = q + (c0 + c) * ld + r;
+  stg16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+  stg16(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  sc[(c0 + c) * (ld / 32) + r / 32] = (uint8_t)code;
+}
+
 // E4M3FN code -> its value as fp32 (exact; codes 0x7F / 0xFF, NaN in E4M3FN,
 // are never produced by the quantizer).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -107,6 +164,16 @@ hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, in
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
   const dim3 grid((unsigned)((cols + kQC - 1) / kQC), (unsigned)((rows + kQR - 1) / kQR), (unsigned)batch);
   quantize_cols_kernel<<<grid, 256, 0, s>>>((const uint16_t*)src, rows, cols, ld, col0, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols_seg(const void* src, int64_t rows, int64_t cols, int64_t ld, const int32_t* rows_end,
+                                    const int32_t* row_route, int64_t K, const int32_t* shared0, int64_t N,
+                                    uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (cols == 0 || ld == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + kQC - 1) / kQC), (unsigned)(ld / kQR), 1);
+  quantize_cols_seg_kernel<<<grid, 256, 0, s>>>((const uint16_t*)src, rows, cols, ld, rows_end, row_route, (int)K,
+                                                shared0, N, q, sc);
   return hipGetLastError();
 }
 

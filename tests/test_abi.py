@@ -120,7 +120,7 @@ def test_struct_layouts_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     hdr = os.path.join(os.path.dirname(__file__), "..", "include", "moe_rocm.h")
     checks = {"moe_dims": (M.Dims, ["N", "renorm", "n_group", "topk_group"]),
-              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha", "wdt_q", "wgut_s", "ready_test_polls"]),
+              "moe_layer_args": (M.LayerArgs, ["x", "wd_s", "aux_alpha", "wdt_q", "wgut_s", "ready_test_polls", "mx_wgrad"]),
               "moe_layer_saved": (M.LayerSaved, ["logits", "y", "aux", "status"]),
               "moe_layer_grads": (M.LayerGrads, ["dx", "dlogits", "d_aux"]),
               "moe_gemm_fwd_args": (M.GemmFwdArgs, ["dtype", "act_scales"]),

@@ -566,3 +566,51 @@ def test_layer_bwd_mxfp8_recompute_mode():
     print(f"  dw_down rel {err:.2e}", flush=True)
     assert err <= 5e-3, err
     assert not torch.equal(g1["dw_down"].view(torch.uint8), g2["dw_down"].view(torch.uint8))
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("name", list(MX_BWD_CASES))
+def test_layer_bwd_mxfp8_native_wgrad(name, shared):
+    """Native MXFP8 weight gradients (OLMo-core Appendix A, A.15) through
+    moe_layer_bwd with mx_wgrad = 1, against the oracle's mx_wgrad: block-
+    scaled products on column-wise copies of dY_d, H, dG, dU and X_d, each
+    quantized from its bf16 values.  The copies of X_d are exact on both
+    sides (gathered from the same token rows); dY_d, dG, dU and H can differ
+    in a last bf16 bit between fp32 and float64 accumulation, which moves an
+    E4M3 code by one step on a small fraction of elements: relative Frobenius
+    1e-2.  The other gradients are bitwise those of the default mode."""
+    cfg = MX_BWD_CASES[name]
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8"], name + "_nat", bwd=True, **cfg)
+    print(f"layer bwd mxfp8 native wgrad {name} shared={shared}", flush=True)
+    inp = S.make_inputs(wl, 35)
+    wg, wu, wd = _with_shared(inp, 35) if shared else (inp.w_gate, inp.w_up, inp.w_down)
+    q = O.quantize_weights_mxfp8(wg, wu, wd)
+    qt = O.quantize_weights_mxfp8_dgrad(wg, wu, wd)
+    w = M.LayerWeights(w_r=dev_bf16(inp.w_r), bias=dev(inp.bias) if inp.bias is not None else None)
+    w.wq = {k: dev(v) for k, v in q.items()}
+    w.wq.update({k: dev(v) for k, v in qt.items()})
+    x, dout = dev_bf16(inp.x), dev_bf16(inp.dout)
+    base = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, with_bwd=True)
+    base.forward(x)
+    gb = {k: v.clone() for k, v in base.backward(x, dout).items()}
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, with_bwd=True, mx_wgrad=True)
+    layer.forward(x)
+    for t in layer.grads.values():
+        t.view(torch.uint8).fill_(0xFF)
+    g = layer.backward(x, dout)
+    torch.cuda.synchronize()
+    for k in ("dx", "dprob"):
+        assert torch.equal(g[k].view(torch.uint8), gb[k].view(torch.uint8)), k
+    ref = O.layer_fwd_mxfp8(inp.x, inp.w_r, inp.bias, q, wl.K, n_shared=1 if shared else 0,
+                            logits=logits_checked(layer.saved, inp))
+    assert_same_route(layer.saved, ref)
+    rb = O.layer_bwd_mxfp8(ref, inp.dout, qt, wgrad="mx")
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        got = vals(g[k])
+        assert np.all(np.isfinite(got)), k
+        err = rel_frobenius(got, rb[k])
+        print(f"  {k} rel {err:.2e}", flush=True)
+        assert err <= 1e-2, (k, err)
+    for e in np.nonzero(ref["counts"] == 0)[0]:
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            assert not bits(g[k])[e].any(), (k, e)
