@@ -69,9 +69,11 @@ def gemm2_work(R, D, H, E_act, b=2.0):
     return F, Q
 
 
-def dispatch_bytes(N, D, K, R, b=2.0):
-    """Each token row read once and written to each of its valid routes."""
-    return 2 * N * D + b * R * D + 4 * N * K
+def dispatch_bytes(N, D, K, R, b=2.0, pad_rows=0):
+    """Each token row read once and written to each of its valid routes; with
+    32-row groups (MXFP8) the padding rows of each group are part of the
+    output (zero codes and scales) and are written too."""
+    return 2 * N * D + b * (R + pad_rows) * D + 4 * N * K
 
 
 def combine_bytes(N, D, K, R):
@@ -509,7 +511,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
     roof["per_launch_algorithmic"] = dict(flops=F1, bytes=Q1, t_star_ms=t_star(F1, Q1, peak) * 1e3)
 
     gemm_tflops = routed_flops(R, D, H) / (t1 + t2) / 1e12
-    qd = dispatch_bytes(N, D, K, R, b)
+    pad = int((((counts + wl.align - 1) // wl.align) * wl.align - counts).sum()) if wl.align > 1 else 0
+    qd = dispatch_bytes(N, D, K, R, b, pad)
     qc = combine_bytes(N, D, K, R)
     tstar_layer = sum([t_star(*router_work(N, D, E), peak), qd / (PEAK_HBM_GBS * 1e9), t_star(F1, Q1, peak),
                        t_star(F2, Q2, peak), qc / (PEAK_HBM_GBS * 1e9)])

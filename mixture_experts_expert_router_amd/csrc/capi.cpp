@@ -137,14 +137,15 @@ RouterBwdLayout router_bwd_layout(const moe_dims& d) {
 // [dG | dU] quantized and X_d dequantized, then the router backward's scratch
 struct BwdLayout {
   size_t dyd, dxd, dg, du, h, dyq, dys, guq, gus, xdeq, router, total;
-  // native MXFP8 wgrad: column-wise copies [width][ldt] and scales [width][ldt/32]
-  size_t dyt_q, dyt_s, xt_q, xt_s, ht_q, ht_s, dgt_q, dgt_s, dut_q, dut_s;
+  // native MXFP8 wgrad: per-expert block offsets and the column-wise copies
+  // (width x ldt codes, width x ldt / 32 scales)
+  size_t toff, dyt_q, dyt_s, xt_q, xt_s, ht_q, ht_s, dgt_q, dgt_s, dut_q, dut_s;
   int64_t ldt;
 };
 
-// columns of the column-wise copies: every row of the expert-contiguous
-// buffers, rounded up to whole 128-column contraction steps
-int64_t cols_ld(const moe_dims& d) { return (rows_cap_of(d) + 127) / 128 * 128; }
+// columns of the column-wise copies: each expert's rows rounded up to whole
+// 128-column contraction steps, so at most rows_cap + 96 per expert
+int64_t cols_ld(const moe_dims& d) { return (rows_cap_of(d) + 96 * experts_of(d) + 127) / 128 * 128; }
 
 BwdLayout bwd_layout(const moe_dims& d, bool mx, bool mxw = false) {
   BwdLayout l{};
@@ -169,6 +170,7 @@ BwdLayout bwd_layout(const moe_dims& d, bool mx, bool mxw = false) {
   if (mx && mxw) {
     const size_t ldt = (size_t)cols_ld(d);
     l.ldt = (int64_t)ldt;
+    take(l.toff, ((size_t)experts_of(d) + 1) * 4);
     take(l.dyt_q, D * ldt);
     take(l.dyt_s, D * ldt / 32);
     take(l.xt_q, D * ldt);
@@ -686,7 +688,8 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     if (mxw) {
       REQUIRE(sv->row_route);
       REQUIRE(a->x);
-      if (!moe::gemm_wgrad_mx_ok(d.D, d.H, cols_ld(d)) || !moe::gemm_wgrad_mx_ok(d.H, d.D, cols_ld(d)))
+      const int64_t max_len = (rows_cap_of(d) + 127) / 128 * 128;   // one expert holding every row
+      if (!moe::gemm_wgrad_mx_ok(d.D, d.H, max_len) || !moe::gemm_wgrad_mx_ok(d.H, d.D, max_len))
         return MOE_ERR_SHAPE;
     }
     REQUIRE(a->wdt_q);
@@ -775,31 +778,33 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
       // saved G and U, dG and dU from the down dgrad, X_d gathered from x
       const int64_t ld = bl.ldt;
       auto cp = [&](size_t o) { return (uint8_t*)(p0 + o); };
+      int32_t* toff = (int32_t*)(p0 + bl.toff);
+      if (e == hipSuccess) e = moe::launch_seg128_scan(sv->offsets, Ex, toff, s);
       if (e == hipSuccess) e = moe::launch_swiglu(sv->g, sv->u, rc, d.H, hdq, nullptr, nullptr, s);
       if (e == hipSuccess)
-        e = moe::launch_quantize_cols_seg(dyd, rc, d.D, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dyt_q),
+        e = moe::launch_quantize_cols_seg(dyd, d.D, sv->offsets, Ex, toff, ld, nullptr, 0, nullptr, 0, cp(bl.dyt_q),
                                           cp(bl.dyt_s), s);
       if (e == hipSuccess)
-        e = moe::launch_quantize_cols_seg(hdq, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.ht_q),
+        e = moe::launch_quantize_cols_seg(hdq, d.H, sv->offsets, Ex, toff, ld, nullptr, 0, nullptr, 0, cp(bl.ht_q),
                                           cp(bl.ht_s), s);
       if (e == hipSuccess)
-        e = moe::launch_quantize_cols_seg(dg, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dgt_q),
+        e = moe::launch_quantize_cols_seg(dg, d.H, sv->offsets, Ex, toff, ld, nullptr, 0, nullptr, 0, cp(bl.dgt_q),
                                           cp(bl.dgt_s), s);
       if (e == hipSuccess)
-        e = moe::launch_quantize_cols_seg(du, rc, d.H, ld, rows_end, nullptr, 0, nullptr, 0, cp(bl.dut_q),
+        e = moe::launch_quantize_cols_seg(du, d.H, sv->offsets, Ex, toff, ld, nullptr, 0, nullptr, 0, cp(bl.dut_q),
                                           cp(bl.dut_s), s);
       if (e == hipSuccess)
-        e = moe::launch_quantize_cols_seg(a->x, rc, d.D, ld, rows_end, sv->row_route, d.K, shared_row0, d.N,
+        e = moe::launch_quantize_cols_seg(a->x, d.D, sv->offsets, Ex, toff, ld, sv->row_route, d.K, shared_row0, d.N,
                                           cp(bl.xt_q), cp(bl.xt_s), s);
       // dW_down[e] [D][H] = dY_e^T H_e; dW_gate / dW_up [H][D] = dG_e^T X_e, dU_e^T X_e
       if (e == hipSuccess)
-        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.D, d.H, ld, cp(bl.dyt_q), cp(bl.dyt_s), cp(bl.ht_q),
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, toff, Ex, d.D, d.H, cp(bl.dyt_q), cp(bl.dyt_s), cp(bl.ht_q),
                                       cp(bl.ht_s), gr->dw_down, table, s);
       if (e == hipSuccess)
-        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.H, d.D, ld, cp(bl.dgt_q), cp(bl.dgt_s), cp(bl.xt_q),
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, toff, Ex, d.H, d.D, cp(bl.dgt_q), cp(bl.dgt_s), cp(bl.xt_q),
                                       cp(bl.xt_s), gr->dw_gate, table, s);
       if (e == hipSuccess)
-        e = moe::launch_gemm_wgrad_mx(sv->offsets, Ex, d.H, d.D, ld, cp(bl.dut_q), cp(bl.dut_s), cp(bl.xt_q),
+        e = moe::launch_gemm_wgrad_mx(sv->offsets, toff, Ex, d.H, d.D, cp(bl.dut_q), cp(bl.dut_s), cp(bl.xt_q),
                                       cp(bl.xt_s), gr->dw_up, table, s);
     } else {
       // weight gradients: bf16 products on the dequantized activations; in the

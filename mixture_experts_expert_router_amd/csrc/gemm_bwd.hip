@@ -383,31 +383,31 @@ __global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restr
 // Native block-scaled weight gradient (OLMo-core Appendix A, A.15; KOSMOS
 // section 3.3.2 step 1: the operands' column-wise copies quantized from their
 // bf16 values):  db[e][m][n] = sum over the rows r of expert e of
-// aT[m][r] bT[n][r] (eq. 87), with aT [M][ld] and bT [N][ld] E4M3 copies
-// quantized along r in blocks of 32 and their E8M0 scales [M][ld/32],
-// [N][ld/32].  Items are (expert, 256-row tile of db, 256-column tile) on the
-// wgrad planner's order and queues.  An expert's rows start on a multiple of
-// 32, so its contraction window starts inside a 128-column step: the steps
-// are taken 128-aligned in the copies (whole chunks and 4-byte scale
-// groups) and the B tile's columns outside the window are zeroed in LDS.
+// aT[m][r] bT[n][r] (eq. 87).  The copies hold one contiguous block per
+// expert (quantize_cols_seg_kernel): expert e's aT is [M][len128] E4M3 at byte
+// M * toff[e] with scales [M][len128 / 32] at M * toff[e] / 32 (bT likewise
+// with N), len128 = its rows rounded up to 128, the columns past its rows
+// zero, so whole 128-column steps contract exactly its rows.  Items are
+// (expert, 256-row tile of db, 256-column tile) on the wgrad planner's order
+// and queues; an expert without rows clears its db.
 
 struct WgradMxParams {
   const int32_t* offsets;   // [E+1], row segments (multiples of 32)
+  const int32_t* toff;      // [E+1], the copies' block offsets (columns)
   const int32_t* plan;      // wgrad planner output
   int32_t* head;            // queue heads
   int E, M, N, m_tiles, n_tiles;
-  int64_t ld;               // columns of the copies (bytes per code row), % 128 == 0
-  const uint8_t* aq;        // [M][ld]
-  const uint8_t* as;        // [M][ld/32]
-  const uint8_t* bq;        // [N][ld]
-  const uint8_t* bs;        // [N][ld/32]
+  const uint8_t* aq;        // the copies of aT (width M) and bT (width N)
+  const uint8_t* as;
+  const uint8_t* bq;
+  const uint8_t* bs;
   uint16_t* c;              // [E][M][N] bf16
 };
 
 using WmxTile = tile::TileCfg<256, 256, 2, 4, 2, false, true>;   // 2 x 64 KB ring + scale groups
 
 struct WmxItem {
-  int e, c0, c1, m0, n0, idx;   // contraction window [c0, c1) of the copies' columns
+  int e, t0, len, m0, n0, idx;   // the expert's block: columns [t0, t0 + len) of the copies
   bool valid;
 };
 
@@ -418,8 +418,8 @@ __device__ __forceinline__ WmxItem claim_wmx(const WgradMxParams& p, int* s_item
   const int per_e = p.m_tiles * p.n_tiles;
   const int ei = item / per_e;
   it.e = p.plan[1 + ei];
-  it.c0 = p.offsets[it.e];
-  it.c1 = p.offsets[it.e + 1];
+  it.t0 = p.toff[it.e];
+  it.len = p.toff[it.e + 1] - it.t0;
   int mt, nt;
   it.idx = item - ei * per_e;
   superblock_decode(it.idx, p.m_tiles, p.n_tiles, mt, nt);
@@ -429,9 +429,7 @@ __device__ __forceinline__ WmxItem claim_wmx(const WgradMxParams& p, int* s_item
   return it;
 }
 
-__device__ __forceinline__ int wmx_steps(const WmxItem& it) {
-  return it.c1 > it.c0 ? (it.c1 + tile::kRB - 1) / tile::kRB - it.c0 / tile::kRB : 0;
-}
+__device__ __forceinline__ int wmx_steps(const WmxItem& it) { return it.len / tile::kRB; }
 
 // DMA sources (rows past M or N reload the last row and are never stored);
 // scale load q of a wave: A rows, then B rows, then padding rows that reload
@@ -440,26 +438,25 @@ __device__ __forceinline__ void sources_wmx(const WgradMxParams& p, const WmxIte
   using namespace tile;
   using C = WmxTile;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s0 = it.c0 / kRB;
   const int d_chunk = dma_chunk();
-  src.a = uniform_ptr(p.aq + (int64_t)s0 * kRB);
-  src.b = uniform_ptr(p.bq + (int64_t)s0 * kRB);
+  src.a = uniform_ptr(p.aq + (int64_t)p.M * it.t0);
+  src.b = uniform_ptr(p.bq + (int64_t)p.N * it.t0);
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q)
-    src.a_off[q] = (uint32_t)(min(it.m0 + dma_row(wave, C::A_INS, q), p.M - 1) * p.ld + d_chunk * 16);
+    src.a_off[q] = (uint32_t)(min(it.m0 + dma_row(wave, C::A_INS, q), p.M - 1) * it.len + d_chunk * 16);
 #pragma unroll
   for (int q = 0; q < C::B_INS; ++q)
-    src.b_off[q] = (uint32_t)(min(it.n0 + dma_row(wave, C::B_INS, q), p.N - 1) * p.ld + d_chunk * 16);
-  src.s_ks = (int)(p.ld / 32);
+    src.b_off[q] = (uint32_t)(min(it.n0 + dma_row(wave, C::B_INS, q), p.N - 1) * it.len + d_chunk * 16);
+  src.s_ks = it.len / 32;
 #pragma unroll
   for (int q = 0; q < C::SCI; ++q) {
     const int r0 = wave * C::SRW + q * 16;
     if (r0 < C::BM || r0 >= C::BM + C::BN) {
-      src.s[q] = uniform_ptr(p.as + (int64_t)s0 * 4);
+      src.s[q] = uniform_ptr(p.as + (int64_t)p.M * it.t0 / 32);
       src.s_row0[q] = it.m0 + (r0 < C::BM ? r0 : 0);
       src.s_lim[q] = p.M - 1;
     } else {
-      src.s[q] = uniform_ptr(p.bs + (int64_t)s0 * 4);
+      src.s[q] = uniform_ptr(p.bs + (int64_t)p.N * it.t0 / 32);
       src.s_row0[q] = __builtin_amdgcn_readfirstlane(it.n0 + r0 - C::BM);
       src.s_lim[q] = p.N - 1;
     }
@@ -501,6 +498,8 @@ __device__ __forceinline__ void zero_wmx(const WgradMxParams& p, const WmxItem& 
     *reinterpret_cast<uint4*>(base + off) = make_uint4(0, 0, 0, 0);
 }
 
+// Items are claimed one ahead: the claim of the item after next (an atomic
+// round trip) overlaps the next item's first loads and this item's stores.
 __global__ __launch_bounds__(512) void gemm_wgrad_mx_kernel(WgradMxParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[WmxTile::LDS];
   __shared__ int s_item;
@@ -508,6 +507,8 @@ __global__ __launch_bounds__(512) void gemm_wgrad_mx_kernel(WgradMxParams p) {
   const int xcd = xcd_id();
   WmxItem it = claim_wmx(p, &s_item, xcd);
   if (!it.valid) return;
+  __syncthreads();   // every wave has read s_item before it is reused
+  WmxItem next = claim_wmx(p, &s_item, xcd);
   if (wmx_steps(it) > 0) {
     tile::Src<WmxTile> src;
     sources_wmx(p, it, src);
@@ -519,20 +520,20 @@ __global__ __launch_bounds__(512) void gemm_wgrad_mx_kernel(WgradMxParams p) {
     if (nk > 0) {
       tile::Src<WmxTile> src;
       sources_wmx(p, it, src);
-      const int s0 = it.c0 / tile::kRB;
-      tile::mainloop_mx_window<WmxTile>(smem, lds0, src, nk, it.c0 - s0 * tile::kRB,
-                                        it.c1 - (s0 + nk - 1) * tile::kRB, acc);
+      tile::mainloop_mx<WmxTile>(smem, lds0, src, nk, acc);   // ends with a barrier
+    } else {
+      __syncthreads();   // every wave has read s_item before the claim below rewrites it
     }
-    __syncthreads();   // every wave has read s_item before the next claim rewrites it
-    const WmxItem next = claim_wmx(p, &s_item, xcd);
     if (next.valid && wmx_steps(next) > 0) {
       tile::Src<WmxTile> ns;
       sources_wmx(p, next, ns);
       tile::prologue<WmxTile>(lds0, ns, wmx_steps(next));
     }
+    const WmxItem after = next.valid ? claim_wmx(p, &s_item, xcd) : WmxItem{};
     if (nk > 0) epilogue_wmx(p, it, acc);
     else zero_wmx(p, it);
     it = next;
+    next = after;
   }
 }
 
@@ -622,24 +623,24 @@ hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, in
   return hipGetLastError();
 }
 
-// MXFP8 wgrad: copies of ld columns (% 128), output dims % 32, 32-bit
-// offsets into the copies
-bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t ld) {
-  return M % 32 == 0 && N % 32 == 0 && M >= 32 && N >= 32 && ld % 128 == 0 && M * ld < (int64_t(1) << 31) &&
-         N * ld < (int64_t(1) << 31);
+// MXFP8 wgrad: output dims % 32, 32-bit offsets into an expert's block of
+// at most max_len columns
+bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t max_len) {
+  return M % 32 == 0 && N % 32 == 0 && M >= 32 && N >= 32 && M * max_len < (int64_t(1) << 31) &&
+         N * max_len < (int64_t(1) << 31);
 }
 
-hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, int64_t E, int64_t M, int64_t N, int64_t ld,
+hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, const int32_t* toff, int64_t E, int64_t M, int64_t N,
                                 const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, void* db,
                                 int32_t* ws, hipStream_t s) {
   WgradMxParams p{};
   p.offsets = offsets;
+  p.toff = toff;
   p.E = (int)E;
   p.M = (int)M;
   p.N = (int)N;
   p.m_tiles = (p.M + WmxTile::BM - 1) / WmxTile::BM;
   p.n_tiles = (p.N + WmxTile::BN - 1) / WmxTile::BN;
-  p.ld = ld;
   p.aq = aq;
   p.as = as;
   p.bq = bq;

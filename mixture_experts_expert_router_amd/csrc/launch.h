@@ -108,14 +108,17 @@ hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uin
 // along r; scales [b][c][(col0 + r) / 32] (row stride ld / 32)
 hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                                 int64_t col0, uint8_t* q, uint8_t* sc, hipStream_t s);
-// column-wise copy for the native MXFP8 wgrad: src bf16 [rows][cols] (or the
-// token rows x [N][cols] gathered through row_route / K and the shared
-// segment at *shared0 when row_route is given) -> q [cols][ld] and scales
-// [cols][ld/32], blocks of 32 rows of one column; rows >= *rows_end and
-// columns past rows are zero (ld % 128 == 0)
-hipError_t launch_quantize_cols_seg(const void* src, int64_t rows, int64_t cols, int64_t ld, const int32_t* rows_end,
-                                    const int32_t* row_route, int64_t K, const int32_t* shared0, int64_t N,
-                                    uint8_t* q, uint8_t* sc, hipStream_t s);
+// column-wise copies for the native MXFP8 wgrad, one contiguous block per
+// expert: toff[e] = exclusive scan of the segments rounded up to 128 rows
+// (Ex + 1 entries); the copy of src bf16 [rows][cols] (or of the token rows x
+// [N][cols] gathered through row_route / K and the shared segment at
+// *shared0 when row_route is given) holds expert e as q[C * toff[e] +
+// c * len128 + i] (E4M3, blocks of 32 rows i), scales at the byte offset / 32;
+// max_cols bounds toff[Ex] (the grid's extent)
+hipError_t launch_seg128_scan(const int32_t* offsets, int64_t Ex, int32_t* toff, hipStream_t s);
+hipError_t launch_quantize_cols_seg(const void* src, int64_t cols, const int32_t* offsets, int64_t Ex,
+                                    const int32_t* toff, int64_t max_cols, const int32_t* row_route, int64_t K,
+                                    const int32_t* shared0, int64_t N, uint8_t* q, uint8_t* sc, hipStream_t s);
 // bf16 [rows][cols] from E4M3 + E8M0 row-wise blocks; rows >= *rows_end skipped
 hipError_t launch_dequant_rows(const uint8_t* q, const uint8_t* sc, int64_t rows, int64_t cols,
                                const int32_t* rows_end, void* out, hipStream_t s);
@@ -170,10 +173,10 @@ bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db);
 hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s,
                                   bool f32 = false);
 // native MXFP8 wgrad: db[e][m][n] = sum over expert e's rows r of aT[m][r] bT[n][r]
-// with column-wise copies aT [M][ld], bT [N][ld] (E4M3) and scales [.][ld/32];
-// row segments from offsets (multiples of 32); bf16 db [E][M][N]
-bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t ld);
-hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, int64_t E, int64_t M, int64_t N, int64_t ld,
+// with the per-expert column-wise copies of launch_quantize_cols_seg (aT of
+// width M, bT of width N, both laid out by toff); bf16 db [E][M][N]
+bool gemm_wgrad_mx_ok(int64_t M, int64_t N, int64_t max_len);
+hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, const int32_t* toff, int64_t E, int64_t M, int64_t N,
                                 const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, void* db,
                                 int32_t* ws, hipStream_t s);
 

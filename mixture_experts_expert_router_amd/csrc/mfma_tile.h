@@ -331,68 +331,6 @@ __device__ __forceinline__ void mainloop_mx(const uint8_t* smem, uint32_t lds0, 
   __syncthreads();   // every wave is done reading the ring before it is refilled
 }
 
-// The MXFP8 main loop over a contraction window that need not start or end
-// on a step boundary: only columns [lo, 128) of step 0 and [0, hi) of step
-// nk - 1 are inside it (lo, hi multiples of 16).  The B tile's chunks outside
-// the window are zeroed in LDS after they land, so their products with the A
-// tile (finite codes, finite scales) add exactly 0.
-template <class C>
-__device__ __forceinline__ void mainloop_mx_window(const uint8_t* smem, uint32_t lds0, const Src<C>& src, int nk,
-                                                   int lo, int hi, f32x4_t (&acc)[C::TM][C::TN]) {
-  static_assert(C::MX, "MXFP8 tiles");
-  static_assert(C::A_WAVES == C::NW, "every wave loads A rows");
-  constexpr int TM = C::TM, TN = C::TN, NS = C::NS;
-  const FragBase<C> fb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WAVES_N_, wn = wave % C::WAVES_N_;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const uint32_t as_b = (uint32_t)(C::SC_BASE + (wm * C::WM + l16) * 16 + lg);
-  const uint32_t bs_b = (uint32_t)(C::SC_BASE + (C::BM + wn * C::WNB + l16) * 16 + lg);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_step_mx<C>(kt, nk);
-    __syncthreads();   // step kt landed for every wave; every wave is done with step kt-1
-    if (kt + NS - 1 < nk) issue_step<C>(lds0, src, kt + NS - 1, nk);
-    const int zlo = kt == 0 ? lo : 0, zhi = kt == nk - 1 ? hi : kRB;
-    if (zlo > 0 || zhi < kRB) {
-      uint8_t* bt = const_cast<uint8_t*>(smem) + (kt % NS) * C::STAGE + C::A_BYTES;
-      for (int idx = threadIdx.x; idx < C::BN * 8; idx += C::NW * 64) {
-        const int r = idx >> 3, c = idx & 7;
-        if (c * 16 < zlo || c * 16 >= zhi)
-          *reinterpret_cast<uint4*>(bt + r * kRB + (slot_of(r, c) << 4)) = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-    }
-    const uint8_t* st = smem + (kt % NS) * C::STAGE;
-    const uint8_t* alo = st + fb.a_lo;
-    const uint8_t* ahi = st + fb.a_hi;
-    const uint8_t* blo = st + fb.b_lo;
-    const uint8_t* bhi = st + fb.b_hi;
-    const int sgo = ((kt / kScG) & 1) * C::SG_BYTES + (kt % kScG) * 4;
-    const uint8_t* sa_p = smem + as_b + sgo;
-    const uint8_t* sb_p = smem + bs_b + sgo;
-    i32x8_t af[TM];
-    int sa[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      af[i] = load_frag8(alo + i * 16 * kRB, ahi + i * 16 * kRB);
-      sa[i] = sa_p[i * 16 * 16];
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const i32x8_t b = load_frag8(blo + b_frag_row<C>(j) * kRB, bhi + b_frag_row<C>(j) * kRB);
-      const int sb = sb_p[b_frag_row<C>(j) * 16];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, af[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
-    }
-  }
-  __syncthreads();   // every wave is done reading the ring before it is refilled
-}
-
 // ---------------------------------------------------------------------------
 // k-major (transposed-storage) operands, for the backward GEMMs: the operand
 // is stored with its contraction index k as the row and the tile's own index

@@ -65,32 +65,76 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
   sc[(b * C + c0 + c) * (ld / 32) + (col0 + r) / 32] = (uint8_t)code;
 }
 
-// Column-wise copy of a row-segmented matrix for the native MXFP8 weight
-// gradient: src bf16 [R][C] (expert segments along the rows, multiples of 32
-// rows) -> q[c][r] (row stride ld, ld % 128 == 0), blocks of 32 rows of one
-// column, scales [c][r / 32] (row stride ld / 32).  Rows at or past
-// *rows_end, and the columns r in [R, ld), are written as zero codes and
-// scales.  gather: row r of src is instead token row_route[r] / K of x (rows
-// without a route are zero), and the shared expert's segment (shared0 ..
-// shared0 + N, when given) holds x itself; this reads the bf16 token rows a
-// dispatched matrix was made from.
-__global__ __launch_bounds__(256) void quantize_cols_seg_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                                int64_t C, int64_t ld,
-                                                                const int32_t* __restrict__ rows_end,
+// Column-wise copies of a row-segmented matrix for the native MXFP8 weight
+// gradient, one contiguous block per expert.  Expert e's rows
+// [offsets[e], offsets[e+1]) (a multiple of 32) become a [C][len128]
+// E4M3 block, len128 = the segment rounded up to 128 columns, quantized
+// along its rows in blocks of 32, columns past the segment zero; the blocks
+// follow each other: expert e's starts at byte C * toff[e] (toff = the
+// exclusive scan of len128) and its scales ([C][len128 / 32]) at byte
+// C * toff[e] / 32.  A weight-gradient tile then reads 128-column steps of one
+// expert's rows as contiguous runs instead of short pieces of long rows.
+//
+// seg128_scan_kernel: toff[0..Ex] in one workgroup (Ex <= 1024).
+__global__ __launch_bounds__(1024) void seg128_scan_kernel(const int32_t* __restrict__ offsets, int Ex,
+                                                           int32_t* __restrict__ toff) {
+  __shared__ int s_w[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int len = t < Ex ? offsets[t + 1] - offsets[t] : 0;
+  const int own = (len + 127) / 128 * 128;
+  int inc = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) s_w[wv] = inc;
+  __syncthreads();
+  if (t == 0) {
+    int r = 0;
+    for (int w = 0; w < 16; ++w) { const int v = s_w[w]; s_w[w] = r; r += v; }
+  }
+  __syncthreads();
+  inc += s_w[wv];
+  if (t < Ex) toff[t] = inc - own;
+  if (t == Ex - 1) toff[Ex] = inc;
+}
+
+// Block y of the grid covers destination columns [128 y, 128 y + 128) of the
+// concatenated blocks (one 128-column chunk of one expert): source rows
+// offsets[e] + 128 y - toff[e] + (0..127), zero past the segment.  gather:
+// source row r is token row_route[r] / K of x (zero without a route), and
+// the shared expert's segment (shared0 .. shared0 + N, when given) holds x.
+// Blocks past toff[Ex] exit.
+__global__ __launch_bounds__(256) void quantize_cols_seg_kernel(const uint16_t* __restrict__ src, int64_t C,
+                                                                const int32_t* __restrict__ offsets, int Ex,
+                                                                const int32_t* __restrict__ toff,
                                                                 const int32_t* __restrict__ row_route, int K,
                                                                 const int32_t* __restrict__ shared0, int64_t N,
                                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kQR][kQC + kQPad];
-  const int64_t r0 = (int64_t)blockIdx.y * kQR, c0 = (int64_t)blockIdx.x * kQC;
-  const int64_t rend = min(R, (int64_t)*rows_end);
+  const int64_t p = (int64_t)blockIdx.y * kQR;   // destination column of the chunk
+  if (p >= toff[Ex]) return;
+  // the expert whose block holds column p (toff is non-decreasing)
+  int lo = 0, hi = Ex - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (toff[mid] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int64_t local = p - toff[e];
+  const int64_t seg0 = offsets[e], seg1 = offsets[e + 1];
+  const int64_t len128 = toff[e + 1] - toff[e];
+  const int64_t c0 = (int64_t)blockIdx.x * kQC;
   const int64_t s0 = shared0 ? (int64_t)*shared0 : -1;
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kQR / 32; ++i) {
     const int rr = t / 8 + 32 * i, cc = (t % 8) * 8;
-    const int64_t r = r0 + rr;
+    const int64_t r = seg0 + local + rr;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < rend && c0 + cc < C) {
+    if (r < seg1 && c0 + cc < C) {
       int64_t srow = r;
       if (row_route) {
         const int rt = row_route[r];
@@ -102,8 +146,7 @@ __global__ __launch_bounds__(256) void quantize_cols_seg_kernel(const uint16_t* 
   }
   __syncthreads();
   const int c = t % kQC, blk = t / kQC;
-  const int64_t r = r0 + 32 * blk;
-  if (c0 + c >= C || r >= ld) return;
+  if (c0 + c >= C) return;
   float f[32];
   float amax = 0.0f;
 #pragma unroll
@@ -112,14 +155,15 @@ __global__ __launch_bounds__(256) void quantize_cols_seg_kernel(const uint16_t* 
     amax = fmaxf(amax, fabsf(f[i]));
   }
   const int code = e8m0_code(amax);
-  const int e = code - 127;
+  const int ex = code - 127;
   uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], e);
-  uint8_t* dst = q + (c0 + c) * ld + r;
+  for (int i = 0; i < 8; ++i) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], ex);
+  const int64_t col = local + 32 * blk;   // within the expert's block
+  uint8_t* dst = q + C * toff[e] + (c0 + c) * len128 + col;
   stg16(dst, make_uint4(w[0], w[1], w[2], w[3]));
   stg16(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
-  sc[(c0 + c) * (ld / 32) + r / 32] = (uint8_t)code;
+  sc[(C * toff[e] + (c0 + c) * len128 + col) / 32] = (uint8_t)code;
 }
 
 // E4M3FN code -> its value as fp32 (exact; codes 0x7F / 0xFF, NaN in E4M3FN,
@@ -167,13 +211,18 @@ hipError_t launch_quantize_cols(const void* src, int64_t batch, int64_t rows, in
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_cols_seg(const void* src, int64_t rows, int64_t cols, int64_t ld, const int32_t* rows_end,
-                                    const int32_t* row_route, int64_t K, const int32_t* shared0, int64_t N,
-                                    uint8_t* q, uint8_t* sc, hipStream_t s) {
-  if (cols == 0 || ld == 0) return hipSuccess;
-  const dim3 grid((unsigned)((cols + kQC - 1) / kQC), (unsigned)(ld / kQR), 1);
-  quantize_cols_seg_kernel<<<grid, 256, 0, s>>>((const uint16_t*)src, rows, cols, ld, rows_end, row_route, (int)K,
-                                                shared0, N, q, sc);
+hipError_t launch_seg128_scan(const int32_t* offsets, int64_t Ex, int32_t* toff, hipStream_t s) {
+  seg128_scan_kernel<<<1, 1024, 0, s>>>(offsets, (int)Ex, toff);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols_seg(const void* src, int64_t cols, const int32_t* offsets, int64_t Ex,
+                                    const int32_t* toff, int64_t max_cols, const int32_t* row_route, int64_t K,
+                                    const int32_t* shared0, int64_t N, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (cols == 0 || max_cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + kQC - 1) / kQC), (unsigned)((max_cols + kQR - 1) / kQR), 1);
+  quantize_cols_seg_kernel<<<grid, 256, 0, s>>>((const uint16_t*)src, cols, offsets, (int)Ex, toff, row_route,
+                                                (int)K, shared0, N, q, sc);
   return hipGetLastError();
 }
 
