@@ -765,11 +765,16 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     moe::GemmFwd gu{Ex, rc, 2 * d.H, d.D, sv->offsets, guq, gus, a->wgut_q, a->wgut_s, nullptr,
                     nullptr, dxd, nullptr, nullptr, nullptr, nullptr, false};
     if (!moe::gemm_fwd_fast_ok(dn, true) || !moe::gemm_fwd_fast_ok(gu, true)) return MOE_ERR_SHAPE;
+    // dY arrives in bf16 and is quantized where it lands (KOSMOS section 3.3.2
+    // step 1): in the combine backward itself when D % 128 == 0, else by a
+    // pass over dY_d
+    const bool fuse_q = moe::combine_bwd_quant_ok(d.D, dyq, dys);
     e = moe::launch_combine_bwd(dout, sv->dst_rows, sv->topk_prob, sv->y, d.N, d.D, d.K, dyd, gr->dprob, s,
-                                shared_row0);
-    if (e == hipSuccess) e = moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
-    // dY arrives in bf16 and is quantized where it lands (KOSMOS section 3.3.2 step 1)
-    if (e == hipSuccess) e = moe::launch_quantize_rows(dyd, rc, d.D, dyq, dys, s, rows_end);
+                                shared_row0, fuse_q ? dyq : nullptr, fuse_q ? dys : nullptr);
+    if (e == hipSuccess)
+      e = fuse_q ? moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, d.D, dyq, s, d.D / 32, dys)
+                 : moe::launch_zero_padding(sv->counts, sv->offsets, Ex, d.D * 2, dyd, 0, nullptr, s);
+    if (e == hipSuccess && !fuse_q) e = moe::launch_quantize_rows(dyd, rc, d.D, dyq, dys, s, rows_end);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(dn, true, table, s);
     if (e == hipSuccess) e = moe::launch_gemm_fwd_fast(gu, true, table, s);
     if (mxw) {

@@ -91,17 +91,22 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
                                  int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s,
                                  const int32_t* shared_row0 = nullptr, const int32_t* pad_counts = nullptr,
                                  const int32_t* pad_offsets = nullptr, int64_t pad_E = 0);
+// zero the padding rows of every expert segment in a (row_bytes, a multiple
+// of 16), b and c (optional)
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
-                               hipStream_t s);
+                               hipStream_t s, int64_t row_bytes3 = 0, void* c = nullptr);
 // addend (bf16 [N][D], optional) is added to each token's fp32 sum before rounding
 hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* weight, int64_t N,
                           int64_t D, int64_t K, void* out, hipStream_t s, const void* addend = nullptr,
                           const int32_t* shared_row0 = nullptr);
+// q/sc (optional): dY_d also quantized row-wise to MXFP8 as it is written
+// (needs combine_bwd_quant_ok)
 hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
                               const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
                               float* dprob, hipStream_t s,
-                         const int32_t* shared_row0 = nullptr);
+                         const int32_t* shared_row0 = nullptr, uint8_t* q = nullptr, uint8_t* sc = nullptr);
+bool combine_bwd_quant_ok(int64_t D, const void* q, const void* sc);
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
                                 uint8_t* sc, hipStream_t s, const int32_t* rows_end = nullptr);
 // src bf16 [batch][rows][cols] -> q[b][c][col0 + r] (row stride ld), quantized

@@ -232,7 +232,9 @@ __global__ __launch_bounds__(kPadThreads) void zero_padding_kernel(const int32_t
                                                                    const int32_t* __restrict__ offsets,
                                                                    int64_t row_bytes, uint8_t* __restrict__ a,
                                                                    int64_t row_bytes2,
-                                                                   uint8_t* __restrict__ b) {
+                                                                   uint8_t* __restrict__ b,
+                                                                   int64_t row_bytes3,
+                                                                   uint8_t* __restrict__ c) {
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r0 = offsets[e] + counts[e];
@@ -240,9 +242,16 @@ __global__ __launch_bounds__(kPadThreads) void zero_padding_kernel(const int32_t
   for (int64_t r = r0 + wave; r < r1; r += kPadThreads / 64) {
     uint4* pa = reinterpret_cast<uint4*>(a + r * row_bytes);
     for (int64_t i = lane; i < row_bytes / 16; i += 64) pa[i] = make_uint4(0, 0, 0, 0);
-    if (b) {
+    if (b && (row_bytes2 & 15) == 0) {
+      uint4* pb = reinterpret_cast<uint4*>(b + r * row_bytes2);
+      for (int64_t i = lane; i < row_bytes2 / 16; i += 64) pb[i] = make_uint4(0, 0, 0, 0);
+    } else if (b) {
       uint8_t* pb = b + r * row_bytes2;
       for (int64_t i = lane; i < row_bytes2; i += 64) pb[i] = 0;
+    }
+    if (c) {
+      uint8_t* pc = c + r * row_bytes3;
+      for (int64_t i = lane; i < row_bytes3; i += 64) pc[i] = 0;
     }
   }
 }
@@ -327,13 +336,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 // combine backward: dyd[dst] = bf16(w * dout[t]); dprob[t,k] = <dout[t], y[dst]>
+// QUANT (D % 128 == 0): each dY_d row is also quantized row-wise to MXFP8
+// where it lands (KOSMOS section 3.3.2 step 1), the same codes a separate
+// quantize_rows pass over dyd gives: a lane holds 8 elements, so a 32-block
+// is a lane quad; 8-byte code stores, and lanes 16i store the scales of four
+// consecutive blocks as one word.
+template <bool QUANT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dout,
                                                           const int32_t* __restrict__ dst_rows,
                                                           const float* __restrict__ weight,
                                                           const uint16_t* __restrict__ y, int N,
                                                           int D, int K, uint16_t* __restrict__ dyd,
                                                           float* __restrict__ dprob,
-                                                          const int32_t* __restrict__ shared_row0) {
+                                                          const int32_t* __restrict__ shared_row0,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
   // routes in chunks of KCH: every Y row of the chunk is loaded before any
   // product uses it, so the gathers overlap instead of waiting one by one;
   // each lane still sums its vectors in increasing order
@@ -381,8 +397,31 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
           const int v = v0 + lane + j * kWave;
+          const uint4 o = scale_bf16x8(r[j], wk[kk]);
+          if constexpr (QUANT) {
+            // every lane takes part in the shuffles; a quad is all in or all
+            // out (nvec % 16 == 0), and lanes past the row hold zeros
+            const float f[8] = {bf16lo(o.x), bf16hi(o.x), bf16lo(o.y), bf16hi(o.y),
+                                bf16lo(o.z), bf16hi(o.z), bf16lo(o.w), bf16hi(o.w)};
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const int code = e8m0_code(amax);
+            const int e = code - 127;
+            const uint2 qv = make_uint2(quant4(f, e), quant4(f + 4, e));
+            const uint32_t c1 = (uint32_t)__shfl_down(code, 4, 64), c2 = (uint32_t)__shfl_down(code, 8, 64),
+                           c3 = (uint32_t)__shfl_down(code, 12, 64);
+            if (v < nvec) {
+              *reinterpret_cast<uint2*>(q + (int64_t)dk[kk] * D + v * 8) = qv;
+              if ((lane & 15) == 0)
+                *reinterpret_cast<uint32_t*>(sc + (int64_t)dk[kk] * (D >> 5) + (v >> 2)) =
+                    (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+            }
+          }
           if (v >= nvec) continue;
-          stg16(dyd + (int64_t)dk[kk] * D + v * 8, scale_bf16x8(r[j], wk[kk]));
+          stg16(dyd + (int64_t)dk[kk] * D + v * 8, o);
           if (dprob) {
             const uint4 q = yy[kk][j];
             float s2 = dot[kk];
@@ -557,10 +596,10 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
 
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,
                                int64_t row_bytes, void* a, int64_t row_bytes2, void* b,
-                               hipStream_t s) {
+                               hipStream_t s, int64_t row_bytes3, void* c) {
   if (E == 0) return hipSuccess;
   zero_padding_kernel<<<(unsigned)E, kPadThreads, 0, s>>>(counts, offsets, row_bytes, (uint8_t*)a,
-                                                   row_bytes2, (uint8_t*)b);
+                                                   row_bytes2, (uint8_t*)b, row_bytes3, (uint8_t*)c);
   return hipGetLastError();
 }
 
@@ -581,12 +620,23 @@ hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* w
 
 hipError_t launch_combine_bwd(const void* dout, const int32_t* dst_rows, const float* weight,
                               const void* y, int64_t N, int64_t D, int64_t K, void* dyd,
-                              float* dprob, hipStream_t s, const int32_t* shared_row0) {
+                              float* dprob, hipStream_t s, const int32_t* shared_row0, uint8_t* q, uint8_t* sc) {
   if (N == 0) return hipSuccess;
-  combine_bwd_kernel<<<waves_grid(N), 256, 0, s>>>((const uint16_t*)dout, dst_rows, weight,
-                                                   (const uint16_t*)y, (int)N, (int)D, (int)K,
-                                                   (uint16_t*)dyd, dprob, shared_row0);
+  if (q) {
+    if (!combine_bwd_quant_ok(D, q, sc)) return hipErrorInvalidValue;
+    combine_bwd_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)dout, dst_rows, weight,
+                                                           (const uint16_t*)y, (int)N, (int)D, (int)K,
+                                                           (uint16_t*)dyd, dprob, shared_row0, q, sc);
+  } else {
+    combine_bwd_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)dout, dst_rows, weight,
+                                                            (const uint16_t*)y, (int)N, (int)D, (int)K,
+                                                            (uint16_t*)dyd, dprob, shared_row0, nullptr, nullptr);
+  }
   return hipGetLastError();
+}
+
+bool combine_bwd_quant_ok(int64_t D, const void* q, const void* sc) {
+  return D % 128 == 0 && ((uintptr_t)q & 15) == 0 && ((uintptr_t)sc & 3) == 0;
 }
 
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* q,
