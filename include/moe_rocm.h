@@ -58,9 +58,11 @@ extern "C" {
  * moe_layer_fwd writes these bits into the optional device int32
  * moe_layer_saved.status (0 = nothing to report).  They describe device-side
  * events that no host check can see; the call itself has returned MOE_OK. */
-#define MOE_STATUS_WAIT_EXPIRED 1   /* MOE_SCHED_READY: a bounded readiness wait gave
-                                       up; the items that waited were skipped, so
-                                       G, U, H, Y and the output are incomplete      */
+#define MOE_STATUS_WAIT_EXPIRED 1   /* MOE_SCHED_READY / MOE_SCHED_SINGLE: a bounded
+                                       readiness or barrier wait gave up; the items
+                                       (or, at a barrier, the rest of the launch) that
+                                       waited were skipped, so the outputs are
+                                       incomplete                                    */
 #define MOE_STATUS_NO_FINITE_LOGIT 2 /* a token had fewer than K non-NaN logits; each
                                        slot left without one has topk_idx = -1,
                                        probability 0 and no row (an invalid route)   */
@@ -314,11 +316,23 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
                                gated on their GEMM1 row blocks.  MOE_ERR_UNSUPPORTED
                                for MXFP8, a shared expert, or D, H off the rule
                                D % 64 == 0 and H % 64 == 0                       */
+/* MOE_SCHED_SINGLE (KOSMOS section 3.3, Figure 6: one launch from route to
+ * fold): the whole bf16 layer forward in one persistent launch, after a
+ * one-workgroup reset of its barrier words.  Its workgroups (one per CU) run
+ * the router tiles, then the logits, softmax and top-K per chunk of tokens,
+ * the histogram scan and plans (one workgroup), the scatter, each step ended
+ * by a grid barrier, then the MOE_SCHED_READY queue (dispatch, GEMM1 by
+ * readiness, GEMM2 gated on GEMM1 row blocks) followed by the fold, which
+ * waits until every workgroup has stored its GEMM2 tiles.  Every output is
+ * bitwise the staged forward's.  Same rules as MOE_SCHED_READY, and also the
+ * tiled router (D % 64 == 0, 16 <= E <= 512), K <= 32, no grouped top-K and
+ * no aux loss; else MOE_ERR_UNSUPPORTED.  Workspace MOE_OP_LAYER_FWD. */
+#define MOE_SCHED_SINGLE 2
 
 typedef struct moe_layer_args {
   moe_dims dims;
   int32_t dtype;
-  int32_t sched;        /* MOE_SCHED_STAGED or MOE_SCHED_READY (forward only)  */
+  int32_t sched;        /* MOE_SCHED_STAGED, _READY or _SINGLE (forward only)  */
   const void* x;        /* bf16 [N][D] */
   const void* w_r;      /* bf16 [E][D] */
   const float* bias;    /* fp32 [E] or NULL */
@@ -346,10 +360,11 @@ typedef struct moe_layer_args {
   const uint8_t* wgut_q;
   const uint8_t* wgut_s;
   /* Testing the status word only; 0 in normal use.  A positive value makes a
-   * MOE_SCHED_READY forward withhold its readiness flags and give up every
-   * bounded wait after this many polls, so that each wait expires, the
-   * waiting items are skipped, every kernel exits normally and
-   * MOE_STATUS_WAIT_EXPIRED is reported.  Ignored by the staged schedule. */
+   * MOE_SCHED_READY or MOE_SCHED_SINGLE forward withhold its readiness flags
+   * (and barrier arrivals) and give up every bounded wait after this many
+   * polls, so that each wait expires, the waiting items are skipped, every
+   * kernel exits normally and MOE_STATUS_WAIT_EXPIRED is reported.  Ignored
+   * by the staged schedule. */
   int32_t ready_test_polls;
   /* MXFP8 backward only: 0 = weight gradients as bf16 products on the
    * dequantized activations (OLMo-core Appendix A, A.13); 1 = native

@@ -27,7 +27,7 @@ MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_BWD = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_GEMM, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD, MOE_OP_ROUTER = 1, 2, 3, 4, 5
 MOE_OP_LAYER_BWD_MXFP8 = 6
 MOE_OP_LAYER_BWD_MXFP8_NATIVE = 7
-MOE_SCHED_STAGED, MOE_SCHED_READY = 0, 1
+MOE_SCHED_STAGED, MOE_SCHED_READY, MOE_SCHED_SINGLE = 0, 1, 2
 
 _vp = C.c_void_p
 _i64 = C.c_int64
@@ -450,7 +450,8 @@ def saved_tensors(sv: dict) -> dict:
 class MoeLayer:
     """Holds the weights, saved tensors and workspaces of one layer so that
     repeated forward/backward calls allocate nothing.  sched selects the
-    forward's launch scheme (MOE_SCHED_STAGED or MOE_SCHED_READY)."""
+    forward's launch scheme (MOE_SCHED_STAGED, MOE_SCHED_READY or
+    MOE_SCHED_SINGLE)."""
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
                  device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False, n_group=0,
@@ -469,7 +470,7 @@ class MoeLayer:
         _, self.d = _layer_args(self._x_proto, wts, K, drop, renorm, mxfp8, **self._opts)
         self.saved = alloc_saved(self.d, mxfp8, device)
         self._sv = _saved_struct(self.saved)
-        self.ready_test_polls = 0      # testing the status word of the READY schedule only
+        self.ready_test_polls = 0      # testing the status word of the READY / SINGLE schedules only
         self.out = torch.empty((N, D), dtype=torch.bfloat16, device=device)
         self.ws_f = workspace(MOE_OP_LAYER_FWD, self.d, device)
         self.grads = None

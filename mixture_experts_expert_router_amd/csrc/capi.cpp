@@ -553,15 +553,21 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                   size_t ws_bytes, void* stream) {
   if (!a || !sv) return MOE_ERR_NULL;
   if (a->dtype != MOE_BF16 && a->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
-  if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY) return MOE_ERR_DTYPE;
+  if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY && a->sched != MOE_SCHED_SINGLE)
+    return MOE_ERR_DTYPE;
   const bool mx = a->dtype == MOE_MXFP8;
   const moe_dims& d = a->dims;
   int st = check_dims(&d, true, mx);
   if (st) return st;
   const bool ready = a->sched == MOE_SCHED_READY;
+  const bool single = a->sched == MOE_SCHED_SINGLE;
   // the readiness-ordered launch is the bf16 persistent engine, routed experts only
-  if (ready && (mx || d.n_shared || d.align != 1 || !moe::gemm_fwd_fast_ok(d.D, d.H) ||
-                !moe::gemm_fwd_fast_ok(d.H, d.D)))
+  if ((ready || single) && (mx || d.n_shared || d.align != 1 || !moe::gemm_fwd_fast_ok(d.D, d.H) ||
+                            !moe::gemm_fwd_fast_ok(d.H, d.D)))
+    return MOE_ERR_UNSUPPORTED;
+  // the single launch also runs the tiled router and the plain top-K
+  if (single && (!moe::layer_fwd_single_ok(d.D, d.E, d.K) || d.n_group > 1 ||
+                 (sv->aux != nullptr && a->aux_alpha != 0.0f)))
     return MOE_ERR_UNSUPPORTED;
   if (a->ready_test_polls < 0) return MOE_ERR_SHAPE;
   REQUIRE(a->x);
@@ -612,6 +618,25 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   int32_t* table = (int32_t*)((char*)ws + rb);
   void* ws_router = (char*)ws + rb + tb;
 
+  if (single) {
+    // router, route, dispatch, GEMM1, GEMM2 and the fold in one persistent launch
+    moe::LayerFwdSingle one{};
+    one.x = moe::ExpertsFwd{d.E,     d.K,      d.D,      d.H,   rc,    d.N,   sv->offsets,
+                            sv->row_route, a->x, a->w_gate, a->w_up, a->w_down, sv->xd, sv->g,
+                            sv->u,   sv->h,    sv->y,    sv->status, a->ready_test_polls};
+    one.x_tokens = a->x;
+    one.w_r = a->w_r;
+    one.bias = a->bias;
+    one.logits = sv->logits;
+    one.drop = a->drop;
+    one.renorm = d.renorm;
+    one.topk_idx = sv->topk_idx;
+    one.topk_prob = sv->topk_prob;
+    one.counts = sv->counts;
+    one.dst_rows = sv->dst_rows;
+    one.out = out;
+    return hip_status(moe::launch_layer_fwd_single(one, table, ws_route, ws_router, s));
+  }
   hipError_t e = sv->status ? moe::launch_status_clear(sv->status, s) : hipSuccess;
   if (e == hipSuccess)
     e = moe::launch_router_logits(a->x, a->w_r, a->bias, d.N, d.D, d.E, sv->logits, ws_router, s);
@@ -633,7 +658,7 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g2, table, s);
   } else if (ready) {
     // dispatch, GEMM1 and GEMM2 in one persistent launch scheduled by readiness
-    moe::ExpertsFwd xf{d.E, d.K, d.D, d.H, rc, sv->offsets, sv->row_route, a->x, a->w_gate, a->w_up,
+    moe::ExpertsFwd xf{d.E, d.K, d.D, d.H, rc, d.N, sv->offsets, sv->row_route, a->x, a->w_gate, a->w_up,
                        a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y, sv->status, a->ready_test_polls};
     if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
   } else {

@@ -50,6 +50,9 @@
 #include "launch.h"
 #include "mfma_tile.h"
 #include "sched.h"
+#include "permute_dev.h"
+#include "route_dev.h"
+#include "router_dev.h"
 
 namespace moe {
 
@@ -519,10 +522,22 @@ __device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* sme
 __device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
-__global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  __shared__ int s_info[4];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+// The fold after the fused queue (single-launch layer): items of 8 tokens, a
+// wave per token.  Every workgroup publishes once, when it first claims past
+// the GEMM2 items (each of its GEMM2 tiles then is stored), and a fold item
+// waits until all of them have: the fold reads Y rows of any expert.
+struct FoldArgs {
+  const int32_t* dst_rows;   // [N][K]
+  const float* weight;       // [N][K] route weights
+  int N;
+  uint16_t* out;             // [N][D]
+  int32_t* passed;           // workgroups past the GEMM2 items (zeroed before the launch)
+};
+
+// The readiness-ordered queue: dispatch, GEMM1 and GEMM2 items, then the
+// fold when fold != nullptr.
+__device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t* smem, uint32_t lds0, int* s_info,
+                                            const FoldArgs* fold) {
   const int E = f.g1.E;
   int32_t* st = f.st;
   const int ND = f.fplan[0], NMB = f.fplan[1], L = f.fplan[2];
@@ -531,13 +546,35 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
   const int N1 = NMB * f.nt1, N2 = NMB * f.nt2;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int ld = 0, p1 = 0, p2 = 0;   // walk positions (claims only increase)
+  const int NF = fold ? (fold->N + 7) / 8 : 0;
+  bool passed = false;
 
   for (;;) {
     if (tid == 0) s_info[0] = atomicAdd(st + st_head(), 1);
     __syncthreads();
     const int item = s_info[0];
     __syncthreads();
-    if (item >= ND + N1 + N2) break;
+    if (item >= ND + N1 + N2) {
+      if (!fold) break;
+      if (!passed) {
+        passed = true;
+        release_fence();
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (item >= ND + N1 + N2 + NF) break;
+      // ---- fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] ----------------------
+      if (tid == 0) s_info[3] = wait_ge(f, fold->passed, (int)gridDim.x);
+      __syncthreads();
+      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
+      acquire_fence();
+      const int t = __builtin_amdgcn_readfirstlane((item - ND - N1 - N2) * 8 + wave);
+      if (t < fold->N)
+        perm::combine_token<true>(t, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K, fold->out, nullptr,
+                                  nullptr);
+      continue;
+    }
 
     if (item < ND) {
       // ---- dispatch chunk: gather token rows into X_d ------------------------
@@ -635,13 +672,20 @@ __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
   }
 }
 
+__global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ int s_info[4];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  fused_items(f, smem, lds0, s_info, nullptr);
+}
+
 // Fused planner: one workgroup.  Dispatch order = the GEMM planner's expert
 // order; fplan = {ND, NMB, L, order[E], dispatch prefix[E+1]}.  Zeroes the
 // queue state for this launch.
-__global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restrict__ offsets, int E, int max_mb,
-                                                          const int32_t* __restrict__ gplan,
-                                                          int32_t* __restrict__ fplan, int32_t* __restrict__ st) {
-  __shared__ int s_w[16], s_m[16];
+template <int THREADS>
+__device__ __forceinline__ void plan_fused_body(const int32_t* __restrict__ offsets, int E, int max_mb,
+                                                const int32_t* __restrict__ gplan, int32_t* __restrict__ fplan,
+                                                int32_t* __restrict__ st, int* s_w, int* s_m) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int L = gplan[1];
   int chunks = 0, mbs = 0;
@@ -661,7 +705,7 @@ __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restr
   __syncthreads();
   if (t == 0) {
     int r = 0, rm = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < THREADS / 64; ++w) {
       const int a = s_w[w], b = s_m[w];
       s_w[w] = r; s_m[w] = rm;
       r += a; rm += b;
@@ -676,7 +720,151 @@ __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restr
     fplan[3 + t] = gplan[2 + t];
     fplan[3 + E + t] = inc - chunks + s_w[wv];
   }
-  for (int i = t; i < 4 + 4 * E + max_mb; i += blockDim.x) st[i] = 0;
+  for (int i = t; i < 4 + 4 * E + max_mb; i += THREADS) st[i] = 0;
+}
+
+__global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restrict__ offsets, int E, int max_mb,
+                                                          const int32_t* __restrict__ gplan,
+                                                          int32_t* __restrict__ fplan, int32_t* __restrict__ st) {
+  __shared__ int s_w[16], s_m[16];
+  plan_fused_body<1024>(offsets, E, max_mb, gplan, fplan, st, s_w, s_m);
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch layer forward (KOSMOS section 3.3 and Figure 6: one launch
+// from route to fold; section 3.3.1 steps 1-5), on one GPU.  One persistent
+// workgroup per CU runs, in order:
+//   1. the router tiles (the same items and contraction split as the router
+//      launch, so the same partial sums), and marks every row unused;
+//   2. per chunk of 16 tokens: the logits (partials added in split order,
+//      then the bias), softmax and top-K, the in-chunk ranks and histogram;
+//   3. workgroup 0: the histogram scan (counts, offsets, chunk bases) and the
+//      GEMM and queue plans;
+//   4. the scatter of every route to its row;
+//   5. the readiness-ordered queue: dispatch chunks, GEMM1 tiles as experts
+//      become ready, GEMM2 tiles as their GEMM1 row blocks complete, then
+//      the fold, 8 tokens per item.
+// Steps 1-4 end at a grid barrier: a counter every workgroup adds to after an
+// agent-scope release, waited on (bounded) and acquired.  Every workgroup is
+// resident (one per CU), so each barrier is reached by all; a wait that
+// expires reports MOE_STATUS_WAIT_EXPIRED and the workgroup stops.  Each
+// step computes what its separate launch computes, so the outputs are
+// bitwise those of the staged launches.
+// ---------------------------------------------------------------------------
+
+struct SingleFwdParams {
+  FusedParams f;                // dispatch, GEMM1, GEMM2 (queue state and plans in the workspace)
+  FoldArgs fold;
+  router::RouterParams rp;      // out: partials [S][N][E] when S > 1, else the logits
+  int rbn, r_items;             // router column tile, router items
+  const float* bias;            // [E] or null
+  float* logits;                // [N][E]
+  const uint8_t* drop;          // [N][K] or null
+  int N, E, K, renorm, npl, nchunks, align;
+  int64_t rows_cap;
+  int32_t *topk_idx, *counts, *offsets, *dst_rows, *row_route;
+  float* topk_prob;
+  int32_t *hist, *rank;         // route workspace: histogram / chunk bases, in-chunk ranks
+  int32_t *gplan, *head;        // GEMM plan and queue heads
+  int max_mb;
+  int32_t* bar;                 // grid barrier counters [4] (zeroed before the launch)
+};
+
+// every workgroup: after its stores, add to *bar and wait until all have
+__device__ __forceinline__ bool grid_sync(const FusedParams& f, int32_t* bar, int* s_info) {
+  release_fence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, f.publish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_info[3] = wait_ge(f, bar, (int)gridDim.x);
+  }
+  __syncthreads();
+  const bool ok = s_info[3] != 0;
+  acquire_fence();
+  return ok;
+}
+
+template <int NPL>
+__device__ __forceinline__ void topk_single(const SingleFwdParams& p, int c, int* s_sel, int* s_hist) {
+  route::topk_chunk<NPL, 512>(c, p.logits, p.drop, p.N, p.E, p.K, p.renorm, p.topk_idx, p.topk_prob, p.hist,
+                              p.rank, 0, 0, nullptr, p.f.status, s_sel, s_hist, nullptr);
+}
+
+__global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ int s_info[4];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const FusedParams& f = p.f;
+  const int tid = threadIdx.x;
+  const int64_t gthreads = (int64_t)gridDim.x * 512;
+
+  // ---- 1. router tiles; every row unused until the scatter --------------------
+  for (int64_t i = (int64_t)blockIdx.x * 512 + tid; i < p.rows_cap; i += gthreads) p.row_route[i] = -1;
+  for (int it = blockIdx.x; it < p.r_items; it += gridDim.x) {
+    if (p.rbn == 64) router::router_tile_item<128, 64>(p.rp, it, smem, lds0);
+    else if (p.rbn == 128) router::router_tile_item<128, 128>(p.rp, it, smem, lds0);
+    else router::router_tile_item<128, 256>(p.rp, it, smem, lds0);
+  }
+  if (!grid_sync(f, p.bar + 0, s_info)) return;
+
+  // ---- 2. logits and top-K, a chunk of 16 tokens at a time ---------------------
+  int* s_sel = reinterpret_cast<int*>(smem);
+  int* s_hist = s_sel + route::kChunk * 32;
+  const int S = p.rp.S;
+  for (int c = blockIdx.x; c < p.nchunks; c += gridDim.x) {
+    __syncthreads();   // the previous chunk is done with the LDS
+    if (S > 1) {
+      // the router's reduce, element by element: partials in split order, then the bias
+      const int t0 = c * route::kChunk;
+      const int nt = min(route::kChunk, p.N - t0);
+      const int64_t NE = (int64_t)p.N * p.E;
+      for (int i = tid; i < nt * p.E; i += 512) {
+        const int64_t o = (int64_t)t0 * p.E + i;
+        float v = p.rp.out[o];
+        for (int k = 1; k < S; ++k) v += p.rp.out[(int64_t)k * NE + o];
+        if (p.bias) v += p.bias[i % p.E];
+        p.logits[o] = v;
+      }
+      __syncthreads();   // the chunk's logits are visible to every wave of the workgroup
+    }
+    if (p.npl == 1) topk_single<1>(p, c, s_sel, s_hist);
+    else if (p.npl == 2) topk_single<2>(p, c, s_sel, s_hist);
+    else if (p.npl == 4) topk_single<4>(p, c, s_sel, s_hist);
+    else topk_single<8>(p, c, s_sel, s_hist);
+  }
+  if (!grid_sync(f, p.bar + 1, s_info)) return;
+
+  // ---- 3. scan and plans, workgroup 0 ------------------------------------------
+  if (blockIdx.x == 0) {
+    int* w = reinterpret_cast<int*>(smem);
+    int *s_part = w, *s_tot = w + 512, *s_off = w + 1024, *s_wsum = w + 1600;
+    route::scan_hist<512>(p.hist, p.nchunks, p.E, p.align, p.counts, p.offsets, p.N, 0, s_part, s_tot, s_off,
+                          s_wsum);
+    __syncthreads();   // offsets written by this workgroup, read below
+    int *s_w0 = w + 2048, *s_w1 = w + 2064, *s_tot2 = w + 2080, *s_pref = w + 2096;
+    float* s_key = reinterpret_cast<float*>(w + 2560);
+    int *s_items = w + 3072, *s_ids = w + 3584;
+    sched::plan_rows_body<512>(p.offsets, p.E, f.nt1, p.gplan, p.head, s_w0, s_w1, s_tot2, s_key, s_items, s_ids,
+                               s_pref);
+    __syncthreads();   // the GEMM plan, read by the queue plan
+    plan_fused_body<512>(p.offsets, p.E, p.max_mb, p.gplan, const_cast<int32_t*>(f.fplan), f.st, w + 4096,
+                         w + 4112);
+  }
+  if (!grid_sync(f, p.bar + 2, s_info)) return;
+
+  // ---- 4. scatter ---------------------------------------------------------------
+  const int64_t NK = (int64_t)p.N * p.K;
+  for (int64_t r = (int64_t)blockIdx.x * 512 + tid; r < NK; r += gthreads)
+    route::scatter_route(r, p.topk_idx, p.drop, p.hist, p.rank, p.K, p.E, p.dst_rows, p.row_route);
+  if (!grid_sync(f, p.bar + 3, s_info)) return;
+
+  // ---- 5. dispatch, GEMM1, GEMM2 by readiness, then the fold ------------------
+  fused_items(f, smem, lds0, s_info, &p.fold);
+}
+
+__global__ void single_reset_kernel(int32_t* bar, int n, int32_t* status) {
+  if ((int)threadIdx.x < n) bar[threadIdx.x] = 0;
+  if (threadIdx.x == 0 && status) *status = 0;
 }
 
 }  // namespace
@@ -742,8 +930,11 @@ size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E) {
   return (size_t)(kGemmHeadInts + gemm_fwd_plan_ints(E) + (3 + 2 * E + 8) + (4 + 4 * E + max_mb) + 64);
 }
 
-hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s) {
-  FusedParams f{};
+namespace {
+// the fused queue's parameters and the places of its plans in the workspace
+void fused_params(const ExpertsFwd& x, int32_t* ws, FusedParams& f, int32_t** gplan_out, int* max_mb_out,
+                  int32_t** bar_out) {
+  f = FusedParams{};
   FwdParams& g1 = f.g1;
   g1.offsets = x.offsets;
   g1.E = (int)x.E;
@@ -774,21 +965,92 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   int32_t* fplan = gplan + gemm_fwd_plan_ints(x.E);
   int32_t* st = fplan + (3 + 2 * x.E + 8);
   st = (int32_t*)(((uintptr_t)st + 7) & ~(uintptr_t)7);   // 8-byte aligned ticket
+  const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
   f.st = st;
   f.fplan = fplan;
   f.status = x.status;
   f.polls = x.test_polls > 0 ? x.test_polls : kSpinLimit;
   f.publish = x.test_polls > 0 ? 0 : 1;
-  const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
-  plan_rows_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
-  plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, fplan, st);
+  *gplan_out = gplan;
+  *max_mb_out = max_mb;
+  // the single launch's barrier words: after the queue state, in the
+  // workspace's slack (experts_fused_ws_ints)
+  int32_t* bar = st + 4 + 4 * x.E + max_mb;
+  *bar_out = (int32_t*)(((uintptr_t)bar + 31) & ~(uintptr_t)31);
+}
+
+hipError_t resident_grid(const void* kern, int* grid) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, experts_fwd_fused_kernel, 512, 0);
-  if (err != hipSuccess) return err;
+  if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 512, 0);
   if (per_cu < 1) per_cu = 1;
-  experts_fwd_fused_kernel<<<cus * per_cu, 512, 0, s>>>(f);
+  *grid = cus * per_cu;
+  return err;
+}
+}  // namespace
+
+hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s) {
+  FusedParams f;
+  int32_t* gplan = nullptr;
+  int32_t* bar = nullptr;
+  int max_mb = 0;
+  fused_params(x, ws, f, &gplan, &max_mb, &bar);
+  plan_rows_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
+  plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, const_cast<int32_t*>(f.fplan), f.st);
+  int grid = 0;
+  hipError_t err = resident_grid((const void*)experts_fwd_fused_kernel, &grid);
+  if (err != hipSuccess) return err;
+  experts_fwd_fused_kernel<<<grid, 512, 0, s>>>(f);
+  return hipGetLastError();
+}
+
+bool layer_fwd_single_ok(int64_t D, int64_t E, int64_t K) {
+  return router::router_tiled(D, E) && E <= 512 && K <= 32;
+}
+
+hipError_t launch_layer_fwd_single(const LayerFwdSingle& a, int32_t* ws, void* route_ws, void* router_ws,
+                                   hipStream_t s) {
+  const ExpertsFwd& x = a.x;
+  if (!layer_fwd_single_ok(x.D, x.E, x.K)) return hipErrorInvalidValue;
+  SingleFwdParams p{};
+  int32_t* bar = nullptr;
+  fused_params(x, ws, p.f, &p.gplan, &p.max_mb, &bar);
+  p.head = ws;
+  p.bar = bar;
+  const router::RouterPlan r = router::router_plan(x.N_tokens, x.D, x.E);
+  p.rp = router::RouterParams{(const uint16_t*)a.x_tokens, (const uint16_t*)a.w_r, a.bias,
+                              r.S > 1 ? (float*)router_ws : a.logits, (int)x.N_tokens, (int)x.D, (int)x.E, r.S,
+                              (int)((x.N_tokens + 127) / 128), r.ntiles};
+  p.rbn = r.bn;
+  p.r_items = (int)(((x.N_tokens + 127) / 128) * r.ntiles * r.S);
+  p.bias = a.bias;
+  p.logits = a.logits;
+  p.drop = a.drop;
+  p.N = (int)x.N_tokens;
+  p.E = (int)x.E;
+  p.K = (int)x.K;
+  p.renorm = a.renorm;
+  int npl = 1;
+  while (npl * kWave < x.E) npl <<= 1;
+  p.npl = npl;
+  p.nchunks = (int)((x.N_tokens + route::kChunk - 1) / route::kChunk);
+  p.align = 1;
+  p.rows_cap = x.rows_cap;
+  p.topk_idx = a.topk_idx;
+  p.topk_prob = a.topk_prob;
+  p.counts = a.counts;
+  p.offsets = const_cast<int32_t*>(x.offsets);
+  p.dst_rows = a.dst_rows;
+  p.row_route = const_cast<int32_t*>(x.row_route);
+  p.hist = (int32_t*)route_ws;
+  p.rank = (int32_t*)((char*)route_ws + route::hist_bytes(x.N_tokens, x.E));
+  p.fold = FoldArgs{a.dst_rows, a.topk_prob, (int)x.N_tokens, (uint16_t*)a.out, bar + 4};
+  int grid = 0;
+  hipError_t err = resident_grid((const void*)layer_fwd_single_kernel, &grid);
+  if (err != hipSuccess) return err;
+  single_reset_kernel<<<1, 64, 0, s>>>(bar, 5, x.status);
+  layer_fwd_single_kernel<<<grid, 512, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -141,6 +141,7 @@ hipError_t launch_gemm_wgrad_bf16(const GemmBwd& b, const void* dc, void* db, hi
 // persistent launch (gemm_fwd.hip)
 struct ExpertsFwd {
   int64_t E, K, D, H, rows_cap;
+  int64_t N_tokens;                  // tokens (the single-launch layer)
   const int32_t* offsets;
   const int32_t* row_route;
   const void* x;
@@ -161,6 +162,29 @@ struct ExpertsFwd {
 // (k_dim % 64 == 0, n_dim % 16 == 0 for both of its GEMMs)
 size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E);
 hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_t s);
+
+// single-launch layer forward (gemm_fwd.hip): router, route, dispatch, GEMM1,
+// GEMM2 and the fold in one persistent launch (after a one-workgroup reset
+// of its barrier words); bf16 routed experts, the fused queue's shape rules,
+// plus layer_fwd_single_ok.  ws: the GEMM table workspace; route_ws and
+// router_ws: the route and router workspaces of the staged launches.
+struct LayerFwdSingle {
+  ExpertsFwd x;                      // x.x: the token rows; offsets / row_route: the route outputs
+  const void* x_tokens;              // [N][D] (the same as x.x)
+  const void* w_r;                   // [E][D]
+  const float* bias;                 // [E] or null
+  float* logits;                     // [N][E]
+  const uint8_t* drop;               // [N][K] or null
+  int renorm;
+  int32_t* topk_idx;
+  float* topk_prob;
+  int32_t* counts;
+  int32_t* dst_rows;
+  void* out;                         // [N][D]
+};
+bool layer_fwd_single_ok(int64_t D, int64_t E, int64_t K);
+hipError_t launch_layer_fwd_single(const LayerFwdSingle& a, int32_t* ws, void* route_ws, void* router_ws,
+                                   hipStream_t s);
 size_t gemm_fwd_plan_ints(int64_t E);
 // The persistent GEMMs' workspace starts with the per-XCD queue heads, each
 // on its own 128-byte line (claims on one head serialize at the memory side;

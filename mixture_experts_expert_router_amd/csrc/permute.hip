@@ -9,19 +9,13 @@
 // K rows of a token and folds them in fp32 in ascending k with fmaf.
 #include "common.h"
 #include "launch.h"
+#include "permute_dev.h"
 
 namespace moe {
 
 constexpr int kVPL = 8;   // 16-byte vectors per lane per pass
 
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
-  uint4 o;
-  o.x = pack_bf16x2(w * bf16lo(v.x), w * bf16hi(v.x));
-  o.y = pack_bf16x2(w * bf16lo(v.y), w * bf16hi(v.y));
-  o.z = pack_bf16x2(w * bf16lo(v.z), w * bf16hi(v.z));
-  o.w = pack_bf16x2(w * bf16lo(v.w), w * bf16hi(v.w));
-  return o;
-}
+using perm::scale_bf16x8;
 
 // Destination row of route k of token t (wave-uniform t and k, so a scalar
 // load): routes 0..K-1 from dst_rows, route K the shared expert's row srow.
@@ -154,9 +148,7 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
 // Same result for D % 128 == 0: each lane quantizes 16 adjacent elements (a
 // 32-block is a lane pair), so a route gets one 16-byte data store per lane
 // and lanes 8i pack the codes of four consecutive blocks into one 4-byte store.
-__device__ __forceinline__ uint32_t quant4(const float* f, int e) {
-  return e4m3x4(f[0], f[1], f[2], f[3], e);
-}
+using perm::quant4;
 
 __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ dst_rows,
@@ -256,10 +248,7 @@ __global__ __launch_bounds__(kPadThreads) void zero_padding_kernel(const int32_t
   }
 }
 
-// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), fp32 fmaf in ascending k.
-// The rows of up to 8 routes are loaded before any of them is added, so a
-// lane keeps 16 loads in flight instead of waiting on one route at a time.
-// The gathered rows and the output are touched once: non-temporal accesses.
+// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), a wave per token
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ dst_rows,
@@ -267,80 +256,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       int D, int K, uint16_t* __restrict__ out,
                                                       const uint16_t* __restrict__ addend,
                                                       const int32_t* __restrict__ shared_row0) {
-  constexpr int VPL = 2, KCH = 8;
-  const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  const int nvec = D >> 3;
-  // route K (when there is a shared expert): its row of this token, weight 1
-  const int KK = K + (shared_row0 ? 1 : 0);
-  const int srow = shared_row0 ? *shared_row0 + t : -1;
-  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-    float acc[VPL][8];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + lane + j * kWave;
-      const uint4 q = (addend && v < nvec) ? ldg16(addend + (int64_t)t * D + v * 8) : make_uint4(0, 0, 0, 0);
-      acc[j][0] = bf16lo(q.x);
-      acc[j][1] = bf16hi(q.x);
-      acc[j][2] = bf16lo(q.y);
-      acc[j][3] = bf16hi(q.y);
-      acc[j][4] = bf16lo(q.z);
-      acc[j][5] = bf16hi(q.z);
-      acc[j][6] = bf16lo(q.w);
-      acc[j][7] = bf16hi(q.w);
-    }
-    for (int kb = 0; kb < KK; kb += KCH) {
-      uint4 r[KCH][VPL];
-      int dk[KCH];
-      float wk[KCH];
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const int k = kb + kk;
-        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
-        wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
-        const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int v = v0 + lane + j * kWave;
-          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16_nt(src + v * 8) : make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        if (dk[kk] < 0) continue;
-        const float w = wk[kk];
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const uint4 q = r[kk][j];
-          acc[j][0] = fmaf(w, bf16lo(q.x), acc[j][0]);
-          acc[j][1] = fmaf(w, bf16hi(q.x), acc[j][1]);
-          acc[j][2] = fmaf(w, bf16lo(q.y), acc[j][2]);
-          acc[j][3] = fmaf(w, bf16hi(q.y), acc[j][3]);
-          acc[j][4] = fmaf(w, bf16lo(q.z), acc[j][4]);
-          acc[j][5] = fmaf(w, bf16hi(q.z), acc[j][5]);
-          acc[j][6] = fmaf(w, bf16lo(q.w), acc[j][6]);
-          acc[j][7] = fmaf(w, bf16hi(q.w), acc[j][7]);
-        }
-      }
-    }
-    uint16_t* o = out + (int64_t)t * D;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + lane + j * kWave;
-      if (v < nvec)
-        stg16_nt(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
-                                       pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
-    }
-  }
+  perm::combine_token<WEIGHTED>(t, y, dst_rows, weight, D, K, out, addend, shared_row0);
 }
 
-// combine backward: dyd[dst] = bf16(w * dout[t]); dprob[t,k] = <dout[t], y[dst]>
-// QUANT (D % 128 == 0): each dY_d row is also quantized row-wise to MXFP8
-// where it lands (KOSMOS section 3.3.2 step 1), the same codes a separate
-// quantize_rows pass over dyd gives: a lane holds 8 elements, so a 32-block
-// is a lane quad; 8-byte code stores, and lanes 16i store the scales of four
-// consecutive blocks as one word.
+// combine backward, a wave per token (QUANT: dY_d also quantized row-wise)
 template <bool QUANT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __restrict__ dout,
                                                           const int32_t* __restrict__ dst_rows,
@@ -350,102 +271,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* __rest
                                                           float* __restrict__ dprob,
                                                           const int32_t* __restrict__ shared_row0,
                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  // routes in chunks of KCH: every Y row of the chunk is loaded before any
-  // product uses it, so the gathers overlap instead of waiting one by one;
-  // each lane still sums its vectors in increasing order
-  constexpr int VPL = 2, KCH = 8;
-  const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  const int nvec = D >> 3;
-  const uint16_t* src = dout + (int64_t)t * D;
-  // route K (when there is a shared expert): dY of its row is dOut, weight 1,
-  // and it has no route weight to differentiate
-  const int KK = K + (shared_row0 ? 1 : 0);
-  const int srow = shared_row0 ? *shared_row0 + t : -1;
-  for (int kb = 0; kb < KK; kb += KCH) {
-    int dk[KCH];
-    float wk[KCH], dot[KCH];
-#pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) {
-      const int k = kb + kk;
-      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
-      wk[kk] = k < K ? weight[(int64_t)t * K + k] : 1.0f;
-      dot[kk] = 0.0f;
-    }
-    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-      uint4 r[VPL];
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const int v = v0 + lane + j * kWave;
-        r[j] = v < nvec ? ldg16(src + v * 8) : make_uint4(0, 0, 0, 0);
-      }
-      uint4 yy[KCH][VPL];
-      if (dprob) {
-#pragma unroll
-        for (int kk = 0; kk < KCH; ++kk)
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) {
-            const int v = v0 + lane + j * kWave;
-            yy[kk][j] = (dk[kk] >= 0 && kb + kk < K && v < nvec) ? ldg16_nt(y + (int64_t)dk[kk] * D + v * 8)
-                                                                  : make_uint4(0, 0, 0, 0);
-          }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        if (dk[kk] < 0) continue;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int v = v0 + lane + j * kWave;
-          const uint4 o = scale_bf16x8(r[j], wk[kk]);
-          if constexpr (QUANT) {
-            // every lane takes part in the shuffles; a quad is all in or all
-            // out (nvec % 16 == 0), and lanes past the row hold zeros
-            const float f[8] = {bf16lo(o.x), bf16hi(o.x), bf16lo(o.y), bf16hi(o.y),
-                                bf16lo(o.z), bf16hi(o.z), bf16lo(o.w), bf16hi(o.w)};
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-            const int code = e8m0_code(amax);
-            const int e = code - 127;
-            const uint2 qv = make_uint2(quant4(f, e), quant4(f + 4, e));
-            const uint32_t c1 = (uint32_t)__shfl_down(code, 4, 64), c2 = (uint32_t)__shfl_down(code, 8, 64),
-                           c3 = (uint32_t)__shfl_down(code, 12, 64);
-            if (v < nvec) {
-              *reinterpret_cast<uint2*>(q + (int64_t)dk[kk] * D + v * 8) = qv;
-              if ((lane & 15) == 0)
-                *reinterpret_cast<uint32_t*>(sc + (int64_t)dk[kk] * (D >> 5) + (v >> 2)) =
-                    (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
-            }
-          }
-          if (v >= nvec) continue;
-          stg16(dyd + (int64_t)dk[kk] * D + v * 8, o);
-          if (dprob) {
-            const uint4 q = yy[kk][j];
-            float s2 = dot[kk];
-            s2 = fmaf(bf16lo(r[j].x), bf16lo(q.x), s2);
-            s2 = fmaf(bf16hi(r[j].x), bf16hi(q.x), s2);
-            s2 = fmaf(bf16lo(r[j].y), bf16lo(q.y), s2);
-            s2 = fmaf(bf16hi(r[j].y), bf16hi(q.y), s2);
-            s2 = fmaf(bf16lo(r[j].z), bf16lo(q.z), s2);
-            s2 = fmaf(bf16hi(r[j].z), bf16hi(q.z), s2);
-            s2 = fmaf(bf16lo(r[j].w), bf16lo(q.w), s2);
-            s2 = fmaf(bf16hi(r[j].w), bf16hi(q.w), s2);
-            dot[kk] = s2;
-          }
-        }
-      }
-    }
-    if (dprob) {
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const float sum = wave_sum(dot[kk]);
-        if (lane == 0 && kb + kk < K) dprob[(int64_t)t * K + kb + kk] = dk[kk] >= 0 ? sum : 0.0f;
-      }
-    }
-  }
+  perm::combine_bwd_token<QUANT>(t, dout, dst_rows, weight, y, D, K, dyd, dprob, shared_row0, q, sc);
 }
 
 // row-wise MXFP8 quantization of bf16 [rows][cols]; one wave per row.  Rows

@@ -1,0 +1,214 @@
+// Device bodies of the token-row permutes that the single-launch layer runs
+// inside its persistent workgroups as well: the fold (combine) and the
+// combine backward of one token by one wave, and their vector helpers.
+// permute.hip launches them a wave per token.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace perm {
+
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
+  uint4 o;
+  o.x = pack_bf16x2(w * bf16lo(v.x), w * bf16hi(v.x));
+  o.y = pack_bf16x2(w * bf16lo(v.y), w * bf16hi(v.y));
+  o.z = pack_bf16x2(w * bf16lo(v.z), w * bf16hi(v.z));
+  o.w = pack_bf16x2(w * bf16lo(v.w), w * bf16hi(v.w));
+  return o;
+}
+
+__device__ __forceinline__ uint32_t quant4(const float* f, int e) {
+  return e4m3x4(f[0], f[1], f[2], f[3], e);
+}
+
+// The fold of token t (wave-uniform) by one wave: out[t] = bf16(sum over k of
+// w[t,k] y[dst[t,k]] (+ addend[t])), fp32 fmaf in ascending k.  The rows of
+// up to 8 routes are loaded before any of them is added, so a lane keeps 16
+// loads in flight instead of waiting on one route at a time.  The gathered
+// rows and the output are touched once: non-temporal accesses.
+template <bool WEIGHTED>
+__device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict__ y,
+                                              const int32_t* __restrict__ dst_rows,
+                                              const float* __restrict__ weight, int D, int K,
+                                              uint16_t* __restrict__ out, const uint16_t* __restrict__ addend,
+                                              const int32_t* __restrict__ shared_row0) {
+  constexpr int VPL = 2, KCH = 8;
+  const int lane = threadIdx.x & 63;
+  const int nvec = D >> 3;
+  // route K (when there is a shared expert): its row of this token, weight 1
+  const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+    float acc[VPL][8];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      const uint4 q = (addend && v < nvec) ? ldg16(addend + (int64_t)t * D + v * 8) : make_uint4(0, 0, 0, 0);
+      acc[j][0] = bf16lo(q.x);
+      acc[j][1] = bf16hi(q.x);
+      acc[j][2] = bf16lo(q.y);
+      acc[j][3] = bf16hi(q.y);
+      acc[j][4] = bf16lo(q.z);
+      acc[j][5] = bf16hi(q.z);
+      acc[j][6] = bf16lo(q.w);
+      acc[j][7] = bf16hi(q.w);
+    }
+    for (int kb = 0; kb < KK; kb += KCH) {
+      uint4 r[KCH][VPL];
+      int dk[KCH];
+      float wk[KCH];
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const int k = kb + kk;
+        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
+        wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
+        const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + lane + j * kWave;
+          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16_nt(src + v * 8) : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        if (dk[kk] < 0) continue;
+        const float w = wk[kk];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const uint4 q = r[kk][j];
+          acc[j][0] = fmaf(w, bf16lo(q.x), acc[j][0]);
+          acc[j][1] = fmaf(w, bf16hi(q.x), acc[j][1]);
+          acc[j][2] = fmaf(w, bf16lo(q.y), acc[j][2]);
+          acc[j][3] = fmaf(w, bf16hi(q.y), acc[j][3]);
+          acc[j][4] = fmaf(w, bf16lo(q.z), acc[j][4]);
+          acc[j][5] = fmaf(w, bf16hi(q.z), acc[j][5]);
+          acc[j][6] = fmaf(w, bf16lo(q.w), acc[j][6]);
+          acc[j][7] = fmaf(w, bf16hi(q.w), acc[j][7]);
+        }
+      }
+    }
+    uint16_t* o = out + (int64_t)t * D;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + lane + j * kWave;
+      if (v < nvec)
+        stg16_nt(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
+                                       pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
+    }
+  }
+}
+
+// combine backward: dyd[dst] = bf16(w * dout[t]); dprob[t,k] = <dout[t], y[dst]>
+// The combine backward of token t (wave-uniform) by one wave: dY_d rows of
+// its valid routes and dprob.  QUANT (D % 128 == 0): each dY_d row is also quantized row-wise to MXFP8
+// where it lands (KOSMOS section 3.3.2 step 1), the same codes a separate
+// quantize_rows pass over dyd gives: a lane holds 8 elements, so a 32-block
+// is a lane quad; 8-byte code stores, and lanes 16i store the scales of four
+// consecutive blocks as one word.
+template <bool QUANT>
+__device__ __forceinline__ void combine_bwd_token(int t, const uint16_t* __restrict__ dout,
+                                                  const int32_t* __restrict__ dst_rows,
+                                                  const float* __restrict__ weight,
+                                                  const uint16_t* __restrict__ y, int D, int K,
+                                                  uint16_t* __restrict__ dyd, float* __restrict__ dprob,
+                                                  const int32_t* __restrict__ shared_row0,
+                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  // routes in chunks of KCH: every Y row of the chunk is loaded before any
+  // product uses it, so the gathers overlap instead of waiting one by one;
+  // each lane still sums its vectors in increasing order
+  constexpr int VPL = 2, KCH = 8;
+  const int lane = threadIdx.x & 63;
+  const int nvec = D >> 3;
+  const uint16_t* src = dout + (int64_t)t * D;
+  // route K (when there is a shared expert): dY of its row is dOut, weight 1,
+  // and it has no route weight to differentiate
+  const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
+  for (int kb = 0; kb < KK; kb += KCH) {
+    int dk[KCH];
+    float wk[KCH], dot[KCH];
+#pragma unroll
+    for (int kk = 0; kk < KCH; ++kk) {
+      const int k = kb + kk;
+      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
+      wk[kk] = k < K ? weight[(int64_t)t * K + k] : 1.0f;
+      dot[kk] = 0.0f;
+    }
+    for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
+      uint4 r[VPL];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + lane + j * kWave;
+        r[j] = v < nvec ? ldg16(src + v * 8) : make_uint4(0, 0, 0, 0);
+      }
+      uint4 yy[KCH][VPL];
+      if (dprob) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk)
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + lane + j * kWave;
+            yy[kk][j] = (dk[kk] >= 0 && kb + kk < K && v < nvec) ? ldg16_nt(y + (int64_t)dk[kk] * D + v * 8)
+                                                                  : make_uint4(0, 0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        if (dk[kk] < 0) continue;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + lane + j * kWave;
+          const uint4 o = scale_bf16x8(r[j], wk[kk]);
+          if constexpr (QUANT) {
+            // every lane takes part in the shuffles; a quad is all in or all
+            // out (nvec % 16 == 0), and lanes past the row hold zeros
+            const float f[8] = {bf16lo(o.x), bf16hi(o.x), bf16lo(o.y), bf16hi(o.y),
+                                bf16lo(o.z), bf16hi(o.z), bf16lo(o.w), bf16hi(o.w)};
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const int code = e8m0_code(amax);
+            const int e = code - 127;
+            const uint2 qv = make_uint2(quant4(f, e), quant4(f + 4, e));
+            const uint32_t c1 = (uint32_t)__shfl_down(code, 4, 64), c2 = (uint32_t)__shfl_down(code, 8, 64),
+                           c3 = (uint32_t)__shfl_down(code, 12, 64);
+            if (v < nvec) {
+              *reinterpret_cast<uint2*>(q + (int64_t)dk[kk] * D + v * 8) = qv;
+              if ((lane & 15) == 0)
+                *reinterpret_cast<uint32_t*>(sc + (int64_t)dk[kk] * (D >> 5) + (v >> 2)) =
+                    (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+            }
+          }
+          if (v >= nvec) continue;
+          stg16(dyd + (int64_t)dk[kk] * D + v * 8, o);
+          if (dprob) {
+            const uint4 q = yy[kk][j];
+            float s2 = dot[kk];
+            s2 = fmaf(bf16lo(r[j].x), bf16lo(q.x), s2);
+            s2 = fmaf(bf16hi(r[j].x), bf16hi(q.x), s2);
+            s2 = fmaf(bf16lo(r[j].y), bf16lo(q.y), s2);
+            s2 = fmaf(bf16hi(r[j].y), bf16hi(q.y), s2);
+            s2 = fmaf(bf16lo(r[j].z), bf16lo(q.z), s2);
+            s2 = fmaf(bf16hi(r[j].z), bf16hi(q.z), s2);
+            s2 = fmaf(bf16lo(r[j].w), bf16lo(q.w), s2);
+            s2 = fmaf(bf16hi(r[j].w), bf16hi(q.w), s2);
+            dot[kk] = s2;
+          }
+        }
+      }
+    }
+    if (dprob) {
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const float sum = wave_sum(dot[kk]);
+        if (lane == 0 && kb + kk < K) dprob[(int64_t)t * K + kb + kk] = dk[kk] >= 0 ? sum : 0.0f;
+      }
+    }
+  }
+}
+
+}  // namespace perm
+}  // namespace moe

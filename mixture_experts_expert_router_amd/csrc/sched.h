@@ -143,11 +143,14 @@ __device__ __forceinline__ Item claim_rows(const int32_t* plan, const int32_t* o
 // gets ceil(rows / BM) * n_tiles items, BM by its tile class.  The experts of
 // each class keep ascending id; the two classes are merged by the midpoint of
 // each expert's items within its class, so both progress at the same rate.
-__global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restrict__ offsets, int E, int n_tiles,
-                                                        int32_t* __restrict__ plan, int32_t* __restrict__ head) {
-  __shared__ int s_w0[16], s_w1[16], s_tot[2];
-  __shared__ float s_key[1024];
-  __shared__ int s_items[1024], s_ids[1024], s_pref[16];
+// The planner's body for a workgroup of THREADS threads (E <= THREADS).
+// LDS: s_w0, s_w1, s_pref [THREADS / 64] and s_tot [2] ints, s_key [THREADS]
+// floats, s_items, s_ids [THREADS] ints.
+template <int THREADS>
+__device__ __forceinline__ void plan_rows_body(const int32_t* __restrict__ offsets, int E, int n_tiles,
+                                               int32_t* __restrict__ plan, int32_t* __restrict__ head, int* s_w0,
+                                               int* s_w1, int* s_tot, float* s_key, int* s_items, int* s_ids,
+                                               int* s_pref) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   int items = 0, big = 0;
   if (t < E) {
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restri
   __syncthreads();
   if (t == 0) {
     int r0 = 0, r1 = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < THREADS / 64; ++w) {
       const int a = s_w0[w], b = s_w1[w];
       s_w0[w] = r0; s_w1[w] = r1;
       r0 += a; r1 += b;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restri
   __syncthreads();
   if (t == 0) {
     int r = 0;
-    for (int w = 0; w < 16; ++w) { const int a = s_pref[w]; s_pref[w] = r; r += a; }
+    for (int w = 0; w < THREADS / 64; ++w) { const int a = s_pref[w]; s_pref[w] = r; r += a; }
     plan[0] = r;
     plan[1] = L;
     plan[2 + E + L] = r;
@@ -212,6 +215,14 @@ __global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restri
     plan[2 + t] = s_ids[t];
     plan[2 + E + t] = inc - v + s_pref[wv];
   }
+}
+
+__global__ __launch_bounds__(1024) void plan_rows_kernel(const int32_t* __restrict__ offsets, int E, int n_tiles,
+                                                        int32_t* __restrict__ plan, int32_t* __restrict__ head) {
+  __shared__ int s_w0[16], s_w1[16], s_tot[2];
+  __shared__ float s_key[1024];
+  __shared__ int s_items[1024], s_ids[1024], s_pref[16];
+  plan_rows_body<1024>(offsets, E, n_tiles, plan, head, s_w0, s_w1, s_tot, s_key, s_items, s_ids, s_pref);
 }
 
 }  // namespace

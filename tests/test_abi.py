@@ -87,7 +87,7 @@ def test_null_align_workspace_errors():
     a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0)
     sv = M.LayerSaved()
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -1
-    a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0, 2)             # unknown schedule
+    a = M.LayerArgs(M.dims(16, 64, 8, 2, 64), 0, 3)             # unknown schedule
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 16, 16, 1 << 20, None) == -3
     # column-wise quantization: rows % 32, cols % 8, ld % 32, col0 % 32, col0 + rows <= ld
     qc = lib.moe_quantize_mxfp8_cols
@@ -183,6 +183,25 @@ def test_ready_schedule_is_refused_where_it_does_not_run():
     a.ready_test_polls = -1
     sv = _full_saved(lib, d, M.MOE_BF16)
     assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 1 << 20, 1 << 20, 1 << 40, None) == -2
+
+
+def test_single_schedule_is_refused_where_it_does_not_run():
+    """MOE_SCHED_SINGLE has the READY rules plus the tiled router (16 <= E <=
+    512), the plain top-K and no aux loss; anything else gets
+    MOE_ERR_UNSUPPORTED before any launch (fake aligned pointers)."""
+    lib = M.load()
+    cases = [(M.dims(64, 256, 32, 2, 128, align=32), M.MOE_MXFP8, 0.0),
+             (M.dims(64, 256, 32, 2, 128, n_shared=1), M.MOE_BF16, 0.0),
+             (M.dims(64, 256, 8, 2, 128), M.MOE_BF16, 0.0),              # E < 16: the router's direct kernel
+             (M.dims(64, 256, 520, 2, 128), M.MOE_BF16, 0.0),            # E > 512
+             (M.dims(64, 256, 32, 2, 128, n_group=4, topk_group=2), M.MOE_BF16, 0.0),
+             (M.dims(64, 256, 32, 2, 128), M.MOE_BF16, 0.01),            # aux loss
+             (M.dims(64, 264, 32, 2, 128), M.MOE_BF16, 0.0)]
+    for d, dt, alpha in cases:
+        a = M.LayerArgs(d, dt, M.MOE_SCHED_SINGLE, *([1 << 20] * 15))
+        a.aux_alpha = alpha
+        sv = _full_saved(lib, d, dt)
+        assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 1 << 20, 1 << 20, 1 << 40, None) == -6, (d.E, d.D, dt)
 
 
 def test_saved_size_and_carve():

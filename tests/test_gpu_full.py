@@ -171,6 +171,22 @@ def test_full_size_forward_bf16(name):
     assert np.array_equal(bits(layer.out), staged["out"])
     assert np.array_equal(bits(sv["h"])[:n], staged["h"][:n])
     assert np.array_equal(bits(sv["y"])[:n], staged["y"][:n])
+    # and the single launch from the router to the fold (experts >= 16: the
+    # tiled router), every saved tensor poisoned first
+    if wl.E >= 16:
+        want = {k: host(sv[k].view(torch.uint8)).copy() for k in ("logits", "topk_idx", "topk_prob", "counts",
+                                                                   "offsets", "dst_rows", "row_route")}
+        for t in list(sv.values()) + [layer.out]:
+            t.view(torch.uint8).fill_(0xA5)
+        layer.sched = M.MOE_SCHED_SINGLE
+        layer.forward(x)
+        torch.cuda.synchronize()
+        assert int(host(sv["status"])[0]) == 0
+        for k, v in want.items():
+            assert np.array_equal(host(sv[k].view(torch.uint8)), v), k
+        assert np.array_equal(bits(layer.out), staged["out"])
+        assert np.array_equal(bits(sv["h"])[:n], staged["h"][:n])
+        assert np.array_equal(bits(sv["y"])[:n], staged["y"][:n])
 
 
 def test_full_size_forward_mxfp8():

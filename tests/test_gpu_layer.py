@@ -109,6 +109,78 @@ def test_layer_fwd_bf16(name, sched):
     assert_bf16_close(vals(out)[same], ref["out"][same], "out")
 
 
+SINGLE_CASES = {
+    "dsv3_shape_small": LAYER_CASES["dsv3_shape_small"],
+    "qwen3_shape_small": LAYER_CASES["qwen3_shape_small"],
+    # ragged: tokens not a multiple of a route chunk (16) or router block, few experts empty
+    "ragged_e24": S.scaled(S.WORKLOADS["dsv3_bf16"], "ragged_e24", N=333, D=192, E=24, K=3, H=320),
+    # 2048+ tokens: the staged router takes 128-row blocks (and another split)
+    "router_bm128": S.scaled(S.WORKLOADS["qwen3_235b_bf16_fwdbwd"], "router_bm128", N=2100, D=128, E=64, K=6,
+                             H=192),
+}
+SINGLE_KEYS = ("logits", "topk_idx", "topk_prob", "counts", "offsets", "dst_rows", "row_route", "xd", "g", "u",
+               "h", "y")
+
+
+@pytest.mark.parametrize("name", list(SINGLE_CASES))
+def test_layer_fwd_single_launch_equals_staged(name):
+    """The single-launch forward (router, route, dispatch, GEMM1, GEMM2 and
+    the fold in one persistent launch) computes each step as its separate
+    launch does: every saved tensor and the output are bitwise the staged
+    forward's, whose parity with the oracle the tests above establish.  The
+    single-launch outputs are poisoned first, so an element it fails to write
+    cannot pass."""
+    wl = SINGLE_CASES[name]
+    print(f"single-launch fwd {name}", flush=True)
+    inp = S.make_inputs(wl, 3)
+    w, _ = _weights(inp)
+    drop = dev(inp.drop) if inp.drop is not None else None
+    x = dev_bf16(inp.x)
+    staged = M.MoeLayer(w, wl.N, wl.K, drop=drop)
+    want = staged.forward(x)
+    one = M.MoeLayer(w, wl.N, wl.K, drop=drop, sched=M.MOE_SCHED_SINGLE)
+    for t in list(one.saved.values()) + [one.out]:
+        t.view(torch.uint8).fill_(0xA5)
+    got = one.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(one.saved["status"])[0]) == 0
+    n = int(host(staged.saved["offsets"])[-1])
+    for k in SINGLE_KEYS:
+        a, b = staged.saved[k], one.saved[k]
+        if k in ("xd", "g", "u", "h", "y"):
+            a, b = a[:n], b[:n]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), k
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "out"
+    # and the oracle on the same logits, for the output
+    ref = O.layer_fwd(inp.x, inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K, drop=inp.drop,
+                      logits=logits_checked(one.saved, inp))
+    assert_same_route(one.saved, ref)
+    assert_bf16_close(vals(got), ref["out"], "out")
+
+
+def test_single_launch_barrier_expiry_is_reported_and_the_next_call_recovers():
+    """Barrier arrivals and readiness withheld from the host, every wait
+    bounded to a few polls: each barrier wait expires, the workgroups stop,
+    the launch ends and the status word reports MOE_STATUS_WAIT_EXPIRED.  The
+    next call reports 0 and equals the staged forward bit for bit."""
+    wl = SINGLE_CASES["ragged_e24"]
+    print("single-launch fwd: forced barrier expiry", flush=True)
+    inp = S.make_inputs(wl, 4)
+    w, _ = _weights(inp)
+    x = dev_bf16(inp.x)
+    want = M.MoeLayer(w, wl.N, wl.K).forward(x).clone()
+    layer = M.MoeLayer(w, wl.N, wl.K, sched=M.MOE_SCHED_SINGLE)
+    layer.ready_test_polls = 4
+    layer.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(layer.saved["status"])[0]) == M.MOE_STATUS_WAIT_EXPIRED
+    layer.ready_test_polls = 0
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(layer.saved["status"])[0]) == 0
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
 @pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_shape_small", "dsv3_shape_small"])
 def test_layer_bwd_bf16(name):
     wl = LAYER_CASES[name]
@@ -439,7 +511,7 @@ def test_weight_prequantization_bit_exact():
         assert np.array_equal(host(q[k]), ref[k]), k
 
 
-@pytest.mark.parametrize("sched", [M.MOE_SCHED_STAGED, M.MOE_SCHED_READY])
+@pytest.mark.parametrize("sched", [M.MOE_SCHED_STAGED, M.MOE_SCHED_READY, M.MOE_SCHED_SINGLE])
 def test_layer_deterministic_and_overwrites_outputs(sched):
     """Bitwise identical results run to run, with every output poisoned in
     between (catches unwritten elements and races)."""
