@@ -326,13 +326,25 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * waits until every workgroup has stored its GEMM2 tiles.  Every output is
  * bitwise the staged forward's.  Same rules as MOE_SCHED_READY, and also the
  * tiled router (D % 64 == 0, 16 <= E <= 512), K <= 32, no grouped top-K and
- * no aux loss; else MOE_ERR_UNSUPPORTED.  Workspace MOE_OP_LAYER_FWD. */
+ * no aux loss; else MOE_ERR_UNSUPPORTED.  Workspace MOE_OP_LAYER_FWD.
+ * moe_layer_bwd with MOE_SCHED_SINGLE (KOSMOS section 3.3.2) runs the whole
+ * bf16 backward in one persistent launch (after the same kind of reset):
+ * the combine backward and the GEMM plans; the down dgrad (SwiGLU backward)
+ * and wgrad queues and the router backward blocks; the gate/up dgrad, the
+ * gate and up wgrads and the router's dX_r and dW_r; then the router's
+ * reductions and the fold, phases separated by grid barriers.  Every
+ * gradient is bitwise the staged backward's.  It needs the saved H (no
+ * recompute), routed experts only, E <= 512 and the persistent GEMMs' shape
+ * rules (with the router backward, E % 64 == 0: dX_r contracts over E in
+ * whole steps); else MOE_ERR_UNSUPPORTED.  An expired barrier wait is or-ed into
+ * saved->status (MOE_STATUS_WAIT_EXPIRED).  MOE_SCHED_READY backward calls
+ * run staged. */
 #define MOE_SCHED_SINGLE 2
 
 typedef struct moe_layer_args {
   moe_dims dims;
   int32_t dtype;
-  int32_t sched;        /* MOE_SCHED_STAGED, _READY or _SINGLE (forward only)  */
+  int32_t sched;        /* MOE_SCHED_STAGED, _READY (forward) or _SINGLE        */
   const void* x;        /* bf16 [N][D] */
   const void* w_r;      /* bf16 [E][D] */
   const float* bias;    /* fp32 [E] or NULL */

@@ -450,8 +450,8 @@ def saved_tensors(sv: dict) -> dict:
 class MoeLayer:
     """Holds the weights, saved tensors and workspaces of one layer so that
     repeated forward/backward calls allocate nothing.  sched selects the
-    forward's launch scheme (MOE_SCHED_STAGED, MOE_SCHED_READY or
-    MOE_SCHED_SINGLE)."""
+    launch scheme: MOE_SCHED_STAGED, MOE_SCHED_READY (forward; the backward
+    then runs staged) or MOE_SCHED_SINGLE (one launch per direction)."""
 
     def __init__(self, wts: LayerWeights, N: int, K: int, mxfp8=False, renorm=0, drop=None,
                  device="cuda", with_bwd=False, sched=MOE_SCHED_STAGED, router_bwd=False, n_group=0,
@@ -511,7 +511,8 @@ class MoeLayer:
         """recompute_h: do not read the saved H (bf16) or H codes (MXFP8); the
         library recomputes H from the saved G and U (SwiGLU-recompute mode).
         d_aux: upstream gradient of the aux loss (used when aux_alpha != 0)."""
-        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, **self._opts)
+        a, _ = _layer_args(x, self.wts, self.K, self.drop, self.renorm, self.mxfp8, self.sched, **self._opts)
+        a.ready_test_polls = int(self.ready_test_polls)
         a.mx_wgrad = int(self.mx_wgrad)
         self._gr.d_aux = float(d_aux)
         sv = self._sv

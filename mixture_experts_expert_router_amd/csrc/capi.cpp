@@ -136,7 +136,7 @@ RouterBwdLayout router_bwd_layout(const moe_dims& d) {
 // (recomputed, or dequantized from h_q), then for MXFP8 dY_d quantized,
 // [dG | dU] quantized and X_d dequantized, then the router backward's scratch
 struct BwdLayout {
-  size_t dyd, dxd, dg, du, h, dyq, dys, guq, gus, xdeq, router, total;
+  size_t dyd, dxd, dg, du, h, dyq, dys, guq, gus, xdeq, router, single, total;
   // native MXFP8 wgrad: per-expert block offsets and the column-wise copies
   // (width x ldt codes, width x ldt / 32 scales)
   size_t toff, dyt_q, dyt_s, xt_q, xt_s, ht_q, ht_s, dgt_q, dgt_s, dut_q, dut_s;
@@ -183,6 +183,8 @@ BwdLayout bwd_layout(const moe_dims& d, bool mx, bool mxw = false) {
     take(l.dut_s, H * ldt / 32);
   }
   take(l.router, router_bwd_layout(d).total);
+  // the single-launch backward's queue plans and barrier words
+  take(l.single, moe::layer_bwd_single_ints(experts_of(d), router_bwd_layout(d).S) * 4);
   l.total = o;
   return l;
 }
@@ -706,6 +708,12 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
   if (st) return st;
   if (a->mx_wgrad != 0 && (a->mx_wgrad != 1 || !mx)) return MOE_ERR_DTYPE;
   const bool mxw = mx && a->mx_wgrad == 1;
+  if (a->sched != MOE_SCHED_STAGED && a->sched != MOE_SCHED_READY && a->sched != MOE_SCHED_SINGLE)
+    return MOE_ERR_DTYPE;
+  // MOE_SCHED_SINGLE: the bf16 routed-expert backward from the saved H, in one launch
+  const bool single = a->sched == MOE_SCHED_SINGLE;
+  if (single && (mx || d.n_shared || d.align != 1 || !sv->h || d.E > 512)) return MOE_ERR_UNSUPPORTED;
+  if (single && a->ready_test_polls < 0) return MOE_ERR_SHAPE;
   if (mx) {
     // the block-scaled dgrads run on the persistent engine: whole 128-element
     // contraction steps over D and over 2H
@@ -852,6 +860,58 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
       if (e == hipSuccess) e = gemm_wgrad(wgu, dg, gr->dw_gate, table, s);
       if (e == hipSuccess) e = gemm_wgrad(wgu, du, gr->dw_up, table, s);
     }
+  } else if (single) {
+    // the whole backward in one persistent launch (the router's too when asked)
+    moe::LayerBwdSingle one{};
+    one.dout = dout;
+    one.dst_rows = sv->dst_rows;
+    one.topk_prob = sv->topk_prob;
+    one.y = sv->y;
+    one.N = d.N;
+    one.D = d.D;
+    one.K = d.K;
+    one.E = d.E;
+    one.dyd = dyd;
+    one.dprob = gr->dprob;
+    one.down = moe::GemmBwd{Ex, rc, d.H, d.D, sv->offsets, sv->h, a->w_down, nullptr, dyd, nullptr, nullptr,
+                            sv->g, sv->u, dg, du, true};
+    one.gu = moe::GemmBwd{Ex, rc, d.D, d.H, sv->offsets, sv->xd, a->w_gate, a->w_up, dg, du, dxd,
+                          nullptr, nullptr, nullptr, nullptr, false};
+    one.dw_down = gr->dw_down;
+    one.dw_gate = gr->dw_gate;
+    one.dw_up = gr->dw_up;
+    one.router = gr->dw_r != nullptr;
+    if (one.router) {
+      char* p = p0 + bl.router;
+      const RouterBwdLayout l = router_bwd_layout(d);
+      const bool aux = a->aux_alpha != 0.0f && gr->d_aux != 0.0f;
+      one.logits = sv->logits;
+      one.topk_idx = sv->topk_idx;
+      one.renorm = d.renorm;
+      one.dl = gr->dlogits ? gr->dlogits : (float*)(p + l.dl);
+      one.dlb = (uint16_t*)(p + l.dlb);
+      one.colpart = (float*)(p + l.colpart);
+      one.offs = (int32_t*)(p + l.offs);
+      one.offs1 = one.offs + 48;
+      one.S = l.S;
+      one.aux_counts = aux ? sv->counts : nullptr;
+      one.aux_c = aux ? gr->d_aux * a->aux_alpha * (float)d.E / ((float)d.N * (float)d.N * (float)d.K) : 0.0f;
+      one.rt = moe::GemmBwd{1, d.N, d.D, d.E, one.offs1, a->x, a->w_r, nullptr, one.dlb, nullptr, p + l.dxr,
+                            nullptr, nullptr, nullptr, nullptr, false};
+      one.rs = moe::GemmBwd{l.S, d.N, d.D, d.E, one.offs, a->x, a->w_r, nullptr, one.dlb, nullptr, nullptr,
+                            nullptr, nullptr, nullptr, nullptr, false};
+      one.part = (float*)(p + l.part);
+      one.split = moe::gemm_wgrad_fast_ok(one.rs, one.dlb, one.part);
+      one.dw_r = gr->dw_r;
+      one.db_r = gr->db_r;
+      one.dxr = p + l.dxr;
+    }
+    one.dxd = dxd;
+    one.dx = gr->dx;
+    one.status = sv->status;
+    one.test_polls = a->ready_test_polls;
+    if (!moe::layer_bwd_single_ok(one)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_layer_bwd_single(one, (int32_t*)(p0 + bl.single), s));
   } else {
     // SwiGLU-recompute mode: H = silu(G) U from the saved bf16 G and U, the
     // same arithmetic as GEMM1's epilogue, so it equals the forward's H bit for bit

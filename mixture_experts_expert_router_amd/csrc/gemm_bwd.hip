@@ -24,6 +24,8 @@
 #include "launch.h"
 #include "mfma_tile.h"
 #include "sched.h"
+#include "permute_dev.h"
+#include "router_dev.h"
 
 namespace moe {
 
@@ -182,21 +184,27 @@ __device__ __forceinline__ Item run_dg(const DgradParams& p, const uint8_t* smem
   return next;
 }
 
+// A workgroup's share of a dgrad queue: items until the queue is empty.
+template <bool SWB>
+__device__ __forceinline__ void dgrad_loop(const DgradParams& p, const uint8_t* smem, uint32_t lds0, int* s_item) {
+  const int xcd = xcd_id();
+  int li = 0;
+  Item it = claim_dg(p, s_item, li, xcd);
+  if (!it.valid) return;
+  if (it.big) start_dg<DgBig>(p, lds0, it);
+  else start_dg<DgSmall>(p, lds0, it);
+  while (it.valid) {
+    if (it.big) it = run_dg<DgBig, SWB>(p, smem, lds0, s_item, li, xcd, it);
+    else it = run_dg<DgSmall, SWB>(p, smem, lds0, s_item, li, xcd, it);
+  }
+}
+
 template <bool SWB>
 __global__ __launch_bounds__(512) void gemm_dgrad_kernel(DgradParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDgLds];
   __shared__ int s_item;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const int xcd = xcd_id();
-  int li = 0;
-  Item it = claim_dg(p, &s_item, li, xcd);
-  if (!it.valid) return;
-  if (it.big) start_dg<DgBig>(p, lds0, it);
-  else start_dg<DgSmall>(p, lds0, it);
-  while (it.valid) {
-    if (it.big) it = run_dg<DgBig, SWB>(p, smem, lds0, &s_item, li, xcd, it);
-    else it = run_dg<DgSmall, SWB>(p, smem, lds0, &s_item, li, xcd, it);
-  }
+  dgrad_loop<SWB>(p, smem, lds0, &s_item);
 }
 
 // ---------------------------------------------------------------- wgrad ----
@@ -324,15 +332,12 @@ __device__ __forceinline__ void zero_wg(const WgradParams& p, const WgItem& it) 
 // Tiles of experts without rows have no steps: they issue no loads and clear
 // a flat range of the expert's gradient, and the tile after one issues its
 // own first step.
-__global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[WgTile::LDS];
-  __shared__ int s_item;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+__device__ __forceinline__ void wgrad_loop(const WgradParams& p, const uint8_t* smem, uint32_t lds0, int* s_item) {
   const int xcd = xcd_id();
-  WgItem it = claim_wg(p, &s_item, xcd);
+  WgItem it = claim_wg(p, s_item, xcd);
   if (!it.valid) return;
   __syncthreads();   // every wave has read s_item before it is reused
-  WgItem next = claim_wg(p, &s_item, xcd);
+  WgItem next = claim_wg(p, s_item, xcd);
   tile::SrcB<WgTile> src;
   sources_wg(p, it, src);
   bool issued = false;   // step 0 of `it` is in the ring at position g0
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
     f32x4_t acc[WgTile::TM][WgTile::TN];
     tile::mainloop_b_stream<WgTile>(smem, lds0, src, nk, it.rows - 64 * (nk - 1), ns, stream, g0, acc);
     // claim the tile after next while next's first step is in flight
-    const WgItem after = next.valid ? claim_wg(p, &s_item, xcd) : WgItem{};
+    const WgItem after = next.valid ? claim_wg(p, s_item, xcd) : WgItem{};
     if (nk > 0) epilogue_wg(p, it, acc);
     else zero_wg(p, it);
     g0 += nk;
@@ -359,10 +364,17 @@ __global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
   }
 }
 
-// Expert order for wgrad: most rows first (ties: lower id), one workgroup.
-__global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restrict__ offsets, int E, int per_e,
-                                                          int32_t* __restrict__ plan, int32_t* __restrict__ head) {
-  __shared__ int s_rows[1024];
+__global__ __launch_bounds__(512) void gemm_wgrad_kernel(WgradParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WgTile::LDS];
+  __shared__ int s_item;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  wgrad_loop(p, smem, lds0, &s_item);
+}
+
+// Expert order for wgrad: most rows first (ties: lower id), one workgroup
+// (E <= its thread count); s_rows: one int of LDS per thread.
+__device__ __forceinline__ void plan_wgrad_body(const int32_t* __restrict__ offsets, int E, int per_e,
+                                                int32_t* __restrict__ plan, int32_t* __restrict__ head, int* s_rows) {
   const int t = threadIdx.x;
   const int rows = t < E ? offsets[t + 1] - offsets[t] : -1;
   s_rows[t] = rows;
@@ -377,6 +389,12 @@ __global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restr
   }
   if (t == 0) plan[0] = E * per_e;
   if (t < kXcds) head[t * kHeadStride] = 0;
+}
+
+__global__ __launch_bounds__(1024) void plan_wgrad_kernel(const int32_t* __restrict__ offsets, int E, int per_e,
+                                                          int32_t* __restrict__ plan, int32_t* __restrict__ head) {
+  __shared__ int s_rows[1024];
+  plan_wgrad_body(offsets, E, per_e, plan, head, s_rows);
 }
 
 // ---------------------------------------------------------- MXFP8 wgrad ----
@@ -537,6 +555,181 @@ __global__ __launch_bounds__(512) void gemm_wgrad_mx_kernel(WgradMxParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-launch layer backward (KOSMOS section 3.3 and Figure 6: one launch
+// per direction; section 3.3.2 steps 1-4), on one GPU.  One persistent
+// workgroup per CU runs four phases, each ended by a grid barrier (every
+// workgroup adds to a counter after an agent-scope release and waits,
+// bounded, until all have):
+//   0. the combine backward (dY_d rows and dprob), 8 tokens per item, and
+//      the plans of the GEMM queues (a workgroup each);
+//   1. the down dgrad queue (SwiGLU backward in its epilogue: dG, dU), the
+//      down wgrad queue, then the router backward blocks (dlogits);
+//   2. the gate/up dgrad queue (dX_d), the gate and up wgrad queues, the
+//      router's dX_r and dW_r queues;
+//   3. the router's dW_r and db_r reductions and the fold (dx, plus dX_r).
+// A workgroup drains the queues of a phase one after another, so a queue's
+// tail overlaps the next queue's items.  Each item computes what it does in
+// its separate launch, so the gradients are bitwise the staged backward's.
+// ---------------------------------------------------------------------------
+
+struct SingleBwdParams {
+  const uint16_t* dout;       // [N][D]
+  const int32_t* dst_rows;    // [N][K]
+  const float* topk_prob;     // [N][K]
+  const uint16_t* y;          // saved Y [rows][D]
+  int N, D, K, E;
+  uint16_t* dyd;              // dY_d [rows][D]
+  float* dprob;               // [N][K]
+  DgradParams dg_dn, dg_gu, dg_rt;
+  WgradParams wg_dn, wg_g, wg_u, wg_rt;
+  int router;                 // the router backward is on
+  int rt_split;               // dW_r through fp32 token-split partials
+  const float* logits;
+  const int32_t* topk_idx;
+  int renorm;
+  float* dl;                  // dlogits fp32 [N][E]
+  uint16_t* dlb;              // and bf16
+  float* colpart;             // [ceil(N / 64)][E]
+  int32_t* offs;              // S + 1 token-split offsets
+  int S;
+  int32_t* offs1;             // {0, N}
+  const int32_t* aux_counts;
+  float aux_c;
+  int rb_blocks;              // ceil(N / 64) router backward blocks
+  uint16_t* dw_r;
+  float* db_r;
+  const uint16_t* dxd;        // dX_d [rows][D]
+  uint16_t* dx;               // [N][D]
+  const uint16_t* dxr;        // dX_r [N][D] or null
+  int32_t* bar;               // [3] barriers, [3]: router block queue (zeroed before the launch)
+  int32_t* status;
+  int polls, publish;
+};
+
+constexpr int kSbLds = kDgLds > WgTile::LDS ? kDgLds : WgTile::LDS;
+static_assert(kSbLds >= 2 * 4 * router::kRbMaxE * 4, "the router backward's LDS rows");
+
+// thread 0 of each workgroup: after the workgroup's stores, add to *bar and
+// wait (bounded) until every workgroup has; false if the wait expired
+__device__ __forceinline__ bool bar_sync(const SingleBwdParams& p, int32_t* bar, int* s_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, p.publish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = false;
+    for (int it = 0; it < p.polls && !ok; ++it) {
+      ok = __hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (int)gridDim.x;
+      if (!ok) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!ok && p.status) atomicOr(p.status, 1);
+    *s_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *s_flag != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
+__global__ __launch_bounds__(512) void layer_bwd_single_kernel(SingleBwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSbLds];
+  __shared__ int s_item;
+  __shared__ int s_flag;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int nt8 = (p.N + 7) / 8;
+
+  // ---- 0. combine backward; the GEMM plans -----------------------------------
+  for (int it = blockIdx.x; it < nt8; it += gridDim.x) {
+    const int t = __builtin_amdgcn_readfirstlane(it * 8 + wave);
+    if (t < p.N)
+      perm::combine_bwd_token<false>(t, p.dout, p.dst_rows, p.topk_prob, p.y, p.D, p.K, p.dyd, p.dprob, nullptr,
+                                     nullptr, nullptr);
+  }
+  {
+    int* w = reinterpret_cast<int*>(smem);
+    const int nplans = p.router ? 7 : 5;
+    for (int j = (int)gridDim.x - 1 - (int)blockIdx.x; j < nplans; j += gridDim.x) {
+      __syncthreads();   // the LDS of the previous plan
+      if (j == 0) sched::plan_rows_body<512>(p.dg_dn.offsets, p.dg_dn.E, p.dg_dn.n_tiles, const_cast<int32_t*>(p.dg_dn.plan),
+                                             p.dg_dn.head, w, w + 16, w + 32, reinterpret_cast<float*>(w + 512),
+                                             w + 1024, w + 1536, w + 48);
+      else if (j == 1) sched::plan_rows_body<512>(p.dg_gu.offsets, p.dg_gu.E, p.dg_gu.n_tiles,
+                                                  const_cast<int32_t*>(p.dg_gu.plan), p.dg_gu.head, w, w + 16, w + 32,
+                                                  reinterpret_cast<float*>(w + 512), w + 1024, w + 1536, w + 48);
+      else if (j < 5) {
+        const WgradParams& q = j == 2 ? p.wg_dn : (j == 3 ? p.wg_g : p.wg_u);
+        plan_wgrad_body(q.offsets, q.E, q.m_tiles * q.n_tiles, const_cast<int32_t*>(q.plan), q.head, w);
+      } else {
+        // the router's token splits (the router backward's first block writes the same)
+        if (tid <= p.S) p.offs[tid] = (int)((int64_t)p.N * tid / p.S);
+        if (tid < 2) p.offs1[tid] = tid ? p.N : 0;
+        __syncthreads();
+        if (j == 5) sched::plan_rows_body<512>(p.dg_rt.offsets, p.dg_rt.E, p.dg_rt.n_tiles,
+                                               const_cast<int32_t*>(p.dg_rt.plan), p.dg_rt.head, w, w + 16, w + 32,
+                                               reinterpret_cast<float*>(w + 512), w + 1024, w + 1536, w + 48);
+        else plan_wgrad_body(p.wg_rt.offsets, p.wg_rt.E, p.wg_rt.m_tiles * p.wg_rt.n_tiles,
+                             const_cast<int32_t*>(p.wg_rt.plan), p.wg_rt.head, w);
+      }
+    }
+  }
+  if (!bar_sync(p, p.bar + 0, &s_flag)) return;
+
+  // ---- 1. down dgrad, down wgrad, router backward blocks ----------------------
+  dgrad_loop<true>(p.dg_dn, smem, lds0, &s_item);
+  __syncthreads();   // the ring and s_item are free
+  wgrad_loop(p.wg_dn, smem, lds0, &s_item);
+  __syncthreads();
+  if (p.router) {
+    float (*s_g)[router::kRbMaxE] = reinterpret_cast<float (*)[router::kRbMaxE]>(smem) + 4 * (tid >> 8);
+    const int npairs = (p.rb_blocks + 1) / 2;
+    for (;;) {
+      if (tid == 0) s_item = atomicAdd(p.bar + 3, 1);
+      __syncthreads();
+      const int pr = s_item;
+      __syncthreads();
+      if (pr >= npairs) break;
+      const int blk = 2 * pr + (tid >> 8);
+      router::router_bwd_block(blk, blk < p.rb_blocks, tid & 255, s_g, p.logits, p.topk_idx, p.dprob, p.N, p.E, p.K,
+                               p.renorm, p.dl, p.dlb, p.colpart, p.offs, p.S, p.offs1, p.aux_counts, p.aux_c);
+    }
+  }
+  if (!bar_sync(p, p.bar + 1, &s_flag)) return;
+
+  // ---- 2. gate/up dgrad, gate and up wgrad, the router's GEMMs ----------------
+  dgrad_loop<false>(p.dg_gu, smem, lds0, &s_item);
+  __syncthreads();
+  wgrad_loop(p.wg_g, smem, lds0, &s_item);
+  __syncthreads();
+  wgrad_loop(p.wg_u, smem, lds0, &s_item);
+  __syncthreads();
+  if (p.router) {
+    dgrad_loop<false>(p.dg_rt, smem, lds0, &s_item);
+    __syncthreads();
+    wgrad_loop(p.wg_rt, smem, lds0, &s_item);
+  }
+  if (!bar_sync(p, p.bar + 2, &s_flag)) return;
+
+  // ---- 3. the router's reductions and the fold ---------------------------------
+  if (p.router) {
+    const int64_t ED = (int64_t)p.E * p.D;
+    if (p.rt_split)
+      for (int64_t i = (int64_t)blockIdx.x * 512 + tid; i < ED / 4; i += (int64_t)gridDim.x * 512)
+        router::router_reduce_dw4(i, reinterpret_cast<const float*>(p.wg_rt.c), p.S, ED, p.dw_r);
+    if (p.db_r)
+      for (int e = blockIdx.x * 8 + wave; e < p.E; e += gridDim.x * 8)
+        router::router_reduce_db(e, p.colpart, p.rb_blocks, p.E, p.db_r);
+  }
+  for (int it = blockIdx.x; it < nt8; it += gridDim.x) {
+    const int t = __builtin_amdgcn_readfirstlane(it * 8 + wave);
+    if (t < p.N) perm::combine_token<false>(t, p.dxd, p.dst_rows, nullptr, p.D, p.K, p.dx, p.dxr, nullptr);
+  }
+}
+
+__global__ void single_bwd_reset_kernel(int32_t* bar, int n) {
+  if ((int)threadIdx.x < n) bar[threadIdx.x] = 0;
+}
+
 hipError_t grid_for(const void* kern, int* grid) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -562,7 +755,8 @@ bool gemm_dgrad_fast_ok(const GemmBwd& b) {
   return true;
 }
 
-hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) {
+namespace {
+DgradParams dgrad_params(const GemmBwd& b, int32_t* ws) {
   DgradParams p{};
   p.offsets = b.offsets;
   p.E = (int)b.E;
@@ -581,6 +775,29 @@ hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) 
   p.u = (const uint16_t*)b.u;
   p.head = ws;
   p.plan = ws + kGemmHeadInts;
+  return p;
+}
+
+WgradParams wgrad_params(const GemmBwd& b, const void* dc, void* db, int32_t* ws, bool f32) {
+  WgradParams p{};
+  p.offsets = b.offsets;
+  p.E = (int)b.E;
+  p.M = (int)b.n_dim;
+  p.N = (int)b.k_dim;
+  p.m_tiles = (p.M + WgTile::BM - 1) / WgTile::BM;
+  p.n_tiles = (p.N + WgTile::BN - 1) / WgTile::BN;
+  p.a = (const uint8_t*)dc;
+  p.b = (const uint8_t*)b.a;
+  p.c = db;
+  p.f32 = f32;
+  p.head = ws;
+  p.plan = ws + kGemmHeadInts;
+  return p;
+}
+}  // namespace
+
+hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) {
+  const DgradParams p = dgrad_params(b, ws);
   plan_rows_kernel<<<1, 1024, 0, s>>>(b.offsets, (int)b.E, p.n_tiles, ws + kGemmHeadInts, ws);
   const void* kern = b.swiglu_bwd ? (const void*)gemm_dgrad_kernel<true> : (const void*)gemm_dgrad_kernel<false>;
   int grid = 0;
@@ -602,24 +819,87 @@ bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db) {
 
 hipError_t launch_gemm_wgrad_fast(const GemmBwd& b, const void* dc, void* db, int32_t* ws, hipStream_t s,
                                   bool f32) {
-  WgradParams p{};
-  p.offsets = b.offsets;
-  p.E = (int)b.E;
-  p.M = (int)b.n_dim;
-  p.N = (int)b.k_dim;
-  p.m_tiles = (p.M + WgTile::BM - 1) / WgTile::BM;
-  p.n_tiles = (p.N + WgTile::BN - 1) / WgTile::BN;
-  p.a = (const uint8_t*)dc;
-  p.b = (const uint8_t*)b.a;
-  p.c = db;
-  p.f32 = f32;
-  p.head = ws;
-  p.plan = ws + kGemmHeadInts;
+  const WgradParams p = wgrad_params(b, dc, db, ws, f32);
   plan_wgrad_kernel<<<1, 1024, 0, s>>>(b.offsets, p.E, p.m_tiles * p.n_tiles, ws + kGemmHeadInts, ws);
   int grid = 0;
   hipError_t err = grid_for((const void*)gemm_wgrad_kernel, &grid);
   if (err != hipSuccess) return err;
   gemm_wgrad_kernel<<<grid, 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// plans and queue heads of the single-launch backward's seven GEMM queues,
+// then its four barrier words
+size_t layer_bwd_single_ints(int64_t E, int S) {
+  const int64_t w = E > S ? E : S;
+  return (size_t)(7 * (kGemmHeadInts + gemm_fwd_plan_ints(w)) + 64);
+}
+
+bool layer_bwd_single_ok(const LayerBwdSingle& a) {
+  if (a.E > 512 || a.S > 512) return false;
+  if (!gemm_dgrad_fast_ok(a.down) || !gemm_dgrad_fast_ok(a.gu)) return false;
+  if (!gemm_wgrad_fast_ok(a.down, a.dyd, a.dw_down) || !gemm_wgrad_fast_ok(a.gu, a.gu.dc0, a.dw_gate) ||
+      !gemm_wgrad_fast_ok(a.gu, a.gu.dc1, a.dw_up))
+    return false;
+  if (a.router && (!gemm_dgrad_fast_ok(a.rt) ||
+                   !(a.split ? gemm_wgrad_fast_ok(a.rs, a.rs.dc0, a.part) : gemm_wgrad_fast_ok(a.rt, a.rt.dc0, a.dw_r))))
+    return false;
+  return true;
+}
+
+hipError_t launch_layer_bwd_single(const LayerBwdSingle& a, int32_t* ws, hipStream_t s) {
+  if (!layer_bwd_single_ok(a)) return hipErrorInvalidValue;
+  const int64_t w = a.E > a.S ? a.E : a.S;
+  const int64_t q = kGemmHeadInts + (int64_t)gemm_fwd_plan_ints(w);
+  SingleBwdParams p{};
+  p.dout = (const uint16_t*)a.dout;
+  p.dst_rows = a.dst_rows;
+  p.topk_prob = a.topk_prob;
+  p.y = (const uint16_t*)a.y;
+  p.N = (int)a.N;
+  p.D = (int)a.D;
+  p.K = (int)a.K;
+  p.E = (int)a.E;
+  p.dyd = (uint16_t*)a.dyd;
+  p.dprob = a.dprob;
+  p.dg_dn = dgrad_params(a.down, ws + 0 * q);
+  p.wg_dn = wgrad_params(a.down, a.dyd, a.dw_down, ws + 1 * q, false);
+  p.dg_gu = dgrad_params(a.gu, ws + 2 * q);
+  p.wg_g = wgrad_params(a.gu, a.gu.dc0, a.dw_gate, ws + 3 * q, false);
+  p.wg_u = wgrad_params(a.gu, a.gu.dc1, a.dw_up, ws + 4 * q, false);
+  p.router = a.router;
+  if (a.router) {
+    p.dg_rt = dgrad_params(a.rt, ws + 5 * q);
+    p.rt_split = a.split;
+    p.wg_rt = a.split ? wgrad_params(a.rs, a.rs.dc0, a.part, ws + 6 * q, true)
+                      : wgrad_params(a.rt, a.rt.dc0, a.dw_r, ws + 6 * q, false);
+    p.logits = a.logits;
+    p.topk_idx = a.topk_idx;
+    p.renorm = a.renorm;
+    p.dl = a.dl;
+    p.dlb = a.dlb;
+    p.colpart = a.colpart;
+    p.offs = a.offs;
+    p.S = a.S;
+    p.offs1 = a.offs1;
+    p.aux_counts = a.aux_counts;
+    p.aux_c = a.aux_c;
+    p.rb_blocks = (int)((a.N + 63) / 64);
+    p.dw_r = (uint16_t*)a.dw_r;
+    p.db_r = a.db_r;
+  }
+  p.dxd = (const uint16_t*)a.dxd;
+  p.dx = (uint16_t*)a.dx;
+  p.dxr = (const uint16_t*)a.dxr;
+  p.bar = ws + 7 * q;
+  p.status = a.status;
+  p.polls = a.test_polls > 0 ? a.test_polls : (1 << 22);
+  p.publish = a.test_polls > 0 ? 0 : 1;
+  int grid = 0;
+  hipError_t err = grid_for((const void*)layer_bwd_single_kernel, &grid);
+  if (err != hipSuccess) return err;
+  single_bwd_reset_kernel<<<1, 64, 0, s>>>(p.bar, 4);
+  layer_bwd_single_kernel<<<grid, 512, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -209,6 +209,52 @@ hipError_t launch_gemm_wgrad_mx(const int32_t* offsets, const int32_t* toff, int
                                 const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, void* db,
                                 int32_t* ws, hipStream_t s);
 
+// single-launch layer backward (gemm_bwd.hip): the combine backward, the
+// expert dgrads and wgrads, the router backward and the fold in one
+// persistent launch (after a one-workgroup reset of its barrier words); bf16,
+// routed experts, the fast paths' shape rules, E <= 512.  ws: the plans and
+// barriers block of layer_bwd_single_ints ints.
+struct LayerBwdSingle {
+  const void* dout;                  // [N][D]
+  const int32_t* dst_rows;           // [N][K]
+  const float* topk_prob;            // [N][K]
+  const void* y;                     // saved Y
+  int64_t N, D, K, E;
+  void* dyd;                         // dY_d scratch
+  float* dprob;                      // [N][K]
+  GemmBwd down;                      // down dgrad (SwiGLU backward) and, with dc = dyd, its wgrad
+  GemmBwd gu;                        // gate/up dgrad (dc0 = dG, dc1 = dU) and their wgrads
+  void* dw_down;
+  void* dw_gate;
+  void* dw_up;
+  int router;                        // router backward on
+  const float* logits;
+  const int32_t* topk_idx;
+  int renorm;
+  float* dl;
+  uint16_t* dlb;
+  float* colpart;
+  int32_t* offs;
+  int S;
+  int32_t* offs1;
+  const int32_t* aux_counts;
+  float aux_c;
+  GemmBwd rt;                        // dX_r = dL W_r (one expert of N rows; dc0 = dL bf16)
+  GemmBwd rs;                        // dW_r over the S token splits (dc0 = dL bf16)
+  bool split;                        // dW_r through fp32 partials (part) reduced in order
+  float* part;
+  void* dw_r;
+  float* db_r;
+  const void* dxd;                   // dX_d
+  void* dx;                          // [N][D]
+  const void* dxr;                   // dX_r or null
+  int32_t* status;                   // optional status word (expired barrier waits)
+  int test_polls;
+};
+size_t layer_bwd_single_ints(int64_t E, int S);
+bool layer_bwd_single_ok(const LayerBwdSingle& a);
+hipError_t launch_layer_bwd_single(const LayerBwdSingle& a, int32_t* ws, hipStream_t s);
+
 // gemm_mxfp8.hip
 hipError_t launch_gemm_fwd_mxfp8(const GemmFwd& f, int32_t* table, hipStream_t s);
 

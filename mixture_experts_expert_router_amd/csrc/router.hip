@@ -197,17 +197,7 @@ hipError_t launch_router_logits(const void* x, const void* w_r, const float* bia
 // dX_r = dL W_r and dW_r = dL^T x run on the grouped-GEMM kernels.
 // ---------------------------------------------------------------------------
 
-constexpr int kRbTok = 16;
-constexpr int kRbMaxE = 1024;
-constexpr int kRbCols = kRbMaxE / 64;   // logits per lane
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+using router::kRbMaxE;
 
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits,
                                                          const int32_t* __restrict__ topk_idx,
@@ -218,93 +208,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
                                                          int32_t* __restrict__ offs1,
                                                          const int32_t* __restrict__ aux_counts, float aux_c) {
   __shared__ float s_g[4][kRbMaxE];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (blockIdx.x == 0) {
-    if ((int)threadIdx.x <= S) offs[threadIdx.x] = (int)((int64_t)N * threadIdx.x / S);
-    if (threadIdx.x < 2) offs1[threadIdx.x] = threadIdx.x ? N : 0;
-  }
-  const int nI = (E + 63) >> 6;
-  float* g = s_g[w];
-  float col[kRbCols];
-#pragma unroll
-  for (int i = 0; i < kRbCols; ++i) {
-    col[i] = 0.0f;
-    if (i < nI && lane + 64 * i < E) g[lane + 64 * i] = 0.0f;
-  }
-  // aux loss (optional): a_e = aux_c counts_e joins g for every expert
-  float aj[kRbCols];
-#pragma unroll
-  for (int i = 0; i < kRbCols; ++i)
-    aj[i] = (aux_counts && i < nI && lane + 64 * i < E) ? aux_c * (float)aux_counts[lane + 64 * i] : 0.0f;
-  wave_lds_fence();
-  const int t0 = blockIdx.x * 64 + w * kRbTok;
-  for (int j = 0; j < kRbTok; ++j) {
-    const int t = t0 + j;
-    if (t >= N) break;
-    const float* Lr = logits + (int64_t)t * E;
-    float l[kRbCols];
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kRbCols; ++i) {
-      const int e = lane + 64 * i;
-      l[i] = (i < nI && e < E) ? Lr[e] : -INFINITY;
-      m = fmaxf(m, l[i]);
-    }
-    m = wave_max(m);
-    float z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kRbCols; ++i)
-      if (i < nI && lane + 64 * i < E) z += expf(l[i] - m);
-    z = wave_sum(z);
-    const float rz = 1.0f / z;
-    // the selected slots: lane k < K
-    int ek = -1;
-    float sk = 0.0f, dk = 0.0f;
-    if (lane < K) {
-      ek = topk_idx[(int64_t)t * K + lane];
-      dk = dprob[(int64_t)t * K + lane];
-      if (ek >= 0 && ek < E) sk = expf(Lr[ek] - m) * rz;
-      else ek = -1;
-    }
-    float ds = dk;
-    if (renorm) {
-      const float tot = wave_sum(sk);
-      const float c = wave_sum(sk * dk) / tot;   // sum_j w_j dprob_j
-      ds = (dk - c) / tot;
-    }
-    float pa = 0.0f;
-    if (aux_counts) {
-#pragma unroll
-      for (int i = 0; i < kRbCols; ++i)
-        if (i < nI && lane + 64 * i < E) pa += expf(l[i] - m) * rz * aj[i];
-    }
-    const float dot = wave_sum(sk * ds + pa);
-    if (ek >= 0) g[ek] = ds;
-    wave_lds_fence();
-    float* dlr = dl + (int64_t)t * E;
-    uint16_t* dlbr = dlb + (int64_t)t * E;
-#pragma unroll
-    for (int i = 0; i < kRbCols; ++i) {
-      const int e = lane + 64 * i;
-      if (i < nI && e < E) {
-        const float d = expf(l[i] - m) * rz * (g[e] + aj[i] - dot);
-        dlr[e] = d;
-        dlbr[e] = (uint16_t)(pack_bf16x2(d, 0.0f) & 0xFFFFu);
-        col[i] += d;
-      }
-    }
-    wave_lds_fence();
-    if (ek >= 0) g[ek] = 0.0f;
-    wave_lds_fence();
-  }
-  // column partials of this workgroup's tokens, added in wave order
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kRbCols; ++i)
-    if (i < nI && lane + 64 * i < E) s_g[w][lane + 64 * i] = col[i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256)
-    colpart[(int64_t)blockIdx.x * E + e] = ((s_g[0][e] + s_g[1][e]) + s_g[2][e]) + s_g[3][e];
+  router::router_bwd_block(blockIdx.x, true, threadIdx.x, s_g, logits, topk_idx, dprob, N, E, K, renorm, dl, dlb,
+                           colpart, offs, S, offs1, aux_counts, aux_c);
 }
 
 __global__ __launch_bounds__(256) void router_bwd_reduce_kernel(const float* __restrict__ part, int S, int64_t ED,
@@ -313,28 +218,9 @@ __global__ __launch_bounds__(256) void router_bwd_reduce_kernel(const float* __r
                                                                 int64_t E, float* __restrict__ db_r) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (part) {
-    for (int64_t i = tid; i < ED / 4; i += stride) {
-      float4 a = reinterpret_cast<const float4*>(part)[i];
-      for (int sp = 1; sp < S; ++sp) {
-        const float4 b = reinterpret_cast<const float4*>(part + (int64_t)sp * ED)[i];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-      }
-      reinterpret_cast<uint2*>(dw_r)[i] = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
-    }
-  }
-  if (db_r && blockIdx.x < E && threadIdx.x < 64) {
-    // one wave per expert: lane l adds partials l, l + 64, ... in order, then
-    // the lanes' sums are added by a fixed shuffle tree
-    const int64_t e = blockIdx.x;
-    float a = 0.0f;
-    for (int64_t b = threadIdx.x; b < P; b += 64) a += colpart[b * E + e];
-    a = wave_sum(a);
-    if (threadIdx.x == 0) db_r[e] = a;
-  }
+  if (part)
+    for (int64_t i = tid; i < ED / 4; i += stride) router::router_reduce_dw4(i, part, S, ED, dw_r);
+  if (db_r && blockIdx.x < E && threadIdx.x < 64) router::router_reduce_db(blockIdx.x, colpart, P, E, db_r);
 }
 
 // token splits of the router's wgrad: about 256 tiles, at least 64 rows each

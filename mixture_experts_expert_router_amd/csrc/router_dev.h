@@ -106,5 +106,146 @@ inline RouterPlan router_plan(int64_t N, int64_t D, int64_t E) {
 
 inline bool router_tiled(int64_t D, int64_t E) { return D % tile::kBK == 0 && E >= 16; }
 
+
+constexpr int kRbTok = 16;
+constexpr int kRbMaxE = 1024;
+constexpr int kRbCols = kRbMaxE / 64;   // logits per lane
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// One block of 64 tokens (4 waves of kRbTok tokens) of the router backward by
+// 256 threads ltid = 0..255 of a workgroup, with their own LDS rows s_g[4]; a
+// 512-thread workgroup runs two blocks at once.  The body calls
+// __syncthreads() twice, so every thread of the workgroup makes the call;
+// live == false (a block past the tokens) writes nothing.
+__device__ __forceinline__ void router_bwd_block(int blk, bool live, int ltid, float (*s_g)[kRbMaxE],
+                                                 const float* __restrict__ logits,
+                                                 const int32_t* __restrict__ topk_idx,
+                                                 const float* __restrict__ dprob, int N, int E, int K, int renorm,
+                                                 float* __restrict__ dl, uint16_t* __restrict__ dlb,
+                                                 float* __restrict__ colpart, int32_t* __restrict__ offs, int S,
+                                                 int32_t* __restrict__ offs1, const int32_t* __restrict__ aux_counts,
+                                                 float aux_c) {
+  const int lane = ltid & 63, w = ltid >> 6;
+  if (blk == 0 && live) {
+    if (ltid <= S) offs[ltid] = (int)((int64_t)N * ltid / S);
+    if (ltid < 2) offs1[ltid] = ltid ? N : 0;
+  }
+  const int nI = (E + 63) >> 6;
+  float* g = s_g[w];
+  float col[kRbCols];
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i) {
+    col[i] = 0.0f;
+    if (i < nI && lane + 64 * i < E) g[lane + 64 * i] = 0.0f;
+  }
+  // aux loss (optional): a_e = aux_c counts_e joins g for every expert
+  float aj[kRbCols];
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i)
+    aj[i] = (aux_counts && i < nI && lane + 64 * i < E) ? aux_c * (float)aux_counts[lane + 64 * i] : 0.0f;
+  wave_lds_fence();
+  const int t0 = blk * 64 + w * kRbTok;
+  for (int j = 0; j < kRbTok; ++j) {
+    const int t = t0 + j;
+    if (t >= N) break;
+    const float* Lr = logits + (int64_t)t * E;
+    float l[kRbCols];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = (i < nI && e < E) ? Lr[e] : -INFINITY;
+      m = fmaxf(m, l[i]);
+    }
+    m = wave_max(m);
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i)
+      if (i < nI && lane + 64 * i < E) z += expf(l[i] - m);
+    z = wave_sum(z);
+    const float rz = 1.0f / z;
+    // the selected slots: lane k < K
+    int ek = -1;
+    float sk = 0.0f, dk = 0.0f;
+    if (lane < K) {
+      ek = topk_idx[(int64_t)t * K + lane];
+      dk = dprob[(int64_t)t * K + lane];
+      if (ek >= 0 && ek < E) sk = expf(Lr[ek] - m) * rz;
+      else ek = -1;
+    }
+    float ds = dk;
+    if (renorm) {
+      const float tot = wave_sum(sk);
+      const float c = wave_sum(sk * dk) / tot;   // sum_j w_j dprob_j
+      ds = (dk - c) / tot;
+    }
+    float pa = 0.0f;
+    if (aux_counts) {
+#pragma unroll
+      for (int i = 0; i < kRbCols; ++i)
+        if (i < nI && lane + 64 * i < E) pa += expf(l[i] - m) * rz * aj[i];
+    }
+    const float dot = wave_sum(sk * ds + pa);
+    if (ek >= 0) g[ek] = ds;
+    wave_lds_fence();
+    float* dlr = dl + (int64_t)t * E;
+    uint16_t* dlbr = dlb + (int64_t)t * E;
+#pragma unroll
+    for (int i = 0; i < kRbCols; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nI && e < E) {
+        const float d = expf(l[i] - m) * rz * (g[e] + aj[i] - dot);
+        dlr[e] = d;
+        dlbr[e] = (uint16_t)(pack_bf16x2(d, 0.0f) & 0xFFFFu);
+        col[i] += d;
+      }
+    }
+    wave_lds_fence();
+    if (ek >= 0) g[ek] = 0.0f;
+    wave_lds_fence();
+  }
+  // column partials of this workgroup's tokens, added in wave order
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRbCols; ++i)
+    if (i < nI && lane + 64 * i < E) s_g[w][lane + 64 * i] = col[i];
+  __syncthreads();
+  if (live)
+    for (int e = ltid; e < E; e += 256)
+      colpart[(int64_t)blk * E + e] = ((s_g[0][e] + s_g[1][e]) + s_g[2][e]) + s_g[3][e];
+}
+
+// dw_r element block i (4 values): the S fp32 partials added in split order
+__device__ __forceinline__ void router_reduce_dw4(int64_t i, const float* __restrict__ part, int S, int64_t ED,
+                                                  uint16_t* __restrict__ dw_r) {
+  float4 a = reinterpret_cast<const float4*>(part)[i];
+  for (int sp = 1; sp < S; ++sp) {
+    const float4 b = reinterpret_cast<const float4*>(part + (int64_t)sp * ED)[i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  reinterpret_cast<uint2*>(dw_r)[i] = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+}
+
+// db_r[e] by one wave: lane l adds the column partials l, l + 64, ... in
+// order, then the lanes' sums are added by a fixed shuffle tree
+__device__ __forceinline__ void router_reduce_db(int64_t e, const float* __restrict__ colpart, int64_t P, int64_t E,
+                                                 float* __restrict__ db_r) {
+  const int lane = threadIdx.x & 63;
+  float a = 0.0f;
+  for (int64_t b = lane; b < P; b += 64) a += colpart[b * E + e];
+  a = wave_sum(a);
+  if (lane == 0) db_r[e] = a;
+}
+
 }  // namespace router
 }  // namespace moe

@@ -204,6 +204,25 @@ def test_single_schedule_is_refused_where_it_does_not_run():
         assert lib.moe_layer_fwd(C.byref(a), C.byref(sv), 1 << 20, 1 << 20, 1 << 40, None) == -6, (d.E, d.D, dt)
 
 
+def test_single_schedule_backward_is_refused_where_it_does_not_run():
+    """The single-launch backward takes the bf16 routed layer from the saved
+    H: MXFP8, a shared expert or the recompute mode (saved H NULL) get
+    MOE_ERR_UNSUPPORTED before any launch (fake aligned pointers)."""
+    lib = M.load()
+    cases = [(M.dims(64, 256, 32, 2, 128, align=32), M.MOE_MXFP8, False),
+             (M.dims(64, 256, 32, 2, 128, n_shared=1), M.MOE_BF16, False),
+             (M.dims(64, 256, 32, 2, 128), M.MOE_BF16, True)]
+    for d, dt, no_h in cases:
+        a = M.LayerArgs(d, dt, M.MOE_SCHED_SINGLE, *([1 << 20] * 15))
+        a.wdt_q = a.wdt_s = a.wgut_q = a.wgut_s = 1 << 20
+        sv = _full_saved(lib, d, dt)
+        if no_h:
+            sv.h = None
+        gr = M.LayerGrads(*([1 << 20] * 5))
+        assert lib.moe_layer_bwd(C.byref(a), C.byref(sv), 1 << 20, C.byref(gr), 1 << 20, 1 << 40, None) == -6, \
+            (d.n_shared, dt, no_h)
+
+
 def test_saved_size_and_carve():
     """moe_saved_size covers every saved tensor at 256-byte offsets in the
     struct's field order; moe_saved_carve fills exactly the fields the dtype

@@ -284,6 +284,15 @@ def test_full_size_backward_qwen3():
         assert_bf16_close(vals(g["dw_down"][int(e)]), eb["dw_down"][0], f"dw_down[{e}]")
         assert_bf16_close(vals(g["dw_gate"][int(e)]), eb["dw_gate"][0], f"dw_gate[{e}]")
         assert_bf16_close(vals(g["dw_up"][int(e)]), eb["dw_up"][0], f"dw_up[{e}]")
+    # the single-launch backward reproduces every gradient bit for bit
+    want = {k: v.clone() for k, v in g.items()}
+    for t in g.values():
+        t.view(torch.uint8).fill_(0xA5)
+    layer.sched = M.MOE_SCHED_SINGLE
+    g = layer.backward(x, torch.from_numpy(dout.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    for k in want:
+        assert torch.equal(want[k].view(torch.uint8), g[k].view(torch.uint8)), k
 
 
 def test_full_size_backward_mxfp8():

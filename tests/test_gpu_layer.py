@@ -181,6 +181,79 @@ def test_single_launch_barrier_expiry_is_reported_and_the_next_call_recovers():
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
 
+# the router's dX_r product contracts over E in whole 64-column steps, so the
+# single launch takes the router backward for E % 64 == 0
+SINGLE_CASES["router_e64"] = S.scaled(S.WORKLOADS["qwen3_235b_bf16_fwdbwd"], "router_e64", N=700, D=256, E=64,
+                                      K=4, H=192)
+BWD_SINGLE_CASES = [("tiny_bf16", False), ("qwen3_shape_small", False), ("dsv3_shape_small", False),
+                    ("ragged_e24", False), ("router_e64", True), ("router_bm128", True)]
+
+
+@pytest.mark.parametrize("name,router", BWD_SINGLE_CASES)
+def test_layer_bwd_single_launch_equals_staged(name, router):
+    """The single-launch backward (combine backward, both dgrads and all
+    weight gradients, the router backward and the fold in one persistent
+    launch) gives every gradient bitwise equal to the staged backward's,
+    whose parity with the oracle the tests below establish.  The gradients
+    are poisoned first.  Its forward is the staged one (any E)."""
+    wl = {**LAYER_CASES, **SINGLE_CASES}[name]
+    print(f"single-launch bwd {name} router={router}", flush=True)
+    inp = S.make_inputs(wl, 6)
+    dout = dev_bf16(inp.dout if inp.dout is not None else S.random_bf16((wl.N, wl.D), 6, 9))
+    w, _ = _weights(inp)
+    drop = dev(inp.drop) if inp.drop is not None else None
+    x = dev_bf16(inp.x)
+    want = M.MoeLayer(w, wl.N, wl.K, drop=drop, with_bwd=True, router_bwd=router)
+    want.forward(x)
+    gs = {k: v.clone() for k, v in want.backward(x, dout).items()}
+    one = M.MoeLayer(w, wl.N, wl.K, drop=drop, with_bwd=True, router_bwd=router)
+    one.forward(x)
+    one.sched = M.MOE_SCHED_SINGLE
+    for t in one.grads.values():
+        t.view(torch.uint8).fill_(0xA5)
+    g1 = one.backward(x, dout)
+    torch.cuda.synchronize()
+    assert int(host(one.saved["status"])[0]) == 0
+    assert set(gs) == set(g1)
+    for k in gs:
+        assert torch.equal(gs[k].view(torch.uint8), g1[k].view(torch.uint8)), k
+
+
+def test_single_launch_backward_with_aux_loss_and_barrier_expiry():
+    """The aux loss's gradient joins the router backward in the single launch
+    too (bitwise the staged result); and with barrier arrivals withheld every
+    barrier wait of the backward expires and is reported, after which the
+    next call is exact again."""
+    wl = SINGLE_CASES["router_e64"]
+    inp = S.make_inputs(wl, 7)
+    dout = dev_bf16(S.random_bf16((wl.N, wl.D), 7, 9))
+    w, _ = _weights(inp)
+    x = dev_bf16(inp.x)
+    want = M.MoeLayer(w, wl.N, wl.K, with_bwd=True, router_bwd=True, aux_alpha=0.01)
+    want.forward(x)
+    gs = {k: v.clone() for k, v in want.backward(x, dout, d_aux=1.5).items()}
+    one = M.MoeLayer(w, wl.N, wl.K, with_bwd=True, router_bwd=True, aux_alpha=0.01)
+    one.forward(x)
+    one.sched = M.MOE_SCHED_SINGLE
+    g1 = one.backward(x, dout, d_aux=1.5)
+    torch.cuda.synchronize()
+    for k in gs:
+        assert torch.equal(gs[k].view(torch.uint8), g1[k].view(torch.uint8)), k
+    print("single-launch bwd: forced barrier expiry", flush=True)
+    one.saved["status"].zero_()
+    one.ready_test_polls = 4
+    one.backward(x, dout, d_aux=1.5)
+    torch.cuda.synchronize()
+    assert int(host(one.saved["status"])[0]) == M.MOE_STATUS_WAIT_EXPIRED
+    one.ready_test_polls = 0
+    one.saved["status"].zero_()
+    g1 = one.backward(x, dout, d_aux=1.5)
+    torch.cuda.synchronize()
+    assert int(host(one.saved["status"])[0]) == 0
+    for k in gs:
+        assert torch.equal(gs[k].view(torch.uint8), g1[k].view(torch.uint8)), k
+
+
 @pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_shape_small", "dsv3_shape_small"])
 def test_layer_bwd_bf16(name):
     wl = LAYER_CASES[name]
