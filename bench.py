@@ -421,8 +421,15 @@ def _host_threads():
 EXTRA_WORKLOADS = ("mixtral_bf16", "qwen3_235b_bf16_fwdbwd", "dsv3_mxfp8")
 
 
+def single_launch_ok(wl, bwd):
+    """The single-launch layer's rules (bf16 routed experts; the tiled router,
+    16 <= E <= 512; D, H multiples of 64; with the router backward E % 64)."""
+    return (not wl.mxfp8 and 16 <= wl.E <= 512 and wl.D % 64 == 0 and wl.H % 64 == 0 and wl.K <= 32
+            and (not bwd or wl.E % 64 == 0))
+
+
 def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False,
-            mx_wgrad=False):
+            mx_wgrad=False, single=False):
     """Time `steps` steps of one workload (after `warmup`), inputs resident in
     HBM; returns the result dict of the JSON line (without cpu_baseline)."""
     bwd = wl.bwd or backward
@@ -479,7 +486,30 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    layer_ms = time_layer(layer) if (layer_call or shared_expert) else None
+    layer_ms = time_layer(layer) if (layer_call or shared_expert or single) else None
+    single_out = None
+    if single and single_launch_ok(wl, bwd):
+        # the same layer in one persistent launch per direction (outputs bitwise
+        # the staged launches'), timed call by call like layer_call_ms
+        lay_1 = M.MoeLayer(w, wl.N, wl.K, mxfp8=False, drop=drop, renorm=wl.renorm, with_bwd=bwd, router_bwd=bwd,
+                           sched=M.MOE_SCHED_SINGLE)
+        single_out = {"layer_fwd_ms": time_layer(lay_1), "staged_layer_fwd_ms": layer_ms}
+        if bwd:
+            def time_bwd(lay):
+                for _ in range(2):
+                    lay.backward(x, dout)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    lay.backward(x, dout)
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / steps
+            single_out["layer_bwd_ms"] = time_bwd(lay_1)
+            single_out["staged_layer_bwd_ms"] = time_bwd(layer)
+        single_out["note"] = ("moe_layer_fwd / moe_layer_bwd with MOE_SCHED_SINGLE: router to fold in one "
+                              "persistent launch per direction, grid barriers between its phases")
+        del lay_1
     shared = None
     if shared_expert:
         ws = shared_expert_weights(M, w, wl, seed, torch)
@@ -560,6 +590,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         out["layer_call_ms"] = layer_ms
     if shared is not None:
         out["shared_expert"] = shared
+    if single_out is not None:
+        out["single_launch"] = single_out
     del layer, st, x, w, drop, dout
     return out
 
@@ -567,7 +599,7 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
 def summary_of(r):
     """The keys of a non-headline workload's result kept in the JSON line."""
     keep = ("value", "unit", "ms_per_step", "fwd_ms", "dtype", "config", "roofline", "grouped_gemm", "dispatch",
-            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward")
+            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward", "single_launch")
     return {k: r[k] for k in keep if k in r}
 
 
@@ -650,7 +682,8 @@ def main(argv=None):
         del src, dst
 
     out = measure(M, torch, wl, inp, args.steps, args.warmup, args.seed, backward=args.backward,
-                  layer_call=args.layer_call, shared_expert=args.shared_expert, mx_wgrad=args.mx_wgrad)
+                  layer_call=args.layer_call, shared_expert=args.shared_expert, mx_wgrad=args.mx_wgrad,
+                  single=not args.headline_only)
     if not args.headline_only:
         # the other workloads of the same run, each its own step (parity cases
         # aside from the headline): keys only, the headline value is above
@@ -664,7 +697,7 @@ def main(argv=None):
                 (wl.N, wl.D, wl.E, wl.K, wl.H, wl.zipf_s, wl.p_drop)
             ix = inp if same_inputs else S.make_inputs(wx, args.seed)
             print(f"# {name}: inputs in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
-            r = measure(M, torch, wx, ix, args.steps, args.warmup, args.seed)
+            r = measure(M, torch, wx, ix, args.steps, args.warmup, args.seed, single=True)
             extra[name] = summary_of(r)
             print(f"# {name}: {extra[name]['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
             del ix
