@@ -610,13 +610,13 @@ struct SingleBwdParams {
 constexpr int kSbLds = kDgLds > WgTile::LDS ? kDgLds : WgTile::LDS;
 static_assert(kSbLds >= 2 * 4 * router::kRbMaxE * 4, "the router backward's LDS rows");
 
-// thread 0 of each workgroup: after the workgroup's stores, add to *bar and
-// wait (bounded) until every workgroup has; false if the wait expired
+// after the workgroup's stores: thread 0 adds to *bar with an agent-scope
+// release and waits (bounded, acquire loads) until every workgroup has;
+// false if the wait expired
 __device__ __forceinline__ bool bar_sync(const SingleBwdParams& p, int32_t* bar, int* s_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
+  __syncthreads();   // the workgroup's stores precede thread 0's release
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, p.publish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(bar, p.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     bool ok = false;
     for (int it = 0; it < p.polls && !ok; ++it) {
       ok = __hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= (int)gridDim.x;
@@ -625,10 +625,8 @@ __device__ __forceinline__ bool bar_sync(const SingleBwdParams& p, int32_t* bar,
     if (!ok && p.status) atomicOr(p.status, 1);
     *s_flag = ok;
   }
-  __syncthreads();
-  const bool ok = *s_flag != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
+  __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+  return *s_flag != 0;
 }
 
 __global__ __launch_bounds__(512) void layer_bwd_single_kernel(SingleBwdParams p) {

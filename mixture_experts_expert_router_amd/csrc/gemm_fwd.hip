@@ -427,8 +427,12 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
 //      (expert, row block) has stored H.
 // Every wait is on items claimed earlier by running workgroups, and those
 // never wait on later items, so the queue drains whatever the grid size.
-// Writers publish with an agent-scope release (fence, then atomic); readers
-// acquire before touching the data.  Waits are bounded: a wait that expires
+// A writer workgroup ends its stores with a workgroup barrier, then its
+// thread 0 publishes with an agent-scope release atomic (the release covers
+// the whole workgroup's stores, which the barrier ordered before it); a
+// reader's thread 0 waits with agent-scope acquire loads and a workgroup
+// barrier orders the other threads' loads after that acquire.  One release
+// per published item, not one per wave: each is a write-back of the L2.  Waits are bounded: a wait that expires
 // or-s MOE_STATUS_WAIT_EXPIRED into the caller's status word and the item that
 // waited is skipped (no load, no store), so no wave can hang and nothing is
 // computed from unpublished data.
@@ -519,8 +523,6 @@ __device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* sme
   epilogue<C>(p, it, acc);
 }
 
-__device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // The fold after the fused queue (single-launch layer): items of 8 tokens, a
 // wave per token.  Every workgroup publishes once, when it first claims past
@@ -558,17 +560,15 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
       if (!fold) break;
       if (!passed) {
         passed = true;
-        release_fence();
-        __syncthreads();
+        __syncthreads();   // the workgroup's stores precede thread 0's release below
         if (tid == 0)
           __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (item >= ND + N1 + N2 + NF) break;
       // ---- fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] ----------------------
       if (tid == 0) s_info[3] = wait_ge(f, fold->passed, (int)gridDim.x);
-      __syncthreads();
+      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
       if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      acquire_fence();
       const int t = __builtin_amdgcn_readfirstlane((item - ND - N1 - N2) * 8 + wave);
       if (t < fold->N)
         perm::combine_token<true>(t, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K, fold->out, nullptr,
@@ -601,8 +601,7 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
           }
         }
       }
-      release_fence();
-      __syncthreads();
+      __syncthreads();   // the workgroup's stores precede thread 0's release below
       if (tid == 0) {
         const int m = m1 - m0;
         // acquire-release: the workgroup that completes the expert acquires
@@ -628,9 +627,8 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
         s_info[1] = e;
         s_info[2] = cum;
       }
-      __syncthreads();
+      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
       if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      acquire_fence();
       const int e = s_info[1], cum = s_info[2];
       const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
       const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
@@ -638,8 +636,7 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
       Item it{e, m0 + mb * bm, m1, n_t * BigTile<true>::NCOL, is_big(m1 - m0), true};
       if (it.big) run_plain<BigTile<true>>(f.g1, smem, lds0, it);
       else run_plain<SmallTile<true>>(f.g1, smem, lds0, it);
-      release_fence();
-      __syncthreads();
+      __syncthreads();   // the workgroup's stores precede thread 0's release below
       if (tid == 0)
         __hip_atomic_fetch_add(st + st_g1_done(E) + cum + mb, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -658,9 +655,8 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
         s_info[1] = e;
         s_info[2] = cum;
       }
-      __syncthreads();
+      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
       if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      acquire_fence();
       const int e = s_info[1], cum = s_info[2];
       const int m0 = f.g2.offsets[e], m1 = f.g2.offsets[e + 1];
       const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
@@ -772,16 +768,13 @@ struct SingleFwdParams {
 
 // every workgroup: after its stores, add to *bar and wait until all have
 __device__ __forceinline__ bool grid_sync(const FusedParams& f, int32_t* bar, int* s_info) {
-  release_fence();
-  __syncthreads();
+  __syncthreads();   // the workgroup's stores precede thread 0's release
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, f.publish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(bar, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     s_info[3] = wait_ge(f, bar, (int)gridDim.x);
   }
-  __syncthreads();
-  const bool ok = s_info[3] != 0;
-  acquire_fence();
-  return ok;
+  __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+  return s_info[3] != 0;
 }
 
 template <int NPL>
