@@ -523,6 +523,20 @@ __device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* sme
   epilogue<C>(p, it, acc);
 }
 
+// A row block of the fused queue on the tile class the staged launches give
+// it: 256-row tiles for a large expert's row blocks, except a last one of at
+// most 128 rows, which (like every small expert's single block) takes the
+// smallest class that holds it.  Every class accumulates the same steps in
+// the same order, so the result is the same.
+template <bool DUAL>
+__device__ __forceinline__ void run_class(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
+  const int left = it.m1 - it.m_start;
+  if (it.big && left > kSmallBM) run_plain<BigTile<DUAL>>(p, smem, lds0, it);
+  else if (left <= kTiny32Rows) run_plain<Tiny32Tile<DUAL, false>>(p, smem, lds0, it);
+  else if (left <= kTinyRows) run_plain<TinyTile<DUAL>>(p, smem, lds0, it);
+  else run_plain<SmallTile<DUAL>>(p, smem, lds0, it);
+}
+
 
 // The fold after the fused queue (single-launch layer): items of 8 tokens, a
 // wave per token.  Every workgroup publishes once, when it first claims past
@@ -633,9 +647,7 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
       const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
       const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
       const int w = j - cum * f.nt1, n_t = w / nmb, mb = w - n_t * nmb;
-      Item it{e, m0 + mb * bm, m1, n_t * BigTile<true>::NCOL, is_big(m1 - m0), true};
-      if (it.big) run_plain<BigTile<true>>(f.g1, smem, lds0, it);
-      else run_plain<SmallTile<true>>(f.g1, smem, lds0, it);
+      run_class<true>(f.g1, smem, lds0, Item{e, m0 + mb * bm, m1, n_t * BigTile<true>::NCOL, is_big(m1 - m0), true});
       __syncthreads();   // the workgroup's stores precede thread 0's release below
       if (tid == 0)
         __hip_atomic_fetch_add(st + st_g1_done(E) + cum + mb, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -661,9 +673,7 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
       const int m0 = f.g2.offsets[e], m1 = f.g2.offsets[e + 1];
       const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
       const int w = j - cum * f.nt2, n_t = w / nmb, mb = w - n_t * nmb;
-      Item it{e, m0 + mb * bm, m1, n_t * BigTile<false>::NCOL, is_big(m1 - m0), true};
-      if (it.big) run_plain<BigTile<false>>(f.g2, smem, lds0, it);
-      else run_plain<SmallTile<false>>(f.g2, smem, lds0, it);
+      run_class<false>(f.g2, smem, lds0, Item{e, m0 + mb * bm, m1, n_t * BigTile<false>::NCOL, is_big(m1 - m0), true});
     }
   }
 }
