@@ -807,11 +807,11 @@ hipError_t launch_gemm_dgrad_fast(const GemmBwd& b, int32_t* ws, hipStream_t s) 
 }
 
 // wgrad: both output dims multiples of 16 (at least 16), 16-byte aligned
-// operands, every row offset inside an expert's segment within 32 bits
+// operands, a contraction step's 64 rows within 32-bit offsets
 bool gemm_wgrad_fast_ok(const GemmBwd& b, const void* dc, const void* db) {
   if (b.n_dim % 16 || b.k_dim % 16 || b.n_dim < 16 || b.k_dim < 16) return false;
   const int64_t w = b.n_dim > b.k_dim ? b.n_dim : b.k_dim;
-  if ((b.rows_cap + 64) * w * 2 >= (int64_t(1) << 31)) return false;
+  if (65 * w * 2 >= (int64_t(1) << 31)) return false;
   return aligned16(dc) && aligned16(b.a) && aligned16(db);
 }
 

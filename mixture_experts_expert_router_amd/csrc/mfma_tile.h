@@ -410,12 +410,17 @@ __device__ __forceinline__ void issue_step_b_at(uint32_t lds0, const SrcB<C>& sr
   const int kk = second ? kt - src.nk1 : kt;
   const uint8_t* a = second ? src.a[1] : src.a[0];
   const uint8_t* b = second ? src.b[1] : src.b[0];
+  // k-major operands: the step's first row in the 64-bit base, so a lane's
+  // 32-bit offset spans only the step's 64 rows (an expert's rows may span
+  // more than 4 GiB of k-major bytes)
+  const uint8_t* ak = C::AT ? uniform_ptr(a + (int64_t)kk * 64 * src.a_rs) : a;
+  const uint8_t* bk = C::BT ? uniform_ptr(b + (int64_t)kk * 64 * src.b_rs) : b;
 #pragma unroll
   for (int q = 0; q < C::A_INS; ++q) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(wave_a + q * 1024u);
     if constexpr (C::AT) {
-      const int row = min(kk * 64 + trow_of(wave * C::A_INS + q), src.a_lim);
-      lds_dma16(a, (uint32_t)row * (uint32_t)src.a_rs + src.a_off[q], dst);
+      const int row = min(trow_of(wave * C::A_INS + q), src.a_lim - kk * 64);
+      lds_dma16(ak, (uint32_t)row * (uint32_t)src.a_rs + src.a_off[q], dst);
     } else {
       lds_dma16(a + (int64_t)kk * kRB, src.a_off[q], dst);
     }
@@ -424,8 +429,8 @@ __device__ __forceinline__ void issue_step_b_at(uint32_t lds0, const SrcB<C>& sr
   for (int q = 0; q < C::B_INS; ++q) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(wave_b + q * 1024u);
     if constexpr (C::BT) {
-      const int row = min(kk * 64 + trow_of(wave * C::B_INS + q), src.b_lim);
-      lds_dma16(b, (uint32_t)row * (uint32_t)src.b_rs + src.b_off[q], dst);
+      const int row = min(trow_of(wave * C::B_INS + q), src.b_lim - kk * 64);
+      lds_dma16(bk, (uint32_t)row * (uint32_t)src.b_rs + src.b_off[q], dst);
     } else {
       lds_dma16(b + (int64_t)kk * kRB, src.b_off[q], dst);
     }

@@ -383,3 +383,28 @@ def test_full_size_backward_mxfp8():
             assert err <= tol, (name, int(e), err)
     for e in np.nonzero(c == 0)[0][:8]:
         assert not bits(g["dw_down"][int(e)]).any()
+
+
+def test_wgrad_of_an_expert_past_32_bit_row_offsets():
+    """One expert whose k-major operand spans more than 2 GiB (70 000 rows of
+    a 16 384-wide dC): the persistent wgrad keeps each contraction step's 64
+    rows in 32-bit offsets from a 64-bit step base, so this shape runs on it
+    rather than on a slower fallback.  Sampled output rows of dW = dC^T A are
+    compared with the oracle's exact sums over all 70 000 rows."""
+    rows, M_out, N_out = 70000, 16384, 16
+    print(f"wgrad: {rows} rows x {M_out} (dC bytes {rows * M_out * 2 / 2**30:.2f} GiB)", flush=True)
+    rng = np.random.default_rng(11)
+    dc_bits = np.empty((rows, M_out), np.uint16)
+    for r0 in range(0, rows, 10000):
+        dc_bits[r0:r0 + 10000] = S.f32_to_bf16_bits(rng.standard_normal((min(10000, rows - r0), M_out),
+                                                                        dtype=np.float32))
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((rows, N_out), dtype=np.float32))
+    dc = torch.from_numpy(dc_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    a = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    offs = torch.tensor([0, rows], dtype=torch.int32, device="cuda")
+    g = M.grouped_gemm_bwd(offs, dc, a=a, dgrad=False, wgrad=True)
+    torch.cuda.synchronize()
+    db = vals(g["db0"])[0]                       # [M_out][N_out]
+    ms = np.sort(rng.choice(M_out, 48, replace=False))
+    ref = O.values(dc_bits[:, ms]).T @ O.values(a_bits)
+    assert_bf16_close(db[ms], ref, "dW rows")
