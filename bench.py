@@ -624,6 +624,10 @@ def main(argv=None):
     ap.add_argument("--shared-expert", action="store_true",
                     help="also time moe_layer_fwd with one shared expert (N(0,1/D), N(0,1/H) weights) in the same "
                          "grouped-GEMM launches, beside the routed-only layer call")
+    ap.add_argument("--single-only", action="store_true",
+                    help="run only the workload's single-launch layer (MOE_SCHED_SINGLE: forward, and backward "
+                         "with the router backward for a fwd+bwd workload) warmup + steps times and print its "
+                         "times (for a kernel trace of that launch)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
                          "that calibrates the HBM byte counters of a profiler run")
@@ -670,6 +674,36 @@ def main(argv=None):
     t0 = time.perf_counter()
     inp = S.make_inputs(wl, args.seed)
     print(f"# inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    if args.single_only:
+        bwd = wl.bwd or args.backward
+        if not single_launch_ok(wl, bwd):
+            print(f"{wl.name}: outside the single-launch layer's rules", file=sys.stderr)
+            return 2
+        x, w, drop = device_inputs(M, inp, False, torch, backward=bwd)
+        dout_bits = inp.dout if inp.dout is not None else S.random_bf16((wl.N, wl.D), args.seed, 9)
+        dout = torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
+        lay = M.MoeLayer(w, wl.N, wl.K, drop=drop, renorm=wl.renorm, with_bwd=bwd, router_bwd=bwd,
+                         sched=M.MOE_SCHED_SINGLE)
+        ev = []
+        for i in range(args.warmup + args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            lay.forward(x)
+            e[1].record()
+            if bwd:
+                lay.backward(x, dout)
+            e[2].record()
+            if i >= args.warmup:
+                ev.append(e)
+        torch.cuda.synchronize()
+        assert int(lay.saved["status"].item()) == 0
+        res = {"workload": wl.name, "sched": "single", "steps": args.steps,
+               "fwd_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))}
+        if bwd:
+            res["bwd_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        print(json.dumps(res), flush=True)
+        return 0
 
     if args.copy_probe:
         n = args.copy_probe << 20
