@@ -203,6 +203,50 @@ def mfma_report(run_dir, cus=256, xcds=8):
     return rows
 
 
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS",
+                  "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def stall_report(run_dir, cus=256, xcds=8):
+    """Where the GEMM kernels' waves spend their cycles, from one rocprofv3
+    --pmc run with STALL_COUNTERS.  SQ_WAVE_CYCLES, SQ_WAIT_ANY (waiting on a
+    dependency: s_waitcnt or a barrier), SQ_WAIT_INST_ANY (ready but not
+    issued), SQ_WAIT_INST_LDS and the SQ_ACTIVE_INST_* counters share one unit
+    (wave quad-cycles), so each is reported as a share of SQ_WAVE_CYCLES; the
+    shares overlap and need not sum to 100.  MFMA busy is per SIMD, as in
+    mfma_report.  Averaged over each kernel's dispatches."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    disp = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault((f, r["Dispatch_Id"]), {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) -
+                                                              int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    keys = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+            "SQ_ACTIVE_INST_VMEM")
+    per = {}
+    for d in disp.values():
+        wc = d.get("SQ_WAVE_CYCLES", 0.0)
+        if "gemm" not in d["name"] or not wc or not d.get("GRBM_GUI_ACTIVE"):
+            continue
+        gui = d["GRBM_GUI_ACTIVE"] / xcds
+        v = [100.0 * d.get(k, 0.0) / wc for k in keys]
+        v.append(100.0 * d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * cus * 4))
+        v.append(d["ns"] / 1e3)
+        per.setdefault(d["name"], []).append(v)
+    rows = []
+    for name, vs in per.items():
+        n = len(vs)
+        m = [sum(x[i] for x in vs) / n for i in range(len(vs[0]))]
+        rows.append(dict(kernel=name, dispatches=n, wait_dep=m[0], wait_issue=m[1], active=m[2], lds_active=m[3],
+                         lds_issue_wait=m[4], vmem_active=m[5], mfma_busy=m[6], us=m[7]))
+    rows.sort(key=lambda r: -r["us"] * r["dispatches"])
+    return rows
+
+
 def recorded_traffic(workload, seed=0):
     """Bytes per launch of GEMM1 from the committed counter summary of this
     workload, or None when there is none, the GEMM sources changed since, or
@@ -634,6 +678,9 @@ def main(argv=None):
     ap.add_argument("--pmc-mfma-report", metavar="DIR",
                     help="print MFMA utilisation per GEMM kernel from one rocprofv3 --pmc run with the counters "
                          + " ".join(MFMA_COUNTERS) + ", and exit")
+    ap.add_argument("--pmc-stall-report", metavar="DIR",
+                    help="print where each GEMM kernel's waves spend their cycles from one rocprofv3 --pmc run "
+                         "with the counters " + " ".join(STALL_COUNTERS) + ", and exit")
     ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this script with --copy-probe, and exit")
@@ -646,6 +693,16 @@ def main(argv=None):
         for r in mfma_report(args.pmc_mfma_report):
             print(f"| `{r['kernel'][:100]}` | {r['dispatches']} | {r['us']:.1f} | {r['ghz']:.2f} | {r['busy_pct']:.1f} | "
                   f"{r['tflops']:.0f} ({r['dtype']}) | {r['pct_peak']:.1f} |")
+        return 0
+
+    if args.pmc_stall_report:
+        print("| kernel | dispatches | avg us (counted run) | dependency wait % | issue wait % | active % "
+              "| LDS active % | LDS issue wait % | VMEM active % | MFMA busy % |")
+        print("|---|---|---|---|---|---|---|---|---|---|")
+        for r in stall_report(args.pmc_stall_report):
+            print(f"| `{r['kernel'][:100]}` | {r['dispatches']} | {r['us']:.1f} | {r['wait_dep']:.1f} | "
+                  f"{r['wait_issue']:.1f} | {r['active']:.1f} | {r['lds_active']:.1f} | {r['lds_issue_wait']:.1f} | "
+                  f"{r['vmem_active']:.1f} | {r['mfma_busy']:.1f} |")
         return 0
 
     if args.pmc_report:
