@@ -248,17 +248,19 @@ __global__ __launch_bounds__(kPadThreads) void zero_padding_kernel(const int32_t
   }
 }
 
-// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), a wave per token
+// combine: out[t] = bf16(sum_k w[t,k] * y[dst[t,k]]), a wave per segment of
+// a token row (nseg segments a row)
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ dst_rows,
                                                       const float* __restrict__ weight, int N,
                                                       int D, int K, uint16_t* __restrict__ out,
                                                       const uint16_t* __restrict__ addend,
-                                                      const int32_t* __restrict__ shared_row0) {
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+                                                      const int32_t* __restrict__ shared_row0, int nseg) {
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = w / nseg;
   if (t >= N) return;
-  perm::combine_token<WEIGHTED>(t, y, dst_rows, weight, D, K, out, addend, shared_row0);
+  perm::combine_seg<WEIGHTED>(t, w - t * nseg, nseg, y, dst_rows, weight, D, K, out, addend, shared_row0);
 }
 
 // combine backward, a wave per token (QUANT: dY_d also quantized row-wise)
@@ -435,14 +437,14 @@ hipError_t launch_combine(const void* y, const int32_t* dst_rows, const float* w
                           int64_t D, int64_t K, void* out, hipStream_t s, const void* addend,
                           const int32_t* shared_row0) {
   if (N == 0) return hipSuccess;
+  const int nseg = perm::combine_segs((int)(D >> 3));
+  const unsigned grid = waves_grid(N * nseg);
   if (weight)
-    combine_kernel<true><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, weight, (int)N,
-                                                      (int)D, (int)K, (uint16_t*)out, (const uint16_t*)addend,
-                                                      shared_row0);
+    combine_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)y, dst_rows, weight, (int)N, (int)D, (int)K,
+                                             (uint16_t*)out, (const uint16_t*)addend, shared_row0, nseg);
   else
-    combine_kernel<false><<<waves_grid(N), 256, 0, s>>>((const uint16_t*)y, dst_rows, nullptr,
-                                                       (int)N, (int)D, (int)K, (uint16_t*)out,
-                                                       (const uint16_t*)addend, shared_row0);
+    combine_kernel<false><<<grid, 256, 0, s>>>((const uint16_t*)y, dst_rows, nullptr, (int)N, (int)D, (int)K,
+                                              (uint16_t*)out, (const uint16_t*)addend, shared_row0, nseg);
   return hipGetLastError();
 }
 

@@ -22,81 +22,101 @@ __device__ __forceinline__ uint32_t quant4(const float* f, int e) {
   return e4m3x4(f[0], f[1], f[2], f[3], e);
 }
 
-// The fold of token t (wave-uniform) by one wave: out[t] = bf16(sum over k of
-// w[t,k] y[dst[t,k]] (+ addend[t])), fp32 fmaf in ascending k.  The rows of
-// up to 8 routes are loaded before any of them is added, so a lane keeps 16
-// loads in flight instead of waiting on one route at a time.  The gathered
-// rows and the output are touched once: non-temporal accesses.
+// The fold (combine) of token rows: out[t] = bf16(sum over k of w[t,k]
+// y[dst[t,k]] (+ addend[t])), fp32 fmaf in ascending k, the shared expert's
+// row (weight 1) last.  A row of nvec 16-byte vectors is cut into
+// combine_segs(nvec) segments of at most kSegV vectors per lane; one wave
+// folds one segment, reading each route's part of the row as one long run
+// (measured: 7 KB runs of two routes at a time keep HBM busier than 2 KB runs
+// of eight routes) with the next route's run in flight while one is added.
+// The gathered rows and the output are touched once: non-temporal accesses.
+constexpr int kSegV = 7;
+__device__ __host__ __forceinline__ int combine_segs(int nvec) {
+  return (nvec + kSegV * kWave - 1) / (kSegV * kWave);
+}
+
+template <bool WEIGHTED>
+__device__ __forceinline__ void combine_seg(int t, int seg, int nseg, const uint16_t* __restrict__ y,
+                                            const int32_t* __restrict__ dst_rows,
+                                            const float* __restrict__ weight, int D, int K,
+                                            uint16_t* __restrict__ out, const uint16_t* __restrict__ addend,
+                                            const int32_t* __restrict__ shared_row0) {
+  constexpr int KC = 2;
+  const int lane = threadIdx.x & 63;
+  const int nvec = D >> 3;
+  const int vl = (nvec + nseg * kWave - 1) / (nseg * kWave);   // vectors per lane, at most kSegV
+  const int vb = seg * vl * kWave + lane;                      // this lane's first vector
+  // route K (when there is a shared expert): its row of this token, weight 1
+  const int KK = K + (shared_row0 ? 1 : 0);
+  const int srow = shared_row0 ? *shared_row0 + t : -1;
+  float acc[kSegV][8];
+#pragma unroll
+  for (int j = 0; j < kSegV; ++j) {
+    const int v = vb + j * kWave;
+    const uint4 q = (addend && j < vl && v < nvec) ? ldg16(addend + (int64_t)t * D + v * 8) : make_uint4(0, 0, 0, 0);
+    acc[j][0] = bf16lo(q.x);
+    acc[j][1] = bf16hi(q.x);
+    acc[j][2] = bf16lo(q.y);
+    acc[j][3] = bf16hi(q.y);
+    acc[j][4] = bf16lo(q.z);
+    acc[j][5] = bf16hi(q.z);
+    acc[j][6] = bf16lo(q.w);
+    acc[j][7] = bf16hi(q.w);
+  }
+  for (int k0 = 0; k0 < KK; k0 += KC) {
+    uint4 r[KC][kSegV];
+    int dk[KC];
+    float wk[KC];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const int k = k0 + kk;
+      dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
+      wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
+      const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
+#pragma unroll
+      for (int j = 0; j < kSegV; ++j) {
+        const int v = vb + j * kWave;
+        r[kk][j] = (dk[kk] >= 0 && j < vl && v < nvec) ? ldg16_nt(src + v * 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      if (dk[kk] < 0) continue;
+      const float w = wk[kk];
+#pragma unroll
+      for (int j = 0; j < kSegV; ++j) {
+        const uint4 q = r[kk][j];
+        acc[j][0] = fmaf(w, bf16lo(q.x), acc[j][0]);
+        acc[j][1] = fmaf(w, bf16hi(q.x), acc[j][1]);
+        acc[j][2] = fmaf(w, bf16lo(q.y), acc[j][2]);
+        acc[j][3] = fmaf(w, bf16hi(q.y), acc[j][3]);
+        acc[j][4] = fmaf(w, bf16lo(q.z), acc[j][4]);
+        acc[j][5] = fmaf(w, bf16hi(q.z), acc[j][5]);
+        acc[j][6] = fmaf(w, bf16lo(q.w), acc[j][6]);
+        acc[j][7] = fmaf(w, bf16hi(q.w), acc[j][7]);
+      }
+    }
+  }
+  uint16_t* o = out + (int64_t)t * D;
+#pragma unroll
+  for (int j = 0; j < kSegV; ++j) {
+    const int v = vb + j * kWave;
+    if (j < vl && v < nvec)
+      stg16_nt(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
+                                     pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
+  }
+}
+
+// The fold of token t (wave-uniform) by one wave, segment after segment.
 template <bool WEIGHTED>
 __device__ __forceinline__ void combine_token(int t, const uint16_t* __restrict__ y,
                                               const int32_t* __restrict__ dst_rows,
                                               const float* __restrict__ weight, int D, int K,
                                               uint16_t* __restrict__ out, const uint16_t* __restrict__ addend,
                                               const int32_t* __restrict__ shared_row0) {
-  constexpr int VPL = 2, KCH = 8;
-  const int lane = threadIdx.x & 63;
-  const int nvec = D >> 3;
-  // route K (when there is a shared expert): its row of this token, weight 1
-  const int KK = K + (shared_row0 ? 1 : 0);
-  const int srow = shared_row0 ? *shared_row0 + t : -1;
-  for (int v0 = 0; v0 < nvec; v0 += kWave * VPL) {
-    float acc[VPL][8];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + lane + j * kWave;
-      const uint4 q = (addend && v < nvec) ? ldg16(addend + (int64_t)t * D + v * 8) : make_uint4(0, 0, 0, 0);
-      acc[j][0] = bf16lo(q.x);
-      acc[j][1] = bf16hi(q.x);
-      acc[j][2] = bf16lo(q.y);
-      acc[j][3] = bf16hi(q.y);
-      acc[j][4] = bf16lo(q.z);
-      acc[j][5] = bf16hi(q.z);
-      acc[j][6] = bf16lo(q.w);
-      acc[j][7] = bf16hi(q.w);
-    }
-    for (int kb = 0; kb < KK; kb += KCH) {
-      uint4 r[KCH][VPL];
-      int dk[KCH];
-      float wk[KCH];
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const int k = kb + kk;
-        dk[kk] = k < K ? dst_rows[(int64_t)t * K + k] : (k == K ? srow : -1);
-        wk[kk] = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
-        const uint16_t* src = y + (int64_t)(dk[kk] < 0 ? 0 : dk[kk]) * D;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int v = v0 + lane + j * kWave;
-          r[kk][j] = (dk[kk] >= 0 && v < nvec) ? ldg16_nt(src + v * 8) : make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        if (dk[kk] < 0) continue;
-        const float w = wk[kk];
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const uint4 q = r[kk][j];
-          acc[j][0] = fmaf(w, bf16lo(q.x), acc[j][0]);
-          acc[j][1] = fmaf(w, bf16hi(q.x), acc[j][1]);
-          acc[j][2] = fmaf(w, bf16lo(q.y), acc[j][2]);
-          acc[j][3] = fmaf(w, bf16hi(q.y), acc[j][3]);
-          acc[j][4] = fmaf(w, bf16lo(q.z), acc[j][4]);
-          acc[j][5] = fmaf(w, bf16hi(q.z), acc[j][5]);
-          acc[j][6] = fmaf(w, bf16lo(q.w), acc[j][6]);
-          acc[j][7] = fmaf(w, bf16hi(q.w), acc[j][7]);
-        }
-      }
-    }
-    uint16_t* o = out + (int64_t)t * D;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + lane + j * kWave;
-      if (v < nvec)
-        stg16_nt(o + v * 8, make_uint4(pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3]),
-                                       pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])));
-    }
-  }
+  const int nseg = combine_segs(D >> 3);
+  for (int s = 0; s < nseg; ++s)
+    combine_seg<WEIGHTED>(t, s, nseg, y, dst_rows, weight, D, K, out, addend, shared_row0);
 }
 
 // combine backward: dyd[dst] = bf16(w * dout[t]); dprob[t,k] = <dout[t], y[dst]>
