@@ -185,8 +185,11 @@ def test_dispatch_mxfp8_bit_exact(N, D, E, K):
 
 
 # --------------------------------------------------------------- combine ----
+# D = 3584 is one full row segment (7 vectors a lane), 3592 one vector more
+# (two segments of 4), 4104 a ragged second segment, 8 a single lane
 @pytest.mark.parametrize("N,D,E,K,pdrop", [(256, 128, 8, 2, 0.0), (300, 7168, 64, 8, 0.05),
-                                           (97, 8, 4, 2, 0.3), (200, 4104, 16, 4, 1.0)])
+                                           (97, 8, 4, 2, 0.3), (200, 4104, 16, 4, 1.0),
+                                           (150, 3584, 16, 3, 0.1), (150, 3592, 16, 9, 0.1)])
 def test_combine_and_unweighted(N, D, E, K, pdrop):
     print(f"combine N={N} D={D} E={E} K={K} drop={pdrop}", flush=True)
     wl, inp, idx, prob, c, o, d, r = _routed(N, D, E, K, 1, 13, pdrop=pdrop)
