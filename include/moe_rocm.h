@@ -311,18 +311,20 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * gradient takes H = bf16(silu(G) U) recomputed from the saved bf16 G and U
  * instead of the dequantized h_q; h_s is then ignored. */
 #define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
-#define MOE_SCHED_READY 1   /* bf16: one persistent launch; GEMM1 tiles claimed in
-                               the order dispatch finishes experts, GEMM2 tiles
-                               gated on their GEMM1 row blocks.  MOE_ERR_UNSUPPORTED
-                               for MXFP8, a shared expert, or D, H off the rule
+#define MOE_SCHED_READY 1   /* bf16: dispatch, GEMM1 and GEMM2 in one persistent
+                               launch: GEMM1 tiles (in the staged launch's queue
+                               order) gated on the dispatch, GEMM2 tiles gated on
+                               their GEMM1 row blocks, so GEMM2 starts while
+                               GEMM1's last tiles run.  MOE_ERR_UNSUPPORTED for
+                               MXFP8, a shared expert, or D, H off the rule
                                D % 64 == 0 and H % 64 == 0                       */
 /* MOE_SCHED_SINGLE (KOSMOS section 3.3, Figure 6: one launch from route to
  * fold): the whole bf16 layer forward in one persistent launch, after a
  * one-workgroup reset of its barrier words.  Its workgroups (one per CU) run
  * the router tiles, then the logits, softmax and top-K per chunk of tokens,
  * the histogram scan and plans (one workgroup), the scatter, each step ended
- * by a grid barrier, then the MOE_SCHED_READY queue (dispatch, GEMM1 by
- * readiness, GEMM2 gated on GEMM1 row blocks) followed by the fold, which
+ * by a grid barrier, then the MOE_SCHED_READY queue (dispatch, GEMM1 after
+ * it, GEMM2 gated on GEMM1 row blocks) followed by the fold, which
  * waits until every workgroup has stored its GEMM2 tiles.  Every output is
  * bitwise the staged forward's.  Same rules as MOE_SCHED_READY, and also the
  * tiled router (D % 64 == 0, 16 <= E <= 512), K <= 32, no grouped top-K and

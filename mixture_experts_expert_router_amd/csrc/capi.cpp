@@ -623,9 +623,9 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (single) {
     // router, route, dispatch, GEMM1, GEMM2 and the fold in one persistent launch
     moe::LayerFwdSingle one{};
-    one.x = moe::ExpertsFwd{d.E,     d.K,      d.D,      d.H,   rc,    d.N,   sv->offsets,
-                            sv->row_route, a->x, a->w_gate, a->w_up, a->w_down, sv->xd, sv->g,
-                            sv->u,   sv->h,    sv->y,    sv->status, a->ready_test_polls};
+    one.x = moe::ExpertsFwd{d.E,     d.K,      d.D,      d.H,    rc,     d.N,     sv->offsets,
+                            sv->row_route, sv->dst_rows, a->x, a->w_gate, a->w_up, a->w_down, sv->xd,
+                            sv->g,   sv->u,    sv->h,    sv->y,  sv->status, a->ready_test_polls};
     one.x_tokens = a->x;
     one.w_r = a->w_r;
     one.bias = a->bias;
@@ -660,8 +660,9 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     if (e == hipSuccess) e = gemm_fwd_mxfp8(g2, table, s);
   } else if (ready) {
     // dispatch, GEMM1 and GEMM2 in one persistent launch scheduled by readiness
-    moe::ExpertsFwd xf{d.E, d.K, d.D, d.H, rc, d.N, sv->offsets, sv->row_route, a->x, a->w_gate, a->w_up,
-                       a->w_down, sv->xd, sv->g, sv->u, sv->h, sv->y, sv->status, a->ready_test_polls};
+    moe::ExpertsFwd xf{d.E,     d.K,        d.D,   d.H,   rc,    d.N,   sv->offsets, sv->row_route,
+                       sv->dst_rows, a->x, a->w_gate, a->w_up, a->w_down, sv->xd, sv->g, sv->u,
+                       sv->h,   sv->y,      sv->status, a->ready_test_polls};
     if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
   } else {
     if (e == hipSuccess)

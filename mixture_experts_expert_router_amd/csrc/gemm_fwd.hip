@@ -414,38 +414,48 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Fused expert forward: dispatch -> GEMM1 -> GEMM2 in one persistent launch,
-// scheduled by data readiness (KOSMOS section 3.1.1 and section 3.3.1 steps
-// 3-4, on one GPU).  One queue, claimed in order:
-//   1. dispatch items: (expert, chunk of kDispRows rows); each gathers its
-//      rows from the token rows (row_route) into X_d.  The workgroup that
-//      finishes an expert's last chunk appends the expert to the ready list
-//      with one 64-bit atomic that returns both its position and the number
-//      of row blocks of all experts appended before it;
-//   2. GEMM1 items, expert by expert in ready order (the order dispatch
-//      finished them): each waits until its position is published;
-//   3. GEMM2 items, same order; each waits until every GEMM1 n-tile of its
-//      (expert, row block) has stored H.
-// Every wait is on items claimed earlier by running workgroups, and those
-// never wait on later items, so the queue drains whatever the grid size.
+// each tile gated on data readiness (KOSMOS section 3.1.1 and section 3.3.1
+// steps 3-4, on one GPU).  A workgroup runs, in order:
+//   1. its share of the dispatch: each token row read once and written to
+//      its routes' rows of X_d (as the dispatch launch does), then one
+//      release adding the share to a count;
+//   2. GEMM1 tiles from the staged launch's per-XCD queues, in its order
+//      (the two tile classes interleaved in proportion to their work,
+//      super-blocks of neighbouring tiles on one XCD's L2); a workgroup's
+//      first tile waits until every workgroup's share is counted;
+//   3. GEMM2 tiles the same way (a plan of their own); each waits until
+//      every GEMM1 n-tile of its (expert, row block) has stored H, so GEMM2
+//      starts on the row blocks GEMM1 finished while its last tiles run.
+// The dispatch shares never wait, and a workgroup goes from GEMM1 to GEMM2
+// when its claims come back empty, so every GEMM1 tile is claimed, by a
+// running workgroup, before any GEMM2 tile: items only wait on earlier
+// steps, and the queue drains whatever the grid size.  On one GPU the rows
+// of an expert come from tokens all over the batch, so an expert is complete
+// only when nearly the whole dispatch is.  Two per-expert readiness orders
+// were measured slower than this (DeepSeek-V3 bf16 forward 5.10-5.42 ms
+// against 4.3 here): GEMM tiles claimed in the order dispatch completed the
+// experts gave phases of only weight-streaming and of only MFMA-bound tiles
+// and lost the per-XCD L2 sharing, and an expert-major gather (a wave per
+// X_d row) read each token row K times.
 // A writer workgroup ends its stores with a workgroup barrier, then its
-// thread 0 publishes with an agent-scope release atomic (the release covers
-// the whole workgroup's stores, which the barrier ordered before it); a
-// reader's thread 0 waits with agent-scope acquire loads and a workgroup
-// barrier orders the other threads' loads after that acquire.  One release
-// per published item, not one per wave: each is a write-back of the L2.  Waits are bounded: a wait that expires
-// or-s MOE_STATUS_WAIT_EXPIRED into the caller's status word and the item that
-// waited is skipped (no load, no store), so no wave can hang and nothing is
-// computed from unpublished data.
+// thread 0 publishes with an agent-scope release (the release covers the
+// whole workgroup's stores, which the barrier ordered before it); a reader's
+// thread 0 waits with agent-scope acquire loads and a workgroup barrier
+// orders the other threads' loads after that acquire.  Each release is a
+// write-back of the L2, so there is one per published item (GEMM1 tiles:
+// one per batch, flush_g1), never one per wave.
+// Waits are bounded: a wait that expires or-s MOE_STATUS_WAIT_EXPIRED into
+// the caller's status word and the item that waited is skipped (no load, no
+// store), so no wave can hang and nothing is computed from unpublished data.
 // ---------------------------------------------------------------------------
 
-constexpr int kDispRows = 64;
 constexpr int kSpinLimit = 1 << 22;
 
 struct FusedParams {
-  FwdParams g1, g2;             // g1: X_d -> G, U, H;  g2: H -> Y
+  FwdParams g1, g2;             // g1: X_d -> G, U, H;  g2: H -> Y (plans and queue heads in each)
   const uint16_t* x;            // [N][D] token rows
-  const int32_t* row_route;     // [rows_cap]
-  int K;                        // routes per token
+  const int32_t* dst_rows;      // [N][K] row of each route in X_d, -1 if none
+  int N, K;                     // tokens, routes per token
   int32_t* st;                  // queue state (zeroed by the planner)
   const int32_t* fplan;         // fused plan
   int nt1, nt2;                 // n-tiles of GEMM1 / GEMM2
@@ -454,21 +464,22 @@ struct FusedParams {
   int publish;                  // 0: readiness withheld (testing the bound)
 };
 
-// queue state layout (int32 units)
-__device__ __host__ __forceinline__ int st_head() { return 0; }
-__device__ __host__ __forceinline__ int st_err() { return 1; }
-__device__ __host__ __forceinline__ int st_ticket() { return 2; }   // uint64 at ints 2..3
-__device__ __host__ __forceinline__ int st_ready_e(int E) { (void)E; return 4; }
-__device__ __host__ __forceinline__ int st_ready_cum(int E) { return 4 + E; }
-__device__ __host__ __forceinline__ int st_ready_ok(int E) { return 4 + 2 * E; }
-__device__ __host__ __forceinline__ int st_rows_done(int E) { return 4 + 3 * E; }
-__device__ __host__ __forceinline__ int st_g1_done(int E) { return 4 + 4 * E; }
+// queue state layout (int32 units; 128-byte aligned): the GEMM2 queue heads,
+// then the counters and per-expert and per-row-block words
+__device__ __host__ __forceinline__ int st_err() { return kGemmHeadInts + 1; }
+__device__ __host__ __forceinline__ int st_fold_head() { return kGemmHeadInts + 2; }
+__device__ __host__ __forceinline__ int st_disp_done() { return kGemmHeadInts + 3; }  // dispatch items stored
+__device__ __host__ __forceinline__ int st_g1_done() { return kGemmHeadInts + 4; }    // [row block]
+__device__ __host__ __forceinline__ int st_ints(int max_mb) { return kGemmHeadInts + 4 + max_mb; }
+
+// fused plan layout (int32 units): each expert's first row block in the
+// planner's order [E], then the GEMM2 plan (the GEMM planner's layout:
+// items, L, order, item prefix)
+__device__ __host__ __forceinline__ int fp_plan2(int E) { return E; }
+__device__ __host__ __forceinline__ int fp_ints(int E) { return E + (int)gemm_fwd_plan_ints(E) + 8; }
 
 __device__ __forceinline__ int ld_acquire(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_relaxed(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // thread 0: wait until *p >= target (bounded); false if the bound expired,
@@ -485,255 +496,313 @@ __device__ __forceinline__ bool wait_ge(const FusedParams& f, const int32_t* p, 
 
 __device__ __forceinline__ int rows_bm(int rows) { return is_big(rows) ? 256 : 128; }
 
-// thread 0: find the ready position holding GEMM item j (units of nt tiles per
-// row block), walking forward from *pos; gives the expert and its first
-// row-block number in ready order.  false if a wait expired: the item is then
-// skipped.
-__device__ __forceinline__ bool locate(const FusedParams& f, int j, int nt, int* pos, int* e_out, int* cum_out) {
-  const int E = f.g1.E;
-  int32_t* st = f.st;
-  for (;;) {
-    const int ps = *pos;
-    if (ps >= E) {   // reached only after an expired wait left an expert unpublished
-      atomicOr(st + st_err(), 1);
-      if (f.status) atomicOr(f.status, 1);
-      return false;
-    }
-    if (!wait_ge(f, st + st_ready_ok(E) + ps, 1)) return false;
-    const int e = ld_relaxed(st + st_ready_e(E) + ps);
-    const int cum = ld_relaxed(st + st_ready_cum(E) + ps);
-    const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
-    const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
-    if (j < (cum + nmb) * nt) {
-      *e_out = e;
-      *cum_out = cum;
-      return true;
-    }
-    *pos = ps + 1;
-  }
+// row block of a claimed tile within its expert (blocks of the expert's own
+// size, 256 or 128 rows, whatever tile class runs the last one)
+__device__ __forceinline__ int claimed_block(const FwdParams& p, const Item& it) {
+  const int m0 = p.offsets[it.e];
+  return (it.m_start - m0) / rows_bm(it.m1 - m0);
 }
 
-template <class C>
-__device__ __forceinline__ void run_plain(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
+// thread 0: the readiness word of a claimed tile and the value it waits
+// for: GEMM1 the count of stored dispatch items, GEMM2 its GEMM1 row
+// block's count of stored n-tiles
+template <bool DUAL>
+__device__ __forceinline__ const int32_t* gate_word(const FusedParams& f, const int32_t* mbase, const Item& it,
+                                                    int* target) {
+  if (DUAL) {
+    *target = (int)gridDim.x;   // every workgroup's share of the dispatch
+    return f.st + st_disp_done();
+  }
+  *target = f.nt1;
+  return f.st + st_g1_done() + mbase[it.e] + claimed_block(f.g2, it);
+}
+
+// thread 0: is the tile ready?  One acquire load (block = false), or a
+// bounded wait (block = true; false if it expired, reported).  GEMM1's gate
+// is the same for every tile: once acquired (*done) it stays acquired for
+// the workgroup's later loads.
+template <bool DUAL>
+__device__ __forceinline__ bool gate(const FusedParams& f, const int32_t* mbase, const Item& it, bool block,
+                                     bool* done) {
+  if (DUAL && *done) return true;
+  int target = 0;
+  const int32_t* w = gate_word<DUAL>(f, mbase, it, &target);
+  const bool ok = block ? wait_ge(f, w, target) : ld_acquire(w) >= target;
+  if (DUAL && ok) *done = true;
+  return ok;
+}
+
+template <bool DUAL>
+__device__ __forceinline__ void start_claimed(const FwdParams& p, uint32_t lds0, const Item& it) {
+  if (it.big) start<BigTile<DUAL>>(p, lds0, it);
+  else if (it.tiny32) start<Tiny32Tile<DUAL, false>>(p, lds0, it);
+  else if (it.tiny) start<TinyTile<DUAL>>(p, lds0, it);
+  else start<SmallTile<DUAL>>(p, lds0, it);
+}
+
+// GEMM1 tiles are published to their row blocks' counts in batches: thread
+// 0 lists each stored tile's row block (s_info[4 ..], kPend entries) and a
+// flush makes them all visible with one agent-scope release fence, then adds
+// them to the counts with relaxed atomics.  On gfx950 an agent-scope release
+// writes back the L2, so one per batch instead of one per tile; every count
+// is a read-modify-write, so a reader that acquires the complete count
+// synchronizes with each contributor's fence.  A workgroup flushes when its
+// list is full, and after every tile once its claims reach the last two
+// tiles a workgroup of the queue (GEMM2 tiles start while those run, and
+// must not wait for tiles stored long before but held in a list).
+constexpr int kPend = 64;
+constexpr int kInfoInts = 4 + kPend;   // s_info: 4 words, then the pending list
+
+// every thread, npend the same in all: publish the listed GEMM1 tiles
+__device__ __forceinline__ void flush_g1(const FusedParams& f, int* s_info, int& npend) {
+  __syncthreads();   // the workgroup's stores precede thread 0's release fence
+  if (threadIdx.x == 0 && npend > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int i = 0; i < npend; ++i)
+      __hip_atomic_fetch_add(f.st + st_g1_done() + s_info[4 + i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  npend = 0;
+}
+
+// Run a claimed tile whose prologue is issued, as the staged engine does:
+// after its main loop, claim the next tile and, if that one is already
+// ready, issue its prologue before this tile's stores, so its loads overlap
+// them.  A GEMM1 tile then joins the pending list (npend: the same count in
+// every thread).  Returns the next tile; *next_started says whether its
+// prologue is issued.
+template <class C, bool DUAL>
+__device__ __forceinline__ Item fused_tile(const FusedParams& f, const FwdParams& p, const uint8_t* smem,
+                                           uint32_t lds0, int* s_info, int& li, int xcd, bool* gated,
+                                           const int32_t* mbase, const Item& it, bool* next_started, int& npend) {
   tile::Src<C> src;
   sources<C>(p, it, src);
-  tile::prologue<C>(lds0, src, p.nk);
   f32x4_t acc[C::TM][C::TN];
   mainloop_any<C>(smem, lds0, src, p.nk, acc);
+  const Item next = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
+  // s_info[0] still holds the claim's place in the queue (-1: none left)
+  const bool late = !next.valid || s_info[0] >= p.plan[0] - 2 * (int)gridDim.x;
+  bool started = false;
+  if (next.valid) {
+    if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, next, false, gated);
+    __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+    started = s_info[3] != 0;
+    if (started) start_claimed<DUAL>(p, lds0, next);
+  }
   epilogue<C>(p, it, acc);
+  if (DUAL) {
+    if (threadIdx.x == 0) s_info[4 + npend] = mbase[it.e] + claimed_block(p, it);
+    if (++npend == kPend || late) flush_g1(f, s_info, npend);
+  }
+  *next_started = started;
+  return next;
 }
 
-// A row block of the fused queue on the tile class the staged launches give
-// it: 256-row tiles for a large expert's row blocks, except a last one of at
-// most 128 rows, which (like every small expert's single block) takes the
-// smallest class that holds it.  Every class accumulates the same steps in
-// the same order, so the result is the same.
+// Every tile of one GEMM from its per-XCD queues, each after its readiness
+// word; a tile whose bounded wait expires is skipped (reported).
 template <bool DUAL>
-__device__ __forceinline__ void run_class(const FwdParams& p, const uint8_t* smem, uint32_t lds0, const Item& it) {
-  const int left = it.m1 - it.m_start;
-  if (it.big && left > kSmallBM) run_plain<BigTile<DUAL>>(p, smem, lds0, it);
-  else if (left <= kTiny32Rows) run_plain<Tiny32Tile<DUAL, false>>(p, smem, lds0, it);
-  else if (left <= kTinyRows) run_plain<TinyTile<DUAL>>(p, smem, lds0, it);
-  else run_plain<SmallTile<DUAL>>(p, smem, lds0, it);
+__device__ __forceinline__ void gemm_phase(const FusedParams& f, const FwdParams& p, const uint8_t* smem,
+                                           uint32_t lds0, int* s_info, int xcd, const int32_t* mbase) {
+  int li = 0, npend = 0;
+  bool gated = false;   // thread 0: GEMM1's gate acquired
+  Item it = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
+  bool started = false;
+  while (it.valid) {
+    if (!started) {
+      if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, it, true, &gated);
+      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+      if (!s_info[3]) {   // the wait expired: skip the tile
+        it = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
+        continue;
+      }
+      start_claimed<DUAL>(p, lds0, it);
+    }
+    if (it.big)
+      it = fused_tile<BigTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
+    else if (it.tiny32)
+      it = fused_tile<Tiny32Tile<DUAL, false>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it,
+                                                     &started, npend);
+    else if (it.tiny)
+      it = fused_tile<TinyTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
+    else
+      it = fused_tile<SmallTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
+  }
+  if (DUAL) flush_g1(f, s_info, npend);   // the rest of this workgroup's GEMM1 tiles
 }
-
 
 // The fold after the fused queue (single-launch layer): items of 8 tokens, a
-// wave per token.  Every workgroup publishes once, when it first claims past
-// the GEMM2 items (each of its GEMM2 tiles then is stored), and a fold item
+// wave per token.  Every workgroup publishes once, when it has claimed its
+// last GEMM2 tile (each of its GEMM2 tiles then is stored), and a fold item
 // waits until all of them have: the fold reads Y rows of any expert.
 struct FoldArgs {
   const int32_t* dst_rows;   // [N][K]
   const float* weight;       // [N][K] route weights
   int N;
   uint16_t* out;             // [N][D]
-  int32_t* passed;           // workgroups past the GEMM2 items (zeroed before the launch)
+  int32_t* passed;           // workgroups past the GEMM2 tiles (zeroed before the launch)
 };
 
-// The readiness-ordered queue: dispatch, GEMM1 and GEMM2 items, then the
-// fold when fold != nullptr.
+// The readiness-gated queue: dispatch items, GEMM1 and GEMM2 tiles, then the
+// fold when fold != nullptr.  s_info: kInfoInts ints of LDS.
 __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t* smem, uint32_t lds0, int* s_info,
                                             const FoldArgs* fold) {
   const int E = f.g1.E;
   int32_t* st = f.st;
-  const int ND = f.fplan[0], NMB = f.fplan[1], L = f.fplan[2];
-  const int32_t* dorder = f.fplan + 3;
-  const int32_t* dpref = f.fplan + 3 + E;
-  const int N1 = NMB * f.nt1, N2 = NMB * f.nt2;
+  const int32_t* mbase = f.fplan;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int ld = 0, p1 = 0, p2 = 0;   // walk positions (claims only increase)
-  const int NF = fold ? (fold->N + 7) / 8 : 0;
-  bool passed = false;
+  const int xcd = xcd_id();
 
-  for (;;) {
-    if (tid == 0) s_info[0] = atomicAdd(st + st_head(), 1);
-    __syncthreads();
-    const int item = s_info[0];
-    __syncthreads();
-    if (item >= ND + N1 + N2) {
-      if (!fold) break;
-      if (!passed) {
-        passed = true;
-        __syncthreads();   // the workgroup's stores precede thread 0's release below
-        if (tid == 0)
-          __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (item >= ND + N1 + N2 + NF) break;
-      // ---- fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] ----------------------
-      if (tid == 0) s_info[3] = wait_ge(f, fold->passed, (int)gridDim.x);
-      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      const int t = __builtin_amdgcn_readfirstlane((item - ND - N1 - N2) * 8 + wave);
-      if (t < fold->N)
-        perm::combine_token<true>(t, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K, fold->out, nullptr,
-                                  nullptr);
-      continue;
-    }
-
-    if (item < ND) {
-      // ---- dispatch chunk: gather token rows into X_d ------------------------
-      while (ld + 1 < L && dpref[ld + 1] <= item) ++ld;
-      const int e = dorder[ld];
-      const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
-      const int r0 = m0 + (item - dpref[ld]) * kDispRows, r1 = min(r0 + kDispRows, m1);
-      const int D = f.g1.K, nvec = D >> 3;
-      for (int i = r0 + wave; i < r1; i += 8) {
-        const int t = f.row_route[i] / f.K;
-        const uint16_t* src = f.x + (int64_t)t * D;
-        uint16_t* dst = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(f.g1.a)) + (int64_t)i * D;
-        for (int v0 = 0; v0 < nvec; v0 += 4 * 64) {
-          uint4 r[4];
+  // ---- 1. dispatch: each token row read once, written to its routes' rows ------
+  // Workgroup b takes the token groups b, b + G, ... of 8 tokens (G the grid
+  // size), a wave one token a group.  Its loop keeps the next token's row in
+  // flight while it stores the current one's K copies: vector memory
+  // operations complete in order, so loads issued after the stores would
+  // wait for them.
+  {
+    constexpr int VB = 16;   // vectors a lane of a row in one pass (rows up to 8192 elements)
+    const int D = f.g1.K, nvec = D >> 3;
+    uint16_t* xd = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(f.g1.a));
+    const int step = (int)gridDim.x * 8;
+    int t = (int)blockIdx.x * 8 + wave;
+    if (nvec <= VB * 64) {
+      uint4 cur[VB], nxt[VB];
+      auto load = [&](uint4 (&r)[VB], int tok) {
+        const uint16_t* src = f.x + (int64_t)tok * D;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < VB; ++j) {
+          const int v = lane + j * 64;
+          if (v < nvec) r[j] = ldg16(src + v * 8);
+        }
+      };
+      if (t < f.N) load(cur, t);
+      for (; t < f.N; t += step) {
+        if (t + step < f.N) load(nxt, t + step);
+        for (int k = 0; k < f.K; ++k) {
+          const int dk = f.dst_rows[(int64_t)t * f.K + k];
+          if (dk < 0) continue;
+#pragma unroll
+          for (int j = 0; j < VB; ++j) {
+            const int v = lane + j * 64;
+            if (v < nvec) stg16(xd + (int64_t)dk * D + v * 8, cur[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < VB; ++j) cur[j] = nxt[j];
+      }
+    } else {
+      for (; t < f.N; t += step) {
+        const uint16_t* src = f.x + (int64_t)t * D;
+        for (int v0 = 0; v0 < nvec; v0 += VB * 64) {
+          uint4 r[VB];
+#pragma unroll
+          for (int j = 0; j < VB; ++j) {
             const int v = v0 + lane + j * 64;
             if (v < nvec) r[j] = ldg16(src + v * 8);
           }
+          for (int k = 0; k < f.K; ++k) {
+            const int dk = f.dst_rows[(int64_t)t * f.K + k];
+            if (dk < 0) continue;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int v = v0 + lane + j * 64;
-            if (v < nvec) stg16(dst + v * 8, r[j]);
+            for (int j = 0; j < VB; ++j) {
+              const int v = v0 + lane + j * 64;
+              if (v < nvec) stg16(xd + (int64_t)dk * D + v * 8, r[j]);
+            }
           }
         }
       }
-      __syncthreads();   // the workgroup's stores precede thread 0's release below
-      if (tid == 0) {
-        const int m = m1 - m0;
-        // acquire-release: the workgroup that completes the expert acquires
-        // every other chunk's release, so its release below carries them all
-        const int done = __hip_atomic_fetch_add(st + st_rows_done(E) + e, r1 - r0, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT) + (r1 - r0);
-        if (done == m && f.publish) {
-          const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
-          const unsigned long long t =
-              atomicAdd(reinterpret_cast<unsigned long long*>(st + st_ticket()), (1ull << 32) | (unsigned)nmb);
-          const int pos = (int)(t >> 32), cum = (int)(t & 0xffffffffu);
-          __hip_atomic_store(st + st_ready_e(E) + pos, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(st + st_ready_cum(E) + pos, cum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(st + st_ready_ok(E) + pos, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    } else if (item < ND + N1) {
-      // ---- GEMM1 tile, experts in ready order ---------------------------------
-      const int j = item - ND;
-      if (tid == 0) {
-        int e = 0, cum = 0;
-        s_info[3] = locate(f, j, f.nt1, &p1, &e, &cum);
-        s_info[1] = e;
-        s_info[2] = cum;
-      }
-      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      const int e = s_info[1], cum = s_info[2];
-      const int m0 = f.g1.offsets[e], m1 = f.g1.offsets[e + 1];
-      const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
-      const int w = j - cum * f.nt1, n_t = w / nmb, mb = w - n_t * nmb;
-      run_class<true>(f.g1, smem, lds0, Item{e, m0 + mb * bm, m1, n_t * BigTile<true>::NCOL, is_big(m1 - m0), true});
-      __syncthreads();   // the workgroup's stores precede thread 0's release below
-      if (tid == 0)
-        __hip_atomic_fetch_add(st + st_g1_done(E) + cum + mb, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      // ---- GEMM2 tile, gated on its GEMM1 row block ----------------------------
-      const int j = item - ND - N1;
-      if (tid == 0) {
-        int e = 0, cum = 0;
-        bool ok = locate(f, j, f.nt2, &p2, &e, &cum);
-        if (ok) {
-          const int m = f.g1.offsets[e + 1] - f.g1.offsets[e];
-          const int nmb = (m + rows_bm(m) - 1) / rows_bm(m);
-          const int mb = (j - cum * f.nt2) % nmb;
-          ok = wait_ge(f, st + st_g1_done(E) + cum + mb, f.nt1);
-        }
-        s_info[3] = ok;
-        s_info[1] = e;
-        s_info[2] = cum;
-      }
-      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-      if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-      const int e = s_info[1], cum = s_info[2];
-      const int m0 = f.g2.offsets[e], m1 = f.g2.offsets[e + 1];
-      const int bm = rows_bm(m1 - m0), nmb = (m1 - m0 + bm - 1) / bm;
-      const int w = j - cum * f.nt2, n_t = w / nmb, mb = w - n_t * nmb;
-      run_class<false>(f.g2, smem, lds0, Item{e, m0 + mb * bm, m1, n_t * BigTile<false>::NCOL, is_big(m1 - m0), true});
     }
+    __syncthreads();   // the workgroup's stores precede thread 0's release below
+    if (tid == 0) __hip_atomic_fetch_add(st + st_disp_done(), f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- 2. GEMM1 tiles, each after its expert is ready --------------------------
+  gemm_phase<true>(f, f.g1, smem, lds0, s_info, xcd, mbase);
+  // ---- 3. GEMM2 tiles, each after its GEMM1 row block ---------------------------
+  gemm_phase<false>(f, f.g2, smem, lds0, s_info, xcd, mbase);
+  if (!fold) return;
+
+  // ---- 4. the fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] -------------------
+  __syncthreads();   // the workgroup's stores precede thread 0's release below
+  if (tid == 0) __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const int NF = (fold->N + 7) / 8;
+  bool all_passed = false;   // thread 0: every workgroup's release acquired
+  for (;;) {
+    if (tid == 0) s_info[0] = atomicAdd(st + st_fold_head(), 1);
+    __syncthreads();
+    const int item = s_info[0];
+    __syncthreads();
+    if (item >= NF) break;
+    if (tid == 0) {
+      if (!all_passed) all_passed = wait_ge(f, fold->passed, (int)gridDim.x);
+      s_info[3] = all_passed;
+    }
+    __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+    if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
+    const int t = __builtin_amdgcn_readfirstlane(item * 8 + wave);
+    if (t < fold->N)
+      perm::combine_token<true>(t, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K, fold->out, nullptr, nullptr);
   }
 }
 
 __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  __shared__ int s_info[4];
+  __shared__ int s_info[kInfoInts];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   fused_items(f, smem, lds0, s_info, nullptr);
 }
 
-// Fused planner: one workgroup.  Dispatch order = the GEMM planner's expert
-// order; fplan = {ND, NMB, L, order[E], dispatch prefix[E+1]}.  Zeroes the
-// queue state for this launch.
+// Fused planner: one workgroup, after the GEMM1 plan (gplan): each expert's
+// first row block in the planner's order, the GEMM2 plan in the same expert
+// order (fp_* above), and zeroes the queue state (the GEMM2 queue heads
+// included) for this launch.  LDS: s_m [THREADS / 64] ints.
 template <int THREADS>
-__device__ __forceinline__ void plan_fused_body(const int32_t* __restrict__ offsets, int E, int max_mb,
+__device__ __forceinline__ void plan_fused_body(const int32_t* __restrict__ offsets, int E, int max_mb, int nt2,
                                                 const int32_t* __restrict__ gplan, int32_t* __restrict__ fplan,
-                                                int32_t* __restrict__ st, int* s_w, int* s_m) {
+                                                int32_t* __restrict__ st, int* s_m) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int L = gplan[1];
-  int chunks = 0, mbs = 0;
+  int mbs = 0;
   if (t < L) {
     const int e = gplan[2 + t];
     const int m = offsets[e + 1] - offsets[e];
-    chunks = (m + kDispRows - 1) / kDispRows;
     mbs = (m + rows_bm(m) - 1) / rows_bm(m);
   }
-  int inc = chunks, incm = mbs;
+  int incm = mbs;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(inc, o, 64), b = __shfl_up(incm, o, 64);
-    if (lane >= o) { inc += a; incm += b; }
+    const int b = __shfl_up(incm, o, 64);
+    if (lane >= o) incm += b;
   }
-  if (lane == 63) { s_w[wv] = inc; s_m[wv] = incm; }
+  if (lane == 63) s_m[wv] = incm;
+  for (int i = t; i < st_ints(max_mb); i += THREADS) st[i] = 0;
   __syncthreads();
   if (t == 0) {
-    int r = 0, rm = 0;
+    int rm = 0;
     for (int w = 0; w < THREADS / 64; ++w) {
-      const int a = s_w[w], b = s_m[w];
-      s_w[w] = r; s_m[w] = rm;
-      r += a; rm += b;
+      const int b = s_m[w];
+      s_m[w] = rm;
+      rm += b;
     }
-    fplan[0] = r;
-    fplan[1] = rm;
-    fplan[2] = L;
-    fplan[3 + E + L] = r;
+    int32_t* plan2 = fplan + fp_plan2(E);
+    plan2[0] = rm * nt2;
+    plan2[1] = L;
+    plan2[2 + E + L] = rm * nt2;
   }
   __syncthreads();
   if (t < L) {
-    fplan[3 + t] = gplan[2 + t];
-    fplan[3 + E + t] = inc - chunks + s_w[wv];
+    const int e = gplan[2 + t];
+    const int mb0 = incm - mbs + s_m[wv];   // the expert's first row block in planner order
+    fplan[e] = mb0;
+    int32_t* plan2 = fplan + fp_plan2(E);
+    plan2[2 + t] = e;
+    plan2[2 + E + t] = mb0 * nt2;
   }
-  for (int i = t; i < 4 + 4 * E + max_mb; i += THREADS) st[i] = 0;
 }
 
 __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restrict__ offsets, int E, int max_mb,
-                                                          const int32_t* __restrict__ gplan,
+                                                          int nt2, const int32_t* __restrict__ gplan,
                                                           int32_t* __restrict__ fplan, int32_t* __restrict__ st) {
-  __shared__ int s_w[16], s_m[16];
-  plan_fused_body<1024>(offsets, E, max_mb, gplan, fplan, st, s_w, s_m);
+  __shared__ int s_m[16];
+  plan_fused_body<1024>(offsets, E, max_mb, nt2, gplan, fplan, st, s_m);
 }
 
 // ---------------------------------------------------------------------------
@@ -747,9 +816,9 @@ __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restr
 //   3. workgroup 0: the histogram scan (counts, offsets, chunk bases) and the
 //      GEMM and queue plans;
 //   4. the scatter of every route to its row;
-//   5. the readiness-ordered queue: dispatch chunks, GEMM1 tiles as experts
-//      become ready, GEMM2 tiles as their GEMM1 row blocks complete, then
-//      the fold, 8 tokens per item.
+//   5. the readiness-gated queue: the dispatch, GEMM1 tiles after it, GEMM2
+//      tiles as their GEMM1 row blocks complete, then the fold, 8 tokens per
+//      item.
 // Steps 1-4 end at a grid barrier: a counter every workgroup adds to after an
 // agent-scope release, waited on (bounded) and acquired.  Every workgroup is
 // resident (one per CU), so each barrier is reached by all; a wait that
@@ -795,7 +864,7 @@ __device__ __forceinline__ void topk_single(const SingleFwdParams& p, int c, int
 
 __global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  __shared__ int s_info[4];
+  __shared__ int s_info[kInfoInts];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const FusedParams& f = p.f;
   const int tid = threadIdx.x;
@@ -850,7 +919,7 @@ __global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p
     sched::plan_rows_body<512>(p.offsets, p.E, f.nt1, p.gplan, p.head, s_w0, s_w1, s_tot2, s_key, s_items, s_ids,
                                s_pref);
     __syncthreads();   // the GEMM plan, read by the queue plan
-    plan_fused_body<512>(p.offsets, p.E, p.max_mb, p.gplan, const_cast<int32_t*>(f.fplan), f.st, w + 4096,
+    plan_fused_body<512>(p.offsets, p.E, p.max_mb, f.nt2, p.gplan, const_cast<int32_t*>(f.fplan), f.st,
                          w + 4112);
   }
   if (!grid_sync(f, p.bar + 2, s_info)) return;
@@ -930,7 +999,7 @@ hipError_t launch_gemm_fwd_fast(const GemmFwd& f, bool mx, int32_t* ws, hipStrea
 // Workspace of the fused forward: GEMM plan, fused plan and queue state.
 size_t experts_fused_ws_ints(int64_t rows_cap, int64_t E) {
   const int64_t max_mb = rows_cap / 128 + E + 1;
-  return (size_t)(kGemmHeadInts + gemm_fwd_plan_ints(E) + (3 + 2 * E + 8) + (4 + 4 * E + max_mb) + 64);
+  return (size_t)(kGemmHeadInts + gemm_fwd_plan_ints(E) + fp_ints((int)E) + st_ints((int)max_mb) + 96);
 }
 
 namespace {
@@ -960,15 +1029,25 @@ void fused_params(const ExpertsFwd& x, int32_t* ws, FusedParams& f, int32_t** gp
   g2.b0 = (const uint8_t*)x.w_down;
   g2.c0 = (uint16_t*)x.y;
   f.x = (const uint16_t*)x.x;
-  f.row_route = x.row_route;
+  f.dst_rows = x.dst_rows;
+  f.N = (int)x.N_tokens;
   f.K = (int)x.K;
   f.nt1 = (int)((x.H + BigTile<true>::NCOL - 1) / BigTile<true>::NCOL);
   f.nt2 = (int)((x.D + BigTile<false>::NCOL - 1) / BigTile<false>::NCOL);
+  // workspace: GEMM1 queue heads, GEMM1 plan, fused plan (GEMM2 plan in it),
+  // queue state (GEMM2 queue heads first, 128-byte aligned), then the single
+  // launch's barrier words
   int32_t* gplan = ws + kGemmHeadInts;
   int32_t* fplan = gplan + gemm_fwd_plan_ints(x.E);
-  int32_t* st = fplan + (3 + 2 * x.E + 8);
-  st = (int32_t*)(((uintptr_t)st + 7) & ~(uintptr_t)7);   // 8-byte aligned ticket
+  int32_t* st = fplan + fp_ints((int)x.E);
+  st = (int32_t*)(((uintptr_t)st + 127) & ~(uintptr_t)127);
   const int max_mb = (int)(x.rows_cap / 128 + x.E + 1);
+  g1.plan = gplan;
+  g1.head = ws;
+  g2.plan = fplan + fp_plan2((int)x.E);
+  g2.head = st;
+  g1.n_tiles = f.nt1;
+  g2.n_tiles = f.nt2;
   f.st = st;
   f.fplan = fplan;
   f.status = x.status;
@@ -978,7 +1057,7 @@ void fused_params(const ExpertsFwd& x, int32_t* ws, FusedParams& f, int32_t** gp
   *max_mb_out = max_mb;
   // the single launch's barrier words: after the queue state, in the
   // workspace's slack (experts_fused_ws_ints)
-  int32_t* bar = st + 4 + 4 * x.E + max_mb;
+  int32_t* bar = st + st_ints(max_mb);
   *bar_out = (int32_t*)(((uintptr_t)bar + 31) & ~(uintptr_t)31);
 }
 
@@ -1000,7 +1079,8 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   int max_mb = 0;
   fused_params(x, ws, f, &gplan, &max_mb, &bar);
   plan_rows_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, f.nt1, gplan, ws);
-  plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, gplan, const_cast<int32_t*>(f.fplan), f.st);
+  plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, f.nt2, gplan, const_cast<int32_t*>(f.fplan),
+                                       f.st);
   int grid = 0;
   hipError_t err = resident_grid((const void*)experts_fwd_fused_kernel, &grid);
   if (err != hipSuccess) return err;

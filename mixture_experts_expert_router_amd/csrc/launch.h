@@ -144,6 +144,7 @@ struct ExpertsFwd {
   int64_t N_tokens;                  // tokens (the single-launch layer)
   const int32_t* offsets;
   const int32_t* row_route;
+  const int32_t* dst_rows;
   const void* x;
   const void* w_gate;
   const void* w_up;
