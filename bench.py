@@ -472,6 +472,12 @@ def single_launch_ok(wl, bwd):
             and (not bwd or wl.E % 64 == 0))
 
 
+def ready_queue_ok(wl):
+    """The readiness-gated launch's rules (bf16 routed experts, D and H
+    multiples of 64)."""
+    return not wl.mxfp8 and wl.D % 64 == 0 and wl.H % 64 == 0
+
+
 def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False,
             mx_wgrad=False, single=False):
     """Time `steps` steps of one workload (after `warmup`), inputs resident in
@@ -531,6 +537,16 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         return e0.elapsed_time(e1) / steps
 
     layer_ms = time_layer(layer) if (layer_call or shared_expert or single) else None
+    ready_out = None
+    if single and ready_queue_ok(wl):
+        # dispatch, GEMM1 and GEMM2 in one readiness-gated launch (outputs
+        # bitwise the staged launches'), timed call by call like layer_call_ms
+        lay_r = M.MoeLayer(w, wl.N, wl.K, mxfp8=False, drop=drop, renorm=wl.renorm, sched=M.MOE_SCHED_READY)
+        ready_out = {"layer_fwd_ms": time_layer(lay_r), "staged_layer_fwd_ms": layer_ms,
+                     "note": "moe_layer_fwd with MOE_SCHED_READY: router and route launches, then dispatch, "
+                             "GEMM1 and GEMM2 in one persistent launch (GEMM2 tiles gated per GEMM1 row "
+                             "block), then the combine"}
+        del lay_r
     single_out = None
     if single and single_launch_ok(wl, bwd):
         # the same layer in one persistent launch per direction (outputs bitwise
@@ -636,6 +652,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         out["shared_expert"] = shared
     if single_out is not None:
         out["single_launch"] = single_out
+    if ready_out is not None:
+        out["ready_queue"] = ready_out
     del layer, st, x, w, drop, dout
     return out
 
@@ -643,7 +661,7 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
 def summary_of(r):
     """The keys of a non-headline workload's result kept in the JSON line."""
     keep = ("value", "unit", "ms_per_step", "fwd_ms", "dtype", "config", "roofline", "grouped_gemm", "dispatch",
-            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward", "single_launch")
+            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward", "single_launch", "ready_queue")
     return {k: r[k] for k in keep if k in r}
 
 

@@ -550,7 +550,7 @@ __device__ __forceinline__ void start_claimed(const FwdParams& p, uint32_t lds0,
 // list is full, and after every tile once its claims reach the last two
 // tiles a workgroup of the queue (GEMM2 tiles start while those run, and
 // must not wait for tiles stored long before but held in a list).
-constexpr int kPend = 64;
+constexpr int kPend = 16;
 constexpr int kInfoInts = 4 + kPend;   // s_info: 4 words, then the pending list
 
 // every thread, npend the same in all: publish the listed GEMM1 tiles

@@ -158,6 +158,46 @@ def test_layer_fwd_single_launch_equals_staged(name):
     assert_bf16_close(vals(got), ref["out"], "out")
 
 
+READY_CASES = {
+    # rows wider than one pass of the dispatch's two-row loop (D > 8192)
+    "wide_rows": S.scaled(S.WORKLOADS["dsv3_bf16"], "wide_rows", N=96, D=8256, E=16, K=2, H=128),
+    # fewer tokens than workgroups: most dispatch shares are empty
+    "five_tokens": S.scaled(S.WORKLOADS["dsv3_bf16"], "five_tokens", N=5, D=256, E=16, K=4, H=128),
+    # enough GEMM1 tiles (about 6000) that workgroups publish full batches
+    # of stored tiles before the queue's last window
+    "many_tiles": S.scaled(S.WORKLOADS["qwen3_235b_bf16_fwdbwd"], "many_tiles", N=9216, D=256, E=64, K=8,
+                           H=2048),
+}
+
+
+@pytest.mark.parametrize("name", list(READY_CASES))
+def test_ready_queue_equals_staged(name):
+    """The readiness-gated launch (dispatch shares, GEMM1 tiles after the
+    dispatch, GEMM2 tiles per GEMM1 row block) stores every row of X_d, G,
+    U, H and Y bitwise as the staged launches do, outputs poisoned first."""
+    wl = READY_CASES[name]
+    print(f"READY fwd {name}", flush=True)
+    inp = S.make_inputs(wl, 5)
+    w, _ = _weights(inp)
+    drop = dev(inp.drop) if inp.drop is not None else None
+    x = dev_bf16(inp.x)
+    staged = M.MoeLayer(w, wl.N, wl.K, drop=drop)
+    want = staged.forward(x)
+    ready = M.MoeLayer(w, wl.N, wl.K, drop=drop, sched=M.MOE_SCHED_READY)
+    for t in list(ready.saved.values()) + [ready.out]:
+        t.view(torch.uint8).fill_(0xA5)
+    got = ready.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(ready.saved["status"])[0]) == 0
+    n = int(host(staged.saved["offsets"])[-1])
+    for k in ("counts", "offsets", "dst_rows", "xd", "g", "u", "h", "y"):
+        a, b = staged.saved[k], ready.saved[k]
+        if k in ("xd", "g", "u", "h", "y"):
+            a, b = a[:n], b[:n]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), k
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "out"
+
+
 def test_single_launch_barrier_expiry_is_reported_and_the_next_call_recovers():
     """Barrier arrivals and readiness withheld from the host, every wait
     bounded to a few polls: each barrier wait expires, the workgroups stop,
