@@ -813,9 +813,11 @@ __global__ __launch_bounds__(1024) void plan_fused_kernel(const int32_t* __restr
 //      launch, so the same partial sums), and marks every row unused;
 //   2. per chunk of 16 tokens: the logits (partials added in split order,
 //      then the bias), softmax and top-K, the in-chunk ranks and histogram;
-//   3. workgroup 0: the histogram scan (counts, offsets, chunk bases) and the
-//      GEMM and queue plans;
-//   4. the scatter of every route to its row;
+//   3. the histogram scan, one expert a workgroup: each chunk's first row of
+//      the expert within its segment, and the expert's count;
+//   4. every workgroup the segment offsets from the counts; workgroup 0
+//      stores them and builds the GEMM and queue plans while the others
+//      scatter every route to its row;
 //   5. the readiness-gated queue: the dispatch, GEMM1 tiles after it, GEMM2
 //      tiles as their GEMM1 row blocks complete, then the fold, 8 tokens per
 //      item.
@@ -906,28 +908,41 @@ __global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p
   }
   if (!grid_sync(f, p.bar + 1, s_info)) return;
 
-  // ---- 3. scan and plans, workgroup 0 ------------------------------------------
-  if (blockIdx.x == 0) {
-    int* w = reinterpret_cast<int*>(smem);
-    int *s_part = w, *s_tot = w + 512, *s_off = w + 1024, *s_wsum = w + 1600;
-    route::scan_hist<512>(p.hist, p.nchunks, p.E, p.align, p.counts, p.offsets, p.N, 0, s_part, s_tot, s_off,
-                          s_wsum);
-    __syncthreads();   // offsets written by this workgroup, read below
-    int *s_w0 = w + 2048, *s_w1 = w + 2064, *s_tot2 = w + 2080, *s_pref = w + 2096;
-    float* s_key = reinterpret_cast<float*>(w + 2560);
-    int *s_items = w + 3072, *s_ids = w + 3584;
-    sched::plan_rows_body<512>(p.offsets, p.E, f.nt1, p.gplan, p.head, s_w0, s_w1, s_tot2, s_key, s_items, s_ids,
-                               s_pref);
-    __syncthreads();   // the GEMM plan, read by the queue plan
-    plan_fused_body<512>(p.offsets, p.E, p.max_mb, f.nt2, p.gplan, const_cast<int32_t*>(f.fplan), f.st,
-                         w + 4112);
+  // ---- 3. the histogram scan, an expert a workgroup ------------------------------
+  {
+    int* s_w = reinterpret_cast<int*>(smem);
+    for (int e = blockIdx.x; e < p.E; e += gridDim.x)
+      route::scan_expert<512>(p.hist, p.nchunks, p.E, e, p.counts, s_w);
   }
   if (!grid_sync(f, p.bar + 2, s_info)) return;
 
-  // ---- 4. scatter ---------------------------------------------------------------
-  const int64_t NK = (int64_t)p.N * p.K;
-  for (int64_t r = (int64_t)blockIdx.x * 512 + tid; r < NK; r += gthreads)
-    route::scatter_route(r, p.topk_idx, p.drop, p.hist, p.rank, p.K, p.E, p.dst_rows, p.row_route);
+  // ---- 4. segment offsets (every workgroup), the scatter; workgroup 0 the plans --
+  {
+    int* w = reinterpret_cast<int*>(smem);
+    int *s_off = w, *s_wsum = w + 1024;
+    route::offsets_of<512>(p.counts, p.E, p.align, s_off, s_wsum);
+    if (blockIdx.x == 0) {
+      for (int e = tid; e <= p.E; e += 512) p.offsets[e] = s_off[e];
+      __syncthreads();   // offsets written by this workgroup, read by its planners below
+      int *s_w0 = w + 2048, *s_w1 = w + 2064, *s_tot2 = w + 2080, *s_pref = w + 2096;
+      float* s_key = reinterpret_cast<float*>(w + 2560);
+      int *s_items = w + 3072, *s_ids = w + 3584;
+      sched::plan_rows_body<512>(p.offsets, p.E, f.nt1, p.gplan, p.head, s_w0, s_w1, s_tot2, s_key, s_items,
+                                 s_ids, s_pref);
+      __syncthreads();   // the GEMM plan, read by the queue plan
+      plan_fused_body<512>(p.offsets, p.E, p.max_mb, f.nt2, p.gplan, const_cast<int32_t*>(f.fplan), f.st,
+                           w + 4112);
+    }
+    // the other workgroups scatter every route to its row (all of them when
+    // the grid is one workgroup)
+    const int g0 = gridDim.x > 1 ? 1 : 0;
+    const int64_t NK = (int64_t)p.N * p.K;
+    const int64_t nth = (int64_t)(gridDim.x - g0) * 512;
+    if ((int)blockIdx.x >= g0)
+      for (int64_t r = (int64_t)(blockIdx.x - g0) * 512 + tid; r < NK; r += nth)
+        route::scatter_route_seg(r, p.topk_idx, p.drop, p.hist, s_off, p.rank, p.K, p.E, p.dst_rows,
+                                 p.row_route);
+  }
   if (!grid_sync(f, p.bar + 3, s_info)) return;
 
   // ---- 5. dispatch, GEMM1, GEMM2 by readiness, then the fold ------------------

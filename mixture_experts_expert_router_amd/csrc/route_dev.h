@@ -310,5 +310,89 @@ __device__ __forceinline__ void scatter_route(int64_t r, const int32_t* __restri
   row_route[dst] = (int32_t)r;
 }
 
+// The single-launch layer's form of the scan, spread over the workgroups:
+// expert e's column of the histogram is scanned by one workgroup of THREADS
+// threads, each chunk's count replaced by the rows of e in the chunks before
+// it (its first row relative to the expert's segment), the total written to
+// counts[e].  The same prefix sums as scan_hist, in the same order.  LDS:
+// s_w [THREADS / 64] ints.
+template <int THREADS>
+__device__ __forceinline__ void scan_expert(int32_t* __restrict__ hist, int nchunks, int E, int e,
+                                            int32_t* __restrict__ counts, int* s_w) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int cpt = (nchunks + THREADS - 1) / THREADS;
+  const int c0 = min(nchunks, t * cpt), c1 = min(nchunks, c0 + cpt);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += hist[(int64_t)c * E + e];
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) s_w[wv] = inc;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int w = 0; w < THREADS / 64; ++w) { const int a = s_w[w]; s_w[w] = run; run += a; }
+  }
+  __syncthreads();
+  int run = inc - sum + s_w[wv];
+  for (int c = c0; c < c1; ++c) {
+    const int h = hist[(int64_t)c * E + e];
+    hist[(int64_t)c * E + e] = run;
+    run += h;
+  }
+  if (t == THREADS - 1) counts[e] = run;
+  __syncthreads();   // s_w is free for the next expert
+}
+
+// Segment offsets from the counts (E <= THREADS): s_off[e] = the aligned
+// sizes of the experts before e, s_off[E] = the total, as scan_hist sets
+// them.  LDS: s_off [E + 1], s_w [THREADS / 64] ints.
+template <int THREADS>
+__device__ __forceinline__ void offsets_of(const int32_t* __restrict__ counts, int E, int align, int* s_off,
+                                           int* s_w) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int own = t < E ? ((counts[t] + align - 1) / align) * align : 0;
+  int inc = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) s_w[wv] = inc;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int w = 0; w < THREADS / 64; ++w) { const int a = s_w[w]; s_w[w] = run; run += a; }
+  }
+  __syncthreads();
+  inc += s_w[wv];
+  if (t < E) s_off[t] = inc - own;
+  if (t == E - 1) s_off[E] = inc;
+  if (E == 0 && t == 0) s_off[0] = 0;
+  __syncthreads();
+}
+
+// scatter_route with chunk bases relative to the segments (scan_expert) and
+// the segment offsets seg (offsets_of).
+__device__ __forceinline__ void scatter_route_seg(int64_t r, const int32_t* __restrict__ topk_idx,
+                                                  const uint8_t* __restrict__ drop,
+                                                  const int32_t* __restrict__ base, const int* seg,
+                                                  const int32_t* __restrict__ rank, int K, int E,
+                                                  int32_t* __restrict__ dst_rows, int32_t* __restrict__ row_route) {
+  const int e = topk_idx[r];
+  const bool valid = (drop == nullptr || drop[r] == 0) && e >= 0 && e < E;
+  if (!valid) {
+    dst_rows[r] = -1;
+    return;
+  }
+  const int64_t chunk = (r / K) / kChunk;
+  const int dst = seg[e] + base[chunk * E + e] + rank[r];
+  dst_rows[r] = dst;
+  row_route[dst] = (int32_t)r;
+}
+
 }  // namespace route
 }  // namespace moe
