@@ -518,18 +518,12 @@ __device__ __forceinline__ const int32_t* gate_word(const FusedParams& f, const 
 }
 
 // thread 0: is the tile ready?  One acquire load (block = false), or a
-// bounded wait (block = true; false if it expired, reported).  GEMM1's gate
-// is the same for every tile: once acquired (*done) it stays acquired for
-// the workgroup's later loads.
+// bounded wait (block = true; false if it expired, reported).
 template <bool DUAL>
-__device__ __forceinline__ bool gate(const FusedParams& f, const int32_t* mbase, const Item& it, bool block,
-                                     bool* done) {
-  if (DUAL && *done) return true;
+__device__ __forceinline__ bool gate(const FusedParams& f, const int32_t* mbase, const Item& it, bool block) {
   int target = 0;
   const int32_t* w = gate_word<DUAL>(f, mbase, it, &target);
-  const bool ok = block ? wait_ge(f, w, target) : ld_acquire(w) >= target;
-  if (DUAL && ok) *done = true;
-  return ok;
+  return block ? wait_ge(f, w, target) : ld_acquire(w) >= target;
 }
 
 template <bool DUAL>
@@ -583,9 +577,14 @@ __device__ __forceinline__ Item fused_tile(const FusedParams& f, const FwdParams
   const bool late = !next.valid || s_info[0] >= p.plan[0] - 2 * (int)gridDim.x;
   bool started = false;
   if (next.valid) {
-    if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, next, false, gated);
-    __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-    started = s_info[3] != 0;
+    if (DUAL && *gated) {
+      started = true;   // GEMM1's gate is the same for every tile: acquired once
+    } else {
+      if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, next, false);
+      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+      started = s_info[3] != 0;
+      if (DUAL && started) *gated = true;
+    }
     if (started) start_claimed<DUAL>(p, lds0, next);
   }
   epilogue<C>(p, it, acc);
@@ -603,16 +602,19 @@ template <bool DUAL>
 __device__ __forceinline__ void gemm_phase(const FusedParams& f, const FwdParams& p, const uint8_t* smem,
                                            uint32_t lds0, int* s_info, int xcd, const int32_t* mbase) {
   int li = 0, npend = 0;
-  bool gated = false;   // thread 0: GEMM1's gate acquired
+  bool gated = false;   // GEMM1's gate acquired (the same in every thread)
   Item it = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
   bool started = false;
   while (it.valid) {
     if (!started) {
-      if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, it, true, &gated);
-      __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-      if (!s_info[3]) {   // the wait expired: skip the tile
-        it = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
-        continue;
+      if (!(DUAL && gated)) {
+        if (threadIdx.x == 0) s_info[3] = gate<DUAL>(f, mbase, it, true);
+        __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+        if (!s_info[3]) {   // the wait expired: skip the tile
+          it = claim_rows(p.plan, p.offsets, p.head, p.E, p.n_tiles, BigTile<DUAL>::NCOL, s_info, li, xcd);
+          continue;
+        }
+        if (DUAL) gated = true;
       }
       start_claimed<DUAL>(p, lds0, it);
     }
