@@ -473,9 +473,10 @@ def single_launch_ok(wl, bwd):
 
 
 def ready_queue_ok(wl):
-    """The readiness-gated launch's rules (bf16 routed experts, D and H
-    multiples of 64)."""
-    return not wl.mxfp8 and wl.D % 64 == 0 and wl.H % 64 == 0
+    """The readiness-gated launch's rules (routed experts; bf16 with D and H
+    multiples of 64, MXFP8 with D and H multiples of 128)."""
+    m = 128 if wl.mxfp8 else 64
+    return wl.D % m == 0 and wl.H % m == 0
 
 
 def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=False, shared_expert=False,
@@ -541,7 +542,7 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
     if single and ready_queue_ok(wl):
         # dispatch, GEMM1 and GEMM2 in one readiness-gated launch (outputs
         # bitwise the staged launches'), timed call by call like layer_call_ms
-        lay_r = M.MoeLayer(w, wl.N, wl.K, mxfp8=False, drop=drop, renorm=wl.renorm, sched=M.MOE_SCHED_READY)
+        lay_r = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, sched=M.MOE_SCHED_READY)
         ready_out = {"layer_fwd_ms": time_layer(lay_r), "staged_layer_fwd_ms": layer_ms,
                      "note": "moe_layer_fwd with MOE_SCHED_READY: router and route launches, then dispatch, "
                              "GEMM1 and GEMM2 in one persistent launch (GEMM2 tiles gated per GEMM1 row "

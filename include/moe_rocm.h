@@ -107,8 +107,8 @@ typedef struct moe_dims {
    * moe_route appends counts[E] = N and offsets[E+1] (its segment, N rows
    * rounded up to align, after the routed ones; so counts/offsets hold E + 1 /
    * E + 2 entries), and rows_cap grows by N + align - 1.  moe_dispatch,
-   * moe_combine and moe_combine_bwd reject it (MOE_ERR_UNSUPPORTED), as does
-   * the MOE_SCHED_READY forward. */
+   * moe_combine and moe_combine_bwd reject it (MOE_ERR_UNSUPPORTED), as do
+   * the MOE_SCHED_READY and MOE_SCHED_SINGLE layers. */
   int32_t n_shared;
   int32_t reserved;     /* 0 */
 } moe_dims;
@@ -311,13 +311,16 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * gradient takes H = bf16(silu(G) U) recomputed from the saved bf16 G and U
  * instead of the dequantized h_q; h_s is then ignored. */
 #define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
-#define MOE_SCHED_READY 1   /* bf16: dispatch, GEMM1 and GEMM2 in one persistent
+#define MOE_SCHED_READY 1   /* dispatch, GEMM1 and GEMM2 in one persistent
                                launch: GEMM1 tiles (in the staged launch's queue
                                order) gated on the dispatch, GEMM2 tiles gated on
                                their GEMM1 row blocks, so GEMM2 starts while
-                               GEMM1's last tiles run.  MOE_ERR_UNSUPPORTED for
-                               MXFP8, a shared expert, or D, H off the rule
-                               D % 64 == 0 and H % 64 == 0                       */
+                               GEMM1's last tiles run.  bf16: align 1,
+                               D % 64 == 0 and H % 64 == 0.  MXFP8 (the dispatch
+                               quantizes and zeroes the padding rows, GEMM1
+                               stores H quantized): D % 128 == 0,
+                               H % 128 == 0.  MOE_ERR_UNSUPPORTED for a shared
+                               expert or shapes off these rules                 */
 /* MOE_SCHED_SINGLE (KOSMOS section 3.3, Figure 6: one launch from route to
  * fold): the whole bf16 layer forward in one persistent launch, after a
  * one-workgroup reset of its barrier words.  Its workgroups (one per CU) run
@@ -326,9 +329,9 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * by a grid barrier, then the MOE_SCHED_READY queue (dispatch, GEMM1 after
  * it, GEMM2 gated on GEMM1 row blocks) followed by the fold, which
  * waits until every workgroup has stored its GEMM2 tiles.  Every output is
- * bitwise the staged forward's.  Same rules as MOE_SCHED_READY, and also the
- * tiled router (D % 64 == 0, 16 <= E <= 512), K <= 32, no grouped top-K and
- * no aux loss; else MOE_ERR_UNSUPPORTED.  Workspace MOE_OP_LAYER_FWD.
+ * bitwise the staged forward's.  bf16 only, under the bf16 rules of
+ * MOE_SCHED_READY and also the tiled router (D % 64 == 0, 16 <= E <= 512),
+ * K <= 32, no grouped top-K and no aux loss; else MOE_ERR_UNSUPPORTED.  Workspace MOE_OP_LAYER_FWD.
  * moe_layer_bwd with MOE_SCHED_SINGLE (KOSMOS section 3.3.2) runs the whole
  * bf16 backward in one persistent launch (after the same kind of reset):
  * the combine backward and the GEMM plans; the down dgrad (SwiGLU backward)

@@ -563,9 +563,15 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   if (st) return st;
   const bool ready = a->sched == MOE_SCHED_READY;
   const bool single = a->sched == MOE_SCHED_SINGLE;
-  // the readiness-ordered launch is the bf16 persistent engine, routed experts only
-  if ((ready || single) && (mx || d.n_shared || d.align != 1 || !moe::gemm_fwd_fast_ok(d.D, d.H) ||
-                            !moe::gemm_fwd_fast_ok(d.H, d.D)))
+  // the readiness-ordered launches run the persistent GEMM engine on routed
+  // experts only: bf16 unpadded, or MXFP8 (READY only) with both GEMMs'
+  // reduction dimensions whole 128-value steps
+  if ((ready || single) && d.n_shared) return MOE_ERR_UNSUPPORTED;
+  if (single && mx) return MOE_ERR_UNSUPPORTED;
+  if ((ready || single) && !mx &&
+      (d.align != 1 || !moe::gemm_fwd_fast_ok(d.D, d.H) || !moe::gemm_fwd_fast_ok(d.H, d.D)))
+    return MOE_ERR_UNSUPPORTED;
+  if (ready && mx && (d.D % 128 || d.H % 128 || d.D * d.H >= (int64_t(1) << 31)))
     return MOE_ERR_UNSUPPORTED;
   // the single launch also runs the tiled router and the plain top-K
   if (single && (!moe::layer_fwd_single_ok(d.D, d.E, d.K) || d.n_group > 1 ||
@@ -647,7 +653,22 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                           sv->topk_prob, sv->counts, sv->offsets, sv->dst_rows, sv->row_route,
                           ws_route, s, d.n_group, d.topk_group, aux, d.n_shared, sv->status);
   if (e == hipSuccess && aux) e = moe::launch_aux_loss(ws_route, d.N, d.E, d.K, sv->counts, a->aux_alpha, sv->aux, s);
-  if (mx) {
+  if (mx && ready) {
+    // quantize-on-dispatch, GEMM1 (H stored quantized) and GEMM2 in one
+    // persistent launch scheduled by readiness
+    moe::ExpertsFwd xf{d.E,     d.K,        d.D,      d.H,      rc,    d.N,   sv->offsets, sv->row_route,
+                       sv->dst_rows, a->x, a->wg_q, a->wu_q, a->wd_q, sv->xd_q, sv->g, sv->u,
+                       nullptr, sv->y,      sv->status, a->ready_test_polls};
+    xf.mx = true;
+    xf.xd_s = sv->xd_s;
+    xf.wg_s = a->wg_s;
+    xf.wu_s = a->wu_s;
+    xf.wd_s = a->wd_s;
+    xf.h_q = sv->h_q;
+    xf.h_s = sv->h_s;
+    xf.counts = sv->counts;
+    if (e == hipSuccess) e = moe::launch_experts_fwd_fused(xf, table, s);
+  } else if (mx) {
     // quantize-on-dispatch; the same launch zeroes the padding rows
     if (e == hipSuccess)
       e = moe::launch_dispatch_mxfp8(a->x, sv->dst_rows, d.N, d.D, d.K, sv->xd_q, sv->xd_s, s, shared_row0,

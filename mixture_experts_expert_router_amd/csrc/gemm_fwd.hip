@@ -455,6 +455,7 @@ struct FusedParams {
   FwdParams g1, g2;             // g1: X_d -> G, U, H;  g2: H -> Y (plans and queue heads in each)
   const uint16_t* x;            // [N][D] token rows
   const int32_t* dst_rows;      // [N][K] row of each route in X_d, -1 if none
+  const int32_t* counts;        // MXFP8: [E] rows of each expert (the rest of its segment is padding)
   int N, K;                     // tokens, routes per token
   int32_t* st;                  // queue state (zeroed by the planner)
   const int32_t* fplan;         // fused plan
@@ -526,12 +527,12 @@ __device__ __forceinline__ bool gate(const FusedParams& f, const int32_t* mbase,
   return block ? wait_ge(f, w, target) : ld_acquire(w) >= target;
 }
 
-template <bool DUAL>
+template <bool DUAL, bool MX>
 __device__ __forceinline__ void start_claimed(const FwdParams& p, uint32_t lds0, const Item& it) {
-  if (it.big) start<BigTile<DUAL>>(p, lds0, it);
-  else if (it.tiny32) start<Tiny32Tile<DUAL, false>>(p, lds0, it);
-  else if (it.tiny) start<TinyTile<DUAL>>(p, lds0, it);
-  else start<SmallTile<DUAL>>(p, lds0, it);
+  if (it.big) start<BigTile<DUAL, MX>>(p, lds0, it);
+  else if (!MX && it.tiny32) start<Tiny32Tile<DUAL, false>>(p, lds0, it);
+  else if (it.tiny) start<TinyTile<DUAL, MX>>(p, lds0, it);
+  else start<SmallTile<DUAL, MX>>(p, lds0, it);
 }
 
 // GEMM1 tiles are published to their row blocks' counts in batches: thread
@@ -585,7 +586,7 @@ __device__ __forceinline__ Item fused_tile(const FusedParams& f, const FwdParams
       started = s_info[3] != 0;
       if (DUAL && started) *gated = true;
     }
-    if (started) start_claimed<DUAL>(p, lds0, next);
+    if (started) start_claimed<DUAL, C::MX>(p, lds0, next);
   }
   epilogue<C>(p, it, acc);
   if (DUAL) {
@@ -598,7 +599,7 @@ __device__ __forceinline__ Item fused_tile(const FusedParams& f, const FwdParams
 
 // Every tile of one GEMM from its per-XCD queues, each after its readiness
 // word; a tile whose bounded wait expires is skipped (reported).
-template <bool DUAL>
+template <bool DUAL, bool MX>
 __device__ __forceinline__ void gemm_phase(const FusedParams& f, const FwdParams& p, const uint8_t* smem,
                                            uint32_t lds0, int* s_info, int xcd, const int32_t* mbase) {
   int li = 0, npend = 0;
@@ -616,17 +617,20 @@ __device__ __forceinline__ void gemm_phase(const FusedParams& f, const FwdParams
         }
         if (DUAL) gated = true;
       }
-      start_claimed<DUAL>(p, lds0, it);
+      start_claimed<DUAL, MX>(p, lds0, it);
     }
     if (it.big)
-      it = fused_tile<BigTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
-    else if (it.tiny32)
+      it = fused_tile<BigTile<DUAL, MX>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started,
+                                               npend);
+    else if (!MX && it.tiny32)
       it = fused_tile<Tiny32Tile<DUAL, false>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it,
                                                      &started, npend);
     else if (it.tiny)
-      it = fused_tile<TinyTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
+      it = fused_tile<TinyTile<DUAL, MX>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started,
+                                                npend);
     else
-      it = fused_tile<SmallTile<DUAL>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started, npend);
+      it = fused_tile<SmallTile<DUAL, MX>, DUAL>(f, p, smem, lds0, s_info, li, xcd, &gated, mbase, it, &started,
+                                                 npend);
   }
   if (DUAL) flush_g1(f, s_info, npend);   // the rest of this workgroup's GEMM1 tiles
 }
@@ -644,7 +648,11 @@ struct FoldArgs {
 };
 
 // The readiness-gated queue: dispatch items, GEMM1 and GEMM2 tiles, then the
-// fold when fold != nullptr.  s_info: kInfoInts ints of LDS.
+// fold when fold != nullptr (bf16 only).  MX: the dispatch quantizes each
+// token row (the MXFP8 dispatch launch's body) and zeroes the padding rows
+// of the 32-row groups, and the GEMMs run on the block-scaled tiles.
+// s_info: kInfoInts ints of LDS.
+template <bool MX>
 __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t* smem, uint32_t lds0, int* s_info,
                                             const FoldArgs* fold) {
   const int E = f.g1.E;
@@ -665,7 +673,15 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
     uint16_t* xd = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(f.g1.a));
     const int step = (int)gridDim.x * 8;
     int t = (int)blockIdx.x * 8 + wave;
-    if (nvec <= VB * 64) {
+    if (MX) {
+      // padding rows of experts blockIdx.x, + G, ...; then the token rows
+      for (int e = blockIdx.x; e < f.g1.E; e += gridDim.x)
+        perm::zero_pad_rows_mx(e, f.counts, f.g1.offsets, D, const_cast<uint8_t*>(f.g1.a),
+                               const_cast<uint8_t*>(f.g1.as), 8);
+      for (; t < f.N; t += step)
+        perm::dispatch_mx_token(t, f.x, f.dst_rows, D, f.K, -1, const_cast<uint8_t*>(f.g1.a),
+                                const_cast<uint8_t*>(f.g1.as));
+    } else if (nvec <= VB * 64) {
       uint4 cur[VB], nxt[VB];
       auto load = [&](uint4 (&r)[VB], int tok) {
         const uint16_t* src = f.x + (int64_t)tok * D;
@@ -717,10 +733,10 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
   }
 
   // ---- 2. GEMM1 tiles, each after its expert is ready --------------------------
-  gemm_phase<true>(f, f.g1, smem, lds0, s_info, xcd, mbase);
+  gemm_phase<true, MX>(f, f.g1, smem, lds0, s_info, xcd, mbase);
   // ---- 3. GEMM2 tiles, each after its GEMM1 row block ---------------------------
-  gemm_phase<false>(f, f.g2, smem, lds0, s_info, xcd, mbase);
-  if (!fold) return;
+  gemm_phase<false, MX>(f, f.g2, smem, lds0, s_info, xcd, mbase);
+  if (MX || !fold) return;
 
   // ---- 4. the fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] -------------------
   __syncthreads();   // the workgroup's stores precede thread 0's release below
@@ -745,11 +761,12 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
   }
 }
 
+template <bool MX>
 __global__ __launch_bounds__(512) void experts_fwd_fused_kernel(FusedParams f) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<MX>()];
   __shared__ int s_info[kInfoInts];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  fused_items(f, smem, lds0, s_info, nullptr);
+  fused_items<MX>(f, smem, lds0, s_info, nullptr);
 }
 
 // Fused planner: one workgroup, after the GEMM1 plan (gplan): each expert's
@@ -948,7 +965,7 @@ __global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p
   if (!grid_sync(f, p.bar + 3, s_info)) return;
 
   // ---- 5. dispatch, GEMM1, GEMM2 by readiness, then the fold ------------------
-  fused_items(f, smem, lds0, s_info, &p.fold);
+  fused_items<false>(f, smem, lds0, s_info, &p.fold);
 }
 
 __global__ void single_reset_kernel(int32_t* bar, int n, int32_t* status) {
@@ -1045,8 +1062,24 @@ void fused_params(const ExpertsFwd& x, int32_t* ws, FusedParams& f, int32_t** gp
   g2.a = (const uint8_t*)x.h;
   g2.b0 = (const uint8_t*)x.w_down;
   g2.c0 = (uint16_t*)x.y;
+  if (x.mx) {
+    // E4M3 operands (a step is 128 values), E8M0 scales; GEMM1 stores G, U
+    // and H quantized (no bf16 H), GEMM2 reads the quantized H
+    g1.nk = (int)(x.D / tile::kRB);
+    g1.as = x.xd_s;
+    g1.bs0 = x.wg_s;
+    g1.bs1 = x.wu_s;
+    g1.c2 = nullptr;
+    g1.hq = x.h_q;
+    g1.hs = x.h_s;
+    g2.nk = (int)(x.H / tile::kRB);
+    g2.a = x.h_q;
+    g2.as = x.h_s;
+    g2.bs0 = x.wd_s;
+  }
   f.x = (const uint16_t*)x.x;
   f.dst_rows = x.dst_rows;
+  f.counts = x.counts;
   f.N = (int)x.N_tokens;
   f.K = (int)x.K;
   f.nt1 = (int)((x.H + BigTile<true>::NCOL - 1) / BigTile<true>::NCOL);
@@ -1099,9 +1132,11 @@ hipError_t launch_experts_fwd_fused(const ExpertsFwd& x, int32_t* ws, hipStream_
   plan_fused_kernel<<<1, 1024, 0, s>>>(x.offsets, (int)x.E, max_mb, f.nt2, gplan, const_cast<int32_t*>(f.fplan),
                                        f.st);
   int grid = 0;
-  hipError_t err = resident_grid((const void*)experts_fwd_fused_kernel, &grid);
+  const void* kern = x.mx ? (const void*)experts_fwd_fused_kernel<true> : (const void*)experts_fwd_fused_kernel<false>;
+  hipError_t err = resident_grid(kern, &grid);
   if (err != hipSuccess) return err;
-  experts_fwd_fused_kernel<<<grid, 512, 0, s>>>(f);
+  if (x.mx) experts_fwd_fused_kernel<true><<<grid, 512, 0, s>>>(f);
+  else experts_fwd_fused_kernel<false><<<grid, 512, 0, s>>>(f);
   return hipGetLastError();
 }
 

@@ -156,6 +156,17 @@ struct ExpertsFwd {
   void* y;
   int32_t* status;   // optional device status word: MOE_STATUS_WAIT_EXPIRED is or-ed in
   int test_polls;    // > 0: withhold readiness, bound every wait to this many polls
+  // MXFP8 (the readiness-gated launch): xd, w_* hold E4M3 codes, these their
+  // E8M0 scales; h_q / h_s the quantized H (h is not written); counts for the
+  // padding rows of the 32-row groups
+  bool mx = false;
+  const uint8_t* xd_s = nullptr;
+  const uint8_t* wg_s = nullptr;
+  const uint8_t* wu_s = nullptr;
+  const uint8_t* wd_s = nullptr;
+  uint8_t* h_q = nullptr;
+  uint8_t* h_s = nullptr;
+  const int32_t* counts = nullptr;
 };
 
 // gemm_fwd.hip: persistent forward grouped GEMM, bf16 or MXFP8 (shape and

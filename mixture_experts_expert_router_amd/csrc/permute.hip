@@ -79,24 +79,6 @@ __device__ __forceinline__ uint2 quant_vec(uint4 v, int& code_out) {
   return make_uint2(e4m3x4(f[0], f[1], f[2], f[3], e), e4m3x4(f[4], f[5], f[6], f[7], e));
 }
 
-// Zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of expert e in
-// the MXFP8 dispatch output: codes (D bytes a row, 16-byte stores) and scales
-// (D/32 bytes a row).  Run by the dispatch launch's trailing workgroups, one
-// per expert, its four waves taking the rows in turn.
-__device__ __forceinline__ void zero_pad_rows_mx(int e, const int32_t* __restrict__ counts,
-                                                 const int32_t* __restrict__ offsets, int D,
-                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
-  const int nb = D >> 5;
-  for (int64_t r = r0 + wave; r < r1; r += 4) {
-    uint4* pq = reinterpret_cast<uint4*>(q + r * D);
-    for (int i = lane; i < (D >> 4); i += 64) pq[i] = make_uint4(0, 0, 0, 0);
-    uint8_t* ps = sc + r * nb;
-    for (int i = lane; i < nb; i += 64) ps[i] = 0;
-  }
-}
-
 // dispatch (MXFP8): quantize each token row once along D, write q and scales
 // to its K rows.  D is a multiple of 32, so 4 consecutive lanes own a block
 // and every wave-wide pass covers whole blocks.
@@ -110,7 +92,7 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
   // trailing workgroups: one per expert, zeroing its padding rows
   const int tok_blocks = (N + 3) / 4;
   if (pad_counts && (int)blockIdx.x >= tok_blocks) {
-    zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc);
+    perm::zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc, 4);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -145,9 +127,8 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
   }
 }
 
-// Same result for D % 128 == 0: each lane quantizes 16 adjacent elements (a
-// 32-block is a lane pair), so a route gets one 16-byte data store per lane
-// and lanes 8i pack the codes of four consecutive blocks into one 4-byte store.
+// Same result for D % 128 == 0, a wave per token (perm::dispatch_mx_token:
+// a lane quantizes 16 adjacent elements, a 32-block is a lane pair).
 using perm::quant4;
 
 __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16_t* __restrict__ x,
@@ -160,59 +141,13 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
   // trailing workgroups: one per expert, zeroing its padding rows
   const int tok_blocks = (N + 3) / 4;
   if (pad_counts && (int)blockIdx.x >= tok_blocks) {
-    zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc);
+    perm::zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc, 4);
     return;
   }
-  constexpr int PP = 4;   // lane pairs of vectors per pass
-  const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= N) return;
-  const int KK = K + (shared_row0 ? 1 : 0);
   const int srow = shared_row0 ? *shared_row0 + t : -1;   // the shared expert's row of this token
-  const int npair = D >> 4;              // 16-element pieces per row
-  const int nblk = D >> 5;
-  const uint16_t* src = x + (int64_t)t * D;
-  for (int p0 = 0; p0 < npair; p0 += kWave * PP) {
-    uint4 qv[PP];
-    uint32_t packed[PP];
-#pragma unroll
-    for (int j = 0; j < PP; ++j) {
-      const int pc = p0 + lane + j * kWave;   // this lane's 16-element piece
-      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
-      if (pc < npair) {
-        r0 = ldg16(src + pc * 16);
-        r1 = ldg16(src + pc * 16 + 8);
-      }
-      float f[16] = {bf16lo(r0.x), bf16hi(r0.x), bf16lo(r0.y), bf16hi(r0.y), bf16lo(r0.z), bf16hi(r0.z),
-                     bf16lo(r0.w), bf16hi(r0.w), bf16lo(r1.x), bf16hi(r1.x), bf16lo(r1.y), bf16hi(r1.y),
-                     bf16lo(r1.z), bf16hi(r1.z), bf16lo(r1.w), bf16hi(r1.w)};
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      const int code = e8m0_code(amax);
-      const int e = code - 127;
-      qv[j] = make_uint4(quant4(f, e), quant4(f + 4, e), quant4(f + 8, e), quant4(f + 12, e));
-      // block codes of lanes 8i, 8i+2, 8i+4, 8i+6 into lane 8i
-      const uint32_t c1 = (uint32_t)__shfl_down(code, 2, 64), c2 = (uint32_t)__shfl_down(code, 4, 64),
-                     c3 = (uint32_t)__shfl_down(code, 6, 64);
-      packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
-    for (int k = 0; k < KK; ++k) {
-      const int dk = route_row(dst_rows, t, K, k, srow);
-      if (dk < 0) continue;
-      uint8_t* qrow = q + (int64_t)dk * D;
-      uint8_t* crow = sc + (int64_t)dk * nblk;
-#pragma unroll
-      for (int j = 0; j < PP; ++j) {
-        const int pc = p0 + lane + j * kWave;
-        if (pc < npair) {
-          *reinterpret_cast<uint4*>(qrow + pc * 16) = qv[j];
-          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(crow + (pc >> 1)) = packed[j];
-        }
-      }
-    }
-  }
+  perm::dispatch_mx_token(t, x, dst_rows, D, K, srow, q, sc);
 }
 
 // zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert:

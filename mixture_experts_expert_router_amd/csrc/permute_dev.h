@@ -22,6 +22,81 @@ __device__ __forceinline__ uint32_t quant4(const float* f, int e) {
   return e4m3x4(f[0], f[1], f[2], f[3], e);
 }
 
+// MXFP8 dispatch of token t by one wave (D % 128 == 0): the row quantized
+// once along D and its codes and scales written to the token's rows (route k
+// to dst_rows[t, k], the shared expert's row srow last when srow >= 0).  A
+// lane takes 16 adjacent elements, so a 32-block is a lane pair; a route gets
+// one 16-byte code store a lane, and lanes 8i pack the codes of four
+// consecutive blocks into one 4-byte store.
+__device__ __forceinline__ void dispatch_mx_token(int t, const uint16_t* __restrict__ x,
+                                                  const int32_t* __restrict__ dst_rows, int D, int K, int srow,
+                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  constexpr int PP = 4;   // lane pairs of vectors per pass
+  const int lane = threadIdx.x & 63;
+  const int KK = K + (srow >= 0 ? 1 : 0);
+  const int npair = D >> 4;              // 16-element pieces per row
+  const int nblk = D >> 5;
+  const uint16_t* src = x + (int64_t)t * D;
+  for (int p0 = 0; p0 < npair; p0 += kWave * PP) {
+    uint4 qv[PP];
+    uint32_t packed[PP];
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      const int pc = p0 + lane + j * kWave;   // this lane's 16-element piece
+      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
+      if (pc < npair) {
+        r0 = ldg16(src + pc * 16);
+        r1 = ldg16(src + pc * 16 + 8);
+      }
+      float f[16] = {bf16lo(r0.x), bf16hi(r0.x), bf16lo(r0.y), bf16hi(r0.y), bf16lo(r0.z), bf16hi(r0.z),
+                     bf16lo(r0.w), bf16hi(r0.w), bf16lo(r1.x), bf16hi(r1.x), bf16lo(r1.y), bf16hi(r1.y),
+                     bf16lo(r1.z), bf16hi(r1.z), bf16lo(r1.w), bf16hi(r1.w)};
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const int code = e8m0_code(amax);
+      const int e = code - 127;
+      qv[j] = make_uint4(quant4(f, e), quant4(f + 4, e), quant4(f + 8, e), quant4(f + 12, e));
+      // block codes of lanes 8i, 8i+2, 8i+4, 8i+6 into lane 8i
+      const uint32_t c1 = (uint32_t)__shfl_down(code, 2, 64), c2 = (uint32_t)__shfl_down(code, 4, 64),
+                     c3 = (uint32_t)__shfl_down(code, 6, 64);
+      packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    for (int k = 0; k < KK; ++k) {
+      const int dk = k < K ? dst_rows[(int64_t)t * K + k] : srow;
+      if (dk < 0) continue;
+      uint8_t* qrow = q + (int64_t)dk * D;
+      uint8_t* crow = sc + (int64_t)dk * nblk;
+#pragma unroll
+      for (int j = 0; j < PP; ++j) {
+        const int pc = p0 + lane + j * kWave;
+        if (pc < npair) {
+          *reinterpret_cast<uint4*>(qrow + pc * 16) = qv[j];
+          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(crow + (pc >> 1)) = packed[j];
+        }
+      }
+    }
+  }
+}
+
+// Zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of expert e in
+// the MXFP8 dispatch output: codes (D bytes a row, 16-byte stores) and scales
+// (D/32 bytes a row), the workgroup's nwaves waves taking the rows in turn.
+__device__ __forceinline__ void zero_pad_rows_mx(int e, const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ offsets, int D,
+                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ sc, int nwaves) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
+  const int nb = D >> 5;
+  for (int64_t r = r0 + wave; r < r1; r += nwaves) {
+    uint4* pq = reinterpret_cast<uint4*>(q + r * D);
+    for (int i = lane; i < (D >> 4); i += 64) pq[i] = make_uint4(0, 0, 0, 0);
+    uint8_t* ps = sc + r * nb;
+    for (int i = lane; i < nb; i += 64) ps[i] = 0;
+  }
+}
+
 // The fold (combine) of token rows: out[t] = bf16(sum over k of w[t,k]
 // y[dst[t,k]] (+ addend[t])), fp32 fmaf in ascending k, the shared expert's
 // row (weight 1) last.  A row of nvec 16-byte vectors is cut into

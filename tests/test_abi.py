@@ -165,13 +165,17 @@ def _full_saved(lib, d, dt, base=1 << 20):
 
 
 def test_ready_schedule_is_refused_where_it_does_not_run():
-    """MOE_SCHED_READY exists for bf16 routed experts with D, H multiples of
-    64; MXFP8, a shared expert, and other widths get MOE_ERR_UNSUPPORTED
-    instead of silently running staged.  (Every pointer is a fake aligned
-    address: the call returns before any launch.)"""
+    """MOE_SCHED_READY exists for routed experts: bf16 unpadded with D, H
+    multiples of 64, MXFP8 with D, H multiples of 128.  A shared expert,
+    padded bf16 and other widths get MOE_ERR_UNSUPPORTED instead of silently
+    running staged.  (Every pointer is a fake aligned address: the call
+    returns before any launch.)"""
     lib = M.load()
-    cases = [(M.dims(64, 256, 8, 2, 128, align=32), M.MOE_MXFP8),
+    cases = [(M.dims(64, 288, 8, 2, 128, align=32), M.MOE_MXFP8),
+             (M.dims(64, 256, 8, 2, 160, align=32), M.MOE_MXFP8),
+             (M.dims(64, 256, 8, 2, 128, align=32, n_shared=1), M.MOE_MXFP8),
              (M.dims(64, 256, 8, 2, 128, n_shared=1), M.MOE_BF16),
+             (M.dims(64, 256, 8, 2, 128, align=32), M.MOE_BF16),
              (M.dims(64, 264, 8, 2, 128), M.MOE_BF16),
              (M.dims(64, 256, 8, 2, 136), M.MOE_BF16)]
     for d, dt in cases:
@@ -186,8 +190,8 @@ def test_ready_schedule_is_refused_where_it_does_not_run():
 
 
 def test_single_schedule_is_refused_where_it_does_not_run():
-    """MOE_SCHED_SINGLE has the READY rules plus the tiled router (16 <= E <=
-    512), the plain top-K and no aux loss; anything else gets
+    """MOE_SCHED_SINGLE has the bf16 READY rules plus the tiled router (16 <=
+    E <= 512), the plain top-K and no aux loss; MXFP8 or anything else gets
     MOE_ERR_UNSUPPORTED before any launch (fake aligned pointers)."""
     lib = M.load()
     cases = [(M.dims(64, 256, 32, 2, 128, align=32), M.MOE_MXFP8, 0.0),

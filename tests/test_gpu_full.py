@@ -237,6 +237,23 @@ def test_full_size_forward_mxfp8():
     q = host(sv["xd_q"][: int(off[-1])])
     for e in np.nonzero(off[1:] - off[:-1] > cnt)[0][:16]:
         assert not q[off[e] + cnt[e]: off[e + 1]].any()
+    # the readiness-gated launch (quantize-on-dispatch, GEMM1, GEMM2 in one
+    # persistent launch) reproduces the staged MXFP8 results bit for bit,
+    # padding rows included, every expert-row output poisoned first
+    n = int(off[-1])
+    keys = ("xd_q", "xd_s", "g", "u", "h_q", "h_s", "y")
+    staged = {k: host(sv[k][:n].view(torch.uint8)).copy() for k in keys}
+    staged_out = bits(layer.out)
+    for k in keys:
+        sv[k].view(torch.uint8).fill_(0xA5)
+    layer.out.view(torch.uint8).fill_(0xA5)
+    layer.sched = M.MOE_SCHED_READY
+    layer.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(sv["status"])[0]) == 0
+    for k in keys:
+        assert np.array_equal(host(sv[k][:n].view(torch.uint8)), staged[k]), k
+    assert np.array_equal(bits(layer.out), staged_out)
 
 
 def test_full_size_backward_qwen3():

@@ -647,6 +647,67 @@ def test_layer_deterministic_and_overwrites_outputs(sched):
         assert np.array_equal(runs[0][k], runs[1][k]), k
 
 
+READY_MX_CASES = {
+    # padding rows in every expert, GEMM2's last n-tile ragged (D = 640)
+    "mx_small": S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_small", N=300, D=640, E=32, K=8, H=384),
+    # most experts empty, most dispatch shares empty
+    "mx_five_tokens": S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_five_tokens", N=5, D=256, E=16, K=4, H=128),
+    # thousands of GEMM1 tiles: full publication batches, Big and Small tiles
+    "mx_many_tiles": S.scaled(S.WORKLOADS["dsv3_mxfp8"], "mx_many_tiles", N=6144, D=512, E=64, K=8, H=2048),
+}
+
+
+@pytest.mark.parametrize("name", list(READY_MX_CASES))
+def test_ready_queue_mxfp8_equals_staged(name):
+    """The readiness-gated MXFP8 launch (quantize-on-dispatch shares with the
+    padding rows zeroed, block-scaled GEMM1 storing G, U and the quantized H,
+    GEMM2 gated per GEMM1 row block) stores every row of X_d, its scales, G,
+    U, H, H's scales and Y bitwise as the staged MXFP8 launches do, outputs
+    poisoned first."""
+    wl = READY_MX_CASES[name]
+    print(f"READY fwd mxfp8 {name}", flush=True)
+    inp = S.make_inputs(wl, 6)
+    w, _ = _weights(inp, mxfp8=True)
+    x = dev_bf16(inp.x)
+    staged = M.MoeLayer(w, wl.N, wl.K, mxfp8=True)
+    want = staged.forward(x)
+    ready = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, sched=M.MOE_SCHED_READY)
+    for t in list(ready.saved.values()) + [ready.out]:
+        t.view(torch.uint8).fill_(0xA5)
+    got = ready.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(ready.saved["status"])[0]) == 0
+    n = int(host(staged.saved["offsets"])[-1])
+    for k in ("counts", "offsets", "dst_rows", "xd_q", "xd_s", "g", "u", "h_q", "h_s", "y"):
+        a, b = staged.saved[k], ready.saved[k]
+        if k not in ("counts", "offsets", "dst_rows"):
+            a, b = a[:n], b[:n]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), k
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), "out"
+
+
+def test_ready_mxfp8_wait_expiry_is_reported_and_the_next_call_recovers():
+    """The MXFP8 form of the forced give-up: every bounded wait expires and
+    is reported, all kernels exit, and the next call equals the staged
+    MXFP8 forward bit for bit."""
+    wl = READY_MX_CASES["mx_small"]
+    print("READY schedule mxfp8: forced wait expiry", flush=True)
+    inp = S.make_inputs(wl, 9)
+    w, _ = _weights(inp, mxfp8=True)
+    x = dev_bf16(inp.x)
+    want = M.MoeLayer(w, wl.N, wl.K, mxfp8=True).forward(x).clone()
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=True, sched=M.MOE_SCHED_READY)
+    layer.ready_test_polls = 4
+    layer.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(layer.saved["status"])[0]) == M.MOE_STATUS_WAIT_EXPIRED
+    layer.ready_test_polls = 0
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert int(host(layer.saved["status"])[0]) == 0
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
 def test_ready_wait_expiry_is_reported_and_the_next_call_recovers():
     """A forced give-up from the host (readiness withheld, every wait bounded
     to a few polls): each wait expires, the waiting items are skipped, all
