@@ -678,9 +678,14 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
       for (int e = blockIdx.x; e < f.g1.E; e += gridDim.x)
         perm::zero_pad_rows_mx(e, f.counts, f.g1.offsets, D, const_cast<uint8_t*>(f.g1.a),
                                const_cast<uint8_t*>(f.g1.as), 8);
-      for (; t < f.N; t += step)
-        perm::dispatch_mx_token(t, f.x, f.dst_rows, D, f.K, -1, const_cast<uint8_t*>(f.g1.a),
+      // a wave per row segment of a token
+      const int nseg = perm::mx_dispatch_segs(D);
+      const int nitems = f.N * nseg;
+      for (int i = t; i < nitems; i += step) {
+        const int tt = i / nseg;
+        perm::dispatch_mx_token(tt, i - tt * nseg, f.x, f.dst_rows, D, f.K, -1, const_cast<uint8_t*>(f.g1.a),
                                 const_cast<uint8_t*>(f.g1.as));
+      }
     } else if (nvec <= VB * 64) {
       uint4 cur[VB], nxt[VB];
       auto load = [&](uint4 (&r)[VB], int tok) {

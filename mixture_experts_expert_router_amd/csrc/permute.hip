@@ -127,8 +127,9 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint16_t* __r
   }
 }
 
-// Same result for D % 128 == 0, a wave per token (perm::dispatch_mx_token:
-// a lane quantizes 16 adjacent elements, a 32-block is a lane pair).
+// Same result for D % 128 == 0, a wave per row segment of a token
+// (perm::dispatch_mx_token: a lane quantizes 16 adjacent elements, a 32-block
+// is a lane pair).
 using perm::quant4;
 
 __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16_t* __restrict__ x,
@@ -139,15 +140,17 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
                                                              const int32_t* __restrict__ shared_row0,
     const int32_t* __restrict__ pad_counts, const int32_t* __restrict__ pad_offsets) {
   // trailing workgroups: one per expert, zeroing its padding rows
-  const int tok_blocks = (N + 3) / 4;
+  const int nseg = perm::mx_dispatch_segs(D);
+  const int tok_blocks = (int)(((int64_t)N * nseg + 3) / 4);
   if (pad_counts && (int)blockIdx.x >= tok_blocks) {
     perm::zero_pad_rows_mx((int)blockIdx.x - tok_blocks, pad_counts, pad_offsets, D, q, sc, 4);
     return;
   }
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = w / nseg;
   if (t >= N) return;
   const int srow = shared_row0 ? *shared_row0 + t : -1;   // the shared expert's row of this token
-  perm::dispatch_mx_token(t, x, dst_rows, D, K, srow, q, sc);
+  perm::dispatch_mx_token(t, w - t * nseg, x, dst_rows, D, K, srow, q, sc);
 }
 
 // zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert:
@@ -349,8 +352,10 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
                                  int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s, const int32_t* shared_row0,
                                  const int32_t* pad_counts, const int32_t* pad_offsets, int64_t pad_E) {
   if (N == 0) return hipSuccess;
-  const unsigned grid = waves_grid(N) + (pad_counts ? (unsigned)pad_E : 0u);
-  if (D % 128 == 0 && ((uintptr_t)sc & 3) == 0)
+  const bool packed = D % 128 == 0 && ((uintptr_t)sc & 3) == 0;
+  const unsigned grid = waves_grid(packed ? N * perm::mx_dispatch_segs((int)D) : N) +
+                        (pad_counts ? (unsigned)pad_E : 0u);
+  if (packed)
     dispatch_mxfp8_packed_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D, (int)K, q,
                                                       sc, shared_row0, pad_counts, pad_offsets);
   else

@@ -22,22 +22,31 @@ __device__ __forceinline__ uint32_t quant4(const float* f, int e) {
   return e4m3x4(f[0], f[1], f[2], f[3], e);
 }
 
-// MXFP8 dispatch of token t by one wave (D % 128 == 0): the row quantized
-// once along D and its codes and scales written to the token's rows (route k
-// to dst_rows[t, k], the shared expert's row srow last when srow >= 0).  A
-// lane takes 16 adjacent elements, so a 32-block is a lane pair; a route gets
-// one 16-byte code store a lane, and lanes 8i pack the codes of four
-// consecutive blocks into one 4-byte store.
-__device__ __forceinline__ void dispatch_mx_token(int t, const uint16_t* __restrict__ x,
+// MXFP8 dispatch of segment seg of token t's row by one wave (D % 128 == 0):
+// the segment quantized once and its codes and scales written to the token's
+// rows (route k to dst_rows[t, k], the shared expert's row srow last when
+// srow >= 0).  A lane takes 16 adjacent elements, so a 32-block is a lane
+// pair; a route gets one 16-byte code store a lane, and lanes 8i pack the
+// codes of four consecutive blocks into one 4-byte store.  A segment is one
+// pass of kMxSegPieces 16-element pieces (4 a lane), so a wave's loads never
+// queue behind its own stores of an earlier pass (vector memory operations
+// complete in order).
+constexpr int kMxSegPieces = kWave * 4;
+__device__ __host__ __forceinline__ int mx_dispatch_segs(int D) {
+  return ((D >> 4) + kMxSegPieces - 1) / kMxSegPieces;
+}
+
+__device__ __forceinline__ void dispatch_mx_token(int t, int seg, const uint16_t* __restrict__ x,
                                                   const int32_t* __restrict__ dst_rows, int D, int K, int srow,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  constexpr int PP = 4;   // lane pairs of vectors per pass
+  constexpr int PP = kMxSegPieces / kWave;   // lane pairs of vectors per pass
   const int lane = threadIdx.x & 63;
   const int KK = K + (srow >= 0 ? 1 : 0);
   const int npair = D >> 4;              // 16-element pieces per row
   const int nblk = D >> 5;
   const uint16_t* src = x + (int64_t)t * D;
-  for (int p0 = 0; p0 < npair; p0 += kWave * PP) {
+  {
+    const int p0 = seg * kMxSegPieces;
     uint4 qv[PP];
     uint32_t packed[PP];
 #pragma unroll
