@@ -94,10 +94,15 @@ def t_star(F, Q, peak_tflops, peak_gbs=PEAK_HBM_GBS):
 # ---------------------------------------------------------------------------
 
 def gemm_source_hash():
+    """Hash of the GEMM kernel sources with comments and blank space taken
+    out, so that a change of wording alone keeps recorded counters valid."""
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

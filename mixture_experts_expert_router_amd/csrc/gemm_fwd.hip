@@ -417,9 +417,12 @@ hipError_t run_fwd(FwdParams p, int32_t* plan, hipStream_t s) {
 // each tile gated on data readiness (KOSMOS section 3.1.1 and section 3.3.1
 // steps 3-4, on one GPU).  A workgroup runs, in order:
 //   1. its share of the dispatch: each token row read once and written to
-//      its routes' rows of X_d (as the dispatch launch does), then one
-//      release adding the share to a count;
-//   2. GEMM1 tiles from the staged launch's per-XCD queues, in its order
+//      its routes' rows of X_d (as the dispatch launch does; MXFP8: quantized
+//      on the way, a wave per row segment, after the share's experts'
+//      padding rows are zeroed), then one release adding the share to a
+//      count;
+//   2. GEMM1 tiles (MXFP8: block-scaled, H stored quantized) from the
+//      staged launch's per-XCD queues, in its order
 //      (the two tile classes interleaved in proportion to their work,
 //      super-blocks of neighbouring tiles on one XCD's L2); a workgroup's
 //      first tile waits until every workgroup's share is counted;
