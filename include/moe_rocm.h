@@ -309,7 +309,12 @@ int moe_grouped_gemm_bwd(const moe_gemm_bwd_args* g, void* ws, size_t ws_bytes, 
  * With saved->h_q NULL (SwiGLU-recompute mode, OLMo-core Appendix A, A.14:
  * H is rebuilt in the backward instead of being saved) the down weight
  * gradient takes H = bf16(silu(G) U) recomputed from the saved bf16 G and U
- * instead of the dequantized h_q; h_s is then ignored. */
+ * instead of the dequantized h_q; h_s is then ignored.
+ * An empty batch (N = 0) is accepted under every schedule: the forward writes
+ * counts and offsets (all 0), row_route (every row -1) and an aux loss of 0;
+ * the backward writes every weight gradient as 0 (and db_r when given).
+ * Buffers that then hold no element (of N tokens, or of rows_cap rows) may be
+ * NULL. */
 #define MOE_SCHED_STAGED 0  /* dispatch, GEMM1, GEMM2: one persistent launch each  */
 #define MOE_SCHED_READY 1   /* dispatch, GEMM1 and GEMM2 in one persistent
                                launch: GEMM1 tiles (in the staged launch's queue

@@ -578,22 +578,24 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
                  (sv->aux != nullptr && a->aux_alpha != 0.0f)))
     return MOE_ERR_UNSUPPORTED;
   if (a->ready_test_polls < 0) return MOE_ERR_SHAPE;
-  REQUIRE(a->x);
+  // buffers of N tokens, or of rows_cap rows, may be NULL when that is 0
+  const bool no_tok = d.N == 0, no_rows = rows_cap_of(d) == 0;
+  REQUIRE_UNLESS(no_tok, a->x);
   REQUIRE(a->w_r);
   OPTIONAL(a->bias);
   OPTIONAL(a->drop);
-  REQUIRE(out);
+  REQUIRE_UNLESS(no_tok, out);
   REQUIRE(ws);
-  REQUIRE(sv->logits);
-  REQUIRE(sv->topk_idx);
-  REQUIRE(sv->topk_prob);
+  REQUIRE_UNLESS(no_tok, sv->logits);
+  REQUIRE_UNLESS(no_tok, sv->topk_idx);
+  REQUIRE_UNLESS(no_tok, sv->topk_prob);
   REQUIRE(sv->counts);
   REQUIRE(sv->offsets);
-  REQUIRE(sv->dst_rows);
-  REQUIRE(sv->row_route);
-  REQUIRE(sv->g);
-  REQUIRE(sv->u);
-  REQUIRE(sv->y);
+  REQUIRE_UNLESS(no_tok, sv->dst_rows);
+  REQUIRE_UNLESS(no_rows, sv->row_route);
+  REQUIRE_UNLESS(no_rows, sv->g);
+  REQUIRE_UNLESS(no_rows, sv->u);
+  REQUIRE_UNLESS(no_rows, sv->y);
   OPTIONAL(sv->status);
   if (mx) {
     OPTIONAL(sv->h);   // not written: the MXFP8 path keeps H quantized only
@@ -603,16 +605,16 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
     REQUIRE(a->wu_s);
     REQUIRE(a->wd_q);
     REQUIRE(a->wd_s);
-    REQUIRE(sv->xd_q);
-    REQUIRE(sv->xd_s);
-    REQUIRE(sv->h_q);
-    REQUIRE(sv->h_s);
+    REQUIRE_UNLESS(no_rows, sv->xd_q);
+    REQUIRE_UNLESS(no_rows, sv->xd_s);
+    REQUIRE_UNLESS(no_rows, sv->h_q);
+    REQUIRE_UNLESS(no_rows, sv->h_s);
   } else {
     REQUIRE(a->w_gate);
     REQUIRE(a->w_up);
     REQUIRE(a->w_down);
-    REQUIRE(sv->xd);
-    REQUIRE(sv->h);
+    REQUIRE_UNLESS(no_rows, sv->xd);
+    REQUIRE_UNLESS(no_rows, sv->h);
   }
   OPTIONAL(sv->aux);
   const bool aux = sv->aux != nullptr && a->aux_alpha != 0.0f;
@@ -626,6 +628,18 @@ int moe_layer_fwd(const moe_layer_args* a, moe_layer_saved* sv, void* out, void*
   int32_t* table = (int32_t*)((char*)ws + rb);
   void* ws_router = (char*)ws + rb + tb;
 
+  if (no_tok) {
+    // no tokens, under every schedule: the route step alone (counts and
+    // offsets 0, every row of row_route -1, no expert row to compute) and an
+    // aux loss of 0
+    hipError_t e = sv->status ? moe::launch_status_clear(sv->status, s) : hipSuccess;
+    if (e == hipSuccess)
+      e = moe::launch_route(nullptr, nullptr, 0, d.E, d.K, d.renorm, d.align, rc, nullptr, nullptr, sv->counts,
+                            sv->offsets, nullptr, sv->row_route, ws_route, s, d.n_group, d.topk_group, false,
+                            d.n_shared, sv->status);
+    if (e == hipSuccess && aux) e = moe::launch_zero_bytes(sv->aux, 4, s);
+    return hip_status(e);
+  }
   if (single) {
     // router, route, dispatch, GEMM1, GEMM2 and the fold in one persistent launch
     moe::LayerFwdSingle one{};
@@ -734,12 +748,32 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     return MOE_ERR_DTYPE;
   // MOE_SCHED_SINGLE: the bf16 routed-expert backward from the saved H, in one launch
   const bool single = a->sched == MOE_SCHED_SINGLE;
-  if (single && (mx || d.n_shared || d.align != 1 || !sv->h || d.E > 512)) return MOE_ERR_UNSUPPORTED;
+  if (single && (mx || d.n_shared || d.align != 1 || (!sv->h && rows_cap_of(d) > 0) || d.E > 512))
+    return MOE_ERR_UNSUPPORTED;
   if (single && a->ready_test_polls < 0) return MOE_ERR_SHAPE;
+  // MXFP8: the block-scaled dgrads run on the persistent engine, whole
+  // 128-element contraction steps over D and over 2H; the router's GEMMs read
+  // dlogits rows in 16-byte chunks
+  if (mx && (d.D % 128 || d.H % 64)) return MOE_ERR_SHAPE;
+  if (gr->dw_r && d.E % 8) return MOE_ERR_SHAPE;
+  if (d.N == 0) {
+    // no tokens, under every schedule: every weight gradient is 0 (dx,
+    // dprob and dlogits hold no element)
+    REQUIRE(gr->dw_gate);
+    REQUIRE(gr->dw_up);
+    REQUIRE(gr->dw_down);
+    OPTIONAL(gr->dw_r);
+    OPTIONAL(gr->db_r);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t Ex = experts_of(d), whd = Ex * d.H * d.D * 2;
+    hipError_t e = moe::launch_zero_bytes(gr->dw_gate, whd, s);
+    if (e == hipSuccess) e = moe::launch_zero_bytes(gr->dw_up, whd, s);
+    if (e == hipSuccess) e = moe::launch_zero_bytes(gr->dw_down, whd, s);
+    if (e == hipSuccess && gr->dw_r) e = moe::launch_zero_bytes(gr->dw_r, d.E * d.D * 2, s);
+    if (e == hipSuccess && gr->dw_r && gr->db_r) e = moe::launch_zero_bytes(gr->db_r, d.E * 4, s);
+    return hip_status(e);
+  }
   if (mx) {
-    // the block-scaled dgrads run on the persistent engine: whole 128-element
-    // contraction steps over D and over 2H
-    if (d.D % 128 || d.H % 64) return MOE_ERR_SHAPE;
     if (mxw) {
       REQUIRE(sv->row_route);
       REQUIRE(a->x);
@@ -784,7 +818,6 @@ int moe_layer_bwd(const moe_layer_args* a, const moe_layer_saved* sv, const void
     REQUIRE(a->w_r);
     OPTIONAL(gr->db_r);
     OPTIONAL(gr->dlogits);
-    if (d.E % 8) return MOE_ERR_SHAPE;   // the router's GEMMs read dlogits rows in 16-byte chunks
   }
   const int64_t rc = rows_cap_of(d);
   const int64_t Ex = experts_of(d);

@@ -91,6 +91,10 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
                                  int64_t K, uint8_t* q, uint8_t* sc, hipStream_t s,
                                  const int32_t* shared_row0 = nullptr, const int32_t* pad_counts = nullptr,
                                  const int32_t* pad_offsets = nullptr, int64_t pad_E = 0);
+// zero `bytes` bytes at p (16-byte aligned), with a kernel (no memset node
+// in a captured graph)
+hipError_t launch_zero_bytes(void* p, int64_t bytes, hipStream_t s);
+
 // zero the padding rows of every expert segment in a (row_bytes, a multiple
 // of 16), b and c (optional)
 hipError_t launch_zero_padding(const int32_t* counts, const int32_t* offsets, int64_t E,

@@ -153,6 +153,15 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_packed_kernel(const uint16
   perm::dispatch_mx_token(t, w - t * nseg, x, dst_rows, D, K, srow, q, sc);
 }
 
+// zero n16 16-byte vectors from p, then the bytes up to `bytes`
+__global__ __launch_bounds__(256) void zero_bytes_kernel(uint8_t* __restrict__ p, int64_t n16, int64_t bytes) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint4* q = reinterpret_cast<uint4*>(p);
+  for (int64_t j = i; j < n16; j += stride) q[j] = make_uint4(0, 0, 0, 0);
+  for (int64_t j = n16 * 16 + i; j < bytes; j += stride) p[j] = 0;
+}
+
 // zero the padding rows [offsets[e] + counts[e], offsets[e+1]) of each expert:
 // one workgroup of 16 waves per expert, padding row i on wave i % 16, 16-byte
 // stores for the data rows (row_bytes is a multiple of 16) and bytes for the
@@ -361,6 +370,15 @@ hipError_t launch_dispatch_mxfp8(const void* x, const int32_t* dst_rows, int64_t
   else
     dispatch_mxfp8_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, dst_rows, (int)N, (int)D, (int)K, q, sc,
                                                shared_row0, pad_counts, pad_offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void* p, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks));
+  zero_bytes_kernel<<<grid, 256, 0, s>>>((uint8_t*)p, n16, bytes);
   return hipGetLastError();
 }
 

@@ -733,6 +733,38 @@ def test_ready_wait_expiry_is_reported_and_the_next_call_recovers():
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
 
+@pytest.mark.parametrize("mxfp8,sched", [(False, M.MOE_SCHED_STAGED), (False, M.MOE_SCHED_READY),
+                                         (False, M.MOE_SCHED_SINGLE), (True, M.MOE_SCHED_STAGED),
+                                         (True, M.MOE_SCHED_READY)])
+def test_empty_batch(mxfp8, sched):
+    """N = 0 under every schedule: the forward writes counts and offsets of 0
+    and marks every row unused, the backward writes every weight gradient
+    (and the router's) as 0; outputs poisoned first."""
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8" if mxfp8 else "dsv3_bf16"], "empty", N=8, D=256, E=16, K=4, H=128)
+    print(f"empty batch mxfp8={mxfp8} sched={sched}", flush=True)
+    inp = S.make_inputs(wl, 4)
+    w, _ = _weights(inp, mxfp8=mxfp8)
+    if mxfp8:
+        wg, wu, wd = dev_bf16(inp.w_gate), dev_bf16(inp.w_up), dev_bf16(inp.w_down)
+        w.wq.update(M.quantize_weights_mxfp8_dgrad(wg, wu, wd))
+    layer = M.MoeLayer(w, 0, wl.K, mxfp8=mxfp8, with_bwd=True, router_bwd=not mxfp8, sched=sched)
+    for t in list(layer.saved.values()) + list(layer.grads.values()):
+        t.view(torch.uint8).fill_(0xA5)
+    x = torch.empty((0, wl.D), dtype=torch.bfloat16, device="cuda")
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.D)
+    sv = layer.saved
+    assert int(host(sv["status"])[0]) == 0
+    assert not host(sv["counts"]).any() and not host(sv["offsets"]).any()
+    assert np.all(host(sv["row_route"]) == -1)
+    g = layer.backward(x, torch.empty((0, wl.D), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    names = ["dw_gate", "dw_up", "dw_down"] + ([] if mxfp8 else ["dw_r", "db_r"])
+    for k in names:
+        assert not host(g[k].view(torch.uint8)).any(), k
+
+
 def test_nan_logits_leave_slots_invalid_and_set_the_status():
     """Logits that are NaN never win a slot; a slot with no candidate left is
     an invalid route (expert -1, probability 0, no row).  Through moe_route on
