@@ -765,6 +765,66 @@ def test_empty_batch(mxfp8, sched):
         assert not host(g[k].view(torch.uint8)).any(), k
 
 
+DEGENERATE_CASES = {
+    # every route dropped: every expert segment is empty
+    "all_dropped": S.scaled(S.WORKLOADS["dsv3_bf16"], "all_dropped", N=100, D=256, E=16, K=4, H=128),
+    # K = E: every expert takes every token
+    "k_equals_e": S.scaled(S.WORKLOADS["dsv3_bf16"], "k_equals_e", N=96, D=256, E=16, K=16, H=128),
+}
+
+
+@pytest.mark.parametrize("mxfp8,sched", [(False, M.MOE_SCHED_STAGED), (False, M.MOE_SCHED_READY),
+                                         (False, M.MOE_SCHED_SINGLE), (True, M.MOE_SCHED_STAGED),
+                                         (True, M.MOE_SCHED_READY)])
+@pytest.mark.parametrize("name", list(DEGENERATE_CASES))
+def test_degenerate_routing(name, mxfp8, sched):
+    """Routing's degenerate cases through the whole layer under every
+    schedule, against the oracle: with every route dropped no expert has a
+    row, the output is exactly 0 and every weight gradient is 0; with K = E
+    every expert holds every token."""
+    wl = DEGENERATE_CASES[name]
+    print(f"degenerate routing {name} mxfp8={mxfp8} sched={sched}", flush=True)
+    inp = S.make_inputs(wl, 7)
+    drop = np.ones((wl.N, wl.K), np.uint8) if name == "all_dropped" else None
+    w, q = _weights(inp, mxfp8=mxfp8)
+    if mxfp8:
+        w.wq.update(M.quantize_weights_mxfp8_dgrad(dev_bf16(inp.w_gate), dev_bf16(inp.w_up), dev_bf16(inp.w_down)))
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, drop=dev(drop) if drop is not None else None, with_bwd=True,
+                       sched=sched)
+    for t in list(layer.saved.values()) + [layer.out] + list(layer.grads.values()):
+        t.view(torch.uint8).fill_(0xA5)
+    x = dev_bf16(inp.x)
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    sv = layer.saved
+    assert int(host(sv["status"])[0]) == 0
+    logits = logits_checked(sv, inp)
+    if mxfp8:
+        ref = O.layer_fwd_mxfp8(inp.x, inp.w_r, inp.bias, q, wl.K, drop=drop, logits=logits)
+    else:
+        ref = O.layer_fwd(inp.x, inp.w_r, inp.bias, inp.w_gate, inp.w_up, inp.w_down, wl.K, drop=drop,
+                          logits=logits)
+    assert_same_route(sv, ref)
+    if name == "all_dropped":
+        assert not host(sv["counts"]).any() and not host(sv["offsets"]).any()
+        assert not bits(out).any()
+    else:
+        assert np.all(host(sv["counts"]) == wl.N)
+        if mxfp8:
+            assert rel_frobenius(vals(out), ref["out"]) <= 3e-2
+        else:
+            assert_bf16_close(vals(out), ref["out"], "out")
+    dout = dev_bf16(S.random_bf16((wl.N, wl.D), 7, 9))
+    g = layer.backward(x, dout)
+    torch.cuda.synchronize()
+    if name == "all_dropped":
+        for k in ("dw_gate", "dw_up", "dw_down", "dx", "dprob"):
+            assert not host(g[k].view(torch.uint8)).any(), k
+    else:
+        for k in ("dw_gate", "dw_up", "dw_down", "dx"):
+            assert np.all(np.isfinite(vals(g[k]))), k
+
+
 def test_nan_logits_leave_slots_invalid_and_set_the_status():
     """Logits that are NaN never win a slot; a slot with no candidate left is
     an invalid route (expert -1, probability 0, no row).  Through moe_route on
