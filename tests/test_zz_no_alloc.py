@@ -35,20 +35,26 @@ def _same(a, b, what):
     assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), what
 
 
-@pytest.mark.parametrize("base,mxfp8", [("dsv3_bf16", False), ("qwen3_235b_bf16_fwdbwd", False),
-                                        ("dsv3_mxfp8", True)])
-def test_noalloc_forward_equals_layer_fwd_on_two_calls(base, mxfp8):
+@pytest.mark.parametrize("base,mxfp8,sched", [("dsv3_bf16", False, M.MOE_SCHED_STAGED),
+                                              ("qwen3_235b_bf16_fwdbwd", False, M.MOE_SCHED_STAGED),
+                                              ("dsv3_mxfp8", True, M.MOE_SCHED_STAGED),
+                                              ("dsv3_bf16", False, M.MOE_SCHED_READY),
+                                              ("dsv3_mxfp8", True, M.MOE_SCHED_READY),
+                                              ("qwen3_235b_bf16_fwdbwd", False, M.MOE_SCHED_SINGLE)])
+def test_noalloc_forward_equals_layer_fwd_on_two_calls(base, mxfp8, sched):
+    """Under each schedule: the readiness queue's state and the single
+    launch's barrier words also live in the scratch, reset by each call."""
     shapes = [dict(N=640, D=512, E=32, K=8, H=256), dict(N=96, D=256, E=16, K=4, H=128)]
     for i, shp in enumerate(shapes):
         wl = S.scaled(S.WORKLOADS[base], f"noalloc_{i}", **shp)
-        print(f"noalloc {base} call {i}: {shp}", flush=True)
+        print(f"noalloc {base} sched {sched} call {i}: {shp}", flush=True)
         inp = S.make_inputs(wl, 40 + i)
         w = _weights(inp, mxfp8)
         drop = dev(inp.drop) if inp.drop is not None else None
         x = dev_bf16(inp.x)
-        ref = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, drop=drop)
+        ref = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, drop=drop, sched=sched)
         ref.forward(x)
-        got = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, drop=drop)
+        got = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, drop=drop, sched=sched)
         got.saved["_buf"].fill_(0xFF)                 # every saved tensor poisoned
         got.out.view(torch.int16).fill_(0x7FA0)
         got.forward_noalloc(x)
