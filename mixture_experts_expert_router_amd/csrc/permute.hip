@@ -3,8 +3,9 @@
 // route-weight gradient, and the MXFP8 row quantizer (OLMo-core Appendix A,
 // A.1-A.4; KOSMOS section 3.3.1 steps 3 and 5, section 3.3.2 step 1).
 //
-// All of them move whole rows with 16-byte vectors, one wave per token row,
-// several vectors in flight per lane.  Dispatch reads each token row once and
+// All of them move rows with 16-byte vectors, one wave per token row or per
+// row segment (the combine, the MXFP8 dispatch), several vectors in flight
+// per lane.  Dispatch reads each token row once and
 // writes it K times (scatter form), so x crosses HBM once.  Combine gathers the
 // K rows of a token and folds them in fp32 in ascending k with fmaf.
 #include "common.h"

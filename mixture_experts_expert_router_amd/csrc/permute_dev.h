@@ -1,7 +1,8 @@
-// Device bodies of the token-row permutes that the single-launch layer runs
-// inside its persistent workgroups as well: the fold (combine) and the
-// combine backward of one token by one wave, and their vector helpers.
-// permute.hip launches them a wave per token.
+// Device bodies of the token-row permutes that the persistent layer kernels
+// run inside their workgroups as well: the MXFP8 dispatch of a row segment,
+// the fold (combine) of a row segment, the combine backward of a token, and
+// their vector helpers.  permute.hip launches them a wave per segment or
+// token.
 #pragma once
 
 #include "common.h"
