@@ -747,9 +747,11 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
   if (MX || !fold) return;
 
   // ---- 4. the fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] -------------------
+  // a wave per row segment of a token (the combine launch's items), 8 a claim
   __syncthreads();   // the workgroup's stores precede thread 0's release below
   if (tid == 0) __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  const int NF = (fold->N + 7) / 8;
+  const int nseg = perm::combine_segs(f.g2.N >> 3);
+  const int NF = (int)(((int64_t)fold->N * nseg + 7) / 8);
   bool all_passed = false;   // thread 0: every workgroup's release acquired
   for (;;) {
     if (tid == 0) s_info[0] = atomicAdd(st + st_fold_head(), 1);
@@ -763,9 +765,11 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
     }
     __syncthreads();   // thread 0 acquired; the workgroup's loads follow
     if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-    const int t = __builtin_amdgcn_readfirstlane(item * 8 + wave);
+    const int w = __builtin_amdgcn_readfirstlane(item * 8 + wave);
+    const int t = w / nseg;
     if (t < fold->N)
-      perm::combine_token<true>(t, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K, fold->out, nullptr, nullptr);
+      perm::combine_seg<true>(t, w - t * nseg, nseg, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K,
+                              fold->out, nullptr, nullptr);
   }
 }
 
@@ -919,12 +923,27 @@ __global__ __launch_bounds__(512) void layer_fwd_single_kernel(SingleFwdParams p
       const int t0 = c * route::kChunk;
       const int nt = min(route::kChunk, p.N - t0);
       const int64_t NE = (int64_t)p.N * p.E;
-      for (int i = tid; i < nt * p.E; i += 512) {
-        const int64_t o = (int64_t)t0 * p.E + i;
-        float v = p.rp.out[o];
-        for (int k = 1; k < S; ++k) v += p.rp.out[(int64_t)k * NE + o];
-        if (p.bias) v += p.bias[i % p.E];
-        p.logits[o] = v;
+      if ((p.E & 3) == 0) {
+        // four adjacent logits a thread, the same sums element by element
+        const int64_t o4 = (int64_t)t0 * p.E / 4, NE4 = NE / 4;
+        const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(p.rp.out);
+        for (int i = tid; i < nt * p.E / 4; i += 512) {
+          f32x4_t v = p4[o4 + i];
+          for (int k = 1; k < S; ++k) v += p4[(int64_t)k * NE4 + o4 + i];
+          if (p.bias) {
+            const int e = (4 * i) % p.E;
+            v += f32x4_t{p.bias[e], p.bias[e + 1], p.bias[e + 2], p.bias[e + 3]};
+          }
+          reinterpret_cast<f32x4_t*>(p.logits)[o4 + i] = v;
+        }
+      } else {
+        for (int i = tid; i < nt * p.E; i += 512) {
+          const int64_t o = (int64_t)t0 * p.E + i;
+          float v = p.rp.out[o];
+          for (int k = 1; k < S; ++k) v += p.rp.out[(int64_t)k * NE + o];
+          if (p.bias) v += p.bias[i % p.E];
+          p.logits[o] = v;
+        }
       }
       __syncthreads();   // the chunk's logits are visible to every wave of the workgroup
     }
