@@ -117,6 +117,9 @@ SINGLE_CASES = {
     # 2048+ tokens: the staged router takes 128-row blocks (and another split)
     "router_bm128": S.scaled(S.WORKLOADS["qwen3_235b_bf16_fwdbwd"], "router_bm128", N=2100, D=128, E=64, K=6,
                              H=192),
+    # rows of three fold segments, the last one short, and dispatch rows wider
+    # than one pass of its two-row loop
+    "wide_rows": S.scaled(S.WORKLOADS["dsv3_bf16"], "wide_rows", N=96, D=8256, E=16, K=2, H=128),
 }
 SINGLE_KEYS = ("logits", "topk_idx", "topk_prob", "counts", "offsets", "dst_rows", "row_route", "xd", "g", "u",
                "h", "y")
