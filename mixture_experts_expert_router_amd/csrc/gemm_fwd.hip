@@ -471,10 +471,9 @@ struct FusedParams {
 // queue state layout (int32 units; 128-byte aligned): the GEMM2 queue heads,
 // then the counters and per-expert and per-row-block words
 __device__ __host__ __forceinline__ int st_err() { return kGemmHeadInts + 1; }
-__device__ __host__ __forceinline__ int st_fold_head() { return kGemmHeadInts + 2; }
-__device__ __host__ __forceinline__ int st_disp_done() { return kGemmHeadInts + 3; }  // dispatch items stored
-__device__ __host__ __forceinline__ int st_g1_done() { return kGemmHeadInts + 4; }    // [row block]
-__device__ __host__ __forceinline__ int st_ints(int max_mb) { return kGemmHeadInts + 4 + max_mb; }
+__device__ __host__ __forceinline__ int st_disp_done() { return kGemmHeadInts + 2; }  // dispatch items stored
+__device__ __host__ __forceinline__ int st_g1_done() { return kGemmHeadInts + 3; }    // [row block]
+__device__ __host__ __forceinline__ int st_ints(int max_mb) { return kGemmHeadInts + 3 + max_mb; }
 
 // fused plan layout (int32 units): each expert's first row block in the
 // planner's order [E], then the GEMM2 plan (the GEMM planner's layout:
@@ -747,29 +746,23 @@ __device__ __forceinline__ void fused_items(const FusedParams& f, const uint8_t*
   if (MX || !fold) return;
 
   // ---- 4. the fold: out[t] = sum over k of w[t,k] Y[dst[t,k]] -------------------
-  // a wave per row segment of a token (the combine launch's items), 8 a claim
+  // after every workgroup has passed its GEMM2 tiles; a wave per row segment
+  // of a token (the combine launch's items), wave w of the grid taking
+  // segments w, w + 8G, ...: no claims, and the waves of a workgroup run
+  // independently
   __syncthreads();   // the workgroup's stores precede thread 0's release below
-  if (tid == 0) __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_fetch_add(fold->passed, f.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_info[3] = wait_ge(f, fold->passed, (int)gridDim.x);
+  }
+  __syncthreads();   // thread 0 acquired; the workgroup's loads follow
+  if (!s_info[3]) return;   // the wait expired (reported): no fold
   const int nseg = perm::combine_segs(f.g2.N >> 3);
-  const int NF = (int)(((int64_t)fold->N * nseg + 7) / 8);
-  bool all_passed = false;   // thread 0: every workgroup's release acquired
-  for (;;) {
-    if (tid == 0) s_info[0] = atomicAdd(st + st_fold_head(), 1);
-    __syncthreads();
-    const int item = s_info[0];
-    __syncthreads();
-    if (item >= NF) break;
-    if (tid == 0) {
-      if (!all_passed) all_passed = wait_ge(f, fold->passed, (int)gridDim.x);
-      s_info[3] = all_passed;
-    }
-    __syncthreads();   // thread 0 acquired; the workgroup's loads follow
-    if (!s_info[3]) continue;   // a wait expired: skip the item (reported)
-    const int w = __builtin_amdgcn_readfirstlane(item * 8 + wave);
-    const int t = w / nseg;
-    if (t < fold->N)
-      perm::combine_seg<true>(t, w - t * nseg, nseg, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N, f.K,
-                              fold->out, nullptr, nullptr);
+  const int64_t nitems = (int64_t)fold->N * nseg;
+  for (int64_t w = (int64_t)blockIdx.x * 8 + wave; w < nitems; w += (int64_t)gridDim.x * 8) {
+    const int t = (int)(w / nseg);
+    perm::combine_seg<true>(t, (int)(w - (int64_t)t * nseg), nseg, f.g2.c0, fold->dst_rows, fold->weight, f.g2.N,
+                            f.K, fold->out, nullptr, nullptr);
   }
 }
 
