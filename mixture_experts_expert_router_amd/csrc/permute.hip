@@ -43,6 +43,10 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
   const int srow = shared_row0 ? *shared_row0 + t : -1;
   const int nvec = D >> 3;
   const uint16_t* src = x + (int64_t)t * D;
+  // the token's destination rows (and weights), lane k holding route k's:
+  // one vector load, read back with readlane in the store loop
+  const int dkl = lane < K ? dst_rows[(int64_t)t * K + lane] : -1;
+  const float wkl = (WEIGHTED && lane < K) ? weight[(int64_t)t * K + lane] : 1.0f;
   for (int v0 = 0; v0 < nvec; v0 += kWave * kVPL) {
     uint4 r[kVPL];
 #pragma unroll
@@ -51,9 +55,11 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(const uint16_t* __re
       if (v < nvec) r[j] = ldg16(src + v * 8);
     }
     for (int k = 0; k < KK; ++k) {
-      const int dk = route_row(dst_rows, t, K, k, srow);
+      const int dk = k < K ? __builtin_amdgcn_readlane(dkl, k) : srow;
       if (dk < 0) continue;
-      const float wk = (WEIGHTED && k < K) ? weight[(int64_t)t * K + k] : 1.0f;
+      const float wk = (WEIGHTED && k < K) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                  __builtin_bit_cast(int, wkl), k))
+                                           : 1.0f;
       uint16_t* out = xd + (int64_t)dk * D;
 #pragma unroll
       for (int j = 0; j < kVPL; ++j) {

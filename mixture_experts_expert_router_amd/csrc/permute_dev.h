@@ -46,6 +46,9 @@ __device__ __forceinline__ void dispatch_mx_token(int t, int seg, const uint16_t
   const int npair = D >> 4;              // 16-element pieces per row
   const int nblk = D >> 5;
   const uint16_t* src = x + (int64_t)t * D;
+  // the token's destination rows, lane k holding route k's: one vector load,
+  // read back with readlane, so the store loop waits on no load per route
+  const int dkl = lane < K ? dst_rows[(int64_t)t * K + lane] : -1;
   {
     const int p0 = seg * kMxSegPieces;
     uint4 qv[PP];
@@ -74,7 +77,7 @@ __device__ __forceinline__ void dispatch_mx_token(int t, int seg, const uint16_t
       packed[j] = (uint32_t)code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
     for (int k = 0; k < KK; ++k) {
-      const int dk = k < K ? dst_rows[(int64_t)t * K + k] : srow;
+      const int dk = k < K ? __builtin_amdgcn_readlane(dkl, k) : srow;
       if (dk < 0) continue;
       uint8_t* qrow = q + (int64_t)dk * D;
       uint8_t* crow = sc + (int64_t)dk * nblk;
