@@ -543,6 +543,27 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         return e0.elapsed_time(e1) / steps
 
     layer_ms = time_layer(layer) if (layer_call or shared_expert or single) else None
+
+    def time_graph(lay):
+        # the same forward call captured once in a HIP graph and replayed
+        # (every step of the call is a kernel, so it captures whole)
+        lay.forward(x)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay.forward(x)
+        for _ in range(2):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        assert int(lay.saved["status"].item()) == 0
+        return e0.elapsed_time(e1) / steps
+
+    graph_ms = time_graph(layer) if single else None
     ready_out = None
     if single and ready_queue_ok(wl):
         # dispatch, GEMM1 and GEMM2 in one readiness-gated launch (outputs
@@ -654,6 +675,9 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
                                               " (MXFP8: block-scaled dgrads, bf16 wgrads)") if wl.mxfp8 else "")}
     if layer_ms is not None:
         out["layer_call_ms"] = layer_ms
+    if graph_ms is not None:
+        out["graph_replay"] = {"layer_fwd_ms": graph_ms, "layer_call_ms": layer_ms,
+                               "note": "the staged moe_layer_fwd call captured in one HIP graph and replayed"}
     if shared is not None:
         out["shared_expert"] = shared
     if single_out is not None:
@@ -667,7 +691,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
 def summary_of(r):
     """The keys of a non-headline workload's result kept in the JSON line."""
     keep = ("value", "unit", "ms_per_step", "fwd_ms", "dtype", "config", "roofline", "grouped_gemm", "dispatch",
-            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward", "single_launch", "ready_queue")
+            "combine", "stage_ms", "layer_fwd_pct_of_roofline", "load", "backward", "single_launch", "ready_queue",
+            "graph_replay")
     return {k: r[k] for k in keep if k in r}
 
 

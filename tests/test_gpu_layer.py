@@ -955,3 +955,47 @@ def test_layer_bwd_mxfp8_native_wgrad(name, shared):
     for e in np.nonzero(ref["counts"] == 0)[0]:
         for k in ("dw_gate", "dw_up", "dw_down"):
             assert not bits(g[k])[e].any(), (k, e)
+
+
+@pytest.mark.parametrize("mxfp8,sched", [(False, M.MOE_SCHED_STAGED), (False, M.MOE_SCHED_READY),
+                                         (False, M.MOE_SCHED_SINGLE), (True, M.MOE_SCHED_STAGED),
+                                         (True, M.MOE_SCHED_READY)])
+def test_layer_calls_replay_from_a_captured_graph(mxfp8, sched):
+    """The layer forward and backward captured in one HIP graph (every step is
+    a kernel: queue heads, plans, barrier words and the status word are reset
+    by kernels of the call, no memset node) and replayed three times, with
+    eager calls and synchronizations between the replays: every replay
+    reproduces the eager results bit for bit, outputs poisoned before each."""
+    wl = S.scaled(S.WORKLOADS["dsv3_mxfp8" if mxfp8 else "dsv3_bf16"], "graph", N=300, D=256, E=64, K=4, H=128)
+    print(f"graph capture mxfp8={mxfp8} sched={sched}", flush=True)
+    inp = S.make_inputs(wl, 11)
+    w, _ = _weights(inp, mxfp8=mxfp8)
+    if mxfp8:
+        w.wq.update(M.quantize_weights_mxfp8_dgrad(dev_bf16(inp.w_gate), dev_bf16(inp.w_up), dev_bf16(inp.w_down)))
+    x = dev_bf16(inp.x)
+    dout = dev_bf16(S.random_bf16((wl.N, wl.D), 11, 9))
+    eager = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, with_bwd=True, router_bwd=not mxfp8, sched=sched)
+    want_out = eager.forward(x).clone()
+    want_g = {k: v.clone() for k, v in eager.backward(x, dout).items()}
+    torch.cuda.synchronize()
+    layer = M.MoeLayer(w, wl.N, wl.K, mxfp8=mxfp8, with_bwd=True, router_bwd=not mxfp8, sched=sched)
+    layer.forward(x)   # warm-up outside the capture (the binding resolves its symbols once)
+    layer.backward(x, dout)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x)
+        layer.backward(x, dout)
+    for rep in range(3):
+        layer.out.view(torch.int16).fill_(0x7FA0)
+        for t in layer.grads.values():
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(host(layer.saved["status"])[0]) == 0, rep
+        assert torch.equal(layer.out.view(torch.int16), want_out.view(torch.int16)), rep
+        for k, v in want_g.items():
+            assert torch.equal(layer.grads[k].view(torch.uint8), v.view(torch.uint8)), (rep, k)
+        eager.forward(x)   # eager work on the same stream between replays
+        torch.cuda.synchronize()
