@@ -721,6 +721,9 @@ def main(argv=None):
                     help="run only the workload's single-launch layer (MOE_SCHED_SINGLE: forward, and backward "
                          "with the router backward for a fwd+bwd workload) warmup + steps times and print its "
                          "times (for a kernel trace of that launch)")
+    ap.add_argument("--ready-only", action="store_true",
+                    help="run only the workload's readiness-gated forward (MOE_SCHED_READY; bf16 or MXFP8) "
+                         "warmup + steps times and print its time (for a kernel trace of that launch)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once: a kernel of known traffic "
                          "that calibrates the HBM byte counters of a profiler run")
@@ -781,6 +784,25 @@ def main(argv=None):
     inp = S.make_inputs(wl, args.seed)
     print(f"# inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
+    if args.ready_only:
+        if not ready_queue_ok(wl):
+            print(f"{wl.name}: outside the readiness-gated launch's rules", file=sys.stderr)
+            return 2
+        x, w, drop = device_inputs(M, inp, wl.mxfp8, torch)
+        lay = M.MoeLayer(w, wl.N, wl.K, mxfp8=wl.mxfp8, drop=drop, renorm=wl.renorm, sched=M.MOE_SCHED_READY)
+        ev = []
+        for i in range(args.warmup + args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            lay.forward(x)
+            e[1].record()
+            if i >= args.warmup:
+                ev.append(e)
+        torch.cuda.synchronize()
+        assert int(lay.saved["status"].item()) == 0
+        print(json.dumps({"workload": wl.name, "sched": "ready", "steps": args.steps,
+                          "fwd_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))}), flush=True)
+        return 0
     if args.single_only:
         bwd = wl.bwd or args.backward
         if not single_launch_ok(wl, bwd):
