@@ -563,7 +563,13 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
         assert int(lay.saved["status"].item()) == 0
         return e0.elapsed_time(e1) / steps
 
-    graph_ms = time_graph(layer) if single else None
+    graph_ms, graph_err = None, None
+    if single:
+        try:
+            graph_ms = time_graph(layer)
+        except Exception as ex:   # a capture the runtime refuses: reported, never fatal to the bench
+            graph_err = f"{type(ex).__name__}: {ex}"
+            torch.cuda.synchronize()
     ready_out = None
     if single and ready_queue_ok(wl):
         # dispatch, GEMM1 and GEMM2 in one readiness-gated launch (outputs
@@ -678,6 +684,8 @@ def measure(M, torch, wl, inp, steps, warmup, seed, backward=False, layer_call=F
     if graph_ms is not None:
         out["graph_replay"] = {"layer_fwd_ms": graph_ms, "layer_call_ms": layer_ms,
                                "note": "the staged moe_layer_fwd call captured in one HIP graph and replayed"}
+    elif graph_err is not None:
+        out["graph_replay"] = {"error": graph_err}
     if shared is not None:
         out["shared_expert"] = shared
     if single_out is not None:
